@@ -1,0 +1,120 @@
+"""Serial fp64 CPU oracle for the GradLev fast-weight scan (ctypes wrapper).
+
+TEST INFRASTRUCTURE ONLY.  Only the test-suite, ``__graft_entry__.smoke()`` and
+the CPU-baseline leg of ``bench.py`` may import this package.  It shares no code
+with the HIP library ``weight_scans_amd`` and never touches a GPU.
+
+The arithmetic lives in ``oracle.c`` (plain C, fp64, one token at a time); this
+module only builds it with gcc and marshals numpy arrays.  See ``oracle.h`` for
+the recurrence and the page passages it follows.
+
+Parity status of each function: ``fwd`` and ``bwd`` are pinned by the CPU tests
+in ``tests/test_oracle.py`` (closed forms, the parallel discounted-sum form,
+torch autograd, finite differences, serial-learner recovery, the causal fixed
+point and the gate-gradient identity).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile oracle.c into liboracle.so with gcc (-O2, no fast-math)."""
+    if force or not os.path.exists(_LIB_PATH):
+        tmp = _LIB_PATH + ".tmp"
+        subprocess.check_call(["gcc", "-O2", "-std=c11", "-fPIC", "-shared",
+                               "-o", tmp, _SRC, "-lpthread"])
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            build(force=True)
+        lib = ctypes.CDLL(_LIB_PATH)
+        i64, i32, p = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p
+        lib.oracle_seq_fwd.argtypes = [i64, i64, i64] + [p] * 8
+        lib.oracle_seq_fwd.restype = None
+        lib.oracle_seq_bwd.argtypes = [i64, i64, i64] + [p] * 6 + [i64, i32] + [p] * 5
+        lib.oracle_seq_bwd.restype = None
+        lib.oracle_fwd.argtypes = [i64] * 5 + [p] * 6 + [i32]
+        lib.oracle_fwd.restype = None
+        lib.oracle_bwd.argtypes = [i64] * 5 + [p] * 6 + [i64, i32] + [p] * 5 + [i32]
+        lib.oracle_bwd.restype = None
+        _lib = lib
+    return _lib
+
+
+def _f64(a):
+    return np.ascontiguousarray(a, dtype=np.float64)
+
+
+def _ptr(a):
+    return a.ctypes.data_as(ctypes.c_void_p) if a is not None else None
+
+
+def default_threads() -> int:
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        return os.cpu_count() or 1
+
+
+def fwd(x, g, eta, alpha, W0, nthreads: int = 1):
+    """y[B,H,T,d_out] = serial readout of the adapted map (fp64)."""
+    x, g, eta, alpha, W0 = map(_f64, (x, g, eta, alpha, W0))
+    B, H, T, d_in = x.shape
+    d_out = g.shape[-1]
+    assert g.shape == (B, H, T, d_out) and eta.shape == (B, H, T)
+    assert alpha.shape == (B, H, T) and W0.shape == (H, d_out, d_in)
+    y = np.empty((B, H, T, d_out), np.float64)
+    _load().oracle_fwd(B, H, T, d_in, d_out, _ptr(x), _ptr(g), _ptr(eta),
+                       _ptr(alpha), _ptr(W0), _ptr(y), int(nthreads))
+    return y
+
+
+def bwd(x, g, eta, alpha, W0, dy, nthreads: int = 1, ckpt: int = 256,
+        variant: int = 0):
+    """(dx, dg, deta, dalpha, dW0) of L = sum <dy, y> by the serial adjoint.
+
+    ``variant=1`` is the page's negative control (W0^T instead of the adapted
+    transpose in the input gradient); it exists only for the mutation test.
+    """
+    x, g, eta, alpha, W0, dy = map(_f64, (x, g, eta, alpha, W0, dy))
+    B, H, T, d_in = x.shape
+    d_out = g.shape[-1]
+    assert dy.shape == g.shape and W0.shape == (H, d_out, d_in)
+    dx = np.empty_like(x)
+    dg = np.empty_like(g)
+    deta = np.empty_like(eta)
+    dalpha = np.empty_like(alpha)
+    dW0 = np.empty_like(W0)
+    _load().oracle_bwd(B, H, T, d_in, d_out, _ptr(x), _ptr(g), _ptr(eta),
+                       _ptr(alpha), _ptr(W0), _ptr(dy), int(ckpt), int(variant),
+                       _ptr(dx), _ptr(dg), _ptr(deta), _ptr(dalpha), _ptr(dW0),
+                       int(nthreads))
+    return dx, dg, deta, dalpha, dW0
+
+
+def seq_fwd(x, g, eta, alpha, W0, S_init=None):
+    """One sequence: returns (y[T,d_out], D_T[d_out,d_in])."""
+    x, g, eta, alpha, W0 = map(_f64, (x, g, eta, alpha, W0))
+    T, d_in = x.shape
+    d_out = g.shape[-1]
+    y = np.empty((T, d_out), np.float64)
+    S = np.empty((d_out, d_in), np.float64)
+    Si = _f64(S_init) if S_init is not None else None
+    _load().oracle_seq_fwd(T, d_in, d_out, _ptr(x), _ptr(g), _ptr(eta),
+                           _ptr(alpha), _ptr(W0), _ptr(Si), _ptr(y), _ptr(S))
+    return y, S

@@ -1,0 +1,334 @@
+"""Pins for the fp64 CPU oracle (no GPU).
+
+Every test here checks the oracle against something other than its own loop:
+closed forms, the parallel discounted-sum form of the weight correction, torch
+autograd, finite differences, exact recovery of the closed-loop serial learner,
+the causal fixed point and a gate-gradient identity.  Page references are to
+"Parallelize the Training, Keep the Learning Serial" (cognaptus.com) unless
+stated otherwise.
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from weight_scans_amd.synth import Workload, make_inputs
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "recovery_magnitudes.txt")
+
+
+def small(B=1, H=1, T=16, d_in=8, d_out=8, seed=7, alpha="base", x="gauss"):
+    w = Workload("t", B, H, T, d_in, d_out, "f64", alpha, x, seed)
+    return make_inputs(w)
+
+
+def relmax(a, b):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    den = np.max(np.abs(b))
+    return float(np.max(np.abs(a - b)) / (den if den > 0 else 1.0))
+
+
+def run_both(inp, **kw):
+    y = oracle.fwd(inp["x"], inp["g"], inp["eta"], inp["alpha"], inp["W0"])
+    grads = oracle.bwd(inp["x"], inp["g"], inp["eta"], inp["alpha"], inp["W0"],
+                       inp["dy"], **kw)
+    return y, grads
+
+
+# ---------------------------------------------------------------------------
+# Independent parallel (closed) form: the adaptation is a discounted sum of the
+# earlier rank-one updates (section "Once the gradient signals are known, the
+# weight trajectory becomes parallelizable").  With V = -diag(eta) G and
+# M[i, j] = prod_{r=j+1}^{i-1} alpha_r for j < i (else 0):
+#   y  = X W0^T + (M o X X^T) V
+# and the adjoint of that dense expression, derived by hand:
+#   dV = (M o XX^T)^T dY,  dg = -eta dV,  deta = -rowsum(G o dV)
+#   E  = M o (dY V^T),     dX = dY W0 + E X + E^T X,   dW0 = dY^T X
+#   dlog(alpha_r) = sum_{j < r < i} (M o XX^T o dY V^T)[i, j]
+# ---------------------------------------------------------------------------
+def decay_matrix(alpha):
+    T = len(alpha)
+    M = np.zeros((T, T))
+    for i in range(T):
+        p = 1.0
+        for j in range(i - 1, -1, -1):
+            M[i, j] = p
+            p *= alpha[j]
+    return M
+
+
+def parallel_form(x, g, eta, alpha, W0, dy):
+    X, G, dY = x, g, dy
+    M = decay_matrix(alpha)
+    V = -eta[:, None] * G
+    XX = X @ X.T
+    P = M * XX
+    y = X @ W0.T + P @ V
+    dV = P.T @ dY
+    dg = -eta[:, None] * dV
+    deta = -np.sum(G * dV, axis=1)
+    E = M * (dY @ V.T)
+    dX = dY @ W0 + E @ X + E.T @ X
+    dW0 = dY.T @ X
+    Z = M * XX * (dY @ V.T)
+    T = len(alpha)
+    dlog = np.zeros(T)
+    for r in range(T):
+        dlog[r] = Z[r + 1:, :r].sum()
+    return y, dX, dg, deta, dlog / alpha, dW0
+
+
+def test_identity_gates_reduce_to_static_map():
+    """alpha = 1, eta = 0: no adaptation, y = W0 x; closed forms for the rest."""
+    inp = small(B=2, H=2, T=24, d_in=6, d_out=5, seed=11)
+    inp["alpha"][:] = 1.0
+    inp["eta"][:] = 0.0
+    y, (dx, dg, deta, dal, dW0) = run_both(inp)
+    X, G, dY, W0 = inp["x"], inp["g"], inp["dy"], inp["W0"]
+    y_ref = np.einsum("hoi,bhti->bhto", W0, X)
+    assert relmax(y, y_ref) < 1e-14
+    assert relmax(dx, np.einsum("hoi,bhto->bhti", W0, dY)) < 1e-14
+    assert np.all(dg == 0.0) and np.all(dal == 0.0)
+    assert relmax(dW0, np.einsum("bhto,bhti->hoi", dY, X)) < 1e-14
+    # deta_t = -sum_{u > t} (g_t . dy_u)(x_u . x_t)
+    gd = np.einsum("bhto,bhuo->bhtu", G, dY)
+    xx = np.einsum("bhui,bhti->bhtu", X, X)
+    strict_upper = np.triu(np.ones((24, 24)), k=1)
+    deta_ref = -np.sum(gd * xx * strict_upper, axis=-1)
+    assert relmax(deta, deta_ref) < 1e-13
+
+
+def test_structural_zeros():
+    """D_0 = 0 gives dalpha_0 = 0; the last update is never read, so
+    deta, dg and dalpha vanish at t = T-1."""
+    inp = small(B=2, H=3, T=37, d_in=5, d_out=7, seed=3)
+    _, (dx, dg, deta, dal, dW0) = run_both(inp)
+    assert np.all(dal[..., 0] == 0.0)
+    assert np.all(deta[..., -1] == 0.0)
+    assert np.all(dg[..., -1, :] == 0.0)
+    assert np.all(dal[..., -1] == 0.0)
+
+
+def test_first_two_tokens_by_hand():
+    """y_0 = W0 x_0 and y_1 = W0 x_1 - eta_0 (x_0 . x_1) g_0; neither depends
+    on any alpha (alpha_0 multiplies the zero adaptation)."""
+    inp = small(T=2, d_in=4, d_out=3, seed=5)
+    X, G, e, W0 = inp["x"][0, 0], inp["g"][0, 0], inp["eta"][0, 0], inp["W0"][0]
+    y = oracle.fwd(inp["x"], inp["g"], inp["eta"], inp["alpha"], inp["W0"])[0, 0]
+    assert relmax(y[0], W0 @ X[0]) < 1e-15
+    assert relmax(y[1], W0 @ X[1] - e[0] * (X[0] @ X[1]) * G[0]) < 1e-15
+    inp2 = dict(inp)
+    inp2["alpha"] = np.full_like(inp["alpha"], 0.123)
+    y2 = oracle.fwd(inp2["x"], inp2["g"], inp2["eta"], inp2["alpha"], inp2["W0"])[0, 0]
+    assert np.array_equal(y, y2)
+    # T = 1: a single readout from W0
+    one = small(T=1, d_in=4, d_out=3, seed=9)
+    y1, (dx1, dg1, de1, da1, dW1) = run_both(one)
+    assert relmax(y1[0, 0, 0], one["W0"][0] @ one["x"][0, 0, 0]) < 1e-15
+    assert np.all(dg1 == 0) and np.all(de1 == 0) and np.all(da1 == 0)
+
+
+@pytest.mark.parametrize("seed,alpha", [(21, "base"), (22, "mix"), (23, "near1")])
+def test_parallel_discounted_sum_form(seed, alpha):
+    """Serial loop vs the dense parallel form (forward and all gradients)."""
+    inp = small(T=48, d_in=7, d_out=6, seed=seed, alpha=alpha)
+    y, (dx, dg, deta, dal, dW0) = run_both(inp)
+    ref = parallel_form(*(inp[k][0, 0] if k != "W0" else inp[k][0]
+                          for k in ("x", "g", "eta", "alpha", "W0", "dy")))
+    for got, want in zip((y[0, 0], dx[0, 0], dg[0, 0], deta[0, 0], dal[0, 0], dW0[0]), ref):
+        assert relmax(got, want) < 1e-12
+
+
+def _torch_serial(x, g, eta, alpha, W0):
+    D = torch.zeros_like(W0)
+    ys = []
+    for t in range(x.shape[0]):
+        ys.append((W0 + D) @ x[t])
+        D = alpha[t] * D - eta[t] * torch.outer(g[t], x[t])
+    return torch.stack(ys)
+
+
+def test_torch_autograd_small():
+    """Brute-force autodiff (torch fp64 CPU) through the serial loop."""
+    inp = small(B=1, H=1, T=14, d_in=6, d_out=5, seed=31, alpha="mix")
+    names = ("x", "g", "eta", "alpha")
+    tens = {k: torch.tensor(inp[k][0, 0], requires_grad=True) for k in names}
+    W0 = torch.tensor(inp["W0"][0], requires_grad=True)
+    y = _torch_serial(tens["x"], tens["g"], tens["eta"], tens["alpha"], W0)
+    (y * torch.tensor(inp["dy"][0, 0])).sum().backward()
+    _, (dx, dg, deta, dal, dW0) = run_both(inp)
+    assert relmax(dx[0, 0], tens["x"].grad.numpy()) < 1e-13
+    assert relmax(dg[0, 0], tens["g"].grad.numpy()) < 1e-13
+    assert relmax(deta[0, 0], tens["eta"].grad.numpy()) < 1e-13
+    assert relmax(dal[0, 0], tens["alpha"].grad.numpy()) < 1e-13
+    assert relmax(dW0[0], W0.grad.numpy()) < 1e-13
+
+
+def test_central_finite_differences():
+    inp = small(B=1, H=1, T=6, d_in=3, d_out=4, seed=41)
+    _, grads = run_both(inp)
+    names = ("x", "g", "eta", "alpha", "W0")
+    h = 1e-6
+
+    def f(d):
+        y = oracle.fwd(d["x"], d["g"], d["eta"], d["alpha"], d["W0"])
+        return float(np.sum(y * d["dy"]))
+
+    for name, grad in zip(names, (grads[0], grads[1], grads[2], grads[3], grads[4])):
+        fd = np.zeros_like(inp[name])
+        for idx in np.ndindex(inp[name].shape):
+            p = {k: v.copy() for k, v in inp.items()}
+            m = {k: v.copy() for k, v in inp.items()}
+            p[name][idx] += h
+            m[name][idx] -= h
+            fd[idx] = (f(p) - f(m)) / (2 * h)
+        assert np.max(np.abs(fd - grad)) < 1e-8, name
+
+
+def test_adjoint_dot_product():
+    """<grad, v> equals the directional derivative along a random v."""
+    inp = small(B=2, H=2, T=120, d_in=12, d_out=10, seed=51, alpha="mix")
+    _, grads = run_both(inp)
+    names = ("x", "g", "eta", "alpha", "W0")
+    rng = np.random.default_rng(0)
+    v = {k: rng.standard_normal(inp[k].shape) for k in names}
+    eps = 1e-5
+
+    def f(s):
+        d = dict(inp)
+        for k in names:
+            d[k] = inp[k] + s * v[k]
+        y = oracle.fwd(d["x"], d["g"], d["eta"], d["alpha"], d["W0"])
+        return float(np.sum(y * inp["dy"]))
+
+    fd = (f(eps) - f(-eps)) / (2 * eps)
+    an = sum(float(np.sum(gr * v[k])) for k, gr in zip(names, grads))
+    assert abs(fd - an) <= 1e-7 * max(1.0, abs(an))
+
+
+def _golden():
+    vals = {}
+    with open(GOLDEN) as fh:
+        for line in fh:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                k, v = line.split()
+                vals[k] = float(v)
+    return vals
+
+
+def _closed_loop_learner(X, R, eta, alpha, W0):
+    """Ordinary serial learner with token loss 0.5 |y_t - r_t|^2: it computes
+    its own costate g_t = y_t - r_t and updates immediately."""
+    D = np.zeros_like(W0)
+    Y, G = [], []
+    for t in range(X.shape[0]):
+        y = (W0 + D) @ X[t]
+        g = y - R[t]
+        D = alpha[t] * D - eta[t] * np.outer(g, X[t])
+        Y.append(y)
+        G.append(g)
+    return np.array(Y), np.array(G)
+
+
+def test_exact_recovery_of_serial_learner():
+    """Supplying the serial learner's own costates G* to the open-loop scan
+    reproduces its outputs, and the costates reconstructed from those outputs
+    equal G*, at rounding scale (section "The synthetic test checks the
+    mechanism, not model quality": ~1e-16 discrepancies)."""
+    inp = small(T=200, d_in=16, d_out=16, seed=61, alpha="mix")
+    X, eta, alpha, W0 = inp["x"][0, 0], inp["eta"][0, 0], inp["alpha"][0, 0], inp["W0"][0]
+    R = np.random.default_rng(62).standard_normal((200, 16))
+    Y_star, G_star = _closed_loop_learner(X, R, eta, alpha, W0)
+    y = oracle.fwd(X[None, None], G_star[None, None], eta[None, None],
+                   alpha[None, None], W0[None])[0, 0]
+    g_rec = y - R
+    page = _golden()
+    scale = max(np.max(np.abs(Y_star)), 1.0)
+    err_y = np.max(np.abs(y - Y_star)) / scale
+    err_g = np.max(np.abs(g_rec - G_star)) / scale
+    # rounding scale: within two orders of the largest printed discrepancy
+    bound = 100 * max(page["outputs"], page["hidden_costates"], page["first_matrix_gradients"])
+    assert err_y < bound and err_g < bound
+
+
+def test_causal_fixed_point_iteration():
+    """The costate map is causal: g~_t depends only on g^_{<t}.  Picard
+    iteration from zero fixes one more token per sweep and reaches the serial
+    learner's costates after T sweeps (section "The predictor is constrained
+    by the learner it is supposed to reproduce")."""
+    T = 12
+    inp = small(T=T, d_in=5, d_out=5, seed=71, alpha="base")
+    X, eta, alpha, W0 = inp["x"][0, 0], inp["eta"][0, 0], inp["alpha"][0, 0], inp["W0"][0]
+    inp["eta"][:] = 0.5  # strong coupling so that the iterates really differ
+    eta = inp["eta"][0, 0]
+    R = np.random.default_rng(72).standard_normal((T, 5))
+    _, G_star = _closed_loop_learner(X, R, eta, alpha, W0)
+    G = np.zeros_like(G_star)
+    for k in range(1, T + 1):
+        y = oracle.fwd(X[None, None], G[None, None], eta[None, None],
+                       alpha[None, None], W0[None])[0, 0]
+        G = y - R
+        assert np.max(np.abs(G[:k] - G_star[:k])) < 1e-12
+        if k <= 4:
+            # not yet fixed: the next token still carries the earlier error
+            assert np.max(np.abs(G[k] - G_star[k])) > 1e-9
+    assert np.max(np.abs(G - G_star)) < 1e-12
+
+
+def test_gate_gradient_identity():
+    """dalpha_r alpha_r = sum_{t>r} q_t - sum_{s>=r} k_s with
+    q_t = dy_t . (y_t - W0 x_t) and k_s = eta_s deta_s: the oracle's direct
+    <Lambda, D> form agrees with a form built from its other outputs."""
+    inp = small(B=2, H=2, T=90, d_in=9, d_out=7, seed=81, alpha="mix")
+    y, (dx, dg, deta, dal, dW0) = run_both(inp)
+    q = np.einsum("bhto,bhto->bht", inp["dy"],
+                  y - np.einsum("hoi,bhti->bhto", inp["W0"], inp["x"]))
+    k = inp["eta"] * deta
+    suf_q = np.flip(np.cumsum(np.flip(q, -1), -1), -1)   # sum_{t >= r}
+    suf_k = np.flip(np.cumsum(np.flip(k, -1), -1), -1)
+    rhs = (suf_q - q) - suf_k
+    assert relmax(dal * inp["alpha"], rhs) < 1e-11
+
+
+def test_segment_composition_and_checkpoints_are_exact():
+    """Associativity in practice: running [0, T1) then [T1, T) from the handed
+    over adaptation equals one run; the backward's checkpoint interval and the
+    thread count do not change a single bit."""
+    inp = small(B=3, H=2, T=77, d_in=6, d_out=5, seed=91, alpha="mix")
+    X, G, e, a, W0 = (inp["x"][1, 1], inp["g"][1, 1], inp["eta"][1, 1],
+                      inp["alpha"][1, 1], inp["W0"][1])
+    y_full, S_full = oracle.seq_fwd(X, G, e, a, W0)
+    y_a, S_a = oracle.seq_fwd(X[:30], G[:30], e[:30], a[:30], W0)
+    y_b, S_b = oracle.seq_fwd(X[30:], G[30:], e[30:], a[30:], W0, S_init=S_a)
+    assert np.array_equal(np.concatenate([y_a, y_b]), y_full)
+    assert np.array_equal(S_b, S_full)
+    ref = oracle.bwd(inp["x"], inp["g"], inp["eta"], inp["alpha"], inp["W0"], inp["dy"], ckpt=1)
+    for ck, nt in ((5, 1), (77, 3), (256, 4)):
+        got = oracle.bwd(inp["x"], inp["g"], inp["eta"], inp["alpha"], inp["W0"],
+                         inp["dy"], ckpt=ck, nthreads=nt)
+        for a_, b_ in zip(got, ref):
+            assert np.array_equal(a_, b_)
+
+
+def test_control_variant_is_caught():
+    """The page's negative control (W0^T in place of the adapted transpose in
+    the backward) leaves the forward and the other gradients untouched but
+    moves the input gradient by O(1) -- the autograd pin detects it."""
+    inp = small(B=1, H=1, T=40, d_in=8, d_out=8, seed=101)
+    inp["eta"][:] = 0.5
+    good = oracle.bwd(inp["x"], inp["g"], inp["eta"], inp["alpha"], inp["W0"], inp["dy"])
+    bad = oracle.bwd(inp["x"], inp["g"], inp["eta"], inp["alpha"], inp["W0"], inp["dy"], variant=1)
+    for i in (1, 2, 3, 4):
+        assert np.array_equal(good[i], bad[i])
+    tx = torch.tensor(inp["x"][0, 0], requires_grad=True)
+    y = _torch_serial(tx, torch.tensor(inp["g"][0, 0]), torch.tensor(inp["eta"][0, 0]),
+                      torch.tensor(inp["alpha"][0, 0]), torch.tensor(inp["W0"][0]))
+    (y * torch.tensor(inp["dy"][0, 0])).sum().backward()
+    assert relmax(good[0][0, 0], tx.grad.numpy()) < 1e-13
+    page = _golden()
+    # same order as the printed control discrepancies (0.3757 / 0.6261)
+    assert relmax(bad[0][0, 0], tx.grad.numpy()) > 0.1 * page["control_hidden_costates"]
