@@ -1,0 +1,122 @@
+/*
+ * gl_scan.h -- C ABI of the GradLev fast-weight scan library (libglscan.so).
+ *
+ * The operation ("Parallelize the Training, Keep the Learning Serial",
+ * cognaptus.com, section "Once the gradient signals are known, the weight
+ * trajectory becomes parallelizable"; GradLev abstract, omanscience.com):
+ * an adaptive linear map with persistent weight W0 and temporary adaptation
+ * D_t = W_t - W0 is updated after every token by one online gradient-descent
+ * step with update size eta_t and retention alpha_t of the previous
+ * adaptation, driven by the costate g_t (gradient of the token loss w.r.t. the
+ * layer output).  Per sequence-head, tokens t = 0..T-1, D_0 = 0:
+ *
+ *     y_t     = (W0 + D_t) x_t            read from the pre-update weight
+ *     D_{t+1} = alpha_t D_t - eta_t g_t x_t^T
+ *
+ * Because the recurrence is affine in D, the library evaluates it as a chunked
+ * associative prefix scan (gl_scan_fwd) and its exact adjoint as the matching
+ * reverse-time scan (gl_scan_bwd), which returns the gradients of
+ * L = sum_t <dy_t, y_t> w.r.t. x, g, eta, alpha and W0.
+ *
+ * Layouts: dense, row-major, last index fastest.
+ *   x, dx                    [B][H][T][d_in]     io dtype
+ *   g, y, dy, dg             [B][H][T][d_out]    io dtype
+ *   eta, alpha, deta, dalpha [B][H][T]           gate dtype (fp64 if io is
+ *                                                F64, else fp32)
+ *   W0                       [H][d_out][d_in]    io dtype (shared by the batch)
+ *   dW0                      [H][d_out][d_in]    gate dtype (sum over batch)
+ *
+ * Ownership: every data pointer is a DEVICE pointer allocated and owned by
+ * the caller; the library keeps no state between calls and allocates no
+ * memory.  Scratch memory is passed in as `ws` (size from
+ * gl_scan_workspace_size).  Outputs are overwritten, never accumulated, and
+ * must not alias inputs.  Calls are asynchronous on `stream` (a hipStream_t;
+ * NULL = the default stream); the caller synchronises.
+ *
+ * Errors: every argument check runs before anything is launched; on error the
+ * call returns a status and touches no output.  GL_ERROR_HIP reports a failed
+ * launch (text via gl_last_error()).  Nothing aborts, prints or throws.
+ *
+ * Numerical preconditions (documented, not checked on the device): inputs
+ * are finite; 0 < alpha_t (the scan works with log alpha; alpha <= 1 keeps
+ * every decay factor at or below one).
+ */
+#ifndef GL_SCAN_H
+#define GL_SCAN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  GL_DTYPE_F64 = 0,  /* fp64 everywhere                                   */
+  GL_DTYPE_F32 = 1,  /* fp32 io, gates, state                             */
+  GL_DTYPE_BF16 = 2  /* bf16 io; fp32 gates, accumulation and state       */
+} gl_dtype_t;
+
+typedef enum {
+  GL_SUCCESS = 0,
+  GL_ERROR_INVALID_VALUE = 1,        /* NULL pointer, negative size, bad enum   */
+  GL_ERROR_NOT_SUPPORTED = 2,        /* shape / dtype / chunk not implemented    */
+  GL_ERROR_MISALIGNED = 3,           /* a data pointer is not 16-byte aligned    */
+  GL_ERROR_WORKSPACE_TOO_SMALL = 4,  /* ws_bytes below gl_scan_workspace_size    */
+  GL_ERROR_HIP = 5                   /* a HIP runtime call or launch failed      */
+} gl_status_t;
+
+/* Flags for gl_scan_desc_t.flags */
+#define GL_FLAG_GENERIC 1u  /* use the portable VALU kernels even where a matrix-
+                               core kernel exists (cross-checking only)        */
+
+typedef struct {
+  int64_t B, H, T;      /* batch, heads, tokens; any may be 0 (no-op)          */
+  int64_t d_in, d_out;  /* 1..128 each; the matrix-core kernels take
+                           d_in == d_out in {64, 128} with BF16 io            */
+  int32_t io_dtype;     /* gl_dtype_t                                          */
+  int32_t chunk;        /* tokens per chunk; 0 = default of the chosen kernels */
+  uint32_t flags;       /* GL_FLAG_*                                           */
+  uint32_t reserved;    /* must be 0                                           */
+} gl_scan_desc_t;
+
+/* Bytes of the optional `saved` buffer that gl_scan_fwd can fill with chunk-
+ * boundary adaptation states for gl_scan_bwd (opaque layout; the same desc
+ * must be used for both calls). */
+gl_status_t gl_scan_saved_size(const gl_scan_desc_t* desc, size_t* saved_bytes);
+
+/* Workspace bytes for gl_scan_fwd and gl_scan_bwd.  have_saved != 0: the bwd
+ * call will receive the fwd's `saved` buffer; 0: the bwd recomputes the
+ * chunk-boundary states itself inside the workspace. */
+gl_status_t gl_scan_workspace_size(const gl_scan_desc_t* desc, int have_saved,
+                                   size_t* fwd_ws_bytes, size_t* bwd_ws_bytes);
+
+/* Forward prefix scan: y.  `saved` may be NULL; otherwise it receives
+ * gl_scan_saved_size bytes of chunk-boundary states. */
+gl_status_t gl_scan_fwd(const gl_scan_desc_t* desc, const void* x, const void* g,
+                        const void* eta, const void* alpha, const void* W0,
+                        void* y, void* saved, void* ws, size_t ws_bytes,
+                        void* stream);
+
+/* Reverse scan: dx, dg, deta, dalpha, dW0 for upstream gradient dy.
+ * `saved` is NULL or the buffer filled by gl_scan_fwd with the same inputs. */
+gl_status_t gl_scan_bwd(const gl_scan_desc_t* desc, const void* x, const void* g,
+                        const void* eta, const void* alpha, const void* W0,
+                        const void* dy, const void* saved, void* dx, void* dg,
+                        void* deta, void* dalpha, void* dW0, void* ws,
+                        size_t ws_bytes, void* stream);
+
+/* Static description of a status code. */
+const char* gl_status_string(gl_status_t status);
+
+/* Text of the last GL_ERROR_HIP / validation failure on the calling thread. */
+const char* gl_last_error(void);
+
+/* Name of the kernel family the library selects for desc ("generic-f64",
+ * "mfma-bf16-d128", ...), or NULL if desc is unsupported. */
+const char* gl_scan_path_name(const gl_scan_desc_t* desc);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* GL_SCAN_H */

@@ -1,0 +1,124 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, and rejects bad arguments before launching anything (the
+pointers passed here are never dereferenced)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import weight_scans_amd as ws
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                      "include", "gl_scan.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gl_\w+)\s*\(", text)))
+
+
+def test_header_and_binding_agree():
+    assert sorted(ws.EXPORTS) == declared_functions()
+
+
+def test_library_exports_every_declared_symbol():
+    L = ws.lib()
+    for name in declared_functions():
+        assert hasattr(L, name), name
+
+
+def desc(**kw):
+    base = dict(B=2, H=3, T=100, d_in=64, d_out=64, io_dtype=ws.GL_DTYPE_BF16, chunk=0, flags=0)
+    base.update(kw)
+    return ws.make_desc(**base)
+
+
+def status(fn, *args):
+    return getattr(ws.lib(), fn)(*args)
+
+
+def test_status_strings():
+    L = ws.lib()
+    for code in range(6):
+        assert L.gl_status_string(code)
+    assert L.gl_status_string(99) == b"unknown status"
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=-1), 1), (dict(T=-5), 1), (dict(d_in=0), 1), (dict(io_dtype=7), 1),
+    (dict(flags=8), 1), (dict(chunk=-1), 1),
+    (dict(d_in=129), 2), (dict(d_out=256), 2), (dict(chunk=48), 2),
+    (dict(io_dtype=ws.GL_DTYPE_F64, chunk=32), 2),
+])
+def test_descriptor_validation(kw, code):
+    d = desc(**kw)
+    n = ctypes.c_size_t()
+    assert ws.lib().gl_scan_saved_size(ctypes.byref(d), ctypes.byref(n)) == code
+    assert ws.path_name(d) is None
+
+
+def test_null_desc():
+    n = ctypes.c_size_t()
+    assert ws.lib().gl_scan_saved_size(None, ctypes.byref(n)) == 1
+
+
+def test_sizes_are_consistent():
+    d = desc()
+    s = ws.saved_size(d)
+    f1, b1 = ws.workspace_size(d, True)
+    f0, b0 = ws.workspace_size(d, False)
+    assert s > 0 and b0 >= b1 + s - 256 and f0 == f1
+    assert ws.path_name(d)
+
+
+FAKE = 0x10000  # 16-byte aligned, never dereferenced
+
+
+def _fwd(d, ptrs, ws_bytes=0):
+    P = [ctypes.c_void_p(p) if p is not None else None for p in ptrs]
+    return ws.lib().gl_scan_fwd(ctypes.byref(d), *P, ctypes.c_void_p(FAKE), ws_bytes, None)
+
+
+def _bwd(d, ptrs, wsp, ws_bytes):
+    P = [ctypes.c_void_p(p) if p is not None else None for p in ptrs]
+    return ws.lib().gl_scan_bwd(ctypes.byref(d), *P, ctypes.c_void_p(wsp) if wsp else None,
+                                ws_bytes, None)
+
+
+def test_fwd_argument_errors_before_launch():
+    d = desc()
+    ok = [FAKE] * 6 + [None]  # x g eta alpha W0 y saved
+    bad_null = list(ok)
+    bad_null[2] = None
+    assert _fwd(d, bad_null) == 1
+    bad_al = list(ok)
+    bad_al[0] = FAKE + 2
+    assert _fwd(d, bad_al) == 3
+    bad_saved = list(ok)
+    bad_saved[6] = FAKE + 8
+    assert _fwd(d, bad_saved) == 3
+    assert b"aligned" in ws.lib().gl_last_error()
+
+
+def test_bwd_argument_errors_before_launch():
+    d = desc()
+    ptrs = [FAKE] * 6 + [None] + [FAKE] * 5  # x g eta alpha W0 dy saved dx dg deta dalpha dW0
+    _, need = ws.workspace_size(d, False)
+    assert _bwd(d, ptrs, FAKE, need - 1) == 4
+    assert _bwd(d, ptrs, None, need) == 1
+    p2 = list(ptrs)
+    p2[10] = None
+    assert _bwd(d, p2, FAKE, need) == 1
+    p3 = list(ptrs)
+    p3[8] = FAKE + 4
+    assert _bwd(d, p3, FAKE, need) == 3
+
+
+def test_empty_forward_is_a_noop():
+    # B*H*T == 0: nothing is launched and no pointer is needed
+    for kw in (dict(T=0), dict(B=0), dict(H=0)):
+        assert _fwd(desc(**kw), [None] * 7) == 0
+    # an empty head count needs no dW0 either
+    assert _bwd(desc(H=0), [None] * 12, None, 0) == 0

@@ -1,0 +1,159 @@
+"""GPU-vs-oracle parity through the C ABI (needs an MI355X).
+
+Small workloads are compared element by element over every output; the large
+ones (the 340M / 1.3B / long-context shapes) run in full on the GPU and are
+compared on whole sampled sequence-heads, which the oracle computes one by one,
+plus dW0 of one head summed over the batch.  Tolerances are in parity_util.
+"""
+import numpy as np
+import pytest
+import torch
+
+import weight_scans_amd as ws
+from parity_util import (NAMES, TOL, compare_full, compare_sampled, host, oracle_all,
+                         oracle_sampled, relmax, run_gpu, to_device)
+from weight_scans_amd.synth import CONFIGS, Workload, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "these tests need a GPU"
+    ws.lib()
+
+
+def _full_case(w: Workload, **kw):
+    say(f"case {w} {kw}")
+    inp = make_inputs(w)
+    dev = to_device(inp, w.dtype)
+    gpu = run_gpu(dev, chunk=w.chunk if "chunk" not in kw else kw.pop("chunk"), **kw)
+    ref = oracle_all(inp)
+    errs, bad = compare_full(gpu, ref, TOL[w.dtype])
+    say(f"  errs {errs}")
+    assert not bad, errs
+    return gpu, ref
+
+
+def test_c1_fp64_full():
+    _full_case(CONFIGS["c1"])
+
+
+def test_c1_fp64_recompute_path():
+    _full_case(CONFIGS["c1"], use_saved=False)
+
+
+def test_c2_fp32_full():
+    _full_case(CONFIGS["c2"].with_(chunk=0))
+
+
+@pytest.mark.parametrize("name,pairs,head", [
+    ("c3", [(0, 0), (7, 15), (3, 9)], 5),
+    ("c4", [(0, 0), (3, 15)], 7),
+    ("c5", [(0, 0), (0, 11)], 3),
+])
+def test_large_sampled(name, pairs, head):
+    w = CONFIGS[name]
+    say(f"case {w}")
+    inp = make_inputs(w)
+    dev = to_device(inp, w.dtype)
+    gpu = run_gpu(dev)
+    ref = oracle_sampled(inp, pairs, dW0_head=head)
+    errs = compare_sampled(gpu, ref, dW0_head=head)
+    say(f"  errs {errs}")
+    bad = {k: e for k, e in errs.items() if not e <= TOL[w.dtype]}
+    assert not bad, errs
+    for n in NAMES:
+        assert torch.isfinite(gpu[n]).all(), n
+
+
+EDGE = [
+    ("f64", 1, 1, 1, 8, 8), ("f64", 1, 2, 2, 5, 3), ("f64", 2, 1, 17, 1, 1),
+    ("f64", 1, 2, 33, 128, 3), ("f32", 2, 2, 63, 32, 32), ("f32", 1, 3, 64, 48, 80),
+    ("f32", 1, 1, 65, 64, 64), ("f32", 1, 2, 1000, 16, 24), ("bf16", 2, 2, 65, 64, 64),
+    ("bf16", 1, 2, 1000, 128, 128), ("bf16", 1, 1, 2, 128, 128), ("bf16", 3, 1, 129, 40, 72),
+]
+
+
+@pytest.mark.parametrize("io,B,H,T,di,do", EDGE)
+def test_edge_shapes(io, B, H, T, di, do):
+    _full_case(Workload("edge", B, H, T, di, do, io, "mix", "gauss", 500 + T + di))
+
+
+@pytest.mark.parametrize("io", ["f64", "f32", "bf16"])
+def test_identity_gates(io):
+    """alpha = 1, eta = 0: y = W0 x and no adaptation gradients."""
+    w = Workload("id", 2, 2, 130, 64, 64, io, "base", "gauss", 77)
+    inp = make_inputs(w)
+    inp["alpha"][:] = 1.0
+    inp["eta"][:] = 0.0
+    gpu = run_gpu(to_device(inp, io))
+    ref = oracle_all(inp)
+    errs, bad = compare_full(gpu, ref, TOL[io])
+    assert not bad, errs
+    assert float(gpu["dg"].abs().max()) == 0.0
+
+
+@pytest.mark.parametrize("io,chunks", [("f64", (8, 16)), ("f32", (8, 16, 32)),
+                                        ("bf16", (8, 16, 32))])
+def test_chunk_invariance(io, chunks):
+    w = Workload("ch", 1, 2, 200, 32, 32, io, "mix", "gauss", 91)
+    inp = make_inputs(w)
+    dev = to_device(inp, io)
+    ref = oracle_all(inp)
+    for c in chunks:
+        gpu = run_gpu(dev, chunk=c)
+        errs, bad = compare_full(gpu, ref, TOL[io])
+        assert not bad, (c, errs)
+
+
+def test_run_to_run_bitwise_determinism():
+    w = CONFIGS["c3"].with_(B=2, T=1024)
+    dev = to_device(make_inputs(w), w.dtype)
+    a = run_gpu(dev)
+    b = run_gpu(dev)
+    for n in NAMES:
+        assert torch.equal(a[n], b[n]), n
+
+
+def test_nan_stays_in_its_sequence():
+    w = Workload("nan", 3, 2, 70, 32, 32, "f32", "base", "gauss", 5)
+    inp = make_inputs(w)
+    dev = to_device(inp, "f32")
+    clean = run_gpu(dev)
+    dev["x"][1, 0, 40, 3] = float("nan")
+    dirty = run_gpu(dev)
+    for n in ("y", "dx", "dg", "deta", "dalpha"):
+        for b in range(3):
+            for h in range(2):
+                if (b, h) == (1, 0):
+                    continue
+                assert torch.equal(clean[n][b, h], dirty[n][b, h]), (n, b, h)
+    assert torch.equal(clean["dW0"][1], dirty["dW0"][1])
+    assert not torch.isfinite(dirty["dW0"][0]).all()
+
+
+def test_autograd_function_matches_bwd():
+    w = Workload("ag", 2, 2, 90, 32, 32, "f64", "mix", "gauss", 13)
+    inp = make_inputs(w)
+    dev = to_device(inp, "f64")
+    leaves = {k: dev[k].clone().requires_grad_(True) for k in ("x", "g", "eta", "alpha", "W0")}
+    y = ws.scan(leaves["x"], leaves["g"], leaves["eta"], leaves["alpha"], leaves["W0"])
+    (y * dev["dy"]).sum().backward()
+    ref = oracle_all(inp)
+    for k, n in (("x", "dx"), ("g", "dg"), ("eta", "deta"), ("alpha", "dalpha"), ("W0", "dW0")):
+        assert relmax(host(leaves[k].grad), ref[n]) < TOL["f64"], k
+
+
+def test_empty_inputs():
+    for io in ("f64", "bf16"):
+        w = Workload("e", 2, 3, 0, 16, 16, io, "base", "gauss", 1)
+        inp = make_inputs(w)
+        dev = to_device(inp, io)
+        out = run_gpu(dev)
+        assert out["y"].numel() == 0
+        assert out["dW0"].shape == (3, 16, 16) and float(out["dW0"].abs().max()) == 0.0

@@ -1,5 +1,223 @@
 """weight_scans_amd: GradLev fast-weight scans on MI355X (HIP, gfx950).
 
-The compute lives in the HIP shared library ``libglscan.so`` behind the C ABI
-declared in ``include/gl_scan.h``; this package only marshals arguments.
+All arithmetic runs in the HIP shared library ``libglscan.so`` behind the C ABI
+of ``include/gl_scan.h``.  This module only marshals torch tensors (device
+memory and the current stream) into those calls; it has no compute fallback and
+raises if the library is missing.
+
+    y, saved = gl_scan_fwd(x, g, eta, alpha, W0)
+    dx, dg, deta, dalpha, dW0 = gl_scan_bwd(x, g, eta, alpha, W0, dy, saved)
+    y = scan(x, g, eta, alpha, W0)          # autograd-aware
+
+Shapes: x [B,H,T,d_in], g [B,H,T,d_out], eta/alpha [B,H,T], W0 [H,d_out,d_in].
 """
+from __future__ import annotations
+
+import ctypes
+import os
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libglscan.so")
+
+EXPORTS = (
+    "gl_scan_saved_size",
+    "gl_scan_workspace_size",
+    "gl_scan_fwd",
+    "gl_scan_bwd",
+    "gl_status_string",
+    "gl_last_error",
+    "gl_scan_path_name",
+)
+
+GL_FLAG_GENERIC = 1
+GL_DTYPE_F64, GL_DTYPE_F32, GL_DTYPE_BF16 = 0, 1, 2
+STATUS_NAMES = {0: "GL_SUCCESS", 1: "GL_ERROR_INVALID_VALUE", 2: "GL_ERROR_NOT_SUPPORTED",
+                3: "GL_ERROR_MISALIGNED", 4: "GL_ERROR_WORKSPACE_TOO_SMALL", 5: "GL_ERROR_HIP"}
+
+
+class GLScanError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+
+
+class Desc(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int64), ("H", ctypes.c_int64), ("T", ctypes.c_int64),
+                ("d_in", ctypes.c_int64), ("d_out", ctypes.c_int64),
+                ("io_dtype", ctypes.c_int32), ("chunk", ctypes.c_int32),
+                ("flags", ctypes.c_uint32), ("reserved", ctypes.c_uint32)]
+
+
+_lib = None
+
+
+def lib():
+    """Load libglscan.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m weight_scans_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        P, S, I = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
+        pd = ctypes.POINTER(Desc)
+        ps = ctypes.POINTER(ctypes.c_size_t)
+        L.gl_scan_saved_size.argtypes = [pd, ps]
+        L.gl_scan_workspace_size.argtypes = [pd, I, ps, ps]
+        L.gl_scan_fwd.argtypes = [pd] + [P] * 7 + [P, S, P]
+        L.gl_scan_bwd.argtypes = [pd] + [P] * 12 + [P, S, P]
+        for f in ("gl_scan_saved_size", "gl_scan_workspace_size", "gl_scan_fwd", "gl_scan_bwd"):
+            getattr(L, f).restype = ctypes.c_int
+        L.gl_status_string.argtypes = [I]
+        L.gl_status_string.restype = ctypes.c_char_p
+        L.gl_last_error.argtypes = []
+        L.gl_last_error.restype = ctypes.c_char_p
+        L.gl_scan_path_name.argtypes = [pd]
+        L.gl_scan_path_name.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def _check(status: int):
+    if status != 0:
+        raise GLScanError(status, lib().gl_last_error().decode())
+
+
+def make_desc(B, H, T, d_in, d_out, io_dtype, chunk=0, flags=0) -> Desc:
+    return Desc(B, H, T, d_in, d_out, io_dtype, chunk, flags, 0)
+
+
+def path_name(desc: Desc) -> str | None:
+    r = lib().gl_scan_path_name(ctypes.byref(desc))
+    return r.decode() if r else None
+
+
+def saved_size(desc: Desc) -> int:
+    n = ctypes.c_size_t()
+    _check(lib().gl_scan_saved_size(ctypes.byref(desc), ctypes.byref(n)))
+    return n.value
+
+
+def workspace_size(desc: Desc, have_saved: bool):
+    f, b = ctypes.c_size_t(), ctypes.c_size_t()
+    _check(lib().gl_scan_workspace_size(ctypes.byref(desc), int(have_saved),
+                                        ctypes.byref(f), ctypes.byref(b)))
+    return f.value, b.value
+
+
+# ---------------------------------------------------------------- torch glue
+def _torch():
+    import torch
+    return torch
+
+
+def _io_code(dtype):
+    torch = _torch()
+    return {torch.float64: GL_DTYPE_F64, torch.float32: GL_DTYPE_F32,
+            torch.bfloat16: GL_DTYPE_BF16}[dtype]
+
+
+def gate_dtype(io_dtype):
+    torch = _torch()
+    return torch.float64 if io_dtype == torch.float64 else torch.float32
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _stream(device):
+    return ctypes.c_void_p(_torch().cuda.current_stream(device).cuda_stream)
+
+
+def _validate(x, g, eta, alpha, W0, dy=None):
+    if x.dim() != 4 or g.dim() != 4:
+        raise ValueError("x and g must be [B,H,T,d]")
+    B, H, T, d_in = x.shape
+    d_out = g.shape[-1]
+    gd = gate_dtype(x.dtype)
+    if g.shape[:3] != (B, H, T) or tuple(W0.shape) != (H, d_out, d_in):
+        raise ValueError("shape mismatch between x, g and W0")
+    if eta.shape != (B, H, T) or alpha.shape != (B, H, T):
+        raise ValueError("eta/alpha must be [B,H,T]")
+    if dy is not None and dy.shape != g.shape:
+        raise ValueError("dy must have the shape of g")
+    for t in (x, g, W0) + ((dy,) if dy is not None else ()):
+        if t.dtype != x.dtype:
+            raise TypeError("x, g, W0 and dy must share the io dtype")
+    for t in (eta, alpha):
+        if t.dtype != gd:
+            raise TypeError(f"eta/alpha must be {gd}")
+    for t in (x, g, eta, alpha, W0) + ((dy,) if dy is not None else ()):
+        if not t.is_cuda:
+            raise ValueError("all tensors must be on a GPU device")
+        if not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous")
+    return B, H, T, d_in, d_out
+
+
+def gl_scan_fwd(x, g, eta, alpha, W0, *, chunk=0, flags=0, save=True):
+    """Forward scan.  Returns (y, saved) where saved is None if save=False."""
+    torch = _torch()
+    B, H, T, d_in, d_out = _validate(x, g, eta, alpha, W0)
+    desc = make_desc(B, H, T, d_in, d_out, _io_code(x.dtype), chunk, flags)
+    y = torch.empty((B, H, T, d_out), dtype=x.dtype, device=x.device)
+    saved = None
+    if save:
+        saved = torch.empty(max(saved_size(desc), 16), dtype=torch.uint8, device=x.device)
+    fws, _ = workspace_size(desc, save)
+    ws = torch.empty(max(fws, 16), dtype=torch.uint8, device=x.device)
+    _check(lib().gl_scan_fwd(ctypes.byref(desc), _ptr(x), _ptr(g), _ptr(eta), _ptr(alpha),
+                             _ptr(W0), _ptr(y), _ptr(saved), _ptr(ws), fws,
+                             _stream(x.device)))
+    return y, saved
+
+
+def gl_scan_bwd(x, g, eta, alpha, W0, dy, saved=None, *, chunk=0, flags=0):
+    """Reverse scan.  Returns (dx, dg, deta, dalpha, dW0)."""
+    torch = _torch()
+    B, H, T, d_in, d_out = _validate(x, g, eta, alpha, W0, dy)
+    desc = make_desc(B, H, T, d_in, d_out, _io_code(x.dtype), chunk, flags)
+    gd = gate_dtype(x.dtype)
+    dx = torch.empty_like(x)
+    dg = torch.empty_like(g)
+    deta = torch.empty_like(eta)
+    dalpha = torch.empty_like(alpha)
+    dW0 = torch.empty((H, d_out, d_in), dtype=gd, device=x.device)
+    _, bws = workspace_size(desc, saved is not None)
+    ws = torch.empty(max(bws, 16), dtype=torch.uint8, device=x.device)
+    _check(lib().gl_scan_bwd(ctypes.byref(desc), _ptr(x), _ptr(g), _ptr(eta), _ptr(alpha),
+                             _ptr(W0), _ptr(dy), _ptr(saved), _ptr(dx), _ptr(dg), _ptr(deta),
+                             _ptr(dalpha), _ptr(dW0), _ptr(ws), bws, _stream(x.device)))
+    return dx, dg, deta, dalpha, dW0
+
+
+def _make_function():
+    torch = _torch()
+
+    class ScanFunction(torch.autograd.Function):
+        @staticmethod
+        def forward(ctx, x, g, eta, alpha, W0, chunk, flags):
+            y, saved = gl_scan_fwd(x, g, eta, alpha, W0, chunk=chunk, flags=flags)
+            ctx.save_for_backward(x, g, eta, alpha, W0, saved)
+            ctx.chunk, ctx.flags = chunk, flags
+            return y
+
+        @staticmethod
+        def backward(ctx, dy):
+            x, g, eta, alpha, W0, saved = ctx.saved_tensors
+            dx, dg, deta, dalpha, dW0 = gl_scan_bwd(x, g, eta, alpha, W0, dy.contiguous(),
+                                                    saved, chunk=ctx.chunk, flags=ctx.flags)
+            return dx, dg, deta, dalpha, dW0.to(W0.dtype), None, None
+
+    return ScanFunction
+
+
+_fn = None
+
+
+def scan(x, g, eta, alpha, W0, chunk=0, flags=0):
+    """Autograd-aware forward scan y = scan(x, g, eta, alpha, W0)."""
+    global _fn
+    if _fn is None:
+        _fn = _make_function()
+    return _fn.apply(x, g, eta, alpha, W0, chunk, flags)

@@ -1,0 +1,236 @@
+// gl_scan.cpp -- host side of the C ABI (include/gl_scan.h): argument checks,
+// kernel-family selection, workspace layout and launches.  Every check runs
+// before the first launch; nothing here allocates device memory.
+#include "gl_scan.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "internal.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+void set_err(const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+}
+
+gl_status_t fail(gl_status_t st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+constexpr size_t kAlign = 256;
+size_t round_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+// Everything the launches need, derived from the descriptor alone so that the
+// forward and the backward agree on the layout of `saved`.
+struct Plan {
+  int io = 0;
+  bool mfma = false;
+  int chunk = 0, n_chunks = 0, ckpt_every = 1, n_ckpt = 0, n_tiles = 0;
+  size_t comp = 8;          // bytes of the compute / gate / state type
+  size_t saved_bytes = 0;   // chunk-boundary states
+  size_t part_bytes = 0;    // deta + dalpha partials
+  size_t dw_bytes = 0;      // dW0 partials (per batch entry)
+  const char* name = "";
+};
+
+gl_status_t make_plan(const gl_scan_desc_t* d, Plan* p) {
+  if (!d) return fail(GL_ERROR_INVALID_VALUE, "desc is NULL");
+  if (d->B < 0 || d->H < 0 || d->T < 0)
+    return fail(GL_ERROR_INVALID_VALUE, "negative B/H/T (%lld, %lld, %lld)", (long long)d->B,
+                (long long)d->H, (long long)d->T);
+  if (d->d_in < 1 || d->d_out < 1)
+    return fail(GL_ERROR_INVALID_VALUE, "d_in and d_out must be >= 1");
+  if (d->io_dtype < GL_DTYPE_F64 || d->io_dtype > GL_DTYPE_BF16)
+    return fail(GL_ERROR_INVALID_VALUE, "unknown io_dtype %d", d->io_dtype);
+  if (d->reserved != 0 || (d->flags & ~GL_FLAG_GENERIC) != 0)
+    return fail(GL_ERROR_INVALID_VALUE, "unknown flags or nonzero reserved field");
+  if (d->chunk < 0) return fail(GL_ERROR_INVALID_VALUE, "negative chunk");
+  if (d->d_in > gls::kGenericMaxD || d->d_out > gls::kGenericMaxD)
+    return fail(GL_ERROR_NOT_SUPPORTED, "d_in/d_out above %d", gls::kGenericMaxD);
+  if (d->B * d->H > 0x7fffffffLL)
+    return fail(GL_ERROR_NOT_SUPPORTED, "B*H above 2^31-1");
+
+  p->io = d->io_dtype;
+  p->comp = (p->io == GL_DTYPE_F64) ? 8 : 4;
+  p->mfma = false;
+  if (d->chunk != 0 && !gls::generic_chunk_ok(p->io, d->chunk))
+    return fail(GL_ERROR_NOT_SUPPORTED, "chunk %d not supported for this dtype", d->chunk);
+  p->chunk = d->chunk ? d->chunk : gls::generic_default_chunk(p->io);
+  p->ckpt_every = 1;
+  p->n_tiles = static_cast<int>((std::max(d->d_in, d->d_out) + gls::kGenericTile - 1) /
+                                gls::kGenericTile);
+  p->name = (p->io == GL_DTYPE_F64) ? "generic-f64"
+            : (p->io == GL_DTYPE_F32) ? "generic-f32" : "generic-bf16";
+
+  p->n_chunks = static_cast<int>((d->T + p->chunk - 1) / p->chunk);
+  p->n_ckpt = (p->n_chunks + p->ckpt_every - 1) / p->ckpt_every;
+  const size_t dd = static_cast<size_t>(d->d_in) * static_cast<size_t>(d->d_out);
+  const size_t BH = static_cast<size_t>(d->B) * static_cast<size_t>(d->H);
+  p->saved_bytes = round_up(BH * p->n_ckpt * dd * p->comp);
+  p->part_bytes = round_up(static_cast<size_t>(p->n_tiles) * BH * d->T * p->comp);
+  p->dw_bytes = round_up(BH * dd * p->comp);
+  return GL_SUCCESS;
+}
+
+size_t bwd_ws(const Plan& p, bool have_saved) {
+  return 2 * p.part_bytes + p.dw_bytes + (have_saved ? 0 : p.saved_bytes);
+}
+
+bool misaligned(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) != 0; }
+
+gl_status_t hip_status(hipError_t e, const char* where) {
+  if (e == hipSuccess) return GL_SUCCESS;
+  set_err("%s: %s", where, hipGetErrorString(e));
+  return GL_ERROR_HIP;
+}
+
+gls::FwdArgs fwd_args(const gl_scan_desc_t* d, const Plan& p, const void* x, const void* g,
+                      const void* eta, const void* alpha, const void* W0, void* y,
+                      void* states) {
+  gls::FwdArgs a;
+  a.x = x; a.g = g; a.eta = eta; a.alpha = alpha; a.W0 = W0; a.y = y; a.states = states;
+  a.B = d->B; a.H = d->H; a.T = d->T;
+  a.d_in = static_cast<int>(d->d_in); a.d_out = static_cast<int>(d->d_out);
+  a.chunk = p.chunk; a.n_chunks = p.n_chunks; a.ckpt_every = p.ckpt_every; a.n_ckpt = p.n_ckpt;
+  return a;
+}
+
+hipError_t launch_fwd(const Plan& p, const gls::FwdArgs& a, hipStream_t s) {
+  return gls::launch_generic_fwd(p.io, a, s);
+}
+
+}  // namespace
+
+extern "C" {
+
+gl_status_t gl_scan_saved_size(const gl_scan_desc_t* desc, size_t* saved_bytes) {
+  Plan p;
+  gl_status_t st = make_plan(desc, &p);
+  if (st != GL_SUCCESS) return st;
+  if (!saved_bytes) return fail(GL_ERROR_INVALID_VALUE, "saved_bytes is NULL");
+  *saved_bytes = p.saved_bytes;
+  return GL_SUCCESS;
+}
+
+gl_status_t gl_scan_workspace_size(const gl_scan_desc_t* desc, int have_saved,
+                                   size_t* fwd_ws_bytes, size_t* bwd_ws_bytes) {
+  Plan p;
+  gl_status_t st = make_plan(desc, &p);
+  if (st != GL_SUCCESS) return st;
+  if (fwd_ws_bytes) *fwd_ws_bytes = 0;
+  if (bwd_ws_bytes) *bwd_ws_bytes = bwd_ws(p, have_saved != 0);
+  return GL_SUCCESS;
+}
+
+gl_status_t gl_scan_fwd(const gl_scan_desc_t* desc, const void* x, const void* g,
+                        const void* eta, const void* alpha, const void* W0, void* y,
+                        void* saved, void* ws, size_t ws_bytes, void* stream) {
+  (void)ws;
+  (void)ws_bytes;
+  Plan p;
+  gl_status_t st = make_plan(desc, &p);
+  if (st != GL_SUCCESS) return st;
+  if (desc->B * desc->H * desc->T == 0) return GL_SUCCESS;
+  if (!x || !g || !eta || !alpha || !W0 || !y)
+    return fail(GL_ERROR_INVALID_VALUE, "NULL input or output pointer");
+  for (const void* q : {x, g, eta, alpha, W0, static_cast<const void*>(y),
+                        static_cast<const void*>(saved)})
+    if (q && misaligned(q)) return fail(GL_ERROR_MISALIGNED, "pointer %p not 16-byte aligned", q);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return hip_status(launch_fwd(p, fwd_args(desc, p, x, g, eta, alpha, W0, y, saved), s),
+                    "forward launch");
+}
+
+gl_status_t gl_scan_bwd(const gl_scan_desc_t* desc, const void* x, const void* g,
+                        const void* eta, const void* alpha, const void* W0, const void* dy,
+                        const void* saved, void* dx, void* dg, void* deta, void* dalpha,
+                        void* dW0, void* ws, size_t ws_bytes, void* stream) {
+  Plan p;
+  gl_status_t st = make_plan(desc, &p);
+  if (st != GL_SUCCESS) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const size_t dd = static_cast<size_t>(desc->d_in) * static_cast<size_t>(desc->d_out);
+  if (desc->B * desc->H * desc->T == 0) {
+    // empty batch / sequence: dW0 is the (zero) empty sum
+    if (desc->H == 0) return GL_SUCCESS;
+    if (!dW0) return fail(GL_ERROR_INVALID_VALUE, "dW0 is NULL");
+    if (misaligned(dW0)) return fail(GL_ERROR_MISALIGNED, "dW0 not 16-byte aligned");
+    return hip_status(hipMemsetAsync(dW0, 0, desc->H * dd * p.comp, s), "dW0 clear");
+  }
+  if (!x || !g || !eta || !alpha || !W0 || !dy || !dx || !dg || !deta || !dalpha || !dW0)
+    return fail(GL_ERROR_INVALID_VALUE, "NULL input or output pointer");
+  if (!ws) return fail(GL_ERROR_INVALID_VALUE, "workspace is NULL");
+  for (const void* q : {x, g, eta, alpha, W0, dy, saved, static_cast<const void*>(dx),
+                        static_cast<const void*>(dg), static_cast<const void*>(deta),
+                        static_cast<const void*>(dalpha), static_cast<const void*>(dW0),
+                        static_cast<const void*>(ws)})
+    if (q && misaligned(q)) return fail(GL_ERROR_MISALIGNED, "pointer %p not 16-byte aligned", q);
+  const size_t need = bwd_ws(p, saved != nullptr);
+  if (ws_bytes < need)
+    return fail(GL_ERROR_WORKSPACE_TOO_SMALL, "workspace %zu bytes, need %zu", ws_bytes, need);
+
+  char* w = static_cast<char*>(ws);
+  void* part_eta = w;
+  void* part_alpha = w + p.part_bytes;
+  void* part_dW0 = w + 2 * p.part_bytes;
+  const void* states = saved;
+  if (!saved) {
+    void* rec = w + 2 * p.part_bytes + p.dw_bytes;
+    st = hip_status(launch_fwd(p, fwd_args(desc, p, x, g, eta, alpha, W0, nullptr, rec), s),
+                    "state recompute launch");
+    if (st != GL_SUCCESS) return st;
+    states = rec;
+  }
+
+  gls::BwdArgs b;
+  b.x = x; b.g = g; b.eta = eta; b.alpha = alpha; b.W0 = W0; b.dy = dy; b.states = states;
+  b.dx = dx; b.dg = dg; b.part_eta = part_eta; b.part_alpha = part_alpha; b.part_dW0 = part_dW0;
+  b.B = desc->B; b.H = desc->H; b.T = desc->T;
+  b.d_in = static_cast<int>(desc->d_in); b.d_out = static_cast<int>(desc->d_out);
+  b.chunk = p.chunk; b.n_chunks = p.n_chunks; b.ckpt_every = p.ckpt_every; b.n_ckpt = p.n_ckpt;
+  b.n_tiles = p.n_tiles;
+  st = hip_status(gls::launch_generic_bwd(p.io, b, s), "backward launch");
+  if (st != GL_SUCCESS) return st;
+
+  gls::FinArgs f;
+  f.part_eta = part_eta; f.part_alpha = part_alpha; f.part_dW0 = part_dW0;
+  f.deta = deta; f.dalpha = dalpha; f.dW0 = dW0;
+  f.B = desc->B; f.H = desc->H; f.T = desc->T;
+  f.d_in = b.d_in; f.d_out = b.d_out; f.n_tiles = p.n_tiles;
+  return hip_status(gls::launch_finalize(p.io, f, s), "finalize launch");
+}
+
+const char* gl_status_string(gl_status_t status) {
+  switch (status) {
+    case GL_SUCCESS: return "success";
+    case GL_ERROR_INVALID_VALUE: return "invalid value";
+    case GL_ERROR_NOT_SUPPORTED: return "not supported";
+    case GL_ERROR_MISALIGNED: return "pointer not 16-byte aligned";
+    case GL_ERROR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case GL_ERROR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+const char* gl_last_error(void) { return g_err; }
+
+const char* gl_scan_path_name(const gl_scan_desc_t* desc) {
+  Plan p;
+  if (make_plan(desc, &p) != GL_SUCCESS) return nullptr;
+  return p.name;
+}
+
+}  // extern "C"

@@ -1,0 +1,75 @@
+// internal.hpp -- argument blocks and launchers shared by the host API and the
+// kernel translation units of libglscan.so.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+namespace gls {
+
+enum IoType { IO_F64 = 0, IO_F32 = 1, IO_BF16 = 2 };
+
+// Forward scan.  One work-group owns one (b, h) and a tile of rows of the
+// adaptation D (rows are independent chains: y reduces over columns only).
+struct FwdArgs {
+  const void* x;      // [B][H][T][d_in]   io
+  const void* g;      // [B][H][T][d_out]  io
+  const void* eta;    // [B][H][T]         gate
+  const void* alpha;  // [B][H][T]         gate
+  const void* W0;     // [H][d_out][d_in]  io
+  void* y;            // [B][H][T][d_out]  io, may be null (states only)
+  void* states;       // [B*H][n_ckpt][d_out][d_in] compute type, may be null
+  int64_t B, H, T;
+  int d_in, d_out;
+  int chunk;          // tokens per chunk
+  int n_chunks;       // ceil(T / chunk)
+  int ckpt_every;     // a state is stored before every ckpt_every-th chunk
+  int n_ckpt;         // ceil(n_chunks / ckpt_every)
+};
+
+// Reverse scan.  Work-group (k, b*H+h) owns column tile k of D and Lambda
+// (for dx) and row tile k of Lambda (for dg); per-token scalars and dW0 are
+// emitted as partials and summed by the finalize kernel in a fixed order.
+struct BwdArgs {
+  const void* x;
+  const void* g;
+  const void* eta;
+  const void* alpha;
+  const void* W0;
+  const void* dy;
+  const void* states;  // chunk-boundary states written by the forward kernel
+  void* dx;
+  void* dg;
+  void* part_eta;      // [n_tiles][B*H*T]  compute type
+  void* part_alpha;    // [n_tiles][B*H*T]  compute type
+  void* part_dW0;      // [B*H][d_out][d_in] compute type
+  int64_t B, H, T;
+  int d_in, d_out;
+  int chunk, n_chunks, ckpt_every, n_ckpt;
+  int n_tiles;
+};
+
+struct FinArgs {
+  const void* part_eta;
+  const void* part_alpha;
+  const void* part_dW0;
+  void* deta;
+  void* dalpha;
+  void* dW0;
+  int64_t B, H, T;
+  int d_in, d_out;
+  int n_tiles;
+};
+
+// Generic (VALU) kernels: any 1 <= d_in, d_out <= 128, all io types.
+constexpr int kGenericMaxD = 128;
+constexpr int kGenericTile = 16;  // rows per forward tile, cols/rows per bwd tile
+bool generic_chunk_ok(int io, int chunk);
+int generic_default_chunk(int io);
+hipError_t launch_generic_fwd(int io, const FwdArgs& a, hipStream_t s);
+hipError_t launch_generic_bwd(int io, const BwdArgs& a, hipStream_t s);
+hipError_t launch_finalize(int io, const FinArgs& a, hipStream_t s);
+
+}  // namespace gls
