@@ -72,4 +72,8 @@ hipError_t launch_generic_fwd(int io, const FwdArgs& a, hipStream_t s);
 hipError_t launch_generic_bwd(int io, const BwdArgs& a, hipStream_t s);
 hipError_t launch_finalize(int io, const FinArgs& a, hipStream_t s);
 
+// Matrix-core kernels: bf16 io, d_in == d_out in {64, 128}, chunk 64.
+constexpr int kMfmaChunk = 64;
+hipError_t launch_mfma_fwd(const FwdArgs& a, hipStream_t s);
+
 }  // namespace gls
