@@ -42,8 +42,7 @@ struct Plan {
   int chunk = 0, n_chunks = 0, ckpt_every = 1, n_ckpt = 0, n_tiles = 0;
   size_t comp = 8;          // bytes of the compute / gate / state type
   size_t saved_bytes = 0;   // chunk-boundary states
-  int gchunk = 0, gn_chunks = 0;
-  size_t gstates_bytes = 0; // states of the generic kernels
+  size_t state_elem = 4;    // bytes per stored state element
   size_t part_bytes = 0;    // deta + dalpha partials
   size_t dw_bytes = 0;      // dW0 partials (per batch entry)
   const char* name = "";
@@ -72,44 +71,34 @@ gl_status_t make_plan(const gl_scan_desc_t* d, Plan* p) {
                           (d->d_in == 64 || d->d_in == 128) && !(d->flags & GL_FLAG_GENERIC);
   const size_t dd = static_cast<size_t>(d->d_in) * static_cast<size_t>(d->d_out);
   const size_t BH = static_cast<size_t>(d->B) * static_cast<size_t>(d->H);
-  // generic kernels (always needed by the backward for now)
-  const int gchunk = (d->chunk && gls::generic_chunk_ok(p->io, d->chunk))
-                         ? d->chunk : gls::generic_default_chunk(p->io);
-  p->gchunk = gchunk;
-  p->gn_chunks = static_cast<int>((d->T + gchunk - 1) / gchunk);
-  p->n_tiles = static_cast<int>((std::max(d->d_in, d->d_out) + gls::kGenericTile - 1) /
-                                gls::kGenericTile);
-  p->gstates_bytes = round_up(BH * p->gn_chunks * dd * p->comp);
   if (mfma_shape && (d->chunk == 0 || d->chunk == gls::kMfmaChunk)) {
     p->mfma = true;
     p->chunk = gls::kMfmaChunk;
-    p->n_chunks = static_cast<int>((d->T + p->chunk - 1) / p->chunk);
-    p->ckpt_every = 1;
-    p->n_ckpt = p->n_chunks;
-    p->saved_bytes = round_up(BH * p->n_chunks * dd * 2);
+    p->n_tiles = gls::mfma_bwd_tiles(static_cast<int>(d->d_in));
     p->name = d->d_in == 64 ? "mfma-bf16-d64" : "mfma-bf16-d128";
+    p->state_elem = 2;  // bf16 chunk-start states
   } else {
     if (d->chunk != 0 && !gls::generic_chunk_ok(p->io, d->chunk))
       return fail(GL_ERROR_NOT_SUPPORTED, "chunk %d not supported for this dtype/shape", d->chunk);
     p->mfma = false;
-    p->chunk = gchunk;
-    p->n_chunks = p->gn_chunks;
-    p->ckpt_every = 1;
-    p->n_ckpt = p->n_chunks;
-    p->saved_bytes = p->gstates_bytes;
+    p->chunk = d->chunk ? d->chunk : gls::generic_default_chunk(p->io);
+    p->n_tiles = static_cast<int>((std::max(d->d_in, d->d_out) + gls::kGenericTile - 1) /
+                                  gls::kGenericTile);
     p->name = (p->io == GL_DTYPE_F64) ? "generic-f64"
               : (p->io == GL_DTYPE_F32) ? "generic-f32" : "generic-bf16";
+    p->state_elem = p->comp;
   }
+  p->n_chunks = static_cast<int>((d->T + p->chunk - 1) / p->chunk);
+  p->ckpt_every = 1;
+  p->n_ckpt = p->n_chunks;
+  p->saved_bytes = round_up(BH * p->n_ckpt * dd * p->state_elem);
   p->part_bytes = round_up(static_cast<size_t>(p->n_tiles) * BH * d->T * p->comp);
   p->dw_bytes = round_up(BH * dd * p->comp);
   return GL_SUCCESS;
 }
 
 size_t bwd_ws(const Plan& p, bool have_saved) {
-  // the generic backward cannot read the matrix-core forward's states: it
-  // recomputes its own
-  const bool own = p.mfma || !have_saved;
-  return 2 * p.part_bytes + p.dw_bytes + (own ? p.gstates_bytes : 0);
+  return 2 * p.part_bytes + p.dw_bytes + (have_saved ? 0 : p.saved_bytes);
 }
 
 bool misaligned(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) != 0; }
@@ -134,18 +123,6 @@ gls::FwdArgs fwd_args(const gl_scan_desc_t* d, const Plan& p, const void* x, con
 hipError_t launch_fwd(const Plan& p, const gls::FwdArgs& a, hipStream_t s) {
   if (p.mfma) return gls::launch_mfma_fwd(a, s);
   return gls::launch_generic_fwd(p.io, a, s);
-}
-
-// Generic-kernel view of a plan (used by the backward for every shape).
-Plan generic_view(const Plan& p) {
-  Plan g = p;
-  g.mfma = false;
-  g.chunk = p.gchunk;
-  g.n_chunks = p.gn_chunks;
-  g.ckpt_every = 1;
-  g.n_ckpt = p.gn_chunks;
-  g.saved_bytes = p.gstates_bytes;
-  return g;
 }
 
 }  // namespace
@@ -222,11 +199,10 @@ gl_status_t gl_scan_bwd(const gl_scan_desc_t* desc, const void* x, const void* g
   void* part_eta = w;
   void* part_alpha = w + p.part_bytes;
   void* part_dW0 = w + 2 * p.part_bytes;
-  const Plan gp = generic_view(p);
-  const void* states = p.mfma ? nullptr : saved;
+  const void* states = saved;
   if (!states) {
     void* rec = w + 2 * p.part_bytes + p.dw_bytes;
-    st = hip_status(launch_fwd(gp, fwd_args(desc, gp, x, g, eta, alpha, W0, nullptr, rec), s),
+    st = hip_status(launch_fwd(p, fwd_args(desc, p, x, g, eta, alpha, W0, nullptr, rec), s),
                     "state recompute launch");
     if (st != GL_SUCCESS) return st;
     states = rec;
@@ -237,9 +213,10 @@ gl_status_t gl_scan_bwd(const gl_scan_desc_t* desc, const void* x, const void* g
   b.dx = dx; b.dg = dg; b.part_eta = part_eta; b.part_alpha = part_alpha; b.part_dW0 = part_dW0;
   b.B = desc->B; b.H = desc->H; b.T = desc->T;
   b.d_in = static_cast<int>(desc->d_in); b.d_out = static_cast<int>(desc->d_out);
-  b.chunk = gp.chunk; b.n_chunks = gp.n_chunks; b.ckpt_every = gp.ckpt_every; b.n_ckpt = gp.n_ckpt;
+  b.chunk = p.chunk; b.n_chunks = p.n_chunks; b.ckpt_every = p.ckpt_every; b.n_ckpt = p.n_ckpt;
   b.n_tiles = p.n_tiles;
-  st = hip_status(gls::launch_generic_bwd(p.io, b, s), "backward launch");
+  st = hip_status(p.mfma ? gls::launch_mfma_bwd(b, s) : gls::launch_generic_bwd(p.io, b, s),
+                  "backward launch");
   if (st != GL_SUCCESS) return st;
 
   gls::FinArgs f;

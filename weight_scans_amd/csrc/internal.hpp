@@ -75,5 +75,7 @@ hipError_t launch_finalize(int io, const FinArgs& a, hipStream_t s);
 // Matrix-core kernels: bf16 io, d_in == d_out in {64, 128}, chunk 64.
 constexpr int kMfmaChunk = 64;
 hipError_t launch_mfma_fwd(const FwdArgs& a, hipStream_t s);
+hipError_t launch_mfma_bwd(const BwdArgs& a, hipStream_t s);
+int mfma_bwd_tiles(int d);
 
 }  // namespace gls

@@ -31,17 +31,6 @@ constexpr int kC = 64;    // tokens per chunk
 constexpr int kTN = 32;   // rows of the adaptation per work-group
 constexpr int kNT = 256;  // threads (4 waves)
 
-// LDS barrier that does not wait for outstanding global loads (the next
-// chunk's prefetch stays in flight across it).
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-
-__device__ __forceinline__ uint32_t half_of(const uint4& u, int q) {
-  const uint32_t w = (q >> 1) == 0 ? u.x : (q >> 1) == 1 ? u.y : (q >> 1) == 2 ? u.z : u.w;
-  return (q & 1) ? (w >> 16) : (w & 0xffffu);
-}
-
 template <int D>
 struct FwdSmem {
   static constexpr int XP = D + 8;   // row stride of token-major tiles (elements)
@@ -174,16 +163,9 @@ __global__ __launch_bounds__(kNT) void fwd_mfma(FwdArgs a) {
 
     // gates: wave 0, lane = token
     if (wave == 0) {
-      const float al = sm.alpha_raw[lane], et = sm.eta_raw[lane];
-      float l = log2f(al);
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const float v = __shfl_up(l, off, 64);
-        if (lane >= off) l += v;
-      }
-      float lp = __shfl_up(l, 1, 64);
-      if (lane == 0) lp = 0.f;
-      const float ll = __shfl(l, 63, 64);
+      const float et = sm.eta_raw[lane];
+      const ChunkGates cg = chunk_gates(sm.alpha_raw[lane], lane);
+      const float l = cg.l, lp = cg.lq, ll = cg.llast;
       sm.lq[lane] = lp;
       sm.li[lane] = l;
       sm.eq[lane] = exp2f(lp);

@@ -41,4 +41,38 @@ __device__ __forceinline__ float bf16_val(uint16_t b) {
   return __uint_as_float(static_cast<uint32_t>(b) << 16);
 }
 
+// LDS barrier that does not wait for outstanding global loads, so a prefetch
+// of the next chunk stays in flight across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// 16-bit element q (0..7) of a 16-byte vector of bf16.
+__device__ __forceinline__ uint32_t half_of(const uint4& u, int q) {
+  const uint32_t w = (q >> 1) == 0 ? u.x : (q >> 1) == 1 ? u.y : (q >> 1) == 2 ? u.z : u.w;
+  return (q & 1) ? (w >> 16) : (w & 0xffffu);
+}
+
+// Chunk gates, lane = token (one wave, 64 tokens).  Works in log2:
+//   l_i = sum_{r <= i} log2 alpha_r (inclusive),  lq_i = l_{i-1} (l_{-1} = 0)
+// Padding tokens must carry alpha = 1, eta = 0.
+struct ChunkGates {
+  float l, lq, llast;
+};
+__device__ __forceinline__ ChunkGates chunk_gates(float alpha, int lane) {
+  float l = log2f(alpha);
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const float v = __shfl_up(l, off, 64);
+    if (lane >= off) l += v;
+  }
+  float lp = __shfl_up(l, 1, 64);
+  if (lane == 0) lp = 0.f;
+  ChunkGates g;
+  g.l = l;
+  g.lq = lp;
+  g.llast = __shfl(l, 63, 64);
+  return g;
+}
+
 }  // namespace gls
