@@ -5,6 +5,9 @@ ones (the 340M / 1.3B / long-context shapes) run in full on the GPU and are
 compared on whole sampled sequence-heads, which the oracle computes one by one,
 plus dW0 of one head summed over the batch.  Tolerances are in parity_util.
 """
+import json
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -21,6 +24,14 @@ def say(msg):
     print(msg, flush=True)
 
 
+def report(case, errs):
+    """Append the measured errors to $PARITY_REPORT (JSON lines), if set."""
+    path = os.environ.get("PARITY_REPORT")
+    if path:
+        with open(path, "a") as fh:
+            fh.write(json.dumps({"case": str(case), "errs": errs}) + "\n")
+
+
 @pytest.fixture(scope="module", autouse=True)
 def _gpu():
     assert torch.cuda.is_available(), "these tests need a GPU"
@@ -35,7 +46,8 @@ def _full_case(w: Workload, **kw):
     ref = oracle_all(inp)
     errs, bad = compare_full(gpu, ref, TOL[w.dtype])
     say(f"  errs {errs}")
-    assert not bad, errs
+    report(w.name, errs)
+    assert not bad, "\n".join(f"{k}: {v:.3e}" for k, v in errs.items())
     return gpu, ref
 
 
@@ -65,8 +77,9 @@ def test_large_sampled(name, pairs, head):
     ref = oracle_sampled(inp, pairs, dW0_head=head)
     errs = compare_sampled(gpu, ref, dW0_head=head)
     say(f"  errs {errs}")
+    report(name, errs)
     bad = {k: e for k, e in errs.items() if not e <= TOL[w.dtype]}
-    assert not bad, errs
+    assert not bad, "\n".join(f"{k}: {v:.3e}" for k, v in errs.items())
     for n in NAMES:
         assert torch.isfinite(gpu[n]).all(), n
 

@@ -19,9 +19,12 @@
 //              + (sum_{u>i} x_u.(Be X)_u - sum_{j>=i} x_j.(Be^T X)_j) / alpha_i
 //   dW0     += sum_u dy_u x_u^T
 // D_in (the adaptation at the chunk start) comes from the forward's saved
-// states.  The backward needs the adjoint both by rows (u reduces over
-// columns) and by columns (dx reduces over rows), so every (b, h) gets two
-// kinds of work-group in one launch:
+// states (bf16, natural [row][col] layout).  LDS tiles are token-major; products
+// that contract over tokens or rows use transposing LDS reads, and outputs are
+// produced transposed so that every write is 8 or 16 bytes wide.
+// The backward needs the adjoint both by rows (u reduces over columns) and by
+// columns (dx reduces over rows), so every (b, h) gets two kinds of
+// work-group in one launch:
 //   role A, row tile R (32 rows): Lam[R, :] -> dg[:, R], deta partial, dW0[R, :]
 //   role B, col tile K (32 cols): Lam[:, K], D_in[:, K] -> dx[:, K], dalpha partial
 // Per-token partials are summed over the tiles by the finalize kernel in a
@@ -38,29 +41,30 @@ namespace {
 constexpr int kC = 64;    // tokens per chunk
 constexpr int kT = 32;    // rows / columns per tile
 constexpr int kNT = 256;  // threads (4 waves)
+constexpr int NP = kT + 8, CP = kC + 8;
 
 template <int D>
 struct SmA {
-  static constexpr int XP = D + 8, TP = kC + 8, RP = kT + 8;
-  __bf16 X[kC][XP];   // x                       [token][feature]
-  __bf16 Xt[D][TP];   // x^T                     [feature][token]
-  __bf16 Dt[kT][TP];  // dy of the row tile, ^T  [row][token]
-  __bf16 PT[kC][TP];  // PT[i][u] = P_ui (u > i)
-  __bf16 L[kT][XP];   // Lam_out[R, :] (bf16)    [row][col]
-  __bf16 Gr[kC][RP];  // g of the row tile       [token][row]
-  __bf16 DGs[kC][RP]; // dg staging              [token][row]
+  static constexpr int XP = D + 8;
+  __bf16 X[kC][XP];    // x                          [token][feature]
+  __bf16 Dr[kC][NP];   // dy of the row tile         [token][row]
+  __bf16 Drs[kC][NP];  // e(lq_u) dy of the row tile [token][row]
+  __bf16 Gr[kC][NP];   // g of the row tile          [token][row]
+  __bf16 PT[kC][CP];   // PT[i][u] = P_ui (u > i)
+  __bf16 L[kT][XP];    // Lam_out[R, :] (bf16)       [row][col]
+  __bf16 DGs[kC][NP];  // dg staging                 [token][row]
 };
 
 template <int D>
 struct SmB {
-  static constexpr int XP = D + 8, TP = kC + 8;
-  __bf16 Dy[kC][XP];  // dy                      [token][feature]
-  __bf16 G[kC][XP];   // g                       [token][feature]
-  __bf16 Xt[kT][TP];  // x of the col tile, ^T   [col][token]
-  __bf16 Be[kC][TP];  // Be[i][j]
-  __bf16 BeT[kC][TP]; // BeT[j][i] = Be[i][j]
-  __bf16 Sn[kT][XP];  // D_in[:, K]^T (bf16)     [col][row]
-  __bf16 L[kT][XP];   // Lam_out[:, K]^T (bf16)  [col][row]
+  static constexpr int XP = D + 8;
+  __bf16 Dy[kC][XP];   // dy                         [token][feature]
+  __bf16 G[kC][XP];    // g                          [token][feature]
+  __bf16 Xk[kC][NP];   // x of the column tile       [token][col]
+  __bf16 Xks[kC][NP];  // e(lq_u) x of the col tile  [token][col]
+  __bf16 BeT[kC][CP];  // BeT[j][i] = Be_ij (j < i)
+  __bf16 Sn[D][NP];    // D_in[:, K] (bf16)          [row][col]
+  __bf16 L[D][NP];     // Lam_out[:, K] (bf16)       [row][col]
 };
 
 template <int D>
@@ -70,30 +74,10 @@ union BwdSmem {
 };
 
 struct GateSmem {
-  float lq[kC], li[kC], eq[kC], e2[kC], neta[kC], al[kC];
-  float eta_raw[kC], alpha_raw[kC];
+  float lq[kC], li[kC], e2[kC], eq[kC], neta[kC], al[kC];
   float sp[kC], sr[kC], sq[kC], sk[kC];
   float red[4];
-  float gam, llast;
 };
-
-__constant__ int kBlkI[10] = {0, 1, 1, 2, 2, 2, 3, 3, 3, 3};
-__constant__ int kBlkJ[10] = {0, 0, 1, 0, 1, 2, 0, 1, 2, 3};
-
-__device__ __forceinline__ void gates_to_smem(GateSmem& gs, int lane) {
-  const float et = gs.eta_raw[lane], al = gs.alpha_raw[lane];
-  const ChunkGates cg = chunk_gates(al, lane);
-  gs.lq[lane] = cg.lq;
-  gs.li[lane] = cg.l;
-  gs.eq[lane] = exp2f(cg.lq);
-  gs.e2[lane] = exp2f(cg.llast - cg.l);
-  gs.neta[lane] = -et;
-  gs.al[lane] = al;
-  if (lane == 0) {
-    gs.gam = exp2f(cg.llast);
-    gs.llast = cg.llast;
-  }
-}
 
 __device__ __forceinline__ float sum16(float v) {
   v += __shfl_xor(v, 1, 64);
@@ -103,11 +87,68 @@ __device__ __forceinline__ float sum16(float v) {
   return v;
 }
 
+__device__ __forceinline__ float sum_groups(float v) {  // over the 4 lane groups of 16
+  v += __shfl_xor(v, 16, 64);
+  v += __shfl_xor(v, 32, 64);
+  return v;
+}
+
+__device__ __forceinline__ uint4 scale_bf16x8(const uint4& v, float s) {
+  uint4 r;
+  r.x = bf16_bits(bf16_val(v.x & 0xffffu) * s) | (bf16_bits(bf16_val(v.x >> 16) * s) << 16);
+  r.y = bf16_bits(bf16_val(v.y & 0xffffu) * s) | (bf16_bits(bf16_val(v.y >> 16) * s) << 16);
+  r.z = bf16_bits(bf16_val(v.z & 0xffffu) * s) | (bf16_bits(bf16_val(v.z >> 16) * s) << 16);
+  r.w = bf16_bits(bf16_val(v.w & 0xffffu) * s) | (bf16_bits(bf16_val(v.w >> 16) * s) << 16);
+  return r;
+}
+
+__device__ __forceinline__ uint2 pack4(const f32x4& v) {
+  uint2 p;
+  p.x = bf16_bits(v[0]) | (bf16_bits(v[1]) << 16);
+  p.y = bf16_bits(v[2]) | (bf16_bits(v[3]) << 16);
+  return p;
+}
+
+__device__ __forceinline__ f32x4 unpack4(const uint2& p) {
+  f32x4 v;
+  v[0] = bf16_val(p.x & 0xffffu);
+  v[1] = bf16_val(p.x >> 16);
+  v[2] = bf16_val(p.y & 0xffffu);
+  v[3] = bf16_val(p.y >> 16);
+  return v;
+}
+
+// Gates of the staged chunk, every wave (lane = token); wave 0 publishes them.
+struct LaneGates {
+  float lq, l, llast, eq, e2, neta, al;
+};
+__device__ __forceinline__ LaneGates lane_gates(float eta, float alpha, int lane, int cv) {
+  LaneGates r;
+  const float et = lane < cv ? eta : 0.f;
+  r.al = lane < cv ? alpha : 1.f;
+  const ChunkGates g = chunk_gates(r.al, lane);
+  r.lq = g.lq;
+  r.l = g.l;
+  r.llast = g.llast;
+  r.eq = fexp2(g.lq);
+  r.e2 = fexp2(g.llast - g.l);
+  r.neta = -et;
+  return r;
+}
+__device__ __forceinline__ void publish_gates(GateSmem& gs, const LaneGates& g, int lane) {
+  gs.lq[lane] = g.lq;
+  gs.li[lane] = g.l;
+  gs.e2[lane] = g.e2;
+  gs.eq[lane] = g.eq;
+  gs.neta[lane] = g.neta;
+  gs.al[lane] = g.al;
+}
+
 // ----------------------------------------------------------------- role A
 template <int D>
 __device__ __forceinline__ void role_a(const BwdArgs& a, SmA<D>& sm, GateSmem& gs, int64_t bh,
                                        int tile) {
-  constexpr int XP = SmA<D>::XP, TP = SmA<D>::TP;
+  constexpr int XP = SmA<D>::XP;
   constexpr int RPT = kC * D / (8 * kNT);
   constexpr int CG = D / 8;
   constexpr int NS = (2 * (D / 16)) / 4;
@@ -122,7 +163,7 @@ __device__ __forceinline__ void role_a(const BwdArgs& a, SmA<D>& sm, GateSmem& g
   uint16_t* dg = static_cast<uint16_t*>(a.dg) + bh * T * D;
   float* pe = static_cast<float*>(a.part_eta) + tile * BHT + bh * T;
 
-  for (int idx = tid; idx < kC * TP; idx += kNT) (&sm.PT[0][0])[idx] = static_cast<__bf16>(0.f);
+  for (int idx = tid; idx < kC * CP; idx += kNT) (&sm.PT[0][0])[idx] = static_cast<__bf16>(0.f);
   for (int idx = tid; idx < kT * XP; idx += kNT) (&sm.L[0][0])[idx] = static_cast<__bf16>(0.f);
   f32x4 lam[NS], dw[NS];
 #pragma unroll
@@ -140,153 +181,114 @@ __device__ __forceinline__ void role_a(const BwdArgs& a, SmA<D>& sm, GateSmem& g
   auto load = [&](int c) {
     const int64_t t0 = static_cast<int64_t>(c) * kC;
     const int cv = static_cast<int>(std::min<int64_t>(kC, T - t0));
-    const uint4 z = make_uint4(0, 0, 0, 0);
 #pragma unroll
-    for (int s = 0; s < RPT; ++s) {
-      const int j = rg * RPT + s;
-      pf.x[s] = (j < cv) ? *reinterpret_cast<const uint4*>(x + (t0 + j) * D + 8 * cg) : z;
-    }
-    pf.dy = (jg < cv) ? *reinterpret_cast<const uint4*>(dy + (t0 + jg) * D + r0 + c8) : z;
-    pf.g = (jg < cv) ? *reinterpret_cast<const uint4*>(g + (t0 + jg) * D + r0 + c8) : z;
-    if (tid < kC) {
-      pf.eta = (tid < cv) ? eta[t0 + tid] : 0.f;
-      pf.alpha = (tid < cv) ? alpha[t0 + tid] : 1.f;
-    }
+    for (int s = 0; s < RPT; ++s) pf.x[s] = load_row16(x + t0 * D + 8 * cg, D, rg * RPT + s, cv);
+    pf.dy = load_row16(dy + t0 * D + r0 + c8, D, jg, cv);
+    pf.g = load_row16(g + t0 * D + r0 + c8, D, jg, cv);
+    const int jt = tid & (kC - 1), jc = jt < cv ? jt : cv - 1;
+    pf.eta = eta[t0 + jc];
+    pf.alpha = alpha[t0 + jc];
   };
 
   load(a.n_chunks - 1);
   for (int c = a.n_chunks - 1; c >= 0; --c) {
     const int64_t t0 = static_cast<int64_t>(c) * kC;
     const int cv = static_cast<int>(std::min<int64_t>(kC, T - t0));
-    // ---- stage the chunk
+    const LaneGates lg = lane_gates(pf.eta, pf.alpha, lane, cv);
+    const float gam = fexp2(lg.llast);
+    if (wave == 0) publish_gates(gs, lg, lane);
 #pragma unroll
-    for (int s = 0; s < RPT; ++s) *reinterpret_cast<uint4*>(&sm.X[rg * RPT + s][8 * cg]) = pf.x[s];
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      uint16_t* dst = reinterpret_cast<uint16_t*>(&sm.Xt[8 * cg + q][rg * RPT]);
-      if constexpr (RPT == 4) {
-        uint2 v;
-        v.x = half_of(pf.x[0], q) | (half_of(pf.x[1], q) << 16);
-        v.y = half_of(pf.x[2], q) | (half_of(pf.x[3], q) << 16);
-        *reinterpret_cast<uint2*>(dst) = v;
-      } else {
-        *reinterpret_cast<uint32_t*>(dst) = half_of(pf.x[0], q) | (half_of(pf.x[1], q) << 16);
-      }
-      reinterpret_cast<uint16_t*>(&sm.Dt[c8 + q][0])[jg] = static_cast<uint16_t>(half_of(pf.dy, q));
+    for (int s = 0; s < RPT; ++s)
+      *reinterpret_cast<uint4*>(&sm.X[rg * RPT + s][8 * cg]) = keep_row(pf.x[s], rg * RPT + s, cv);
+    {
+      const uint4 dv = keep_row(pf.dy, jg, cv);
+      *reinterpret_cast<uint4*>(&sm.Dr[jg][c8]) = dv;
+      *reinterpret_cast<uint4*>(&sm.Drs[jg][c8]) = scale_bf16x8(dv, __shfl(lg.eq, jg, 64));
+      *reinterpret_cast<uint4*>(&sm.Gr[jg][c8]) = keep_row(pf.g, jg, cv);
     }
-    *reinterpret_cast<uint4*>(&sm.Gr[jg][c8]) = pf.g;
-    if (tid < kC) {
-      gs.eta_raw[tid] = pf.eta;
-      gs.alpha_raw[tid] = pf.alpha;
-    }
-    lds_barrier();  // S1
-    if (c > 0) load(c - 1);
-    if (wave == 0) gates_to_smem(gs, lane);
+    lds_barrier();  // B1: chunk tiles and gates visible
+    load(c > 0 ? c - 1 : 0);  // the first chunk is re-read and ignored at the end
 
-    // x_u . x_i for u-block >= i-block
-    f32x4 xx[3];
+    // P^T[i][u] = e(lq_u - l_i) (x_u . x_i) for u > i
 #pragma unroll
     for (int s = 0; s < 3; ++s) {
       const int b = wave + 4 * s;
-      xx[s] = zero4();
       if (b < 10) {
-        const int ub = kBlkI[b], ib = kBlkJ[b];
+        const int ub = tri_i(b), ib = tri_j(b);
+        f32x4 xx = zero4();
 #pragma unroll
         for (int kb = 0; kb < D / 32; ++kb)
-          xx[s] = mfma16x16x32(frag(&sm.X[0][0], XP, ub * 16, kb * 32, lane),
-                               frag(&sm.X[0][0], XP, ib * 16, kb * 32, lane), xx[s]);
-      }
-    }
-    lds_barrier();  // S2: gates visible
-
-#pragma unroll
-    for (int s = 0; s < 3; ++s) {
-      const int b = wave + 4 * s;
-      if (b < 10) {
-        const int ub = kBlkI[b], ib = kBlkJ[b];
+          xx = mfma16x16x32(frag(&sm.X[0][0], XP, ub * 16, kb * 32, lane),
+                            frag(&sm.X[0][0], XP, ib * 16, kb * 32, lane), xx);
         const int i = ib * 16 + l16, u0 = ub * 16 + 4 * g4;
         const float li = gs.li[i];
-        float v[4];
+        const f32x4 lqu = *reinterpret_cast<const f32x4*>(&gs.lq[u0]);
+        f32x4 v;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) v[q] = (i < u0 + q) ? xx[s][q] * exp2f(gs.lq[u0 + q] - li) : 0.f;
-        uint2 pk;
-        pk.x = bf16_bits(v[0]) | (bf16_bits(v[1]) << 16);
-        pk.y = bf16_bits(v[2]) | (bf16_bits(v[3]) << 16);
-        *reinterpret_cast<uint2*>(&sm.PT[i][u0]) = pk;
+        for (int q = 0; q < 4; ++q) {
+          const float e = xx[q] * fexp2(lqu[q] - li);
+          v[q] = (i < u0 + q) ? e : 0.f;
+        }
+        *reinterpret_cast<uint2*>(&sm.PT[i][u0]) = pack4(v);
       }
     }
-    lds_barrier();  // S3: P visible
+    lds_barrier();  // B2: P visible
 
     {
-      const int ib = wave;
+      // u^T[r][i] = e(l_last - l_i) (Lam_out x_i)[r] + sum_{u>i} P_ui dy_u[r]
+      const int w = wave, i = w * 16 + l16;
       f32x4 ain[2] = {zero4(), zero4()}, apd[2] = {zero4(), zero4()};
 #pragma unroll
       for (int kb = 0; kb < D / 32; ++kb) {
-        const bf16x8 xf = frag(&sm.X[0][0], XP, ib * 16, kb * 32, lane);
+        const bf16x8 xf = frag(&sm.X[0][0], XP, w * 16, kb * 32, lane);
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb)
-          ain[nb] = mfma16x16x32(xf, frag(&sm.L[0][0], XP, nb * 16, kb * 32, lane), ain[nb]);
+        for (int rb = 0; rb < 2; ++rb)
+          ain[rb] = mfma16x16x32(frag(&sm.L[0][0], XP, rb * 16, kb * 32, lane), xf, ain[rb]);
       }
-      for (int kb = ib / 2; kb < 2; ++kb) {
-        const bf16x8 pf_ = frag(&sm.PT[0][0], TP, ib * 16, kb * 32, lane);
+      for (int kb = w / 2; kb < 2; ++kb) {
+        const bf16x8 pf_ = frag(&sm.PT[0][0], CP, w * 16, kb * 32, lane);
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb)
-          apd[nb] = mfma16x16x32(pf_, frag(&sm.Dt[0][0], TP, nb * 16, kb * 32, lane), apd[nb]);
+        for (int rb = 0; rb < 2; ++rb)
+          apd[rb] = mfma16x16x32(frag_t(&sm.Dr[0][0], NP, kb * 32, rb * 16, lane), pf_, apd[rb]);
       }
-      float dpart[4] = {0.f, 0.f, 0.f, 0.f};
+      const float e2 = gs.e2[i], ne = gs.neta[i];
+      float dpart = 0.f;
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int i = ib * 16 + 4 * g4 + q, r = nb * 16 + l16;
-          const float u = gs.e2[i] * ain[nb][q] + apd[nb][q];
-          sm.DGs[i][r] = static_cast<__bf16>(gs.neta[i] * u);
-          dpart[q] += static_cast<float>(sm.Gr[i][r]) * u;
-        }
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float s = sum16(dpart[q]);
-        const int i = ib * 16 + 4 * g4 + q;
-        if (l16 == 0 && i < cv) pe[t0 + i] = -s;
+      for (int rb = 0; rb < 2; ++rb) {
+        const f32x4 u = ain[rb] * e2 + apd[rb];
+        *reinterpret_cast<uint2*>(&sm.DGs[i][rb * 16 + 4 * g4]) = pack4(u * ne);
+        const f32x4 gv = unpack4(*reinterpret_cast<const uint2*>(&sm.Gr[i][rb * 16 + 4 * g4]));
+        dpart += gv[0] * u[0] + gv[1] * u[1] + gv[2] * u[2] + gv[3] * u[3];
       }
+      dpart = sum_groups(dpart);
+      if (g4 == 0 && i < cv) pe[t0 + i] = -dpart;
     }
-    lds_barrier();  // S4: dg staged; reads of L done
+    lds_barrier();  // B3: dg staged; reads of L, PT, Dr done
 
-    {
-      const int i = tid >> 2, cc = 8 * (tid & 3);
-      if (i < cv)
-        *reinterpret_cast<uint4*>(dg + (t0 + i) * D + r0 + cc) =
-            *reinterpret_cast<const uint4*>(&sm.DGs[i][cc]);
-    }
-    const float gam = gs.gam;
+    if (jg < cv)
+      *reinterpret_cast<uint4*>(dg + (t0 + jg) * D + r0 + c8) =
+          *reinterpret_cast<const uint4*>(&sm.DGs[jg][c8]);
+    // Lam^T[c][r] = Gamma Lam^T + sum_u x_u[c] e(lq_u) dy_u[r];  dW0^T += sum_u x_u[c] dy_u[r]
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
-      const int b = wave + 4 * s, rb = b / (D / 16), cb = b % (D / 16);
+      const int b = wave + 4 * s, cb = b >> 1, rb = b & 1;
       lam[s] = lam[s] * gam;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        const bf16x8 dr = frag(&sm.Dt[0][0], TP, rb * 16, kb * 32, lane);
-        bf16x8 ds;
-        const int u0 = kb * 32 + 8 * g4;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) ds[e] = static_cast<__bf16>(static_cast<float>(dr[e]) * gs.eq[u0 + e]);
-        const bf16x8 xb = frag(&sm.Xt[0][0], TP, cb * 16, kb * 32, lane);
-        lam[s] = mfma16x16x32(ds, xb, lam[s]);
-        dw[s] = mfma16x16x32(dr, xb, dw[s]);
+        const bf16x8 xa = frag_t(&sm.X[0][0], XP, kb * 32, cb * 16, lane);
+        lam[s] = mfma16x16x32(xa, frag_t(&sm.Drs[0][0], NP, kb * 32, rb * 16, lane), lam[s]);
+        dw[s] = mfma16x16x32(xa, frag_t(&sm.Dr[0][0], NP, kb * 32, rb * 16, lane), dw[s]);
       }
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        sm.L[rb * 16 + 4 * g4 + q][cb * 16 + l16] = static_cast<__bf16>(lam[s][q]);
+      *reinterpret_cast<uint2*>(&sm.L[rb * 16 + l16][cb * 16 + 4 * g4]) = pack4(lam[s]);
     }
-    lds_barrier();  // S5
+    lds_barrier();  // B4
   }
 
   float* pw = static_cast<float*>(a.part_dW0) + bh * D * D;
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
-    const int b = wave + 4 * s, rb = b / (D / 16), cb = b % (D / 16);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) pw[(r0 + rb * 16 + 4 * g4 + q) * D + cb * 16 + l16] = dw[s][q];
+    const int b = wave + 4 * s, cb = b >> 1, rb = b & 1;
+    *reinterpret_cast<f32x4*>(pw + (r0 + rb * 16 + l16) * D + cb * 16 + 4 * g4) = dw[s];
   }
 }
 
@@ -294,11 +296,11 @@ __device__ __forceinline__ void role_a(const BwdArgs& a, SmA<D>& sm, GateSmem& g
 template <int D>
 __device__ __forceinline__ void role_b(const BwdArgs& a, SmB<D>& sm, GateSmem& gs, int64_t bh,
                                        int tile) {
-  constexpr int XP = SmB<D>::XP, TP = SmB<D>::TP;
+  constexpr int XP = SmB<D>::XP;
   constexpr int RPT = kC * D / (8 * kNT);
   constexpr int CG = D / 8;
-  constexpr int SPT = kT * D / (8 * kNT);  // state rows per thread (16-byte units)
-  constexpr int NS = ((D / 16) * 2) / 4;
+  constexpr int SPT = D * kT / (8 * kNT);  // 16-byte state pieces per thread
+  constexpr int NS = (2 * (D / 16)) / 4;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g4 = lane >> 4, l16 = lane & 15;
   const int k0 = tile * kT;
   const int h = static_cast<int>(bh % a.H);
@@ -313,25 +315,21 @@ __device__ __forceinline__ void role_b(const BwdArgs& a, SmB<D>& sm, GateSmem& g
   uint16_t* dx = static_cast<uint16_t*>(a.dx) + bh * T * D;
   float* pa = static_cast<float*>(a.part_alpha) + tile * BHT + bh * T;
 
-  // W0[:, K]^T fragments (constant): stage through Sn once
-  for (int idx = tid; idx < D * 4; idx += kNT) {
-    const int r = idx >> 2, cc = 8 * (idx & 3);
-    const uint4 v = *reinterpret_cast<const uint4*>(W0 + static_cast<int64_t>(r) * D + k0 + cc);
+  // W0[:, K] fragments as the A operand of W0[:,K]^T dy^T (constant): via Sn
 #pragma unroll
-    for (int q = 0; q < 8; ++q)
-      reinterpret_cast<uint16_t*>(&sm.Sn[cc + q][0])[r] = static_cast<uint16_t>(half_of(v, q));
+  for (int s = 0; s < SPT; ++s) {
+    const int idx = tid + kNT * s, r = idx >> 2, cc = 8 * (idx & 3);
+    *reinterpret_cast<uint4*>(&sm.Sn[r][cc]) =
+        *reinterpret_cast<const uint4*>(W0 + static_cast<int64_t>(r) * D + k0 + cc);
   }
-  for (int idx = tid; idx < kC * TP; idx += kNT) {
-    (&sm.Be[0][0])[idx] = static_cast<__bf16>(0.f);
-    (&sm.BeT[0][0])[idx] = static_cast<__bf16>(0.f);
-  }
-  for (int idx = tid; idx < kT * XP; idx += kNT) (&sm.L[0][0])[idx] = static_cast<__bf16>(0.f);
+  for (int idx = tid; idx < kC * CP; idx += kNT) (&sm.BeT[0][0])[idx] = static_cast<__bf16>(0.f);
+  for (int idx = tid; idx < D * NP; idx += kNT) (&sm.L[0][0])[idx] = static_cast<__bf16>(0.f);
   lds_barrier();
   bf16x8 w0f[D / 32][2];
 #pragma unroll
   for (int kb = 0; kb < D / 32; ++kb)
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb) w0f[kb][nb] = frag(&sm.Sn[0][0], XP, nb * 16, kb * 32, lane);
+    for (int cb = 0; cb < 2; ++cb) w0f[kb][cb] = frag_t(&sm.Sn[0][0], NP, kb * 32, cb * 16, lane);
   lds_barrier();
 
   f32x4 lam[NS];
@@ -348,105 +346,88 @@ __device__ __forceinline__ void role_b(const BwdArgs& a, SmB<D>& sm, GateSmem& g
   auto load = [&](int c) {
     const int64_t t0 = static_cast<int64_t>(c) * kC;
     const int cv = static_cast<int>(std::min<int64_t>(kC, T - t0));
-    const uint4 z = make_uint4(0, 0, 0, 0);
 #pragma unroll
     for (int s = 0; s < RPT; ++s) {
-      const int j = rg * RPT + s;
-      pf.dy[s] = (j < cv) ? *reinterpret_cast<const uint4*>(dy + (t0 + j) * D + 8 * cg) : z;
-      pf.g[s] = (j < cv) ? *reinterpret_cast<const uint4*>(g + (t0 + j) * D + 8 * cg) : z;
+      pf.dy[s] = load_row16(dy + t0 * D + 8 * cg, D, rg * RPT + s, cv);
+      pf.g[s] = load_row16(g + t0 * D + 8 * cg, D, rg * RPT + s, cv);
     }
-    pf.x = (jg < cv) ? *reinterpret_cast<const uint4*>(x + (t0 + jg) * D + k0 + c8) : z;
-    const uint16_t* sc = st + (static_cast<int64_t>(c) * D + k0) * D;
+    pf.x = load_row16(x + t0 * D + k0 + c8, D, jg, cv);
+    const uint16_t* sc = st + static_cast<int64_t>(c) * D * D + k0;
 #pragma unroll
     for (int s = 0; s < SPT; ++s) {
       const int idx = tid + kNT * s;
-      pf.sn[s] = *reinterpret_cast<const uint4*>(sc + (idx / CG) * D + 8 * (idx % CG));
+      pf.sn[s] = *reinterpret_cast<const uint4*>(sc + (idx >> 2) * D + 8 * (idx & 3));
     }
-    if (tid < kC) {
-      pf.eta = (tid < cv) ? eta[t0 + tid] : 0.f;
-      pf.alpha = (tid < cv) ? alpha[t0 + tid] : 1.f;
-    }
+    const int jt = tid & (kC - 1), jc = jt < cv ? jt : cv - 1;
+    pf.eta = eta[t0 + jc];
+    pf.alpha = alpha[t0 + jc];
   };
 
   load(a.n_chunks - 1);
   for (int c = a.n_chunks - 1; c >= 0; --c) {
     const int64_t t0 = static_cast<int64_t>(c) * kC;
     const int cv = static_cast<int>(std::min<int64_t>(kC, T - t0));
-    // ---- stage the chunk
+    const LaneGates lg = lane_gates(pf.eta, pf.alpha, lane, cv);
+    const float gam = fexp2(lg.llast);
+    if (wave == 0) publish_gates(gs, lg, lane);
 #pragma unroll
     for (int s = 0; s < RPT; ++s) {
-      *reinterpret_cast<uint4*>(&sm.Dy[rg * RPT + s][8 * cg]) = pf.dy[s];
-      *reinterpret_cast<uint4*>(&sm.G[rg * RPT + s][8 * cg]) = pf.g[s];
+      *reinterpret_cast<uint4*>(&sm.Dy[rg * RPT + s][8 * cg]) = keep_row(pf.dy[s], rg * RPT + s, cv);
+      *reinterpret_cast<uint4*>(&sm.G[rg * RPT + s][8 * cg]) = keep_row(pf.g[s], rg * RPT + s, cv);
     }
-#pragma unroll
-    for (int q = 0; q < 8; ++q)
-      reinterpret_cast<uint16_t*>(&sm.Xt[c8 + q][0])[jg] = static_cast<uint16_t>(half_of(pf.x, q));
+    {
+      const uint4 xv = keep_row(pf.x, jg, cv);
+      *reinterpret_cast<uint4*>(&sm.Xk[jg][c8]) = xv;
+      *reinterpret_cast<uint4*>(&sm.Xks[jg][c8]) = scale_bf16x8(xv, __shfl(lg.eq, jg, 64));
+    }
 #pragma unroll
     for (int s = 0; s < SPT; ++s) {
       const int idx = tid + kNT * s;
-      *reinterpret_cast<uint4*>(&sm.Sn[idx / CG][8 * (idx % CG)]) = pf.sn[s];
+      *reinterpret_cast<uint4*>(&sm.Sn[idx >> 2][8 * (idx & 3)]) = pf.sn[s];
     }
-    if (tid < kC) {
-      gs.eta_raw[tid] = pf.eta;
-      gs.alpha_raw[tid] = pf.alpha;
-    }
-    lds_barrier();  // S1
-    if (c > 0) load(c - 1);
-    if (wave == 0) gates_to_smem(gs, lane);
+    lds_barrier();  // B1: chunk tiles and gates visible
+    load(c > 0 ? c - 1 : 0);  // the first chunk is re-read and ignored at the end
 
-    // dy_i . g_j for i-block >= j-block
-    f32x4 dgx[3];
+    // Be_ij = e(lq_i - l_j)(-eta_j)(dy_i . g_j), j < i, stored as BeT[j][i]
 #pragma unroll
     for (int s = 0; s < 3; ++s) {
       const int b = wave + 4 * s;
-      dgx[s] = zero4();
       if (b < 10) {
-        const int ib = kBlkI[b], jb = kBlkJ[b];
+        const int ib = tri_i(b), jb = tri_j(b);
+        f32x4 d = zero4();
 #pragma unroll
         for (int kb = 0; kb < D / 32; ++kb)
-          dgx[s] = mfma16x16x32(frag(&sm.Dy[0][0], XP, ib * 16, kb * 32, lane),
-                                frag(&sm.G[0][0], XP, jb * 16, kb * 32, lane), dgx[s]);
+          d = mfma16x16x32(frag(&sm.Dy[0][0], XP, ib * 16, kb * 32, lane),
+                           frag(&sm.G[0][0], XP, jb * 16, kb * 32, lane), d);
+        const int j = jb * 16 + l16, i0 = ib * 16 + 4 * g4;
+        const float lj = gs.li[j], nj = gs.neta[j];
+        const f32x4 lqi = *reinterpret_cast<const f32x4*>(&gs.lq[i0]);
+        f32x4 v;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float e = d[q] * fexp2(lqi[q] - lj) * nj;
+          v[q] = (j < i0 + q) ? e : 0.f;
+        }
+        *reinterpret_cast<uint2*>(&sm.BeT[j][i0]) = pack4(v);
       }
     }
-    // <Lam_out, D_in> over this tile's columns
     {
+      // <Lam_out, D_in> over this tile's columns
       float p = 0.f;
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
-        const int b = wave + 4 * s, rb = b >> 1, cb = b & 1;
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-          p += lam[s][q] * static_cast<float>(sm.Sn[cb * 16 + l16][rb * 16 + 4 * g4 + q]);
+        const int b = wave + 4 * s, cb = b & 1, rb = b >> 1;
+        const f32x4 sv = unpack4(*reinterpret_cast<const uint2*>(&sm.Sn[rb * 16 + l16][cb * 16 + 4 * g4]));
+        p += lam[s][0] * sv[0] + lam[s][1] * sv[1] + lam[s][2] * sv[2] + lam[s][3] * sv[3];
       }
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) p += __shfl_xor(p, off, 64);
+      p = sum_groups(sum16(p));
       if (lane == 0) gs.red[wave] = p;
     }
-    lds_barrier();  // S2: gates visible
-
-#pragma unroll
-    for (int s = 0; s < 3; ++s) {
-      const int b = wave + 4 * s;
-      if (b < 10) {
-        const int ib = kBlkI[b], jb = kBlkJ[b];
-        const int j = jb * 16 + l16, i0 = ib * 16 + 4 * g4;
-        const float lj = gs.li[j], nj = gs.neta[j];
-        float v[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          v[q] = (j < i0 + q) ? dgx[s][q] * exp2f(gs.lq[i0 + q] - lj) * nj : 0.f;
-          sm.Be[i0 + q][j] = static_cast<__bf16>(v[q]);
-        }
-        uint2 pk;
-        pk.x = bf16_bits(v[0]) | (bf16_bits(v[1]) << 16);
-        pk.y = bf16_bits(v[2]) | (bf16_bits(v[3]) << 16);
-        *reinterpret_cast<uint2*>(&sm.BeT[j][i0]) = pk;
-      }
-    }
-    lds_barrier();  // S3: Be visible
+    lds_barrier();  // B2: Be visible
 
     {
-      const int w = wave;
+      // dx^T[c][i] for this wave's token block, both column blocks
+      const int w = wave, i = w * 16 + l16;
       f32x4 aws[2] = {zero4(), zero4()}, as_[2] = {zero4(), zero4()}, al[2] = {zero4(), zero4()};
       f32x4 aq[2] = {zero4(), zero4()}, ak[2] = {zero4(), zero4()};
 #pragma unroll
@@ -454,110 +435,90 @@ __device__ __forceinline__ void role_b(const BwdArgs& a, SmB<D>& sm, GateSmem& g
         const bf16x8 df = frag(&sm.Dy[0][0], XP, w * 16, kb * 32, lane);
         const bf16x8 gf = frag(&sm.G[0][0], XP, w * 16, kb * 32, lane);
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb) {
-          aws[nb] = mfma16x16x32(df, w0f[kb][nb], aws[nb]);
-          as_[nb] = mfma16x16x32(df, frag(&sm.Sn[0][0], XP, nb * 16, kb * 32, lane), as_[nb]);
-          al[nb] = mfma16x16x32(gf, frag(&sm.L[0][0], XP, nb * 16, kb * 32, lane), al[nb]);
+        for (int cb = 0; cb < 2; ++cb) {
+          aws[cb] = mfma16x16x32(w0f[kb][cb], df, aws[cb]);
+          as_[cb] = mfma16x16x32(frag_t(&sm.Sn[0][0], NP, kb * 32, cb * 16, lane), df, as_[cb]);
+          al[cb] = mfma16x16x32(frag_t(&sm.L[0][0], NP, kb * 32, cb * 16, lane), gf, al[cb]);
         }
       }
       for (int kb = 0; kb < (w + 2) / 2; ++kb) {
-        const bf16x8 bf = frag(&sm.Be[0][0], TP, w * 16, kb * 32, lane);
+        const bf16x8 bf = frag_t(&sm.BeT[0][0], CP, kb * 32, w * 16, lane);
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb)
-          aq[nb] = mfma16x16x32(bf, frag(&sm.Xt[0][0], TP, nb * 16, kb * 32, lane), aq[nb]);
+        for (int cb = 0; cb < 2; ++cb)
+          aq[cb] = mfma16x16x32(frag_t(&sm.Xk[0][0], NP, kb * 32, cb * 16, lane), bf, aq[cb]);
       }
       for (int kb = w / 2; kb < 2; ++kb) {
-        const bf16x8 bt = frag(&sm.BeT[0][0], TP, w * 16, kb * 32, lane);
+        const bf16x8 bt = frag(&sm.BeT[0][0], CP, w * 16, kb * 32, lane);
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb)
-          ak[nb] = mfma16x16x32(bt, frag(&sm.Xt[0][0], TP, nb * 16, kb * 32, lane), ak[nb]);
+        for (int cb = 0; cb < 2; ++cb)
+          ak[cb] = mfma16x16x32(frag_t(&sm.Xk[0][0], NP, kb * 32, cb * 16, lane), bt, ak[cb]);
       }
-      float pp[4] = {0.f, 0.f, 0.f, 0.f}, rr[4] = {0.f, 0.f, 0.f, 0.f};
-      float qq[4] = {0.f, 0.f, 0.f, 0.f}, kk[4] = {0.f, 0.f, 0.f, 0.f};
+      const float eqi = gs.eq[i], fl = gs.neta[i] * gs.e2[i];
+      float pp = 0.f, rr = 0.f, qq = 0.f, kk = 0.f;
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
-        const int cc = nb * 16 + l16;
-        const uint2 xr = *reinterpret_cast<const uint2*>(&sm.Xt[cc][w * 16 + 4 * g4]);
-        const float xv[4] = {bf16_val(xr.x & 0xffffu), bf16_val(xr.x >> 16),
-                             bf16_val(xr.y & 0xffffu), bf16_val(xr.y >> 16)};
+      for (int cb = 0; cb < 2; ++cb) {
+        const f32x4 v = aws[cb] + as_[cb] * eqi + aq[cb] + ak[cb] + al[cb] * fl;
+        if (i < cv)
+          *reinterpret_cast<uint2*>(dx + (t0 + i) * D + k0 + cb * 16 + 4 * g4) = pack4(v);
+        const f32x4 xv = unpack4(*reinterpret_cast<const uint2*>(&sm.Xk[i][cb * 16 + 4 * g4]));
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const int i = w * 16 + 4 * g4 + q;
-          const float v = aws[nb][q] + gs.eq[i] * as_[nb][q] + aq[nb][q] + ak[nb][q] +
-                          gs.neta[i] * gs.e2[i] * al[nb][q];
-          if (i < cv) dx[(t0 + i) * D + k0 + cc] = static_cast<uint16_t>(bf16_bits(v));
-          pp[q] += xv[q] * al[nb][q];
-          rr[q] += xv[q] * as_[nb][q];
-          qq[q] += xv[q] * aq[nb][q];
-          kk[q] += xv[q] * ak[nb][q];
+          pp += xv[q] * al[cb][q];
+          rr += xv[q] * as_[cb][q];
+          qq += xv[q] * aq[cb][q];
+          kk += xv[q] * ak[cb][q];
         }
       }
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float p = sum16(pp[q]), r = sum16(rr[q]), qv = sum16(qq[q]), kv = sum16(kk[q]);
-        if (l16 == 0) {
-          const int i = w * 16 + 4 * g4 + q;
-          gs.sp[i] = p;
-          gs.sr[i] = r;
-          gs.sq[i] = qv;
-          gs.sk[i] = kv;
-        }
+      pp = sum_groups(pp);
+      rr = sum_groups(rr);
+      qq = sum_groups(qq);
+      kk = sum_groups(kk);
+      if (g4 == 0) {
+        gs.sp[i] = pp;
+        gs.sr[i] = rr;
+        gs.sq[i] = qq;
+        gs.sk[i] = kk;
       }
     }
-    lds_barrier();  // S4: per-token dots visible; reads of L, Sn, Xt-for-dx done
+    lds_barrier();  // B3: per-token dots visible; reads of L, Sn, BeT done
 
     {
-      // dalpha partial, tokens of this wave's block; lane = (token, quarter of the chunk)
+      // dalpha partial of this wave's tokens; lane = (token, quarter of the chunk)
       const int i = wave * 16 + l16, qd = g4;
       const float lqi = gs.lq[i], lii = gs.li[i];
       float s2 = 0.f, s3 = 0.f, s4 = 0.f;
 #pragma unroll 4
       for (int e = 0; e < 16; ++e) {
         const int j = qd * 16 + e;
-        if (j < i) s2 += exp2f(lqi - gs.li[j]) * gs.neta[j] * gs.sp[j];
-        if (j > i) {
-          s3 += exp2f(gs.lq[j] - lii) * gs.sr[j];
-          s4 += gs.sq[j];
-        }
-        if (j >= i) s4 -= gs.sk[j];
+        const float e2 = fexp2(lqi - gs.li[j]) * gs.neta[j] * gs.sp[j];
+        const float e3 = fexp2(gs.lq[j] - lii) * gs.sr[j];
+        s2 += (j < i) ? e2 : 0.f;
+        s3 += (j > i) ? e3 : 0.f;
+        s4 += (j > i) ? gs.sq[j] : 0.f;
+        s4 -= (j >= i) ? gs.sk[j] : 0.f;
       }
-      s2 += __shfl_xor(s2, 16, 64);
-      s2 += __shfl_xor(s2, 32, 64);
-      s3 += __shfl_xor(s3, 16, 64);
-      s3 += __shfl_xor(s3, 32, 64);
-      s4 += __shfl_xor(s4, 16, 64);
-      s4 += __shfl_xor(s4, 32, 64);
+      s2 = sum_groups(s2);
+      s3 = sum_groups(s3);
+      s4 = sum_groups(s4);
       if (qd == 0 && i < cv) {
         const float c0 = gs.red[0] + gs.red[1] + gs.red[2] + gs.red[3];
-        const float ll = gs.llast;
-        const float t1 = exp2f(ll - lii + lqi) * c0;
-        const float t2 = exp2f(ll - lii) * s2;
-        const float t3 = exp2f(lqi) * s3;
-        const float t4 = s4 / gs.al[i];
-        pa[t0 + i] = t1 + t2 + t3 + t4;
+        const float ll = lg.llast;
+        pa[t0 + i] = fexp2(ll - lii + lqi) * c0 + fexp2(ll - lii) * s2 + fexp2(lqi) * s3 +
+                     s4 / gs.al[i];
       }
     }
-    // adjoint columns: Lam[:, K] = Gamma Lam + sum_u e(lq_u) dy_u x_u[K]^T
-    const float gam = gs.gam;
+    // Lam^T[c][r] = Gamma Lam^T + sum_u e(lq_u) x_u[c] dy_u[r]   (c in K)
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
-      const int b = wave + 4 * s, rb = b >> 1, cb = b & 1;
+      const int b = wave + 4 * s, cb = b & 1, rb = b >> 1;
       lam[s] = lam[s] * gam;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        bf16x8 av;
-        const int u0 = kb * 32 + 8 * g4;
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          av[e] = static_cast<__bf16>(static_cast<float>(sm.Dy[u0 + e][rb * 16 + l16]) * gs.eq[u0 + e]);
-        lam[s] = mfma16x16x32(av, frag(&sm.Xt[0][0], TP, cb * 16, kb * 32, lane), lam[s]);
-      }
-      uint2 pk;
-      pk.x = bf16_bits(lam[s][0]) | (bf16_bits(lam[s][1]) << 16);
-      pk.y = bf16_bits(lam[s][2]) | (bf16_bits(lam[s][3]) << 16);
-      *reinterpret_cast<uint2*>(&sm.L[cb * 16 + l16][rb * 16 + 4 * g4]) = pk;
+      for (int kb = 0; kb < 2; ++kb)
+        lam[s] = mfma16x16x32(frag_t(&sm.Xks[0][0], NP, kb * 32, cb * 16, lane),
+                              frag_t(&sm.Dy[0][0], XP, kb * 32, rb * 16, lane), lam[s]);
+      *reinterpret_cast<uint2*>(&sm.L[rb * 16 + l16][cb * 16 + 4 * g4]) = pack4(lam[s]);
     }
-    lds_barrier();  // S5
+    lds_barrier();  // B4
   }
 }
 

@@ -4,8 +4,10 @@
 //   A (16 x 32):  lane l supplies A[l % 16][8*(l/16) + q],  q = 0..7
 //   B (32 x 16):  lane l supplies B[8*(l/16) + q][l % 16],  q = 0..7
 //   D (16 x 16):  lane l holds    D[4*(l/16) + q][l % 16],  q = 0..3
-// Fragments are read from LDS tiles stored "K-contiguous" (the 8 values a lane
-// needs are adjacent), so each operand is a single 16-byte LDS read.
+// Fragments are read either from tiles stored "K-contiguous" (the 8 values a
+// lane needs are adjacent: one 16-byte LDS read, frag) or, for products that
+// contract over the rows of a row-major tile, with two transposing 8-byte
+// reads (frag_t).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -32,6 +34,25 @@ __device__ __forceinline__ bf16x8 frag(const __bf16* base, int ld, int row0, int
   return *reinterpret_cast<const bf16x8*>(base + (row0 + (lane & 15)) * ld + k0 + 8 * (lane >> 4));
 }
 
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+
+// Fragment whose K dimension runs down the rows of a row-major LDS tile T
+// (row stride `ld` elements): lane l receives T[k0 + 8*(l/16) + q][c0 + l%16],
+// q = 0..7 -- the A operand of a product contracting over T's rows (m = column
+// of T) or, identically, the B operand (n = column of T).  Uses the gfx950
+// transposing LDS read: each 16-lane group reads a 4 x 16 sub-tile (every lane
+// 8 bytes of one row) and lane n receives column n.
+__device__ __forceinline__ bf16x8 frag_t(const __bf16* base, int ld, int k0, int c0, int lane) {
+  const int g = lane >> 4, s = lane & 15;
+  const __bf16* p0 = base + (k0 + 8 * g + (s >> 2)) * ld + c0 + 4 * (s & 3);
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0));
+  const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0 + 4 * ld));
+  const s16x8 c = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, c);
+}
+
 __device__ __forceinline__ uint32_t bf16_bits(float f) {
   __bf16 h = static_cast<__bf16>(f);
   return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, h));
@@ -39,6 +60,33 @@ __device__ __forceinline__ uint32_t bf16_bits(float f) {
 
 __device__ __forceinline__ float bf16_val(uint16_t b) {
   return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// Hardware base-2 exponential / logarithm (v_exp_f32 / v_log_f32).  Decay
+// factors are always <= 1; results below the normal range flush to zero.
+__device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float flog2(float x) { return __builtin_amdgcn_logf(x); }
+
+// Causal lower-triangle block b (0..9) of the 4x4 grid of 16x16 blocks of a
+// 64x64 score matrix, row-major over the triangle: (0,0),(1,0),(1,1),(2,0)...
+// Computed from packed nibbles so that no memory load is involved.
+__device__ __forceinline__ int tri_i(int b) {
+  return static_cast<int>((0x3333222110ull >> (4 * b)) & 0xfull);
+}
+__device__ __forceinline__ int tri_j(int b) {
+  return static_cast<int>((0x3210210100ull >> (4 * b)) & 0xfull);
+}
+
+// 16-byte load of row `j` of a token-major tile with the row clamped to the
+// valid range [0, cv): the load is unconditional (rows j >= cv are zeroed
+// later, when the tile is staged, so that the prefetch never waits here).
+__device__ __forceinline__ uint4 load_row16(const uint16_t* base, int64_t row_stride, int j, int cv) {
+  const int jj = j < cv ? j : cv - 1;
+  return *reinterpret_cast<const uint4*>(base + static_cast<int64_t>(jj) * row_stride);
+}
+
+__device__ __forceinline__ uint4 keep_row(const uint4& v, int j, int cv) {
+  return j < cv ? v : make_uint4(0, 0, 0, 0);
 }
 
 // LDS barrier that does not wait for outstanding global loads, so a prefetch
@@ -60,7 +108,7 @@ struct ChunkGates {
   float l, lq, llast;
 };
 __device__ __forceinline__ ChunkGates chunk_gates(float alpha, int lane) {
-  float l = log2f(alpha);
+  float l = flog2(alpha);
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
     const float v = __shfl_up(l, off, 64);
