@@ -23,6 +23,8 @@ COMMON = [
     "-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC",
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # keep MFMA accumulators in ordinary VGPRs (no AGPR round trips)
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall", "-Wno-unused-function",
 ]
 

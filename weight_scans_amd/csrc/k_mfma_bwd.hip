@@ -44,19 +44,18 @@ constexpr int kNT = 256;  // threads (4 waves)
 constexpr int NP = kT + 8, CP = kC + 8;
 
 template <int D>
-struct SmA {
+struct alignas(16) SmA {
   static constexpr int XP = D + 8;
   __bf16 X[kC][XP];    // x                          [token][feature]
   __bf16 Dr[kC][NP];   // dy of the row tile         [token][row]
   __bf16 Drs[kC][NP];  // e(lq_u) dy of the row tile [token][row]
   __bf16 Gr[kC][NP];   // g of the row tile          [token][row]
   __bf16 PT[kC][CP];   // PT[i][u] = P_ui (u > i)
-  __bf16 L[kT][XP];    // Lam_out[R, :] (bf16)       [row][col]
-  __bf16 DGs[kC][NP];  // dg staging                 [token][row]
+  __bf16 L[2][kT][XP]; // Lam_out[R, :] (bf16)       [row][col], double-buffered
 };
 
 template <int D>
-struct SmB {
+struct alignas(16) SmB {
   static constexpr int XP = D + 8;
   __bf16 Dy[kC][XP];   // dy                         [token][feature]
   __bf16 G[kC][XP];    // g                          [token][feature]
@@ -68,15 +67,16 @@ struct SmB {
 };
 
 template <int D>
-union BwdSmem {
+union alignas(16) BwdSmem {
   SmA<D> a;
   SmB<D> b;
 };
 
-struct GateSmem {
+struct alignas(16) GateSmem {
   float lq[kC], li[kC], e2[kC], eq[kC], neta[kC], al[kC];
   float sp[kC], sr[kC], sq[kC], sk[kC];
   float red[4];
+  float gam, llast, pad_[2];
 };
 
 __device__ __forceinline__ float sum16(float v) {
@@ -95,17 +95,17 @@ __device__ __forceinline__ float sum_groups(float v) {  // over the 4 lane group
 
 __device__ __forceinline__ uint4 scale_bf16x8(const uint4& v, float s) {
   uint4 r;
-  r.x = bf16_bits(bf16_val(v.x & 0xffffu) * s) | (bf16_bits(bf16_val(v.x >> 16) * s) << 16);
-  r.y = bf16_bits(bf16_val(v.y & 0xffffu) * s) | (bf16_bits(bf16_val(v.y >> 16) * s) << 16);
-  r.z = bf16_bits(bf16_val(v.z & 0xffffu) * s) | (bf16_bits(bf16_val(v.z >> 16) * s) << 16);
-  r.w = bf16_bits(bf16_val(v.w & 0xffffu) * s) | (bf16_bits(bf16_val(v.w >> 16) * s) << 16);
+  r.x = pack2(bf16_val(v.x & 0xffffu) * s, bf16_val(v.x >> 16) * s);
+  r.y = pack2(bf16_val(v.y & 0xffffu) * s, bf16_val(v.y >> 16) * s);
+  r.z = pack2(bf16_val(v.z & 0xffffu) * s, bf16_val(v.z >> 16) * s);
+  r.w = pack2(bf16_val(v.w & 0xffffu) * s, bf16_val(v.w >> 16) * s);
   return r;
 }
 
 __device__ __forceinline__ uint2 pack4(const f32x4& v) {
   uint2 p;
-  p.x = bf16_bits(v[0]) | (bf16_bits(v[1]) << 16);
-  p.y = bf16_bits(v[2]) | (bf16_bits(v[3]) << 16);
+  p.x = pack2(v[0], v[1]);
+  p.y = pack2(v[2], v[3]);
   return p;
 }
 
@@ -142,6 +142,10 @@ __device__ __forceinline__ void publish_gates(GateSmem& gs, const LaneGates& g, 
   gs.eq[lane] = g.eq;
   gs.neta[lane] = g.neta;
   gs.al[lane] = g.al;
+  if (lane == 0) {
+    gs.gam = fexp2(g.llast);
+    gs.llast = g.llast;
+  }
 }
 
 // ----------------------------------------------------------------- role A
@@ -164,7 +168,7 @@ __device__ __forceinline__ void role_a(const BwdArgs& a, SmA<D>& sm, GateSmem& g
   float* pe = static_cast<float*>(a.part_eta) + tile * BHT + bh * T;
 
   for (int idx = tid; idx < kC * CP; idx += kNT) (&sm.PT[0][0])[idx] = static_cast<__bf16>(0.f);
-  for (int idx = tid; idx < kT * XP; idx += kNT) (&sm.L[0][0])[idx] = static_cast<__bf16>(0.f);
+  for (int idx = tid; idx < 2 * kT * XP; idx += kNT) (&sm.L[0][0][0])[idx] = static_cast<__bf16>(0.f);
   f32x4 lam[NS], dw[NS];
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
@@ -190,24 +194,30 @@ __device__ __forceinline__ void role_a(const BwdArgs& a, SmA<D>& sm, GateSmem& g
     pf.alpha = alpha[t0 + jc];
   };
 
-  load(a.n_chunks - 1);
-  for (int c = a.n_chunks - 1; c >= 0; --c) {
-    const int64_t t0 = static_cast<int64_t>(c) * kC;
-    const int cv = static_cast<int>(std::min<int64_t>(kC, T - t0));
+  // Stage the loaded chunk (cv valid tokens) and publish its gates.
+  const auto stage = [&](int cv) {
     const LaneGates lg = lane_gates(pf.eta, pf.alpha, lane, cv);
-    const float gam = fexp2(lg.llast);
     if (wave == 0) publish_gates(gs, lg, lane);
 #pragma unroll
     for (int s = 0; s < RPT; ++s)
       *reinterpret_cast<uint4*>(&sm.X[rg * RPT + s][8 * cg]) = keep_row(pf.x[s], rg * RPT + s, cv);
-    {
-      const uint4 dv = keep_row(pf.dy, jg, cv);
-      *reinterpret_cast<uint4*>(&sm.Dr[jg][c8]) = dv;
-      *reinterpret_cast<uint4*>(&sm.Drs[jg][c8]) = scale_bf16x8(dv, __shfl(lg.eq, jg, 64));
-      *reinterpret_cast<uint4*>(&sm.Gr[jg][c8]) = keep_row(pf.g, jg, cv);
-    }
-    lds_barrier();  // B1: chunk tiles and gates visible
-    load(c > 0 ? c - 1 : 0);  // the first chunk is re-read and ignored at the end
+    const uint4 dv = keep_row(pf.dy, jg, cv);
+    *reinterpret_cast<uint4*>(&sm.Dr[jg][c8]) = dv;
+    *reinterpret_cast<uint4*>(&sm.Drs[jg][c8]) = scale_bf16x8(dv, __shfl(lg.eq, jg, 64));
+    *reinterpret_cast<uint4*>(&sm.Gr[jg][c8]) = keep_row(pf.g, jg, cv);
+  };
+  const auto cv_of = [&](int c) {
+    return static_cast<int>(std::min<int64_t>(kC, T - static_cast<int64_t>(c) * kC));
+  };
+
+  load(a.n_chunks - 1);
+  stage(cv_of(a.n_chunks - 1));
+  lds_barrier();
+  for (int c = a.n_chunks - 1; c >= 0; --c) {
+    const int64_t t0 = static_cast<int64_t>(c) * kC;
+    const int cv = cv_of(c);
+    // loads of the previous chunk: issued now, staged at the end of this iteration
+    if (c > 0) load(c - 1);
 
     // P^T[i][u] = e(lq_u - l_i) (x_u . x_i) for u > i
 #pragma unroll
@@ -232,10 +242,11 @@ __device__ __forceinline__ void role_a(const BwdArgs& a, SmA<D>& sm, GateSmem& g
         *reinterpret_cast<uint2*>(&sm.PT[i][u0]) = pack4(v);
       }
     }
-    lds_barrier();  // B2: P visible
+    lds_barrier();  // P visible
 
     {
-      // u^T[r][i] = e(l_last - l_i) (Lam_out x_i)[r] + sum_{u>i} P_ui dy_u[r]
+      // u^T[r][i] = e(l_last - l_i) (Lam_out x_i)[r] + sum_{u>i} P_ui dy_u[r];
+      // dg stored straight from the accumulators (4 rows of one token per lane)
       const int w = wave, i = w * 16 + l16;
       f32x4 ain[2] = {zero4(), zero4()}, apd[2] = {zero4(), zero4()};
 #pragma unroll
@@ -243,7 +254,7 @@ __device__ __forceinline__ void role_a(const BwdArgs& a, SmA<D>& sm, GateSmem& g
         const bf16x8 xf = frag(&sm.X[0][0], XP, w * 16, kb * 32, lane);
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb)
-          ain[rb] = mfma16x16x32(frag(&sm.L[0][0], XP, rb * 16, kb * 32, lane), xf, ain[rb]);
+          ain[rb] = mfma16x16x32(frag(&sm.L[c & 1][0][0], XP, rb * 16, kb * 32, lane), xf, ain[rb]);
       }
       for (int kb = w / 2; kb < 2; ++kb) {
         const bf16x8 pf_ = frag(&sm.PT[0][0], CP, w * 16, kb * 32, lane);
@@ -256,19 +267,17 @@ __device__ __forceinline__ void role_a(const BwdArgs& a, SmA<D>& sm, GateSmem& g
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb) {
         const f32x4 u = ain[rb] * e2 + apd[rb];
-        *reinterpret_cast<uint2*>(&sm.DGs[i][rb * 16 + 4 * g4]) = pack4(u * ne);
+        if (i < cv) *reinterpret_cast<uint2*>(dg + (t0 + i) * D + r0 + rb * 16 + 4 * g4) = pack4(u * ne);
         const f32x4 gv = unpack4(*reinterpret_cast<const uint2*>(&sm.Gr[i][rb * 16 + 4 * g4]));
         dpart += gv[0] * u[0] + gv[1] * u[1] + gv[2] * u[2] + gv[3] * u[3];
       }
       dpart = sum_groups(dpart);
       if (g4 == 0 && i < cv) pe[t0 + i] = -dpart;
     }
-    lds_barrier();  // B3: dg staged; reads of L, PT, Dr done
 
-    if (jg < cv)
-      *reinterpret_cast<uint4*>(dg + (t0 + jg) * D + r0 + c8) =
-          *reinterpret_cast<const uint4*>(&sm.DGs[jg][c8]);
     // Lam^T[c][r] = Gamma Lam^T + sum_u x_u[c] e(lq_u) dy_u[r];  dW0^T += sum_u x_u[c] dy_u[r]
+    // (written to the other Lam buffer: the current one may still be read)
+    const float gam = gs.gam;
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
       const int b = wave + 4 * s, cb = b >> 1, rb = b & 1;
@@ -279,9 +288,13 @@ __device__ __forceinline__ void role_a(const BwdArgs& a, SmA<D>& sm, GateSmem& g
         lam[s] = mfma16x16x32(xa, frag_t(&sm.Drs[0][0], NP, kb * 32, rb * 16, lane), lam[s]);
         dw[s] = mfma16x16x32(xa, frag_t(&sm.Dr[0][0], NP, kb * 32, rb * 16, lane), dw[s]);
       }
-      *reinterpret_cast<uint2*>(&sm.L[rb * 16 + l16][cb * 16 + 4 * g4]) = pack4(lam[s]);
+      *reinterpret_cast<uint2*>(&sm.L[(c & 1) ^ 1][rb * 16 + l16][cb * 16 + 4 * g4]) = pack4(lam[s]);
     }
-    lds_barrier();  // B4
+    lds_barrier();  // every read of this chunk's tiles is done
+    if (c > 0) {
+      stage(cv_of(c - 1));
+      lds_barrier();
+    }
   }
 
   float* pw = static_cast<float*>(a.part_dW0) + bh * D * D;
@@ -363,30 +376,38 @@ __device__ __forceinline__ void role_b(const BwdArgs& a, SmB<D>& sm, GateSmem& g
     pf.alpha = alpha[t0 + jc];
   };
 
-  load(a.n_chunks - 1);
-  for (int c = a.n_chunks - 1; c >= 0; --c) {
-    const int64_t t0 = static_cast<int64_t>(c) * kC;
-    const int cv = static_cast<int>(std::min<int64_t>(kC, T - t0));
+  // Stage the loaded chunk and publish its gates; returns the lane gates
+  // (lane = token) of the staged chunk.
+  const auto stage = [&](int cv) {
     const LaneGates lg = lane_gates(pf.eta, pf.alpha, lane, cv);
-    const float gam = fexp2(lg.llast);
     if (wave == 0) publish_gates(gs, lg, lane);
 #pragma unroll
     for (int s = 0; s < RPT; ++s) {
       *reinterpret_cast<uint4*>(&sm.Dy[rg * RPT + s][8 * cg]) = keep_row(pf.dy[s], rg * RPT + s, cv);
       *reinterpret_cast<uint4*>(&sm.G[rg * RPT + s][8 * cg]) = keep_row(pf.g[s], rg * RPT + s, cv);
     }
-    {
-      const uint4 xv = keep_row(pf.x, jg, cv);
-      *reinterpret_cast<uint4*>(&sm.Xk[jg][c8]) = xv;
-      *reinterpret_cast<uint4*>(&sm.Xks[jg][c8]) = scale_bf16x8(xv, __shfl(lg.eq, jg, 64));
-    }
+    const uint4 xv = keep_row(pf.x, jg, cv);
+    *reinterpret_cast<uint4*>(&sm.Xk[jg][c8]) = xv;
+    *reinterpret_cast<uint4*>(&sm.Xks[jg][c8]) = scale_bf16x8(xv, __shfl(lg.eq, jg, 64));
 #pragma unroll
     for (int s = 0; s < SPT; ++s) {
       const int idx = tid + kNT * s;
       *reinterpret_cast<uint4*>(&sm.Sn[idx >> 2][8 * (idx & 3)]) = pf.sn[s];
     }
-    lds_barrier();  // B1: chunk tiles and gates visible
-    load(c > 0 ? c - 1 : 0);  // the first chunk is re-read and ignored at the end
+    return lg;
+  };
+  const auto cv_of = [&](int c) {
+    return static_cast<int>(std::min<int64_t>(kC, T - static_cast<int64_t>(c) * kC));
+  };
+
+  load(a.n_chunks - 1);
+  LaneGates lg = stage(cv_of(a.n_chunks - 1));
+  lds_barrier();
+  for (int c = a.n_chunks - 1; c >= 0; --c) {
+    const int64_t t0 = static_cast<int64_t>(c) * kC;
+    const int cv = cv_of(c);
+    // loads of the previous chunk: issued now, staged at the end of this iteration
+    if (c > 0) load(c - 1);
 
     // Be_ij = e(lq_i - l_j)(-eta_j)(dy_i . g_j), j < i, stored as BeT[j][i]
 #pragma unroll
@@ -423,10 +444,11 @@ __device__ __forceinline__ void role_b(const BwdArgs& a, SmB<D>& sm, GateSmem& g
       p = sum_groups(sum16(p));
       if (lane == 0) gs.red[wave] = p;
     }
-    lds_barrier();  // B2: Be visible
+    lds_barrier();  // Be visible
 
     {
-      // dx^T[c][i] for this wave's token block, both column blocks
+      // dx^T[c][i] for this wave's token block, both column blocks; stored
+      // straight from the accumulators (4 columns of one token per lane)
       const int w = wave, i = w * 16 + l16;
       f32x4 aws[2] = {zero4(), zero4()}, as_[2] = {zero4(), zero4()}, al[2] = {zero4(), zero4()};
       f32x4 aq[2] = {zero4(), zero4()}, ak[2] = {zero4(), zero4()};
@@ -480,34 +502,30 @@ __device__ __forceinline__ void role_b(const BwdArgs& a, SmB<D>& sm, GateSmem& g
         gs.sk[i] = kk;
       }
     }
-    lds_barrier();  // B3: per-token dots visible; reads of L, Sn, BeT done
+    lds_barrier();  // per-token dots visible; reads of L, Sn, BeT done
 
-    {
-      // dalpha partial of this wave's tokens; lane = (token, quarter of the chunk)
-      const int i = wave * 16 + l16, qd = g4;
-      const float lqi = gs.lq[i], lii = gs.li[i];
-      float s2 = 0.f, s3 = 0.f, s4 = 0.f;
-#pragma unroll 4
-      for (int e = 0; e < 16; ++e) {
-        const int j = qd * 16 + e;
-        const float e2 = fexp2(lqi - gs.li[j]) * gs.neta[j] * gs.sp[j];
-        const float e3 = fexp2(gs.lq[j] - lii) * gs.sr[j];
-        s2 += (j < i) ? e2 : 0.f;
-        s3 += (j > i) ? e3 : 0.f;
-        s4 += (j > i) ? gs.sq[j] : 0.f;
-        s4 -= (j >= i) ? gs.sk[j] : 0.f;
-      }
-      s2 = sum_groups(s2);
-      s3 = sum_groups(s3);
-      s4 = sum_groups(s4);
-      if (qd == 0 && i < cv) {
-        const float c0 = gs.red[0] + gs.red[1] + gs.red[2] + gs.red[3];
-        const float ll = lg.llast;
+    if (wave == 0) {
+      // dalpha partial, lane = token i.  With the decay Mf_ij = prod_{j<r<i} alpha_r:
+      //   s2_i = sum_{j<i} Mf_ij (-eta_j) p_j      forward affine scan
+      //   s3_i = sum_{u>i} Mf_ui r_u               same scan over reversed lanes
+      //   s4_i = sum_{u>i} q_u - sum_{j>=i} k_j    suffix sums
+      const int i = lane;
+      float a2 = lg.al, b2 = lg.neta * gs.sp[i];
+      wave_scan_affine(a2, b2);
+      const float s2 = wave_shift_up(b2, 0.f);
+      float a3 = wave_reverse(lg.al, lane), b3 = wave_reverse(gs.sr[i], lane);
+      wave_scan_affine(a3, b3);
+      const float s3 = wave_reverse(wave_shift_up(b3, 0.f), lane);
+      const float qsuf = wave_reverse(wave_shift_up(wave_scan_add(wave_reverse(gs.sq[i], lane)), 0.f), lane);
+      const float ksuf = wave_reverse(wave_scan_add(wave_reverse(gs.sk[i], lane)), lane);
+      const float c0 = gs.red[0] + gs.red[1] + gs.red[2] + gs.red[3];
+      const float ll = lg.llast, lii = lg.l, lqi = lg.lq;
+      if (i < cv)
         pa[t0 + i] = fexp2(ll - lii + lqi) * c0 + fexp2(ll - lii) * s2 + fexp2(lqi) * s3 +
-                     s4 / gs.al[i];
-      }
+                     (qsuf - ksuf) / lg.al;
     }
     // Lam^T[c][r] = Gamma Lam^T + sum_u e(lq_u) x_u[c] dy_u[r]   (c in K)
+    const float gam = gs.gam;
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
       const int b = wave + 4 * s, cb = b & 1, rb = b >> 1;
@@ -518,7 +536,11 @@ __device__ __forceinline__ void role_b(const BwdArgs& a, SmB<D>& sm, GateSmem& g
                               frag_t(&sm.Dy[0][0], XP, kb * 32, rb * 16, lane), lam[s]);
       *reinterpret_cast<uint2*>(&sm.L[rb * 16 + l16][cb * 16 + 4 * g4]) = pack4(lam[s]);
     }
-    lds_barrier();  // B4
+    lds_barrier();  // every read of this chunk's tiles is done
+    if (c > 0) {
+      lg = stage(cv_of(c - 1));
+      lds_barrier();
+    }
   }
 }
 

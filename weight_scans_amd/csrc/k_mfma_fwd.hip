@@ -35,19 +35,27 @@ constexpr int kC = 64;    // tokens per chunk
 constexpr int kTN = 32;   // rows of the adaptation per work-group
 constexpr int kNT = 256;  // threads (4 waves)
 
+// Chunk inputs (double-buffered: chunk c + 1 is staged while chunk c is used).
 template <int D>
-struct FwdSmem {
+struct alignas(16) FwdChunk {
   static constexpr int XP = D + 8;    // row stride of [token][D] tiles (elements)
   static constexpr int NP = kTN + 8;  // row stride of [token][kTN] tiles
-  static constexpr int CP = kC + 8;   // row stride of [token][token] tiles
   __bf16 X[kC][XP];                   // x of the chunk
   __bf16 G[kC][NP];                   // g of the row tile
   __bf16 Gs[kC][NP];                  // e(l_last - l_j)(-eta_j) g_j
-  __bf16 AT[kC][CP];                  // AT[j][i] = A_ij
-  __bf16 S[kTN][XP];                  // D_in of the tile, bf16 [row][col]
-  __bf16 W[kTN][XP];                  // W0 of the tile [row][col]
-  __bf16 Y[kC][NP];                   // y staging [token][row]
   float lq[kC], li[kC], eq[kC], neta[kC];
+  float gam;
+};
+
+template <int D>
+struct alignas(16) FwdSmem {
+  static constexpr int XP = D + 8;
+  static constexpr int NP = kTN + 8;
+  static constexpr int CP = kC + 8;   // row stride of [token][token] tiles
+  FwdChunk<D> ch[2];
+  __bf16 AT[kC][CP];                  // AT[j][i] = A_ij
+  __bf16 S[2][kTN][XP];               // D_in of the tile, bf16 [row][col] (double-buffered)
+  __bf16 W[kTN][XP];                  // W0 of the tile [row][col]
 };
 
 template <int D>
@@ -75,10 +83,10 @@ __device__ __forceinline__ void load_chunk(Prefetch<D>& p, const uint16_t* x, co
 
 __device__ __forceinline__ uint4 scale_bf16x8(const uint4& v, float s) {
   uint4 r;
-  r.x = bf16_bits(bf16_val(v.x & 0xffffu) * s) | (bf16_bits(bf16_val(v.x >> 16) * s) << 16);
-  r.y = bf16_bits(bf16_val(v.y & 0xffffu) * s) | (bf16_bits(bf16_val(v.y >> 16) * s) << 16);
-  r.z = bf16_bits(bf16_val(v.z & 0xffffu) * s) | (bf16_bits(bf16_val(v.z >> 16) * s) << 16);
-  r.w = bf16_bits(bf16_val(v.w & 0xffffu) * s) | (bf16_bits(bf16_val(v.w >> 16) * s) << 16);
+  r.x = pack2(bf16_val(v.x & 0xffffu) * s, bf16_val(v.x >> 16) * s);
+  r.y = pack2(bf16_val(v.y & 0xffffu) * s, bf16_val(v.y >> 16) * s);
+  r.z = pack2(bf16_val(v.z & 0xffffu) * s, bf16_val(v.z >> 16) * s);
+  r.w = pack2(bf16_val(v.w & 0xffffu) * s, bf16_val(v.w >> 16) * s);
   return r;
 }
 
@@ -113,7 +121,7 @@ __global__ __launch_bounds__(kNT) void fwd_mfma(FwdArgs a) {
     const int r = idx / (D / 8), cc = 8 * (idx % (D / 8));
     *reinterpret_cast<uint4*>(&sm.W[r][cc]) =
         *reinterpret_cast<const uint4*>(W0 + static_cast<int64_t>(r0 + r) * D + cc);
-    *reinterpret_cast<uint4*>(&sm.S[r][cc]) = make_uint4(0, 0, 0, 0);
+    *reinterpret_cast<uint4*>(&sm.S[0][r][cc]) = make_uint4(0, 0, 0, 0);
   }
   for (int idx = tid; idx < kC * CP; idx += kNT) (&sm.AT[0][0])[idx] = static_cast<__bf16>(0.f);
 
@@ -121,40 +129,45 @@ __global__ __launch_bounds__(kNT) void fwd_mfma(FwdArgs a) {
 #pragma unroll
   for (int s = 0; s < NS; ++s) sacc[s] = zero4();
 
-  Prefetch<D> pf;
-  load_chunk<D>(pf, x, g, eta, alpha, 0, static_cast<int>(std::min<int64_t>(kC, T)), r0, tid);
-
-  for (int c = 0; c < a.n_chunks; ++c) {
-    const int64_t t0 = static_cast<int64_t>(c) * kC;
-    const int cv = static_cast<int>(std::min<int64_t>(kC, T - t0));
-
-    // ---- gates (every wave, lane = token) and staging of the chunk
+  const auto cv_of = [&](int c) {
+    return static_cast<int>(std::min<int64_t>(kC, T - static_cast<int64_t>(c) * kC));
+  };
+  // Stage a loaded chunk (and its gates) into LDS buffer `buf`.
+  const auto stage = [&](const Prefetch<D>& pf, FwdChunk<D>& buf, int cv) {
     const float et = lane < cv ? pf.eta : 0.f;
     const ChunkGates gt = chunk_gates(lane < cv ? pf.alpha : 1.f, lane);
     const float bk = -et * fexp2(gt.llast - gt.l);
-    const float gam = fexp2(gt.llast);
     if (wave == 0) {
-      sm.lq[lane] = gt.lq;
-      sm.li[lane] = gt.l;
-      sm.eq[lane] = fexp2(gt.lq);
-      sm.neta[lane] = -et;
+      buf.lq[lane] = gt.lq;
+      buf.li[lane] = gt.l;
+      buf.eq[lane] = fexp2(gt.lq);
+      buf.neta[lane] = -et;
+      if (lane == 0) buf.gam = fexp2(gt.llast);
     }
 #pragma unroll
     for (int s = 0; s < RPT; ++s)
-      *reinterpret_cast<uint4*>(&sm.X[rg * RPT + s][8 * cg]) = keep_row(pf.x[s], rg * RPT + s, cv);
-    {
-      const uint4 gv = keep_row(pf.g, jg, cv);
-      *reinterpret_cast<uint4*>(&sm.G[jg][c8]) = gv;
-      *reinterpret_cast<uint4*>(&sm.Gs[jg][c8]) = scale_bf16x8(gv, __shfl(bk, jg, 64));
-    }
-    lds_barrier();  // B1: chunk tiles and gates visible
-    {
-      // prefetch the next chunk (the last chunk is re-read and ignored)
-      const int cn = std::min(c + 1, a.n_chunks - 1);
-      const int64_t t1 = static_cast<int64_t>(cn) * kC;
-      load_chunk<D>(pf, x, g, eta, alpha, t1, static_cast<int>(std::min<int64_t>(kC, T - t1)),
-                    r0, tid);
-    }
+      *reinterpret_cast<uint4*>(&buf.X[rg * RPT + s][8 * cg]) = keep_row(pf.x[s], rg * RPT + s, cv);
+    const uint4 gv = keep_row(pf.g, jg, cv);
+    *reinterpret_cast<uint4*>(&buf.G[jg][c8]) = gv;
+    *reinterpret_cast<uint4*>(&buf.Gs[jg][c8]) = scale_bf16x8(gv, __shfl(bk, jg, 64));
+  };
+
+  {
+    Prefetch<D> pf;
+    load_chunk<D>(pf, x, g, eta, alpha, 0, cv_of(0), r0, tid);
+    stage(pf, sm.ch[0], cv_of(0));
+  }
+  lds_barrier();
+
+  for (int c = 0; c < a.n_chunks; ++c) {
+    const int64_t t0 = static_cast<int64_t>(c) * kC;
+    const int cv = cv_of(c);
+    FwdChunk<D>& cur = sm.ch[c & 1];
+    // loads of the next chunk are issued now and consumed at the end of this
+    // iteration, hidden behind this chunk's arithmetic
+    const bool more = c + 1 < a.n_chunks;
+    Prefetch<D> pf;
+    if (more) load_chunk<D>(pf, x, g, eta, alpha, t0 + kC, cv_of(c + 1), r0, tid);
 
     if (y) {
       // causal decayed scores, written transposed: AT[j][i]
@@ -166,20 +179,20 @@ __global__ __launch_bounds__(kNT) void fwd_mfma(FwdArgs a) {
           f32x4 xx = zero4();
 #pragma unroll
           for (int kb = 0; kb < D / 32; ++kb)
-            xx = mfma16x16x32(frag(&sm.X[0][0], XP, ib * 16, kb * 32, lane),
-                              frag(&sm.X[0][0], XP, jb * 16, kb * 32, lane), xx);
+            xx = mfma16x16x32(frag(&cur.X[0][0], XP, ib * 16, kb * 32, lane),
+                              frag(&cur.X[0][0], XP, jb * 16, kb * 32, lane), xx);
           const int j = jb * 16 + l16, i0 = ib * 16 + 4 * g4;
-          const float lj = sm.li[j], nj = sm.neta[j];
-          const f32x4 lqi = *reinterpret_cast<const f32x4*>(&sm.lq[i0]);
-          float v[4];
+          const float lj = cur.li[j], nj = cur.neta[j];
+          const f32x4 lqi = *reinterpret_cast<const f32x4*>(&cur.lq[i0]);
+          f32x4 v;
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const float e = xx[q] * fexp2(lqi[q] - lj) * nj;
             v[q] = (j < i0 + q) ? e : 0.f;
           }
           uint2 pk;
-          pk.x = bf16_bits(v[0]) | (bf16_bits(v[1]) << 16);
-          pk.y = bf16_bits(v[2]) | (bf16_bits(v[3]) << 16);
+          pk.x = pack2(v[0], v[1]);
+          pk.y = pack2(v[2], v[3]);
           *reinterpret_cast<uint2*>(&sm.AT[j][i0]) = pk;
         }
       }
@@ -190,63 +203,67 @@ __global__ __launch_bounds__(kNT) void fwd_mfma(FwdArgs a) {
       for (int s = 0; s < NS; ++s) {
         const int b = wave + 4 * s, cb = b >> 1, rb = b & 1;
         uint2 v;
-        v.x = bf16_bits(sacc[s][0]) | (bf16_bits(sacc[s][1]) << 16);
-        v.y = bf16_bits(sacc[s][2]) | (bf16_bits(sacc[s][3]) << 16);
+        v.x = pack2(sacc[s][0], sacc[s][1]);
+        v.y = pack2(sacc[s][2], sacc[s][3]);
         *reinterpret_cast<uint2*>(st + (static_cast<int64_t>(c) * D + r0 + rb * 16 + l16) * D +
                                   cb * 16 + 4 * g4) = v;
       }
     }
-    lds_barrier();  // B2: scores visible
+    lds_barrier();  // scores visible
 
+    const __bf16* S_in = &sm.S[c & 1][0][0];
     if (y) {
-      // y^T[r][i] for i in this wave's token block, both row blocks
+      // y^T[r][i] for i in this wave's token block, both row blocks; each lane
+      // stores 4 consecutive rows of one token straight from the accumulators
       const int w = wave;
       f32x4 ya[2] = {zero4(), zero4()}, yb[2] = {zero4(), zero4()};
       for (int kb = 0; kb < (w + 2) / 2; ++kb) {
         const bf16x8 af = frag_t(&sm.AT[0][0], CP, kb * 32, w * 16, lane);
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb)
-          ya[rb] = mfma16x16x32(frag_t(&sm.G[0][0], NP, kb * 32, rb * 16, lane), af, ya[rb]);
+          ya[rb] = mfma16x16x32(frag_t(&cur.G[0][0], NP, kb * 32, rb * 16, lane), af, ya[rb]);
       }
 #pragma unroll
       for (int kb = 0; kb < D / 32; ++kb) {
-        const bf16x8 xf = frag(&sm.X[0][0], XP, w * 16, kb * 32, lane);
+        const bf16x8 xf = frag(&cur.X[0][0], XP, w * 16, kb * 32, lane);
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb) {
           ya[rb] = mfma16x16x32(frag(&sm.W[0][0], XP, rb * 16, kb * 32, lane), xf, ya[rb]);
-          yb[rb] = mfma16x16x32(frag(&sm.S[0][0], XP, rb * 16, kb * 32, lane), xf, yb[rb]);
+          yb[rb] = mfma16x16x32(frag(S_in, XP, rb * 16, kb * 32, lane), xf, yb[rb]);
         }
       }
       const int i = w * 16 + l16;
-      const float eqi = sm.eq[i];
+      const float eqi = cur.eq[i];
+      if (i < cv) {
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb) {
-        uint2 pk;
-        pk.x = bf16_bits(ya[rb][0] + eqi * yb[rb][0]) | (bf16_bits(ya[rb][1] + eqi * yb[rb][1]) << 16);
-        pk.y = bf16_bits(ya[rb][2] + eqi * yb[rb][2]) | (bf16_bits(ya[rb][3] + eqi * yb[rb][3]) << 16);
-        *reinterpret_cast<uint2*>(&sm.Y[i][rb * 16 + 4 * g4]) = pk;
+        for (int rb = 0; rb < 2; ++rb) {
+          uint2 pk;
+          pk.x = pack2(ya[rb][0] + eqi * yb[rb][0], ya[rb][1] + eqi * yb[rb][1]);
+          pk.y = pack2(ya[rb][2] + eqi * yb[rb][2], ya[rb][3] + eqi * yb[rb][3]);
+          *reinterpret_cast<uint2*>(y + (t0 + i) * D + r0 + rb * 16 + 4 * g4) = pk;
+        }
       }
     }
-    lds_barrier();  // B3: y staged; reads of S, AT, G done
 
-    if (y && jg < cv)
-      *reinterpret_cast<uint4*>(y + (t0 + jg) * D + r0 + c8) =
-          *reinterpret_cast<const uint4*>(&sm.Y[jg][c8]);
-    // state update, transposed: D^T[c][r] = Gamma D^T + sum_j x_j[c] (bk_j g_j[r])
+    // state update, transposed: D^T[c][r] = Gamma D^T + sum_j x_j[c] (bk_j g_j[r]),
+    // written to the other state buffer (the current one may still be read)
+    __bf16 (*S_out)[XP] = sm.S[(c + 1) & 1];
+    const float gam = cur.gam;
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
       const int b = wave + 4 * s, cb = b >> 1, rb = b & 1;
       sacc[s] = sacc[s] * gam;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
-        sacc[s] = mfma16x16x32(frag_t(&sm.X[0][0], XP, kb * 32, cb * 16, lane),
-                               frag_t(&sm.Gs[0][0], NP, kb * 32, rb * 16, lane), sacc[s]);
+        sacc[s] = mfma16x16x32(frag_t(&cur.X[0][0], XP, kb * 32, cb * 16, lane),
+                               frag_t(&cur.Gs[0][0], NP, kb * 32, rb * 16, lane), sacc[s]);
       uint2 pk;
-      pk.x = bf16_bits(sacc[s][0]) | (bf16_bits(sacc[s][1]) << 16);
-      pk.y = bf16_bits(sacc[s][2]) | (bf16_bits(sacc[s][3]) << 16);
-      *reinterpret_cast<uint2*>(&sm.S[rb * 16 + l16][cb * 16 + 4 * g4]) = pk;
+      pk.x = pack2(sacc[s][0], sacc[s][1]);
+      pk.y = pack2(sacc[s][2], sacc[s][3]);
+      *reinterpret_cast<uint2*>(&S_out[rb * 16 + l16][cb * 16 + 4 * g4]) = pk;
     }
-    lds_barrier();  // B4: new state visible; chunk tiles free
+    if (more) stage(pf, sm.ch[(c + 1) & 1], cv_of(c + 1));
+    lds_barrier();  // new state and next chunk visible
   }
 }
 

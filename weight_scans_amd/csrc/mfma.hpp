@@ -58,6 +58,14 @@ __device__ __forceinline__ uint32_t bf16_bits(float f) {
   return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, h));
 }
 
+// Two floats -> packed bf16 pair (round to nearest even), one v_cvt_pk_bf16_f32.
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+  const f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
 __device__ __forceinline__ float bf16_val(uint16_t b) {
   return __uint_as_float(static_cast<uint32_t>(b) << 16);
 }
@@ -101,6 +109,59 @@ __device__ __forceinline__ uint32_t half_of(const uint4& u, int q) {
   return (q & 1) ? (w >> 16) : (w & 0xffffu);
 }
 
+// ---- wave64 scans on DPP (register-only cross-lane moves, GFX9 controls) ----
+// dpp<CTRL, ROW_MASK>(old, v): v moved by the DPP pattern; lanes whose source
+// is outside the pattern, or whose row is masked off, receive `old`.
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ float dpp(float old, float v) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, old), __builtin_bit_cast(int, v),
+                                         CTRL, ROW_MASK, 0xf, false));
+}
+constexpr int kRowShr1 = 0x111, kRowShr2 = 0x112, kRowShr4 = 0x114, kRowShr8 = 0x118;
+constexpr int kRowBcast15 = 0x142, kRowBcast31 = 0x143, kWaveShr1 = 0x138;
+
+// Inclusive prefix sum over the 64 lanes.
+__device__ __forceinline__ float wave_scan_add(float x) {
+  x += dpp<kRowShr1>(0.f, x);
+  x += dpp<kRowShr2>(0.f, x);
+  x += dpp<kRowShr4>(0.f, x);
+  x += dpp<kRowShr8>(0.f, x);
+  x += dpp<kRowBcast15, 0xa>(0.f, x);
+  x += dpp<kRowBcast31, 0xc>(0.f, x);
+  return x;
+}
+
+// Value of the previous lane (lane 0 receives `first`).
+__device__ __forceinline__ float wave_shift_up(float x, float first) {
+  return dpp<kWaveShr1>(first, x);
+}
+
+// Inclusive scan of affine pairs over the lanes: with (a_i, b_i) per lane the
+// result is (prod_{j<=i} a_j, sum_{j<=i} (prod_{j<r<=i} a_r) b_j), i.e. the
+// state after lane i of z <- a_i z + b_i started from z = 0 (the composition
+// of the affine maps of lanes 0..i; identity (1, 0)).
+template <int CTRL, int RM = 0xf>
+__device__ __forceinline__ void affine_step(float& a, float& b) {
+  const float as = dpp<CTRL, RM>(1.f, a), bs = dpp<CTRL, RM>(0.f, b);
+  b = b + a * bs;
+  a = a * as;
+}
+__device__ __forceinline__ void wave_scan_affine(float& a, float& b) {
+  affine_step<kRowShr1>(a, b);
+  affine_step<kRowShr2>(a, b);
+  affine_step<kRowShr4>(a, b);
+  affine_step<kRowShr8>(a, b);
+  affine_step<kRowBcast15, 0xa>(a, b);
+  affine_step<kRowBcast31, 0xc>(a, b);
+}
+
+// Lane order reversed (lane i <- lane 63 - i).
+__device__ __forceinline__ float wave_reverse(float x, int lane) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute((63 - lane) << 2,
+                                                                 __builtin_bit_cast(int, x)));
+}
+
 // Chunk gates, lane = token (one wave, 64 tokens).  Works in log2:
 //   l_i = sum_{r <= i} log2 alpha_r (inclusive),  lq_i = l_{i-1} (l_{-1} = 0)
 // Padding tokens must carry alpha = 1, eta = 0.
@@ -108,18 +169,11 @@ struct ChunkGates {
   float l, lq, llast;
 };
 __device__ __forceinline__ ChunkGates chunk_gates(float alpha, int lane) {
-  float l = flog2(alpha);
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const float v = __shfl_up(l, off, 64);
-    if (lane >= off) l += v;
-  }
-  float lp = __shfl_up(l, 1, 64);
-  if (lane == 0) lp = 0.f;
+  (void)lane;
   ChunkGates g;
-  g.l = l;
-  g.lq = lp;
-  g.llast = __shfl(l, 63, 64);
+  g.l = wave_scan_add(flog2(alpha));
+  g.lq = wave_shift_up(g.l, 0.f);
+  g.llast = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, g.l), 63));
   return g;
 }
 
