@@ -135,6 +135,13 @@ def main():
     fws, bws = ws.workspace_size(desc, True)
     wsb = torch.empty(max(fws, bws, 16), dtype=torch.uint8, device=dev)
     flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    # one plain copy of known size (256 MiB each way): the reference that turns
+    # the FETCH_SIZE / WRITE_SIZE counters of a profiled run into bytes
+    calib_src = torch.ones(64 << 20, dtype=torch.float32, device=dev)
+    calib_dst = torch.empty_like(calib_src)
+    torch.neg(calib_src, out=calib_dst)  # a plain elementwise kernel: 256 MiB in, 256 MiB out
+    torch.cuda.synchronize()
+    del calib_src, calib_dst
     L = ws.lib()
     stream = torch.cuda.current_stream(dev)
     sp = ctypes.c_void_p(stream.cuda_stream)
@@ -184,6 +191,14 @@ def main():
     # roofline of the whole step (both passes against their own bounds)
     step_floor = sum(max(alg[p][0] / PEAK_HBM, alg[p][1] / PEAK_MATRIX[w.dtype]) for p in alg)
 
+    traffic = None
+    tpath = os.path.join(ROOT, "profiles", "traffic.json")
+    if os.path.exists(tpath) and not args.generic:
+        from weight_scans_amd.profiling import kernel_source_hash
+        rec_t = json.load(open(tpath)).get(w.name)
+        if rec_t and rec_t.get("kernel_hash") == kernel_source_hash():
+            traffic = rec_t[f"{dom}_bytes"]
+
     rec = {
         "metric": "tokens/s (fwd+bwd scan)",
         "value": value,
@@ -203,7 +218,8 @@ def main():
                    "parallelism": "single GPU"},
         "passes_ms": {"fwd_mean": mf, "bwd_mean": mb, "fwd_min": min(tf), "bwd_min": min(tb)},
         "roofline": {"bound": bound, "achieved": achieved, "peak": peak, "unit": unit,
-                     "frac": achieved / peak, "traffic": None,
+                     "frac": achieved / peak, "traffic": traffic,
+                     "algorithmic_bytes": nbytes, "algorithmic_flops": nflops,
                      "kernel": f"{dom} pass ({path})",
                      "step_frac": step_floor / (ms_step / 1e3)},
         "wall_ms_per_step_incl_flush": wall * 1e3 / args.steps,

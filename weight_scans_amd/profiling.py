@@ -1,0 +1,129 @@
+"""Turn rocprofv3 output into the short text summaries kept under profiles/.
+
+    python -m weight_scans_amd.profiling stats  <kernel_stats.csv>
+    python -m weight_scans_amd.profiling traffic <fetch_dir> <write_dir> <config>
+
+`stats` prints a markdown table from a rocprofv3 `--stats` kernel summary CSV
+(or a rocpd2summary kernels CSV).  `traffic` reads the counter CSVs of two
+`--pmc FETCH_SIZE` / `--pmc WRITE_SIZE` runs of `bench.py`, converts each
+counter (KiB per dispatch) into bytes with a scale factor measured on the
+plain elementwise kernel (torch.neg over 64 Mi fp32) that bench.py launches
+once with a known size (256 MiB read, 256 MiB written), and prints per-pass
+HBM traffic.  With --json it also writes
+the record bench.py reads back into its roofline `traffic` field, keyed by a
+hash of the kernel sources so that a changed kernel invalidates it.
+"""
+from __future__ import annotations
+
+import csv
+import glob
+import hashlib
+import json
+import os
+import sys
+from collections import defaultdict
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CALIB_BYTES = 256 << 20  # the calibration kernel in bench.py: 256 MiB read + 256 MiB written
+
+
+def kernel_source_hash() -> str:
+    """Hash of every source the library is built from."""
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(HERE, "csrc", "*"))):
+        with open(p, "rb") as fh:
+            h.update(os.path.basename(p).encode())
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def short_name(kernel: str) -> str:
+    k = kernel
+    for pre in ("void ", "gls::(anonymous namespace)::", "at::native::"):
+        k = k.replace(pre, "")
+    return k.split("(")[0]
+
+
+def stats_table(path: str) -> str:
+    rows = list(csv.DictReader(open(path)))
+    out = ["| kernel | calls | avg (us) | min (us) | max (us) | share |",
+           "|---|---|---|---|---|---|"]
+    for r in rows:
+        name = r.get("Name") or r.get("KernelName") or r.get("name")
+        calls = int(float(r.get("Calls") or r.get("total_calls")))
+        avg = float(r.get("Average (Nsec)") or r.get("AverageNs") or 0) / 1e3
+        mn = float(r.get("Min (Nsec)") or r.get("MinNs") or 0) / 1e3
+        mx = float(r.get("Max (Nsec)") or r.get("MaxNs") or 0) / 1e3
+        pct = float(r.get("Percent (Inc)") or r.get("Percentage") or 0)
+        out.append(f"| `{short_name(name)}` | {calls} | {avg:.1f} | {mn:.1f} | {mx:.1f} | {pct:.1f}% |")
+    return "\n".join(out)
+
+
+def _counter(dirpath: str, counter: str):
+    """{kernel name: [value per dispatch]} for one counter (summed over dims)."""
+    per = defaultdict(lambda: defaultdict(float))
+    for f in glob.glob(os.path.join(dirpath, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            if r["Counter_Name"] != counter:
+                continue
+            per[r["Kernel_Name"]][r["Dispatch_Id"]] += float(r["Counter_Value"])
+    return {k: list(v.values()) for k, v in per.items()}
+
+
+def _mean(v):
+    return sum(v) / len(v) if v else float("nan")
+
+
+def traffic(fetch_dir: str, write_dir: str):
+    fetch = _counter(fetch_dir, "FETCH_SIZE")
+    write = _counter(write_dir, "WRITE_SIZE")
+    copy = [k for k in fetch if "neg" in k.lower()]
+    if not copy:
+        raise SystemExit("calibration copy kernel not found in the FETCH_SIZE run")
+    # the copy kernel reads and writes CALIB_BYTES; counters are in KiB
+    f_scale = CALIB_BYTES / (_mean(fetch[copy[0]]) * 1024.0)
+    w_scale = CALIB_BYTES / (_mean(write[copy[0]]) * 1024.0)
+    res = {"fetch_scale": f_scale, "write_scale": w_scale, "kernels": {}}
+    for k in fetch:
+        if k not in write:
+            continue
+        fb = _mean(fetch[k]) * 1024.0 * f_scale
+        wb = _mean(write[k]) * 1024.0 * w_scale
+        res["kernels"][short_name(k)] = {"fetch_bytes": fb, "write_bytes": wb,
+                                         "dispatches": len(fetch[k])}
+    return res
+
+
+def main(argv):
+    if len(argv) >= 2 and argv[0] == "stats":
+        print(stats_table(argv[1]))
+        return 0
+    if len(argv) >= 4 and argv[0] == "traffic":
+        res = traffic(argv[1], argv[2])
+        cfg = argv[3]
+        print(f"calibration: FETCH_SIZE x{res['fetch_scale']:.4f}, WRITE_SIZE x{res['write_scale']:.4f}"
+              f" (copy kernel, {CALIB_BYTES >> 20} MiB each way)")
+        print("| kernel | HBM read (MB) | HBM write (MB) | dispatches |")
+        print("|---|---|---|---|")
+        for k, v in res["kernels"].items():
+            print(f"| `{k}` | {v['fetch_bytes'] / 1e6:.1f} | {v['write_bytes'] / 1e6:.1f} | {v['dispatches']} |")
+        if "--json" in argv:
+            path = os.path.join(ROOT, "profiles", "traffic.json")
+            db = json.load(open(path)) if os.path.exists(path) else {}
+            fwd = sum(v["fetch_bytes"] + v["write_bytes"] for k, v in res["kernels"].items()
+                      if "fwd_mfma" in k or "fwd_generic" in k)
+            bwd = sum(v["fetch_bytes"] + v["write_bytes"] for k, v in res["kernels"].items()
+                      if "bwd_mfma" in k or "bwd_generic" in k or "finalize" in k)
+            db[cfg] = {"kernel_hash": kernel_source_hash(), "fwd_bytes": fwd, "bwd_bytes": bwd,
+                       "fetch_scale": res["fetch_scale"], "write_scale": res["write_scale"]}
+            with open(path, "w") as fh:
+                json.dump(db, fh, indent=1, sort_keys=True)
+            print(f"wrote {path}")
+        return 0
+    print(__doc__)
+    return 2
+
+
+if __name__ == "__main__":
+    sys.exit(main(sys.argv[1:]))
