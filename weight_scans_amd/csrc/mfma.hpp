@@ -53,6 +53,119 @@ __device__ __forceinline__ bf16x8 frag_t(const __bf16* base, int ld, int k0, int
   return __builtin_bit_cast(bf16x8, c);
 }
 
+// ---- swizzled LDS tiles ----
+// A [rows][W] bf16 tile (W in {32, 64, 128}) is stored with its 16-byte
+// column groups XOR-permuted per row, so that both fragment reads above hit
+// every LDS bank once.  The gfx950 LDS has 64 four-byte banks; a 16-byte read
+// is served sixteen lanes at a time (lanes 0-7 with 16-23, 8-15 with 24-31,
+// ...) and the transposing 8-byte read thirty-two consecutive lanes at a time.
+// frag reads rows r0..r0+7 (and +8..15) at two adjacent groups, frag_t reads
+// rows R..R+3 and R+8..R+11 at two adjacent groups; the masks below make the
+// pair index of the group (bits 1..) a bijection of the row bits involved.
+template <int W>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (W == 128)
+    return ((r & 1) << 1) | (((r >> 1) & 1) << 2) | ((((r >> 2) ^ (r >> 3)) & 1) << 3);
+  else if constexpr (W == 64)
+    return (((r >> 1) & 1) << 1) | ((((r >> 2) ^ (r >> 3)) & 1) << 2);
+  else
+    return ((r >> 3) & 1) << 1;
+}
+// Element offset of (row r, column c) in a swizzled [rows][W] tile.
+template <int W>
+__device__ __forceinline__ int sidx(int r, int c) {
+  return r * W + ((((c >> 3) ^ swz<W>(r))) << 3) + (c & 7);
+}
+// Fragment reads of swizzled tiles.  The per-lane part of every read
+// address is computed once (LaneOff); a read is then `base + const + (off ^
+// const)`: the K or column block only XORs the 16-byte group bits (the row,
+// group and byte fields of the offset are disjoint bit ranges).  Keeping the
+// address in this short form also lets the compiler attribute every read to
+// its LDS object, which it needs to see that the read does not depend on
+// direct loads still in flight into other objects.
+template <int W>
+struct LaneOff {
+  uint32_t b;       // frag_s: row lane%16, group lane/16
+  uint32_t t0, t1;  // frag_ts: rows 8(g&1) + s/4 (+16(g>>1)), and 4 rows further
+  uint32_t w;       // put4: row lane%16, columns 4*(lane/16)..+3
+};
+template <int W>
+__device__ __forceinline__ LaneOff<W> lane_off(int lane) {
+  static_assert(W == 32 || W == 64 || W == 128, "W");
+  const int l = lane & 15, g = lane >> 4;
+  LaneOff<W> o;
+  o.b = static_cast<uint32_t>(l * W * 2 + ((g ^ swz<W>(l)) << 4));
+  const int rl = 8 * (g & 1) + (l >> 2), rh = 16 * (g >> 1);
+  const int hb = (l >> 1) & 1, e = 8 * (l & 1);
+  o.t0 = static_cast<uint32_t>((rh + rl) * W * 2 + ((hb ^ swz<W>(rl)) << 4) + e);
+  o.t1 = static_cast<uint32_t>((rh + rl + 4) * W * 2 + ((hb ^ swz<W>(rl + 4)) << 4) + e);
+  o.w = static_cast<uint32_t>(l * W * 2 + ((((g >> 1)) ^ swz<W>(l)) << 4) + 8 * (g & 1));
+  return o;
+}
+// frag on a swizzled [rows][W] tile: rows row0.. (multiple of 16), K columns
+// k0.. (multiple of 32).
+template <int W>
+__device__ __forceinline__ bf16x8 frag_s(const __bf16* base, const LaneOff<W>& o, int row0, int k0) {
+  const char* p = reinterpret_cast<const char*>(base) + row0 * W * 2 + (o.b ^ ((k0 >> 3) << 4));
+  return *reinterpret_cast<const bf16x8*>(p);
+}
+// frag_t on a swizzled [rows][W] tile: K rows k0.. (multiple of 32), columns
+// c0.. (multiple of 16).
+template <int W>
+__device__ __forceinline__ bf16x8 frag_ts(const __bf16* base, const LaneOff<W>& o, int k0, int c0) {
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  const char* p = reinterpret_cast<const char*>(base) + k0 * W * 2;
+  const uint32_t x = static_cast<uint32_t>((c0 >> 3) << 4);
+  const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + (o.t0 ^ x)));
+  const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + (o.t1 ^ x)));
+  const s16x8 v = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// 8-byte store of the MFMA result layout into a swizzled tile: lane l writes
+// row row0 + l%16, columns c0 + 4*(l/16) .. +3 (row0 multiple of 16, c0 of 16).
+template <int W>
+__device__ __forceinline__ void put4(__bf16* base, const LaneOff<W>& o, int row0, int c0,
+                                     const uint2& v) {
+  char* p = reinterpret_cast<char*>(base) + row0 * W * 2 + (o.w ^ ((c0 >> 3) << 4));
+  *reinterpret_cast<uint2*>(p) = v;
+}
+
+// ---- direct global -> LDS loads (no VGPR round trip) ----
+// One wave instruction writes 64 consecutive LDS slots of `size` bytes
+// starting at the wave-uniform `lds`, lane i into slot i, from byte offset
+// `voff` (per lane) of a buffer.  Lanes whose offset is at or past the
+// buffer's byte count write zeros.  Completion is tracked by vmcnt only.
+// The per-lane offsets are loop invariants held in VGPRs (the buffer base
+// moves per chunk), so no register that a load in flight reads is reused.
+typedef __attribute__((address_space(3))) void lds_void_t;
+constexpr int kBufferFlags = 0x00020000;  // raw (untyped) buffer, dword3
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), bytes,
+                                           kBufferFlags);
+}
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, void* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)(lds), 16, voff, 0, 0, 0);
+}
+__device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, uint32_t voff, void* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)(lds), 4, voff, 0, 0, 0);
+}
+// 8-byte buffer store (lanes whose offset is past the buffer's byte count
+// store nothing).
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void store8(__amdgpu_buffer_rsrc_t r, uint32_t voff, const uint2& v) {
+  const u32x2_t d = {v.x, v.y};
+  __builtin_amdgcn_raw_buffer_store_b64(d, r, voff, 0, 0);
+}
+
+// Wait until at most N vector-memory operations of this wave are outstanding
+// (they complete in issue order).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
 __device__ __forceinline__ uint32_t bf16_bits(float f) {
   __bf16 h = static_cast<__bf16>(f);
   return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, h));
