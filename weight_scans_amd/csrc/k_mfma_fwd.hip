@@ -14,16 +14,19 @@
 // are known, the weight trajectory becomes parallelizable") composed as an
 // affine scan across chunks.  Every exponent is <= 0.
 //
-// Pipeline: chunk tiles are copied HBM -> LDS by direct loads
-// (global_load_lds) into a ring of kRing slots, kRing - 2 chunks ahead of the
-// chunk being finished, so the serial chain over chunks does not wait for
-// memory latency.  The scores of chunk c + 1 are formed while chunk c is
-// finished, which leaves one work-group barrier per chunk.  All LDS tiles are
-// XOR-swizzled (mfma.hpp) so that fragment reads are free of bank conflicts.
+// Pipeline (one work-group barrier per chunk): chunk tiles are copied
+// HBM -> LDS by direct buffer loads into a ring of kRing slots; while chunk c
+// is finished (y and the state update), the scores of chunk c + 1 are formed
+// and one wave derives the gates of chunk c + 2, and the loads of chunks
+// c + 3 and c + 4 are in flight.  Eight waves (two per SIMD) share the work:
+// wave w owns the 16 x 16 output block (token block w/2, row block w%2) of y
+// and D/64 16 x 16 blocks of the state.  All LDS tiles are XOR-swizzled
+// (mfma.hpp) so that fragment reads are free of bank conflicts.
 //
 // `states` (optional) receives D_in of every chunk in bf16:
 // [B*H][n_chunks][D (row r)][D (col c)] -- read by the matrix-core backward.
 #include <algorithm>
+#include <cstddef>
 #include <type_traits>
 
 #include "dev_common.hpp"
@@ -33,47 +36,66 @@
 namespace gls {
 namespace {
 
-constexpr int kC = 64;     // tokens per chunk
-constexpr int kTN = 32;    // rows of the adaptation per work-group
-constexpr int kNT = 256;   // threads (4 waves)
-constexpr int kRing = 5;   // chunk slots: 2 in use, 3 in flight
+constexpr int kC = 64;         // tokens per chunk
+constexpr int kTN = 32;        // rows of the adaptation per work-group
+constexpr int kNW = 8;         // waves per work-group
+constexpr int kNT = 64 * kNW;  // threads
+constexpr int kRing = 5;       // chunk slots: 3 in use, 2 in flight
+constexpr int kPrepWave = 2;   // the wave that derives the gates
+
+// Per-token factors of a chunk derived from the gates (i = token, b = 16-token
+// block of i, m_b = l_{16 b - 1} with m_0 = 0):
+//   eq_i = e(lq_i),  R_i = e(lq_i - m_b),  C_{b', i} = e(m_b' - l_i)(-eta_i)  (b' = 1..3)
+// so that for i in block b' > block of j:  e(lq_i - l_j)(-eta_j) = R_i C_{b', j},
+// with both factors <= 1 in magnitude (l is non-increasing).
+struct GateRows {
+  float eta[kC], R[kC], C1[kC], C2[kC];  // eta: as loaded; the rest derived
+  float alpha[kC], C3[kC], eq[kC], pad[kC];
+};
 
 template <int D>
 struct alignas(16) Slot {
-  __bf16 X[kC * D];        // x of the chunk, swizzled [token][D]
-  __bf16 G[kC * kTN];      // g of the row tile, swizzled [token][kTN]
-  float q[4][kC];          // raw gates: eta, alpha (rows 2, 3: zero fill)
-  float lq[kC], li[kC], nb[kC], bk[kC];      // l_{i-1}, l_i, -eta_i, e(l_last - l_i)(-eta_i)
+  __bf16 X[kC * D];                      // x of the chunk, swizzled [token][D]
+  __bf16 G[kC * kTN];                    // g of the row tile, swizzled [token][kTN]
+  union {
+    float q[2][4 * kC];                  // loaded: eta = q[0][0..63], alpha = q[1][0..63]
+    GateRows f;                          // after the gate pass (same bytes)
+  };
+  float lq[kC], li[kC], nb[kC], bk[kC];  // l_{i-1}, l_i, -eta_i, e(l_last - l_i)(-eta_i)
+  float gam[4];                          // gam[0] = e(l_last)
 };
 
-// Vector-memory instructions one wave issues per chunk load: D/32 for x, one
-// for g, one for the gates.
-template <int D>
-constexpr int kLoadOps = D / 32 + 2;
-
-// Per-lane byte offsets of the chunk loads (loop invariant).
+// Per-lane byte offsets of the chunk loads (loop invariant).  Wave w loads
+// x units of instructions w + 8 s, and a quarter of the g tile (w < 4) or a
+// gate row (w = 4, 6: eta; 5, 7: alpha -- two waves write the same bytes).
 template <int D>
 struct DmaOff {
-  uint32_t x[D / 32];  // x rows: wave instruction wave + 4 s covers 16-byte units 64 (wave + 4 s) ..
-  uint32_t g;          // g tile: units 64 wave ..
-  uint32_t q;          // gates: lane * 4
+  uint32_t x[D / 64];
+  uint32_t gq;
 };
 template <int D>
 __device__ __forceinline__ DmaOff<D> dma_off(int wave, int lane) {
   constexpr int U = D / 8;  // 16-byte units per row of x
   DmaOff<D> o;
 #pragma unroll
-  for (int s = 0; s < D / 32; ++s) {
-    const int p = (wave + 4 * s) * 64 + lane;
+  for (int s = 0; s < D / 64; ++s) {
+    const int p = (wave + 8 * s) * 64 + lane;
     const int row = p / U, kl = (p % U) ^ swz<D>(row);
     o.x[s] = static_cast<uint32_t>(row * D * 2 + 16 * kl);
   }
-  const int p = wave * 64 + lane;
-  const int row = p >> 2, kl = (p & 3) ^ swz<kTN>(row);
-  o.g = static_cast<uint32_t>(row * D * 2 + 16 * kl);
-  o.q = static_cast<uint32_t>(lane * 4);
+  if (wave < 4) {
+    const int p = wave * 64 + lane;
+    const int row = p >> 2, kl = (p & 3) ^ swz<kTN>(row);
+    o.gq = static_cast<uint32_t>(row * D * 2 + 16 * kl);
+  } else {
+    o.gq = static_cast<uint32_t>(lane * 16);
+  }
   return o;
 }
+
+// Vector-memory instructions one wave issues per chunk load.
+template <int D>
+constexpr int kLoadOps = D / 64 + 1;
 
 // Queue the loads of chunk k into `sl`.  Rows past the sequence end, and
 // chunks past the last one, are zero-filled by the buffer bounds (every wave
@@ -88,89 +110,106 @@ __device__ __forceinline__ void issue_chunk(Slot<D>& sl, const DmaOff<D>& o, con
   const int cv = in ? static_cast<int>(std::min<int64_t>(kC, T - t0)) : 0;
   const __amdgpu_buffer_rsrc_t rx = buffer_rsrc(x + t0 * D, cv * D * 2);
 #pragma unroll
-  for (int s = 0; s < D / 32; ++s) dma16(rx, o.x[s], sl.X + (wave + 4 * s) * 512);
-  const __amdgpu_buffer_rsrc_t rg = buffer_rsrc(g + t0 * D + r0, cv > 0 ? (cv * D - r0) * 2 : 0);
-  dma16(rg, o.g, sl.G + wave * 512);
-  const __amdgpu_buffer_rsrc_t rq = buffer_rsrc((wave == 0 ? eta : alpha) + t0, wave < 2 ? cv * 4 : 0);
-  dma4(rq, o.q, sl.q[wave]);
+  for (int s = 0; s < D / 64; ++s) dma16(rx, o.x[s], sl.X + (wave + 8 * s) * 512);
+  // the same instruction in every wave (no branch): scalar-selected source
+  // and destination offset within the slot
+  const bool gw = wave < 4;
+  const __amdgpu_buffer_rsrc_t r4 =
+      gw ? buffer_rsrc(g + t0 * D + r0, cv > 0 ? (cv * D - r0) * 2 : 0)
+         : buffer_rsrc(((wave & 1) == 0 ? eta : alpha) + t0, cv * 4);
+  const int lds_off = gw ? static_cast<int>(offsetof(Slot<D>, G)) + wave * 1024
+                         : static_cast<int>(offsetof(Slot<D>, q)) + (wave & 1) * 1024;
+  dma16(r4, o.gq, reinterpret_cast<char*>(&sl) + lds_off);
 }
 
-// Gates of a chunk, lane = token (every wave computes them and writes the
-// same values).  Returns Gamma = e(l_last).
+// Gates of a chunk, lane = token (one wave).
 template <int D>
-__device__ __forceinline__ float prep_gates(Slot<D>& sl, int cv, int lane) {
-  const float et = lane < cv ? sl.q[0][lane] : 0.f;
-  const ChunkGates gt = chunk_gates(lane < cv ? sl.q[1][lane] : 1.f, lane);
+__device__ __forceinline__ void prep_gates(Slot<D>& sl, int cv, int lane) {
+  const float et = lane < cv ? sl.f.eta[lane] : 0.f;
+  const ChunkGates gt = chunk_gates(lane < cv ? sl.f.alpha[lane] : 1.f, lane);
+  const float m1 = readlane_f(gt.l, 15), m2 = readlane_f(gt.l, 31), m3 = readlane_f(gt.l, 47);
+  const int b = lane >> 4;
+  const float mb = b == 0 ? 0.f : b == 1 ? m1 : b == 2 ? m2 : m3;
   sl.lq[lane] = gt.lq;
   sl.li[lane] = gt.l;
   sl.nb[lane] = -et;
   sl.bk[lane] = -et * fexp2(gt.llast - gt.l);
-  return fexp2(gt.llast);
+  sl.f.eq[lane] = fexp2(gt.lq);
+  sl.f.R[lane] = fexp2(gt.lq - mb);
+  sl.f.C1[lane] = -et * fexp2(fminf(m1 - gt.l, 0.f));
+  sl.f.C2[lane] = -et * fexp2(fminf(m2 - gt.l, 0.f));
+  sl.f.C3[lane] = -et * fexp2(fminf(m3 - gt.l, 0.f));
+  if (lane == 0) sl.gam[0] = fexp2(gt.llast);
 }
 
-// Causal decayed scores of a chunk, written transposed: AT[j][i] = A_ij.
-// Blocks above the diagonal are never written (they stay zero).
+// Block b (0..9, row-major over the causal triangle of 16 x 16 blocks) of the
+// decayed scores of a chunk, written transposed: AT[j][i] = A_ij.  Blocks
+// above the diagonal are never written (they stay zero).
 template <int D>
-__device__ __forceinline__ void scores(const Slot<D>& sl, __bf16* AT, const LaneOff<D>& oX,
-                                       const LaneOff<kC>& oA, int wave, int lane) {
+__device__ __forceinline__ void score_block(const Slot<D>& sl, __bf16* AT, const LaneOff<D>& oX,
+                                            const LaneOff<kC>& oA, int b, int lane) {
   const int g4 = lane >> 4, l16 = lane & 15;
+  const int ib = tri_i(b), jb = tri_j(b);
+  f32x4 xx = zero4();
 #pragma unroll
-  for (int s = 0; s < 3; ++s) {
-    const int b = wave + 4 * s;
-    if (b < 10) {
-      const int ib = tri_i(b), jb = tri_j(b);
-      f32x4 xx = zero4();
+  for (int kb = 0; kb < D / 32; ++kb)
+    xx = mfma16x16x32(frag_s<D>(sl.X, oX, ib * 16, kb * 32), frag_s<D>(sl.X, oX, jb * 16, kb * 32),
+                      xx);
+  const int j = jb * 16 + l16, i0 = ib * 16 + 4 * g4;
+  f32x4 v;
+  if (ib == jb) {  // diagonal block: decay per element, causal mask
+    const float lj = sl.li[j], nj = sl.nb[j];
+    const f32x4 lqi = *reinterpret_cast<const f32x4*>(&sl.lq[i0]);
 #pragma unroll
-      for (int kb = 0; kb < D / 32; ++kb)
-        xx = mfma16x16x32(frag_s<D>(sl.X, oX, ib * 16, kb * 32),
-                          frag_s<D>(sl.X, oX, jb * 16, kb * 32), xx);
-      const int j = jb * 16 + l16, i0 = ib * 16 + 4 * g4;
-      const float lj = sl.li[j], nj = sl.nb[j];
-      const f32x4 lqi = *reinterpret_cast<const f32x4*>(&sl.lq[i0]);
-      f32x4 v;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float e = xx[q] * fexp2(lqi[q] - lj) * nj;
-        v[q] = (j < i0 + q) ? e : 0.f;
-      }
-      uint2 pk;
-      pk.x = pack2(v[0], v[1]);
-      pk.y = pack2(v[2], v[3]);
-      put4<kC>(AT, oA, jb * 16, ib * 16, pk);
+    for (int q = 0; q < 4; ++q) {
+      const float e = xx[q] * fexp2(lqi[q] - lj) * nj;
+      v[q] = (j < i0 + q) ? e : 0.f;
     }
+  } else {  // every j < i: rank-one decay
+    const float cj = (ib == 1 ? sl.f.C1 : ib == 2 ? sl.f.C2 : sl.f.C3)[j];
+    const f32x4 ri = *reinterpret_cast<const f32x4*>(&sl.f.R[i0]);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) v[q] = xx[q] * (ri[q] * cj);
   }
+  uint2 pk;
+  pk.x = pack2(v[0], v[1]);
+  pk.y = pack2(v[2], v[3]);
+  put4<kC>(AT, oA, jb * 16, ib * 16, pk);
 }
 
-// bf16x8 fragment scaled element-wise by 8 floats (rounded back to bf16).
-__device__ __forceinline__ bf16x8 scale8(const bf16x8& v, const f32x4& s0, const f32x4& s1) {
-  const uint4 u = __builtin_bit_cast(uint4, v);
-  uint4 r;
-  r.x = pack2(bf16_val(u.x & 0xffffu) * s0[0], bf16_val(u.x >> 16) * s0[1]);
-  r.y = pack2(bf16_val(u.y & 0xffffu) * s0[2], bf16_val(u.y >> 16) * s0[3]);
-  r.z = pack2(bf16_val(u.z & 0xffffu) * s1[0], bf16_val(u.z >> 16) * s1[1]);
-  r.w = pack2(bf16_val(u.w & 0xffffu) * s1[2], bf16_val(u.w >> 16) * s1[3]);
-  return __builtin_bit_cast(bf16x8, r);
+// One thread's share of the decay-scaled g tile of a chunk:
+// GS[j][r] = bf16(g_j[r] e(l_last - l_j)(-eta_j)) for 4 consecutive r.
+template <int D>
+__device__ __forceinline__ void scale_g(const Slot<D>& sl, __bf16* GS, uint32_t off, int row) {
+  const uint2 v = *reinterpret_cast<const uint2*>(reinterpret_cast<const char*>(sl.G) + off);
+  const float s = sl.bk[row];
+  uint2 r;
+  r.x = pack2(bf16_val(v.x & 0xffffu) * s, bf16_val(v.x >> 16) * s);
+  r.y = pack2(bf16_val(v.y & 0xffffu) * s, bf16_val(v.y >> 16) * s);
+  *reinterpret_cast<uint2*>(reinterpret_cast<char*>(GS) + off) = r;
 }
 
 template <int D, bool HAS_Y, bool HAS_ST>
 __global__ __launch_bounds__(kNT) void fwd_mfma(FwdArgs a) {
   static_assert(D == 64 || D == 128, "D");
   constexpr int NTILE = D / kTN;
-  constexpr int NS = D / 32;  // 16x16 state blocks per wave
+  constexpr int NS = D / 64;  // 16x16 state blocks per wave
   constexpr int P = kLoadOps<D>;
-  constexpr int S = (HAS_Y ? 2 : 0) + (HAS_ST ? NS : 0);  // stores per wave per chunk
+  constexpr int S = (HAS_Y ? 1 : 0) + (HAS_ST ? NS : 0);  // stores per wave per chunk
   // Each ring slot is a separate LDS object, and every reference to one is
   // static (the chunk loop is unrolled by kRing), so the compiler can tell a
   // slot being read from the slots still being filled and adds no waits.
   __shared__ Slot<D> ring0, ring1, ring2, ring3, ring4;
   __shared__ __bf16 AT_s[2][kC * kC];  // AT[j][i] = A_ij, swizzled, by chunk parity
   __shared__ __bf16 S_s[2][kTN * D];   // D_in of the tile, bf16, swizzled [row][col], by parity
+  __shared__ __bf16 GS_s[2][kC * kTN]; // decay-scaled g tile, swizzled, by chunk parity
   static_assert(kRing == 5, "ring objects");
   Slot<D>* const rs[kRing] = {&ring0, &ring1, &ring2, &ring3, &ring4};
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
   const int g4 = lane >> 4, l16 = lane & 15;
+  const int tb = wave >> 1, rbw = wave & 1;  // this wave's y block / state row block
   // 8 consecutive sequence-heads and all their row tiles share one XCD
   // (work-groups are dealt to the 8 XCDs round-robin), so the x chunk that
   // every tile reads is fetched from HBM once into that XCD's L2.
@@ -191,15 +230,13 @@ __global__ __launch_bounds__(kNT) void fwd_mfma(FwdArgs a) {
   uint16_t* st = HAS_ST ? static_cast<uint16_t*>(a.states) + bh * static_cast<int64_t>(n) * D * D
                         : nullptr;
 
-  // W0 rows of the tile as MFMA A fragments, held in registers throughout
-  bf16x8 wf[2][D / 32];
+  // W0 rows of this wave's row block as MFMA A fragments, in registers throughout
+  bf16x8 wf[D / 32];
   if (HAS_Y) {
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-      for (int kb = 0; kb < D / 32; ++kb)
-        wf[rb][kb] = *reinterpret_cast<const bf16x8*>(
-            W0 + static_cast<int64_t>(r0 + rb * 16 + l16) * D + kb * 32 + 8 * g4);
+    for (int kb = 0; kb < D / 32; ++kb)
+      wf[kb] = *reinterpret_cast<const bf16x8*>(
+          W0 + static_cast<int64_t>(r0 + rbw * 16 + l16) * D + kb * 32 + 8 * g4);
   }
   for (int idx = tid; idx < kTN * D / 8; idx += kNT)
     reinterpret_cast<uint4*>(S_s[0])[idx] = make_uint4(0, 0, 0, 0);
@@ -211,20 +248,24 @@ __global__ __launch_bounds__(kNT) void fwd_mfma(FwdArgs a) {
   const auto cv_of = [&](int c) {
     return static_cast<int>(std::min<int64_t>(kC, T - static_cast<int64_t>(c) * kC));
   };
-
+  const LaneOff<D> oX = lane_off<D>(lane);
+  const LaneOff<kTN> oG = lane_off<kTN>(lane);
+  const LaneOff<kC> oA = lane_off<kC>(lane);
   const DmaOff<D> od = dma_off<D>(wave, lane);
-  const __amdgpu_buffer_rsrc_t r_none = buffer_rsrc(y ? static_cast<const void*>(y) : a.x, 0);
   // per-lane byte offsets of the stores (loop invariant; the buffer base
   // moves per chunk and its byte count drops rows past the sequence end)
-  uint32_t oy[2], os[NS];
-#pragma unroll
-  for (int rb = 0; rb < 2; ++rb)
-    oy[rb] = static_cast<uint32_t>(((wave * 16 + l16) * D + r0 + rb * 16 + 4 * g4) * 2);
+  const uint32_t oy = static_cast<uint32_t>(((tb * 16 + l16) * D + r0 + rbw * 16 + 4 * g4) * 2);
+  uint32_t os[NS];
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
-    const int b = wave + 4 * s, cb = b >> 1, rb = b & 1;
-    os[s] = static_cast<uint32_t>(((r0 + rb * 16 + l16) * D + cb * 16 + 4 * g4) * 2);
+    const int cb = tb + 4 * s;
+    os[s] = static_cast<uint32_t>(((r0 + rbw * 16 + l16) * D + cb * 16 + 4 * g4) * 2);
   }
+  const __amdgpu_buffer_rsrc_t r_none = buffer_rsrc(a.x, 0);
+  // this thread's 4 elements of the scaled g tile: row tid/8, columns 4 (tid%8)..
+  const int gs_row = tid >> 3;
+  const uint32_t gs_off = static_cast<uint32_t>(sidx<kTN>(gs_row, 4 * (tid & 7)) * 2);
+
   // Initial loads, each followed by S stores into a zero-byte buffer (they
   // are dropped) so that the vector-memory instruction stream has the same
   // shape as in the loop: chunk load, S stores, chunk load, ...  Then the
@@ -236,18 +277,21 @@ __global__ __launch_bounds__(kNT) void fwd_mfma(FwdArgs a) {
     if (HAS_ST)
 #pragma unroll
       for (int s = 0; s < NS; ++s) store8(r_none, os[s] + k, make_uint2(0, 0));
-    if (HAS_Y)
-#pragma unroll
-      for (int rb = 0; rb < 2; ++rb) store8(r_none, oy[rb] + k, make_uint2(0, 0));
+    if (HAS_Y) store8(r_none, oy + k, make_uint2(0, 0));
   }
-  // chunk 0 done: after it come kRing - 2 more chunk loads and kRing - 1 store groups
-  wait_vm<(kRing - 2) * P + (kRing - 1) * S>();
+  // chunks 0 and 1 done: after chunk 1 come two more chunk loads and three store groups
+  wait_vm<2 * P + 3 * S>();
   lds_barrier();
-  const LaneOff<D> oX = lane_off<D>(lane);
-  const LaneOff<kTN> oG = lane_off<kTN>(lane);
-  const LaneOff<kC> oA = lane_off<kC>(lane);
-  float gam = prep_gates<D>(*rs[0], cv_of(0), lane);
-  if (HAS_Y) scores<D>(*rs[0], AT_s[0], oX, oA, wave, lane);
+  if (wave == kPrepWave) {
+    prep_gates<D>(*rs[0], cv_of(0), lane);
+    prep_gates<D>(*rs[1], cv_of(1), lane);
+  }
+  lds_barrier();
+  scale_g<D>(*rs[0], GS_s[0], gs_off, gs_row);
+  if (HAS_Y) {
+    score_block<D>(*rs[0], AT_s[0], oX, oA, wave, lane);
+    if (wave < 2) score_block<D>(*rs[0], AT_s[0], oX, oA, wave + 8, lane);
+  }
 
   f32x4 sacc[NS];
 #pragma unroll
@@ -257,85 +301,73 @@ __global__ __launch_bounds__(kNT) void fwd_mfma(FwdArgs a) {
   const auto step = [&](auto KC, int c) {
     constexpr int K = decltype(KC)::value;
     Slot<D>& cur = *rs[K];
-    Slot<D>& nxt = *rs[(K + 1) % kRing];
+    Slot<D>& nx1 = *rs[(K + 1) % kRing];
+    Slot<D>& nx2 = *rs[(K + 2) % kRing];
     Slot<D>& dst = *rs[(K + kRing - 1) % kRing];
     const int64_t t0 = static_cast<int64_t>(c) * kC;
     const int cv = cv_of(c);
-    const bool more = c + 1 < n;
-    // chunk c + 1 done: issued after it are the stores of its own group and
-    // (kRing - 3) x (chunk load + stores); past the end it is a zero fill
-    wait_vm<(kRing - 3) * P + (kRing - 2) * S>();
-    lds_barrier();  // chunk c + 1 loaded; scores of c, D_in of c, gates of c visible
+    // chunk c + 2 loaded: issued after it are its own store group and one
+    // more (chunk load + stores); past the end it is a zero fill
+    wait_vm<P + 2 * S>();
+    lds_barrier();  // scores and gates of c + 1, D_in of c visible
     issue_chunk<D>(dst, od, x, g, eta, alpha, T, c + kRing - 1, n, r0, wave);
 
     if (HAS_ST) {
-      // chunk-start state of this tile (rows r0.., natural layout, bf16)
-      const __amdgpu_buffer_rsrc_t rs_st = buffer_rsrc(st + static_cast<int64_t>(c) * D * D, D * D * 2);
+      // chunk-start state of this wave's blocks (natural layout, bf16)
+      const __amdgpu_buffer_rsrc_t r_st = buffer_rsrc(st + static_cast<int64_t>(c) * D * D, D * D * 2);
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
         uint2 v;
         v.x = pack2(sacc[s][0], sacc[s][1]);
         v.y = pack2(sacc[s][2], sacc[s][3]);
-        store8(rs_st, os[s], v);
+        store8(r_st, os[s], v);
       }
     }
-
-    float gam_next = 1.f;
-    if (more) {
-      gam_next = prep_gates<D>(nxt, cv_of(c + 1), lane);
-      if (HAS_Y) scores<D>(nxt, AT_s[(c + 1) & 1], oX, oA, wave, lane);
+    if (wave == kPrepWave) prep_gates<D>(nx2, cv_of(c + 2), lane);
+    scale_g<D>(nx1, GS_s[(c + 1) & 1], gs_off, gs_row);
+    if (HAS_Y) {
+      __bf16* AT1 = AT_s[(c + 1) & 1];
+      score_block<D>(nx1, AT1, oX, oA, wave, lane);
+      if (wave < 2) score_block<D>(nx1, AT1, oX, oA, wave + 8, lane);
     }
 
     const __bf16* S_in = S_s[c & 1];
     if (HAS_Y) {
-      // y^T[r][i] for i in this wave's token block, both row blocks; each lane
-      // stores 4 consecutive rows of one token straight from the accumulators
-      const int w = wave;
+      // y^T[r][i] for this wave's block; each lane stores 4 consecutive rows
+      // of one token straight from the accumulators.  (For token blocks 0
+      // and 1 the second K block of A^T is zero.)
       const __bf16* AT = AT_s[c & 1];
-      f32x4 ya[2] = {zero4(), zero4()}, yb[2] = {zero4(), zero4()};
-      for (int kb = 0; kb < (w + 2) / 2; ++kb) {
-        const bf16x8 af = frag_ts<kC>(AT, oA, kb * 32, w * 16);
+      f32x4 ya = zero4(), yb = zero4();
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb)
-          ya[rb] = mfma16x16x32(frag_ts<kTN>(cur.G, oG, kb * 32, rb * 16), af, ya[rb]);
-      }
+      for (int kb = 0; kb < 2; ++kb)
+        ya = mfma16x16x32(frag_ts<kTN>(cur.G, oG, kb * 32, rbw * 16),
+                          frag_ts<kC>(AT, oA, kb * 32, tb * 16), ya);
 #pragma unroll
       for (int kb = 0; kb < D / 32; ++kb) {
-        const bf16x8 xf = frag_s<D>(cur.X, oX, w * 16, kb * 32);
-#pragma unroll
-        for (int rb = 0; rb < 2; ++rb) {
-          ya[rb] = mfma16x16x32(wf[rb][kb], xf, ya[rb]);
-          yb[rb] = mfma16x16x32(frag_s<D>(S_in, oX, rb * 16, kb * 32), xf, yb[rb]);
-        }
+        const bf16x8 xf = frag_s<D>(cur.X, oX, tb * 16, kb * 32);
+        ya = mfma16x16x32(wf[kb], xf, ya);
+        yb = mfma16x16x32(frag_s<D>(S_in, oX, rbw * 16, kb * 32), xf, yb);
       }
-      const int i = w * 16 + l16;
-      const float eqi = fexp2(cur.lq[i]);
+      const float eqi = cur.f.eq[tb * 16 + l16];
       const __amdgpu_buffer_rsrc_t ry = buffer_rsrc(y + t0 * D, cv * D * 2);
-#pragma unroll
-      for (int rb = 0; rb < 2; ++rb) {
-        uint2 pk;
-        pk.x = pack2(ya[rb][0] + eqi * yb[rb][0], ya[rb][1] + eqi * yb[rb][1]);
-        pk.y = pack2(ya[rb][2] + eqi * yb[rb][2], ya[rb][3] + eqi * yb[rb][3]);
-        store8(ry, oy[rb], pk);
-      }
+      uint2 pk;
+      pk.x = pack2(ya[0] + eqi * yb[0], ya[1] + eqi * yb[1]);
+      pk.y = pack2(ya[2] + eqi * yb[2], ya[3] + eqi * yb[3]);
+      store8(ry, oy, pk);
     }
 
     // state update, transposed: D^T[c][r] = Gamma D^T + sum_j x_j[c] (bk_j g_j[r]),
     // into the other state buffer (the current one may still be read)
     {
-      const int rbw = wave & 1;
+      const __bf16* GS = GS_s[c & 1];
       bf16x8 gs[2];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const int k0 = kb * 32 + 8 * g4;
-        gs[kb] = scale8(frag_ts<kTN>(cur.G, oG, kb * 32, rbw * 16),
-                        *reinterpret_cast<const f32x4*>(&cur.bk[k0]),
-                        *reinterpret_cast<const f32x4*>(&cur.bk[k0 + 4]));
-      }
+      for (int kb = 0; kb < 2; ++kb) gs[kb] = frag_ts<kTN>(GS, oG, kb * 32, rbw * 16);
+      const float gam = cur.gam[0];
       __bf16* S_out = S_s[(c + 1) & 1];
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
-        const int cb = (wave >> 1) + 2 * s;
+        const int cb = tb + 4 * s;
         sacc[s] = sacc[s] * gam;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
@@ -346,7 +378,6 @@ __global__ __launch_bounds__(kNT) void fwd_mfma(FwdArgs a) {
         put4<D>(S_out, oX, rbw * 16, cb * 16, pk);
       }
     }
-    gam = gam_next;
   };
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;

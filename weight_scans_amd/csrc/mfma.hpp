@@ -55,19 +55,18 @@ __device__ __forceinline__ bf16x8 frag_t(const __bf16* base, int ld, int k0, int
 
 // ---- swizzled LDS tiles ----
 // A [rows][W] bf16 tile (W in {32, 64, 128}) is stored with its 16-byte
-// column groups XOR-permuted per row, so that both fragment reads above hit
-// every LDS bank once.  The gfx950 LDS has 64 four-byte banks; a 16-byte read
-// is served sixteen lanes at a time (lanes 0-7 with 16-23, 8-15 with 24-31,
-// ...) and the transposing 8-byte read thirty-two consecutive lanes at a time.
-// frag reads rows r0..r0+7 (and +8..15) at two adjacent groups, frag_t reads
-// rows R..R+3 and R+8..R+11 at two adjacent groups; the masks below make the
-// pair index of the group (bits 1..) a bijection of the row bits involved.
+// column groups XOR-permuted per row (mask = swz(row), a linear function of
+// the row's low four bits), so that the fragment reads below and the 8-byte
+// result stores spread over the 64 four-byte LDS banks.  The masks were
+// chosen by measuring SQ_LDS_BANK_CONFLICT on gfx950 for these exact access
+// patterns: frag_s and frag_ts are conflict-free; put4 costs two passes
+// (no row-linear mask does better for that pattern).
 template <int W>
 __device__ __forceinline__ int swz(int r) {
   if constexpr (W == 128)
-    return ((r & 1) << 1) | (((r >> 1) & 1) << 2) | ((((r >> 2) ^ (r >> 3)) & 1) << 3);
+    return (((r & 1) << 2) ^ (((r >> 1) & 1) << 1)) ^ (((r >> 3) & 1) * 9);
   else if constexpr (W == 64)
-    return (((r >> 1) & 1) << 1) | ((((r >> 2) ^ (r >> 3)) & 1) << 2);
+    return (r & 1) | (((r >> 1) & 1) << 1) | (((r >> 3) & 1) << 2);
   else
     return ((r >> 3) & 1) << 1;
 }
@@ -273,6 +272,10 @@ __device__ __forceinline__ void wave_scan_affine(float& a, float& b) {
 __device__ __forceinline__ float wave_reverse(float x, int lane) {
   return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute((63 - lane) << 2,
                                                                  __builtin_bit_cast(int, x)));
+}
+
+__device__ __forceinline__ float readlane_f(float v, int l) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
 }
 
 // Chunk gates, lane = token (one wave, 64 tokens).  Works in log2:
