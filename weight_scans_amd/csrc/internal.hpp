@@ -76,6 +76,8 @@ hipError_t launch_finalize(int io, const FinArgs& a, hipStream_t s);
 constexpr int kMfmaChunk = 64;
 hipError_t launch_mfma_fwd(const FwdArgs& a, hipStream_t s);
 hipError_t launch_mfma_bwd(const BwdArgs& a, hipStream_t s);
+hipError_t launch_mfma_bwd_a(const BwdArgs& a, hipStream_t s);  // row tiles: dg, deta, dW0
+hipError_t launch_mfma_bwd_b(const BwdArgs& a, hipStream_t s);  // column tiles: dx, dalpha
 int mfma_bwd_tiles(int d);
 
 }  // namespace gls

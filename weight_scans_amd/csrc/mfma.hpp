@@ -130,6 +130,13 @@ __device__ __forceinline__ void put4(__bf16* base, const LaneOff<W>& o, int row0
   *reinterpret_cast<uint2*>(p) = v;
 }
 
+// The 8 bytes at the put4 position (4 bf16 of row row0 + l%16, columns c0 + 4*(l/16)..).
+template <int W>
+__device__ __forceinline__ uint2 get4(const __bf16* base, const LaneOff<W>& o, int row0, int c0) {
+  const char* p = reinterpret_cast<const char*>(base) + row0 * W * 2 + (o.w ^ ((c0 >> 3) << 4));
+  return *reinterpret_cast<const uint2*>(p);
+}
+
 // ---- direct global -> LDS loads (no VGPR round trip) ----
 // One wave instruction writes 64 consecutive LDS slots of `size` bytes
 // starting at the wave-uniform `lds`, lane i into slot i, from byte offset
@@ -155,6 +162,10 @@ typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ void store8(__amdgpu_buffer_rsrc_t r, uint32_t voff, const uint2& v) {
   const u32x2_t d = {v.x, v.y};
   __builtin_amdgcn_raw_buffer_store_b64(d, r, voff, 0, 0);
+}
+
+__device__ __forceinline__ void store4(__amdgpu_buffer_rsrc_t r, uint32_t voff, float v) {
+  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, v), r, voff, 0, 0);
 }
 
 // Wait until at most N vector-memory operations of this wave are outstanding
