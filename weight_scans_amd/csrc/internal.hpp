@@ -78,6 +78,7 @@ hipError_t launch_mfma_fwd(const FwdArgs& a, hipStream_t s);
 hipError_t launch_mfma_bwd(const BwdArgs& a, hipStream_t s);
 hipError_t launch_mfma_bwd_a(const BwdArgs& a, hipStream_t s);  // row tiles: dg, deta, dW0
 hipError_t launch_mfma_bwd_b(const BwdArgs& a, hipStream_t s);  // column tiles: dx, dalpha
+hipError_t launch_mfma_bwd_ab64(const BwdArgs& a, hipStream_t s);  // both, one launch, D = 64
 int mfma_bwd_tiles(int d);
 
 }  // namespace gls
