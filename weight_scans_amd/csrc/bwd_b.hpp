@@ -274,29 +274,31 @@ __device__ __forceinline__ void role_b_body(const BwdArgs& a, int64_t bh, int ti
   for (int s = 0; s < NS; ++s) lam[s] = zero4();
   LaneGatesB pg = {1.f, 0.f, 0.f, 0.f, 0.f};  // gates of the previous visit (lane = token)
 
-  // dalpha of the chunk visited before (cn), lane = token i
-  const auto dalpha = [&](int cn, int par, const LaneGatesB& lg, __amdgpu_buffer_rsrc_t r) {
+  // dalpha of the chunk visited before, lane = token i (wave kDaWave only).
+  // The two suffix sums run on the reversed lane order; their inputs are
+  // read from LDS already reversed.
+  const auto dalpha = [&](int par, const LaneGatesB& lg) {
     const float* dt = &dots_s[par][0][0][0];
-    const int i = lane;
-    const float pp = dt[0 * kC + i] + dt[4 * kC + 0 * kC + i];
-    const float rr = dt[1 * kC + i] + dt[4 * kC + 1 * kC + i];
-    const float qq = dt[2 * kC + i] + dt[4 * kC + 2 * kC + i];
-    const float kk = dt[3 * kC + i] + dt[4 * kC + 3 * kC + i];
+    const int i = lane, ir = kC - 1 - lane;
+    const auto both = [&](int kind, int t) { return dt[kind * kC + t] + dt[4 * kC + kind * kC + t]; };
+    const float pp = both(0, i), kk = both(3, i);
+    const float rr_r = both(1, ir), z_r = both(2, ir) - both(3, ir);
     float c0 = 0.f;
 #pragma unroll
     for (int w = 0; w < kNW; ++w) c0 += c0_s[par][w];
+    // sum_{j<i} e(l_{i-1} - l_j) (-eta_j) pp_j: forward affine scan
     float a2 = lg.al, b2 = lg.nb * pp;
     wave_scan_affine(a2, b2);
     const float s2 = wave_shift_up(b2, 0.f);
-    float a3 = wave_reverse(lg.al, lane), b3 = wave_reverse(rr, lane);
+    // sum_{u>i} e(l_{u-1} - l_i) rr_u and sum_{u>i} (qq_u - kk_u): reversed scans
+    const float al_r = wave_reverse(lg.al, lane), lq_r = wave_reverse(lg.lq, lane);
+    float a3 = al_r, b3 = rr_r;
     wave_scan_affine(a3, b3);
-    const float s3 = wave_reverse(wave_shift_up(b3, 0.f), lane);
-    const float qsuf = wave_reverse(wave_shift_up(wave_scan_add(wave_reverse(qq, lane)), 0.f), lane);
-    const float ksuf = wave_reverse(wave_scan_add(wave_reverse(kk, lane)), lane);
-    const float v = fexp2(lg.llast - lg.l + lg.lq) * c0 + fexp2(lg.llast - lg.l) * s2 +
-                    fexp2(lg.lq) * s3 + (qsuf - ksuf) / lg.al;
-    (void)cn;
-    store4(r, opa, v);
+    const float s3_r = wave_shift_up(b3, 0.f);
+    const float zs_r = wave_shift_up(wave_scan_add(z_r), 0.f);
+    const float t34 = wave_reverse(fexp2(lq_r) * s3_r + zs_r * __builtin_amdgcn_rcpf(al_r), lane);
+    return fexp2(lg.llast - lg.l + lg.lq) * c0 + fexp2(lg.llast - lg.l) * s2 + t34 -
+           kk * __builtin_amdgcn_rcpf(lg.al);
   };
 
   const auto step = [&](auto KC, int vis) {
@@ -331,8 +333,7 @@ __device__ __forceinline__ void role_b_body(const BwdArgs& a, int64_t bh, int ti
         const f32x4 sv = unpack4(get4<kT>(cur.Sn, oT, (tb + 4 * s) * 16, cbw * 16));
         p += lam[s][0] * sv[0] + lam[s][1] * sv[1] + lam[s][2] * sv[2] + lam[s][3] * sv[3];
       }
-#pragma unroll
-      for (int m = 1; m < 64; m <<= 1) p += __shfl_xor(p, m, 64);
+      p = wave_sum(p);
       if (lane == 0) c0_s[vis & 1][wave] = p;
     }
     {
@@ -341,10 +342,10 @@ __device__ __forceinline__ void role_b_body(const BwdArgs& a, int64_t bh, int ti
       const bool fin = wave == kDaWave && vis > 0;
       const __amdgpu_buffer_rsrc_t r_pa =
           fin ? buffer_rsrc(pa + static_cast<int64_t>(cn) * kC, cv_of(cn) * 4) : r_none;
-      if (wave == kDaWave)
-        dalpha(cn, (vis + 1) & 1, pg, r_pa);
-      else
-        store4(r_none, opa, 0.f);
+      // the store stays outside the branch (one VMEM stream shape for all waves)
+      float v = 0.f;
+      if (wave == kDaWave) v = dalpha((vis + 1) & 1, pg);
+      store4(r_pa, opa, v);
     }
     pg = lg;
     lds_barrier();  // Be, e(lq) x, gates visible
@@ -383,14 +384,10 @@ __device__ __forceinline__ void role_b_body(const BwdArgs& a, int64_t bh, int ti
         qq += xv[q] * aq[q];
         kk += xv[q] * ak[q];
       }
-      pp += __shfl_xor(pp, 16, 64);
-      pp += __shfl_xor(pp, 32, 64);
-      rr += __shfl_xor(rr, 16, 64);
-      rr += __shfl_xor(rr, 32, 64);
-      qq += __shfl_xor(qq, 16, 64);
-      qq += __shfl_xor(qq, 32, 64);
-      kk += __shfl_xor(kk, 16, 64);
-      kk += __shfl_xor(kk, 32, 64);
+      pp = sum_rows(pp);
+      rr = sum_rows(rr);
+      qq = sum_rows(qq);
+      kk = sum_rows(kk);
       if (g4 == 0) {
         float* dt = &dots_s[vis & 1][cbw][0][0];
         dt[0 * kC + i] = pp;
@@ -429,7 +426,7 @@ __device__ __forceinline__ void role_b_body(const BwdArgs& a, int64_t bh, int ti
   }
   wait_vm<0>();
   lds_barrier();
-  if (wave == kDaWave) dalpha(0, (n - 1) & 1, pg, buffer_rsrc(pa, cv_of(0) * 4));
+  if (wave == kDaWave) store4(buffer_rsrc(pa, cv_of(0) * 4), opa, dalpha((n - 1) & 1, pg));
 }
 
 }  // namespace

@@ -312,8 +312,7 @@ __global__ __launch_bounds__(kNT) void bwd_a(BwdArgs a) {
       const uint2 gv = get4<kT>(cur.Gr, oT, tb * 16, rbw * 16);
       float p = bf16_val(gv.x & 0xffffu) * u[0] + bf16_val(gv.x >> 16) * u[1] +
                 bf16_val(gv.y & 0xffffu) * u[2] + bf16_val(gv.y >> 16) * u[3];
-      p += __shfl_xor(p, 16, 64);
-      p += __shfl_xor(p, 32, 64);
+      p = sum_rows(p);
       if (g4 == 0) red_s[v & 1][rbw][i] = p;
     }
 

@@ -234,8 +234,7 @@ __device__ __forceinline__ void role_a2_body(const BwdArgs& a, int64_t bh, int t
       const uint2 gv = get4<kT>(cur.Gr, oT, tb * 16, rbw * 16);
       float p = bf16_val(gv.x & 0xffffu) * u[0] + bf16_val(gv.x >> 16) * u[1] +
                 bf16_val(gv.y & 0xffffu) * u[2] + bf16_val(gv.y >> 16) * u[3];
-      p += __shfl_xor(p, 16, 64);
-      p += __shfl_xor(p, 32, 64);
+      p = sum_rows(p);
       if (g4 == 0) red_s[vis & 1][rbw][i] = p;
     }
     // Lam^T[c][r] = Gamma Lam^T + sum_u x_u[c] e(lq_u) dy_u[r];  dW0^T += sum_u x_u[c] dy_u[r]

@@ -279,14 +279,52 @@ __device__ __forceinline__ void wave_scan_affine(float& a, float& b) {
   affine_step<kRowBcast31, 0xc>(a, b);
 }
 
-// Lane order reversed (lane i <- lane 63 - i).
-__device__ __forceinline__ float wave_reverse(float x, int lane) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute((63 - lane) << 2,
-                                                                 __builtin_bit_cast(int, x)));
-}
 
 __device__ __forceinline__ float readlane_f(float v, int l) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
+}
+
+// ---- cross-row moves (gfx950 v_permlane16_swap / v_permlane32_swap) ----
+// Rows are the four groups of 16 lanes.  With rows a = [a0 a1 a2 a3] and
+// b = [b0 b1 b2 b3], the 32-lane swap leaves a = [a0 a1 b0 b1],
+// b = [a2 a3 b2 b3]; the 16-lane swap leaves a = [a0 b0 a2 b2],
+// b = [a1 b1 a3 b3] (measured).  Written as VALU assembly with two wait
+// states on either side, because the builtins' second result is not
+// reliable in this compiler.
+__device__ __forceinline__ void permlane32_swap(float& a, float& b) {
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ void permlane16_swap(float& a, float& b) {
+  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+}
+
+// x summed over the four lanes that share lane & 15, in every lane.
+__device__ __forceinline__ float sum_rows(float x) {
+  float a = x, b = x;
+  permlane16_swap(a, b);
+  a += b;
+  float c = a, d = a;
+  permlane32_swap(c, d);
+  return c + d;
+}
+
+constexpr int kRowMirror = 0x140;
+
+// Lane order reversed (lane i <- lane 63 - i): each row mirrored by DPP,
+// then the rows put in reverse order by the two swaps.
+__device__ __forceinline__ float wave_reverse(float x, int lane) {
+  const float y = dpp<kRowMirror>(0.f, x);
+  float a = y, b = y;
+  permlane32_swap(a, b);                 // a = [y0 y1 y0 y1], b = [y2 y3 y2 y3]
+  const float h = lane < 32 ? b : a;     // [y2 y3 y0 y1]
+  float c = h, d = h;
+  permlane16_swap(c, d);                 // c = [h0 h0 h2 h2], d = [h1 h1 h3 h3]
+  return (lane & 16) ? c : d;            // [h1 h0 h3 h2] = [y3 y2 y1 y0]
+}
+
+// Sum over the 64 lanes (every lane).
+__device__ __forceinline__ float wave_sum(float x) {
+  return readlane_f(wave_scan_add(x), 63);
 }
 
 // Chunk gates, lane = token (one wave, 64 tokens).  Works in log2:
