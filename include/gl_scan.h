@@ -77,7 +77,11 @@ typedef struct {
   int32_t io_dtype;     /* gl_dtype_t                                          */
   int32_t chunk;        /* tokens per chunk; 0 = default of the chosen kernels */
   uint32_t flags;       /* GL_FLAG_*                                           */
-  uint32_t reserved;    /* must be 0                                           */
+  uint32_t segments;    /* matrix-core kernels: 0 = automatic (long sequences
+                           with few heads are cut into segments so that a pass
+                           fills the GPU), 1 = one segment per sequence, n > 1
+                           = n segments (at most one per chunk); the generic
+                           kernels take 0 or 1 only                         */
 } gl_scan_desc_t;
 
 /* Bytes of the optional `saved` buffer that gl_scan_fwd can fill with chunk-
@@ -87,7 +91,9 @@ gl_status_t gl_scan_saved_size(const gl_scan_desc_t* desc, size_t* saved_bytes);
 
 /* Workspace bytes for gl_scan_fwd and gl_scan_bwd.  have_saved != 0: the bwd
  * call will receive the fwd's `saved` buffer; 0: the bwd recomputes the
- * chunk-boundary states itself inside the workspace. */
+ * chunk-boundary states itself inside the workspace.  The fwd needs a
+ * workspace only when the sequences are cut into segments (0 bytes
+ * otherwise; ws may then be NULL). */
 gl_status_t gl_scan_workspace_size(const gl_scan_desc_t* desc, int have_saved,
                                    size_t* fwd_ws_bytes, size_t* bwd_ws_bytes);
 

@@ -41,12 +41,13 @@ def to_device(inp: dict, io: str, device="cuda"):
     return out
 
 
-def run_gpu(dev: dict, chunk=0, flags=0, use_saved=True):
+def run_gpu(dev: dict, chunk=0, flags=0, use_saved=True, segments=0):
     """Forward then backward through the C ABI; returns device tensors."""
     y, saved = gl_scan_fwd(dev["x"], dev["g"], dev["eta"], dev["alpha"], dev["W0"],
-                           chunk=chunk, flags=flags, save=use_saved)
+                           chunk=chunk, flags=flags, save=use_saved, segments=segments)
     grads = gl_scan_bwd(dev["x"], dev["g"], dev["eta"], dev["alpha"], dev["W0"], dev["dy"],
-                        saved if use_saved else None, chunk=chunk, flags=flags)
+                        saved if use_saved else None, chunk=chunk, flags=flags,
+                        segments=segments)
     torch.cuda.synchronize()
     return dict(zip(NAMES, (y,) + tuple(grads)))
 

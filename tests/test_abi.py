@@ -51,6 +51,8 @@ def test_status_strings():
     (dict(flags=8), 1), (dict(chunk=-1), 1),
     (dict(d_in=129), 2), (dict(d_out=256), 2), (dict(chunk=48), 2),
     (dict(io_dtype=ws.GL_DTYPE_F64, chunk=32), 2),
+    (dict(segments=1 << 21), 1), (dict(io_dtype=ws.GL_DTYPE_F32, segments=2), 2),
+    (dict(flags=ws.GL_FLAG_GENERIC, segments=3), 2),
 ])
 def test_descriptor_validation(kw, code):
     d = desc(**kw)
@@ -71,6 +73,25 @@ def test_sizes_are_consistent():
     f0, b0 = ws.workspace_size(d, False)
     assert s > 0 and b0 >= b1 + s - 256 and f0 == f1
     assert ws.path_name(d)
+
+
+def test_segment_workspace():
+    # one segment: the forward needs no workspace
+    f, _ = ws.workspace_size(desc(T=4096, segments=1), True)
+    assert f == 0
+    # n segments: n fp32 states per sequence-head (+ their log-decays)
+    f4, b4 = ws.workspace_size(desc(T=4096, segments=4), True)
+    _, b1 = ws.workspace_size(desc(T=4096, segments=1), True)
+    assert f4 >= 2 * 3 * 4 * 64 * 64 * 4 and b4 > b1
+    # automatic: few heads and a long sequence are cut into segments, many
+    # heads are not
+    fa, _ = ws.workspace_size(desc(B=1, H=2, T=1 << 15), True)
+    assert fa > 0
+    fb, _ = ws.workspace_size(desc(B=8, H=16, T=4096), True)
+    assert fb == 0
+    # never more segments than chunks
+    fc, _ = ws.workspace_size(desc(T=100, segments=50), True)
+    assert fc == ws.workspace_size(desc(T=100, segments=2), True)[0]
 
 
 FAKE = 0x10000  # 16-byte aligned, never dereferenced
@@ -100,6 +121,16 @@ def test_fwd_argument_errors_before_launch():
     bad_saved[6] = FAKE + 8
     assert _fwd(d, bad_saved) == 3
     assert b"aligned" in ws.lib().gl_last_error()
+
+
+def test_fwd_segment_workspace_errors_before_launch():
+    d = desc(T=4096, segments=4)
+    need, _ = ws.workspace_size(d, True)
+    P = [ctypes.c_void_p(FAKE)] * 6 + [None]
+    L = ws.lib()
+    assert L.gl_scan_fwd(ctypes.byref(d), *P, ctypes.c_void_p(FAKE), need - 1, None) == 4
+    assert L.gl_scan_fwd(ctypes.byref(d), *P, None, need, None) == 1
+    assert L.gl_scan_fwd(ctypes.byref(d), *P, ctypes.c_void_p(FAKE + 4), need, None) == 3
 
 
 def test_bwd_argument_errors_before_launch():

@@ -97,6 +97,34 @@ def test_edge_shapes(io, B, H, T, di, do):
     _full_case(Workload("edge", B, H, T, di, do, io, "mix", "gauss", 500 + T + di))
 
 
+# Segmented scan (sequences cut into segments scanned by separate work-groups,
+# then combined): 8 chunks with a ragged tail; 3 segments start at an odd
+# chunk, 5 requested give 4 of 2 chunks, 8 give one chunk each.
+SEGMENTED = [(64, 3), (64, 5), (64, 8), (128, 3), (128, 5), (128, 8)]
+
+
+@pytest.mark.parametrize("d,segments", SEGMENTED)
+def test_segments_full(d, segments):
+    w = Workload("seg", 1, 2, 64 * 7 + 13, d, d, "bf16", "mix", "unit", 700 + d + segments)
+    _full_case(w, segments=segments)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_segments_recompute_path(d):
+    w = Workload("segr", 2, 1, 64 * 9 + 1, d, d, "bf16", "mix", "unit", 800 + d)
+    _full_case(w, segments=4, use_saved=False)
+
+
+def test_segments_and_none_agree():
+    """The same inputs with and without segments: both within the bf16
+    tolerance of the oracle, and close to each other."""
+    w = Workload("segs", 1, 2, 64 * 16, 64, 64, "bf16", "mix", "unit", 901)
+    gpu1, ref = _full_case(w, segments=1)
+    gpu4, _ = _full_case(w, segments=4)
+    for n in NAMES:
+        assert relmax(host(gpu4[n]), host(gpu1[n])) < TOL["bf16"], n
+
+
 @pytest.mark.parametrize("io", ["f64", "f32", "bf16"])
 def test_identity_gates(io):
     """alpha = 1, eta = 0: y = W0 x and no adaptation gradients."""

@@ -44,7 +44,7 @@ class Desc(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int64), ("H", ctypes.c_int64), ("T", ctypes.c_int64),
                 ("d_in", ctypes.c_int64), ("d_out", ctypes.c_int64),
                 ("io_dtype", ctypes.c_int32), ("chunk", ctypes.c_int32),
-                ("flags", ctypes.c_uint32), ("reserved", ctypes.c_uint32)]
+                ("flags", ctypes.c_uint32), ("segments", ctypes.c_uint32)]
 
 
 _lib = None
@@ -82,8 +82,9 @@ def _check(status: int):
         raise GLScanError(status, lib().gl_last_error().decode())
 
 
-def make_desc(B, H, T, d_in, d_out, io_dtype, chunk=0, flags=0) -> Desc:
-    return Desc(B, H, T, d_in, d_out, io_dtype, chunk, flags, 0)
+def make_desc(B, H, T, d_in, d_out, io_dtype, chunk=0, flags=0, segments=0) -> Desc:
+    """segments: 0 = automatic, 1 = none, n = n segments per sequence."""
+    return Desc(B, H, T, d_in, d_out, io_dtype, chunk, flags, segments)
 
 
 def path_name(desc: Desc) -> str | None:
@@ -155,11 +156,11 @@ def _validate(x, g, eta, alpha, W0, dy=None):
     return B, H, T, d_in, d_out
 
 
-def gl_scan_fwd(x, g, eta, alpha, W0, *, chunk=0, flags=0, save=True):
+def gl_scan_fwd(x, g, eta, alpha, W0, *, chunk=0, flags=0, save=True, segments=0):
     """Forward scan.  Returns (y, saved) where saved is None if save=False."""
     torch = _torch()
     B, H, T, d_in, d_out = _validate(x, g, eta, alpha, W0)
-    desc = make_desc(B, H, T, d_in, d_out, _io_code(x.dtype), chunk, flags)
+    desc = make_desc(B, H, T, d_in, d_out, _io_code(x.dtype), chunk, flags, segments)
     y = torch.empty((B, H, T, d_out), dtype=x.dtype, device=x.device)
     saved = None
     if save:
@@ -172,11 +173,11 @@ def gl_scan_fwd(x, g, eta, alpha, W0, *, chunk=0, flags=0, save=True):
     return y, saved
 
 
-def gl_scan_bwd(x, g, eta, alpha, W0, dy, saved=None, *, chunk=0, flags=0):
+def gl_scan_bwd(x, g, eta, alpha, W0, dy, saved=None, *, chunk=0, flags=0, segments=0):
     """Reverse scan.  Returns (dx, dg, deta, dalpha, dW0)."""
     torch = _torch()
     B, H, T, d_in, d_out = _validate(x, g, eta, alpha, W0, dy)
-    desc = make_desc(B, H, T, d_in, d_out, _io_code(x.dtype), chunk, flags)
+    desc = make_desc(B, H, T, d_in, d_out, _io_code(x.dtype), chunk, flags, segments)
     gd = gate_dtype(x.dtype)
     dx = torch.empty_like(x)
     dg = torch.empty_like(g)

@@ -201,9 +201,11 @@ struct SmemB {
   float* c0;          // [2][kNW]       <Lam_out, D_in> partials by parity, wave
 };
 
-// The column-tile pass for sequence-head bh, column tile `tile`.
+// The column-tile pass for sequence-head bh, column tile `tile`, segment
+// `seg` (its chunks visited from the last; Lam entering from the right is
+// seg_lam, or zero).
 template <int D>
-__device__ __forceinline__ void role_b_body(const BwdArgs& a, int64_t bh, int tile,
+__device__ __forceinline__ void role_b_body(const BwdArgs& a, int64_t bh, int tile, int seg,
                                             const SmemB<D>& m) {
   static_assert(D == 64 || D == 128, "D");
   constexpr int NS = D / 64;  // 16x16 Lam blocks per wave
@@ -224,6 +226,9 @@ __device__ __forceinline__ void role_b_body(const BwdArgs& a, int64_t bh, int ti
   const int h = static_cast<int>(bh % a.H);
   const int64_t T = a.T, BHT = a.B * a.H * T;
   const int n = a.n_chunks;
+  const int c_beg = seg * a.seg_chunks;
+  const int c_end = std::min(n, c_beg + a.seg_chunks);
+  const int nloc = c_end - c_beg;
   const uint16_t* x = static_cast<const uint16_t*>(a.x) + bh * T * D;
   const uint16_t* g = static_cast<const uint16_t*>(a.g) + bh * T * D;
   const uint16_t* dy = static_cast<const uint16_t*>(a.dy) + bh * T * D;
@@ -244,8 +249,6 @@ __device__ __forceinline__ void role_b_body(const BwdArgs& a, int64_t bh, int ti
     *reinterpret_cast<uint4*>(&L_s[1][sidx<kT>(r, cc)]) =
         *reinterpret_cast<const uint4*>(W0 + static_cast<int64_t>(r) * D + k0 + cc);
   }
-  for (int idx = tid; idx < D * kT / 8; idx += kNT)
-    reinterpret_cast<uint4*>(L_s[0])[idx] = make_uint4(0, 0, 0, 0);
   for (int idx = tid; idx < kC * kC / 8; idx += kNT)
     reinterpret_cast<uint4*>(&BeT_s[0])[idx] = make_uint4(0, 0, 0, 0);
   __syncthreads();
@@ -254,8 +257,33 @@ __device__ __forceinline__ void role_b_body(const BwdArgs& a, int64_t bh, int ti
   for (int kb = 0; kb < D / 32; ++kb) w0f[kb] = frag_ts<kT>(L_s[1], oT, kb * 32, cbw * 16);
   __syncthreads();
 
+  // Lam columns of the tile entering from the right (fp32 accumulators, and
+  // the bf16 copy read by the first visit)
+  f32x4 lam[NS];
+  if (a.seg_lam) {
+    const float* sl = a.seg_lam + (bh * a.n_seg + seg) * D * D;
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+      lam[s] = *reinterpret_cast<const f32x4*>(sl + ((tb + 4 * s) * 16 + l16) * D + k0 +
+                                               cbw * 16 + 4 * g4);
+  } else {
+#pragma unroll
+    for (int s = 0; s < NS; ++s) lam[s] = zero4();
+  }
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    uint2 pk;
+    pk.x = pack2(lam[s][0], lam[s][1]);
+    pk.y = pack2(lam[s][2], lam[s][3]);
+    put4<kT>(L_s[0], oT, (tb + 4 * s) * 16, cbw * 16, pk);
+  }
+  wait_vm<0>();
+
+  // valid tokens of chunk c (none outside this segment)
   const auto cv_of = [&](int c) {
-    return c < 0 ? 0 : static_cast<int>(std::min<int64_t>(kC, T - static_cast<int64_t>(c) * kC));
+    return (c < c_beg || c >= c_end)
+               ? 0
+               : static_cast<int>(std::min<int64_t>(kC, T - static_cast<int64_t>(c) * kC));
   };
   const DmaOffB<D> od = dma_off_b<D>(wave, lane);
   const uint32_t odx = static_cast<uint32_t>(((tb * 16 + l16) * D + k0 + cbw * 16 + 4 * g4) * 2);
@@ -265,13 +293,9 @@ __device__ __forceinline__ void role_b_body(const BwdArgs& a, int64_t bh, int ti
   const uint32_t xs_off = static_cast<uint32_t>(sidx<kT>(xs_row, 4 * (tid & 7)) * 2);
 
   // the last chunk, followed by S dropped stores (stream shape as in the loop)
-  issue_chunk_b<D>(*rs[0], od, dy, g, x, st, eta, alpha, T, n - 1, k0, wave);
+  issue_chunk_b<D>(*rs[0], od, dy, g, x, st, eta, alpha, T, c_end - 1, k0, wave);
   store8(r_none, odx, make_uint2(0, 0));
   store4(r_none, opa, 0.f);
-
-  f32x4 lam[NS];
-#pragma unroll
-  for (int s = 0; s < NS; ++s) lam[s] = zero4();
   LaneGatesB pg = {1.f, 0.f, 0.f, 0.f, 0.f};  // gates of the previous visit (lane = token)
 
   // dalpha of the chunk visited before, lane = token i (wave kDaWave only).
@@ -305,12 +329,12 @@ __device__ __forceinline__ void role_b_body(const BwdArgs& a, int64_t bh, int ti
     constexpr int K = decltype(KC)::value;
     SlotB<D>& cur = *rs[K];
     SlotB<D>& dst = *rs[K ^ 1];
-    const int c = n - 1 - vis;
+    const int c = c_end - 1 - vis;
     const int64_t t0 = static_cast<int64_t>(c) * kC;
     const int cv = cv_of(c);
     wait_vm<S>();   // chunk c loaded: after it only the previous visit's stores
     lds_barrier();  // and the previous visit's reads of the other slot are done
-    issue_chunk_b<D>(dst, od, dy, g, x, st, eta, alpha, T, c - 1, k0, wave);
+    issue_chunk_b<D>(dst, od, dy, g, x, st, eta, alpha, T, c - 1 >= c_beg ? c - 1 : -1, k0, wave);
 
     // ---- phase 1
     const LaneGatesB lg = gates_b<D>(cur, gs, cv, lane);
@@ -419,14 +443,16 @@ __device__ __forceinline__ void role_b_body(const BwdArgs& a, int64_t bh, int ti
   };
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
-  for (int vis = 0; vis < n; vis += 2) {
+  for (int vis = 0; vis < nloc; vis += 2) {
     step(I0{}, vis);
-    if (vis + 1 >= n) break;
+    if (vis + 1 >= nloc) break;
     step(I1{}, vis + 1);
   }
   wait_vm<0>();
   lds_barrier();
-  if (wave == kDaWave) store4(buffer_rsrc(pa, cv_of(0) * 4), opa, dalpha((n - 1) & 1, pg));
+  if (wave == kDaWave)
+    store4(buffer_rsrc(pa + static_cast<int64_t>(c_beg) * kC, cv_of(c_beg) * 4), opa,
+           dalpha((nloc - 1) & 1, pg));
 }
 
 }  // namespace

@@ -34,6 +34,12 @@ gl_status_t fail(gl_status_t st, const char* fmt, ...) {
 constexpr size_t kAlign = 256;
 size_t round_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
+// Automatic segmenting: when one pass has fewer work-groups than the GPU has
+// compute units (256 on MI355X), each sequence is cut into segments of at
+// least kMinSegChunks chunks so that the pass fills the chip.
+constexpr int64_t kSegTargetGroups = 256;
+constexpr int kMinSegChunks = 16;
+
 // Everything the launches need, derived from the descriptor alone so that the
 // forward and the backward agree on the layout of `saved`.
 struct Plan {
@@ -44,7 +50,10 @@ struct Plan {
   size_t saved_bytes = 0;   // chunk-boundary states
   size_t state_elem = 4;    // bytes per stored state element
   size_t part_bytes = 0;    // deta + dalpha partials
-  size_t dw_bytes = 0;      // dW0 partials (per batch entry)
+  size_t dw_bytes = 0;      // dW0 partials (per batch entry, per segment)
+  int n_seg = 1, seg_chunks = 0;
+  size_t seg_bytes = 0;     // per-segment states (fp32) + summed log2 alpha
+  size_t seg_state_bytes = 0;
   const char* name = "";
 };
 
@@ -57,8 +66,8 @@ gl_status_t make_plan(const gl_scan_desc_t* d, Plan* p) {
     return fail(GL_ERROR_INVALID_VALUE, "d_in and d_out must be >= 1");
   if (d->io_dtype < GL_DTYPE_F64 || d->io_dtype > GL_DTYPE_BF16)
     return fail(GL_ERROR_INVALID_VALUE, "unknown io_dtype %d", d->io_dtype);
-  if (d->reserved != 0 || (d->flags & ~GL_FLAG_GENERIC) != 0)
-    return fail(GL_ERROR_INVALID_VALUE, "unknown flags or nonzero reserved field");
+  if ((d->flags & ~GL_FLAG_GENERIC) != 0) return fail(GL_ERROR_INVALID_VALUE, "unknown flags");
+  if (d->segments > (1u << 20)) return fail(GL_ERROR_INVALID_VALUE, "segments above 2^20");
   if (d->chunk < 0) return fail(GL_ERROR_INVALID_VALUE, "negative chunk");
   if (d->d_in > gls::kGenericMaxD || d->d_out > gls::kGenericMaxD)
     return fail(GL_ERROR_NOT_SUPPORTED, "d_in/d_out above %d", gls::kGenericMaxD);
@@ -87,18 +96,39 @@ gl_status_t make_plan(const gl_scan_desc_t* d, Plan* p) {
     p->name = (p->io == GL_DTYPE_F64) ? "generic-f64"
               : (p->io == GL_DTYPE_F32) ? "generic-f32" : "generic-bf16";
     p->state_elem = p->comp;
+    if (d->segments > 1)
+      return fail(GL_ERROR_NOT_SUPPORTED, "segments apply to the matrix-core kernels only");
   }
   p->n_chunks = static_cast<int>((d->T + p->chunk - 1) / p->chunk);
+  int nseg = 1;
+  if (p->mfma && p->n_chunks > 0) {
+    const int64_t groups = static_cast<int64_t>(BH) * (d->d_in / 32);
+    if (d->segments > 0) {
+      nseg = static_cast<int>(d->segments);
+    } else if (groups > 0 && groups < kSegTargetGroups) {
+      nseg = static_cast<int>(std::min<int64_t>((kSegTargetGroups + groups - 1) / groups,
+                                                p->n_chunks / kMinSegChunks));
+    }
+    nseg = std::max(1, std::min(nseg, p->n_chunks));
+  }
+  p->seg_chunks = p->n_chunks > 0 ? (p->n_chunks + nseg - 1) / nseg : 0;
+  p->n_seg = p->seg_chunks > 0 ? (p->n_chunks + p->seg_chunks - 1) / p->seg_chunks : 1;
+  if (p->n_seg > 1) {
+    p->seg_state_bytes = round_up(BH * p->n_seg * dd * sizeof(float));
+    p->seg_bytes = p->seg_state_bytes + round_up(BH * p->n_seg * sizeof(float));
+  }
   p->ckpt_every = 1;
   p->n_ckpt = p->n_chunks;
   p->saved_bytes = round_up(BH * p->n_ckpt * dd * p->state_elem);
   p->part_bytes = round_up(static_cast<size_t>(p->n_tiles) * BH * d->T * p->comp);
-  p->dw_bytes = round_up(BH * dd * p->comp);
+  p->dw_bytes = round_up(BH * dd * p->comp * p->n_seg);
   return GL_SUCCESS;
 }
 
+// bwd workspace: deta / dalpha partials, dW0 partials, segment buffers (also
+// used by the state recompute, which runs first), recomputed states
 size_t bwd_ws(const Plan& p, bool have_saved) {
-  return 2 * p.part_bytes + p.dw_bytes + (have_saved ? 0 : p.saved_bytes);
+  return 2 * p.part_bytes + p.dw_bytes + p.seg_bytes + (have_saved ? 0 : p.saved_bytes);
 }
 
 bool misaligned(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) != 0; }
@@ -117,12 +147,30 @@ gls::FwdArgs fwd_args(const gl_scan_desc_t* d, const Plan& p, const void* x, con
   a.B = d->B; a.H = d->H; a.T = d->T;
   a.d_in = static_cast<int>(d->d_in); a.d_out = static_cast<int>(d->d_out);
   a.chunk = p.chunk; a.n_chunks = p.n_chunks; a.ckpt_every = p.ckpt_every; a.n_ckpt = p.n_ckpt;
+  a.seg_chunks = p.seg_chunks; a.n_seg = p.n_seg;
   return a;
 }
 
-hipError_t launch_fwd(const Plan& p, const gls::FwdArgs& a, hipStream_t s) {
-  if (p.mfma) return gls::launch_mfma_fwd(a, s);
-  return gls::launch_generic_fwd(p.io, a, s);
+// The forward scan.  With segments (a buffer of p.seg_bytes at seg_ws): a
+// state-only pass per segment from a zero start, the exclusive affine scan
+// over segments, then the full pass per segment from its incoming state.
+hipError_t launch_fwd(const Plan& p, const gls::FwdArgs& a, void* seg_ws, hipStream_t s) {
+  if (!p.mfma) return gls::launch_generic_fwd(p.io, a, s);
+  if (p.n_seg <= 1) return gls::launch_mfma_fwd(a, s);
+  float* seg = static_cast<float*>(seg_ws);
+  float* lg = reinterpret_cast<float*>(static_cast<char*>(seg_ws) + p.seg_state_bytes);
+  gls::FwdArgs a1 = a;
+  a1.y = nullptr;
+  a1.states = nullptr;
+  a1.seg_out = seg;
+  a1.seg_lg = lg;
+  hipError_t e = gls::launch_mfma_fwd(a1, s);
+  if (e != hipSuccess) return e;
+  e = gls::launch_seg_combine(seg, lg, a.B * a.H, p.n_seg, a.d_in * a.d_out, false, s);
+  if (e != hipSuccess) return e;
+  gls::FwdArgs a3 = a;
+  a3.seg_in = seg;
+  return gls::launch_mfma_fwd(a3, s);
 }
 
 }  // namespace
@@ -143,7 +191,7 @@ gl_status_t gl_scan_workspace_size(const gl_scan_desc_t* desc, int have_saved,
   Plan p;
   gl_status_t st = make_plan(desc, &p);
   if (st != GL_SUCCESS) return st;
-  if (fwd_ws_bytes) *fwd_ws_bytes = 0;
+  if (fwd_ws_bytes) *fwd_ws_bytes = p.seg_bytes;
   if (bwd_ws_bytes) *bwd_ws_bytes = bwd_ws(p, have_saved != 0);
   return GL_SUCCESS;
 }
@@ -151,8 +199,6 @@ gl_status_t gl_scan_workspace_size(const gl_scan_desc_t* desc, int have_saved,
 gl_status_t gl_scan_fwd(const gl_scan_desc_t* desc, const void* x, const void* g,
                         const void* eta, const void* alpha, const void* W0, void* y,
                         void* saved, void* ws, size_t ws_bytes, void* stream) {
-  (void)ws;
-  (void)ws_bytes;
   Plan p;
   gl_status_t st = make_plan(desc, &p);
   if (st != GL_SUCCESS) return st;
@@ -162,8 +208,15 @@ gl_status_t gl_scan_fwd(const gl_scan_desc_t* desc, const void* x, const void* g
   for (const void* q : {x, g, eta, alpha, W0, static_cast<const void*>(y),
                         static_cast<const void*>(saved)})
     if (q && misaligned(q)) return fail(GL_ERROR_MISALIGNED, "pointer %p not 16-byte aligned", q);
+  if (p.seg_bytes > 0) {
+    if (!ws) return fail(GL_ERROR_INVALID_VALUE, "workspace is NULL");
+    if (misaligned(ws)) return fail(GL_ERROR_MISALIGNED, "workspace not 16-byte aligned");
+    if (ws_bytes < p.seg_bytes)
+      return fail(GL_ERROR_WORKSPACE_TOO_SMALL, "workspace %zu bytes, need %zu", ws_bytes,
+                  p.seg_bytes);
+  }
   hipStream_t s = static_cast<hipStream_t>(stream);
-  return hip_status(launch_fwd(p, fwd_args(desc, p, x, g, eta, alpha, W0, y, saved), s),
+  return hip_status(launch_fwd(p, fwd_args(desc, p, x, g, eta, alpha, W0, y, saved), ws, s),
                     "forward launch");
 }
 
@@ -199,11 +252,13 @@ gl_status_t gl_scan_bwd(const gl_scan_desc_t* desc, const void* x, const void* g
   void* part_eta = w;
   void* part_alpha = w + p.part_bytes;
   void* part_dW0 = w + 2 * p.part_bytes;
+  char* seg_ws = w + 2 * p.part_bytes + p.dw_bytes;
   const void* states = saved;
   if (!states) {
-    void* rec = w + 2 * p.part_bytes + p.dw_bytes;
-    st = hip_status(launch_fwd(p, fwd_args(desc, p, x, g, eta, alpha, W0, nullptr, rec), s),
-                    "state recompute launch");
+    void* rec = seg_ws + p.seg_bytes;
+    st = hip_status(
+        launch_fwd(p, fwd_args(desc, p, x, g, eta, alpha, W0, nullptr, rec), seg_ws, s),
+        "state recompute launch");
     if (st != GL_SUCCESS) return st;
     states = rec;
   }
@@ -215,15 +270,38 @@ gl_status_t gl_scan_bwd(const gl_scan_desc_t* desc, const void* x, const void* g
   b.d_in = static_cast<int>(desc->d_in); b.d_out = static_cast<int>(desc->d_out);
   b.chunk = p.chunk; b.n_chunks = p.n_chunks; b.ckpt_every = p.ckpt_every; b.n_ckpt = p.n_ckpt;
   b.n_tiles = p.n_tiles;
-  st = hip_status(p.mfma ? gls::launch_mfma_bwd(b, s) : gls::launch_generic_bwd(p.io, b, s),
-                  "backward launch");
+  b.seg_chunks = p.seg_chunks; b.n_seg = p.n_seg;
+  if (!p.mfma) {
+    st = hip_status(gls::launch_generic_bwd(p.io, b, s), "backward launch");
+  } else if (p.n_seg <= 1) {
+    st = hip_status(gls::launch_mfma_bwd(b, s), "backward launch");
+  } else {
+    // segments: adjoint-only pass per segment from a zero start at its right
+    // end, the exclusive affine scan over segments from the right, then the
+    // full pass per segment from its incoming adjoint
+    float* seg = reinterpret_cast<float*>(seg_ws);
+    float* lg = reinterpret_cast<float*>(seg_ws + p.seg_state_bytes);
+    gls::BwdArgs b1 = b;
+    b1.seg_out = seg;
+    b1.seg_lg = lg;
+    st = hip_status(gls::launch_mfma_bwd_lam(b1, s), "backward segment pass");
+    if (st == GL_SUCCESS)
+      st = hip_status(gls::launch_seg_combine(seg, lg, b.B * b.H, p.n_seg, b.d_in * b.d_out, true,
+                                              s),
+                      "segment combine");
+    if (st == GL_SUCCESS) {
+      gls::BwdArgs b3 = b;
+      b3.seg_lam = seg;
+      st = hip_status(gls::launch_mfma_bwd(b3, s), "backward launch");
+    }
+  }
   if (st != GL_SUCCESS) return st;
 
   gls::FinArgs f;
   f.part_eta = part_eta; f.part_alpha = part_alpha; f.part_dW0 = part_dW0;
   f.deta = deta; f.dalpha = dalpha; f.dW0 = dW0;
   f.B = desc->B; f.H = desc->H; f.T = desc->T;
-  f.d_in = b.d_in; f.d_out = b.d_out; f.n_tiles = p.n_tiles;
+  f.d_in = b.d_in; f.d_out = b.d_out; f.n_tiles = p.n_tiles; f.n_seg = p.n_seg;
   return hip_status(gls::launch_finalize(p.io, f, s), "finalize launch");
 }
 

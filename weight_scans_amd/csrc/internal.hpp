@@ -27,6 +27,15 @@ struct FwdArgs {
   int n_chunks;       // ceil(T / chunk)
   int ckpt_every;     // a state is stored before every ckpt_every-th chunk
   int n_ckpt;         // ceil(n_chunks / ckpt_every)
+  // Segments (matrix-core kernels): each sequence is cut into n_seg runs of
+  // seg_chunks chunks (the last may be shorter), scanned by separate
+  // work-groups.  seg_in: [B*H][n_seg][d_out][d_in] fp32 state entering each
+  // segment (NULL = zero); seg_out / seg_lg: the segment's final state from a
+  // zero start and its summed log2 alpha (state-only pass; NULL = not wanted).
+  int seg_chunks = 0, n_seg = 1;
+  const float* seg_in = nullptr;
+  float* seg_out = nullptr;
+  float* seg_lg = nullptr;
 };
 
 // Reverse scan.  Work-group (k, b*H+h) owns column tile k of D and Lambda
@@ -49,6 +58,14 @@ struct BwdArgs {
   int d_in, d_out;
   int chunk, n_chunks, ckpt_every, n_ckpt;
   int n_tiles;
+  // Segments, mirrored: seg_lam [B*H][n_seg][d_out][d_in] fp32 adjoint
+  // entering each segment from its right end (NULL = zero); seg_out / seg_lg:
+  // the adjoint at the segment's left end from a zero start, and the summed
+  // log2 alpha (adjoint-only pass).  part_dW0 holds [n_seg][B*H][d_out][d_in].
+  int seg_chunks = 0, n_seg = 1;
+  const float* seg_lam = nullptr;
+  float* seg_out = nullptr;
+  float* seg_lg = nullptr;
 };
 
 struct FinArgs {
@@ -61,6 +78,7 @@ struct FinArgs {
   int64_t B, H, T;
   int d_in, d_out;
   int n_tiles;
+  int n_seg = 1;  // dW0 partials per (b, h)
 };
 
 // Generic (VALU) kernels: any 1 <= d_in, d_out <= 128, all io types.
@@ -79,6 +97,11 @@ hipError_t launch_mfma_bwd(const BwdArgs& a, hipStream_t s);
 hipError_t launch_mfma_bwd_a(const BwdArgs& a, hipStream_t s);  // row tiles: dg, deta, dW0
 hipError_t launch_mfma_bwd_b(const BwdArgs& a, hipStream_t s);  // column tiles: dx, dalpha
 hipError_t launch_mfma_bwd_ab64(const BwdArgs& a, hipStream_t s);  // both, one launch, D = 64
+hipError_t launch_mfma_bwd_lam(const BwdArgs& a, hipStream_t s);  // adjoint-only segment pass
+// Exclusive affine scan over the segments of every (b, h): buf[s] <- the state
+// entering segment s (in segment order, or from the right end if reverse).
+hipError_t launch_seg_combine(float* buf, const float* lg, int64_t BH, int n_seg, int dd,
+                              bool reverse, hipStream_t s);
 int mfma_bwd_tiles(int d);
 
 }  // namespace gls

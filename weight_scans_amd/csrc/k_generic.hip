@@ -368,7 +368,7 @@ __global__ __launch_bounds__(kThreads) void finalize_kernel(FinArgs a) {
   }
   for (int64_t i = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; i < HD; i += stride) {
     T s = T(0);
-    for (int64_t b = 0; b < a.B; ++b) s += pw[b * HD + i];
+    for (int64_t b = 0; b < a.B * a.n_seg; ++b) s += pw[b * HD + i];  // [n_seg][B][H][.]
     static_cast<T*>(a.dW0)[i] = s;
   }
 }

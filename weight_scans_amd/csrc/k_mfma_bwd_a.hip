@@ -199,13 +199,19 @@ __global__ __launch_bounds__(kNT) void bwd_a(BwdArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g4 = lane >> 4, l16 = lane & 15;
   const int tb = wave >> 1, rbw = wave & 1;
-  const int grp = blockIdx.x / (8 * NTILE), within = blockIdx.x % (8 * NTILE);
+  // (segment is the slowest index, so the XCD of a head does not change)
+  const int per_seg = static_cast<int>((a.B * a.H + 7) / 8) * 8 * NTILE;
+  const int seg = blockIdx.x / per_seg, bid = blockIdx.x % per_seg;
+  const int grp = bid / (8 * NTILE), within = bid % (8 * NTILE);
   const int64_t bh = static_cast<int64_t>(grp) * 8 + (within & 7);
   const int tile = within >> 3;
   if (bh >= a.B * a.H) return;
   const int r0 = tile * kT;
   const int64_t T = a.T, BHT = a.B * a.H * T;
   const int n = a.n_chunks;
+  const int c_beg = seg * a.seg_chunks;
+  const int c_end = std::min(n, c_beg + a.seg_chunks);
+  const int nloc = c_end - c_beg;
   const uint16_t* x = static_cast<const uint16_t*>(a.x) + bh * T * D;
   const uint16_t* g = static_cast<const uint16_t*>(a.g) + bh * T * D;
   const uint16_t* dy = static_cast<const uint16_t*>(a.dy) + bh * T * D;
@@ -216,12 +222,15 @@ __global__ __launch_bounds__(kNT) void bwd_a(BwdArgs a) {
 
   for (int idx = tid; idx < 2 * kC * kC / 8; idx += kNT)
     reinterpret_cast<uint4*>(&PT_s[0][0])[idx] = make_uint4(0, 0, 0, 0);
-  for (int idx = tid; idx < 2 * kT * D / 8; idx += kNT)
-    reinterpret_cast<uint4*>(&L_s[0][0])[idx] = make_uint4(0, 0, 0, 0);
 
+  // valid tokens of chunk c (none outside this segment)
   const auto cv_of = [&](int c) {
-    return c < 0 ? 0 : static_cast<int>(std::min<int64_t>(kC, T - static_cast<int64_t>(c) * kC));
+    return (c < c_beg || c >= c_end)
+               ? 0
+               : static_cast<int>(std::min<int64_t>(kC, T - static_cast<int64_t>(c) * kC));
   };
+  // chunk index to load for visit v (-1: nothing, a zero fill)
+  const auto chunk_at = [&](int v) { return c_end - 1 - v >= c_beg ? c_end - 1 - v : -1; };
   const LaneOff<D> oX = lane_off<D>(lane);
   const LaneOff<kT> oT = lane_off<kT>(lane);
   const LaneOff<kC> oA = lane_off<kC>(lane);
@@ -232,12 +241,35 @@ __global__ __launch_bounds__(kNT) void bwd_a(BwdArgs a) {
   const int ds_row = tid >> 3;
   const uint32_t ds_off = static_cast<uint32_t>(sidx<kT>(ds_row, 4 * (tid & 7)) * 2);
 
+  // Lam rows of the tile entering from the right (fp32 accumulators, and the
+  // bf16 copy read by the first visit)
+  f32x4 lam[NS], dw[NS];
+  if (a.seg_lam) {
+    const float* sl = a.seg_lam + (bh * a.n_seg + seg) * D * D;
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+      lam[s] = *reinterpret_cast<const f32x4*>(sl + (r0 + rbw * 16 + l16) * D + (tb + 4 * s) * 16 +
+                                               4 * g4);
+  } else {
+#pragma unroll
+    for (int s = 0; s < NS; ++s) lam[s] = zero4();
+  }
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    dw[s] = zero4();
+    uint2 pk;
+    pk.x = pack2(lam[s][0], lam[s][1]);
+    pk.y = pack2(lam[s][2], lam[s][3]);
+    put4<D>(L_s[0], oX, rbw * 16, (tb + 4 * s) * 16, pk);
+  }
+  wait_vm<0>();
+
   // Chunks are visited from the last to the first; visit v handles chunk
   // n - 1 - v, which lives in ring slot v % R.
   // Initial loads, each followed by S dropped stores (stream shape as in the loop).
 #pragma unroll
   for (int v = 0; v < R - 1; ++v) {
-    issue_chunk_a<D>(*rs[v], od, x, dy, g, eta, alpha, T, n - 1 - v, r0, wave);
+    issue_chunk_a<D>(*rs[v], od, x, dy, g, eta, alpha, T, chunk_at(v), r0, wave);
     store8(r_none, odg + v, make_uint2(0, 0));
     store4(r_none, ope + v, 0.f);
   }
@@ -245,20 +277,13 @@ __global__ __launch_bounds__(kNT) void bwd_a(BwdArgs a) {
   wait_vm<S + (R - 3) * (P + S)>();
   lds_barrier();
   if (wave == kPrepWave) {
-    prep_gates_a<D>(*rs[0], cv_of(n - 1), lane);
-    prep_gates_a<D>(*rs[1], cv_of(n - 2), lane);
+    prep_gates_a<D>(*rs[0], cv_of(c_end - 1), lane);
+    prep_gates_a<D>(*rs[1], cv_of(c_end - 2), lane);
   }
   lds_barrier();
   scale_dy<D>(*rs[0], DS_s[0], ds_off, ds_row);
   p_block<D>(*rs[0], PT_s[0], oX, oA, wave, lane);
   if (wave < 2) p_block<D>(*rs[0], PT_s[0], oX, oA, wave + 8, lane);
-
-  f32x4 lam[NS], dw[NS];
-#pragma unroll
-  for (int s = 0; s < NS; ++s) {
-    lam[s] = zero4();
-    dw[s] = zero4();
-  }
 
   const auto step = [&](auto KC, int v) {
     constexpr int K = decltype(KC)::value;
@@ -266,18 +291,18 @@ __global__ __launch_bounds__(kNT) void bwd_a(BwdArgs a) {
     SlotA<D>& nx1 = *rs[(K + 1) % R];
     SlotA<D>& nx2 = *rs[(K + 2) % R];
     SlotA<D>& dst = *rs[(K + R - 1) % R];
-    const int c = n - 1 - v;
+    const int c = c_end - 1 - v;
     const int64_t t0 = static_cast<int64_t>(c) * kC;
     const int cv = cv_of(c);
     // chunk c - 2 loaded (past the first chunk: a zero fill)
     wait_vm<S + (R - 4) * (P + S)>();
     lds_barrier();  // P, scaled dy, gates of c - 1; Lam_out and deta partials of c + 1 visible
-    issue_chunk_a<D>(dst, od, x, dy, g, eta, alpha, T, c - (R - 1), r0, wave);
+    issue_chunk_a<D>(dst, od, x, dy, g, eta, alpha, T, chunk_at(v + R - 1), r0, wave);
 
     // deta of chunk c + 1: sum of the two row-block partials
     {
       const int cn = c + 1;
-      const bool fin = wave == kFinWave && cn < n;
+      const bool fin = wave == kFinWave && cn < c_end;
       const __amdgpu_buffer_rsrc_t r_pe =
           fin ? buffer_rsrc(pe + static_cast<int64_t>(cn) * kC, cv_of(cn) * 4) : r_none;
       const float* rd = &red_s[(v + 1) & 1][0][0];
@@ -350,27 +375,28 @@ __global__ __launch_bounds__(kNT) void bwd_a(BwdArgs a) {
   using I2 = std::integral_constant<int, 2>;
   using I3 = std::integral_constant<int, 3>;
   using I4 = std::integral_constant<int, 4>;
-  for (int v = 0; v < n; v += R) {
+  for (int v = 0; v < nloc; v += R) {
     step(I0{}, v);
-    if (v + 1 >= n) break;
+    if (v + 1 >= nloc) break;
     step(I1{}, v + 1);
-    if (v + 2 >= n) break;
+    if (v + 2 >= nloc) break;
     step(I2{}, v + 2);
-    if (v + 3 >= n) break;
+    if (v + 3 >= nloc) break;
     step(I3{}, v + 3);
     if constexpr (R == 5) {
-      if (v + 4 >= n) break;
+      if (v + 4 >= nloc) break;
       step(I4{}, v + 4);
     }
   }
   wait_vm<0>();
   lds_barrier();
   if (wave == kFinWave) {
-    // deta of chunk 0
-    const float* rd = &red_s[(n - 1) & 1][0][0];
-    store4(buffer_rsrc(pe, cv_of(0) * 4), ope, -(rd[lane] + rd[kC + lane]));
+    // deta of the segment's first chunk
+    const float* rd = &red_s[(nloc - 1) & 1][0][0];
+    store4(buffer_rsrc(pe + static_cast<int64_t>(c_beg) * kC, cv_of(c_beg) * 4), ope,
+           -(rd[lane] + rd[kC + lane]));
   }
-  float* pw = static_cast<float*>(a.part_dW0) + bh * D * D;
+  float* pw = static_cast<float*>(a.part_dW0) + (seg * a.B * a.H + bh) * D * D;
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
     const int cb = tb + 4 * s;
@@ -381,7 +407,7 @@ __global__ __launch_bounds__(kNT) void bwd_a(BwdArgs a) {
 template <int D>
 hipError_t launch_a(const BwdArgs& a, hipStream_t s) {
   const int64_t groups = (a.B * a.H + 7) / 8;
-  const dim3 grid(static_cast<unsigned>(groups * 8 * (D / kT)));
+  const dim3 grid(static_cast<unsigned>(groups * 8 * (D / kT) * a.n_seg));
   hipLaunchKernelGGL(bwd_a<D>, grid, dim3(kNT), 0, s, a);
   return hipGetLastError();
 }

@@ -80,7 +80,8 @@ __device__ __forceinline__ void issue_chunk_a2(SlotA2<D>& sl, const DmaOffA2<D>&
                      (wave & 1) * 1024);
 }
 
-// LDS objects of the row-tile pass (separate LDS variables in the caller).
+// LDS objects of the row-tile pass (separate LDS variables in the caller;
+// the adjoint-only instance never touches PT, L0, L1 and red).
 template <int D>
 struct SmemA2 {
   SlotA2<D>& ring0;
@@ -93,8 +94,13 @@ struct SmemA2 {
   float* red;   // [2][2][kC] deta partial by parity, row block
 };
 
-template <int D>
-__device__ __forceinline__ void role_a2_body(const BwdArgs& a, int64_t bh, int tile,
+// The row-tile pass for sequence-head bh, row tile `tile`, segment `seg`
+// (chunks seg * seg_chunks .. , visited from the last; Lam entering from the
+// right is seg_lam, or zero).  LAM_ONLY: the adjoint-only pass of the
+// segmented scan -- no P, u, dg, deta or dW0; it reports the tile's rows of
+// Lam at the segment's left end (zero start) and the summed log2 alpha.
+template <int D, bool LAM_ONLY>
+__device__ __forceinline__ void role_a2_body(const BwdArgs& a, int64_t bh, int tile, int seg,
                                              const SmemA2<D>& m) {
   static_assert(D == 64 || D == 128, "D");
   constexpr int NS = D / 64;
@@ -111,6 +117,9 @@ __device__ __forceinline__ void role_a2_body(const BwdArgs& a, int64_t bh, int t
   const int r0 = tile * kT;
   const int64_t T = a.T, BHT = a.B * a.H * T;
   const int n = a.n_chunks;
+  const int c_beg = seg * a.seg_chunks;
+  const int c_end = std::min(n, c_beg + a.seg_chunks);
+  const int nloc = c_end - c_beg;
   const uint16_t* x = static_cast<const uint16_t*>(a.x) + bh * T * D;
   const uint16_t* g = static_cast<const uint16_t*>(a.g) + bh * T * D;
   const uint16_t* dy = static_cast<const uint16_t*>(a.dy) + bh * T * D;
@@ -119,13 +128,15 @@ __device__ __forceinline__ void role_a2_body(const BwdArgs& a, int64_t bh, int t
   uint16_t* dg = static_cast<uint16_t*>(a.dg) + bh * T * D;
   float* pe = static_cast<float*>(a.part_eta) + tile * BHT + bh * T;
 
-  for (int idx = tid; idx < kC * kC / 8; idx += kNT)
-    reinterpret_cast<uint4*>(m.PT)[idx] = make_uint4(0, 0, 0, 0);
-  for (int idx = tid; idx < kT * D / 8; idx += kNT)
-    reinterpret_cast<uint4*>(L_s[0])[idx] = make_uint4(0, 0, 0, 0);
+  if constexpr (!LAM_ONLY)
+    for (int idx = tid; idx < kC * kC / 8; idx += kNT)
+      reinterpret_cast<uint4*>(m.PT)[idx] = make_uint4(0, 0, 0, 0);
 
+  // valid tokens of chunk c (none outside this segment)
   const auto cv_of = [&](int c) {
-    return c < 0 ? 0 : static_cast<int>(std::min<int64_t>(kC, T - static_cast<int64_t>(c) * kC));
+    return (c < c_beg || c >= c_end)
+               ? 0
+               : static_cast<int>(std::min<int64_t>(kC, T - static_cast<int64_t>(c) * kC));
   };
   const LaneOff<D> oX = lane_off<D>(lane);
   const LaneOff<kT> oT = lane_off<kT>(lane);
@@ -137,27 +148,46 @@ __device__ __forceinline__ void role_a2_body(const BwdArgs& a, int64_t bh, int t
   const int ds_row = tid >> 3;
   const uint32_t ds_off = static_cast<uint32_t>(sidx<kT>(ds_row, 4 * (tid & 7)) * 2);
 
-  issue_chunk_a2<D>(*rs[0], od, x, dy, g, eta, alpha, T, n - 1, r0, wave);
-  store8(r_none, odg, make_uint2(0, 0));
-  store4(r_none, ope, 0.f);
-
+  // Lam rows of the tile entering from the right (fp32 accumulators, and the
+  // bf16 copy read by the first visit)
   f32x4 lam[NS], dw[NS];
+  if (a.seg_lam) {
+    const float* sl = a.seg_lam + (bh * a.n_seg + seg) * D * D;
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+      lam[s] = *reinterpret_cast<const f32x4*>(sl + (r0 + rbw * 16 + l16) * D + (tb + 4 * s) * 16 +
+                                               4 * g4);
+  } else {
+#pragma unroll
+    for (int s = 0; s < NS; ++s) lam[s] = zero4();
+  }
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
-    lam[s] = zero4();
     dw[s] = zero4();
+    if constexpr (!LAM_ONLY) {
+      uint2 pk;
+      pk.x = pack2(lam[s][0], lam[s][1]);
+      pk.y = pack2(lam[s][2], lam[s][3]);
+      put4<D>(L_s[0], oX, rbw * 16, (tb + 4 * s) * 16, pk);
+    }
   }
+  wait_vm<0>();
+
+  issue_chunk_a2<D>(*rs[0], od, x, dy, g, eta, alpha, T, c_end - 1, r0, wave);
+  store8(r_none, odg, make_uint2(0, 0));
+  store4(r_none, ope, 0.f);
+  float lsum = 0.f;  // sum of l_last over the segment (adjoint-only pass)
 
   const auto step = [&](auto KC, int vis) {
     constexpr int K = decltype(KC)::value;
     SlotA2<D>& cur = *rs[K];
     SlotA2<D>& dst = *rs[K ^ 1];
-    const int c = n - 1 - vis;
+    const int c = c_end - 1 - vis;
     const int64_t t0 = static_cast<int64_t>(c) * kC;
     const int cv = cv_of(c);
     wait_vm<S>();
     lds_barrier();
-    issue_chunk_a2<D>(dst, od, x, dy, g, eta, alpha, T, c - 1, r0, wave);
+    issue_chunk_a2<D>(dst, od, x, dy, g, eta, alpha, T, c - 1 >= c_beg ? c - 1 : -1, r0, wave);
 
     // ---- phase 1: gates (same values from every wave), e(lq) dy, P
     {
@@ -169,6 +199,7 @@ __device__ __forceinline__ void role_a2_body(const BwdArgs& a, int64_t bh, int t
       gs.eq[lane] = fexp2(gt.lq);
       gs.e2[lane] = fexp2(gt.llast - gt.l);
       if (lane == 0) gs.gam[0] = fexp2(gt.llast);
+      lsum += gt.llast;
     }
     {
       const uint2 v = *reinterpret_cast<const uint2*>(reinterpret_cast<const char*>(cur.Dr) + ds_off);
@@ -199,21 +230,29 @@ __device__ __forceinline__ void role_a2_body(const BwdArgs& a, int64_t bh, int t
       pk.y = pack2(v[2], v[3]);
       put4<kC>(m.PT, oA, ib * 16, ub * 16, pk);
     };
-    p_block(wave);
-    if (wave < 2) p_block(wave + 8);
+    if constexpr (!LAM_ONLY) {
+      p_block(wave);
+      if (wave < 2) p_block(wave + 8);
+    }
     {
       // deta of chunk c + 1: sum of the two row-block partials
       const int cn = c + 1;
-      const bool fin = wave == kFinWaveA && vis > 0;
+      const bool fin = !LAM_ONLY && wave == kFinWaveA && vis > 0;
       const __amdgpu_buffer_rsrc_t r_pe =
           fin ? buffer_rsrc(pe + static_cast<int64_t>(cn) * kC, cv_of(cn) * 4) : r_none;
-      const float* rd = &red_s[(vis + 1) & 1][0][0];
-      store4(r_pe, ope, -(rd[lane] + rd[kC + lane]));
+      float val = 0.f;
+      if constexpr (!LAM_ONLY) {
+        const float* rd = &red_s[(vis + 1) & 1][0][0];
+        val = -(rd[lane] + rd[kC + lane]);
+      }
+      store4(r_pe, ope, val);
     }
     lds_barrier();  // gates, e(lq) dy, P visible
 
     // ---- phase 2: u, dg, deta partials
-    {
+    if constexpr (LAM_ONLY) {
+      store8(r_none, odg, make_uint2(0, 0));  // stream shape as in the full pass
+    } else {
       const __bf16* L_in = L_s[vis & 1];
       f32x4 ain = zero4(), apd = zero4();
 #pragma unroll
@@ -255,33 +294,46 @@ __device__ __forceinline__ void role_a2_body(const BwdArgs& a, int64_t bh, int t
         for (int kb = 0; kb < 2; ++kb) {
           const bf16x8 xa = frag_ts<D>(cur.X, oX, kb * 32, cb * 16);
           lam[s] = mfma16x16x32(xa, dsf[kb], lam[s]);
-          dw[s] = mfma16x16x32(xa, drf[kb], dw[s]);
+          if constexpr (!LAM_ONLY) dw[s] = mfma16x16x32(xa, drf[kb], dw[s]);
         }
-        uint2 pk;
-        pk.x = pack2(lam[s][0], lam[s][1]);
-        pk.y = pack2(lam[s][2], lam[s][3]);
-        put4<D>(L_out, oX, rbw * 16, cb * 16, pk);
+        if constexpr (!LAM_ONLY) {
+          uint2 pk;
+          pk.x = pack2(lam[s][0], lam[s][1]);
+          pk.y = pack2(lam[s][2], lam[s][3]);
+          put4<D>(L_out, oX, rbw * 16, cb * 16, pk);
+        }
       }
     }
   };
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
-  for (int vis = 0; vis < n; vis += 2) {
+  for (int vis = 0; vis < nloc; vis += 2) {
     step(I0{}, vis);
-    if (vis + 1 >= n) break;
+    if (vis + 1 >= nloc) break;
     step(I1{}, vis + 1);
   }
   wait_vm<0>();
   lds_barrier();
-  if (wave == kFinWaveA) {
-    const float* rd = &red_s[(n - 1) & 1][0][0];
-    store4(buffer_rsrc(pe, cv_of(0) * 4), ope, -(rd[lane] + rd[kC + lane]));
-  }
-  float* pw = static_cast<float*>(a.part_dW0) + bh * D * D;
+  if constexpr (LAM_ONLY) {
+    float* so = a.seg_out + (bh * a.n_seg + seg) * D * D;
 #pragma unroll
-  for (int s = 0; s < NS; ++s) {
-    const int cb = tb + 4 * s;
-    *reinterpret_cast<f32x4*>(pw + (r0 + rbw * 16 + l16) * D + cb * 16 + 4 * g4) = dw[s];
+    for (int s = 0; s < NS; ++s) {
+      const int cb = tb + 4 * s;
+      *reinterpret_cast<f32x4*>(so + (r0 + rbw * 16 + l16) * D + cb * 16 + 4 * g4) = lam[s];
+    }
+    if (tile == 0 && wave == 0 && lane == 0) a.seg_lg[bh * a.n_seg + seg] = lsum;
+  } else {
+    if (wave == kFinWaveA) {
+      const float* rd = &red_s[(nloc - 1) & 1][0][0];
+      store4(buffer_rsrc(pe + static_cast<int64_t>(c_beg) * kC, cv_of(c_beg) * 4), ope,
+             -(rd[lane] + rd[kC + lane]));
+    }
+    float* pw = static_cast<float*>(a.part_dW0) + (seg * a.B * a.H + bh) * D * D;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const int cb = tb + 4 * s;
+      *reinterpret_cast<f32x4*>(pw + (r0 + rbw * 16 + l16) * D + cb * 16 + 4 * g4) = dw[s];
+    }
   }
 }
 
@@ -294,8 +346,6 @@ constexpr int kD = 64;
 constexpr size_t kRingBytes =
     sizeof(SlotB<kD>) > sizeof(SlotA2<kD>) ? sizeof(SlotB<kD>) : sizeof(SlotA2<kD>);
 constexpr size_t kGateBytes = sizeof(GatesB) > sizeof(GatesA2) ? sizeof(GatesB) : sizeof(GatesA2);
-static_assert(kC * kC * 2 >= kC * kC * 2, "tt");
-static_assert(kD * kT * 2 == kT * kD * 2, "L");
 
 __global__ __launch_bounds__(kNT, 4) void bwd_ab64(BwdArgs a) {
   __shared__ alignas(16) char ring0[kRingBytes], ring1[kRingBytes];
@@ -305,29 +355,61 @@ __global__ __launch_bounds__(kNT, 4) void bwd_ab64(BwdArgs a) {
   __shared__ alignas(16) char gs_s[kGateBytes];
   __shared__ alignas(16) float red_s[2 * 2 * 4 * kC + 2 * kNW];
   constexpr int NTILE = kD / kT;
-  const int grp = blockIdx.x / (16 * NTILE), within = blockIdx.x % (16 * NTILE);
+  // (segment is the slowest index, so the XCD of a head does not change)
+  const int per_seg = static_cast<int>((a.B * a.H + 7) / 8) * 16 * NTILE;
+  const int seg = blockIdx.x / per_seg, bid = blockIdx.x % per_seg;
+  const int grp = bid / (16 * NTILE), within = bid % (16 * NTILE);
   const int64_t bh = static_cast<int64_t>(grp) * 8 + (within & 7);
   if (bh >= a.B * a.H) return;
   const int sub = within >> 3, tile = sub >> 1;
   if ((sub & 1) == 0) {
     const SmemA2<kD> m{*reinterpret_cast<SlotA2<kD>*>(ring0), *reinterpret_cast<SlotA2<kD>*>(ring1),
                        tt_s, L0_s, L1_s, sc_s, *reinterpret_cast<GatesA2*>(gs_s), red_s};
-    role_a2_body<kD>(a, bh, tile, m);
+    role_a2_body<kD, false>(a, bh, tile, seg, m);
   } else {
     const SmemB<kD> m{*reinterpret_cast<SlotB<kD>*>(ring0), *reinterpret_cast<SlotB<kD>*>(ring1),
                       tt_s, L0_s, L1_s, sc_s, *reinterpret_cast<GatesB*>(gs_s), red_s,
                       red_s + 2 * 2 * 4 * kC};
-    role_b_body<kD>(a, bh, tile, m);
+    role_b_body<kD>(a, bh, tile, seg, m);
   }
+}
+
+// Adjoint-only pass of the segmented reverse scan: one work-group per
+// (segment, head, row tile).
+template <int D>
+__global__ __launch_bounds__(kNT) void bwd_lam(BwdArgs a) {
+  __shared__ SlotA2<D> ring0, ring1;
+  __shared__ __bf16 DS_s[kC * kT];
+  __shared__ GatesA2 gs;
+  constexpr int NTILE = D / kT;
+  const int per_seg = static_cast<int>((a.B * a.H + 7) / 8) * 8 * NTILE;
+  const int seg = blockIdx.x / per_seg, bid = blockIdx.x % per_seg;
+  const int grp = bid / (8 * NTILE), within = bid % (8 * NTILE);
+  const int64_t bh = static_cast<int64_t>(grp) * 8 + (within & 7);
+  if (bh >= a.B * a.H) return;
+  const SmemA2<D> m{ring0, ring1, nullptr, nullptr, nullptr, DS_s, gs, nullptr};
+  role_a2_body<D, true>(a, bh, within >> 3, seg, m);
+}
+
+template <int D>
+hipError_t launch_lam(const BwdArgs& a, hipStream_t s) {
+  const int64_t groups = (a.B * a.H + 7) / 8;
+  const dim3 grid(static_cast<unsigned>(groups * 8 * (D / kT) * a.n_seg));
+  hipLaunchKernelGGL(bwd_lam<D>, grid, dim3(kNT), 0, s, a);
+  return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_mfma_bwd_ab64(const BwdArgs& a, hipStream_t s) {
   const int64_t groups = (a.B * a.H + 7) / 8;
-  const dim3 grid(static_cast<unsigned>(groups * 16 * (kD / kT)));
+  const dim3 grid(static_cast<unsigned>(groups * 16 * (kD / kT) * a.n_seg));
   hipLaunchKernelGGL(bwd_ab64, grid, dim3(kNT), 0, s, a);
   return hipGetLastError();
+}
+
+hipError_t launch_mfma_bwd_lam(const BwdArgs& a, hipStream_t s) {
+  return a.d_in == 128 ? launch_lam<128>(a, s) : launch_lam<64>(a, s);
 }
 
 }  // namespace gls

@@ -16,17 +16,20 @@ __global__ __launch_bounds__(kNT) void bwd_b(BwdArgs a) {
   __shared__ GatesB gs;
   __shared__ float dots_s[2 * 2 * 4 * kC];
   __shared__ float c0_s[2 * kNW];
-  const int grp = blockIdx.x / (8 * NTILE), within = blockIdx.x % (8 * NTILE);
+  // (segment is the slowest index, so the XCD of a head does not change)
+  const int per_seg = static_cast<int>((a.B * a.H + 7) / 8) * 8 * NTILE;
+  const int seg = blockIdx.x / per_seg, bid = blockIdx.x % per_seg;
+  const int grp = bid / (8 * NTILE), within = bid % (8 * NTILE);
   const int64_t bh = static_cast<int64_t>(grp) * 8 + (within & 7);
   if (bh >= a.B * a.H) return;
   const SmemB<D> m{ring0, ring1, BeT_s, L0_s, L1_s, XS_s, gs, dots_s, c0_s};
-  role_b_body<D>(a, bh, within >> 3, m);
+  role_b_body<D>(a, bh, within >> 3, seg, m);
 }
 
 template <int D>
 hipError_t launch_b(const BwdArgs& a, hipStream_t s) {
   const int64_t groups = (a.B * a.H + 7) / 8;
-  const dim3 grid(static_cast<unsigned>(groups * 8 * (D / kT)));
+  const dim3 grid(static_cast<unsigned>(groups * 8 * (D / kT) * a.n_seg));
   hipLaunchKernelGGL(bwd_b<D>, grid, dim3(kNT), 0, s, a);
   return hipGetLastError();
 }

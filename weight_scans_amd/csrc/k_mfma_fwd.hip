@@ -25,6 +25,16 @@
 //
 // `states` (optional) receives D_in of every chunk in bf16:
 // [B*H][n_chunks][D (row r)][D (col c)] -- read by the matrix-core backward.
+//
+// Segments: work-group (segment s, head, tile) scans only the chunks of s,
+// starting from the state given in seg_in (zero if absent).  The state-only
+// instance (no y, no states) instead reports the segment's final state from
+// a zero start and its summed log2 alpha; an exclusive affine scan over the
+// segments (k_seg.hip) turns these into each segment's starting state.  This
+// is the associative composition of the scan across chunks
+// ("Parallelize the Training, Keep the Learning Serial", cognaptus.com,
+// section "Once the gradient signals are known, the weight trajectory becomes
+// parallelizable") applied one level up.
 #include <algorithm>
 #include <cstddef>
 #include <type_traits>
@@ -98,14 +108,14 @@ template <int D>
 constexpr int kLoadOps = D / 64 + 1;
 
 // Queue the loads of chunk k into `sl`.  Rows past the sequence end, and
-// chunks past the last one, are zero-filled by the buffer bounds (every wave
+// chunks from c_end on, are zero-filled by the buffer bounds (every wave
 // always issues the same number of loads).
 template <int D>
 __device__ __forceinline__ void issue_chunk(Slot<D>& sl, const DmaOff<D>& o, const uint16_t* x,
                                             const uint16_t* g, const float* eta,
-                                            const float* alpha, int64_t T, int k, int n_chunks,
+                                            const float* alpha, int64_t T, int k, int c_end,
                                             int r0, int wave) {
-  const bool in = k < n_chunks;
+  const bool in = k < c_end;
   const int64_t t0 = in ? static_cast<int64_t>(k) * kC : 0;
   const int cv = in ? static_cast<int>(std::min<int64_t>(kC, T - t0)) : 0;
   const __amdgpu_buffer_rsrc_t rx = buffer_rsrc(x + t0 * D, cv * D * 2);
@@ -122,9 +132,9 @@ __device__ __forceinline__ void issue_chunk(Slot<D>& sl, const DmaOff<D>& o, con
   dma16(r4, o.gq, reinterpret_cast<char*>(&sl) + lds_off);
 }
 
-// Gates of a chunk, lane = token (one wave).
+// Gates of a chunk, lane = token (one wave); returns l_last.
 template <int D>
-__device__ __forceinline__ void prep_gates(Slot<D>& sl, int cv, int lane) {
+__device__ __forceinline__ float prep_gates(Slot<D>& sl, int cv, int lane) {
   const float et = lane < cv ? sl.f.eta[lane] : 0.f;
   const ChunkGates gt = chunk_gates(lane < cv ? sl.f.alpha[lane] : 1.f, lane);
   const float m1 = readlane_f(gt.l, 15), m2 = readlane_f(gt.l, 31), m3 = readlane_f(gt.l, 47);
@@ -140,6 +150,7 @@ __device__ __forceinline__ void prep_gates(Slot<D>& sl, int cv, int lane) {
   sl.f.C2[lane] = -et * fexp2(fminf(m2 - gt.l, 0.f));
   sl.f.C3[lane] = -et * fexp2(fminf(m3 - gt.l, 0.f));
   if (lane == 0) sl.gam[0] = fexp2(gt.llast);
+  return gt.llast;
 }
 
 // Block b (0..9, row-major over the causal triangle of 16 x 16 blocks) of the
@@ -213,7 +224,10 @@ __global__ __launch_bounds__(kNT) void fwd_mfma(FwdArgs a) {
   // 8 consecutive sequence-heads and all their row tiles share one XCD
   // (work-groups are dealt to the 8 XCDs round-robin), so the x chunk that
   // every tile reads is fetched from HBM once into that XCD's L2.
-  const int grp = blockIdx.x / (8 * NTILE), within = blockIdx.x % (8 * NTILE);
+  // (segment is the slowest index, so the XCD of a head does not change)
+  const int per_seg = static_cast<int>((a.B * a.H + 7) / 8) * 8 * NTILE;
+  const int seg = blockIdx.x / per_seg, bid = blockIdx.x % per_seg;
+  const int grp = bid / (8 * NTILE), within = bid % (8 * NTILE);
   const int64_t bh = static_cast<int64_t>(grp) * 8 + (within & 7);
   const int tile = within >> 3;
   if (bh >= a.B * a.H) return;
@@ -221,6 +235,9 @@ __global__ __launch_bounds__(kNT) void fwd_mfma(FwdArgs a) {
   const int h = static_cast<int>(bh % a.H);
   const int64_t T = a.T;
   const int n = a.n_chunks;
+  const int c_beg = seg * a.seg_chunks;
+  const int c_end = std::min(n, c_beg + a.seg_chunks);
+  const int nloc = c_end - c_beg;
   const uint16_t* x = static_cast<const uint16_t*>(a.x) + bh * T * D;
   const uint16_t* g = static_cast<const uint16_t*>(a.g) + bh * T * D;
   const float* eta = static_cast<const float*>(a.eta) + bh * T;
@@ -238,15 +255,29 @@ __global__ __launch_bounds__(kNT) void fwd_mfma(FwdArgs a) {
       wf[kb] = *reinterpret_cast<const bf16x8*>(
           W0 + static_cast<int64_t>(r0 + rbw * 16 + l16) * D + kb * 32 + 8 * g4);
   }
-  for (int idx = tid; idx < kTN * D / 8; idx += kNT)
-    reinterpret_cast<uint4*>(S_s[0])[idx] = make_uint4(0, 0, 0, 0);
+  // starting state of the tile: zero, or the segment's incoming state
+  // (fp32 accumulators, and its bf16 copy for the readout of the first chunk)
+  f32x4 sacc[NS];
+  if (a.seg_in) {
+    const float* si = a.seg_in + (bh * a.n_seg + seg) * D * D;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const int cb = tb + 4 * s;
+      sacc[s] = *reinterpret_cast<const f32x4*>(si + (r0 + rbw * 16 + l16) * D + cb * 16 + 4 * g4);
+    }
+  } else {
+#pragma unroll
+    for (int s = 0; s < NS; ++s) sacc[s] = zero4();
+  }
   if (HAS_Y)
     for (int idx = tid; idx < 2 * kC * kC / 8; idx += kNT)
       reinterpret_cast<uint4*>(&AT_s[0][0])[idx] = make_uint4(0, 0, 0, 0);
   wait_vm<0>();
 
+  // valid tokens of chunk c (none outside this segment)
   const auto cv_of = [&](int c) {
-    return static_cast<int>(std::min<int64_t>(kC, T - static_cast<int64_t>(c) * kC));
+    return c < c_end ? static_cast<int>(std::min<int64_t>(kC, T - static_cast<int64_t>(c) * kC))
+                     : 0;
   };
   const LaneOff<D> oX = lane_off<D>(lane);
   const LaneOff<kTN> oG = lane_off<kTN>(lane);
@@ -265,6 +296,13 @@ __global__ __launch_bounds__(kNT) void fwd_mfma(FwdArgs a) {
   // this thread's 4 elements of the scaled g tile: row tid/8, columns 4 (tid%8)..
   const int gs_row = tid >> 3;
   const uint32_t gs_off = static_cast<uint32_t>(sidx<kTN>(gs_row, 4 * (tid & 7)) * 2);
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    uint2 pk;
+    pk.x = pack2(sacc[s][0], sacc[s][1]);
+    pk.y = pack2(sacc[s][2], sacc[s][3]);
+    put4<D>(S_s[0], oX, rbw * 16, (tb + 4 * s) * 16, pk);
+  }
 
   // Initial loads, each followed by S stores into a zero-byte buffer (they
   // are dropped) so that the vector-memory instruction stream has the same
@@ -272,7 +310,7 @@ __global__ __launch_bounds__(kNT) void fwd_mfma(FwdArgs a) {
   // wait at the top of every iteration is the same constant.
 #pragma unroll
   for (int k = 0; k < kRing - 1; ++k) {
-    issue_chunk<D>(*rs[k], od, x, g, eta, alpha, T, k, n, r0, wave);
+    issue_chunk<D>(*rs[k], od, x, g, eta, alpha, T, c_beg + k, c_end, r0, wave);
     // distinct offsets, so that none of them is merged away
     if (HAS_ST)
 #pragma unroll
@@ -282,9 +320,10 @@ __global__ __launch_bounds__(kNT) void fwd_mfma(FwdArgs a) {
   // chunks 0 and 1 done: after chunk 1 come two more chunk loads and three store groups
   wait_vm<2 * P + 3 * S>();
   lds_barrier();
+  float lsum = 0.f;  // sum of l_last over the segment's chunks (prep wave)
   if (wave == kPrepWave) {
-    prep_gates<D>(*rs[0], cv_of(0), lane);
-    prep_gates<D>(*rs[1], cv_of(1), lane);
+    lsum += prep_gates<D>(*rs[0], cv_of(c_beg), lane);
+    lsum += prep_gates<D>(*rs[1], cv_of(c_beg + 1), lane);
   }
   lds_barrier();
   scale_g<D>(*rs[0], GS_s[0], gs_off, gs_row);
@@ -293,24 +332,21 @@ __global__ __launch_bounds__(kNT) void fwd_mfma(FwdArgs a) {
     if (wave < 2) score_block<D>(*rs[0], AT_s[0], oX, oA, wave + 8, lane);
   }
 
-  f32x4 sacc[NS];
-#pragma unroll
-  for (int s = 0; s < NS; ++s) sacc[s] = zero4();
-
-  // one chunk; K = c % kRing is a compile-time constant
+  // one chunk; K = (c - c_beg) % kRing is a compile-time constant
   const auto step = [&](auto KC, int c) {
     constexpr int K = decltype(KC)::value;
     Slot<D>& cur = *rs[K];
     Slot<D>& nx1 = *rs[(K + 1) % kRing];
     Slot<D>& nx2 = *rs[(K + 2) % kRing];
     Slot<D>& dst = *rs[(K + kRing - 1) % kRing];
+    const int vl = c - c_beg;  // position in the segment: double-buffer parity
     const int64_t t0 = static_cast<int64_t>(c) * kC;
     const int cv = cv_of(c);
     // chunk c + 2 loaded: issued after it are its own store group and one
     // more (chunk load + stores); past the end it is a zero fill
     wait_vm<P + 2 * S>();
     lds_barrier();  // scores and gates of c + 1, D_in of c visible
-    issue_chunk<D>(dst, od, x, g, eta, alpha, T, c + kRing - 1, n, r0, wave);
+    issue_chunk<D>(dst, od, x, g, eta, alpha, T, c + kRing - 1, c_end, r0, wave);
 
     if (HAS_ST) {
       // chunk-start state of this wave's blocks (natural layout, bf16)
@@ -323,20 +359,20 @@ __global__ __launch_bounds__(kNT) void fwd_mfma(FwdArgs a) {
         store8(r_st, os[s], v);
       }
     }
-    if (wave == kPrepWave) prep_gates<D>(nx2, cv_of(c + 2), lane);
-    scale_g<D>(nx1, GS_s[(c + 1) & 1], gs_off, gs_row);
+    if (wave == kPrepWave) lsum += prep_gates<D>(nx2, cv_of(c + 2), lane);
+    scale_g<D>(nx1, GS_s[(vl + 1) & 1], gs_off, gs_row);
     if (HAS_Y) {
-      __bf16* AT1 = AT_s[(c + 1) & 1];
+      __bf16* AT1 = AT_s[(vl + 1) & 1];
       score_block<D>(nx1, AT1, oX, oA, wave, lane);
       if (wave < 2) score_block<D>(nx1, AT1, oX, oA, wave + 8, lane);
     }
 
-    const __bf16* S_in = S_s[c & 1];
+    const __bf16* S_in = S_s[vl & 1];
     if (HAS_Y) {
       // y^T[r][i] for this wave's block; each lane stores 4 consecutive rows
       // of one token straight from the accumulators.  (For token blocks 0
       // and 1 the second K block of A^T is zero.)
-      const __bf16* AT = AT_s[c & 1];
+      const __bf16* AT = AT_s[vl & 1];
       f32x4 ya = zero4(), yb = zero4();
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -359,12 +395,12 @@ __global__ __launch_bounds__(kNT) void fwd_mfma(FwdArgs a) {
     // state update, transposed: D^T[c][r] = Gamma D^T + sum_j x_j[c] (bk_j g_j[r]),
     // into the other state buffer (the current one may still be read)
     {
-      const __bf16* GS = GS_s[c & 1];
+      const __bf16* GS = GS_s[vl & 1];
       bf16x8 gs[2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) gs[kb] = frag_ts<kTN>(GS, oG, kb * 32, rbw * 16);
       const float gam = cur.gam[0];
-      __bf16* S_out = S_s[(c + 1) & 1];
+      __bf16* S_out = S_s[(vl + 1) & 1];
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
         const int cb = tb + 4 * s;
@@ -384,24 +420,34 @@ __global__ __launch_bounds__(kNT) void fwd_mfma(FwdArgs a) {
   using I2 = std::integral_constant<int, 2>;
   using I3 = std::integral_constant<int, 3>;
   using I4 = std::integral_constant<int, 4>;
-  for (int c = 0; c < n; c += kRing) {
-    step(I0{}, c);
-    if (c + 1 >= n) break;
-    step(I1{}, c + 1);
-    if (c + 2 >= n) break;
-    step(I2{}, c + 2);
-    if (c + 3 >= n) break;
-    step(I3{}, c + 3);
-    if (c + 4 >= n) break;
-    step(I4{}, c + 4);
+  for (int v = 0; v < nloc; v += kRing) {
+    step(I0{}, c_beg + v);
+    if (v + 1 >= nloc) break;
+    step(I1{}, c_beg + v + 1);
+    if (v + 2 >= nloc) break;
+    step(I2{}, c_beg + v + 2);
+    if (v + 3 >= nloc) break;
+    step(I3{}, c_beg + v + 3);
+    if (v + 4 >= nloc) break;
+    step(I4{}, c_beg + v + 4);
   }
   wait_vm<0>();  // no load into LDS may outlive the work-group
+  if (a.seg_out) {
+    // the segment's final state (zero start) and its summed log2 alpha
+    float* so = a.seg_out + (bh * a.n_seg + seg) * D * D;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const int cb = tb + 4 * s;
+      *reinterpret_cast<f32x4*>(so + (r0 + rbw * 16 + l16) * D + cb * 16 + 4 * g4) = sacc[s];
+    }
+    if (tile == 0 && wave == kPrepWave && lane == 0) a.seg_lg[bh * a.n_seg + seg] = lsum;
+  }
 }
 
 template <int D, bool HAS_Y, bool HAS_ST>
 hipError_t launch_v(const FwdArgs& a, hipStream_t s) {
   const int64_t groups = (a.B * a.H + 7) / 8;
-  const dim3 grid(static_cast<unsigned>(groups * 8 * (D / kTN)));
+  const dim3 grid(static_cast<unsigned>(groups * 8 * (D / kTN) * a.n_seg));
   hipLaunchKernelGGL((fwd_mfma<D, HAS_Y, HAS_ST>), grid, dim3(kNT), 0, s, a);
   return hipGetLastError();
 }
@@ -411,6 +457,7 @@ hipError_t launch_d(const FwdArgs& a, hipStream_t s) {
   if (a.y && a.states) return launch_v<D, true, true>(a, s);
   if (a.y) return launch_v<D, true, false>(a, s);
   if (a.states) return launch_v<D, false, true>(a, s);
+  if (a.seg_out) return launch_v<D, false, false>(a, s);  // state-only segment pass
   return hipSuccess;
 }
 

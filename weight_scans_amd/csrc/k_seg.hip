@@ -1,0 +1,50 @@
+// k_seg.hip -- combine step of the segmented scan.
+//
+// A long sequence is cut into segments that separate work-groups scan from a
+// zero state.  Each segment s reports its final state L_s and its summed
+// log2 retention lg_s (so the whole segment scales a state by G_s = 2^lg_s).
+// Because the per-token update is affine in the state, composing segments
+// is the same associative combine as composing tokens ("Parallelize the
+// Training, Keep the Learning Serial", cognaptus.com, section "Once the
+// gradient signals are known, the weight trajectory becomes
+// parallelizable"):
+//   state entering segment 0 = 0,  entering s + 1 = G_s (entering s) + L_s.
+// The reverse scan composes its adjoint the same way from the right end.
+// This kernel replaces every L_s by the state entering segment s (an
+// exclusive scan over segments, one thread per matrix element).
+#include "internal.hpp"
+
+namespace gls {
+namespace {
+
+constexpr int kSegThreads = 256;
+
+__global__ __launch_bounds__(kSegThreads) void seg_combine(float* buf, const float* lg,
+                                                           int n_seg, int dd, int reverse) {
+  const int64_t bh = blockIdx.y;
+  const int e = blockIdx.x * kSegThreads + threadIdx.x;
+  if (e >= dd) return;
+  float* p = buf + bh * n_seg * static_cast<int64_t>(dd) + e;
+  const float* l = lg + bh * n_seg;
+  float carry = 0.f;
+  for (int k = 0; k < n_seg; ++k) {
+    const int s = reverse ? n_seg - 1 - k : k;
+    const float local = p[static_cast<int64_t>(s) * dd];
+    p[static_cast<int64_t>(s) * dd] = carry;
+    carry = carry * __builtin_amdgcn_exp2f(l[s]) + local;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_seg_combine(float* buf, const float* lg, int64_t BH, int n_seg, int dd,
+                              bool reverse, hipStream_t s) {
+  if (BH == 0 || n_seg <= 1) return hipSuccess;
+  const dim3 grid(static_cast<unsigned>((dd + kSegThreads - 1) / kSegThreads),
+                  static_cast<unsigned>(BH));
+  hipLaunchKernelGGL(seg_combine, grid, dim3(kSegThreads), 0, s, buf, lg, n_seg, dd,
+                     reverse ? 1 : 0);
+  return hipGetLastError();
+}
+
+}  // namespace gls
