@@ -55,6 +55,18 @@ def binding(w, nbytes, nflops):
     return "mfma", nflops / 1e12, PEAK_MATRIX[w.dtype] / 1e12, "TFLOP/s"
 
 
+def pass_kernels(w, which, segmented, generic):
+    """The kernels one pass launches (the event-timed region of that pass)."""
+    if generic:
+        return {"fwd": "fwd_generic", "bwd": "bwd_generic + finalize_kernel"}[which]
+    if which == "fwd":
+        return ("fwd_mfma (state-only) + seg_combine + fwd_mfma" if segmented else "fwd_mfma")
+    body = "bwd_ab64" if w.d_in == 64 else "bwd_a + bwd_b"
+    if segmented:
+        body = "bwd_lam + seg_combine + " + body
+    return body + " + finalize_kernel"
+
+
 def cpu_baseline(w, budget_s=20.0):
     """Time the fp64 oracle (fwd + bwd) on whole sequence-heads of the same
     workload, as many as fit ~budget_s of CPU work, on this host's cores."""
@@ -102,6 +114,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-flush", action="store_true", help="do not flush caches between steps")
     ap.add_argument("--generic", action="store_true", help="force the portable VALU kernels")
+    ap.add_argument("--segments", type=int, default=0,
+                    help="segments per sequence (0 = the library's automatic choice)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -125,7 +139,7 @@ def main():
     del inp
     flags = ws.GL_FLAG_GENERIC if args.generic else 0
     desc = ws.make_desc(w.B, w.H, w.T, w.d_in, w.d_out,
-                        {"f64": 0, "f32": 1, "bf16": 2}[w.dtype], w.chunk, flags)
+                        {"f64": 0, "f32": 1, "bf16": 2}[w.dtype], w.chunk, flags, args.segments)
     path = ws.path_name(desc)
     y = torch.empty((w.B, w.H, w.T, w.d_out), dtype=tio, device=dev)
     dx, dg = torch.empty_like(t["x"]), torch.empty_like(t["g"])
@@ -133,6 +147,7 @@ def main():
     dW0 = torch.empty((w.H, w.d_out, w.d_in), dtype=gd, device=dev)
     saved = torch.empty(max(ws.saved_size(desc), 16), dtype=torch.uint8, device=dev)
     fws, bws = ws.workspace_size(desc, True)
+    segmented = fws > 0  # the forward needs a workspace only for segments
     wsb = torch.empty(max(fws, bws, 16), dtype=torch.uint8, device=dev)
     flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
     # one plain copy of known size (256 MiB each way): the reference that turns
@@ -220,7 +235,7 @@ def main():
         "roofline": {"bound": bound, "achieved": achieved, "peak": peak, "unit": unit,
                      "frac": achieved / peak, "traffic": traffic,
                      "algorithmic_bytes": nbytes, "algorithmic_flops": nflops,
-                     "kernel": f"{dom} pass ({path})",
+                     "kernel": f"{dom} pass ({path}): " + pass_kernels(w, dom, segmented, args.generic),
                      "step_frac": step_floor / (ms_step / 1e3)},
         "wall_ms_per_step_incl_flush": wall * 1e3 / args.steps,
     }

@@ -111,10 +111,13 @@ def main(argv):
         if "--json" in argv:
             path = os.path.join(ROOT, "profiles", "traffic.json")
             db = json.load(open(path)) if os.path.exists(path) else {}
-            fwd = sum(v["fetch_bytes"] + v["write_bytes"] for k, v in res["kernels"].items()
-                      if "fwd_mfma" in k or "fwd_generic" in k)
-            bwd = sum(v["fetch_bytes"] + v["write_bytes"] for k, v in res["kernels"].items()
-                      if "bwd_mfma" in k or "bwd_generic" in k or "finalize" in k)
+            # per-dispatch bytes of every kernel a pass launches once; the
+            # segment combine runs once in each pass
+            def moved(pred):
+                return sum(v["fetch_bytes"] + v["write_bytes"] for k, v in res["kernels"].items()
+                           if pred(k))
+            fwd = moved(lambda k: k.startswith("fwd_") or "seg_combine" in k)
+            bwd = moved(lambda k: k.startswith("bwd_") or "finalize" in k or "seg_combine" in k)
             db[cfg] = {"kernel_hash": kernel_source_hash(), "fwd_bytes": fwd, "bwd_bytes": bwd,
                        "fetch_scale": res["fetch_scale"], "write_scale": res["write_scale"]}
             with open(path, "w") as fh:
