@@ -17,11 +17,15 @@
 //
 // Pipeline: two chunk slots filled by direct buffer loads (the chunk's full
 // dy and g tiles make a deeper ring too large for LDS at D = 128), two
-// barriers per chunk.  Phase 1 (all eight waves): gates, Be, e(lq) x, the
-// <Lam_out, D_in> partials; wave 7 also finishes dalpha of the previous
-// chunk (four wave-level scans).  Phase 2: wave w owns the 16 x 16 block
-// (token block w/2, column block w%2) of dx and its per-token dots, and D/64
-// 16 x 16 blocks of the Lam update.
+// barriers per chunk.  A slot holds the tiles of one chunk and the gate
+// inputs (eta, alpha) of the chunk visited after it, so the gates of the next
+// chunk are derived one visit early.  Phase 1: e(lq) x, Be, the
+// <Lam_out, D_in> partials; one wave stores dalpha of the chunk visited two
+// visits earlier.  Phase 2: wave w owns the 16 x 16 block (token block w/2,
+// column block w%2) of dx and its per-token dots, and D/64 16 x 16 blocks of
+// the Lam update; meanwhile one wave derives the gates of the next chunk and
+// two waves run the forward and the reversed scans of dalpha of the previous
+// chunk.
 #pragma once
 
 #include <algorithm>
@@ -39,7 +43,10 @@ constexpr int kC = 64;         // tokens per chunk
 constexpr int kT = 32;         // columns per work-group
 constexpr int kNW = 8;         // waves per work-group
 constexpr int kNT = 64 * kNW;  // threads
-constexpr int kDaWave = 7;     // finishes dalpha
+constexpr int kDaWave = 7;     // stores dalpha
+constexpr int kGateWave = 0;   // derives the gates of the next chunk
+constexpr int kFwdWave = 2;    // forward scan of dalpha
+constexpr int kRevWave = 3;    // reversed scans of dalpha
 
 template <int D>
 struct alignas(16) SlotB {
@@ -47,12 +54,14 @@ struct alignas(16) SlotB {
   __bf16 G[kC * D];      // g of the chunk, swizzled [token][D]
   __bf16 Xk[kC * kT];    // x of the column tile, swizzled [token][kT]
   __bf16 Sn[D * kT];     // D_in[:, K], swizzled [row][kT]
-  float q[2][4 * kC];    // eta = q[0][0..63], alpha = q[1][0..63]
+  float q[2][kC];        // eta, alpha of the chunk visited next
 };
 
+// Gates of one chunk (lane = token) and the two parts of its dalpha.
 struct alignas(16) GatesB {
-  float lq[kC], li[kC], nb[kC], eq[kC], e2[kC];
-  float gam[4];
+  float lq[kC], li[kC], nb[kC], eq[kC], e2[kC], al[kC];
+  float fpart[kC], rpart[kC];
+  float gam[4];  // gam[0] = e(l_last), gam[1] = l_last
 };
 
 // Per-lane byte offsets of the chunk loads (loop invariant).
@@ -85,18 +94,28 @@ __device__ __forceinline__ DmaOffB<D> dma_off_b(int wave, int lane) {
     const int row = p >> 2, kl = (p & 3) ^ swz<kT>(row);
     o.xk = static_cast<uint32_t>(row * D * 2 + 16 * kl);
   }
-  o.q = static_cast<uint32_t>(lane * 16);
+  o.q = static_cast<uint32_t>(lane * 4);
   return o;
 }
-template <int D>
-constexpr int kLoadOpsB = D == 128 ? 7 : 4;
 
+// Gate row (eta for even waves, alpha for odd ones; four waves write the
+// same bytes) of chunk k into q, one dword per lane.  k < 0: zero fill.
+__device__ __forceinline__ void issue_gate_row(float (*q)[kC], uint32_t voff, const float* eta,
+                                               const float* alpha, int64_t T, int k, int wave) {
+  const bool in = k >= 0;
+  const int64_t t0 = in ? static_cast<int64_t>(k) * kC : 0;
+  const int cv = in ? static_cast<int>(std::min<int64_t>(kC, T - t0)) : 0;
+  const __amdgpu_buffer_rsrc_t rq = buffer_rsrc(((wave & 1) == 0 ? eta : alpha) + t0, cv * 4);
+  dma4(rq, voff, q[wave & 1]);
+}
+
+// Tiles of chunk k and the gate rows of chunk kq into `sl` (negative: zero fill).
 template <int D>
 __device__ __forceinline__ void issue_chunk_b(SlotB<D>& sl, const DmaOffB<D>& o,
                                               const uint16_t* dy, const uint16_t* g,
                                               const uint16_t* x, const uint16_t* st,
                                               const float* eta, const float* alpha, int64_t T,
-                                              int k, int k0, int wave) {
+                                              int k, int kq, int k0, int wave) {
   const bool in = k >= 0;
   const int64_t t0 = in ? static_cast<int64_t>(k) * kC : 0;
   const int cv = in ? static_cast<int>(std::min<int64_t>(kC, T - t0)) : 0;
@@ -120,35 +139,28 @@ __device__ __forceinline__ void issue_chunk_b(SlotB<D>& sl, const DmaOffB<D>& o,
                        : static_cast<int>(offsetof(SlotB<D>, Xk)) + (wave & 3) * 1024;
     dma16(sw ? rs : rx, sw ? o.sn : o.xk, reinterpret_cast<char*>(&sl) + off);
   }
-  const __amdgpu_buffer_rsrc_t rq = buffer_rsrc(((wave & 1) == 0 ? eta : alpha) + t0, cv * 4);
-  dma16(rq, o.q, reinterpret_cast<char*>(&sl) + static_cast<int>(offsetof(SlotB<D>, q)) +
-                     (wave & 1) * 1024);
+  issue_gate_row(sl.q, o.q, eta, alpha, T, kq, wave);
 }
-
-// Gates of the chunk, lane = token; every wave computes them and writes the
-// same values; returns them in registers too.
-struct LaneGatesB {
-  float al, nb, l, lq, llast;
-};
 template <int D>
-__device__ __forceinline__ LaneGatesB gates_b(const SlotB<D>& sl, GatesB& gs, int cv, int lane) {
-  LaneGatesB r;
-  const float et = lane < cv ? sl.q[0][lane] : 0.f;
-  r.al = lane < cv ? sl.q[1][lane] : 1.f;
-  const ChunkGates gt = chunk_gates(r.al, lane);
-  r.nb = -et;
-  r.l = gt.l;
-  r.lq = gt.lq;
-  r.llast = gt.llast;
+constexpr int kLoadOpsB = D == 128 ? 7 : 4;
+
+// Gates of a chunk from its gate rows (one wave, lane = token).  Padding
+// tokens carry alpha = 1, eta = 0.
+__device__ __forceinline__ void gates_b(const float (*q)[kC], GatesB& gs, int cv, int lane) {
+  const float et = lane < cv ? q[0][lane] : 0.f;
+  const float al = lane < cv ? q[1][lane] : 1.f;
+  const ChunkGates gt = chunk_gates(al, lane);
   gs.lq[lane] = gt.lq;
   gs.li[lane] = gt.l;
   gs.nb[lane] = -et;
   gs.eq[lane] = fexp2(gt.lq);
   gs.e2[lane] = fexp2(gt.llast - gt.l);
-  if (lane == 0) gs.gam[0] = fexp2(gt.llast);
-  return r;
+  gs.al[lane] = al;
+  if (lane == 0) {
+    gs.gam[0] = fexp2(gt.llast);
+    gs.gam[1] = gt.llast;
+  }
 }
-
 // Block b of Be, written transposed: BeT[j][i] = Be_ij (j < i).
 template <int D>
 __device__ __forceinline__ void be_block(const SlotB<D>& sl, const GatesB& gs, __bf16* BeT,
@@ -196,7 +208,7 @@ struct SmemB {
   __bf16* L0;         // [D * kT]       Lam_out[:, K] (bf16) [row][col], even visits
   __bf16* L1;         // [D * kT]       odd visits
   __bf16* XS;         // [kC * kT]      e(lq_u) x_u[K]
-  GatesB& gs;
+  GatesB* gs;         // [3]            gates of the chunk of visit v in gs[v % 3]
   float* dots;        // [2][2][4][kC]  per-token dots by parity, column block, kind
   float* c0;          // [2][kNW]       <Lam_out, D_in> partials by parity, wave
 };
@@ -209,12 +221,11 @@ __device__ __forceinline__ void role_b_body(const BwdArgs& a, int64_t bh, int ti
                                             const SmemB<D>& m) {
   static_assert(D == 64 || D == 128, "D");
   constexpr int NS = D / 64;  // 16x16 Lam blocks per wave
-  constexpr int S = 2;        // stores per wave per chunk: dx, dalpha (or a dropped one)
+  constexpr int S = 2;        // stores per wave per chunk: dalpha (or a dropped one), dx
   SlotB<D>* const rs[2] = {&m.ring0, &m.ring1};
   __bf16* const BeT_s = m.BeT;
   __bf16* const L_s[2] = {m.L0, m.L1};
   __bf16* const XS_s = m.XS;
-  GatesB& gs = m.gs;
   float (*dots_s)[2][4][kC] = reinterpret_cast<float (*)[2][4][kC]>(m.dots);
   float (*c0_s)[kNW] = reinterpret_cast<float (*)[kNW]>(m.c0);
 
@@ -285,6 +296,7 @@ __device__ __forceinline__ void role_b_body(const BwdArgs& a, int64_t bh, int ti
                ? 0
                : static_cast<int>(std::min<int64_t>(kC, T - static_cast<int64_t>(c) * kC));
   };
+  const auto in_seg = [&](int c) { return c >= c_beg ? c : -1; };
   const DmaOffB<D> od = dma_off_b<D>(wave, lane);
   const uint32_t odx = static_cast<uint32_t>(((tb * 16 + l16) * D + k0 + cbw * 16 + 4 * g4) * 2);
   const uint32_t opa = static_cast<uint32_t>(lane * 4);
@@ -292,37 +304,51 @@ __device__ __forceinline__ void role_b_body(const BwdArgs& a, int64_t bh, int ti
   const int xs_row = tid >> 3;
   const uint32_t xs_off = static_cast<uint32_t>(sidx<kT>(xs_row, 4 * (tid & 7)) * 2);
 
-  // the last chunk, followed by S dropped stores (stream shape as in the loop)
-  issue_chunk_b<D>(*rs[0], od, dy, g, x, st, eta, alpha, T, c_end - 1, k0, wave);
-  store8(r_none, odx, make_uint2(0, 0));
+  // The last chunk (its tiles and the gate rows of the chunk before it) into
+  // slot 0; its own gate rows into slot 1, which the first visit's loads
+  // overwrite only after the gates are derived; then S dropped stores
+  // (stream shape as in the loop).
+  issue_chunk_b<D>(*rs[0], od, dy, g, x, st, eta, alpha, T, c_end - 1, in_seg(c_end - 2), k0,
+                   wave);
+  issue_gate_row(rs[1]->q, od.q, eta, alpha, T, c_end - 1, wave);
   store4(r_none, opa, 0.f);
-  LaneGatesB pg = {1.f, 0.f, 0.f, 0.f, 0.f};  // gates of the previous visit (lane = token)
+  store8(r_none, odx, make_uint2(0, 0));
+  wait_vm<S>();
+  lds_barrier();
+  if (wave == kGateWave) gates_b(rs[1]->q, m.gs[0], cv_of(c_end - 1), lane);
 
-  // dalpha of the chunk visited before, lane = token i (wave kDaWave only).
-  // The two suffix sums run on the reversed lane order; their inputs are
-  // read from LDS already reversed.
-  const auto dalpha = [&](int par, const LaneGatesB& lg) {
+  // The two parts of dalpha of a chunk (lane = token), written into its gate
+  // record; the store adds them.  Forward part: the <Lam_out, D_in> term,
+  // the forward affine scan sum_{j<i} e(l_{i-1} - l_j)(-eta_j) pp_j, and
+  // -kk_i / alpha_i.  Reversed part: sum_{u>i} e(l_{u-1} - l_i) rr_u and
+  // sum_{u>i} (qq_u - kk_u), run on the reversed lane order with inputs read
+  // from LDS reversed and the result written back reversed.
+  const auto dalpha_fwd = [&](int par, GatesB& gt) {
     const float* dt = &dots_s[par][0][0][0];
-    const int i = lane, ir = kC - 1 - lane;
-    const auto both = [&](int kind, int t) { return dt[kind * kC + t] + dt[4 * kC + kind * kC + t]; };
-    const float pp = both(0, i), kk = both(3, i);
-    const float rr_r = both(1, ir), z_r = both(2, ir) - both(3, ir);
+    const int i = lane;
+    const float pp = dt[0 * kC + i] + dt[4 * kC + 0 * kC + i];
+    const float kk = dt[3 * kC + i] + dt[4 * kC + 3 * kC + i];
     float c0 = 0.f;
 #pragma unroll
     for (int w = 0; w < kNW; ++w) c0 += c0_s[par][w];
-    // sum_{j<i} e(l_{i-1} - l_j) (-eta_j) pp_j: forward affine scan
-    float a2 = lg.al, b2 = lg.nb * pp;
+    const float al = gt.al[i], l = gt.li[i], lq = gt.lq[i], llast = gt.gam[1];
+    float a2 = al, b2 = gt.nb[i] * pp;
     wave_scan_affine(a2, b2);
     const float s2 = wave_shift_up(b2, 0.f);
-    // sum_{u>i} e(l_{u-1} - l_i) rr_u and sum_{u>i} (qq_u - kk_u): reversed scans
-    const float al_r = wave_reverse(lg.al, lane), lq_r = wave_reverse(lg.lq, lane);
+    gt.fpart[i] = fexp2(llast - l + lq) * c0 + fexp2(llast - l) * s2 -
+                  kk * __builtin_amdgcn_rcpf(al);
+  };
+  const auto dalpha_rev = [&](int par, GatesB& gt) {
+    const float* dt = &dots_s[par][0][0][0];
+    const int ir = kC - 1 - lane;
+    const auto both = [&](int kind) { return dt[kind * kC + ir] + dt[4 * kC + kind * kC + ir]; };
+    const float rr_r = both(1), z_r = both(2) - both(3);
+    const float al_r = gt.al[ir], lq_r = gt.lq[ir];
     float a3 = al_r, b3 = rr_r;
     wave_scan_affine(a3, b3);
     const float s3_r = wave_shift_up(b3, 0.f);
     const float zs_r = wave_shift_up(wave_scan_add(z_r), 0.f);
-    const float t34 = wave_reverse(fexp2(lq_r) * s3_r + zs_r * __builtin_amdgcn_rcpf(al_r), lane);
-    return fexp2(lg.llast - lg.l + lg.lq) * c0 + fexp2(lg.llast - lg.l) * s2 + t34 -
-           kk * __builtin_amdgcn_rcpf(lg.al);
+    gt.rpart[ir] = fexp2(lq_r) * s3_r + zs_r * __builtin_amdgcn_rcpf(al_r);
   };
 
   const auto step = [&](auto KC, int vis) {
@@ -332,23 +358,25 @@ __device__ __forceinline__ void role_b_body(const BwdArgs& a, int64_t bh, int ti
     const int c = c_end - 1 - vis;
     const int64_t t0 = static_cast<int64_t>(c) * kC;
     const int cv = cv_of(c);
+    GatesB& gc = m.gs[vis % 3];        // chunk c
+    GatesB& gn = m.gs[(vis + 1) % 3];  // chunk c + 2, then (phase 2) chunk c - 1
+    GatesB& gp = m.gs[(vis + 2) % 3];  // chunk c + 1
     wait_vm<S>();   // chunk c loaded: after it only the previous visit's stores
     lds_barrier();  // and the previous visit's reads of the other slot are done
-    issue_chunk_b<D>(dst, od, dy, g, x, st, eta, alpha, T, c - 1 >= c_beg ? c - 1 : -1, k0, wave);
+    issue_chunk_b<D>(dst, od, dy, g, x, st, eta, alpha, T, in_seg(c - 1), in_seg(c - 2), k0, wave);
 
     // ---- phase 1
-    const LaneGatesB lg = gates_b<D>(cur, gs, cv, lane);
     {
       // this thread's 4 elements of e(lq_u) x_u[K]
       const uint2 v = *reinterpret_cast<const uint2*>(reinterpret_cast<const char*>(cur.Xk) + xs_off);
-      const float s = gs.eq[xs_row];
+      const float s = gc.eq[xs_row];
       uint2 r;
       r.x = pack2(bf16_val(v.x & 0xffffu) * s, bf16_val(v.x >> 16) * s);
       r.y = pack2(bf16_val(v.y & 0xffffu) * s, bf16_val(v.y >> 16) * s);
       *reinterpret_cast<uint2*>(reinterpret_cast<char*>(XS_s) + xs_off) = r;
     }
-    be_block<D>(cur, gs, BeT_s, oD, oA, wave, lane);
-    if (wave < 2) be_block<D>(cur, gs, BeT_s, oD, oA, wave + 8, lane);
+    be_block<D>(cur, gc, BeT_s, oD, oA, wave, lane);
+    if (wave < 2) be_block<D>(cur, gc, BeT_s, oD, oA, wave + 8, lane);
     {
       // <Lam_out, D_in> over this wave's blocks
       float p = 0.f;
@@ -361,18 +389,16 @@ __device__ __forceinline__ void role_b_body(const BwdArgs& a, int64_t bh, int ti
       if (lane == 0) c0_s[vis & 1][wave] = p;
     }
     {
-      // dalpha of chunk c + 1 (its dots and partials are visible since the barrier)
-      const int cn = c + 1;
-      const bool fin = wave == kDaWave && vis > 0;
-      const __amdgpu_buffer_rsrc_t r_pa =
-          fin ? buffer_rsrc(pa + static_cast<int64_t>(cn) * kC, cv_of(cn) * 4) : r_none;
+      // dalpha of chunk c + 2 (its parts were formed in the previous visit);
       // the store stays outside the branch (one VMEM stream shape for all waves)
+      const bool fin = wave == kDaWave && vis >= 2;
+      const __amdgpu_buffer_rsrc_t r_pa =
+          fin ? buffer_rsrc(pa + static_cast<int64_t>(c + 2) * kC, cv_of(c + 2) * 4) : r_none;
       float v = 0.f;
-      if (wave == kDaWave) v = dalpha((vis + 1) & 1, pg);
+      if (wave == kDaWave) v = gn.fpart[lane] + gn.rpart[lane];
       store4(r_pa, opa, v);
     }
-    pg = lg;
-    lds_barrier();  // Be, e(lq) x, gates visible
+    lds_barrier();  // Be, e(lq) x visible; the gate record of chunk c + 2 is free
 
     // ---- phase 2: dx^T[c][i] of this wave's block, stored straight from the accumulators
     {
@@ -393,7 +419,7 @@ __device__ __forceinline__ void role_b_body(const BwdArgs& a, int64_t bh, int ti
         ak = mfma16x16x32(xf, frag_s<kC>(BeT_s, oA, tb * 16, kb * 32), ak);
       }
       const int i = tb * 16 + l16;
-      const float eqi = gs.eq[i], fl = gs.nb[i] * gs.e2[i];
+      const float eqi = gc.eq[i], fl = gc.nb[i] * gc.e2[i];
       const f32x4 v = aws + as_ * eqi + aq + ak + al * fl;
       uint2 pk;
       pk.x = pack2(v[0], v[1]);
@@ -425,7 +451,7 @@ __device__ __forceinline__ void role_b_body(const BwdArgs& a, int64_t bh, int ti
       bf16x8 xsf[2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) xsf[kb] = frag_ts<kT>(XS_s, oT, kb * 32, cbw * 16);
-      const float gam = gs.gam[0];
+      const float gam = gc.gam[0];
       __bf16* L_out = L_s[(vis + 1) & 1];
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
@@ -440,6 +466,12 @@ __device__ __forceinline__ void role_b_body(const BwdArgs& a, int64_t bh, int ti
         put4<kT>(L_out, oT, rb * 16, cbw * 16, pk);
       }
     }
+    // the gates of chunk c - 1 (its gate rows came with this chunk's tiles),
+    // and the two parts of dalpha of chunk c + 1 (dots and partials of the
+    // previous visit)
+    if (wave == kGateWave) gates_b(cur.q, gn, cv_of(c - 1), lane);
+    if (wave == kFwdWave && vis >= 1) dalpha_fwd((vis + 1) & 1, gp);
+    if (wave == kRevWave && vis >= 1) dalpha_rev((vis + 1) & 1, gp);
   };
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
@@ -448,11 +480,24 @@ __device__ __forceinline__ void role_b_body(const BwdArgs& a, int64_t bh, int ti
     if (vis + 1 >= nloc) break;
     step(I1{}, vis + 1);
   }
+  // dalpha of the last two chunks: chunk c_beg + 1 has its parts, chunk
+  // c_beg needs both
   wait_vm<0>();
   lds_barrier();
-  if (wave == kDaWave)
+  const int vl = nloc - 1;
+  GatesB& gl = m.gs[vl % 3];
+  if (wave == kFwdWave) dalpha_fwd(vl & 1, gl);
+  if (wave == kRevWave) dalpha_rev(vl & 1, gl);
+  lds_barrier();
+  if (wave == kDaWave) {
+    if (nloc >= 2) {
+      GatesB& g1 = m.gs[(vl + 2) % 3];
+      store4(buffer_rsrc(pa + static_cast<int64_t>(c_beg + 1) * kC, cv_of(c_beg + 1) * 4), opa,
+             g1.fpart[lane] + g1.rpart[lane]);
+    }
     store4(buffer_rsrc(pa + static_cast<int64_t>(c_beg) * kC, cv_of(c_beg) * 4), opa,
-           dalpha((nloc - 1) & 1, pg));
+           gl.fpart[lane] + gl.rpart[lane]);
+  }
 }
 
 }  // namespace

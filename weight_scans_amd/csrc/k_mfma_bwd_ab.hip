@@ -345,7 +345,8 @@ __device__ __forceinline__ void role_a2_body(const BwdArgs& a, int64_t bh, int t
 constexpr int kD = 64;
 constexpr size_t kRingBytes =
     sizeof(SlotB<kD>) > sizeof(SlotA2<kD>) ? sizeof(SlotB<kD>) : sizeof(SlotA2<kD>);
-constexpr size_t kGateBytes = sizeof(GatesB) > sizeof(GatesA2) ? sizeof(GatesB) : sizeof(GatesA2);
+constexpr size_t kGateBytes =
+    3 * sizeof(GatesB) > sizeof(GatesA2) ? 3 * sizeof(GatesB) : sizeof(GatesA2);
 
 __global__ __launch_bounds__(kNT, 4) void bwd_ab64(BwdArgs a) {
   __shared__ alignas(16) char ring0[kRingBytes], ring1[kRingBytes];
@@ -368,7 +369,7 @@ __global__ __launch_bounds__(kNT, 4) void bwd_ab64(BwdArgs a) {
     role_a2_body<kD, false>(a, bh, tile, seg, m);
   } else {
     const SmemB<kD> m{*reinterpret_cast<SlotB<kD>*>(ring0), *reinterpret_cast<SlotB<kD>*>(ring1),
-                      tt_s, L0_s, L1_s, sc_s, *reinterpret_cast<GatesB*>(gs_s), red_s,
+                      tt_s, L0_s, L1_s, sc_s, reinterpret_cast<GatesB*>(gs_s), red_s,
                       red_s + 2 * 2 * 4 * kC};
     role_b_body<kD>(a, bh, tile, seg, m);
   }

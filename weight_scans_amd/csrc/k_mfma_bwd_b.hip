@@ -13,7 +13,7 @@ __global__ __launch_bounds__(kNT) void bwd_b(BwdArgs a) {
   __shared__ __bf16 BeT_s[kC * kC];
   __shared__ __bf16 L0_s[D * kT], L1_s[D * kT];
   __shared__ __bf16 XS_s[kC * kT];
-  __shared__ GatesB gs;
+  __shared__ GatesB gs[3];
   __shared__ float dots_s[2 * 2 * 4 * kC];
   __shared__ float c0_s[2 * kNW];
   // (segment is the slowest index, so the XCD of a head does not change)
