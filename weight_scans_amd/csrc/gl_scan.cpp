@@ -54,6 +54,11 @@ struct Plan {
   int n_seg = 1, seg_chunks = 0;
   size_t seg_bytes = 0;     // per-segment states (fp32) + summed log2 alpha
   size_t seg_state_bytes = 0;
+  // chunk-parallel backward (matrix-core kernels, d = 64): stored Lam_out,
+  // per-chunk dots and <Lam_out, D_in> partials, dW0 partial groups
+  bool chunk_par = false;
+  int dw_groups = 1;
+  size_t lam_bytes = 0, dots_bytes = 0, c0_bytes = 0, gate_bytes = 0;
   const char* name = "";
 };
 
@@ -121,14 +126,28 @@ gl_status_t make_plan(const gl_scan_desc_t* d, Plan* p) {
   p->n_ckpt = p->n_chunks;
   p->saved_bytes = round_up(BH * p->n_ckpt * dd * p->state_elem);
   p->part_bytes = round_up(static_cast<size_t>(p->n_tiles) * BH * d->T * p->comp);
-  p->dw_bytes = round_up(BH * dd * p->comp * p->n_seg);
+  p->chunk_par = p->mfma && d->d_in == 64 && p->n_chunks > 0;
+  p->dw_groups = p->chunk_par ? gls::mfma_bwd_c64_groups(static_cast<int64_t>(BH), p->n_chunks)
+                              : p->n_seg;
+  p->dw_bytes = round_up(BH * dd * p->comp * p->dw_groups);
+  if (p->chunk_par) {
+    const gls::ChunkParLayout lay = gls::mfma_bwd_c64_layout();
+    const size_t items = BH * static_cast<size_t>(p->n_chunks);
+    p->n_tiles = lay.eta_parts;
+    p->part_bytes = round_up(static_cast<size_t>(p->n_tiles) * BH * d->T * p->comp);
+    p->lam_bytes = round_up(items * dd * 2);
+    p->dots_bytes = round_up(items * lay.dots_per_chunk * sizeof(float));
+    p->c0_bytes = round_up(items * lay.c0_per_chunk * sizeof(float));
+    p->gate_bytes = round_up(BH * d->T * sizeof(float)) + round_up(items * sizeof(float));
+  }
   return GL_SUCCESS;
 }
 
 // bwd workspace: deta / dalpha partials, dW0 partials, segment buffers (also
 // used by the state recompute, which runs first), recomputed states
 size_t bwd_ws(const Plan& p, bool have_saved) {
-  return 2 * p.part_bytes + p.dw_bytes + p.seg_bytes + (have_saved ? 0 : p.saved_bytes);
+  return 2 * p.part_bytes + p.dw_bytes + p.seg_bytes + (have_saved ? 0 : p.saved_bytes) +
+         p.lam_bytes + p.dots_bytes + p.c0_bytes + p.gate_bytes;
 }
 
 bool misaligned(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) != 0; }
@@ -253,9 +272,15 @@ gl_status_t gl_scan_bwd(const gl_scan_desc_t* desc, const void* x, const void* g
   void* part_alpha = w + p.part_bytes;
   void* part_dW0 = w + 2 * p.part_bytes;
   char* seg_ws = w + 2 * p.part_bytes + p.dw_bytes;
+  char* rec = seg_ws + p.seg_bytes;
+  char* lam_ws = rec + (saved ? 0 : p.saved_bytes);
+  float* dots_ws = reinterpret_cast<float*>(lam_ws + p.lam_bytes);
+  float* c0_ws = reinterpret_cast<float*>(lam_ws + p.lam_bytes + p.dots_bytes);
+  float* eq_ws = reinterpret_cast<float*>(lam_ws + p.lam_bytes + p.dots_bytes + p.c0_bytes);
+  float* gam_ws = eq_ws + round_up(static_cast<size_t>(desc->B * desc->H * desc->T) * sizeof(float)) /
+                              sizeof(float);
   const void* states = saved;
   if (!states) {
-    void* rec = seg_ws + p.seg_bytes;
     st = hip_status(
         launch_fwd(p, fwd_args(desc, p, x, g, eta, alpha, W0, nullptr, rec), seg_ws, s),
         "state recompute launch");
@@ -273,6 +298,36 @@ gl_status_t gl_scan_bwd(const gl_scan_desc_t* desc, const void* x, const void* g
   b.seg_chunks = p.seg_chunks; b.n_seg = p.n_seg;
   if (!p.mfma) {
     st = hip_status(gls::launch_generic_bwd(p.io, b, s), "backward launch");
+  } else if (p.chunk_par) {
+    // the adjoint chain alone, storing Lam_out of every chunk (per segment
+    // from its incoming adjoint if the sequence is cut into segments), then
+    // every chunk's outputs in parallel, then dalpha per chunk
+    gls::BwdArgs b1 = b;
+    b1.lam_out = lam_ws;
+    b1.gate_eq = eq_ws;
+    b1.gate_gam = gam_ws;
+    if (p.n_seg > 1) {
+      float* seg = reinterpret_cast<float*>(seg_ws);
+      float* lg = reinterpret_cast<float*>(seg_ws + p.seg_state_bytes);
+      gls::BwdArgs bs = b;
+      bs.seg_out = seg;
+      bs.seg_lg = lg;
+      st = hip_status(gls::launch_mfma_bwd_lam(bs, s), "backward segment pass");
+      if (st == GL_SUCCESS)
+        st = hip_status(gls::launch_seg_combine(seg, lg, b.B * b.H, p.n_seg, b.d_in * b.d_out,
+                                                true, s),
+                        "segment combine");
+      b1.seg_lam = seg;
+    }
+    if (st == GL_SUCCESS) st = hip_status(gls::launch_mfma_bwd_chain64(b1, s), "adjoint chain");
+    if (st == GL_SUCCESS) {
+      gls::BwdArgs b2 = b;
+      b2.lam_out = lam_ws;
+      b2.part_dots = dots_ws;
+      b2.part_c0 = c0_ws;
+      b2.dalpha_out = dalpha;
+      st = hip_status(gls::launch_mfma_bwd_c64(b2, s), "chunk pass");
+    }
   } else if (p.n_seg <= 1) {
     st = hip_status(gls::launch_mfma_bwd(b, s), "backward launch");
   } else {
@@ -301,7 +356,8 @@ gl_status_t gl_scan_bwd(const gl_scan_desc_t* desc, const void* x, const void* g
   f.part_eta = part_eta; f.part_alpha = part_alpha; f.part_dW0 = part_dW0;
   f.deta = deta; f.dalpha = dalpha; f.dW0 = dW0;
   f.B = desc->B; f.H = desc->H; f.T = desc->T;
-  f.d_in = b.d_in; f.d_out = b.d_out; f.n_tiles = p.n_tiles; f.n_seg = p.n_seg;
+  f.d_in = b.d_in; f.d_out = b.d_out; f.n_tiles = p.n_tiles; f.n_seg = p.dw_groups;
+  f.alpha_done = p.chunk_par;
   return hip_status(gls::launch_finalize(p.io, f, s), "finalize launch");
 }
 

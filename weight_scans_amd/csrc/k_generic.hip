@@ -361,10 +361,10 @@ __global__ __launch_bounds__(kThreads) void finalize_kernel(FinArgs a) {
     T se = T(0), sa = T(0);
     for (int k = 0; k < a.n_tiles; ++k) {
       se += pe[k * BHT + i];
-      sa += pa[k * BHT + i];
+      if (!a.alpha_done) sa += pa[k * BHT + i];
     }
     static_cast<T*>(a.deta)[i] = se;
-    static_cast<T*>(a.dalpha)[i] = sa;
+    if (!a.alpha_done) static_cast<T*>(a.dalpha)[i] = sa;
   }
   for (int64_t i = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; i < HD; i += stride) {
     T s = T(0);

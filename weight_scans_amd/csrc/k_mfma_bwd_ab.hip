@@ -104,7 +104,9 @@ __device__ __forceinline__ void role_a2_body(const BwdArgs& a, int64_t bh, int t
                                              const SmemA2<D>& m) {
   static_assert(D == 64 || D == 128, "D");
   constexpr int NS = D / 64;
-  constexpr int S = 2;  // stores per wave per chunk: dg, deta (or a dropped one)
+  // stores per wave per chunk: deta (or a dropped one), then dg -- or, in
+  // the adjoint-only pass, the NS blocks of Lam_out (dropped unless stored)
+  constexpr int S = LAM_ONLY ? 1 + NS : 2;
   SlotA2<D>* const rs[2] = {&m.ring0, &m.ring1};
   __bf16* const L_s[2] = {m.L0, m.L1};
   GatesA2& gs = m.gs;
@@ -174,8 +176,16 @@ __device__ __forceinline__ void role_a2_body(const BwdArgs& a, int64_t bh, int t
   wait_vm<0>();
 
   issue_chunk_a2<D>(*rs[0], od, x, dy, g, eta, alpha, T, c_end - 1, r0, wave);
-  store8(r_none, odg, make_uint2(0, 0));
+#pragma unroll
+  for (int k = 0; k < S - 1; ++k) store8(r_none, odg + 64 * k, make_uint2(0, 0));  // not merged
   store4(r_none, ope, 0.f);
+  // Lam_out stores of the adjoint-only pass: rows of this wave's blocks
+  uint16_t* lo = a.lam_out ? static_cast<uint16_t*>(a.lam_out) + bh * static_cast<int64_t>(n) * D * D
+                           : nullptr;
+  uint32_t olo[NS];
+#pragma unroll
+  for (int s = 0; s < NS; ++s)
+    olo[s] = static_cast<uint32_t>(((r0 + rbw * 16 + l16) * D + (tb + 4 * s) * 16 + 4 * g4) * 2);
   float lsum = 0.f;  // sum of l_last over the segment (adjoint-only pass)
 
   const auto step = [&](auto KC, int vis) {
@@ -251,7 +261,16 @@ __device__ __forceinline__ void role_a2_body(const BwdArgs& a, int64_t bh, int t
 
     // ---- phase 2: u, dg, deta partials
     if constexpr (LAM_ONLY) {
-      store8(r_none, odg, make_uint2(0, 0));  // stream shape as in the full pass
+      // Lam_out of chunk c (the adjoint entering it from the right), bf16
+      const __amdgpu_buffer_rsrc_t r_lo =
+          lo ? buffer_rsrc(lo + static_cast<int64_t>(c) * D * D, D * D * 2) : r_none;
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        uint2 pk;
+        pk.x = pack2(lam[s][0], lam[s][1]);
+        pk.y = pack2(lam[s][2], lam[s][3]);
+        store8(r_lo, olo[s], pk);
+      }
     } else {
       const __bf16* L_in = L_s[vis & 1];
       f32x4 ain = zero4(), apd = zero4();
@@ -315,13 +334,15 @@ __device__ __forceinline__ void role_a2_body(const BwdArgs& a, int64_t bh, int t
   wait_vm<0>();
   lds_barrier();
   if constexpr (LAM_ONLY) {
-    float* so = a.seg_out + (bh * a.n_seg + seg) * D * D;
+    if (a.seg_out) {
+      float* so = a.seg_out + (bh * a.n_seg + seg) * D * D;
 #pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      const int cb = tb + 4 * s;
-      *reinterpret_cast<f32x4*>(so + (r0 + rbw * 16 + l16) * D + cb * 16 + 4 * g4) = lam[s];
+      for (int s = 0; s < NS; ++s) {
+        const int cb = tb + 4 * s;
+        *reinterpret_cast<f32x4*>(so + (r0 + rbw * 16 + l16) * D + cb * 16 + 4 * g4) = lam[s];
+      }
+      if (tile == 0 && wave == 0 && lane == 0) a.seg_lg[bh * a.n_seg + seg] = lsum;
     }
-    if (tile == 0 && wave == 0 && lane == 0) a.seg_lg[bh * a.n_seg + seg] = lsum;
   } else {
     if (wave == kFinWaveA) {
       const float* rd = &red_s[(nloc - 1) & 1][0][0];
