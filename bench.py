@@ -61,7 +61,8 @@ def pass_kernels(w, which, segmented, generic):
         return {"fwd": "fwd_generic", "bwd": "bwd_generic + finalize_kernel"}[which]
     if which == "fwd":
         return ("fwd_mfma (state-only) + seg_combine + fwd_mfma" if segmented else "fwd_mfma")
-    body = "bwd_ab64" if w.d_in == 64 else "bwd_a + bwd_b"
+    body = ("chunk_gates_eq + bwd_chain64 + bwd_c64 + dalpha_chunks" if w.d_in == 64
+            else "bwd_a + bwd_b")
     if segmented:
         body = "bwd_lam + seg_combine + " + body
     return body + " + finalize_kernel"
