@@ -58,6 +58,11 @@ struct Plan {
   // per-chunk dots and <Lam_out, D_in> partials, dW0 partial groups
   bool chunk_par = false;
   int dw_groups = 1;
+  // fused backward (matrix-core kernels, d = 64): its own segment count (a
+  // work-group per segment and sequence-head), deta / dalpha written directly
+  bool fused = false;
+  int bwd_nseg = 1, bwd_seg_chunks = 0;
+  size_t bwd_seg_bytes = 0, bwd_seg_state_bytes = 0;
   size_t lam_bytes = 0, dots_bytes = 0, c0_bytes = 0, gate_bytes = 0;
   const char* name = "";
 };
@@ -126,9 +131,28 @@ gl_status_t make_plan(const gl_scan_desc_t* d, Plan* p) {
   p->n_ckpt = p->n_chunks;
   p->saved_bytes = round_up(BH * p->n_ckpt * dd * p->state_elem);
   p->part_bytes = round_up(static_cast<size_t>(p->n_tiles) * BH * d->T * p->comp);
-  p->chunk_par = p->mfma && d->d_in == 64 && p->n_chunks > 0;
-  p->dw_groups = p->chunk_par ? gls::mfma_bwd_c64_groups(static_cast<int64_t>(BH), p->n_chunks)
-                              : p->n_seg;
+  p->fused = p->mfma && d->d_in == 64 && p->n_chunks > 0;
+  p->chunk_par = false;
+  if (p->fused) {
+    int nb = 1;
+    if (d->segments > 0) {
+      nb = static_cast<int>(d->segments);
+    } else if (BH > 0 && static_cast<int64_t>(BH) < kSegTargetGroups) {
+      nb = static_cast<int>(std::min<int64_t>((kSegTargetGroups + BH - 1) / BH,
+                                              p->n_chunks / kMinSegChunks));
+    }
+    nb = std::max(1, std::min(nb, p->n_chunks));
+    p->bwd_seg_chunks = (p->n_chunks + nb - 1) / nb;
+    p->bwd_nseg = (p->n_chunks + p->bwd_seg_chunks - 1) / p->bwd_seg_chunks;
+    if (p->bwd_nseg > 1) {
+      p->bwd_seg_state_bytes = round_up(BH * p->bwd_nseg * dd * sizeof(float));
+      p->bwd_seg_bytes = p->bwd_seg_state_bytes + round_up(BH * p->bwd_nseg * sizeof(float));
+    }
+    p->part_bytes = 0;
+  }
+  p->dw_groups = p->fused       ? p->bwd_nseg
+                 : p->chunk_par ? gls::mfma_bwd_c64_groups(static_cast<int64_t>(BH), p->n_chunks)
+                                : p->n_seg;
   p->dw_bytes = round_up(BH * dd * p->comp * p->dw_groups);
   if (p->chunk_par) {
     const gls::ChunkParLayout lay = gls::mfma_bwd_c64_layout();
@@ -146,7 +170,8 @@ gl_status_t make_plan(const gl_scan_desc_t* d, Plan* p) {
 // bwd workspace: deta / dalpha partials, dW0 partials, segment buffers (also
 // used by the state recompute, which runs first), recomputed states
 size_t bwd_ws(const Plan& p, bool have_saved) {
-  return 2 * p.part_bytes + p.dw_bytes + p.seg_bytes + (have_saved ? 0 : p.saved_bytes) +
+  return 2 * p.part_bytes + p.dw_bytes + std::max(p.seg_bytes, p.bwd_seg_bytes) +
+         (have_saved ? 0 : p.saved_bytes) +
          p.lam_bytes + p.dots_bytes + p.c0_bytes + p.gate_bytes;
 }
 
@@ -272,7 +297,7 @@ gl_status_t gl_scan_bwd(const gl_scan_desc_t* desc, const void* x, const void* g
   void* part_alpha = w + p.part_bytes;
   void* part_dW0 = w + 2 * p.part_bytes;
   char* seg_ws = w + 2 * p.part_bytes + p.dw_bytes;
-  char* rec = seg_ws + p.seg_bytes;
+  char* rec = seg_ws + std::max(p.seg_bytes, p.bwd_seg_bytes);
   char* lam_ws = rec + (saved ? 0 : p.saved_bytes);
   float* dots_ws = reinterpret_cast<float*>(lam_ws + p.lam_bytes);
   float* c0_ws = reinterpret_cast<float*>(lam_ws + p.lam_bytes + p.dots_bytes);
@@ -298,6 +323,29 @@ gl_status_t gl_scan_bwd(const gl_scan_desc_t* desc, const void* x, const void* g
   b.seg_chunks = p.seg_chunks; b.n_seg = p.n_seg;
   if (!p.mfma) {
     st = hip_status(gls::launch_generic_bwd(p.io, b, s), "backward launch");
+  } else if (p.fused) {
+    // one work-group per (segment, sequence-head) walks its chunks from the
+    // right; with segments, an adjoint-only pass per segment and the
+    // exclusive affine scan over segments give each its entering adjoint
+    gls::BwdArgs bf = b;
+    bf.seg_chunks = p.bwd_seg_chunks;
+    bf.n_seg = p.bwd_nseg;
+    bf.dalpha_out = dalpha;
+    bf.deta_out = deta;
+    if (p.bwd_nseg > 1) {
+      float* seg = reinterpret_cast<float*>(seg_ws);
+      float* lg = reinterpret_cast<float*>(seg_ws + p.bwd_seg_state_bytes);
+      gls::BwdArgs bs = bf;
+      bs.seg_out = seg;
+      bs.seg_lg = lg;
+      st = hip_status(gls::launch_mfma_bwd_lam(bs, s), "backward segment pass");
+      if (st == GL_SUCCESS)
+        st = hip_status(gls::launch_seg_combine(seg, lg, b.B * b.H, p.bwd_nseg,
+                                                b.d_in * b.d_out, true, s),
+                        "segment combine");
+      bf.seg_lam = seg;
+    }
+    if (st == GL_SUCCESS) st = hip_status(gls::launch_mfma_bwd_f64(bf, s), "fused backward");
   } else if (p.chunk_par) {
     // the adjoint chain alone, storing Lam_out of every chunk (per segment
     // from its incoming adjoint if the sequence is cut into segments), then
@@ -357,7 +405,8 @@ gl_status_t gl_scan_bwd(const gl_scan_desc_t* desc, const void* x, const void* g
   f.deta = deta; f.dalpha = dalpha; f.dW0 = dW0;
   f.B = desc->B; f.H = desc->H; f.T = desc->T;
   f.d_in = b.d_in; f.d_out = b.d_out; f.n_tiles = p.n_tiles; f.n_seg = p.dw_groups;
-  f.alpha_done = p.chunk_par;
+  f.alpha_done = p.chunk_par || p.fused;
+  f.eta_done = p.fused;
   return hip_status(gls::launch_finalize(p.io, f, s), "finalize launch");
 }
 

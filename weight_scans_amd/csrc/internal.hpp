@@ -76,6 +76,8 @@ struct BwdArgs {
   void* dalpha_out = nullptr;
   float* gate_eq = nullptr;   // e(lq) per token [B*H*T] (adjoint chain)
   float* gate_gam = nullptr;  // e(l_last) per chunk [B*H][n_chunks]
+  // Fused backward (d = 64): deta written directly ([B,H,T]), with dalpha_out.
+  void* deta_out = nullptr;
 };
 
 struct FinArgs {
@@ -89,7 +91,8 @@ struct FinArgs {
   int d_in, d_out;
   int n_tiles;
   int n_seg = 1;             // dW0 partials per (b, h)
-  bool alpha_done = false;   // dalpha already written (chunk-parallel backward)
+  bool alpha_done = false;   // dalpha already written (chunk-parallel / fused backward)
+  bool eta_done = false;     // deta already written (fused backward)
 };
 
 // Generic (VALU) kernels: any 1 <= d_in, d_out <= 128, all io types.
@@ -111,6 +114,7 @@ hipError_t launch_mfma_bwd_ab64(const BwdArgs& a, hipStream_t s);  // both, one 
 hipError_t launch_mfma_bwd_lam(const BwdArgs& a, hipStream_t s);  // adjoint-only segment pass
 hipError_t launch_mfma_bwd_c64(const BwdArgs& a, hipStream_t s);  // chunk pass + dalpha, d = 64
 hipError_t launch_mfma_bwd_chain64(const BwdArgs& a, hipStream_t s);  // gates + adjoint chain, d = 64
+hipError_t launch_mfma_bwd_f64(const BwdArgs& a, hipStream_t s);  // fused reverse scan, d = 64
 int mfma_bwd_c64_groups(int64_t BH, int n_chunks);                 // its dW0 partials per (b, h)
 struct ChunkParLayout {
   int eta_parts;       // deta partials per token (part_eta: [eta_parts][B*H*T])

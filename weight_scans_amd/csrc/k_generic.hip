@@ -357,13 +357,14 @@ __global__ __launch_bounds__(kThreads) void finalize_kernel(FinArgs a) {
   const T* pe = static_cast<const T*>(a.part_eta);
   const T* pa = static_cast<const T*>(a.part_alpha);
   const T* pw = static_cast<const T*>(a.part_dW0);
-  for (int64_t i = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; i < BHT; i += stride) {
+  for (int64_t i = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x;
+       !(a.eta_done && a.alpha_done) && i < BHT; i += stride) {
     T se = T(0), sa = T(0);
     for (int k = 0; k < a.n_tiles; ++k) {
-      se += pe[k * BHT + i];
+      if (!a.eta_done) se += pe[k * BHT + i];
       if (!a.alpha_done) sa += pa[k * BHT + i];
     }
-    static_cast<T*>(a.deta)[i] = se;
+    if (!a.eta_done) static_cast<T*>(a.deta)[i] = se;
     if (!a.alpha_done) static_cast<T*>(a.dalpha)[i] = sa;
   }
   for (int64_t i = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; i < HD; i += stride) {
@@ -427,7 +428,8 @@ hipError_t launch_generic_bwd(int io, const BwdArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_finalize(int io, const FinArgs& a, hipStream_t s) {
-  const int64_t n = std::max<int64_t>(a.B * a.H * a.T, a.H * static_cast<int64_t>(a.d_in) * a.d_out);
+  const int64_t n = std::max<int64_t>((a.eta_done && a.alpha_done) ? 0 : a.B * a.H * a.T,
+                                      a.H * static_cast<int64_t>(a.d_in) * a.d_out);
   const unsigned blocks = static_cast<unsigned>(std::min<int64_t>(4096, (n + kThreads - 1) / kThreads));
   if (blocks == 0) return hipSuccess;
   if (io == IO_F64)

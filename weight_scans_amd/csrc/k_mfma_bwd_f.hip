@@ -1,0 +1,692 @@
+// k_mfma_bwd_f.hip -- fused matrix-core reverse scan for bf16 io,
+// d_in = d_out = 64 (gfx950, v_mfma_f32_16x16x32_bf16).
+//
+// One work-group walks the chunks of one (segment, sequence-head) from right
+// to left carrying the adjoint Lam = dL/dD (the exact adjoint of the forward
+// scan, GradLev abstract, omanscience.com) in fp32 registers, and emits every
+// gradient of the chunk it passes.  With chunk-local l (inclusive cumsum of
+// log2 alpha), lq_i = l_{i-1}, e(.) = 2^(.), XX_ui = x_u . x_i:
+//   P_ui  = e(lq_u - l_i) XX_ui                         (u > i)
+//   Be_ij = e(lq_i - l_j)(-eta_j)(dy_i . g_j)           (j < i),  M = Be + Be^T
+//   u_i   = e(l_last - l_i) Lam_out x_i + sum_{u>i} P_ui dy_u
+//   dg_i  = -eta_i u_i,  deta_i = -g_i . u_i
+//   dx_i  = W0^T dy_i + e(lq_i) D_in^T dy_i + (M X)_i - eta_i e(l_last - l_i) Lam_out^T g_i
+//   dW0  += sum_u dy_u x_u^T
+//   Lam_in = e(l_last) Lam_out + sum_u e(lq_u) dy_u x_u^T
+// and dalpha from the dots pp_i = g_i . (Lam_out x_i), rr_i = x_i . (D_in^T dy_i),
+// qq_i = sum_{j<i} Be_ij XX_ij, kk_j = sum_{u>j} Be_uj XX_uj and <Lam_out, D_in>
+// (the rows and columns of Be o XX give the two Be dots without a product).
+// D_in is the chunk-start state the forward kernel stores.
+//
+// Sixteen waves, one of each role on every SIMD (role = wave / 4, quadrant =
+// wave % 4; 32 x 32 output quadrants, so every fragment read serves two
+// MFMAs):
+//   0  dx^T quadrant (columns k, tokens i), its rr share;
+//   1  Lam^T and dW0^T quadrant (columns k, rows r) in fp32 registers, the
+//      <Lam_out, D_in> share, the bf16 copy of the next Lam_out;
+//   2  u^T quadrant (rows r, tokens i): dg, the deta and pp shares;
+//   3  causal 16 x 16 blocks of XX and of dy.g for the NEXT chunk: P^T, M,
+//      the qq / kk partials; wave 14 also derives the gates of the chunk
+//      after it, wave 15 finishes dalpha and deta of the previous chunk.
+// Chunk tiles (x, g, dy, D_in, and the gate rows of the chunk after) come by
+// direct buffer loads into a ring of three slots: while the chunk of step j
+// is finished and the causal blocks of chunk j + 1 are formed, chunk j + 2
+// is in flight.  One barrier per chunk; every wave issues the same vector-
+// memory instructions (three loads, four 8-byte and two 4-byte stores, the
+// unused ones into zero-byte buffers), so the wait at the top of a step is a
+// constant.
+#include <algorithm>
+#include <cstddef>
+#include <type_traits>
+
+#include "dev_common.hpp"
+#include "internal.hpp"
+#include "mfma.hpp"
+
+namespace gls {
+namespace {
+
+constexpr int kD = 64;          // d_in = d_out
+constexpr int kC = 64;          // tokens per chunk
+constexpr int kNW = 16;         // waves per work-group
+constexpr int kNT = 64 * kNW;   // threads
+constexpr int kGateWave = 14;   // derives the gates two chunks ahead
+constexpr int kAlphaWave = 15;  // dalpha and deta one chunk behind
+constexpr int kLoads = 3;       // vector-memory loads per wave per step
+constexpr int kStores = 6;      // vector-memory stores per wave per step
+static_assert(kLoads == 3, "issue_f issues three loads");
+
+struct alignas(16) SlotF {
+  __bf16 X[kC * kD];    // x, swizzled [token][k]
+  __bf16 G[kC * kD];    // g, swizzled [token][r]
+  __bf16 DY[kC * kD];   // dy, swizzled [token][r]
+  __bf16 S[kD * kD];    // D_in, swizzled [r][k]
+  float q[2][kC];       // eta, alpha of the chunk after (in walk order)
+};
+
+struct alignas(16) RecF {  // gates of one chunk, lane = token
+  float lq[kC], li[kC], nb[kC], eq[kC], e2[kC], al[kC];
+  float gam, llast, pad[2];
+};
+
+struct alignas(16) PartF {  // per-token shares of one chunk
+  float pp[2][kC], rr[2][kC], de[2][kC];
+  float c0[4];
+};
+
+struct alignas(16) QkF {  // per causal block: row sums (qq) and column sums (kk) of Be o XX
+  float qq[10][16], kk[10][16];
+};
+
+// Per-lane byte offset of instruction wi (of 8) of a [64][64] bf16 tile load
+// into a swizzled LDS tile (lane i fills 16-byte slot i of the instruction).
+__device__ __forceinline__ uint32_t dma_off_f(int wi, int lane) {
+  const int p = wi * 64 + lane;
+  const int row = p >> 3, kl = (p & 7) ^ swz<kD>(row);
+  return static_cast<uint32_t>(row * kD * 2 + 16 * kl);
+}
+
+// Tiles of chunk k (negative: zero fill) and the gate rows of chunk kq.
+// Waves 0-7 load instruction w of the x and dy tiles, waves 8-15 instruction
+// w - 8 of the g and D_in tiles: the same three instructions in every wave.
+__device__ __forceinline__ void issue_f(SlotF& sl, uint32_t ot, uint32_t oq, const uint16_t* x,
+                                        const uint16_t* g, const uint16_t* dy, const uint16_t* st,
+                                        const float* eta, const float* alpha, int64_t T, int k,
+                                        int kq, int wave) {
+  const bool in = k >= 0;
+  const int64_t t0 = in ? static_cast<int64_t>(k) * kC : 0;
+  const int cv = in ? static_cast<int>(std::min<int64_t>(kC, T - t0)) : 0;
+  const int64_t s0 = (in ? static_cast<int64_t>(k) : 0) * kD * kD;
+  const bool lo = wave < 8;
+  const int wi = wave & 7;
+  char* base = reinterpret_cast<char*>(&sl);
+  const int o1 = (lo ? static_cast<int>(offsetof(SlotF, X)) : static_cast<int>(offsetof(SlotF, G))) +
+                 wi * 1024;
+  const int o2 = (lo ? static_cast<int>(offsetof(SlotF, DY)) : static_cast<int>(offsetof(SlotF, S))) +
+                 wi * 1024;
+  dma16(buffer_rsrc((lo ? x : g) + t0 * kD, cv * kD * 2), ot, base + o1);
+  dma16(lo ? buffer_rsrc(dy + t0 * kD, cv * kD * 2) : buffer_rsrc(st + s0, in ? kD * kD * 2 : 0),
+        ot, base + o2);
+  const bool inq = kq >= 0;
+  const int64_t tq = inq ? static_cast<int64_t>(kq) * kC : 0;
+  const int cq = inq ? static_cast<int>(std::min<int64_t>(kC, T - tq)) : 0;
+  dma4(buffer_rsrc(((wave & 1) == 0 ? eta : alpha) + tq, cq * 4), oq, sl.q[wave & 1]);
+}
+
+// Gates of a chunk from its eta / alpha rows (one wave, lane = token).
+// Padding tokens carry alpha = 1, eta = 0.
+__device__ __forceinline__ void gates_f(const float (*q)[kC], RecF& r, int cv, int lane) {
+  const float et = lane < cv ? q[0][lane] : 0.f;
+  const float al = lane < cv ? q[1][lane] : 1.f;
+  const ChunkGates gt = chunk_gates(al, lane);
+  r.lq[lane] = gt.lq;
+  r.li[lane] = gt.l;
+  r.nb[lane] = -et;
+  r.eq[lane] = fexp2(gt.lq);
+  r.e2[lane] = fexp2(gt.llast - gt.l);
+  r.al[lane] = al;
+  if (lane == 0) {
+    r.gam = fexp2(gt.llast);
+    r.llast = gt.llast;
+  }
+}
+
+__device__ __forceinline__ f32x4 unpack4f(const uint2& p) {
+  f32x4 v;
+  v[0] = bf16_val(p.x & 0xffffu);
+  v[1] = bf16_val(p.x >> 16);
+  v[2] = bf16_val(p.y & 0xffffu);
+  v[3] = bf16_val(p.y >> 16);
+  return v;
+}
+
+__device__ __forceinline__ float dot4f(const f32x4& a, const f32x4& b) {
+  return a[0] * b[0] + a[1] * b[1] + a[2] * b[2] + a[3] * b[3];
+}
+
+__device__ __forceinline__ uint2 pack4f(const f32x4& v) {
+  uint2 pk;
+  pk.x = pack2(v[0], v[1]);
+  pk.y = pack2(v[2], v[3]);
+  return pk;
+}
+
+// The 8 bf16 of a fragment, each times its own factor (e0: elements 0-3,
+// e1: 4-7), rounded back to bf16.
+__device__ __forceinline__ bf16x8 scale8(const bf16x8& f, const f32x4& e0, const f32x4& e1) {
+  bf16x8 r;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    r[q] = static_cast<__bf16>(static_cast<float>(f[q]) * e0[q]);
+    r[q + 4] = static_cast<__bf16>(static_cast<float>(f[q + 4]) * e1[q]);
+  }
+  return r;
+}
+
+// Sum over the 16 lanes of each row of 16; valid in lane 15 of the row.
+__device__ __forceinline__ float row16_sum(float x) {
+  x += dpp<kRowShr1>(0.f, x);
+  x += dpp<kRowShr2>(0.f, x);
+  x += dpp<kRowShr4>(0.f, x);
+  x += dpp<kRowShr8>(0.f, x);
+  return x;
+}
+
+// Causal block b (0..9) of the chunk in `sl`: rows a (block tri_i), columns
+// b' (block tri_j).  XX_ab' and dy_a . g_b' on the matrix cores, then
+//   P^T[b'][a] = e(lq_a - l_b') XX_ab',  M[b'][a] = M[a][b'] = Be_ab'
+// (zero unless b' < a), and the row / column sums of Be o XX.
+__device__ __forceinline__ void causal_f(const SlotF& sl, const RecF& r, __bf16* PT, __bf16* M,
+                                         QkF& qk, const LaneOff<kD>& o, int b, int lane) {
+  const int g4 = lane >> 4, l16 = lane & 15;
+  const int rb = tri_i(b), cb = tri_j(b);
+  f32x4 xx = zero4(), be = zero4();
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk) {
+    xx = mfma16x16x32(frag_s<kD>(sl.X, o, rb * 16, kk * 32), frag_s<kD>(sl.X, o, cb * 16, kk * 32), xx);
+    be = mfma16x16x32(frag_s<kD>(sl.DY, o, rb * 16, kk * 32), frag_s<kD>(sl.G, o, cb * 16, kk * 32),
+                      be);
+  }
+  const int col = cb * 16 + l16, r0 = rb * 16 + 4 * g4;
+  const float lc = r.li[col], nbc = r.nb[col];
+  const f32x4 lqr = *reinterpret_cast<const f32x4*>(&r.lq[r0]);
+  f32x4 p, v, z;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const float e = fexp2(lqr[q] - lc);
+    const bool m = col < r0 + q;
+    p[q] = m ? xx[q] * e : 0.f;
+    v[q] = m ? be[q] * (e * nbc) : 0.f;
+    z[q] = v[q] * xx[q];
+  }
+  put4<kC>(PT, o, cb * 16, rb * 16, pack4f(p));
+  put4<kC>(M, o, cb * 16, rb * 16, pack4f(v));
+  // the mirrored half of M, element by element (after the put4 above: on the
+  // diagonal block both touch the same bytes, and one wave's LDS writes land
+  // in order)
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    if (col < r0 + q) M[sidx<kC>(r0 + q, col)] = static_cast<__bf16>(v[q]);
+  f32x4 zr;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) zr[q] = row16_sum(z[q]);
+  if (l16 == 15) *reinterpret_cast<f32x4*>(&qk.qq[b][4 * g4]) = zr;
+  const float t = sum_rows(z[0] + z[1] + z[2] + z[3]);
+  if (g4 == 0) qk.kk[b][l16] = t;
+}
+
+__global__ __launch_bounds__(kNT) void bwd_f64(BwdArgs a) {
+  __shared__ SlotF ring0, ring1, ring2;
+  __shared__ __bf16 PT_s[2][kC * kC];  // P^T by chunk parity (W0 staging at the start)
+  __shared__ __bf16 M_s[2][kC * kC];   // Be + Be^T by chunk parity
+  __shared__ __bf16 L_s[2][kD * kD];   // Lam_out (bf16, [r][k]) by chunk parity
+  __shared__ RecF rec[4];
+  __shared__ PartF part[2];
+  __shared__ QkF qk[3];
+  SlotF* const rs[3] = {&ring0, &ring1, &ring2};
+
+  const int64_t BH = a.B * a.H, T = a.T;
+  const int n = a.n_chunks;
+  const int64_t bh = blockIdx.x % BH;
+  const int seg = static_cast<int>(blockIdx.x / BH);
+  const int c_beg = seg * a.seg_chunks;
+  const int c_end = std::min(n, c_beg + a.seg_chunks);
+  const int nloc = c_end - c_beg;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int role = wave >> 2, qd = wave & 3;
+  const int g4 = lane >> 4, l16 = lane & 15;
+  const int hq = qd >> 1, lq2 = qd & 1;  // quadrant: high / low half
+  const int h = static_cast<int>(bh % a.H);
+  const uint16_t* x = static_cast<const uint16_t*>(a.x) + bh * T * kD;
+  const uint16_t* g = static_cast<const uint16_t*>(a.g) + bh * T * kD;
+  const uint16_t* dy = static_cast<const uint16_t*>(a.dy) + bh * T * kD;
+  const float* eta = static_cast<const float*>(a.eta) + bh * T;
+  const float* alpha = static_cast<const float*>(a.alpha) + bh * T;
+  const uint16_t* W0 = static_cast<const uint16_t*>(a.W0) + static_cast<int64_t>(h) * kD * kD;
+  const uint16_t* st = static_cast<const uint16_t*>(a.states) + bh * static_cast<int64_t>(n) * kD * kD;
+  uint16_t* dx = static_cast<uint16_t*>(a.dx) + bh * T * kD;
+  uint16_t* dg = static_cast<uint16_t*>(a.dg) + bh * T * kD;
+  float* dal = static_cast<float*>(a.dalpha_out) + bh * T;
+  float* det = static_cast<float*>(a.deta_out) + bh * T;
+
+  const LaneOff<kD> o_in = lane_off<kD>(lane);
+  const LaneOff<kD>& o = o_in;
+  const uint32_t ot = dma_off_f(wave & 7, lane);
+  const uint32_t oq = static_cast<uint32_t>(lane * 4);
+  const __amdgpu_buffer_rsrc_t r_none = buffer_rsrc(a.x, 0);
+
+  // chunk visited v-th (-1: none)
+  const auto chunk_at = [&](int v) { return (v >= 0 && v < nloc) ? c_end - 1 - v : -1; };
+  const auto cv_of = [&](int c) {
+    return c < 0 ? 0 : static_cast<int>(std::min<int64_t>(kC, T - static_cast<int64_t>(c) * kC));
+  };
+
+  // ---- set-up: loads of the first chunk (into slot 1, with the gate rows of
+  // the second) and of its own gate rows (slot 0), W0, the entering adjoint
+  issue_f(*rs[1], ot, oq, x, g, dy, st, eta, alpha, T, chunk_at(0), chunk_at(1), wave);
+  {
+    const int c0 = chunk_at(0);
+    dma4(buffer_rsrc(((wave & 1) == 0 ? eta : alpha) + (c0 >= 0 ? static_cast<int64_t>(c0) * kC : 0),
+                     cv_of(c0) * 4),
+         oq, rs[0]->q[wave & 1]);
+  }
+  // W0 (bf16 [r][k]) staged in PT_s[1]; dx waves keep W0^T fragments
+  for (int idx = tid; idx < kD * kD / 8; idx += kNT) {
+    const int r = idx >> 3, cc = 8 * (idx & 7);
+    *reinterpret_cast<uint4*>(&PT_s[1][sidx<kD>(r, cc)]) =
+        *reinterpret_cast<const uint4*>(W0 + static_cast<int64_t>(r) * kD + cc);
+  }
+  // Registers a wave keeps for the whole walk, by role (one array, so that
+  // the roles share them):
+  //   role 0: pr[2a + kk] = W0^T fragment (column block 2hq + a, K block kk of r)
+  //   role 1: pr[2a + b] = Lam^T block, pr[4 + 2a + b] = dW0^T block
+  //           (k block 2hq + a, r block 2lq2 + b; lane: k = 4 g4 + q, r = l16)
+  f32x4 pr[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) pr[e] = zero4();
+  if (role == 1 && a.seg_lam) {
+    const float* sl = a.seg_lam + (bh * a.n_seg + seg) * kD * kD;
+#pragma unroll
+    for (int aa = 0; aa < 2; ++aa)
+#pragma unroll
+      for (int bb = 0; bb < 2; ++bb)
+        pr[2 * aa + bb] = *reinterpret_cast<const f32x4*>(
+            sl + ((2 * lq2 + bb) * 16 + l16) * kD + (2 * hq + aa) * 16 + 4 * g4);
+  }
+  wait_vm<0>();
+  __syncthreads();
+  if (role == 0) {
+#pragma unroll
+    for (int aa = 0; aa < 2; ++aa)
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+        pr[2 * aa + kk] =
+            __builtin_bit_cast(f32x4, frag_ts<kD>(PT_s[1], o, kk * 32, (2 * hq + aa) * 16));
+  }
+  __syncthreads();
+  for (int idx = tid; idx < 2 * kC * kC / 8; idx += kNT)
+    reinterpret_cast<uint4*>(&PT_s[0][0])[idx] = make_uint4(0, 0, 0, 0);
+  if (role == 1) {
+#pragma unroll
+    for (int aa = 0; aa < 2; ++aa)
+#pragma unroll
+      for (int bb = 0; bb < 2; ++bb)
+        put4<kD>(L_s[0], o, (2 * lq2 + bb) * 16, (2 * hq + aa) * 16, pack4f(pr[2 * aa + bb]));
+  }
+  if (wave == kGateWave) gates_f(rs[0]->q, rec[0], cv_of(chunk_at(0)), lane);
+
+  // per-lane offsets of the dx / dg stores: token 16(2 lq2 + b) + l16,
+  // columns 16(2 hq + a) + 4 g4 ..
+  const uint32_t o8_in = static_cast<uint32_t>((2 * lq2 * 16 + l16) * kD * 2 + (2 * hq * 16 + 4 * g4) * 2);
+
+  // step j: chunk v = j finished (slot K), causal blocks of v = j + 1, loads
+  // of v = j + 2; K = (j + 1) % 3
+  const auto step = [&](auto RC, auto KC, int j) {
+    constexpr int R = decltype(RC)::value;
+    constexpr int K = decltype(KC)::value;
+    SlotF& cur = *rs[K];
+    SlotF& nx = *rs[(K + 1) % 3];
+    SlotF& dst = *rs[(K + 2) % 3];
+    wait_vm<kStores>();  // chunk j + 1 loaded: after it only the previous step's stores
+    lds_barrier();       // and every read of the slot about to be refilled is done
+    // per-lane offsets passed through an empty asm: the addresses derived
+    // from them are formed inside the step instead of being kept live
+    // across the whole walk for every slot and role
+    LaneOff<kD> o = o_in;
+    uint32_t o8 = o8_in;
+    asm volatile("" : "+v"(o.b), "+v"(o.t0), "+v"(o.t1), "+v"(o.w), "+v"(o8));
+    issue_f(dst, ot, oq, x, g, dy, st, eta, alpha, T, chunk_at(j + 2), chunk_at(j + 3), wave);
+
+    const int c = chunk_at(j);
+    const int64_t t0 = c >= 0 ? static_cast<int64_t>(c) * kC : 0;
+    const int cv = cv_of(c);
+    uint2 s8[2][2];
+#pragma unroll
+    for (int aa = 0; aa < 2; ++aa)
+#pragma unroll
+      for (int bb = 0; bb < 2; ++bb) s8[aa][bb] = make_uint2(0, 0);
+    float s4a = 0.f, s4b = 0.f;
+    __amdgpu_buffer_rsrc_t r8 = r_none, ra = r_none, rb = r_none;
+
+    if constexpr (R == 0) {
+      if (c >= 0) {
+        // dx^T[k][i]: k block 2hq + a, token block 2lq2 + b
+        const RecF& rc = rec[j & 3];
+        const __bf16* L = L_s[j & 1];
+        const __bf16* M = M_s[j & 1];
+        float sc[2], eqv[2];
+#pragma unroll
+        for (int bb = 0; bb < 2; ++bb) {
+          const int i = (2 * lq2 + bb) * 16 + l16;
+          sc[bb] = rc.nb[i] * rc.e2[i];
+          eqv[bb] = rc.eq[i];
+        }
+        f32x4 acc[2][2];
+        {
+          // -eta_i e(l_last - l_i) Lam_out^T g_i
+          f32x4 t[2][2];
+#pragma unroll
+          for (int aa = 0; aa < 2; ++aa)
+#pragma unroll
+            for (int bb = 0; bb < 2; ++bb) t[aa][bb] = zero4();
+#pragma unroll
+          for (int kk = 0; kk < 2; ++kk) {
+            __builtin_amdgcn_sched_barrier(0);  // one K step of fragments live at a time
+            bf16x8 lf[2], gf[2];
+#pragma unroll
+            for (int aa = 0; aa < 2; ++aa) lf[aa] = frag_ts<kD>(L, o, kk * 32, (2 * hq + aa) * 16);
+#pragma unroll
+            for (int bb = 0; bb < 2; ++bb) gf[bb] = frag_s<kD>(cur.G, o, (2 * lq2 + bb) * 16, kk * 32);
+#pragma unroll
+            for (int aa = 0; aa < 2; ++aa)
+#pragma unroll
+              for (int bb = 0; bb < 2; ++bb) t[aa][bb] = mfma16x16x32(lf[aa], gf[bb], t[aa][bb]);
+          }
+#pragma unroll
+          for (int aa = 0; aa < 2; ++aa)
+#pragma unroll
+            for (int bb = 0; bb < 2; ++bb) acc[aa][bb] = t[aa][bb] * sc[bb];
+        }
+        {
+          // e(lq_i) D_in^T dy_i, and rr_i = x_i . (D_in^T dy_i) over this k half
+          f32x4 t[2][2];
+#pragma unroll
+          for (int aa = 0; aa < 2; ++aa)
+#pragma unroll
+            for (int bb = 0; bb < 2; ++bb) t[aa][bb] = zero4();
+#pragma unroll
+          for (int kk = 0; kk < 2; ++kk) {
+            __builtin_amdgcn_sched_barrier(0);  // one K step of fragments live at a time
+            bf16x8 sf[2], df[2];
+#pragma unroll
+            for (int aa = 0; aa < 2; ++aa) sf[aa] = frag_ts<kD>(cur.S, o, kk * 32, (2 * hq + aa) * 16);
+#pragma unroll
+            for (int bb = 0; bb < 2; ++bb) df[bb] = frag_s<kD>(cur.DY, o, (2 * lq2 + bb) * 16, kk * 32);
+#pragma unroll
+            for (int aa = 0; aa < 2; ++aa)
+#pragma unroll
+              for (int bb = 0; bb < 2; ++bb) t[aa][bb] = mfma16x16x32(sf[aa], df[bb], t[aa][bb]);
+          }
+          PartF& pw = part[j & 1];
+#pragma unroll
+          for (int bb = 0; bb < 2; ++bb) {
+            float rp = 0.f;
+#pragma unroll
+            for (int aa = 0; aa < 2; ++aa) {
+              const f32x4 xv = unpack4f(get4<kD>(cur.X, o, (2 * lq2 + bb) * 16, (2 * hq + aa) * 16));
+              rp += dot4f(xv, t[aa][bb]);
+              acc[aa][bb] += t[aa][bb] * eqv[bb];
+            }
+            rp = sum_rows(rp);
+            if (g4 == 0) pw.rr[hq][(2 * lq2 + bb) * 16 + l16] = rp;
+          }
+        }
+        // W0^T dy_i + (M X)_i
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          __builtin_amdgcn_sched_barrier(0);  // one K step of fragments live at a time
+          bf16x8 df[2], mf[2], xf[2];
+#pragma unroll
+          for (int bb = 0; bb < 2; ++bb) {
+            df[bb] = frag_s<kD>(cur.DY, o, (2 * lq2 + bb) * 16, kk * 32);
+            mf[bb] = frag_s<kC>(M, o, (2 * lq2 + bb) * 16, kk * 32);
+          }
+#pragma unroll
+          for (int aa = 0; aa < 2; ++aa) xf[aa] = frag_ts<kD>(cur.X, o, kk * 32, (2 * hq + aa) * 16);
+#pragma unroll
+          for (int aa = 0; aa < 2; ++aa)
+#pragma unroll
+            for (int bb = 0; bb < 2; ++bb) {
+              acc[aa][bb] = mfma16x16x32(__builtin_bit_cast(bf16x8, pr[2 * aa + kk]), df[bb],
+                                         acc[aa][bb]);
+              acc[aa][bb] = mfma16x16x32(xf[aa], mf[bb], acc[aa][bb]);
+            }
+        }
+#pragma unroll
+        for (int aa = 0; aa < 2; ++aa)
+#pragma unroll
+          for (int bb = 0; bb < 2; ++bb) s8[aa][bb] = pack4f(acc[aa][bb]);
+        r8 = buffer_rsrc(dx + t0 * kD, cv * kD * 2);
+      }
+    } else if constexpr (R == 1) {
+      if (c >= 0) {
+        // <Lam_out, D_in> share, then Lam^T <- Gamma Lam^T + X^T (e(lq) dy),
+        // dW0^T += X^T dy; k block 2hq + a, r block 2lq2 + b
+        const RecF& rc = rec[j & 3];
+        float c0p = 0.f;
+#pragma unroll
+        for (int aa = 0; aa < 2; ++aa)
+#pragma unroll
+          for (int bb = 0; bb < 2; ++bb)
+            c0p += dot4f(unpack4f(get4<kD>(cur.S, o, (2 * lq2 + bb) * 16, (2 * hq + aa) * 16)),
+                         pr[2 * aa + bb]);
+        c0p = wave_sum(c0p);
+        if (lane == 0) part[j & 1].c0[qd] = c0p;
+        const float gam = rc.gam;
+#pragma unroll
+        for (int aa = 0; aa < 2; ++aa)
+#pragma unroll
+          for (int bb = 0; bb < 2; ++bb) pr[2 * aa + bb] = pr[2 * aa + bb] * gam;
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          __builtin_amdgcn_sched_barrier(0);  // one K step of fragments live at a time
+          bf16x8 xf[2], df[2], de[2];
+#pragma unroll
+          for (int aa = 0; aa < 2; ++aa) xf[aa] = frag_ts<kD>(cur.X, o, kk * 32, (2 * hq + aa) * 16);
+          const f32x4 e0 = *reinterpret_cast<const f32x4*>(&rc.eq[kk * 32 + 8 * g4]);
+          const f32x4 e1 = *reinterpret_cast<const f32x4*>(&rc.eq[kk * 32 + 8 * g4 + 4]);
+#pragma unroll
+          for (int bb = 0; bb < 2; ++bb) {
+            df[bb] = frag_ts<kD>(cur.DY, o, kk * 32, (2 * lq2 + bb) * 16);
+            de[bb] = scale8(df[bb], e0, e1);
+          }
+#pragma unroll
+          for (int aa = 0; aa < 2; ++aa)
+#pragma unroll
+            for (int bb = 0; bb < 2; ++bb) {
+              pr[4 + 2 * aa + bb] = mfma16x16x32(xf[aa], df[bb], pr[4 + 2 * aa + bb]);
+              pr[2 * aa + bb] = mfma16x16x32(xf[aa], de[bb], pr[2 * aa + bb]);
+            }
+        }
+        __bf16* Ln = L_s[(j + 1) & 1];
+#pragma unroll
+        for (int aa = 0; aa < 2; ++aa)
+#pragma unroll
+          for (int bb = 0; bb < 2; ++bb)
+            put4<kD>(Ln, o, (2 * lq2 + bb) * 16, (2 * hq + aa) * 16, pack4f(pr[2 * aa + bb]));
+      }
+    } else if constexpr (R == 2) {
+      if (c >= 0) {
+        // u^T[r][i]: r block 2hq + a, token block 2lq2 + b
+        const RecF& rc = rec[j & 3];
+        const __bf16* L = L_s[j & 1];
+        const __bf16* PT = PT_s[j & 1];
+        f32x4 ain[2][2], apd[2][2];
+#pragma unroll
+        for (int aa = 0; aa < 2; ++aa)
+#pragma unroll
+          for (int bb = 0; bb < 2; ++bb) {
+            ain[aa][bb] = zero4();
+            apd[aa][bb] = zero4();
+          }
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          __builtin_amdgcn_sched_barrier(0);  // one K step of fragments live at a time
+          bf16x8 lf[2], xf[2];
+#pragma unroll
+          for (int aa = 0; aa < 2; ++aa) lf[aa] = frag_s<kD>(L, o, (2 * hq + aa) * 16, kk * 32);
+#pragma unroll
+          for (int bb = 0; bb < 2; ++bb) xf[bb] = frag_s<kD>(cur.X, o, (2 * lq2 + bb) * 16, kk * 32);
+#pragma unroll
+          for (int aa = 0; aa < 2; ++aa)
+#pragma unroll
+            for (int bb = 0; bb < 2; ++bb) ain[aa][bb] = mfma16x16x32(lf[aa], xf[bb], ain[aa][bb]);
+        }
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          __builtin_amdgcn_sched_barrier(0);  // one K step of fragments live at a time
+          bf16x8 tf[2], pf[2];
+#pragma unroll
+          for (int aa = 0; aa < 2; ++aa) tf[aa] = frag_ts<kD>(cur.DY, o, kk * 32, (2 * hq + aa) * 16);
+#pragma unroll
+          for (int bb = 0; bb < 2; ++bb) pf[bb] = frag_s<kC>(PT, o, (2 * lq2 + bb) * 16, kk * 32);
+#pragma unroll
+          for (int aa = 0; aa < 2; ++aa)
+#pragma unroll
+            for (int bb = 0; bb < 2; ++bb) apd[aa][bb] = mfma16x16x32(tf[aa], pf[bb], apd[aa][bb]);
+        }
+        PartF& pw = part[j & 1];
+#pragma unroll
+        for (int bb = 0; bb < 2; ++bb) {
+          const int i = (2 * lq2 + bb) * 16 + l16;
+          const float e2i = rc.e2[i], nbi = rc.nb[i];
+          float dp = 0.f, pp = 0.f;
+#pragma unroll
+          for (int aa = 0; aa < 2; ++aa) {
+            const f32x4 u = ain[aa][bb] * e2i + apd[aa][bb];
+            const f32x4 gv = unpack4f(get4<kD>(cur.G, o, (2 * lq2 + bb) * 16, (2 * hq + aa) * 16));
+            dp += dot4f(gv, u);
+            pp += dot4f(gv, ain[aa][bb]);
+            s8[aa][bb] = pack4f(u * nbi);
+          }
+          dp = sum_rows(dp);
+          pp = sum_rows(pp);
+          if (g4 == 0) {
+            pw.de[hq][i] = -dp;
+            pw.pp[hq][i] = pp;
+          }
+        }
+        r8 = buffer_rsrc(dg + t0 * kD, cv * kD * 2);
+      }
+    } else {
+      // causal blocks of chunk j + 1 (blocks qd, qd + 4, qd + 8)
+      const int cn = chunk_at(j + 1);
+      if (cn >= 0) {
+        const RecF& rn = rec[(j + 1) & 3];
+        __bf16* PT = PT_s[(j + 1) & 1];
+        __bf16* M = M_s[(j + 1) & 1];
+        QkF& qw = qk[(K + 1) % 3];
+        causal_f(nx, rn, PT, M, qw, o, qd, lane);
+        causal_f(nx, rn, PT, M, qw, o, qd + 4, lane);
+        if (qd < 2) causal_f(nx, rn, PT, M, qw, o, qd + 8, lane);
+      }
+      if (wave == kGateWave) {
+        const int c2 = chunk_at(j + 2);
+        if (c2 >= 0) gates_f(nx.q, rec[(j + 2) & 3], cv_of(c2), lane);
+      }
+      if (wave == kAlphaWave) {
+        const int cp = chunk_at(j - 1);
+        if (cp >= 0) {
+          // dalpha_i = e(l_last - l_i + lq_i) c0 + e(l_last - l_i) sum_{j<i} e(lq_i - l_j)(-eta_j) pp_j
+          //            + e(lq_i) sum_{u>i} e(lq_u - l_i) rr_u
+          //            + (sum_{u>i} qq_u - sum_{j>=i} kk_j) / alpha_i
+          // (affine-pair and plain scans over the lanes; the suffix sums run
+          // on the reversed lane order)
+          const RecF& rp = rec[(j - 1) & 3];
+          const PartF& pr = part[(j - 1) & 1];
+          const QkF& qr = qk[(K + 2) % 3];
+          const int ir = kC - 1 - lane;
+          // causal block (R, C) is number R (R + 1) / 2 + C: token i takes
+          // the row sums of blocks (i / 16, 0..i / 16) and the column sums of
+          // blocks (i / 16..3, i / 16) (fixed four terms, clamped indices)
+          const auto qq_of = [&](int i) {
+            const int R = i >> 4, b0 = R * (R + 1) / 2;
+            float s = 0.f;
+#pragma unroll
+            for (int cc = 0; cc < 4; ++cc) {
+              const float v = qr.qq[cc <= R ? b0 + cc : b0][i & 15];
+              s += cc <= R ? v : 0.f;
+            }
+            return s;
+          };
+          const auto kk_of = [&](int i) {
+            const int Cc = i >> 4;
+            float s = 0.f;
+#pragma unroll
+            for (int R = 0; R < 4; ++R) {
+              const float v = qr.kk[R >= Cc ? R * (R + 1) / 2 + Cc : 0][i & 15];
+              s += R >= Cc ? v : 0.f;
+            }
+            return s;
+          };
+          const float c0 = (pr.c0[0] + pr.c0[1]) + (pr.c0[2] + pr.c0[3]);
+          const float pp = pr.pp[0][lane] + pr.pp[1][lane];
+          const float kk = kk_of(lane);
+          const float rr_r = pr.rr[0][ir] + pr.rr[1][ir];
+          const float z_r = qq_of(ir) - kk_of(ir);
+          const float al = rp.al[lane], al_r = rp.al[ir];
+          const float li = rp.li[lane], lqi = rp.lq[lane], lq_r = rp.lq[ir], llast = rp.llast;
+          float a2 = al, b2 = rp.nb[lane] * pp;
+          wave_scan_affine(a2, b2);
+          const float s2 = wave_shift_up(b2, 0.f);
+          float a3 = al_r, b3 = rr_r;
+          wave_scan_affine(a3, b3);
+          const float s3_r = wave_shift_up(b3, 0.f);
+          const float zs_r = wave_shift_up(wave_scan_add(z_r), 0.f);
+          const float t34 =
+              wave_reverse(fexp2(lq_r) * s3_r + zs_r * __builtin_amdgcn_rcpf(al_r), lane);
+          s4a = fexp2(llast - li + lqi) * c0 + fexp2(llast - li) * s2 + t34 -
+                kk * __builtin_amdgcn_rcpf(al);
+          s4b = pr.de[0][lane] + pr.de[1][lane];
+          const int64_t tp = static_cast<int64_t>(cp) * kC;
+          ra = buffer_rsrc(dal + tp, cv_of(cp) * 4);
+          rb = buffer_rsrc(det + tp, cv_of(cp) * 4);
+        }
+      }
+    }
+    // the same six stores in every wave (zero-byte buffers drop them)
+#pragma unroll
+    for (int aa = 0; aa < 2; ++aa)
+#pragma unroll
+      for (int bb = 0; bb < 2; ++bb) store8(r8, o8 + aa * 32 + bb * 16 * kD * 2, s8[aa][bb]);
+    store4(ra, oq, s4a);
+    store4(rb, oq, s4b);
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
+  // each role walks in its own copy of the loop (same barriers, same vector-
+  // memory instructions), so registers are allocated per role
+  const auto walk = [&](auto RC) {
+    for (int j = -1; j <= nloc; j += 3) {
+      step(RC, I0{}, j);
+      if (j + 1 > nloc) break;
+      step(RC, I1{}, j + 1);
+      if (j + 2 > nloc) break;
+      step(RC, I2{}, j + 2);
+    }
+  };
+  if (role == 0)
+    walk(I0{});
+  else if (role == 1)
+    walk(I1{});
+  else if (role == 2)
+    walk(I2{});
+  else
+    walk(I3{});
+  wait_vm<0>();  // no load into LDS may outlive the work-group
+  if (role == 1) {
+    // dW0 partial of this (segment, sequence-head): dW0[r][k], fp32
+    float* pw = static_cast<float*>(a.part_dW0) + (static_cast<int64_t>(seg) * BH + bh) * kD * kD;
+#pragma unroll
+    for (int aa = 0; aa < 2; ++aa)
+#pragma unroll
+      for (int bb = 0; bb < 2; ++bb)
+        *reinterpret_cast<f32x4*>(pw + ((2 * lq2 + bb) * 16 + l16) * kD + (2 * hq + aa) * 16 +
+                                  4 * g4) = pr[4 + 2 * aa + bb];
+  }
+}
+
+}  // namespace
+
+hipError_t launch_mfma_bwd_f64(const BwdArgs& a, hipStream_t s) {
+  const int64_t groups = a.B * a.H * a.n_seg;
+  if (groups == 0) return hipSuccess;
+  hipLaunchKernelGGL(bwd_f64, dim3(static_cast<unsigned>(groups)), dim3(kNT), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace gls
