@@ -66,7 +66,7 @@ def pass_kernels(w, which, segmented, generic):
         # sequence-head) work-groups for 256 CUs, at least 16 chunks each
         bh, nch = w.B * w.H, -(-w.T // 64)
         nseg = max(1, min(-(-256 // bh), nch // 16)) if bh < 256 else 1
-        pre = "bwd_lam + seg_combine + " if (segmented or nseg > 1) else ""
+        pre = "bwd_lam + " if (segmented or nseg > 1) else ""
         return pre + "bwd_f64 + finalize_kernel"
     body = "bwd_a + bwd_b"
     if segmented:

@@ -325,8 +325,8 @@ gl_status_t gl_scan_bwd(const gl_scan_desc_t* desc, const void* x, const void* g
     st = hip_status(gls::launch_generic_bwd(p.io, b, s), "backward launch");
   } else if (p.fused) {
     // one work-group per (segment, sequence-head) walks its chunks from the
-    // right; with segments, an adjoint-only pass per segment and the
-    // exclusive affine scan over segments give each its entering adjoint
+    // right; with segments, an adjoint-only pass gives each segment's own
+    // adjoint, from which every work-group composes the one entering it
     gls::BwdArgs bf = b;
     bf.seg_chunks = p.bwd_seg_chunks;
     bf.n_seg = p.bwd_nseg;
@@ -339,11 +339,8 @@ gl_status_t gl_scan_bwd(const gl_scan_desc_t* desc, const void* x, const void* g
       bs.seg_out = seg;
       bs.seg_lg = lg;
       st = hip_status(gls::launch_mfma_bwd_lam(bs, s), "backward segment pass");
-      if (st == GL_SUCCESS)
-        st = hip_status(gls::launch_seg_combine(seg, lg, b.B * b.H, p.bwd_nseg,
-                                                b.d_in * b.d_out, true, s),
-                        "segment combine");
-      bf.seg_lam = seg;
+      bf.seg_lam = seg;  // composed per segment by the fused kernel itself
+      bf.seg_lg_in = lg;
     }
     if (st == GL_SUCCESS) st = hip_status(gls::launch_mfma_bwd_f64(bf, s), "fused backward");
   } else if (p.chunk_par) {

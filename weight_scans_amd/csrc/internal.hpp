@@ -64,6 +64,10 @@ struct BwdArgs {
   // log2 alpha (adjoint-only pass).  part_dW0 holds [n_seg][B*H][d_out][d_in].
   int seg_chunks = 0, n_seg = 1;
   const float* seg_lam = nullptr;
+  // Fused backward: if seg_lg_in is set, seg_lam holds each segment's own
+  // adjoint (from a zero start, as the adjoint-only pass leaves it) and
+  // seg_lg_in its summed log2 alpha; the kernel composes the entering adjoint.
+  const float* seg_lg_in = nullptr;
   float* seg_out = nullptr;
   float* seg_lg = nullptr;
   // Chunk-parallel backward (d = 64): the adjoint-only pass stores Lam_out of

@@ -405,7 +405,9 @@ __global__ __launch_bounds__(kNT) void bwd_lam(BwdArgs a) {
   __shared__ GatesA2 gs;
   constexpr int NTILE = D / kT;
   const int per_seg = static_cast<int>((a.B * a.H + 7) / 8) * 8 * NTILE;
-  const int seg = blockIdx.x / per_seg, bid = blockIdx.x % per_seg;
+  // segment 0's own adjoint is never used (nothing lies to its left): the
+  // pass covers segments 1 .. n_seg - 1
+  const int seg = 1 + static_cast<int>(blockIdx.x / per_seg), bid = blockIdx.x % per_seg;
   const int grp = bid / (8 * NTILE), within = bid % (8 * NTILE);
   const int64_t bh = static_cast<int64_t>(grp) * 8 + (within & 7);
   if (bh >= a.B * a.H) return;
@@ -416,7 +418,8 @@ __global__ __launch_bounds__(kNT) void bwd_lam(BwdArgs a) {
 template <int D>
 hipError_t launch_lam(const BwdArgs& a, hipStream_t s) {
   const int64_t groups = (a.B * a.H + 7) / 8;
-  const dim3 grid(static_cast<unsigned>(groups * 8 * (D / kT) * a.n_seg));
+  if (a.n_seg <= 1) return hipSuccess;
+  const dim3 grid(static_cast<unsigned>(groups * 8 * (D / kT) * (a.n_seg - 1)));
   hipLaunchKernelGGL(bwd_lam<D>, grid, dim3(kNT), 0, s, a);
   return hipGetLastError();
 }

@@ -52,9 +52,8 @@ constexpr int kNW = 16;         // waves per work-group
 constexpr int kNT = 64 * kNW;   // threads
 constexpr int kGateWave = 14;   // derives the gates two chunks ahead
 constexpr int kAlphaWave = 15;  // dalpha and deta one chunk behind
-constexpr int kLoads = 3;       // vector-memory loads per wave per step
-constexpr int kStores = 6;      // vector-memory stores per wave per step
-static_assert(kLoads == 3, "issue_f issues three loads");
+constexpr int kLoaderStores = 2;  // stores per loader wave (role 3) per step
+constexpr int kMPad = 64;         // bf16 past each M tile: target of masked-off writes
 
 struct alignas(16) SlotF {
   __bf16 X[kC * kD];    // x, swizzled [token][k]
@@ -78,39 +77,45 @@ struct alignas(16) QkF {  // per causal block: row sums (qq) and column sums (kk
   float qq[10][16], kk[10][16];
 };
 
-// Per-lane byte offset of instruction wi (of 8) of a [64][64] bf16 tile load
-// into a swizzled LDS tile (lane i fills 16-byte slot i of the instruction).
-__device__ __forceinline__ uint32_t dma_off_f(int wi, int lane) {
-  const int p = wi * 64 + lane;
-  const int row = p >> 3, kl = (p & 7) ^ swz<kD>(row);
-  return static_cast<uint32_t>(row * kD * 2 + 16 * kl);
+// Per-lane byte offsets of a [64][64] bf16 tile load into a swizzled LDS
+// tile: instruction wi (of 8) fills 16-byte slots wi * 64 + lane, and reads
+// global bytes wi * 1024 + off[wi & 1] (the swizzle of a row depends on the
+// row's low three bits, from the lane, and bit 3, from wi).
+struct DmaOffF {
+  uint32_t e, o;
+};
+__device__ __forceinline__ DmaOffF dma_off_f(int lane) {
+  DmaOffF d;
+  const int rl = lane >> 3, u = lane & 7;
+  d.e = static_cast<uint32_t>(rl * kD * 2 + 16 * (u ^ swz<kD>(rl)));
+  d.o = static_cast<uint32_t>(rl * kD * 2 + 16 * (u ^ swz<kD>(8 + rl)));
+  return d;
 }
 
-// Tiles of chunk k (negative: zero fill) and the gate rows of chunk kq.
-// Waves 0-7 load instruction w of the x and dy tiles, waves 8-15 instruction
-// w - 8 of the g and D_in tiles: the same three instructions in every wave.
-__device__ __forceinline__ void issue_f(SlotF& sl, uint32_t ot, uint32_t oq, const uint16_t* x,
-                                        const uint16_t* g, const uint16_t* dy, const uint16_t* st,
-                                        const float* eta, const float* alpha, int64_t T, int k,
-                                        int kq, int wave) {
+// Loader wave ld (0..3) of a chunk: the whole tile ld (x, g, dy, D_in) of
+// chunk k (negative: zero fill) in eight instructions, then the eta (even
+// ld) or alpha (odd ld) row of chunk kq.
+__device__ __forceinline__ void issue_f(SlotF& sl, const DmaOffF& od, uint32_t oq,
+                                        const uint16_t* x, const uint16_t* g, const uint16_t* dy,
+                                        const uint16_t* st, const float* eta, const float* alpha,
+                                        int64_t T, int k, int kq, int ld) {
   const bool in = k >= 0;
   const int64_t t0 = in ? static_cast<int64_t>(k) * kC : 0;
   const int cv = in ? static_cast<int>(std::min<int64_t>(kC, T - t0)) : 0;
   const int64_t s0 = (in ? static_cast<int64_t>(k) : 0) * kD * kD;
-  const bool lo = wave < 8;
-  const int wi = wave & 7;
-  char* base = reinterpret_cast<char*>(&sl);
-  const int o1 = (lo ? static_cast<int>(offsetof(SlotF, X)) : static_cast<int>(offsetof(SlotF, G))) +
-                 wi * 1024;
-  const int o2 = (lo ? static_cast<int>(offsetof(SlotF, DY)) : static_cast<int>(offsetof(SlotF, S))) +
-                 wi * 1024;
-  dma16(buffer_rsrc((lo ? x : g) + t0 * kD, cv * kD * 2), ot, base + o1);
-  dma16(lo ? buffer_rsrc(dy + t0 * kD, cv * kD * 2) : buffer_rsrc(st + s0, in ? kD * kD * 2 : 0),
-        ot, base + o2);
+  const __amdgpu_buffer_rsrc_t r =
+      ld == 3 ? buffer_rsrc(st + s0, in ? kD * kD * 2 : 0)
+              : buffer_rsrc((ld == 0 ? x : ld == 1 ? g : dy) + t0 * kD, cv * kD * 2);
+  char* base = reinterpret_cast<char*>(&sl) +
+               (ld == 0 ? offsetof(SlotF, X) : ld == 1 ? offsetof(SlotF, G)
+                : ld == 2 ? offsetof(SlotF, DY) : offsetof(SlotF, S));
+#pragma unroll
+  for (int wi = 0; wi < 8; ++wi)
+    dma16(r, (wi & 1 ? od.o : od.e) + wi * 1024, base + wi * 1024);
   const bool inq = kq >= 0;
   const int64_t tq = inq ? static_cast<int64_t>(kq) * kC : 0;
   const int cq = inq ? static_cast<int>(std::min<int64_t>(kC, T - tq)) : 0;
-  dma4(buffer_rsrc(((wave & 1) == 0 ? eta : alpha) + tq, cq * 4), oq, sl.q[wave & 1]);
+  dma4(buffer_rsrc(((ld & 1) == 0 ? eta : alpha) + tq, cq * 4), oq, sl.q[ld & 1]);
 }
 
 // Gates of a chunk from its eta / alpha rows (one wave, lane = token).
@@ -201,12 +206,15 @@ __device__ __forceinline__ void causal_f(const SlotF& sl, const RecF& r, __bf16*
   }
   put4<kC>(PT, o, cb * 16, rb * 16, pack4f(p));
   put4<kC>(M, o, cb * 16, rb * 16, pack4f(v));
-  // the mirrored half of M, element by element (after the put4 above: on the
-  // diagonal block both touch the same bytes, and one wave's LDS writes land
-  // in order)
+  // the mirrored half of M, element by element, after the put4 above (on
+  // the diagonal block both touch the same bytes, and one wave's LDS writes
+  // land in order); lanes with nothing to write there write into the pad
+  // past the tile instead, so that the store is unconditional
 #pragma unroll
-  for (int q = 0; q < 4; ++q)
-    if (col < r0 + q) M[sidx<kC>(r0 + q, col)] = static_cast<__bf16>(v[q]);
+  for (int q = 0; q < 4; ++q) {
+    const int e = col < r0 + q ? sidx<kC>(r0 + q, col) : kC * kC + lane;
+    M[e] = static_cast<__bf16>(v[q]);
+  }
   f32x4 zr;
 #pragma unroll
   for (int q = 0; q < 4; ++q) zr[q] = row16_sum(z[q]);
@@ -218,7 +226,7 @@ __device__ __forceinline__ void causal_f(const SlotF& sl, const RecF& r, __bf16*
 __global__ __launch_bounds__(kNT) void bwd_f64(BwdArgs a) {
   __shared__ SlotF ring0, ring1, ring2;
   __shared__ __bf16 PT_s[2][kC * kC];  // P^T by chunk parity (W0 staging at the start)
-  __shared__ __bf16 M_s[2][kC * kC];   // Be + Be^T by chunk parity
+  __shared__ __bf16 M_s[2][kC * kC + kMPad];  // Be + Be^T by chunk parity (+ pad)
   __shared__ __bf16 L_s[2][kD * kD];   // Lam_out (bf16, [r][k]) by chunk parity
   __shared__ RecF rec[4];
   __shared__ PartF part[2];
@@ -253,7 +261,7 @@ __global__ __launch_bounds__(kNT) void bwd_f64(BwdArgs a) {
 
   const LaneOff<kD> o_in = lane_off<kD>(lane);
   const LaneOff<kD>& o = o_in;
-  const uint32_t ot = dma_off_f(wave & 7, lane);
+  const DmaOffF od = dma_off_f(lane);
   const uint32_t oq = static_cast<uint32_t>(lane * 4);
   const __amdgpu_buffer_rsrc_t r_none = buffer_rsrc(a.x, 0);
 
@@ -265,12 +273,12 @@ __global__ __launch_bounds__(kNT) void bwd_f64(BwdArgs a) {
 
   // ---- set-up: loads of the first chunk (into slot 1, with the gate rows of
   // the second) and of its own gate rows (slot 0), W0, the entering adjoint
-  issue_f(*rs[1], ot, oq, x, g, dy, st, eta, alpha, T, chunk_at(0), chunk_at(1), wave);
-  {
+  if (role == 3) {
+    issue_f(*rs[1], od, oq, x, g, dy, st, eta, alpha, T, chunk_at(0), chunk_at(1), qd);
     const int c0 = chunk_at(0);
-    dma4(buffer_rsrc(((wave & 1) == 0 ? eta : alpha) + (c0 >= 0 ? static_cast<int64_t>(c0) * kC : 0),
+    dma4(buffer_rsrc(((qd & 1) == 0 ? eta : alpha) + (c0 >= 0 ? static_cast<int64_t>(c0) * kC : 0),
                      cv_of(c0) * 4),
-         oq, rs[0]->q[wave & 1]);
+         oq, rs[0]->q[qd & 1]);
   }
   // W0 (bf16 [r][k]) staged in PT_s[1]; dx waves keep W0^T fragments
   for (int idx = tid; idx < kD * kD / 8; idx += kNT) {
@@ -287,13 +295,21 @@ __global__ __launch_bounds__(kNT) void bwd_f64(BwdArgs a) {
 #pragma unroll
   for (int e = 0; e < 8; ++e) pr[e] = zero4();
   if (role == 1 && a.seg_lam) {
-    const float* sl = a.seg_lam + (bh * a.n_seg + seg) * kD * kD;
+    // adjoint entering from the right: given, or composed here from the
+    // segments to the right, nearest last: Lam <- 2^(lg_s) Lam + L_s
+    const int s_lo = a.seg_lg_in ? seg + 1 : seg;
+    const int s_hi = a.seg_lg_in ? a.n_seg - 1 : seg;
+    for (int s2 = s_hi; s2 >= s_lo; --s2) {
+      const float* sl = a.seg_lam + (bh * a.n_seg + s2) * kD * kD;
+      const float gs = a.seg_lg_in ? fexp2(a.seg_lg_in[bh * a.n_seg + s2]) : 0.f;
 #pragma unroll
-    for (int aa = 0; aa < 2; ++aa)
+      for (int aa = 0; aa < 2; ++aa)
 #pragma unroll
-      for (int bb = 0; bb < 2; ++bb)
-        pr[2 * aa + bb] = *reinterpret_cast<const f32x4*>(
-            sl + ((2 * lq2 + bb) * 16 + l16) * kD + (2 * hq + aa) * 16 + 4 * g4);
+        for (int bb = 0; bb < 2; ++bb)
+          pr[2 * aa + bb] = pr[2 * aa + bb] * gs +
+                            *reinterpret_cast<const f32x4*>(
+                                sl + ((2 * lq2 + bb) * 16 + l16) * kD + (2 * hq + aa) * 16 + 4 * g4);
+    }
   }
   wait_vm<0>();
   __syncthreads();
@@ -329,26 +345,33 @@ __global__ __launch_bounds__(kNT) void bwd_f64(BwdArgs a) {
     SlotF& cur = *rs[K];
     SlotF& nx = *rs[(K + 1) % 3];
     SlotF& dst = *rs[(K + 2) % 3];
-    wait_vm<kStores>();  // chunk j + 1 loaded: after it only the previous step's stores
-    lds_barrier();       // and every read of the slot about to be refilled is done
+    // loader waves: chunk j + 1 loaded (after its loads come only the
+    // previous step's stores); then every wave: the slot about to be refilled
+    // is no longer read
+    if constexpr (R == 3) wait_vm<kLoaderStores>();
+    lds_barrier();
     // per-lane offsets passed through an empty asm: the addresses derived
     // from them are formed inside the step instead of being kept live
     // across the whole walk for every slot and role
     LaneOff<kD> o = o_in;
     uint32_t o8 = o8_in;
     asm volatile("" : "+v"(o.b), "+v"(o.t0), "+v"(o.t1), "+v"(o.w), "+v"(o8));
-    issue_f(dst, ot, oq, x, g, dy, st, eta, alpha, T, chunk_at(j + 2), chunk_at(j + 3), wave);
+    if constexpr (R == 3)
+      issue_f(dst, od, oq, x, g, dy, st, eta, alpha, T, chunk_at(j + 2), chunk_at(j + 3), qd);
+    // causal block b of chunk j + 1 (blocks 0-3: dx waves, 4-7: adjoint
+    // waves, 8-9: loader waves 12 and 13)
+    const auto causal_next = [&](int b) {
+      if (chunk_at(j + 1) >= 0)
+        causal_f(nx, rec[(j + 1) & 3], PT_s[(j + 1) & 1], M_s[(j + 1) & 1], qk[(K + 1) % 3], o, b,
+                 lane);
+    };
 
     const int c = chunk_at(j);
     const int64_t t0 = c >= 0 ? static_cast<int64_t>(c) * kC : 0;
     const int cv = cv_of(c);
     uint2 s8[2][2];
-#pragma unroll
-    for (int aa = 0; aa < 2; ++aa)
-#pragma unroll
-      for (int bb = 0; bb < 2; ++bb) s8[aa][bb] = make_uint2(0, 0);
     float s4a = 0.f, s4b = 0.f;
-    __amdgpu_buffer_rsrc_t r8 = r_none, ra = r_none, rb = r_none;
+    __amdgpu_buffer_rsrc_t ra = r_none, rb = r_none;
 
     if constexpr (R == 0) {
       if (c >= 0) {
@@ -448,8 +471,13 @@ __global__ __launch_bounds__(kNT) void bwd_f64(BwdArgs a) {
         for (int aa = 0; aa < 2; ++aa)
 #pragma unroll
           for (int bb = 0; bb < 2; ++bb) s8[aa][bb] = pack4f(acc[aa][bb]);
-        r8 = buffer_rsrc(dx + t0 * kD, cv * kD * 2);
+        const __amdgpu_buffer_rsrc_t r8 = buffer_rsrc(dx + t0 * kD, cv * kD * 2);
+#pragma unroll
+        for (int aa = 0; aa < 2; ++aa)
+#pragma unroll
+          for (int bb = 0; bb < 2; ++bb) store8(r8, o8 + aa * 32 + bb * 16 * kD * 2, s8[aa][bb]);
       }
+      causal_next(qd);
     } else if constexpr (R == 1) {
       if (c >= 0) {
         // <Lam_out, D_in> share, then Lam^T <- Gamma Lam^T + X^T (e(lq) dy),
@@ -497,6 +525,7 @@ __global__ __launch_bounds__(kNT) void bwd_f64(BwdArgs a) {
           for (int bb = 0; bb < 2; ++bb)
             put4<kD>(Ln, o, (2 * lq2 + bb) * 16, (2 * hq + aa) * 16, pack4f(pr[2 * aa + bb]));
       }
+      causal_next(4 + qd);
     } else if constexpr (R == 2) {
       if (c >= 0) {
         // u^T[r][i]: r block 2hq + a, token block 2lq2 + b
@@ -558,20 +587,14 @@ __global__ __launch_bounds__(kNT) void bwd_f64(BwdArgs a) {
             pw.pp[hq][i] = pp;
           }
         }
-        r8 = buffer_rsrc(dg + t0 * kD, cv * kD * 2);
+        const __amdgpu_buffer_rsrc_t r8 = buffer_rsrc(dg + t0 * kD, cv * kD * 2);
+#pragma unroll
+        for (int aa = 0; aa < 2; ++aa)
+#pragma unroll
+          for (int bb = 0; bb < 2; ++bb) store8(r8, o8 + aa * 32 + bb * 16 * kD * 2, s8[aa][bb]);
       }
     } else {
-      // causal blocks of chunk j + 1 (blocks qd, qd + 4, qd + 8)
-      const int cn = chunk_at(j + 1);
-      if (cn >= 0) {
-        const RecF& rn = rec[(j + 1) & 3];
-        __bf16* PT = PT_s[(j + 1) & 1];
-        __bf16* M = M_s[(j + 1) & 1];
-        QkF& qw = qk[(K + 1) % 3];
-        causal_f(nx, rn, PT, M, qw, o, qd, lane);
-        causal_f(nx, rn, PT, M, qw, o, qd + 4, lane);
-        if (qd < 2) causal_f(nx, rn, PT, M, qw, o, qd + 8, lane);
-      }
+      if (qd < 2) causal_next(8 + qd);
       if (wave == kGateWave) {
         const int c2 = chunk_at(j + 2);
         if (c2 >= 0) gates_f(nx.q, rec[(j + 2) & 3], cv_of(c2), lane);
@@ -635,21 +658,18 @@ __global__ __launch_bounds__(kNT) void bwd_f64(BwdArgs a) {
           rb = buffer_rsrc(det + tp, cv_of(cp) * 4);
         }
       }
+      // the same two stores in every loader wave (zero-byte buffers drop
+      // them), so that its wait at the top of a step is a constant
+      store4(ra, oq, s4a);
+      store4(rb, oq, s4b);
     }
-    // the same six stores in every wave (zero-byte buffers drop them)
-#pragma unroll
-    for (int aa = 0; aa < 2; ++aa)
-#pragma unroll
-      for (int bb = 0; bb < 2; ++bb) store8(r8, o8 + aa * 32 + bb * 16 * kD * 2, s8[aa][bb]);
-    store4(ra, oq, s4a);
-    store4(rb, oq, s4b);
   };
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
   using I2 = std::integral_constant<int, 2>;
   using I3 = std::integral_constant<int, 3>;
-  // each role walks in its own copy of the loop (same barriers, same vector-
-  // memory instructions), so registers are allocated per role
+  // each role walks in its own copy of the loop (same barriers), so
+  // registers are allocated per role
   const auto walk = [&](auto RC) {
     for (int j = -1; j <= nloc; j += 3) {
       step(RC, I0{}, j);
@@ -659,14 +679,16 @@ __global__ __launch_bounds__(kNT) void bwd_f64(BwdArgs a) {
       step(RC, I2{}, j + 2);
     }
   };
-  if (role == 0)
-    walk(I0{});
-  else if (role == 1)
-    walk(I1{});
+  // (the loader role first: with this order the compiler's wait analysis
+  // keeps the loaders' loads in flight out of the other roles' loops)
+  if (role == 3)
+    walk(I3{});
   else if (role == 2)
     walk(I2{});
+  else if (role == 1)
+    walk(I1{});
   else
-    walk(I3{});
+    walk(I0{});
   wait_vm<0>();  // no load into LDS may outlive the work-group
   if (role == 1) {
     // dW0 partial of this (segment, sequence-head): dW0[r][k], fp32

@@ -11,7 +11,9 @@
 //   state entering segment 0 = 0,  entering s + 1 = G_s (entering s) + L_s.
 // The reverse scan composes its adjoint the same way from the right end.
 // This kernel replaces every L_s by the state entering segment s (an
-// exclusive scan over segments, one thread per matrix element).
+// exclusive scan over segments, one thread per matrix element).  The segment
+// the scan reaches last never contributes (segment n - 1 forwards, segment 0
+// in reverse): its L_s need not have been computed.
 #include "internal.hpp"
 
 namespace gls {
@@ -29,6 +31,10 @@ __global__ __launch_bounds__(kSegThreads) void seg_combine(float* buf, const flo
   float carry = 0.f;
   for (int k = 0; k < n_seg; ++k) {
     const int s = reverse ? n_seg - 1 - k : k;
+    if (k == n_seg - 1) {  // the segment reached last: its own L_s is never needed
+      p[static_cast<int64_t>(s) * dd] = carry;
+      break;
+    }
     const float local = p[static_cast<int64_t>(s) * dd];
     p[static_cast<int64_t>(s) * dd] = carry;
     carry = carry * __builtin_amdgcn_exp2f(l[s]) + local;
