@@ -54,16 +54,12 @@ struct Plan {
   int n_seg = 1, seg_chunks = 0;
   size_t seg_bytes = 0;     // per-segment states (fp32) + summed log2 alpha
   size_t seg_state_bytes = 0;
-  // chunk-parallel backward (matrix-core kernels, d = 64): stored Lam_out,
-  // per-chunk dots and <Lam_out, D_in> partials, dW0 partial groups
-  bool chunk_par = false;
-  int dw_groups = 1;
+  int dw_groups = 1;        // dW0 partials per (b, h)
   // fused backward (matrix-core kernels, d = 64): its own segment count (a
   // work-group per segment and sequence-head), deta / dalpha written directly
   bool fused = false;
   int bwd_nseg = 1, bwd_seg_chunks = 0;
   size_t bwd_seg_bytes = 0, bwd_seg_state_bytes = 0;
-  size_t lam_bytes = 0, dots_bytes = 0, c0_bytes = 0, gate_bytes = 0;
   const char* name = "";
 };
 
@@ -132,7 +128,6 @@ gl_status_t make_plan(const gl_scan_desc_t* d, Plan* p) {
   p->saved_bytes = round_up(BH * p->n_ckpt * dd * p->state_elem);
   p->part_bytes = round_up(static_cast<size_t>(p->n_tiles) * BH * d->T * p->comp);
   p->fused = p->mfma && d->d_in == 64 && p->n_chunks > 0;
-  p->chunk_par = false;
   if (p->fused) {
     int nb = 1;
     if (d->segments > 0) {
@@ -150,20 +145,8 @@ gl_status_t make_plan(const gl_scan_desc_t* d, Plan* p) {
     }
     p->part_bytes = 0;
   }
-  p->dw_groups = p->fused       ? p->bwd_nseg
-                 : p->chunk_par ? gls::mfma_bwd_c64_groups(static_cast<int64_t>(BH), p->n_chunks)
-                                : p->n_seg;
+  p->dw_groups = p->fused ? p->bwd_nseg : p->n_seg;
   p->dw_bytes = round_up(BH * dd * p->comp * p->dw_groups);
-  if (p->chunk_par) {
-    const gls::ChunkParLayout lay = gls::mfma_bwd_c64_layout();
-    const size_t items = BH * static_cast<size_t>(p->n_chunks);
-    p->n_tiles = lay.eta_parts;
-    p->part_bytes = round_up(static_cast<size_t>(p->n_tiles) * BH * d->T * p->comp);
-    p->lam_bytes = round_up(items * dd * 2);
-    p->dots_bytes = round_up(items * lay.dots_per_chunk * sizeof(float));
-    p->c0_bytes = round_up(items * lay.c0_per_chunk * sizeof(float));
-    p->gate_bytes = round_up(BH * d->T * sizeof(float)) + round_up(items * sizeof(float));
-  }
   return GL_SUCCESS;
 }
 
@@ -171,8 +154,7 @@ gl_status_t make_plan(const gl_scan_desc_t* d, Plan* p) {
 // used by the state recompute, which runs first), recomputed states
 size_t bwd_ws(const Plan& p, bool have_saved) {
   return 2 * p.part_bytes + p.dw_bytes + std::max(p.seg_bytes, p.bwd_seg_bytes) +
-         (have_saved ? 0 : p.saved_bytes) +
-         p.lam_bytes + p.dots_bytes + p.c0_bytes + p.gate_bytes;
+         (have_saved ? 0 : p.saved_bytes);
 }
 
 bool misaligned(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) != 0; }
@@ -298,12 +280,6 @@ gl_status_t gl_scan_bwd(const gl_scan_desc_t* desc, const void* x, const void* g
   void* part_dW0 = w + 2 * p.part_bytes;
   char* seg_ws = w + 2 * p.part_bytes + p.dw_bytes;
   char* rec = seg_ws + std::max(p.seg_bytes, p.bwd_seg_bytes);
-  char* lam_ws = rec + (saved ? 0 : p.saved_bytes);
-  float* dots_ws = reinterpret_cast<float*>(lam_ws + p.lam_bytes);
-  float* c0_ws = reinterpret_cast<float*>(lam_ws + p.lam_bytes + p.dots_bytes);
-  float* eq_ws = reinterpret_cast<float*>(lam_ws + p.lam_bytes + p.dots_bytes + p.c0_bytes);
-  float* gam_ws = eq_ws + round_up(static_cast<size_t>(desc->B * desc->H * desc->T) * sizeof(float)) /
-                              sizeof(float);
   const void* states = saved;
   if (!states) {
     st = hip_status(
@@ -343,36 +319,6 @@ gl_status_t gl_scan_bwd(const gl_scan_desc_t* desc, const void* x, const void* g
       bf.seg_lg_in = lg;
     }
     if (st == GL_SUCCESS) st = hip_status(gls::launch_mfma_bwd_f64(bf, s), "fused backward");
-  } else if (p.chunk_par) {
-    // the adjoint chain alone, storing Lam_out of every chunk (per segment
-    // from its incoming adjoint if the sequence is cut into segments), then
-    // every chunk's outputs in parallel, then dalpha per chunk
-    gls::BwdArgs b1 = b;
-    b1.lam_out = lam_ws;
-    b1.gate_eq = eq_ws;
-    b1.gate_gam = gam_ws;
-    if (p.n_seg > 1) {
-      float* seg = reinterpret_cast<float*>(seg_ws);
-      float* lg = reinterpret_cast<float*>(seg_ws + p.seg_state_bytes);
-      gls::BwdArgs bs = b;
-      bs.seg_out = seg;
-      bs.seg_lg = lg;
-      st = hip_status(gls::launch_mfma_bwd_lam(bs, s), "backward segment pass");
-      if (st == GL_SUCCESS)
-        st = hip_status(gls::launch_seg_combine(seg, lg, b.B * b.H, p.n_seg, b.d_in * b.d_out,
-                                                true, s),
-                        "segment combine");
-      b1.seg_lam = seg;
-    }
-    if (st == GL_SUCCESS) st = hip_status(gls::launch_mfma_bwd_chain64(b1, s), "adjoint chain");
-    if (st == GL_SUCCESS) {
-      gls::BwdArgs b2 = b;
-      b2.lam_out = lam_ws;
-      b2.part_dots = dots_ws;
-      b2.part_c0 = c0_ws;
-      b2.dalpha_out = dalpha;
-      st = hip_status(gls::launch_mfma_bwd_c64(b2, s), "chunk pass");
-    }
   } else if (p.n_seg <= 1) {
     st = hip_status(gls::launch_mfma_bwd(b, s), "backward launch");
   } else {
@@ -402,7 +348,7 @@ gl_status_t gl_scan_bwd(const gl_scan_desc_t* desc, const void* x, const void* g
   f.deta = deta; f.dalpha = dalpha; f.dW0 = dW0;
   f.B = desc->B; f.H = desc->H; f.T = desc->T;
   f.d_in = b.d_in; f.d_out = b.d_out; f.n_tiles = p.n_tiles; f.n_seg = p.dw_groups;
-  f.alpha_done = p.chunk_par || p.fused;
+  f.alpha_done = p.fused;
   f.eta_done = p.fused;
   return hip_status(gls::launch_finalize(p.io, f, s), "finalize launch");
 }

@@ -70,18 +70,9 @@ struct BwdArgs {
   const float* seg_lg_in = nullptr;
   float* seg_out = nullptr;
   float* seg_lg = nullptr;
-  // Chunk-parallel backward (d = 64): the adjoint-only pass stores Lam_out of
-  // every chunk in lam_out (bf16 [B*H][n_chunks][d_out][d_in]); the chunk pass
-  // writes per-chunk dots and <Lam_out, D_in> partials (sizes in
-  // ChunkParLayout), from which dalpha_out ([B,H,T]) is formed.
-  void* lam_out = nullptr;
-  float* part_dots = nullptr;
-  float* part_c0 = nullptr;
-  void* dalpha_out = nullptr;
-  float* gate_eq = nullptr;   // e(lq) per token [B*H*T] (adjoint chain)
-  float* gate_gam = nullptr;  // e(l_last) per chunk [B*H][n_chunks]
-  // Fused backward (d = 64): deta written directly ([B,H,T]), with dalpha_out.
+  // Fused backward (d = 64): deta and dalpha written directly ([B,H,T]).
   void* deta_out = nullptr;
+  void* dalpha_out = nullptr;
 };
 
 struct FinArgs {
@@ -95,7 +86,7 @@ struct FinArgs {
   int d_in, d_out;
   int n_tiles;
   int n_seg = 1;             // dW0 partials per (b, h)
-  bool alpha_done = false;   // dalpha already written (chunk-parallel / fused backward)
+  bool alpha_done = false;   // dalpha already written (fused backward)
   bool eta_done = false;     // deta already written (fused backward)
 };
 
@@ -114,18 +105,8 @@ hipError_t launch_mfma_fwd(const FwdArgs& a, hipStream_t s);
 hipError_t launch_mfma_bwd(const BwdArgs& a, hipStream_t s);
 hipError_t launch_mfma_bwd_a(const BwdArgs& a, hipStream_t s);  // row tiles: dg, deta, dW0
 hipError_t launch_mfma_bwd_b(const BwdArgs& a, hipStream_t s);  // column tiles: dx, dalpha
-hipError_t launch_mfma_bwd_ab64(const BwdArgs& a, hipStream_t s);  // both, one launch, D = 64
 hipError_t launch_mfma_bwd_lam(const BwdArgs& a, hipStream_t s);  // adjoint-only segment pass
-hipError_t launch_mfma_bwd_c64(const BwdArgs& a, hipStream_t s);  // chunk pass + dalpha, d = 64
-hipError_t launch_mfma_bwd_chain64(const BwdArgs& a, hipStream_t s);  // gates + adjoint chain, d = 64
 hipError_t launch_mfma_bwd_f64(const BwdArgs& a, hipStream_t s);  // fused reverse scan, d = 64
-int mfma_bwd_c64_groups(int64_t BH, int n_chunks);                 // its dW0 partials per (b, h)
-struct ChunkParLayout {
-  int eta_parts;       // deta partials per token (part_eta: [eta_parts][B*H*T])
-  int dots_per_chunk;  // floats of part_dots per (b, h, chunk)
-  int c0_per_chunk;    // floats of part_c0 per (b, h, chunk)
-};
-ChunkParLayout mfma_bwd_c64_layout();
 // Exclusive affine scan over the segments of every (b, h): buf[s] <- the state
 // entering segment s (in segment order, or from the right end if reverse).
 hipError_t launch_seg_combine(float* buf, const float* lg, int64_t BH, int n_seg, int dd,

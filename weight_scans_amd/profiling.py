@@ -117,8 +117,7 @@ def main(argv):
                 return sum(v["fetch_bytes"] + v["write_bytes"] for k, v in res["kernels"].items()
                            if pred(k))
             fwd = moved(lambda k: k.startswith("fwd_") or "seg_combine" in k)
-            bwd = moved(lambda k: k.startswith("bwd_") or "finalize" in k or "seg_combine" in k
-                        or "chunk_gates_eq" in k or "dalpha_chunks" in k)
+            bwd = moved(lambda k: k.startswith("bwd_") or "finalize" in k or "seg_combine" in k)
             db[cfg] = {"kernel_hash": kernel_source_hash(), "fwd_bytes": fwd, "bwd_bytes": bwd,
                        "fetch_scale": res["fetch_scale"], "write_scale": res["write_scale"]}
             with open(path, "w") as fh:
