@@ -18,10 +18,13 @@
 // HBM -> LDS by direct buffer loads into a ring of kRing slots; while chunk c
 // is finished (y and the state update), the scores of chunk c + 1 are formed
 // and one wave derives the gates of chunk c + 2, and the loads of chunks
-// c + 3 and c + 4 are in flight.  Eight waves (two per SIMD) share the work:
-// wave w owns the 16 x 16 output block (token block w/2, row block w%2) of y
-// and D/64 16 x 16 blocks of the state.  All LDS tiles are XOR-swizzled
-// (mfma.hpp) so that fragment reads are free of bank conflicts.
+// c + 3 and c + 4 are in flight.  Sixteen waves (four per SIMD) in two roles:
+// y waves 0-7 own the 16 x 16 output block (token block w/2, row block w%2)
+// of y and the score blocks (w, and 8 + w for w < 2); state waves 8-15 own
+// D/64 16 x 16 blocks of the fp32 state, issue every load (and wait for
+// them), scale the g tile and derive the gates.  Each role runs its own copy
+// of the chunk loop, so registers are allocated per role.  All LDS tiles are
+// XOR-swizzled (mfma.hpp) so that fragment reads are free of bank conflicts.
 //
 // `states` (optional) receives D_in of every chunk in bf16:
 // [B*H][n_chunks][D (row r)][D (col c)] -- read by the matrix-core backward.
@@ -48,10 +51,10 @@ namespace {
 
 constexpr int kC = 64;         // tokens per chunk
 constexpr int kTN = 32;        // rows of the adaptation per work-group
-constexpr int kNW = 8;         // waves per work-group
+constexpr int kNW = 16;        // waves per work-group: 8 y waves, 8 state (loader) waves
 constexpr int kNT = 64 * kNW;  // threads
 constexpr int kRing = 5;       // chunk slots: 3 in use, 2 in flight
-constexpr int kPrepWave = 2;   // the wave that derives the gates
+constexpr int kPrepWave = 2;   // the state wave (index among them) that derives the gates
 
 // Per-token factors of a chunk derived from the gates (i = token, b = 16-token
 // block of i, m_b = l_{16 b - 1} with m_0 = 0):
@@ -204,9 +207,9 @@ template <int D, bool HAS_Y, bool HAS_ST>
 __global__ __launch_bounds__(kNT) void fwd_mfma(FwdArgs a) {
   static_assert(D == 64 || D == 128, "D");
   constexpr int NTILE = D / kTN;
-  constexpr int NS = D / 64;  // 16x16 state blocks per wave
+  constexpr int NS = D / 64;  // 16x16 state blocks per state wave
   constexpr int P = kLoadOps<D>;
-  constexpr int S = (HAS_Y ? 1 : 0) + (HAS_ST ? NS : 0);  // stores per wave per chunk
+  constexpr int S = HAS_ST ? NS : 0;  // stores per state wave per chunk
   // Each ring slot is a separate LDS object, and every reference to one is
   // static (the chunk loop is unrolled by kRing), so the compiler can tell a
   // slot being read from the slots still being filled and adds no waits.
@@ -219,8 +222,9 @@ __global__ __launch_bounds__(kNT) void fwd_mfma(FwdArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
+  const int role = wave >> 3, w8 = wave & 7;  // 0: y waves, 1: state (and loader) waves
   const int g4 = lane >> 4, l16 = lane & 15;
-  const int tb = wave >> 1, rbw = wave & 1;  // this wave's y block / state row block
+  const int tb = w8 >> 1, rbw = w8 & 1;  // y block / state row block of this wave
   // 8 consecutive sequence-heads and all their row tiles share one XCD
   // (work-groups are dealt to the 8 XCDs round-robin), so the x chunk that
   // every tile reads is fetched from HBM once into that XCD's L2.
@@ -247,27 +251,27 @@ __global__ __launch_bounds__(kNT) void fwd_mfma(FwdArgs a) {
   uint16_t* st = HAS_ST ? static_cast<uint16_t*>(a.states) + bh * static_cast<int64_t>(n) * D * D
                         : nullptr;
 
-  // W0 rows of this wave's row block as MFMA A fragments, in registers throughout
+  // y waves: W0 rows of this wave's row block as MFMA A fragments, in
+  // registers throughout
   bf16x8 wf[D / 32];
-  if (HAS_Y) {
+  if (HAS_Y && role == 0) {
 #pragma unroll
     for (int kb = 0; kb < D / 32; ++kb)
       wf[kb] = *reinterpret_cast<const bf16x8*>(
           W0 + static_cast<int64_t>(r0 + rbw * 16 + l16) * D + kb * 32 + 8 * g4);
   }
-  // starting state of the tile: zero, or the segment's incoming state
-  // (fp32 accumulators, and its bf16 copy for the readout of the first chunk)
+  // state waves: starting state of the tile, zero or the segment's incoming
+  // state (fp32 accumulators, and its bf16 copy for the first readout)
   f32x4 sacc[NS];
-  if (a.seg_in) {
+#pragma unroll
+  for (int s = 0; s < NS; ++s) sacc[s] = zero4();
+  if (role == 1 && a.seg_in) {
     const float* si = a.seg_in + (bh * a.n_seg + seg) * D * D;
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
       const int cb = tb + 4 * s;
       sacc[s] = *reinterpret_cast<const f32x4*>(si + (r0 + rbw * 16 + l16) * D + cb * 16 + 4 * g4);
     }
-  } else {
-#pragma unroll
-    for (int s = 0; s < NS; ++s) sacc[s] = zero4();
   }
   if (HAS_Y)
     for (int idx = tid; idx < 2 * kC * kC / 8; idx += kNT)
@@ -282,7 +286,7 @@ __global__ __launch_bounds__(kNT) void fwd_mfma(FwdArgs a) {
   const LaneOff<D> oX = lane_off<D>(lane);
   const LaneOff<kTN> oG = lane_off<kTN>(lane);
   const LaneOff<kC> oA = lane_off<kC>(lane);
-  const DmaOff<D> od = dma_off<D>(wave, lane);
+  const DmaOff<D> od = dma_off<D>(w8, lane);
   // per-lane byte offsets of the stores (loop invariant; the buffer base
   // moves per chunk and its byte count drops rows past the sequence end)
   const uint32_t oy = static_cast<uint32_t>(((tb * 16 + l16) * D + r0 + rbw * 16 + 4 * g4) * 2);
@@ -293,47 +297,47 @@ __global__ __launch_bounds__(kNT) void fwd_mfma(FwdArgs a) {
     os[s] = static_cast<uint32_t>(((r0 + rbw * 16 + l16) * D + cb * 16 + 4 * g4) * 2);
   }
   const __amdgpu_buffer_rsrc_t r_none = buffer_rsrc(a.x, 0);
-  // this thread's 4 elements of the scaled g tile: row tid/8, columns 4 (tid%8)..
-  const int gs_row = tid >> 3;
-  const uint32_t gs_off = static_cast<uint32_t>(sidx<kTN>(gs_row, 4 * (tid & 7)) * 2);
+  // a state-wave thread's 4 elements of the scaled g tile: row t/8, columns 4 (t%8)..
+  const int gt_id = tid & 511;
+  const int gs_row = gt_id >> 3;
+  const uint32_t gs_off = static_cast<uint32_t>(sidx<kTN>(gs_row, 4 * (gt_id & 7)) * 2);
+  if (role == 1) {
 #pragma unroll
-  for (int s = 0; s < NS; ++s) {
-    uint2 pk;
-    pk.x = pack2(sacc[s][0], sacc[s][1]);
-    pk.y = pack2(sacc[s][2], sacc[s][3]);
-    put4<D>(S_s[0], oX, rbw * 16, (tb + 4 * s) * 16, pk);
+    for (int s = 0; s < NS; ++s) {
+      uint2 pk;
+      pk.x = pack2(sacc[s][0], sacc[s][1]);
+      pk.y = pack2(sacc[s][2], sacc[s][3]);
+      put4<D>(S_s[0], oX, rbw * 16, (tb + 4 * s) * 16, pk);
+    }
+    // Initial loads, each followed by S state stores into a zero-byte buffer
+    // (they are dropped) so that the vector-memory instruction stream has
+    // the same shape as in the loop: chunk load, S stores, chunk load, ...
+    // Then the wait at the top of every iteration is the same constant.
+#pragma unroll
+    for (int k = 0; k < kRing - 1; ++k) {
+      issue_chunk<D>(*rs[k], od, x, g, eta, alpha, T, c_beg + k, c_end, r0, w8);
+#pragma unroll
+      for (int s = 0; s < S; ++s) store8(r_none, os[s] + 64 * k, make_uint2(0, 0));  // not merged
+    }
+    // chunks 0 and 1 done: after chunk 1 come two more chunk loads and three store groups
+    wait_vm<2 * P + 3 * S>();
   }
-
-  // Initial loads, each followed by S stores into a zero-byte buffer (they
-  // are dropped) so that the vector-memory instruction stream has the same
-  // shape as in the loop: chunk load, S stores, chunk load, ...  Then the
-  // wait at the top of every iteration is the same constant.
-#pragma unroll
-  for (int k = 0; k < kRing - 1; ++k) {
-    issue_chunk<D>(*rs[k], od, x, g, eta, alpha, T, c_beg + k, c_end, r0, wave);
-    // distinct offsets, so that none of them is merged away
-    if (HAS_ST)
-#pragma unroll
-      for (int s = 0; s < NS; ++s) store8(r_none, os[s] + k, make_uint2(0, 0));
-    if (HAS_Y) store8(r_none, oy + k, make_uint2(0, 0));
-  }
-  // chunks 0 and 1 done: after chunk 1 come two more chunk loads and three store groups
-  wait_vm<2 * P + 3 * S>();
   lds_barrier();
   float lsum = 0.f;  // sum of l_last over the segment's chunks (prep wave)
-  if (wave == kPrepWave) {
+  if (role == 1 && w8 == kPrepWave) {
     lsum += prep_gates<D>(*rs[0], cv_of(c_beg), lane);
     lsum += prep_gates<D>(*rs[1], cv_of(c_beg + 1), lane);
   }
   lds_barrier();
-  scale_g<D>(*rs[0], GS_s[0], gs_off, gs_row);
-  if (HAS_Y) {
-    score_block<D>(*rs[0], AT_s[0], oX, oA, wave, lane);
-    if (wave < 2) score_block<D>(*rs[0], AT_s[0], oX, oA, wave + 8, lane);
+  if (role == 1) scale_g<D>(*rs[0], GS_s[0], gs_off, gs_row);
+  if (HAS_Y && role == 0) {
+    score_block<D>(*rs[0], AT_s[0], oX, oA, w8, lane);
+    if (w8 < 2) score_block<D>(*rs[0], AT_s[0], oX, oA, w8 + 8, lane);
   }
 
   // one chunk; K = (c - c_beg) % kRing is a compile-time constant
-  const auto step = [&](auto KC, int c) {
+  const auto step = [&](auto RC, auto KC, int c) {
+    constexpr int R = decltype(RC)::value;
     constexpr int K = decltype(KC)::value;
     Slot<D>& cur = *rs[K];
     Slot<D>& nx1 = *rs[(K + 1) % kRing];
@@ -342,36 +346,54 @@ __global__ __launch_bounds__(kNT) void fwd_mfma(FwdArgs a) {
     const int vl = c - c_beg;  // position in the segment: double-buffer parity
     const int64_t t0 = static_cast<int64_t>(c) * kC;
     const int cv = cv_of(c);
-    // chunk c + 2 loaded: issued after it are its own store group and one
-    // more (chunk load + stores); past the end it is a zero fill
-    wait_vm<P + 2 * S>();
+    // state (loader) waves: chunk c + 2 loaded -- issued after it are its own
+    // store group and one more (chunk load + stores); past the end it is a
+    // zero fill
+    if constexpr (R == 1) wait_vm<P + 2 * S>();
     lds_barrier();  // scores and gates of c + 1, D_in of c visible
-    issue_chunk<D>(dst, od, x, g, eta, alpha, T, c + kRing - 1, c_end, r0, wave);
-
-    if (HAS_ST) {
-      // chunk-start state of this wave's blocks (natural layout, bf16)
-      const __amdgpu_buffer_rsrc_t r_st = buffer_rsrc(st + static_cast<int64_t>(c) * D * D, D * D * 2);
+    if constexpr (R == 1) {
+      issue_chunk<D>(dst, od, x, g, eta, alpha, T, c + kRing - 1, c_end, r0, w8);
+      if (HAS_ST) {
+        // chunk-start state of this wave's blocks (natural layout, bf16)
+        const __amdgpu_buffer_rsrc_t r_st =
+            buffer_rsrc(st + static_cast<int64_t>(c) * D * D, D * D * 2);
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+          uint2 v;
+          v.x = pack2(sacc[s][0], sacc[s][1]);
+          v.y = pack2(sacc[s][2], sacc[s][3]);
+          store8(r_st, os[s], v);
+        }
+      }
+      if (w8 == kPrepWave) lsum += prep_gates<D>(nx2, cv_of(c + 2), lane);
+      scale_g<D>(nx1, GS_s[(vl + 1) & 1], gs_off, gs_row);
+      // state update, transposed: D^T[c][r] = Gamma D^T + sum_j x_j[c] (bk_j g_j[r]),
+      // into the other state buffer (the current one may still be read)
+      const __bf16* GS = GS_s[vl & 1];
+      bf16x8 gs[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) gs[kb] = frag_ts<kTN>(GS, oG, kb * 32, rbw * 16);
+      const float gam = cur.gam[0];
+      __bf16* S_out = S_s[(vl + 1) & 1];
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
-        uint2 v;
-        v.x = pack2(sacc[s][0], sacc[s][1]);
-        v.y = pack2(sacc[s][2], sacc[s][3]);
-        store8(r_st, os[s], v);
+        const int cb = tb + 4 * s;
+        sacc[s] = sacc[s] * gam;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+          sacc[s] = mfma16x16x32(frag_ts<D>(cur.X, oX, kb * 32, cb * 16), gs[kb], sacc[s]);
+        uint2 pk;
+        pk.x = pack2(sacc[s][0], sacc[s][1]);
+        pk.y = pack2(sacc[s][2], sacc[s][3]);
+        put4<D>(S_out, oX, rbw * 16, cb * 16, pk);
       }
-    }
-    if (wave == kPrepWave) lsum += prep_gates<D>(nx2, cv_of(c + 2), lane);
-    scale_g<D>(nx1, GS_s[(vl + 1) & 1], gs_off, gs_row);
-    if (HAS_Y) {
-      __bf16* AT1 = AT_s[(vl + 1) & 1];
-      score_block<D>(nx1, AT1, oX, oA, wave, lane);
-      if (wave < 2) score_block<D>(nx1, AT1, oX, oA, wave + 8, lane);
-    }
-
-    const __bf16* S_in = S_s[vl & 1];
-    if (HAS_Y) {
+    } else if (HAS_Y) {
+      score_block<D>(nx1, AT_s[(vl + 1) & 1], oX, oA, w8, lane);
+      if (w8 < 2) score_block<D>(nx1, AT_s[(vl + 1) & 1], oX, oA, w8 + 8, lane);
       // y^T[r][i] for this wave's block; each lane stores 4 consecutive rows
       // of one token straight from the accumulators.  (For token blocks 0
       // and 1 the second K block of A^T is zero.)
+      const __bf16* S_in = S_s[vl & 1];
       const __bf16* AT = AT_s[vl & 1];
       f32x4 ya = zero4(), yb = zero4();
 #pragma unroll
@@ -391,48 +413,35 @@ __global__ __launch_bounds__(kNT) void fwd_mfma(FwdArgs a) {
       pk.y = pack2(ya[2] + eqi * yb[2], ya[3] + eqi * yb[3]);
       store8(ry, oy, pk);
     }
-
-    // state update, transposed: D^T[c][r] = Gamma D^T + sum_j x_j[c] (bk_j g_j[r]),
-    // into the other state buffer (the current one may still be read)
-    {
-      const __bf16* GS = GS_s[vl & 1];
-      bf16x8 gs[2];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) gs[kb] = frag_ts<kTN>(GS, oG, kb * 32, rbw * 16);
-      const float gam = cur.gam[0];
-      __bf16* S_out = S_s[(vl + 1) & 1];
-#pragma unroll
-      for (int s = 0; s < NS; ++s) {
-        const int cb = tb + 4 * s;
-        sacc[s] = sacc[s] * gam;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-          sacc[s] = mfma16x16x32(frag_ts<D>(cur.X, oX, kb * 32, cb * 16), gs[kb], sacc[s]);
-        uint2 pk;
-        pk.x = pack2(sacc[s][0], sacc[s][1]);
-        pk.y = pack2(sacc[s][2], sacc[s][3]);
-        put4<D>(S_out, oX, rbw * 16, cb * 16, pk);
-      }
-    }
   };
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
   using I2 = std::integral_constant<int, 2>;
   using I3 = std::integral_constant<int, 3>;
   using I4 = std::integral_constant<int, 4>;
-  for (int v = 0; v < nloc; v += kRing) {
-    step(I0{}, c_beg + v);
-    if (v + 1 >= nloc) break;
-    step(I1{}, c_beg + v + 1);
-    if (v + 2 >= nloc) break;
-    step(I2{}, c_beg + v + 2);
-    if (v + 3 >= nloc) break;
-    step(I3{}, c_beg + v + 3);
-    if (v + 4 >= nloc) break;
-    step(I4{}, c_beg + v + 4);
-  }
+  // each role walks in its own copy of the loop (same barriers), so that
+  // registers are allocated per role; the loader role first (with this
+  // order the compiler's wait analysis keeps the loaders' loads in flight
+  // out of the other role's loop)
+  const auto walk = [&](auto RC) {
+    for (int v = 0; v < nloc; v += kRing) {
+      step(RC, I0{}, c_beg + v);
+      if (v + 1 >= nloc) break;
+      step(RC, I1{}, c_beg + v + 1);
+      if (v + 2 >= nloc) break;
+      step(RC, I2{}, c_beg + v + 2);
+      if (v + 3 >= nloc) break;
+      step(RC, I3{}, c_beg + v + 3);
+      if (v + 4 >= nloc) break;
+      step(RC, I4{}, c_beg + v + 4);
+    }
+  };
+  if (role == 1)
+    walk(I1{});
+  else
+    walk(I0{});
   wait_vm<0>();  // no load into LDS may outlive the work-group
-  if (a.seg_out) {
+  if (a.seg_out && role == 1) {
     // the segment's final state (zero start) and its summed log2 alpha
     float* so = a.seg_out + (bh * a.n_seg + seg) * D * D;
 #pragma unroll
@@ -440,7 +449,7 @@ __global__ __launch_bounds__(kNT) void fwd_mfma(FwdArgs a) {
       const int cb = tb + 4 * s;
       *reinterpret_cast<f32x4*>(so + (r0 + rbw * 16 + l16) * D + cb * 16 + 4 * g4) = sacc[s];
     }
-    if (tile == 0 && wave == kPrepWave && lane == 0) a.seg_lg[bh * a.n_seg + seg] = lsum;
+    if (tile == 0 && w8 == kPrepWave && lane == 0) a.seg_lg[bh * a.n_seg + seg] = lsum;
   }
 }
 
