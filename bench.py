@@ -61,17 +61,12 @@ def pass_kernels(w, which, segmented, generic):
         return {"fwd": "fwd_generic", "bwd": "bwd_generic + finalize_kernel"}[which]
     if which == "fwd":
         return ("fwd_mfma (state-only) + seg_combine + fwd_mfma" if segmented else "fwd_mfma")
-    if w.d_in == 64:
-        # the fused backward takes its own segment count: enough (segment,
-        # sequence-head) work-groups for 256 CUs, at least 16 chunks each
-        bh, nch = w.B * w.H, -(-w.T // 64)
-        nseg = max(1, min(-(-256 // bh), nch // 16)) if bh < 256 else 1
-        pre = "bwd_lam + " if (segmented or nseg > 1) else ""
-        return pre + "bwd_f64 + finalize_kernel"
-    body = "bwd_a + bwd_b"
-    if segmented:
-        body = "bwd_lam + seg_combine + " + body
-    return body + " + finalize_kernel"
+    # the fused backward takes its own segment count: enough (segment,
+    # sequence-head) work-groups for 256 CUs, at least 16 chunks each
+    bh, nch = w.B * w.H, -(-w.T // 64)
+    nseg = max(1, min(-(-256 // bh), nch // 16)) if bh < 256 else 1
+    pre = "bwd_lam + " if (segmented or nseg > 1) else ""
+    return pre + ("bwd_f64" if w.d_in == 64 else "bwd_f128") + " + finalize_kernel"
 
 
 def cpu_baseline(w, budget_s=20.0):

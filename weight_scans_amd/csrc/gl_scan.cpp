@@ -127,7 +127,7 @@ gl_status_t make_plan(const gl_scan_desc_t* d, Plan* p) {
   p->n_ckpt = p->n_chunks;
   p->saved_bytes = round_up(BH * p->n_ckpt * dd * p->state_elem);
   p->part_bytes = round_up(static_cast<size_t>(p->n_tiles) * BH * d->T * p->comp);
-  p->fused = p->mfma && d->d_in == 64 && p->n_chunks > 0;
+  p->fused = p->mfma && p->n_chunks > 0;
   if (p->fused) {
     int nb = 1;
     if (d->segments > 0) {
@@ -318,7 +318,9 @@ gl_status_t gl_scan_bwd(const gl_scan_desc_t* desc, const void* x, const void* g
       bf.seg_lam = seg;  // composed per segment by the fused kernel itself
       bf.seg_lg_in = lg;
     }
-    if (st == GL_SUCCESS) st = hip_status(gls::launch_mfma_bwd_f64(bf, s), "fused backward");
+    if (st == GL_SUCCESS)
+      st = hip_status(b.d_in == 64 ? gls::launch_mfma_bwd_f64(bf, s) : gls::launch_mfma_bwd_f128(bf, s),
+                      "fused backward");
   } else if (p.n_seg <= 1) {
     st = hip_status(gls::launch_mfma_bwd(b, s), "backward launch");
   } else {

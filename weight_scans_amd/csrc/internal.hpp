@@ -106,7 +106,8 @@ hipError_t launch_mfma_bwd(const BwdArgs& a, hipStream_t s);
 hipError_t launch_mfma_bwd_a(const BwdArgs& a, hipStream_t s);  // row tiles: dg, deta, dW0
 hipError_t launch_mfma_bwd_b(const BwdArgs& a, hipStream_t s);  // column tiles: dx, dalpha
 hipError_t launch_mfma_bwd_lam(const BwdArgs& a, hipStream_t s);  // adjoint-only segment pass
-hipError_t launch_mfma_bwd_f64(const BwdArgs& a, hipStream_t s);  // fused reverse scan, d = 64
+hipError_t launch_mfma_bwd_f64(const BwdArgs& a, hipStream_t s);   // fused reverse scan, d = 64
+hipError_t launch_mfma_bwd_f128(const BwdArgs& a, hipStream_t s);  // fused reverse scan, d = 128
 // Exclusive affine scan over the segments of every (b, h): buf[s] <- the state
 // entering segment s (in segment order, or from the right end if reverse).
 hipError_t launch_seg_combine(float* buf, const float* lg, int64_t BH, int n_seg, int dd,

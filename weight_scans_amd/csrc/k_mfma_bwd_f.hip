@@ -4,44 +4,40 @@
 // One work-group walks the chunks of one (segment, sequence-head) from right
 // to left carrying the adjoint Lam = dL/dD (the exact adjoint of the forward
 // scan, GradLev abstract, omanscience.com) in fp32 registers, and emits every
-// gradient of the chunk it passes.  With chunk-local l (inclusive cumsum of
-// log2 alpha), lq_i = l_{i-1}, e(.) = 2^(.), XX_ui = x_u . x_i:
-//   P_ui  = e(lq_u - l_i) XX_ui                         (u > i)
-//   Be_ij = e(lq_i - l_j)(-eta_j)(dy_i . g_j)           (j < i),  M = Be + Be^T
+// gradient of the chunk it passes.  With P, Be, M = Be + Be^T and the Be dots
+// as in bwd_fused.hpp:
 //   u_i   = e(l_last - l_i) Lam_out x_i + sum_{u>i} P_ui dy_u
 //   dg_i  = -eta_i u_i,  deta_i = -g_i . u_i
 //   dx_i  = W0^T dy_i + e(lq_i) D_in^T dy_i + (M X)_i - eta_i e(l_last - l_i) Lam_out^T g_i
 //   dW0  += sum_u dy_u x_u^T
 //   Lam_in = e(l_last) Lam_out + sum_u e(lq_u) dy_u x_u^T
-// and dalpha from the dots pp_i = g_i . (Lam_out x_i), rr_i = x_i . (D_in^T dy_i),
-// qq_i = sum_{j<i} Be_ij XX_ij, kk_j = sum_{u>j} Be_uj XX_uj and <Lam_out, D_in>
-// (the rows and columns of Be o XX give the two Be dots without a product).
-// D_in is the chunk-start state the forward kernel stores.
+// and dalpha from pp_i = g_i . (Lam_out x_i), rr_i = x_i . (D_in^T dy_i), the
+// Be dots and <Lam_out, D_in>.  D_in is the chunk-start state the forward
+// kernel stores.
 //
 // Sixteen waves, one of each role on every SIMD (role = wave / 4, quadrant =
 // wave % 4; 32 x 32 output quadrants, so every fragment read serves two
 // MFMAs):
-//   0  dx^T quadrant (columns k, tokens i), its rr share;
+//   0  dx^T quadrant (columns k, tokens i), its rr share; causal block q of
+//      the next chunk;
 //   1  Lam^T and dW0^T quadrant (columns k, rows r) in fp32 registers, the
-//      <Lam_out, D_in> share, the bf16 copy of the next Lam_out;
+//      <Lam_out, D_in> share, the bf16 copy of the next Lam_out; causal
+//      block 4 + q of the next chunk;
 //   2  u^T quadrant (rows r, tokens i): dg, the deta and pp shares;
-//   3  causal 16 x 16 blocks of XX and of dy.g for the NEXT chunk: P^T, M,
-//      the qq / kk partials; wave 14 also derives the gates of the chunk
-//      after it, wave 15 finishes dalpha and deta of the previous chunk.
-// Chunk tiles (x, g, dy, D_in, and the gate rows of the chunk after) come by
-// direct buffer loads into a ring of three slots: while the chunk of step j
-// is finished and the causal blocks of chunk j + 1 are formed, chunk j + 2
-// is in flight.  One barrier per chunk; every wave issues the same vector-
-// memory instructions (three loads, four 8-byte and two 4-byte stores, the
-// unused ones into zero-byte buffers), so the wait at the top of a step is a
-// constant.
+//   3  loaders: tile q (x, g, dy, D_in) of the chunk two ahead and a gate
+//      row; waves 12-13 causal blocks 8-9, wave 14 the gates two chunks
+//      ahead, wave 15 dalpha and deta of the previous chunk.
+// Chunk tiles come by direct buffer loads into a ring of three slots: while
+// the chunk of step j is finished and the causal blocks of chunk j + 1 are
+// formed, chunk j + 2 is in flight.  One barrier per chunk.  Each role walks
+// in its own copy of the loop (registers are allocated per role); only the
+// loaders issue loads and wait for them, and each of them issues the same
+// loads and stores every step, so that wait is a constant.
 #include <algorithm>
 #include <cstddef>
 #include <type_traits>
 
-#include "dev_common.hpp"
-#include "internal.hpp"
-#include "mfma.hpp"
+#include "bwd_fused.hpp"
 
 namespace gls {
 namespace {
@@ -53,7 +49,6 @@ constexpr int kNT = 64 * kNW;   // threads
 constexpr int kGateWave = 14;   // derives the gates two chunks ahead
 constexpr int kAlphaWave = 15;  // dalpha and deta one chunk behind
 constexpr int kLoaderStores = 2;  // stores per loader wave (role 3) per step
-constexpr int kMPad = 64;         // bf16 past each M tile: target of masked-off writes
 
 struct alignas(16) SlotF {
   __bf16 X[kC * kD];    // x, swizzled [token][k]
@@ -63,18 +58,9 @@ struct alignas(16) SlotF {
   float q[2][kC];       // eta, alpha of the chunk after (in walk order)
 };
 
-struct alignas(16) RecF {  // gates of one chunk, lane = token
-  float lq[kC], li[kC], nb[kC], eq[kC], e2[kC], al[kC];
-  float gam, llast, pad[2];
-};
-
 struct alignas(16) PartF {  // per-token shares of one chunk
   float pp[2][kC], rr[2][kC], de[2][kC];
   float c0[4];
-};
-
-struct alignas(16) QkF {  // per causal block: row sums (qq) and column sums (kk) of Be o XX
-  float qq[10][16], kk[10][16];
 };
 
 // Per-lane byte offsets of a [64][64] bf16 tile load into a swizzled LDS
@@ -116,111 +102,6 @@ __device__ __forceinline__ void issue_f(SlotF& sl, const DmaOffF& od, uint32_t o
   const int64_t tq = inq ? static_cast<int64_t>(kq) * kC : 0;
   const int cq = inq ? static_cast<int>(std::min<int64_t>(kC, T - tq)) : 0;
   dma4(buffer_rsrc(((ld & 1) == 0 ? eta : alpha) + tq, cq * 4), oq, sl.q[ld & 1]);
-}
-
-// Gates of a chunk from its eta / alpha rows (one wave, lane = token).
-// Padding tokens carry alpha = 1, eta = 0.
-__device__ __forceinline__ void gates_f(const float (*q)[kC], RecF& r, int cv, int lane) {
-  const float et = lane < cv ? q[0][lane] : 0.f;
-  const float al = lane < cv ? q[1][lane] : 1.f;
-  const ChunkGates gt = chunk_gates(al, lane);
-  r.lq[lane] = gt.lq;
-  r.li[lane] = gt.l;
-  r.nb[lane] = -et;
-  r.eq[lane] = fexp2(gt.lq);
-  r.e2[lane] = fexp2(gt.llast - gt.l);
-  r.al[lane] = al;
-  if (lane == 0) {
-    r.gam = fexp2(gt.llast);
-    r.llast = gt.llast;
-  }
-}
-
-__device__ __forceinline__ f32x4 unpack4f(const uint2& p) {
-  f32x4 v;
-  v[0] = bf16_val(p.x & 0xffffu);
-  v[1] = bf16_val(p.x >> 16);
-  v[2] = bf16_val(p.y & 0xffffu);
-  v[3] = bf16_val(p.y >> 16);
-  return v;
-}
-
-__device__ __forceinline__ float dot4f(const f32x4& a, const f32x4& b) {
-  return a[0] * b[0] + a[1] * b[1] + a[2] * b[2] + a[3] * b[3];
-}
-
-__device__ __forceinline__ uint2 pack4f(const f32x4& v) {
-  uint2 pk;
-  pk.x = pack2(v[0], v[1]);
-  pk.y = pack2(v[2], v[3]);
-  return pk;
-}
-
-// The 8 bf16 of a fragment, each times its own factor (e0: elements 0-3,
-// e1: 4-7), rounded back to bf16.
-__device__ __forceinline__ bf16x8 scale8(const bf16x8& f, const f32x4& e0, const f32x4& e1) {
-  bf16x8 r;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    r[q] = static_cast<__bf16>(static_cast<float>(f[q]) * e0[q]);
-    r[q + 4] = static_cast<__bf16>(static_cast<float>(f[q + 4]) * e1[q]);
-  }
-  return r;
-}
-
-// Sum over the 16 lanes of each row of 16; valid in lane 15 of the row.
-__device__ __forceinline__ float row16_sum(float x) {
-  x += dpp<kRowShr1>(0.f, x);
-  x += dpp<kRowShr2>(0.f, x);
-  x += dpp<kRowShr4>(0.f, x);
-  x += dpp<kRowShr8>(0.f, x);
-  return x;
-}
-
-// Causal block b (0..9) of the chunk in `sl`: rows a (block tri_i), columns
-// b' (block tri_j).  XX_ab' and dy_a . g_b' on the matrix cores, then
-//   P^T[b'][a] = e(lq_a - l_b') XX_ab',  M[b'][a] = M[a][b'] = Be_ab'
-// (zero unless b' < a), and the row / column sums of Be o XX.
-__device__ __forceinline__ void causal_f(const SlotF& sl, const RecF& r, __bf16* PT, __bf16* M,
-                                         QkF& qk, const LaneOff<kD>& o, int b, int lane) {
-  const int g4 = lane >> 4, l16 = lane & 15;
-  const int rb = tri_i(b), cb = tri_j(b);
-  f32x4 xx = zero4(), be = zero4();
-#pragma unroll
-  for (int kk = 0; kk < 2; ++kk) {
-    xx = mfma16x16x32(frag_s<kD>(sl.X, o, rb * 16, kk * 32), frag_s<kD>(sl.X, o, cb * 16, kk * 32), xx);
-    be = mfma16x16x32(frag_s<kD>(sl.DY, o, rb * 16, kk * 32), frag_s<kD>(sl.G, o, cb * 16, kk * 32),
-                      be);
-  }
-  const int col = cb * 16 + l16, r0 = rb * 16 + 4 * g4;
-  const float lc = r.li[col], nbc = r.nb[col];
-  const f32x4 lqr = *reinterpret_cast<const f32x4*>(&r.lq[r0]);
-  f32x4 p, v, z;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const float e = fexp2(lqr[q] - lc);
-    const bool m = col < r0 + q;
-    p[q] = m ? xx[q] * e : 0.f;
-    v[q] = m ? be[q] * (e * nbc) : 0.f;
-    z[q] = v[q] * xx[q];
-  }
-  put4<kC>(PT, o, cb * 16, rb * 16, pack4f(p));
-  put4<kC>(M, o, cb * 16, rb * 16, pack4f(v));
-  // the mirrored half of M, element by element, after the put4 above (on
-  // the diagonal block both touch the same bytes, and one wave's LDS writes
-  // land in order); lanes with nothing to write there write into the pad
-  // past the tile instead, so that the store is unconditional
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int e = col < r0 + q ? sidx<kC>(r0 + q, col) : kC * kC + lane;
-    M[e] = static_cast<__bf16>(v[q]);
-  }
-  f32x4 zr;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) zr[q] = row16_sum(z[q]);
-  if (l16 == 15) *reinterpret_cast<f32x4*>(&qk.qq[b][4 * g4]) = zr;
-  const float t = sum_rows(z[0] + z[1] + z[2] + z[3]);
-  if (g4 == 0) qk.kk[b][l16] = t;
 }
 
 __global__ __launch_bounds__(kNT) void bwd_f64(BwdArgs a) {
@@ -331,7 +212,7 @@ __global__ __launch_bounds__(kNT) void bwd_f64(BwdArgs a) {
       for (int bb = 0; bb < 2; ++bb)
         put4<kD>(L_s[0], o, (2 * lq2 + bb) * 16, (2 * hq + aa) * 16, pack4f(pr[2 * aa + bb]));
   }
-  if (wave == kGateWave) gates_f(rs[0]->q, rec[0], cv_of(chunk_at(0)), lane);
+  if (wave == kGateWave) gates_f(rs[0]->q[0], rs[0]->q[1], rec[0], cv_of(chunk_at(0)), lane);
 
   // per-lane offsets of the dx / dg stores: token 16(2 lq2 + b) + l16,
   // columns 16(2 hq + a) + 4 g4 ..
@@ -362,8 +243,8 @@ __global__ __launch_bounds__(kNT) void bwd_f64(BwdArgs a) {
     // waves, 8-9: loader waves 12 and 13)
     const auto causal_next = [&](int b) {
       if (chunk_at(j + 1) >= 0)
-        causal_f(nx, rec[(j + 1) & 3], PT_s[(j + 1) & 1], M_s[(j + 1) & 1], qk[(K + 1) % 3], o, b,
-                 lane);
+        causal_f<kD>(nx.X, nx.G, nx.DY, rec[(j + 1) & 3], PT_s[(j + 1) & 1], M_s[(j + 1) & 1],
+                     qk[(K + 1) % 3], o, o, b, lane);
     };
 
     const int c = chunk_at(j);
@@ -597,61 +478,19 @@ __global__ __launch_bounds__(kNT) void bwd_f64(BwdArgs a) {
       if (qd < 2) causal_next(8 + qd);
       if (wave == kGateWave) {
         const int c2 = chunk_at(j + 2);
-        if (c2 >= 0) gates_f(nx.q, rec[(j + 2) & 3], cv_of(c2), lane);
+        if (c2 >= 0) gates_f(nx.q[0], nx.q[1], rec[(j + 2) & 3], cv_of(c2), lane);
       }
       if (wave == kAlphaWave) {
         const int cp = chunk_at(j - 1);
         if (cp >= 0) {
-          // dalpha_i = e(l_last - l_i + lq_i) c0 + e(l_last - l_i) sum_{j<i} e(lq_i - l_j)(-eta_j) pp_j
-          //            + e(lq_i) sum_{u>i} e(lq_u - l_i) rr_u
-          //            + (sum_{u>i} qq_u - sum_{j>=i} kk_j) / alpha_i
-          // (affine-pair and plain scans over the lanes; the suffix sums run
-          // on the reversed lane order)
+          // dalpha and deta of the chunk finished one step ago
           const RecF& rp = rec[(j - 1) & 3];
           const PartF& pr = part[(j - 1) & 1];
           const QkF& qr = qk[(K + 2) % 3];
           const int ir = kC - 1 - lane;
-          // causal block (R, C) is number R (R + 1) / 2 + C: token i takes
-          // the row sums of blocks (i / 16, 0..i / 16) and the column sums of
-          // blocks (i / 16..3, i / 16) (fixed four terms, clamped indices)
-          const auto qq_of = [&](int i) {
-            const int R = i >> 4, b0 = R * (R + 1) / 2;
-            float s = 0.f;
-#pragma unroll
-            for (int cc = 0; cc < 4; ++cc) {
-              const float v = qr.qq[cc <= R ? b0 + cc : b0][i & 15];
-              s += cc <= R ? v : 0.f;
-            }
-            return s;
-          };
-          const auto kk_of = [&](int i) {
-            const int Cc = i >> 4;
-            float s = 0.f;
-#pragma unroll
-            for (int R = 0; R < 4; ++R) {
-              const float v = qr.kk[R >= Cc ? R * (R + 1) / 2 + Cc : 0][i & 15];
-              s += R >= Cc ? v : 0.f;
-            }
-            return s;
-          };
           const float c0 = (pr.c0[0] + pr.c0[1]) + (pr.c0[2] + pr.c0[3]);
-          const float pp = pr.pp[0][lane] + pr.pp[1][lane];
-          const float kk = kk_of(lane);
-          const float rr_r = pr.rr[0][ir] + pr.rr[1][ir];
-          const float z_r = qq_of(ir) - kk_of(ir);
-          const float al = rp.al[lane], al_r = rp.al[ir];
-          const float li = rp.li[lane], lqi = rp.lq[lane], lq_r = rp.lq[ir], llast = rp.llast;
-          float a2 = al, b2 = rp.nb[lane] * pp;
-          wave_scan_affine(a2, b2);
-          const float s2 = wave_shift_up(b2, 0.f);
-          float a3 = al_r, b3 = rr_r;
-          wave_scan_affine(a3, b3);
-          const float s3_r = wave_shift_up(b3, 0.f);
-          const float zs_r = wave_shift_up(wave_scan_add(z_r), 0.f);
-          const float t34 =
-              wave_reverse(fexp2(lq_r) * s3_r + zs_r * __builtin_amdgcn_rcpf(al_r), lane);
-          s4a = fexp2(llast - li + lqi) * c0 + fexp2(llast - li) * s2 + t34 -
-                kk * __builtin_amdgcn_rcpf(al);
+          s4a = dalpha_f(rp, qr, pr.pp[0][lane] + pr.pp[1][lane], pr.rr[0][ir] + pr.rr[1][ir], c0,
+                         lane);
           s4b = pr.de[0][lane] + pr.de[1][lane];
           const int64_t tp = static_cast<int64_t>(cp) * kC;
           ra = buffer_rsrc(dal + tp, cv_of(cp) * 4);

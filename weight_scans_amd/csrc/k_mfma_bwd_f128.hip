@@ -1,0 +1,427 @@
+// k_mfma_bwd_f128.hip -- fused matrix-core reverse scan for bf16 io,
+// d_in = d_out = 128 (gfx950, v_mfma_f32_16x16x32_bf16).
+//
+// The same per-chunk mathematics as the d = 64 kernel (k_mfma_bwd_f.hip; P,
+// Be, M = Be + Be^T and the Be dots in bwd_fused.hpp; the exact adjoint of the
+// forward scan, GradLev abstract, omanscience.com):
+//   u_i   = e(l_last - l_i) Lam_out x_i + sum_{u>i} P_ui dy_u
+//   dg_i  = -eta_i u_i,  deta_i = -g_i . u_i
+//   dx_i  = W0^T dy_i + e(lq_i) D_in^T dy_i + (M X)_i - eta_i e(l_last - l_i) Lam_out^T g_i
+//   dW0  += sum_u dy_u x_u^T,  Lam_in = e(l_last) Lam_out + sum_u e(lq_u) dy_u x_u^T
+// One work-group per (segment, sequence-head) walks its chunks from the
+// right with the whole 128 x 128 adjoint and dW0 in fp32 registers.
+//
+// A chunk's tiles (x, g, dy: 16 KB each; D_in: 32 KB) fill one LDS slot; the
+// next chunk is loaded into registers (ten 16-byte units per thread) while
+// this one is worked on, and written into the slot at the top of the next
+// step -- so the slot is single and 80 KB of loads are in flight per CU.
+// Eight waves (two per SIMD: the adjoint, dW0 and the staged chunk need the
+// register room); wave w holds the 32 x 64 region (k rows 32 (w % 4) ..,
+// r columns 64 (w / 4) ..) of Lam and dW0.  Three barriers per step:
+//   top:     the staged chunk into the slot, the bf16 copy of Lam_out, the
+//            loads of the next chunk (and the gate rows of the one after);
+//   phase A: causal blocks (P^T, M, the Be dots: block w, and 8, 9 on waves
+//            4, 5); every wave its region of Lam and dW0 (<Lam_out, D_in>
+//            share, then the update); wave 6 the gates of the next chunk;
+//   phase B: waves 0-3 dx (32 columns each) and the rr shares; waves 4-7 u
+//            (32 rows each): dg, the deta and pp shares; wave 7 dalpha and
+//            deta of the chunk before.
+// Each role walks in its own copy of the loop, so registers are allocated
+// per role.  All loads go to registers (the compiler places the waits); no
+// direct-to-LDS loads are involved.
+#include <type_traits>
+
+#include "bwd_fused.hpp"
+
+namespace gls {
+namespace {
+
+constexpr int kD = 128;        // d_in = d_out
+constexpr int kC = kFC;        // tokens per chunk
+constexpr int kNW = 8;         // waves per work-group
+constexpr int kNT = 64 * kNW;  // threads
+constexpr int kGateWave = 6;   // gates of the next chunk
+constexpr int kAlphaWave = 7;  // dalpha and deta one chunk behind
+
+struct alignas(16) SlotH {
+  __bf16 X[kC * kD];   // x, swizzled [token][k]
+  __bf16 G[kC * kD];   // g, swizzled [token][r]
+  __bf16 DY[kC * kD];  // dy, swizzled [token][r]
+  __bf16 S[kD * kD];   // D_in, swizzled [r][k]
+};
+
+struct alignas(16) PartH {  // per-token shares of one chunk, one per wave
+  float pp[kNW][kC], de[kNW][kC];  // from its 16 rows of u
+  float rr[kNW][kC];               // from its 16 columns of dx
+  float c0[kNW];                   // <Lam_out, D_in> over its region
+};
+
+// 16-byte unit u of a [rows][128] bf16 tile (16 units per row): read from
+// byte u * 16, written to its swizzled place.
+__device__ __forceinline__ uint32_t unit_lds(int u) {
+  return static_cast<uint32_t>(sidx<kD>(u >> 4, 8 * (u & 15)) * 2);
+}
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x4 load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
+
+__global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(1, 2)))
+void bwd_f128(BwdArgs a) {
+  __shared__ SlotH sl;
+  __shared__ __bf16 L_s[kD * kD];           // Lam_out, bf16 [r][k]; W0 staging at the start
+  __shared__ __bf16 PT_s[kC * kC];          // P^T
+  __shared__ __bf16 M_s[kC * kC + kMPad];   // Be + Be^T (+ pad)
+  __shared__ float rows_s[2][2][kC];        // eta, alpha rows by chunk parity
+  __shared__ RecF rec[4];
+  __shared__ PartH part[2];
+  __shared__ QkF qk[2];
+
+  const int64_t BH = a.B * a.H, T = a.T;
+  const int n = a.n_chunks;
+  const int64_t bh = blockIdx.x % BH;
+  const int seg = static_cast<int>(blockIdx.x / BH);
+  const int c_beg = seg * a.seg_chunks;
+  const int c_end = std::min(n, c_beg + a.seg_chunks);
+  const int nloc = c_end - c_beg;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g4 = lane >> 4, l16 = lane & 15;
+  // this wave's region of Lam^T and dW0^T: k blocks 2 kq + a, r blocks 4 rh + b
+  const int kq = wave & 3, rh = wave >> 2;
+  const int h = static_cast<int>(bh % a.H);
+  const uint16_t* x = static_cast<const uint16_t*>(a.x) + bh * T * kD;
+  const uint16_t* g = static_cast<const uint16_t*>(a.g) + bh * T * kD;
+  const uint16_t* dy = static_cast<const uint16_t*>(a.dy) + bh * T * kD;
+  const float* eta = static_cast<const float*>(a.eta) + bh * T;
+  const float* alpha = static_cast<const float*>(a.alpha) + bh * T;
+  const uint16_t* W0 = static_cast<const uint16_t*>(a.W0) + static_cast<int64_t>(h) * kD * kD;
+  const uint16_t* st = static_cast<const uint16_t*>(a.states) + bh * static_cast<int64_t>(n) * kD * kD;
+  uint16_t* dxp = static_cast<uint16_t*>(a.dx) + bh * T * kD;
+  uint16_t* dgp = static_cast<uint16_t*>(a.dg) + bh * T * kD;
+  float* dal = static_cast<float*>(a.dalpha_out) + bh * T;
+  float* det = static_cast<float*>(a.deta_out) + bh * T;
+
+  const LaneOff<kD> o_in = lane_off<kD>(lane);
+  const LaneOff<kC> o64_in = lane_off<kC>(lane);
+
+  const auto chunk_at = [&](int v) { return (v >= 0 && v < nloc) ? c_end - 1 - v : -1; };
+  const auto cv_of = [&](int c) {
+    return c < 0 ? 0 : static_cast<int>(std::min<int64_t>(kC, T - static_cast<int64_t>(c) * kC));
+  };
+
+  // ---- staged loads: x, g, dy units tid and tid + 512; D_in units tid +
+  // 512 j (j < 4); the eta / alpha rows (wave 0, lanes 0-31)
+  u32x4 sx[2], sg[2], sdy[2], ss[4], sq;
+  const auto load_chunk = [&](int c) {
+    const bool in = c >= 0;
+    const int64_t t0 = in ? static_cast<int64_t>(c) * kC : 0;
+    const int cv = cv_of(c);
+    const __amdgpu_buffer_rsrc_t rx = buffer_rsrc(x + t0 * kD, cv * kD * 2);
+    const __amdgpu_buffer_rsrc_t rg = buffer_rsrc(g + t0 * kD, cv * kD * 2);
+    const __amdgpu_buffer_rsrc_t rd = buffer_rsrc(dy + t0 * kD, cv * kD * 2);
+    const __amdgpu_buffer_rsrc_t rs =
+        buffer_rsrc(st + (in ? static_cast<int64_t>(c) : 0) * kD * kD, in ? kD * kD * 2 : 0);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const uint32_t off = static_cast<uint32_t>((tid + kNT * j) * 16);
+      sx[j] = load16(rx, off);
+      sg[j] = load16(rg, off);
+      sdy[j] = load16(rd, off);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) ss[j] = load16(rs, static_cast<uint32_t>((tid + kNT * j) * 16));
+  };
+  const auto load_rows = [&](int c) {
+    if (wave == 0) {
+      const int64_t t0 = c >= 0 ? static_cast<int64_t>(c) * kC : 0;
+      const int cv = cv_of(c);
+      const uint32_t off = static_cast<uint32_t>((lane & 15) * 16);
+      const u32x4 qe = load16(buffer_rsrc(eta + t0, cv * 4), off);
+      const u32x4 qa = load16(buffer_rsrc(alpha + t0, cv * 4), off);
+      sq = lane < 16 ? qe : qa;
+    }
+  };
+  const auto put_chunk = [&]() {
+    char* b = reinterpret_cast<char*>(&sl);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const uint32_t u = unit_lds(tid + kNT * j);
+      *reinterpret_cast<u32x4*>(b + offsetof(SlotH, X) + u) = sx[j];
+      *reinterpret_cast<u32x4*>(b + offsetof(SlotH, G) + u) = sg[j];
+      *reinterpret_cast<u32x4*>(b + offsetof(SlotH, DY) + u) = sdy[j];
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      *reinterpret_cast<u32x4*>(b + offsetof(SlotH, S) + unit_lds(tid + kNT * j)) = ss[j];
+  };
+  const auto put_rows = [&](float (*rw)[kC]) {
+    if (wave == 0 && lane < 32)
+      *reinterpret_cast<u32x4*>(&rw[lane >> 4][4 * (lane & 15)]) = sq;
+  };
+
+  // ---- set-up: first chunk and the gate rows of the first chunk in flight;
+  // W0 staged in L_s for the dx waves' W0^T fragments; the entering adjoint
+  // (given, or composed from the segments to the right)
+  load_chunk(chunk_at(0));
+  load_rows(chunk_at(0));
+  for (int idx = tid; idx < kD * kD / 8; idx += kNT) {
+    const int r = idx >> 4, cc = 8 * (idx & 15);
+    *reinterpret_cast<uint4*>(&L_s[sidx<kD>(r, cc)]) =
+        *reinterpret_cast<const uint4*>(W0 + static_cast<int64_t>(r) * kD + cc);
+  }
+  f32x4 lam[2][4], dw[2][4];  // Lam^T / dW0^T blocks (k block 2 kq + a, r block 4 rh + b)
+#pragma unroll
+  for (int aa = 0; aa < 2; ++aa)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      lam[aa][b] = zero4();
+      dw[aa][b] = zero4();
+    }
+  if (a.seg_lam) {
+    const int s_lo = a.seg_lg_in ? seg + 1 : seg;
+    const int s_hi = a.seg_lg_in ? a.n_seg - 1 : seg;
+    for (int s2 = s_hi; s2 >= s_lo; --s2) {
+      const float* sp = a.seg_lam + (bh * a.n_seg + s2) * kD * kD;
+      const float gs = a.seg_lg_in ? fexp2(a.seg_lg_in[bh * a.n_seg + s2]) : 0.f;
+#pragma unroll
+      for (int aa = 0; aa < 2; ++aa)
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+          lam[aa][b] = lam[aa][b] * gs +
+                       *reinterpret_cast<const f32x4*>(sp + ((4 * rh + b) * 16 + l16) * kD +
+                                                       (2 * kq + aa) * 16 + 4 * g4);
+    }
+  }
+  put_rows(rows_s[0]);
+  __syncthreads();
+  bf16x8 wf[4];  // W0^T fragments of this wave's dx columns (k block `wave`, K block kk of r)
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) wf[kk] = frag_ts<kD>(L_s, o_in, kk * 32, wave * 16);
+  if (wave == kGateWave) gates_f(rows_s[0][0], rows_s[0][1], rec[0], cv_of(chunk_at(0)), lane);
+  for (int idx = tid; idx < kC * kC / 8; idx += kNT)
+    reinterpret_cast<uint4*>(PT_s)[idx] = make_uint4(0, 0, 0, 0);
+  load_rows(chunk_at(1));
+
+  // step v: chunk v of the walk (slot), causal blocks and gates in phase A,
+  // outputs in phase B, dalpha of chunk v - 1
+  const auto step = [&](int v) {
+    const int c = chunk_at(v);
+    lds_barrier();  // B1: the previous step no longer reads the slot, L, P^T or M
+    LaneOff<kD> o = o_in;
+    LaneOff<kC> o64 = o64_in;
+    asm volatile("" : "+v"(o.b), "+v"(o.t0), "+v"(o.t1), "+v"(o.w), "+v"(o64.b), "+v"(o64.w));
+    put_chunk();
+    put_rows(rows_s[(v + 1) & 1]);
+#pragma unroll
+    for (int aa = 0; aa < 2; ++aa)
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+        put4<kD>(L_s, o, (4 * rh + b) * 16, (2 * kq + aa) * 16, pack4f(lam[aa][b]));
+    load_chunk(chunk_at(v + 1));
+    load_rows(chunk_at(v + 2));
+    lds_barrier();  // B2: chunk v, Lam_out, gate rows of v + 1 visible
+
+    // ---- phase A
+    const RecF& rc = rec[v & 3];
+    if (c >= 0) {
+      causal_f<kD>(sl.X, sl.G, sl.DY, rc, PT_s, M_s, qk[v & 1], o, o64, wave, lane);
+      if (wave >= 4 && wave < 6)
+        causal_f<kD>(sl.X, sl.G, sl.DY, rc, PT_s, M_s, qk[v & 1], o, o64, wave + 4, lane);
+      // <Lam_out, D_in> over this wave's region, then
+      // Lam^T <- Gamma Lam^T + X^T (e(lq) dy),  dW0^T += X^T dy
+      float c0p = 0.f;
+#pragma unroll
+      for (int aa = 0; aa < 2; ++aa)
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+          c0p += dot4f(unpack4f(get4<kD>(sl.S, o, (4 * rh + b) * 16, (2 * kq + aa) * 16)),
+                       lam[aa][b]);
+      c0p = wave_sum(c0p);
+      if (lane == 0) part[v & 1].c0[wave] = c0p;
+      const float gam = rc.gam;
+#pragma unroll
+      for (int aa = 0; aa < 2; ++aa)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) lam[aa][b] = lam[aa][b] * gam;
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        __builtin_amdgcn_sched_barrier(0);
+        bf16x8 xf[2];
+#pragma unroll
+        for (int aa = 0; aa < 2; ++aa) xf[aa] = frag_ts<kD>(sl.X, o, kk * 32, (2 * kq + aa) * 16);
+        const f32x4 e0 = *reinterpret_cast<const f32x4*>(&rc.eq[kk * 32 + 8 * g4]);
+        const f32x4 e1 = *reinterpret_cast<const f32x4*>(&rc.eq[kk * 32 + 8 * g4 + 4]);
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const bf16x8 df = frag_ts<kD>(sl.DY, o, kk * 32, (4 * rh + b) * 16);
+          const bf16x8 de = scale8(df, e0, e1);
+#pragma unroll
+          for (int aa = 0; aa < 2; ++aa) {
+            dw[aa][b] = mfma16x16x32(xf[aa], df, dw[aa][b]);
+            lam[aa][b] = mfma16x16x32(xf[aa], de, lam[aa][b]);
+          }
+        }
+      }
+    }
+    if (wave == kGateWave) {
+      const int cn = chunk_at(v + 1);
+      if (cn >= 0)
+        gates_f(rows_s[(v + 1) & 1][0], rows_s[(v + 1) & 1][1], rec[(v + 1) & 3], cv_of(cn), lane);
+    }
+    lds_barrier();  // B3: P^T, M, the Be dots visible
+
+    // ---- phase B: dx^T for k block `wave` and u^T for r block `wave`, all
+    // 64 tokens, in two halves of 32 tokens each
+    const int64_t t0 = c >= 0 ? static_cast<int64_t>(c) * kC : 0;
+    const int cv = cv_of(c);
+    if (c >= 0) {
+      PartH& pw = part[v & 1];
+      const __amdgpu_buffer_rsrc_t rdx = buffer_rsrc(dxp + t0 * kD, cv * kD * 2);
+      const __amdgpu_buffer_rsrc_t rdg = buffer_rsrc(dgp + t0 * kD, cv * kD * 2);
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        float sc[2], eqv[2], e2v[2], nbv[2];
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+          const int i = (2 * hf + b) * 16 + l16;
+          nbv[b] = rc.nb[i];
+          e2v[b] = rc.e2[i];
+          sc[b] = nbv[b] * e2v[b];
+          eqv[b] = rc.eq[i];
+        }
+        {
+          // dx: -eta_i e(l_last - l_i) Lam_out^T g_i + W0^T dy_i + e(lq_i) D_in^T dy_i
+          // + (M X)_i; rr_i = x_i . D_in^T dy_i over these 16 columns
+          f32x4 acc[2], t[2];
+#pragma unroll
+          for (int b = 0; b < 2; ++b) t[b] = zero4();
+#pragma unroll
+          for (int kk = 0; kk < 4; ++kk) {
+            __builtin_amdgcn_sched_barrier(0);
+            const bf16x8 lf = frag_ts<kD>(L_s, o, kk * 32, wave * 16);
+#pragma unroll
+            for (int b = 0; b < 2; ++b)
+              t[b] = mfma16x16x32(lf, frag_s<kD>(sl.G, o, (2 * hf + b) * 16, kk * 32), t[b]);
+          }
+#pragma unroll
+          for (int b = 0; b < 2; ++b) {
+            acc[b] = t[b] * sc[b];
+            t[b] = zero4();
+          }
+#pragma unroll
+          for (int kk = 0; kk < 4; ++kk) {
+            __builtin_amdgcn_sched_barrier(0);
+            const bf16x8 sf = frag_ts<kD>(sl.S, o, kk * 32, wave * 16);
+#pragma unroll
+            for (int b = 0; b < 2; ++b) {
+              const bf16x8 df = frag_s<kD>(sl.DY, o, (2 * hf + b) * 16, kk * 32);
+              t[b] = mfma16x16x32(sf, df, t[b]);
+              acc[b] = mfma16x16x32(wf[kk], df, acc[b]);
+            }
+          }
+#pragma unroll
+          for (int b = 0; b < 2; ++b) {
+            const float rp = sum_rows(
+                dot4f(unpack4f(get4<kD>(sl.X, o, (2 * hf + b) * 16, wave * 16)), t[b]));
+            if (g4 == 0) pw.rr[wave][(2 * hf + b) * 16 + l16] = rp;
+            acc[b] += t[b] * eqv[b];
+          }
+#pragma unroll
+          for (int kk = 0; kk < 2; ++kk) {
+            __builtin_amdgcn_sched_barrier(0);
+            const bf16x8 xf = frag_ts<kD>(sl.X, o, kk * 32, wave * 16);
+#pragma unroll
+            for (int b = 0; b < 2; ++b)
+              acc[b] = mfma16x16x32(xf, frag_s<kC>(M_s, o64, (2 * hf + b) * 16, kk * 32), acc[b]);
+          }
+#pragma unroll
+          for (int b = 0; b < 2; ++b)
+            store8(rdx, static_cast<uint32_t>((((2 * hf + b) * 16 + l16) * kD + wave * 16 + 4 * g4) * 2),
+                   pack4f(acc[b]));
+        }
+        {
+          // u = e(l_last - l_i) Lam_out x_i + sum_u P_ui dy_u (rows `wave`): dg, and
+          // the deta, pp shares over these 16 rows
+          f32x4 ain[2], apd[2];
+#pragma unroll
+          for (int b = 0; b < 2; ++b) {
+            ain[b] = zero4();
+            apd[b] = zero4();
+          }
+#pragma unroll
+          for (int kk = 0; kk < 4; ++kk) {
+            __builtin_amdgcn_sched_barrier(0);
+            const bf16x8 lf = frag_s<kD>(L_s, o, wave * 16, kk * 32);
+#pragma unroll
+            for (int b = 0; b < 2; ++b)
+              ain[b] = mfma16x16x32(lf, frag_s<kD>(sl.X, o, (2 * hf + b) * 16, kk * 32), ain[b]);
+          }
+#pragma unroll
+          for (int kk = 0; kk < 2; ++kk) {
+            __builtin_amdgcn_sched_barrier(0);
+            const bf16x8 tf = frag_ts<kD>(sl.DY, o, kk * 32, wave * 16);
+#pragma unroll
+            for (int b = 0; b < 2; ++b)
+              apd[b] = mfma16x16x32(tf, frag_s<kC>(PT_s, o64, (2 * hf + b) * 16, kk * 32), apd[b]);
+          }
+#pragma unroll
+          for (int b = 0; b < 2; ++b) {
+            const int i = (2 * hf + b) * 16 + l16;
+            const f32x4 u = ain[b] * e2v[b] + apd[b];
+            const f32x4 gv = unpack4f(get4<kD>(sl.G, o, (2 * hf + b) * 16, wave * 16));
+            const float dp = sum_rows(dot4f(gv, u));
+            const float pp = sum_rows(dot4f(gv, ain[b]));
+            store8(rdg, static_cast<uint32_t>((i * kD + wave * 16 + 4 * g4) * 2), pack4f(u * nbv[b]));
+            if (g4 == 0) {
+              pw.de[wave][i] = -dp;
+              pw.pp[wave][i] = pp;
+            }
+          }
+        }
+      }
+    }
+    if (wave == kAlphaWave) {
+      const int cp = chunk_at(v - 1);
+      if (cp >= 0) {
+        // dalpha and deta of the chunk finished one step ago
+        const PartH& pr = part[(v - 1) & 1];
+        const int ir = kC - 1 - lane;
+        float c0 = 0.f, pp = 0.f, de = 0.f, rr_r = 0.f;
+#pragma unroll
+        for (int w = 0; w < kNW; ++w) {
+          c0 += pr.c0[w];
+          pp += pr.pp[w][lane];
+          de += pr.de[w][lane];
+          rr_r += pr.rr[w][ir];
+        }
+        const float da = dalpha_f(rec[(v - 1) & 3], qk[(v - 1) & 1], pp, rr_r, c0, lane);
+        const int64_t tp = static_cast<int64_t>(cp) * kC;
+        store4(buffer_rsrc(dal + tp, cv_of(cp) * 4), static_cast<uint32_t>(lane * 4), da);
+        store4(buffer_rsrc(det + tp, cv_of(cp) * 4), static_cast<uint32_t>(lane * 4), de);
+      }
+    }
+  };
+  for (int v = 0; v <= nloc; ++v) step(v);
+  // dW0 partial of this (segment, sequence-head): dW0[r][k], fp32
+  float* pw = static_cast<float*>(a.part_dW0) + (static_cast<int64_t>(seg) * BH + bh) * kD * kD;
+#pragma unroll
+  for (int aa = 0; aa < 2; ++aa)
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+      *reinterpret_cast<f32x4*>(pw + ((4 * rh + b) * 16 + l16) * kD + (2 * kq + aa) * 16 + 4 * g4) =
+          dw[aa][b];
+}
+
+}  // namespace
+
+hipError_t launch_mfma_bwd_f128(const BwdArgs& a, hipStream_t s) {
+  const int64_t groups = a.B * a.H * a.n_seg;
+  if (groups == 0) return hipSuccess;
+  hipLaunchKernelGGL(bwd_f128, dim3(static_cast<unsigned>(groups)), dim3(kNT), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace gls
