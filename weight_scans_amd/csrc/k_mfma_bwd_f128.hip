@@ -21,13 +21,13 @@
 //   top:     the staged chunk into the slot, the bf16 copy of Lam_out, the
 //            loads of the next chunk (and the gate rows of the one after);
 //   phase A: causal blocks (P^T, M, the Be dots: block w, and 8, 9 on waves
-//            4, 5); every wave its region of Lam and dW0 (<Lam_out, D_in>
+//            2, 3); every wave its region of Lam and dW0 (<Lam_out, D_in>
 //            share, then the update); wave 6 the gates of the next chunk;
-//   phase B: waves 0-3 dx (32 columns each) and the rr shares; waves 4-7 u
-//            (32 rows each): dg, the deta and pp shares; wave 7 dalpha and
-//            deta of the chunk before.
-// Each role walks in its own copy of the loop, so registers are allocated
-// per role.  All loads go to registers (the compiler places the waits); no
+//   phase B: every wave 16 columns of dx (all tokens) with its rr share, and
+//            the 32 x 32 block (rows 32 (w % 4) .., tokens 32 (w / 4) ..) of
+//            u: dg, the deta and pp shares; wave 7 dalpha and deta of the
+//            chunk before.
+// All loads go to registers (the compiler places the waits); no
 // direct-to-LDS loads are involved.
 #include <type_traits>
 
@@ -50,10 +50,10 @@ struct alignas(16) SlotH {
   __bf16 S[kD * kD];   // D_in, swizzled [r][k]
 };
 
-struct alignas(16) PartH {  // per-token shares of one chunk, one per wave
-  float pp[kNW][kC], de[kNW][kC];  // from its 16 rows of u
-  float rr[kNW][kC];               // from its 16 columns of dx
-  float c0[kNW];                   // <Lam_out, D_in> over its region
+struct alignas(16) PartH {  // per-token shares of one chunk
+  float pp[4][kC], de[4][kC];  // over u rows 32 q .. (q = wave % 4)
+  float rr[kNW][kC];           // over dx columns 16 w ..
+  float c0[kNW];               // <Lam_out, D_in> over each wave's region
 };
 
 // 16-byte unit u of a [rows][128] bf16 tile (16 units per row): read from
@@ -197,7 +197,7 @@ void bwd_f128(BwdArgs a) {
   }
   put_rows(rows_s[0]);
   __syncthreads();
-  bf16x8 wf[4];  // W0^T fragments of this wave's dx columns (k block `wave`, K block kk of r)
+  bf16x8 wf[4];  // W0^T fragments of this wave's dx columns (k block `wave`, K block kk)
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) wf[kk] = frag_ts<kD>(L_s, o_in, kk * 32, wave * 16);
   if (wave == kGateWave) gates_f(rows_s[0][0], rows_s[0][1], rec[0], cv_of(chunk_at(0)), lane);
@@ -228,8 +228,8 @@ void bwd_f128(BwdArgs a) {
     const RecF& rc = rec[v & 3];
     if (c >= 0) {
       causal_f<kD>(sl.X, sl.G, sl.DY, rc, PT_s, M_s, qk[v & 1], o, o64, wave, lane);
-      if (wave >= 4 && wave < 6)
-        causal_f<kD>(sl.X, sl.G, sl.DY, rc, PT_s, M_s, qk[v & 1], o, o64, wave + 4, lane);
+      if (wave == 2 || wave == 3)
+        causal_f<kD>(sl.X, sl.G, sl.DY, rc, PT_s, M_s, qk[v & 1], o, o64, wave + 6, lane);
       // <Lam_out, D_in> over this wave's region, then
       // Lam^T <- Gamma Lam^T + X^T (e(lq) dy),  dW0^T += X^T dy
       float c0p = 0.f;
@@ -273,112 +273,128 @@ void bwd_f128(BwdArgs a) {
     }
     lds_barrier();  // B3: P^T, M, the Be dots visible
 
-    // ---- phase B: dx^T for k block `wave` and u^T for r block `wave`, all
-    // 64 tokens, in two halves of 32 tokens each
+    // ---- phase B: the 32 x 32 blocks (k blocks 2 kq + a, token blocks 2 th + b)
+    // of dx^T and (r blocks 2 kq + a, same tokens) of u^T, th = wave / 4
     const int64_t t0 = c >= 0 ? static_cast<int64_t>(c) * kC : 0;
     const int cv = cv_of(c);
     if (c >= 0) {
       PartH& pw = part[v & 1];
-      const __amdgpu_buffer_rsrc_t rdx = buffer_rsrc(dxp + t0 * kD, cv * kD * 2);
-      const __amdgpu_buffer_rsrc_t rdg = buffer_rsrc(dgp + t0 * kD, cv * kD * 2);
+      const int th = rh;
+      float e2v[2], nbv[2];
 #pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        float sc[2], eqv[2], e2v[2], nbv[2];
+      for (int b = 0; b < 2; ++b) {
+        const int i = (2 * th + b) * 16 + l16;
+        nbv[b] = rc.nb[i];
+        e2v[b] = rc.e2[i];
+      }
+      {
+        // dx for columns 16 w .., all tokens:
+        // -eta_i e(l_last - l_i) Lam_out^T g_i + W0^T dy_i + e(lq_i) D_in^T dy_i
+        // + (M X)_i; rr_i = x_i . D_in^T dy_i over these 16 columns
+        const __amdgpu_buffer_rsrc_t rdx = buffer_rsrc(dxp + t0 * kD, cv * kD * 2);
+        f32x4 acc[4], t[4];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) t[b] = zero4();
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+          __builtin_amdgcn_sched_barrier(0);
+          const bf16x8 lf = frag_ts<kD>(L_s, o, kk * 32, wave * 16);
+#pragma unroll
+          for (int b = 0; b < 4; ++b) t[b] = mfma16x16x32(lf, frag_s<kD>(sl.G, o, b * 16, kk * 32), t[b]);
+        }
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const int i = b * 16 + l16;
+          acc[b] = t[b] * (rc.nb[i] * rc.e2[i]);
+          t[b] = zero4();
+        }
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+          __builtin_amdgcn_sched_barrier(0);
+          const bf16x8 sf = frag_ts<kD>(sl.S, o, kk * 32, wave * 16);
+#pragma unroll
+          for (int b = 0; b < 4; ++b) {
+            const bf16x8 df = frag_s<kD>(sl.DY, o, b * 16, kk * 32);
+            t[b] = mfma16x16x32(sf, df, t[b]);
+            acc[b] = mfma16x16x32(wf[kk], df, acc[b]);
+          }
+        }
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const int i = b * 16 + l16;
+          const float rp = sum_rows(dot4f(unpack4f(get4<kD>(sl.X, o, b * 16, wave * 16)), t[b]));
+          if (g4 == 0) pw.rr[wave][i] = rp;
+          acc[b] += t[b] * rc.eq[i];
+        }
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          __builtin_amdgcn_sched_barrier(0);
+          const bf16x8 xf = frag_ts<kD>(sl.X, o, kk * 32, wave * 16);
+#pragma unroll
+          for (int b = 0; b < 4; ++b)
+            acc[b] = mfma16x16x32(xf, frag_s<kC>(M_s, o64, b * 16, kk * 32), acc[b]);
+        }
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+          store8(rdx, static_cast<uint32_t>(((b * 16 + l16) * kD + wave * 16 + 4 * g4) * 2),
+                 pack4f(acc[b]));
+      }
+      {
+        // u = e(l_last - l_i) Lam_out x_i + sum_u P_ui dy_u for rows 32 kq ..: dg,
+        // and the deta, pp shares over these 32 rows
+        const __amdgpu_buffer_rsrc_t rdg = buffer_rsrc(dgp + t0 * kD, cv * kD * 2);
+        f32x4 ain[2][2], apd[2][2];
+#pragma unroll
+        for (int aa = 0; aa < 2; ++aa)
+#pragma unroll
+          for (int b = 0; b < 2; ++b) {
+            ain[aa][b] = zero4();
+            apd[aa][b] = zero4();
+          }
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+          __builtin_amdgcn_sched_barrier(0);
+          bf16x8 lf[2], xf[2];
+#pragma unroll
+          for (int aa = 0; aa < 2; ++aa) lf[aa] = frag_s<kD>(L_s, o, (2 * kq + aa) * 16, kk * 32);
+#pragma unroll
+          for (int b = 0; b < 2; ++b) xf[b] = frag_s<kD>(sl.X, o, (2 * th + b) * 16, kk * 32);
+#pragma unroll
+          for (int aa = 0; aa < 2; ++aa)
+#pragma unroll
+            for (int b = 0; b < 2; ++b) ain[aa][b] = mfma16x16x32(lf[aa], xf[b], ain[aa][b]);
+        }
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          __builtin_amdgcn_sched_barrier(0);
+          bf16x8 tf[2], pf[2];
+#pragma unroll
+          for (int aa = 0; aa < 2; ++aa) tf[aa] = frag_ts<kD>(sl.DY, o, kk * 32, (2 * kq + aa) * 16);
+#pragma unroll
+          for (int b = 0; b < 2; ++b) pf[b] = frag_s<kC>(PT_s, o64, (2 * th + b) * 16, kk * 32);
+#pragma unroll
+          for (int aa = 0; aa < 2; ++aa)
+#pragma unroll
+            for (int b = 0; b < 2; ++b) apd[aa][b] = mfma16x16x32(tf[aa], pf[b], apd[aa][b]);
+        }
 #pragma unroll
         for (int b = 0; b < 2; ++b) {
-          const int i = (2 * hf + b) * 16 + l16;
-          nbv[b] = rc.nb[i];
-          e2v[b] = rc.e2[i];
-          sc[b] = nbv[b] * e2v[b];
-          eqv[b] = rc.eq[i];
-        }
-        {
-          // dx: -eta_i e(l_last - l_i) Lam_out^T g_i + W0^T dy_i + e(lq_i) D_in^T dy_i
-          // + (M X)_i; rr_i = x_i . D_in^T dy_i over these 16 columns
-          f32x4 acc[2], t[2];
+          const int i = (2 * th + b) * 16 + l16;
+          float dp = 0.f, pp = 0.f;
 #pragma unroll
-          for (int b = 0; b < 2; ++b) t[b] = zero4();
-#pragma unroll
-          for (int kk = 0; kk < 4; ++kk) {
-            __builtin_amdgcn_sched_barrier(0);
-            const bf16x8 lf = frag_ts<kD>(L_s, o, kk * 32, wave * 16);
-#pragma unroll
-            for (int b = 0; b < 2; ++b)
-              t[b] = mfma16x16x32(lf, frag_s<kD>(sl.G, o, (2 * hf + b) * 16, kk * 32), t[b]);
+          for (int aa = 0; aa < 2; ++aa) {
+            const f32x4 u = ain[aa][b] * e2v[b] + apd[aa][b];
+            const f32x4 gv = unpack4f(get4<kD>(sl.G, o, (2 * th + b) * 16, (2 * kq + aa) * 16));
+            dp += dot4f(gv, u);
+            pp += dot4f(gv, ain[aa][b]);
+            store8(rdg, static_cast<uint32_t>((i * kD + (2 * kq + aa) * 16 + 4 * g4) * 2),
+                   pack4f(u * nbv[b]));
           }
-#pragma unroll
-          for (int b = 0; b < 2; ++b) {
-            acc[b] = t[b] * sc[b];
-            t[b] = zero4();
-          }
-#pragma unroll
-          for (int kk = 0; kk < 4; ++kk) {
-            __builtin_amdgcn_sched_barrier(0);
-            const bf16x8 sf = frag_ts<kD>(sl.S, o, kk * 32, wave * 16);
-#pragma unroll
-            for (int b = 0; b < 2; ++b) {
-              const bf16x8 df = frag_s<kD>(sl.DY, o, (2 * hf + b) * 16, kk * 32);
-              t[b] = mfma16x16x32(sf, df, t[b]);
-              acc[b] = mfma16x16x32(wf[kk], df, acc[b]);
-            }
-          }
-#pragma unroll
-          for (int b = 0; b < 2; ++b) {
-            const float rp = sum_rows(
-                dot4f(unpack4f(get4<kD>(sl.X, o, (2 * hf + b) * 16, wave * 16)), t[b]));
-            if (g4 == 0) pw.rr[wave][(2 * hf + b) * 16 + l16] = rp;
-            acc[b] += t[b] * eqv[b];
-          }
-#pragma unroll
-          for (int kk = 0; kk < 2; ++kk) {
-            __builtin_amdgcn_sched_barrier(0);
-            const bf16x8 xf = frag_ts<kD>(sl.X, o, kk * 32, wave * 16);
-#pragma unroll
-            for (int b = 0; b < 2; ++b)
-              acc[b] = mfma16x16x32(xf, frag_s<kC>(M_s, o64, (2 * hf + b) * 16, kk * 32), acc[b]);
-          }
-#pragma unroll
-          for (int b = 0; b < 2; ++b)
-            store8(rdx, static_cast<uint32_t>((((2 * hf + b) * 16 + l16) * kD + wave * 16 + 4 * g4) * 2),
-                   pack4f(acc[b]));
-        }
-        {
-          // u = e(l_last - l_i) Lam_out x_i + sum_u P_ui dy_u (rows `wave`): dg, and
-          // the deta, pp shares over these 16 rows
-          f32x4 ain[2], apd[2];
-#pragma unroll
-          for (int b = 0; b < 2; ++b) {
-            ain[b] = zero4();
-            apd[b] = zero4();
-          }
-#pragma unroll
-          for (int kk = 0; kk < 4; ++kk) {
-            __builtin_amdgcn_sched_barrier(0);
-            const bf16x8 lf = frag_s<kD>(L_s, o, wave * 16, kk * 32);
-#pragma unroll
-            for (int b = 0; b < 2; ++b)
-              ain[b] = mfma16x16x32(lf, frag_s<kD>(sl.X, o, (2 * hf + b) * 16, kk * 32), ain[b]);
-          }
-#pragma unroll
-          for (int kk = 0; kk < 2; ++kk) {
-            __builtin_amdgcn_sched_barrier(0);
-            const bf16x8 tf = frag_ts<kD>(sl.DY, o, kk * 32, wave * 16);
-#pragma unroll
-            for (int b = 0; b < 2; ++b)
-              apd[b] = mfma16x16x32(tf, frag_s<kC>(PT_s, o64, (2 * hf + b) * 16, kk * 32), apd[b]);
-          }
-#pragma unroll
-          for (int b = 0; b < 2; ++b) {
-            const int i = (2 * hf + b) * 16 + l16;
-            const f32x4 u = ain[b] * e2v[b] + apd[b];
-            const f32x4 gv = unpack4f(get4<kD>(sl.G, o, (2 * hf + b) * 16, wave * 16));
-            const float dp = sum_rows(dot4f(gv, u));
-            const float pp = sum_rows(dot4f(gv, ain[b]));
-            store8(rdg, static_cast<uint32_t>((i * kD + wave * 16 + 4 * g4) * 2), pack4f(u * nbv[b]));
-            if (g4 == 0) {
-              pw.de[wave][i] = -dp;
-              pw.pp[wave][i] = pp;
-            }
+          dp = sum_rows(dp);
+          pp = sum_rows(pp);
+          if (g4 == 0) {
+            pw.de[kq][i] = -dp;
+            pw.pp[kq][i] = pp;
           }
         }
       }
@@ -393,9 +409,12 @@ void bwd_f128(BwdArgs a) {
 #pragma unroll
         for (int w = 0; w < kNW; ++w) {
           c0 += pr.c0[w];
+          rr_r += pr.rr[w][ir];
+        }
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
           pp += pr.pp[w][lane];
           de += pr.de[w][lane];
-          rr_r += pr.rr[w][ir];
         }
         const float da = dalpha_f(rec[(v - 1) & 3], qk[(v - 1) & 1], pp, rr_r, c0, lane);
         const int64_t tp = static_cast<int64_t>(cp) * kC;
