@@ -20,13 +20,14 @@
 // r columns 64 (w / 4) ..) of Lam and dW0.  Three barriers per step:
 //   top:     the staged chunk into the slot, the bf16 copy of Lam_out, the
 //            loads of the next chunk (and the gate rows of the one after);
+//            wave 1 the gates of the next chunk, wave 2 dalpha and deta of
+//            the chunk before (its shares are complete at the top);
 //   phase A: causal blocks (P^T, M, the Be dots: block w, and 8, 9 on waves
 //            2, 3); every wave its region of Lam and dW0 (<Lam_out, D_in>
-//            share, then the update); wave 6 the gates of the next chunk;
+//            share, then the update);
 //   phase B: every wave 16 columns of dx (all tokens) with its rr share, and
 //            the 32 x 32 block (rows 32 (w % 4) .., tokens 32 (w / 4) ..) of
-//            u: dg, the deta and pp shares; wave 7 dalpha and deta of the
-//            chunk before.
+//            u: dg, the deta and pp shares.
 // All loads go to registers (the compiler places the waits); no
 // direct-to-LDS loads are involved.
 #include <type_traits>
@@ -40,8 +41,8 @@ constexpr int kD = 128;        // d_in = d_out
 constexpr int kC = kFC;        // tokens per chunk
 constexpr int kNW = 8;         // waves per work-group
 constexpr int kNT = 64 * kNW;  // threads
-constexpr int kGateWave = 6;   // gates of the next chunk
-constexpr int kAlphaWave = 7;  // dalpha and deta one chunk behind
+constexpr int kRowWave = 1;    // eta / alpha rows and the gates of the next chunk
+constexpr int kAlphaWave = 2;  // dalpha and deta one chunk behind
 
 struct alignas(16) SlotH {
   __bf16 X[kC * kD];   // x, swizzled [token][k]
@@ -113,7 +114,7 @@ void bwd_f128(BwdArgs a) {
   };
 
   // ---- staged loads: x, g, dy units tid and tid + 512; D_in units tid +
-  // 512 j (j < 4); the eta / alpha rows (wave 0, lanes 0-31)
+  // 512 j (j < 4); the eta / alpha rows (wave 1, lanes 0-31)
   u32x4 sx[2], sg[2], sdy[2], ss[4], sq;
   const auto load_chunk = [&](int c) {
     const bool in = c >= 0;
@@ -135,7 +136,7 @@ void bwd_f128(BwdArgs a) {
     for (int j = 0; j < 4; ++j) ss[j] = load16(rs, static_cast<uint32_t>((tid + kNT * j) * 16));
   };
   const auto load_rows = [&](int c) {
-    if (wave == 0) {
+    if (wave == kRowWave) {
       const int64_t t0 = c >= 0 ? static_cast<int64_t>(c) * kC : 0;
       const int cv = cv_of(c);
       const uint32_t off = static_cast<uint32_t>((lane & 15) * 16);
@@ -158,7 +159,7 @@ void bwd_f128(BwdArgs a) {
       *reinterpret_cast<u32x4*>(b + offsetof(SlotH, S) + unit_lds(tid + kNT * j)) = ss[j];
   };
   const auto put_rows = [&](float (*rw)[kC]) {
-    if (wave == 0 && lane < 32)
+    if (wave == kRowWave && lane < 32)
       *reinterpret_cast<u32x4*>(&rw[lane >> 4][4 * (lane & 15)]) = sq;
   };
 
@@ -200,7 +201,7 @@ void bwd_f128(BwdArgs a) {
   bf16x8 wf[4];  // W0^T fragments of this wave's dx columns (k block `wave`, K block kk)
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) wf[kk] = frag_ts<kD>(L_s, o_in, kk * 32, wave * 16);
-  if (wave == kGateWave) gates_f(rows_s[0][0], rows_s[0][1], rec[0], cv_of(chunk_at(0)), lane);
+  if (wave == kRowWave) gates_f(rows_s[0][0], rows_s[0][1], rec[0], cv_of(chunk_at(0)), lane);
   for (int idx = tid; idx < kC * kC / 8; idx += kNT)
     reinterpret_cast<uint4*>(PT_s)[idx] = make_uint4(0, 0, 0, 0);
   load_rows(chunk_at(1));
@@ -222,6 +223,36 @@ void bwd_f128(BwdArgs a) {
         put4<kD>(L_s, o, (4 * rh + b) * 16, (2 * kq + aa) * 16, pack4f(lam[aa][b]));
     load_chunk(chunk_at(v + 1));
     load_rows(chunk_at(v + 2));
+    if (wave == kRowWave) {
+      // gates of the next chunk from the rows this wave has just written (one
+      // wave's LDS accesses land in order)
+      const int cn = chunk_at(v + 1);
+      if (cn >= 0)
+        gates_f(rows_s[(v + 1) & 1][0], rows_s[(v + 1) & 1][1], rec[(v + 1) & 3], cv_of(cn), lane);
+    }
+    if (wave == kAlphaWave) {
+      const int cp = chunk_at(v - 1);
+      if (cp >= 0) {
+        // dalpha and deta of the chunk finished one step ago
+        const PartH& pr = part[(v - 1) & 1];
+        const int ir = kC - 1 - lane;
+        float c0 = 0.f, pp = 0.f, de = 0.f, rr_r = 0.f;
+#pragma unroll
+        for (int w = 0; w < kNW; ++w) {
+          c0 += pr.c0[w];
+          rr_r += pr.rr[w][ir];
+        }
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          pp += pr.pp[w][lane];
+          de += pr.de[w][lane];
+        }
+        const float da = dalpha_f(rec[(v - 1) & 3], qk[(v - 1) & 1], pp, rr_r, c0, lane);
+        const int64_t tp = static_cast<int64_t>(cp) * kC;
+        store4(buffer_rsrc(dal + tp, cv_of(cp) * 4), static_cast<uint32_t>(lane * 4), da);
+        store4(buffer_rsrc(det + tp, cv_of(cp) * 4), static_cast<uint32_t>(lane * 4), de);
+      }
+    }
     lds_barrier();  // B2: chunk v, Lam_out, gate rows of v + 1 visible
 
     // ---- phase A
@@ -265,11 +296,6 @@ void bwd_f128(BwdArgs a) {
           }
         }
       }
-    }
-    if (wave == kGateWave) {
-      const int cn = chunk_at(v + 1);
-      if (cn >= 0)
-        gates_f(rows_s[(v + 1) & 1][0], rows_s[(v + 1) & 1][1], rec[(v + 1) & 3], cv_of(cn), lane);
     }
     lds_barrier();  // B3: P^T, M, the Be dots visible
 
@@ -397,29 +423,6 @@ void bwd_f128(BwdArgs a) {
             pw.pp[kq][i] = pp;
           }
         }
-      }
-    }
-    if (wave == kAlphaWave) {
-      const int cp = chunk_at(v - 1);
-      if (cp >= 0) {
-        // dalpha and deta of the chunk finished one step ago
-        const PartH& pr = part[(v - 1) & 1];
-        const int ir = kC - 1 - lane;
-        float c0 = 0.f, pp = 0.f, de = 0.f, rr_r = 0.f;
-#pragma unroll
-        for (int w = 0; w < kNW; ++w) {
-          c0 += pr.c0[w];
-          rr_r += pr.rr[w][ir];
-        }
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          pp += pr.pp[w][lane];
-          de += pr.de[w][lane];
-        }
-        const float da = dalpha_f(rec[(v - 1) & 3], qk[(v - 1) & 1], pp, rr_r, c0, lane);
-        const int64_t tp = static_cast<int64_t>(cp) * kC;
-        store4(buffer_rsrc(dal + tp, cv_of(cp) * 4), static_cast<uint32_t>(lane * 4), da);
-        store4(buffer_rsrc(det + tp, cv_of(cp) * 4), static_cast<uint32_t>(lane * 4), de);
       }
     }
   };
