@@ -89,7 +89,7 @@ gl_status_t make_plan(const gl_scan_desc_t* d, Plan* p) {
   if (mfma_shape && (d->chunk == 0 || d->chunk == gls::kMfmaChunk)) {
     p->mfma = true;
     p->chunk = gls::kMfmaChunk;
-    p->n_tiles = gls::mfma_bwd_tiles(static_cast<int>(d->d_in));
+    p->n_tiles = 1;  // the fused backward writes deta / dalpha itself (no tile partials)
     p->name = d->d_in == 64 ? "mfma-bf16-d64" : "mfma-bf16-d128";
     p->state_elem = 2;  // bf16 chunk-start states
   } else {
@@ -127,8 +127,8 @@ gl_status_t make_plan(const gl_scan_desc_t* d, Plan* p) {
   p->n_ckpt = p->n_chunks;
   p->saved_bytes = round_up(BH * p->n_ckpt * dd * p->state_elem);
   p->part_bytes = round_up(static_cast<size_t>(p->n_tiles) * BH * d->T * p->comp);
-  p->fused = p->mfma && p->n_chunks > 0;
-  if (p->fused) {
+  p->fused = p->mfma;
+  if (p->fused && p->n_chunks > 0) {
     int nb = 1;
     if (d->segments > 0) {
       nb = static_cast<int>(d->segments);
@@ -143,8 +143,8 @@ gl_status_t make_plan(const gl_scan_desc_t* d, Plan* p) {
       p->bwd_seg_state_bytes = round_up(BH * p->bwd_nseg * dd * sizeof(float));
       p->bwd_seg_bytes = p->bwd_seg_state_bytes + round_up(BH * p->bwd_nseg * sizeof(float));
     }
-    p->part_bytes = 0;
   }
+  if (p->fused) p->part_bytes = 0;
   p->dw_groups = p->fused ? p->bwd_nseg : p->n_seg;
   p->dw_bytes = round_up(BH * dd * p->comp * p->dw_groups);
   return GL_SUCCESS;
@@ -299,7 +299,7 @@ gl_status_t gl_scan_bwd(const gl_scan_desc_t* desc, const void* x, const void* g
   b.seg_chunks = p.seg_chunks; b.n_seg = p.n_seg;
   if (!p.mfma) {
     st = hip_status(gls::launch_generic_bwd(p.io, b, s), "backward launch");
-  } else if (p.fused) {
+  } else {
     // one work-group per (segment, sequence-head) walks its chunks from the
     // right; with segments, an adjoint-only pass gives each segment's own
     // adjoint, from which every work-group composes the one entering it
@@ -321,27 +321,6 @@ gl_status_t gl_scan_bwd(const gl_scan_desc_t* desc, const void* x, const void* g
     if (st == GL_SUCCESS)
       st = hip_status(b.d_in == 64 ? gls::launch_mfma_bwd_f64(bf, s) : gls::launch_mfma_bwd_f128(bf, s),
                       "fused backward");
-  } else if (p.n_seg <= 1) {
-    st = hip_status(gls::launch_mfma_bwd(b, s), "backward launch");
-  } else {
-    // segments: adjoint-only pass per segment from a zero start at its right
-    // end, the exclusive affine scan over segments from the right, then the
-    // full pass per segment from its incoming adjoint
-    float* seg = reinterpret_cast<float*>(seg_ws);
-    float* lg = reinterpret_cast<float*>(seg_ws + p.seg_state_bytes);
-    gls::BwdArgs b1 = b;
-    b1.seg_out = seg;
-    b1.seg_lg = lg;
-    st = hip_status(gls::launch_mfma_bwd_lam(b1, s), "backward segment pass");
-    if (st == GL_SUCCESS)
-      st = hip_status(gls::launch_seg_combine(seg, lg, b.B * b.H, p.n_seg, b.d_in * b.d_out, true,
-                                              s),
-                      "segment combine");
-    if (st == GL_SUCCESS) {
-      gls::BwdArgs b3 = b;
-      b3.seg_lam = seg;
-      st = hip_status(gls::launch_mfma_bwd(b3, s), "backward launch");
-    }
   }
   if (st != GL_SUCCESS) return st;
 

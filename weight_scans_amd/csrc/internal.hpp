@@ -102,9 +102,6 @@ hipError_t launch_finalize(int io, const FinArgs& a, hipStream_t s);
 // Matrix-core kernels: bf16 io, d_in == d_out in {64, 128}, chunk 64.
 constexpr int kMfmaChunk = 64;
 hipError_t launch_mfma_fwd(const FwdArgs& a, hipStream_t s);
-hipError_t launch_mfma_bwd(const BwdArgs& a, hipStream_t s);
-hipError_t launch_mfma_bwd_a(const BwdArgs& a, hipStream_t s);  // row tiles: dg, deta, dW0
-hipError_t launch_mfma_bwd_b(const BwdArgs& a, hipStream_t s);  // column tiles: dx, dalpha
 hipError_t launch_mfma_bwd_lam(const BwdArgs& a, hipStream_t s);  // adjoint-only segment pass
 hipError_t launch_mfma_bwd_f64(const BwdArgs& a, hipStream_t s);   // fused reverse scan, d = 64
 hipError_t launch_mfma_bwd_f128(const BwdArgs& a, hipStream_t s);  // fused reverse scan, d = 128
@@ -112,6 +109,5 @@ hipError_t launch_mfma_bwd_f128(const BwdArgs& a, hipStream_t s);  // fused reve
 // entering segment s (in segment order, or from the right end if reverse).
 hipError_t launch_seg_combine(float* buf, const float* lg, int64_t BH, int n_seg, int dd,
                               bool reverse, hipStream_t s);
-int mfma_bwd_tiles(int d);
 
 }  // namespace gls
