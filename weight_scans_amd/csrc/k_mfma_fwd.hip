@@ -209,7 +209,7 @@ __global__ __launch_bounds__(kNT) void fwd_mfma(FwdArgs a) {
   constexpr int NTILE = D / kTN;
   constexpr int NS = D / 64;  // 16x16 state blocks per state wave
   constexpr int P = kLoadOps<D>;
-  constexpr int S = HAS_ST ? NS : 0;  // stores per state wave per chunk
+  constexpr int S = HAS_ST ? 1 : 0;  // stores per state wave per chunk
   // Each ring slot is a separate LDS object, and every reference to one is
   // static (the chunk loop is unrolled by kRing), so the compiler can tell a
   // slot being read from the slots still being filled and adds no waits.
@@ -290,17 +290,18 @@ __global__ __launch_bounds__(kNT) void fwd_mfma(FwdArgs a) {
   // per-lane byte offsets of the stores (loop invariant; the buffer base
   // moves per chunk and its byte count drops rows past the sequence end)
   const uint32_t oy = static_cast<uint32_t>(((tb * 16 + l16) * D + r0 + rbw * 16 + 4 * g4) * 2);
-  uint32_t os[NS];
-#pragma unroll
-  for (int s = 0; s < NS; ++s) {
-    const int cb = tb + 4 * s;
-    os[s] = static_cast<uint32_t>(((r0 + rbw * 16 + l16) * D + cb * 16 + 4 * g4) * 2);
-  }
   const __amdgpu_buffer_rsrc_t r_none = buffer_rsrc(a.x, 0);
   // a state-wave thread's 4 elements of the scaled g tile: row t/8, columns 4 (t%8)..
   const int gt_id = tid & 511;
   const int gs_row = gt_id >> 3;
   const uint32_t gs_off = static_cast<uint32_t>(sidx<kTN>(gs_row, 4 * (gt_id & 7)) * 2);
+  // chunk-start state: state-wave thread t stores D / 16 consecutive elements
+  // (row t / 16, columns (D / 16)(t % 16) ..) of the tile's bf16 copy in LDS,
+  // so every store instruction writes whole rows
+  constexpr int kStEl = D / 16;
+  const int st_row = gt_id >> 4, st_col = kStEl * (gt_id & 15);
+  const uint32_t st_l = static_cast<uint32_t>(sidx<D>(st_row, st_col) * 2);
+  const uint32_t st_g = static_cast<uint32_t>(((r0 + st_row) * D + st_col) * 2);
   if (role == 1) {
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
@@ -317,7 +318,7 @@ __global__ __launch_bounds__(kNT) void fwd_mfma(FwdArgs a) {
     for (int k = 0; k < kRing - 1; ++k) {
       issue_chunk<D>(*rs[k], od, x, g, eta, alpha, T, c_beg + k, c_end, r0, w8);
 #pragma unroll
-      for (int s = 0; s < S; ++s) store8(r_none, os[s] + 64 * k, make_uint2(0, 0));  // not merged
+      for (int s = 0; s < S; ++s) store8(r_none, 64 * k, make_uint2(0, 0));  // not merged
     }
     // chunks 0 and 1 done: after chunk 1 come two more chunk loads and three store groups
     wait_vm<2 * P + 3 * S>();
@@ -354,16 +355,15 @@ __global__ __launch_bounds__(kNT) void fwd_mfma(FwdArgs a) {
     if constexpr (R == 1) {
       issue_chunk<D>(dst, od, x, g, eta, alpha, T, c + kRing - 1, c_end, r0, w8);
       if (HAS_ST) {
-        // chunk-start state of this wave's blocks (natural layout, bf16)
+        // chunk-start state (natural layout, bf16): the copy in LDS that the
+        // y waves read in this step, whole rows per store instruction
         const __amdgpu_buffer_rsrc_t r_st =
             buffer_rsrc(st + static_cast<int64_t>(c) * D * D, D * D * 2);
-#pragma unroll
-        for (int s = 0; s < NS; ++s) {
-          uint2 v;
-          v.x = pack2(sacc[s][0], sacc[s][1]);
-          v.y = pack2(sacc[s][2], sacc[s][3]);
-          store8(r_st, os[s], v);
-        }
+        const char* sp = reinterpret_cast<const char*>(S_s[vl & 1]) + st_l;
+        if constexpr (D == 128)
+          store16(r_st, st_g, *reinterpret_cast<const uint4*>(sp));
+        else
+          store8(r_st, st_g, *reinterpret_cast<const uint2*>(sp));
       }
       if (w8 == kPrepWave) lsum += prep_gates<D>(nx2, cv_of(c + 2), lane);
       scale_g<D>(nx1, GS_s[(vl + 1) & 1], gs_off, gs_row);

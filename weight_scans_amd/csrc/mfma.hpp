@@ -164,6 +164,13 @@ __device__ __forceinline__ void store8(__amdgpu_buffer_rsrc_t r, uint32_t voff, 
   __builtin_amdgcn_raw_buffer_store_b64(d, r, voff, 0, 0);
 }
 
+// 16-byte buffer store (same dropping rule).
+__device__ __forceinline__ void store16(__amdgpu_buffer_rsrc_t r, uint32_t voff, const uint4& v) {
+  typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+  const u32x4_t d = {v.x, v.y, v.z, v.w};
+  __builtin_amdgcn_raw_buffer_store_b128(d, r, voff, 0, 0);
+}
+
 __device__ __forceinline__ void store4(__amdgpu_buffer_rsrc_t r, uint32_t voff, float v) {
   __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, v), r, voff, 0, 0);
 }
