@@ -20,11 +20,11 @@
 // r columns 64 (w / 4) ..) of Lam and dW0.  Three barriers per step:
 //   top:     the staged chunk into the slot, the bf16 copy of Lam_out, the
 //            loads of the next chunk (and the gate rows of the one after);
-//            wave 1 the gates of the next chunk, wave 2 dalpha and deta of
-//            the chunk before (its shares are complete at the top);
+//            wave 2 dalpha and deta of the chunk before (its shares are
+//            complete at the top);
 //   phase A: causal blocks (P^T, M, the Be dots: block w, and 8, 9 on waves
 //            2, 3); every wave its region of Lam and dW0 (<Lam_out, D_in>
-//            share, then the update);
+//            share, then the update); wave 0 the gates of the next chunk;
 //   phase B: every wave 16 columns of dx (all tokens) with its rr share, and
 //            the 32 x 32 block (rows 32 (w % 4) .., tokens 32 (w / 4) ..) of
 //            u: dg, the deta and pp shares.
@@ -41,7 +41,8 @@ constexpr int kD = 128;        // d_in = d_out
 constexpr int kC = kFC;        // tokens per chunk
 constexpr int kNW = 8;         // waves per work-group
 constexpr int kNT = 64 * kNW;  // threads
-constexpr int kRowWave = 1;    // eta / alpha rows and the gates of the next chunk
+constexpr int kRowWave = 1;    // eta / alpha rows of the chunk after next
+constexpr int kGateWave = 0;   // gates of the next chunk (phase A)
 constexpr int kAlphaWave = 2;  // dalpha and deta one chunk behind
 
 struct alignas(16) SlotH {
@@ -115,7 +116,7 @@ void bwd_f128(BwdArgs a) {
 
   // ---- staged loads: x, g, dy units tid and tid + 512; D_in units tid +
   // 512 j (j < 4); the eta / alpha rows (wave 1, lanes 0-31)
-  u32x4 sx[2], sg[2], sdy[2], ss[4], sq;
+  u32x4 sx[2], sg[2], sdy[2], ss[4], sqe, sqa;
   const auto load_chunk = [&](int c) {
     const bool in = c >= 0;
     const int64_t t0 = in ? static_cast<int64_t>(c) * kC : 0;
@@ -140,9 +141,9 @@ void bwd_f128(BwdArgs a) {
       const int64_t t0 = c >= 0 ? static_cast<int64_t>(c) * kC : 0;
       const int cv = cv_of(c);
       const uint32_t off = static_cast<uint32_t>((lane & 15) * 16);
-      const u32x4 qe = load16(buffer_rsrc(eta + t0, cv * 4), off);
-      const u32x4 qa = load16(buffer_rsrc(alpha + t0, cv * 4), off);
-      sq = lane < 16 ? qe : qa;
+      // (selected only when written out: a select here would wait for the loads)
+      sqe = load16(buffer_rsrc(eta + t0, cv * 4), off);
+      sqa = load16(buffer_rsrc(alpha + t0, cv * 4), off);
     }
   };
   const auto put_chunk = [&]() {
@@ -160,7 +161,7 @@ void bwd_f128(BwdArgs a) {
   };
   const auto put_rows = [&](float (*rw)[kC]) {
     if (wave == kRowWave && lane < 32)
-      *reinterpret_cast<u32x4*>(&rw[lane >> 4][4 * (lane & 15)]) = sq;
+      *reinterpret_cast<u32x4*>(&rw[lane >> 4][4 * (lane & 15)]) = lane < 16 ? sqe : sqa;
   };
 
   // ---- set-up: first chunk and the gate rows of the first chunk in flight;
@@ -201,7 +202,7 @@ void bwd_f128(BwdArgs a) {
   bf16x8 wf[4];  // W0^T fragments of this wave's dx columns (k block `wave`, K block kk)
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) wf[kk] = frag_ts<kD>(L_s, o_in, kk * 32, wave * 16);
-  if (wave == kRowWave) gates_f(rows_s[0][0], rows_s[0][1], rec[0], cv_of(chunk_at(0)), lane);
+  if (wave == kGateWave) gates_f(rows_s[0][0], rows_s[0][1], rec[0], cv_of(chunk_at(0)), lane);
   for (int idx = tid; idx < kC * kC / 8; idx += kNT)
     reinterpret_cast<uint4*>(PT_s)[idx] = make_uint4(0, 0, 0, 0);
   load_rows(chunk_at(1));
@@ -223,13 +224,6 @@ void bwd_f128(BwdArgs a) {
         put4<kD>(L_s, o, (4 * rh + b) * 16, (2 * kq + aa) * 16, pack4f(lam[aa][b]));
     load_chunk(chunk_at(v + 1));
     load_rows(chunk_at(v + 2));
-    if (wave == kRowWave) {
-      // gates of the next chunk from the rows this wave has just written (one
-      // wave's LDS accesses land in order)
-      const int cn = chunk_at(v + 1);
-      if (cn >= 0)
-        gates_f(rows_s[(v + 1) & 1][0], rows_s[(v + 1) & 1][1], rec[(v + 1) & 3], cv_of(cn), lane);
-    }
     if (wave == kAlphaWave) {
       const int cp = chunk_at(v - 1);
       if (cp >= 0) {
@@ -296,6 +290,12 @@ void bwd_f128(BwdArgs a) {
           }
         }
       }
+    }
+    if (wave == kGateWave) {
+      // gates of the next chunk (its rows were written before B2)
+      const int cn = chunk_at(v + 1);
+      if (cn >= 0)
+        gates_f(rows_s[(v + 1) & 1][0], rows_s[(v + 1) & 1][1], rec[(v + 1) & 3], cv_of(cn), lane);
     }
     lds_barrier();  // B3: P^T, M, the Be dots visible
 
