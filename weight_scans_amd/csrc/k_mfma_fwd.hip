@@ -17,12 +17,14 @@
 // Pipeline (one work-group barrier per chunk): chunk tiles are copied
 // HBM -> LDS by direct buffer loads into a ring of kRing slots; while chunk c
 // is finished (y and the state update), the scores of chunk c + 1 are formed
-// and one wave derives the gates of chunk c + 2, and the loads of chunks
+// and the gates of chunk c + 2 derived, and the loads of chunks
 // c + 3 and c + 4 are in flight.  Sixteen waves (four per SIMD) in two roles:
 // y waves 0-7 own the 16 x 16 output block (token block w/2, row block w%2)
 // of y and the score blocks (w, and 8 + w for w < 2); state waves 8-15 own
 // D/64 16 x 16 blocks of the fp32 state, issue every load (and wait for
-// them), scale the g tile and derive the gates.  Each role runs its own copy
+// them), store the chunk-start states, scale the g tile and (one of them)
+// derive the gates.  In the state-only instance the idle y waves 2 and 3
+// derive the gates instead, one half each.  Each role runs its own copy
 // of the chunk loop, so registers are allocated per role.  All LDS tiles are
 // XOR-swizzled (mfma.hpp) so that fragment reads are free of bank conflicts.
 //
@@ -54,7 +56,10 @@ constexpr int kTN = 32;        // rows of the adaptation per work-group
 constexpr int kNW = 16;        // waves per work-group: 8 y waves, 8 state (loader) waves
 constexpr int kNT = 64 * kNW;  // threads
 constexpr int kRing = 5;       // chunk slots: 3 in use, 2 in flight
-constexpr int kPrepWave = 2;   // the state wave (index among them) that derives the gates
+// the gates: with y, state wave kPrepWave alone; without y (the state-only
+// instance, where the y waves are otherwise idle), y waves kPrepWave and
+// kPrepWave + 1, one half each
+constexpr int kPrepWave = 2;
 
 // Per-token factors of a chunk derived from the gates (i = token, b = 16-token
 // block of i, m_b = l_{16 b - 1} with m_0 = 0):
@@ -135,25 +140,49 @@ __device__ __forceinline__ void issue_chunk(Slot<D>& sl, const DmaOff<D>& o, con
   dma16(r4, o.gq, reinterpret_cast<char*>(&sl) + lds_off);
 }
 
-// Gates of a chunk, lane = token (one wave); returns l_last.
-template <int D>
+// Gates of a chunk, lane = token: PART 0 the per-token decays and Gamma
+// (returns l_last), PART 1 the rank-one factors of the off-diagonal score
+// blocks, PART 2 both (one wave).  Two waves can each take one part, each
+// deriving the log2 cumsum itself.
+template <int D, int PART>
 __device__ __forceinline__ float prep_gates(Slot<D>& sl, int cv, int lane) {
-  const float et = lane < cv ? sl.f.eta[lane] : 0.f;
   const ChunkGates gt = chunk_gates(lane < cv ? sl.f.alpha[lane] : 1.f, lane);
-  const float m1 = readlane_f(gt.l, 15), m2 = readlane_f(gt.l, 31), m3 = readlane_f(gt.l, 47);
-  const int b = lane >> 4;
-  const float mb = b == 0 ? 0.f : b == 1 ? m1 : b == 2 ? m2 : m3;
-  sl.lq[lane] = gt.lq;
-  sl.li[lane] = gt.l;
-  sl.nb[lane] = -et;
-  sl.bk[lane] = -et * fexp2(gt.llast - gt.l);
-  sl.f.eq[lane] = fexp2(gt.lq);
-  sl.f.R[lane] = fexp2(gt.lq - mb);
-  sl.f.C1[lane] = -et * fexp2(fminf(m1 - gt.l, 0.f));
-  sl.f.C2[lane] = -et * fexp2(fminf(m2 - gt.l, 0.f));
-  sl.f.C3[lane] = -et * fexp2(fminf(m3 - gt.l, 0.f));
-  if (lane == 0) sl.gam[0] = fexp2(gt.llast);
-  return gt.llast;
+  if constexpr (PART == 2) {
+    const float et = lane < cv ? sl.f.eta[lane] : 0.f;
+    const float m1 = readlane_f(gt.l, 15), m2 = readlane_f(gt.l, 31), m3 = readlane_f(gt.l, 47);
+    const int b = lane >> 4;
+    const float mb = b == 0 ? 0.f : b == 1 ? m1 : b == 2 ? m2 : m3;
+    sl.lq[lane] = gt.lq;
+    sl.li[lane] = gt.l;
+    sl.nb[lane] = -et;
+    sl.bk[lane] = -et * fexp2(gt.llast - gt.l);
+    sl.f.eq[lane] = fexp2(gt.lq);
+    sl.f.R[lane] = fexp2(gt.lq - mb);
+    sl.f.C1[lane] = -et * fexp2(fminf(m1 - gt.l, 0.f));
+    sl.f.C2[lane] = -et * fexp2(fminf(m2 - gt.l, 0.f));
+    sl.f.C3[lane] = -et * fexp2(fminf(m3 - gt.l, 0.f));
+    if (lane == 0) sl.gam[0] = fexp2(gt.llast);
+    return gt.llast;
+  } else if constexpr (PART == 0) {
+    const float et = lane < cv ? sl.f.eta[lane] : 0.f;
+    sl.lq[lane] = gt.lq;
+    sl.li[lane] = gt.l;
+    sl.nb[lane] = -et;
+    sl.bk[lane] = -et * fexp2(gt.llast - gt.l);
+    sl.f.eq[lane] = fexp2(gt.lq);
+    if (lane == 0) sl.gam[0] = fexp2(gt.llast);
+    return gt.llast;
+  } else {
+    const float et = lane < cv ? sl.f.eta[lane] : 0.f;
+    const float m1 = readlane_f(gt.l, 15), m2 = readlane_f(gt.l, 31), m3 = readlane_f(gt.l, 47);
+    const int b = lane >> 4;
+    const float mb = b == 0 ? 0.f : b == 1 ? m1 : b == 2 ? m2 : m3;
+    sl.f.R[lane] = fexp2(gt.lq - mb);
+    sl.f.C1[lane] = -et * fexp2(fminf(m1 - gt.l, 0.f));
+    sl.f.C2[lane] = -et * fexp2(fminf(m2 - gt.l, 0.f));
+    sl.f.C3[lane] = -et * fexp2(fminf(m3 - gt.l, 0.f));
+    return 0.f;
+  }
 }
 
 // Block b (0..9, row-major over the causal triangle of 16 x 16 blocks) of the
@@ -325,9 +354,17 @@ __global__ __launch_bounds__(kNT) void fwd_mfma(FwdArgs a) {
   }
   lds_barrier();
   float lsum = 0.f;  // sum of l_last over the segment's chunks (prep wave)
-  if (role == 1 && w8 == kPrepWave) {
-    lsum += prep_gates<D>(*rs[0], cv_of(c_beg), lane);
-    lsum += prep_gates<D>(*rs[1], cv_of(c_beg + 1), lane);
+  if (HAS_Y && role == 1 && w8 == kPrepWave) {
+    lsum += prep_gates<D, 2>(*rs[0], cv_of(c_beg), lane);
+    lsum += prep_gates<D, 2>(*rs[1], cv_of(c_beg + 1), lane);
+  }
+  if (!HAS_Y && role == 0 && w8 == kPrepWave) {
+    lsum += prep_gates<D, 0>(*rs[0], cv_of(c_beg), lane);
+    lsum += prep_gates<D, 0>(*rs[1], cv_of(c_beg + 1), lane);
+  }
+  if (!HAS_Y && role == 0 && w8 == kPrepWave + 1) {
+    prep_gates<D, 1>(*rs[0], cv_of(c_beg), lane);
+    prep_gates<D, 1>(*rs[1], cv_of(c_beg + 1), lane);
   }
   lds_barrier();
   if (role == 1) scale_g<D>(*rs[0], GS_s[0], gs_off, gs_row);
@@ -365,7 +402,7 @@ __global__ __launch_bounds__(kNT) void fwd_mfma(FwdArgs a) {
         else
           store8(r_st, st_g, *reinterpret_cast<const uint2*>(sp));
       }
-      if (w8 == kPrepWave) lsum += prep_gates<D>(nx2, cv_of(c + 2), lane);
+      if (HAS_Y && w8 == kPrepWave) lsum += prep_gates<D, 2>(nx2, cv_of(c + 2), lane);
       scale_g<D>(nx1, GS_s[(vl + 1) & 1], gs_off, gs_row);
       // state update, transposed: D^T[c][r] = Gamma D^T + sum_j x_j[c] (bk_j g_j[r]),
       // into the other state buffer (the current one may still be read)
@@ -387,9 +424,18 @@ __global__ __launch_bounds__(kNT) void fwd_mfma(FwdArgs a) {
         pk.y = pack2(sacc[s][2], sacc[s][3]);
         put4<D>(S_out, oX, rbw * 16, cb * 16, pk);
       }
-    } else if (HAS_Y) {
-      score_block<D>(nx1, AT_s[(vl + 1) & 1], oX, oA, w8, lane);
-      if (w8 < 2) score_block<D>(nx1, AT_s[(vl + 1) & 1], oX, oA, w8 + 8, lane);
+    } else {
+      if (HAS_Y) {
+        score_block<D>(nx1, AT_s[(vl + 1) & 1], oX, oA, w8, lane);
+        if (w8 < 2) score_block<D>(nx1, AT_s[(vl + 1) & 1], oX, oA, w8 + 8, lane);
+      }
+      // gates of chunk c + 2 (loaded: the state waves waited for it before
+      // the barrier), two halves on two waves
+      if (!HAS_Y) {
+        if (w8 == kPrepWave) lsum += prep_gates<D, 0>(nx2, cv_of(c + 2), lane);
+        if (w8 == kPrepWave + 1) prep_gates<D, 1>(nx2, cv_of(c + 2), lane);
+        return;
+      }
       // y^T[r][i] for this wave's block; each lane stores 4 consecutive rows
       // of one token straight from the accumulators.  (For token blocks 0
       // and 1 the second K block of A^T is zero.)
@@ -449,8 +495,9 @@ __global__ __launch_bounds__(kNT) void fwd_mfma(FwdArgs a) {
       const int cb = tb + 4 * s;
       *reinterpret_cast<f32x4*>(so + (r0 + rbw * 16 + l16) * D + cb * 16 + 4 * g4) = sacc[s];
     }
-    if (tile == 0 && w8 == kPrepWave && lane == 0) a.seg_lg[bh * a.n_seg + seg] = lsum;
   }
+  if (a.seg_out && role == (HAS_Y ? 1 : 0) && tile == 0 && w8 == kPrepWave && lane == 0)
+    a.seg_lg[bh * a.n_seg + seg] = lsum;
 }
 
 template <int D, bool HAS_Y, bool HAS_ST>
