@@ -367,9 +367,34 @@ __global__ __launch_bounds__(kThreads) void finalize_kernel(FinArgs a) {
     if (!a.eta_done) static_cast<T*>(a.deta)[i] = se;
     if (!a.alpha_done) static_cast<T*>(a.dalpha)[i] = sa;
   }
+  const int64_t nb = a.B * a.n_seg;  // partials [n_seg][B][H][.], summed in this order
+  if constexpr (sizeof(T) == 4) {
+    if ((HD & 3) == 0) {
+      // four elements per thread, the loads of four partials in flight
+      typedef float f4 __attribute__((ext_vector_type(4)));
+      const f4* pw4 = reinterpret_cast<const f4*>(pw);
+      const int64_t HD4 = HD >> 2;
+      for (int64_t i = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; i < HD4;
+           i += stride) {
+        f4 s = {0.f, 0.f, 0.f, 0.f};
+        int64_t b = 0;
+        for (; b + 4 <= nb; b += 4) {
+          const f4 v0 = pw4[b * HD4 + i], v1 = pw4[(b + 1) * HD4 + i];
+          const f4 v2 = pw4[(b + 2) * HD4 + i], v3 = pw4[(b + 3) * HD4 + i];
+          s += v0;
+          s += v1;
+          s += v2;
+          s += v3;
+        }
+        for (; b < nb; ++b) s += pw4[b * HD4 + i];
+        reinterpret_cast<f4*>(a.dW0)[i] = s;
+      }
+      return;
+    }
+  }
   for (int64_t i = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; i < HD; i += stride) {
     T s = T(0);
-    for (int64_t b = 0; b < a.B * a.n_seg; ++b) s += pw[b * HD + i];  // [n_seg][B][H][.]
+    for (int64_t b = 0; b < nb; ++b) s += pw[b * HD + i];
     static_cast<T*>(a.dW0)[i] = s;
   }
 }

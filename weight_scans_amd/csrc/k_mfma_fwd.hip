@@ -106,7 +106,7 @@ __device__ __forceinline__ DmaOff<D> dma_off(int wave, int lane) {
     const int row = p >> 2, kl = (p & 3) ^ swz<kTN>(row);
     o.gq = static_cast<uint32_t>(row * D * 2 + 16 * kl);
   } else {
-    o.gq = static_cast<uint32_t>(lane * 16);
+    o.gq = static_cast<uint32_t>(lane * 4);
   }
   return o;
 }
@@ -137,7 +137,11 @@ __device__ __forceinline__ void issue_chunk(Slot<D>& sl, const DmaOff<D>& o, con
          : buffer_rsrc(((wave & 1) == 0 ? eta : alpha) + t0, cv * 4);
   const int lds_off = gw ? static_cast<int>(offsetof(Slot<D>, G)) + wave * 1024
                          : static_cast<int>(offsetof(Slot<D>, q)) + (wave & 1) * 1024;
-  dma16(r4, o.gq, reinterpret_cast<char*>(&sl) + lds_off);
+  // a gate row is 64 floats: one 4-byte load per lane
+  if (gw)
+    dma16(r4, o.gq, reinterpret_cast<char*>(&sl) + lds_off);
+  else
+    dma4(r4, o.gq, reinterpret_cast<char*>(&sl) + lds_off);
 }
 
 // Gates of a chunk, lane = token: PART 0 the per-token decays and Gamma
