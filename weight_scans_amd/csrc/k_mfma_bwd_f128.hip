@@ -19,12 +19,13 @@
 // register room); wave w holds the 32 x 64 region (k rows 32 (w % 4) ..,
 // r columns 64 (w / 4) ..) of Lam and dW0.  Three barriers per step:
 //   top:     the staged chunk into the slot, the bf16 copy of Lam_out, the
-//            loads of the next chunk (and the gate rows of the one after);
-//            wave 2 dalpha and deta of the chunk before (its shares are
-//            complete at the top);
+//            first loads of the next chunk (and the gate rows of the one
+//            after; the other loads are issued at the start of A and B);
 //   phase A: causal blocks (P^T, M, the Be dots: block w, and 8, 9 on waves
 //            2, 3); every wave its region of Lam and dW0 (<Lam_out, D_in>
-//            share, then the update); wave 0 the gates of the next chunk;
+//            share, then the update); wave 0 the gates of the next chunk,
+//            wave 1 dalpha and deta of the chunk before (its shares are
+//            complete after the first barrier);
 //   phase B: every wave 16 columns of dx (all tokens) with its rr share, and
 //            the 32 x 32 block (rows 32 (w % 4) .., tokens 32 (w / 4) ..) of
 //            u: dg, the deta and pp shares.
@@ -43,7 +44,7 @@ constexpr int kNW = 8;         // waves per work-group
 constexpr int kNT = 64 * kNW;  // threads
 constexpr int kRowWave = 1;    // eta / alpha rows of the chunk after next
 constexpr int kGateWave = 0;   // gates of the next chunk (phase A)
-constexpr int kAlphaWave = 2;  // dalpha and deta one chunk behind
+constexpr int kAlphaWave = 1;  // dalpha and deta one chunk behind (phase A)
 
 struct alignas(16) SlotH {
   __bf16 X[kC * kD];   // x, swizzled [token][k]
@@ -117,25 +118,40 @@ void bwd_f128(BwdArgs a) {
   // ---- staged loads: x, g, dy units tid and tid + 512; D_in units tid +
   // 512 j (j < 4); the eta / alpha rows (wave 1, lanes 0-31)
   u32x4 sx[2], sg[2], sdy[2], ss[4], sqe, sqa;
-  const auto load_chunk = [&](int c) {
+  // issued in three parts, one per phase of the step, so that the address
+  // unit works through them while the matrix cores do (all at once, the
+  // waves issuing last stall behind the queue)
+  const auto load_chunk = [&](int c, auto PC) {
+    constexpr int P = decltype(PC)::value;  // part: 0 x, g; 1 dy, D_in rows 0-31; 2 the rest of D_in
     const bool in = c >= 0;
     const int64_t t0 = in ? static_cast<int64_t>(c) * kC : 0;
     const int cv = cv_of(c);
-    const __amdgpu_buffer_rsrc_t rx = buffer_rsrc(x + t0 * kD, cv * kD * 2);
-    const __amdgpu_buffer_rsrc_t rg = buffer_rsrc(g + t0 * kD, cv * kD * 2);
-    const __amdgpu_buffer_rsrc_t rd = buffer_rsrc(dy + t0 * kD, cv * kD * 2);
-    const __amdgpu_buffer_rsrc_t rs =
-        buffer_rsrc(st + (in ? static_cast<int64_t>(c) : 0) * kD * kD, in ? kD * kD * 2 : 0);
+    if constexpr (P == 0) {
+      const __amdgpu_buffer_rsrc_t rx = buffer_rsrc(x + t0 * kD, cv * kD * 2);
+      const __amdgpu_buffer_rsrc_t rg = buffer_rsrc(g + t0 * kD, cv * kD * 2);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const uint32_t off = static_cast<uint32_t>((tid + kNT * j) * 16);
-      sx[j] = load16(rx, off);
-      sg[j] = load16(rg, off);
-      sdy[j] = load16(rd, off);
+      for (int j = 0; j < 2; ++j) {
+        const uint32_t off = static_cast<uint32_t>((tid + kNT * j) * 16);
+        sx[j] = load16(rx, off);
+        sg[j] = load16(rg, off);
+      }
+    } else {
+      const __amdgpu_buffer_rsrc_t rs =
+          buffer_rsrc(st + (in ? static_cast<int64_t>(c) : 0) * kD * kD, in ? kD * kD * 2 : 0);
+      if constexpr (P == 1) {
+        const __amdgpu_buffer_rsrc_t rd = buffer_rsrc(dy + t0 * kD, cv * kD * 2);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) sdy[j] = load16(rd, static_cast<uint32_t>((tid + kNT * j) * 16));
+        ss[0] = load16(rs, static_cast<uint32_t>(tid * 16));
+      } else {
+#pragma unroll
+        for (int j = 1; j < 4; ++j) ss[j] = load16(rs, static_cast<uint32_t>((tid + kNT * j) * 16));
+      }
     }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) ss[j] = load16(rs, static_cast<uint32_t>((tid + kNT * j) * 16));
   };
+  using P0 = std::integral_constant<int, 0>;
+  using P1 = std::integral_constant<int, 1>;
+  using P2 = std::integral_constant<int, 2>;
   const auto load_rows = [&](int c) {
     if (wave == kRowWave) {
       const int64_t t0 = c >= 0 ? static_cast<int64_t>(c) * kC : 0;
@@ -167,7 +183,9 @@ void bwd_f128(BwdArgs a) {
   // ---- set-up: first chunk and the gate rows of the first chunk in flight;
   // W0 staged in L_s for the dx waves' W0^T fragments; the entering adjoint
   // (given, or composed from the segments to the right)
-  load_chunk(chunk_at(0));
+  load_chunk(chunk_at(0), P0{});
+  load_chunk(chunk_at(0), P1{});
+  load_chunk(chunk_at(0), P2{});
   load_rows(chunk_at(0));
   for (int idx = tid; idx < kD * kD / 8; idx += kNT) {
     const int r = idx >> 4, cc = 8 * (idx & 15);
@@ -222,34 +240,12 @@ void bwd_f128(BwdArgs a) {
 #pragma unroll
       for (int b = 0; b < 4; ++b)
         put4<kD>(L_s, o, (4 * rh + b) * 16, (2 * kq + aa) * 16, pack4f(lam[aa][b]));
-    load_chunk(chunk_at(v + 1));
+    load_chunk(chunk_at(v + 1), P0{});
     load_rows(chunk_at(v + 2));
-    if (wave == kAlphaWave) {
-      const int cp = chunk_at(v - 1);
-      if (cp >= 0) {
-        // dalpha and deta of the chunk finished one step ago
-        const PartH& pr = part[(v - 1) & 1];
-        const int ir = kC - 1 - lane;
-        float c0 = 0.f, pp = 0.f, de = 0.f, rr_r = 0.f;
-#pragma unroll
-        for (int w = 0; w < kNW; ++w) {
-          c0 += pr.c0[w];
-          rr_r += pr.rr[w][ir];
-        }
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          pp += pr.pp[w][lane];
-          de += pr.de[w][lane];
-        }
-        const float da = dalpha_f(rec[(v - 1) & 3], qk[(v - 1) & 1], pp, rr_r, c0, lane);
-        const int64_t tp = static_cast<int64_t>(cp) * kC;
-        store4(buffer_rsrc(dal + tp, cv_of(cp) * 4), static_cast<uint32_t>(lane * 4), da);
-        store4(buffer_rsrc(det + tp, cv_of(cp) * 4), static_cast<uint32_t>(lane * 4), de);
-      }
-    }
     lds_barrier();  // B2: chunk v, Lam_out, gate rows of v + 1 visible
 
     // ---- phase A
+    load_chunk(chunk_at(v + 1), P1{});
     const RecF& rc = rec[v & 3];
     if (c >= 0) {
       causal_f<kD>(sl.X, sl.G, sl.DY, rc, PT_s, M_s, qk[v & 1], o, o64, wave, lane);
@@ -291,6 +287,29 @@ void bwd_f128(BwdArgs a) {
         }
       }
     }
+    if (wave == kAlphaWave) {
+      const int cp = chunk_at(v - 1);
+      if (cp >= 0) {
+        // dalpha and deta of the chunk finished one step ago
+        const PartH& pr = part[(v - 1) & 1];
+        const int ir = kC - 1 - lane;
+        float c0 = 0.f, pp = 0.f, de = 0.f, rr_r = 0.f;
+#pragma unroll
+        for (int w = 0; w < kNW; ++w) {
+          c0 += pr.c0[w];
+          rr_r += pr.rr[w][ir];
+        }
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          pp += pr.pp[w][lane];
+          de += pr.de[w][lane];
+        }
+        const float da = dalpha_f(rec[(v - 1) & 3], qk[(v - 1) & 1], pp, rr_r, c0, lane);
+        const int64_t tp = static_cast<int64_t>(cp) * kC;
+        store4(buffer_rsrc(dal + tp, cv_of(cp) * 4), static_cast<uint32_t>(lane * 4), da);
+        store4(buffer_rsrc(det + tp, cv_of(cp) * 4), static_cast<uint32_t>(lane * 4), de);
+      }
+    }
     if (wave == kGateWave) {
       // gates of the next chunk (its rows were written before B2)
       const int cn = chunk_at(v + 1);
@@ -299,8 +318,9 @@ void bwd_f128(BwdArgs a) {
     }
     lds_barrier();  // B3: P^T, M, the Be dots visible
 
-    // ---- phase B: the 32 x 32 blocks (k blocks 2 kq + a, token blocks 2 th + b)
-    // of dx^T and (r blocks 2 kq + a, same tokens) of u^T, th = wave / 4
+    // ---- phase B: 16 columns of dx (all tokens), the 32 x 32 block (r blocks
+    // 2 kq + a, token blocks 2 th + b) of u^T, th = wave / 4
+    load_chunk(chunk_at(v + 1), P2{});
     const int64_t t0 = c >= 0 ? static_cast<int64_t>(c) * kC : 0;
     const int cv = cv_of(c);
     if (c >= 0) {
