@@ -15,10 +15,16 @@
 // known, the weight trajectory becomes parallelizable", run in reverse).
 // Segment 0's own result is never needed, so it is not computed.
 //
-// One work-group per (segment, sequence-head, 32-row tile of Lam), eight
-// waves; x and the dy rows of the tile come by direct buffer loads into two
-// slots, one chunk ahead; two barriers per chunk (slot free, then e(lq) dy
-// visible to the matrix-core update).
+// One work-group per (segment, sequence-head, half of the rows r of Lam),
+// eight waves; x and the dy rows of the tile come by direct buffer loads into
+// two slots, one chunk ahead; two barriers per chunk (slot free, then e(lq) dy
+// visible to the matrix-core update).  What bounds the pass is the address
+// unit's throughput of direct loads, so no load carries bytes nobody uses:
+// the alpha row is one 4-byte load per lane, and where the dy rows need fewer
+// loads than there are waves, the others load nothing (4 bytes from an empty
+// buffer) to keep one count of loads per wave.  Half-height tiles read x
+// twice per sequence-head (32-row tiles at d = 128 read it four times and ran
+// about 30% longer).
 #include <algorithm>
 #include <cstddef>
 #include <type_traits>
@@ -31,15 +37,18 @@ namespace gls {
 namespace {
 
 constexpr int kC = 64;         // tokens per chunk
-constexpr int kT = 32;         // rows of Lam per work-group
+// rows of Lam per work-group: half of them
+template <int D>
+constexpr int kTile = D / 2;
 constexpr int kNW = 8;         // waves per work-group
 constexpr int kNT = 64 * kNW;  // threads
 
 template <int D>
 struct alignas(16) SlotL {
   __bf16 X[kC * D];    // x of the chunk, swizzled [token][D]
-  __bf16 Dr[kC * kT];  // dy of the row tile, swizzled [token][kT]
-  float q[4 * kC];     // alpha of the chunk (first kC)
+  __bf16 Dr[kC * kTile<D>];  // dy of the row tile, swizzled [token][D / 2]
+  float q[kC];         // alpha of the chunk
+  float pad[kC];       // target of the empty loads
 };
 
 struct alignas(16) GatesL {
@@ -62,16 +71,16 @@ __device__ __forceinline__ DmaOffL<D> dma_off_l(int wave, int lane) {
     const int row = p / U, kl = (p % U) ^ swz<D>(row);
     o.x[s] = static_cast<uint32_t>(row * D * 2 + 16 * kl);
   }
-  const int p = (wave & 3) * 64 + lane;
-  const int row = p >> 2, kl = (p & 3) ^ swz<kT>(row);
+  constexpr int UT = kTile<D> / 8;  // 16-byte units per row of the dy tile
+  const int p = (wave % UT) * 64 + lane;  // (waves past the tile's loads do not use it)
+  const int row = p / UT, kl = (p % UT) ^ swz<kTile<D>>(row);
   o.t = static_cast<uint32_t>(row * D * 2 + 16 * kl);
-  o.q = static_cast<uint32_t>(lane * 16);
+  o.q = static_cast<uint32_t>(lane * 4);
   return o;
 }
 
 // Loads of chunk k (negative: zero fill): x (all waves), the dy rows of the
-// tile (waves 0-3; waves 4-7 repeat them), the alpha row (every wave, the
-// same bytes).
+// tile, the alpha row (every wave, the same bytes).
 template <int D>
 __device__ __forceinline__ void issue_chunk_l(SlotL<D>& sl, const DmaOffL<D>& o, const uint16_t* x,
                                               const uint16_t* dy, const float* alpha, int64_t T,
@@ -82,18 +91,27 @@ __device__ __forceinline__ void issue_chunk_l(SlotL<D>& sl, const DmaOffL<D>& o,
   const __amdgpu_buffer_rsrc_t rx = buffer_rsrc(x + t0 * D, cv * D * 2);
 #pragma unroll
   for (int s = 0; s < D / 64; ++s) dma16(rx, o.x[s], sl.X + (wave + 8 * s) * 512);
-  dma16(buffer_rsrc(dy + t0 * D + r0, cv > 0 ? (cv * D - r0) * 2 : 0), o.t,
-        sl.Dr + (wave & 3) * 512);
-  dma16(buffer_rsrc(alpha + t0, cv * 4), o.q, sl.q);
+  // dy rows of the tile (64 x D/2: 8 or 4 loads of 1 KB); where they take
+  // fewer than 8 loads, the other waves issue a 4-byte load of nothing into a
+  // pad instead (the same count of loads in every wave)
+  constexpr int NLT = kC * kTile<D> / 512;
+  if (wave < NLT)
+    dma16(buffer_rsrc(dy + t0 * D + r0, cv > 0 ? (cv * D - r0) * 2 : 0), o.t, sl.Dr + wave * 512);
+  else
+    dma4(buffer_rsrc(dy, 0), o.q, sl.pad);
+  dma4(buffer_rsrc(alpha + t0, cv * 4), o.q, sl.q);
 }
 
 template <int D>
 __global__ __launch_bounds__(kNT) void bwd_lam(BwdArgs a) {
   static_assert(D == 64 || D == 128, "D");
+  constexpr int kT = kTile<D>;
   constexpr int NTILE = D / kT;
-  constexpr int NS = D / 64;
+  constexpr int NRBT = kT / 16;               // row blocks of the tile
+  constexpr int NS = NRBT * (D / 16) / kNW;   // blocks per wave
+  constexpr int EPT = kC * kT / kNT;          // elements of the dy tile per thread
   __shared__ SlotL<D> ring0, ring1;
-  __shared__ __bf16 DS_s[kC * kT];  // e(lq_u) dy_u of the row tile
+  __shared__ __bf16 DS_s[kC * kTile<D>];  // e(lq_u) dy_u of the row tile
   __shared__ GatesL gs;
   SlotL<D>* const rs[2] = {&ring0, &ring1};
 
@@ -114,7 +132,8 @@ __global__ __launch_bounds__(kNT) void bwd_lam(BwdArgs a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g4 = lane >> 4, l16 = lane & 15;
-  const int tb = wave >> 1, rbw = wave & 1;  // column blocks tb + 4s, row block rbw of the tile
+  // row block rbw of the tile, column blocks tb + (8 / NRBT) s
+  const int rbw = wave % NRBT, tb = wave / NRBT;
   const uint16_t* x = static_cast<const uint16_t*>(a.x) + bh * T * D;
   const uint16_t* dy = static_cast<const uint16_t*>(a.dy) + bh * T * D;
   const float* alpha = static_cast<const float*>(a.alpha) + bh * T;
@@ -123,12 +142,12 @@ __global__ __launch_bounds__(kNT) void bwd_lam(BwdArgs a) {
   const LaneOff<kT> oT = lane_off<kT>(lane);
   const DmaOffL<D> od = dma_off_l<D>(wave, lane);
   const int ds_row = tid >> 3;
-  const uint32_t ds_off = static_cast<uint32_t>(sidx<kT>(ds_row, 4 * (tid & 7)) * 2);
+  const uint32_t ds_off = static_cast<uint32_t>(sidx<kT>(ds_row, EPT * (tid & 7)) * 2);
   const auto cv_of = [&](int c) {
     return static_cast<int>(std::min<int64_t>(kC, T - static_cast<int64_t>(c) * kC));
   };
 
-  // Lam^T blocks of the tile (columns tb + 4s, rows rbw), fp32, from zero
+  // Lam^T blocks of the tile (columns tb + (8 / NRBT) s, rows rbw), fp32, from zero
   f32x4 lam[NS];
 #pragma unroll
   for (int s = 0; s < NS; ++s) lam[s] = zero4();
@@ -151,12 +170,22 @@ __global__ __launch_bounds__(kNT) void bwd_lam(BwdArgs a) {
     const float gam = fexp2(gt.llast);
     lsum += gt.llast;
     {
-      const uint2 v = *reinterpret_cast<const uint2*>(reinterpret_cast<const char*>(cur.Dr) + ds_off);
       const float e = gs.eq[ds_row];
-      uint2 r;
-      r.x = pack2(bf16_val(v.x & 0xffffu) * e, bf16_val(v.x >> 16) * e);
-      r.y = pack2(bf16_val(v.y & 0xffffu) * e, bf16_val(v.y >> 16) * e);
-      *reinterpret_cast<uint2*>(reinterpret_cast<char*>(DS_s) + ds_off) = r;
+      if constexpr (EPT == 4) {
+        const uint2 v = *reinterpret_cast<const uint2*>(reinterpret_cast<const char*>(cur.Dr) + ds_off);
+        uint2 r;
+        r.x = pack2(bf16_val(v.x & 0xffffu) * e, bf16_val(v.x >> 16) * e);
+        r.y = pack2(bf16_val(v.y & 0xffffu) * e, bf16_val(v.y >> 16) * e);
+        *reinterpret_cast<uint2*>(reinterpret_cast<char*>(DS_s) + ds_off) = r;
+      } else {
+        const uint4 v = *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(cur.Dr) + ds_off);
+        uint4 r;
+        r.x = pack2(bf16_val(v.x & 0xffffu) * e, bf16_val(v.x >> 16) * e);
+        r.y = pack2(bf16_val(v.y & 0xffffu) * e, bf16_val(v.y >> 16) * e);
+        r.z = pack2(bf16_val(v.z & 0xffffu) * e, bf16_val(v.z >> 16) * e);
+        r.w = pack2(bf16_val(v.w & 0xffffu) * e, bf16_val(v.w >> 16) * e);
+        *reinterpret_cast<uint4*>(reinterpret_cast<char*>(DS_s) + ds_off) = r;
+      }
     }
     lds_barrier();  // e(lq) dy visible
     // Lam^T[k][r] <- Gamma Lam^T + sum_u x_u[k] e(lq_u) dy_u[r]
@@ -168,7 +197,8 @@ __global__ __launch_bounds__(kNT) void bwd_lam(BwdArgs a) {
       lam[s] = lam[s] * gam;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
-        lam[s] = mfma16x16x32(frag_ts<D>(cur.X, oX, kb * 32, (tb + 4 * s) * 16), dsf[kb], lam[s]);
+        lam[s] = mfma16x16x32(frag_ts<D>(cur.X, oX, kb * 32, (tb + (8 / NRBT) * s) * 16), dsf[kb],
+                              lam[s]);
     }
   };
   using I0 = std::integral_constant<int, 0>;
@@ -182,7 +212,8 @@ __global__ __launch_bounds__(kNT) void bwd_lam(BwdArgs a) {
   float* so = a.seg_out + (bh * a.n_seg + seg) * D * D;
 #pragma unroll
   for (int s = 0; s < NS; ++s)
-    *reinterpret_cast<f32x4*>(so + (r0 + rbw * 16 + l16) * D + (tb + 4 * s) * 16 + 4 * g4) = lam[s];
+    *reinterpret_cast<f32x4*>(so + (r0 + rbw * 16 + l16) * D + (tb + (8 / NRBT) * s) * 16 + 4 * g4) =
+        lam[s];
   if (tile == 0 && wave == 0 && lane == 0) a.seg_lg[bh * a.n_seg + seg] = lsum;
 }
 
@@ -190,7 +221,7 @@ template <int D>
 hipError_t launch_lam(const BwdArgs& a, hipStream_t s) {
   if (a.n_seg <= 1) return hipSuccess;
   const int64_t groups = (a.B * a.H + 7) / 8;
-  const dim3 grid(static_cast<unsigned>(groups * 8 * (D / kT) * (a.n_seg - 1)));
+  const dim3 grid(static_cast<unsigned>(groups * 8 * (D / kTile<D>) * (a.n_seg - 1)));
   hipLaunchKernelGGL(bwd_lam<D>, grid, dim3(kNT), 0, s, a);
   return hipGetLastError();
 }
