@@ -55,7 +55,7 @@ struct Plan {
   size_t seg_bytes = 0;     // per-segment states (fp32) + summed log2 alpha
   size_t seg_state_bytes = 0;
   int dw_groups = 1;        // dW0 partials per (b, h)
-  // fused backward (matrix-core kernels, d = 64): its own segment count (a
+  // fused backward (matrix-core kernels, d = 64 and 128): its own segment count (a
   // work-group per segment and sequence-head), deta / dalpha written directly
   bool fused = false;
   int bwd_nseg = 1, bwd_seg_chunks = 0;

@@ -70,7 +70,7 @@ struct BwdArgs {
   const float* seg_lg_in = nullptr;
   float* seg_out = nullptr;
   float* seg_lg = nullptr;
-  // Fused backward (d = 64): deta and dalpha written directly ([B,H,T]).
+  // Fused backward: deta and dalpha written directly ([B,H,T]).
   void* deta_out = nullptr;
   void* dalpha_out = nullptr;
 };

@@ -183,11 +183,6 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-__device__ __forceinline__ uint32_t bf16_bits(float f) {
-  __bf16 h = static_cast<__bf16>(f);
-  return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, h));
-}
-
 // Two floats -> packed bf16 pair (round to nearest even), one v_cvt_pk_bf16_f32.
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -215,28 +210,10 @@ __device__ __forceinline__ int tri_j(int b) {
   return static_cast<int>((0x3210210100ull >> (4 * b)) & 0xfull);
 }
 
-// 16-byte load of row `j` of a token-major tile with the row clamped to the
-// valid range [0, cv): the load is unconditional (rows j >= cv are zeroed
-// later, when the tile is staged, so that the prefetch never waits here).
-__device__ __forceinline__ uint4 load_row16(const uint16_t* base, int64_t row_stride, int j, int cv) {
-  const int jj = j < cv ? j : cv - 1;
-  return *reinterpret_cast<const uint4*>(base + static_cast<int64_t>(jj) * row_stride);
-}
-
-__device__ __forceinline__ uint4 keep_row(const uint4& v, int j, int cv) {
-  return j < cv ? v : make_uint4(0, 0, 0, 0);
-}
-
 // LDS barrier that does not wait for outstanding global loads, so a prefetch
 // of the next chunk stays in flight across it.
 __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-
-// 16-bit element q (0..7) of a 16-byte vector of bf16.
-__device__ __forceinline__ uint32_t half_of(const uint4& u, int q) {
-  const uint32_t w = (q >> 1) == 0 ? u.x : (q >> 1) == 1 ? u.y : (q >> 1) == 2 ? u.z : u.w;
-  return (q & 1) ? (w >> 16) : (w & 0xffffu);
 }
 
 // ---- wave64 scans on DPP (register-only cross-lane moves, GFX9 controls) ----
