@@ -65,7 +65,7 @@ def pass_kernels(w, which, segmented, generic):
     # sequence-head) work-groups for 256 CUs, at least 16 chunks each
     bh, nch = w.B * w.H, -(-w.T // 64)
     nseg = max(1, min(-(-256 // bh), nch // 16)) if bh < 256 else 1
-    pre = "bwd_lam + " if nseg > 1 else ""
+    pre = ("bwd_lam + seg_combine + " if nseg > 4 else "bwd_lam + ") if nseg > 1 else ""
     return pre + ("bwd_f64" if w.d_in == 64 else "bwd_f128") + " + finalize_kernel"
 
 

@@ -39,6 +39,9 @@ size_t round_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 // least kMinSegChunks chunks so that the pass fills the chip.
 constexpr int64_t kSegTargetGroups = 256;
 constexpr int kMinSegChunks = 16;
+// Above this many backward segments the entering adjoints are composed by one
+// combine launch rather than in every fused work-group's set-up.
+constexpr int kBwdCombineAbove = 4;
 
 // Everything the launches need, derived from the descriptor alone so that the
 // forward and the backward agree on the layout of `saved`.
@@ -315,8 +318,19 @@ gl_status_t gl_scan_bwd(const gl_scan_desc_t* desc, const void* x, const void* g
       bs.seg_out = seg;
       bs.seg_lg = lg;
       st = hip_status(gls::launch_mfma_bwd_lam(bs, s), "backward segment pass");
-      bf.seg_lam = seg;  // composed per segment by the fused kernel itself
-      bf.seg_lg_in = lg;
+      bf.seg_lam = seg;
+      if (p.bwd_nseg > kBwdCombineAbove) {
+        // the adjoint entering every segment, composed from the right in one
+        // launch (in its set-up a work-group would wait for one load per
+        // segment to its right, one after another)
+        if (st == GL_SUCCESS)
+          st = hip_status(gls::launch_seg_combine(seg, lg, b.B * b.H, p.bwd_nseg,
+                                                  b.d_in * b.d_out, true, s),
+                          "backward segment combine");
+        bf.seg_lg_in = nullptr;
+      } else {
+        bf.seg_lg_in = lg;  // few segments: composed by the fused kernel itself
+      }
     }
     if (st == GL_SUCCESS)
       st = hip_status(b.d_in == 64 ? gls::launch_mfma_bwd_f64(bf, s) : gls::launch_mfma_bwd_f128(bf, s),

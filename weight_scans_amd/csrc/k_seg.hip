@@ -28,16 +28,30 @@ __global__ __launch_bounds__(kSegThreads) void seg_combine(float* buf, const flo
   if (e >= dd) return;
   float* p = buf + bh * n_seg * static_cast<int64_t>(dd) + e;
   const float* l = lg + bh * n_seg;
+  // segments in groups of eight: the group's loads are issued together, then
+  // the scan runs through them (one memory round trip per group, not per
+  // segment)
+  constexpr int kGroup = 8;
   float carry = 0.f;
-  for (int k = 0; k < n_seg; ++k) {
-    const int s = reverse ? n_seg - 1 - k : k;
-    if (k == n_seg - 1) {  // the segment reached last: its own L_s is never needed
-      p[static_cast<int64_t>(s) * dd] = carry;
-      break;
+  for (int k0 = 0; k0 < n_seg; k0 += kGroup) {
+    float local[kGroup], lgs[kGroup];
+#pragma unroll
+    for (int j = 0; j < kGroup; ++j) {
+      const int k = k0 + j;
+      const int s = reverse ? n_seg - 1 - k : k;
+      // the segment reached last: its own L_s is never needed (nor read)
+      const bool use = k < n_seg - 1;
+      local[j] = use ? p[static_cast<int64_t>(s) * dd] : 0.f;
+      lgs[j] = use ? l[s] : 0.f;
     }
-    const float local = p[static_cast<int64_t>(s) * dd];
-    p[static_cast<int64_t>(s) * dd] = carry;
-    carry = carry * __builtin_amdgcn_exp2f(l[s]) + local;
+#pragma unroll
+    for (int j = 0; j < kGroup; ++j) {
+      const int k = k0 + j;
+      if (k >= n_seg) break;
+      const int s = reverse ? n_seg - 1 - k : k;
+      p[static_cast<int64_t>(s) * dd] = carry;
+      carry = carry * __builtin_amdgcn_exp2f(lgs[j]) + local[j];
+    }
   }
 }
 

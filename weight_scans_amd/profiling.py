@@ -39,6 +39,8 @@ def kernel_source_hash() -> str:
 
 
 def short_name(kernel: str) -> str:
+    if kernel.startswith("seg_combine ("):  # already a pass-labelled name
+        return kernel
     k = kernel
     for pre in ("void ", "gls::(anonymous namespace)::", "at::native::"):
         k = k.replace(pre, "")
@@ -61,14 +63,28 @@ def stats_table(path: str) -> str:
 
 
 def _counter(dirpath: str, counter: str):
-    """{kernel name: [value per dispatch]} for one counter (summed over dims)."""
-    per = defaultdict(lambda: defaultdict(float))
+    """{kernel name: [value per dispatch]} for one counter (summed over dims).
+    The segment combine serves both passes: a dispatch of it right after the
+    backward's segment pass is named "seg_combine (bwd)", any other one
+    "seg_combine (fwd)"."""
+    per = defaultdict(float)
+    name = {}
     for f in glob.glob(os.path.join(dirpath, "**", "*counter_collection.csv"), recursive=True):
         for r in csv.DictReader(open(f)):
             if r["Counter_Name"] != counter:
                 continue
-            per[r["Kernel_Name"]][r["Dispatch_Id"]] += float(r["Counter_Value"])
-    return {k: list(v.values()) for k, v in per.items()}
+            key = (f, int(r["Dispatch_Id"]))
+            per[key] += float(r["Counter_Value"])
+            name[key] = r["Kernel_Name"]
+    out = defaultdict(list)
+    prev = None
+    for key in sorted(per):
+        k = name[key]
+        if "seg_combine" in k:
+            k = "seg_combine (bwd)" if prev is not None and "bwd_lam" in prev else "seg_combine (fwd)"
+        out[k].append(per[key])
+        prev = name[key]
+    return dict(out)
 
 
 def _mean(v):
@@ -111,13 +127,12 @@ def main(argv):
         if "--json" in argv:
             path = os.path.join(ROOT, "profiles", "traffic.json")
             db = json.load(open(path)) if os.path.exists(path) else {}
-            # per-dispatch bytes of every kernel a pass launches once; the
-            # segment combine runs once in each pass
+            # per-dispatch bytes of every kernel a pass launches once
             def moved(pred):
                 return sum(v["fetch_bytes"] + v["write_bytes"] for k, v in res["kernels"].items()
                            if pred(k))
-            fwd = moved(lambda k: k.startswith("fwd_") or "seg_combine" in k)
-            bwd = moved(lambda k: k.startswith("bwd_") or "finalize" in k or "seg_combine" in k)
+            fwd = moved(lambda k: k.startswith("fwd_") or k == "seg_combine (fwd)")
+            bwd = moved(lambda k: k.startswith("bwd_") or "finalize" in k or k == "seg_combine (bwd)")
             db[cfg] = {"kernel_hash": kernel_source_hash(), "fwd_bytes": fwd, "bwd_bytes": bwd,
                        "fetch_scale": res["fetch_scale"], "write_scale": res["write_scale"]}
             with open(path, "w") as fh:
