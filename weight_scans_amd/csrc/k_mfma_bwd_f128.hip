@@ -187,11 +187,20 @@ void bwd_f128(BwdArgs a) {
   load_chunk(chunk_at(0), P1{});
   load_chunk(chunk_at(0), P2{});
   load_rows(chunk_at(0));
-  for (int idx = tid; idx < kD * kD / 8; idx += kNT) {
-    const int r = idx >> 4, cc = 8 * (idx & 15);
-    *reinterpret_cast<uint4*>(&L_s[sidx<kD>(r, cc)]) =
-        *reinterpret_cast<const uint4*>(W0 + static_cast<int64_t>(r) * kD + cc);
-  }
+  // W0 into L_s (bf16, swizzled), all four loads in flight before the first write
+  const auto stage_w0 = [&]() {
+    uint4 w0v[kD * kD / 8 / kNT];
+#pragma unroll
+    for (int j = 0; j < kD * kD / 8 / kNT; ++j) {
+      const int idx = tid + kNT * j, r = idx >> 4, cc = 8 * (idx & 15);
+      w0v[j] = *reinterpret_cast<const uint4*>(W0 + static_cast<int64_t>(r) * kD + cc);
+    }
+#pragma unroll
+    for (int j = 0; j < kD * kD / 8 / kNT; ++j) {
+      const int idx = tid + kNT * j, r = idx >> 4, cc = 8 * (idx & 15);
+      *reinterpret_cast<uint4*>(&L_s[sidx<kD>(r, cc)]) = w0v[j];
+    }
+  };
   f32x4 lam[2][4], dw[2][4];  // Lam^T / dW0^T blocks (k block 2 kq + a, r block 4 rh + b)
 #pragma unroll
   for (int aa = 0; aa < 2; ++aa)
@@ -203,18 +212,37 @@ void bwd_f128(BwdArgs a) {
   if (a.seg_lam) {
     const int s_lo = a.seg_lg_in ? seg + 1 : seg;
     const int s_hi = a.seg_lg_in ? a.n_seg - 1 : seg;
-    for (int s2 = s_hi; s2 >= s_lo; --s2) {
+    // this thread's elements of segment s2's tile; the next tile's loads are
+    // issued before the current one is folded in
+    const auto tile = [&](int s2, f32x4 (&t)[2][4]) {
       const float* sp = a.seg_lam + (bh * a.n_seg + s2) * kD * kD;
-      const float gs = a.seg_lg_in ? fexp2(a.seg_lg_in[bh * a.n_seg + s2]) : 0.f;
 #pragma unroll
       for (int aa = 0; aa < 2; ++aa)
 #pragma unroll
         for (int b = 0; b < 4; ++b)
-          lam[aa][b] = lam[aa][b] * gs +
-                       *reinterpret_cast<const f32x4*>(sp + ((4 * rh + b) * 16 + l16) * kD +
-                                                       (2 * kq + aa) * 16 + 4 * g4);
+          t[aa][b] = *reinterpret_cast<const f32x4*>(sp + ((4 * rh + b) * 16 + l16) * kD +
+                                                     (2 * kq + aa) * 16 + 4 * g4);
+    };
+    f32x4 cur[2][4], nxt[2][4];
+#pragma unroll
+    for (int aa = 0; aa < 2; ++aa)
+#pragma unroll
+      for (int b = 0; b < 4; ++b) nxt[aa][b] = zero4();
+    if (s_hi >= s_lo) tile(s_hi, cur);
+    stage_w0();  // (its loads overlap those of the first tile)
+    for (int s2 = s_hi; s2 >= s_lo; --s2) {
+      if (s2 - 1 >= s_lo) tile(s2 - 1, nxt);
+      const float gs = a.seg_lg_in ? fexp2(a.seg_lg_in[bh * a.n_seg + s2]) : 0.f;
+#pragma unroll
+      for (int aa = 0; aa < 2; ++aa)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          lam[aa][b] = lam[aa][b] * gs + cur[aa][b];
+          cur[aa][b] = nxt[aa][b];
+        }
     }
   }
+  if (!a.seg_lam) stage_w0();
   put_rows(rows_s[0]);
   __syncthreads();
   bf16x8 wf[4];  // W0^T fragments of this wave's dx columns (k block `wave`, K block kk)
