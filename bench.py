@@ -4,14 +4,22 @@
 One step = gl_scan_fwd + gl_scan_bwd over one batch of synthetic inputs of the
 named workload (default: the 340M-shape layer, [B,H,T,d] = [8,16,4096,64],
 bf16 io with fp32 state).  Inputs are resident in HBM before timing starts.
-Before every timed step a 1 GiB buffer is overwritten (untimed by the events)
-so that neither L2 nor the 256 MB last-level cache holds the step's inputs.
+Before every timed step a 1 GiB buffer is read (untimed by the events) so
+that neither L2 nor the 256 MB last-level cache holds the step's inputs.
 
 Prints ONE JSON line.  `value` = tokens/s = B*T*K / sum of event-timed
 (fwd + bwd) durations (tokens, not token-heads).  `roofline` reports the
 dominant pass against its binding roofline using ALGORITHMIC bytes / flops
 (each input read once, each output written once).  `cpu_baseline` times the
 fp64 CPU oracle on a bounded sample of the same workload on this host.
+
+With --decode it prints instead the deployment line: one step = one new token
+of every sequence of the batch, in the steady state of serving (gl_decode_step
+over all sequence-heads: the previous token's update fused with the new
+token's readout), starting from the hand-over state of the named workload's
+prefill (gl_scan_final_state, timed once).  The separate readout and update
+calls are timed too and reported beside it.  The cached adaptation stays on the
+GPU between tokens, as in serving, so no flush runs between decode steps.
 """
 from __future__ import annotations
 
@@ -107,6 +115,177 @@ def cpu_baseline(w, budget_s=20.0):
                       f"sequence-heads*T/H"}
 
 
+def decode_bytes(w):
+    """Algorithmic bytes of one decode token over all sequence-heads:
+    (readout, update, fused step).  The readout reads the state, W0 and x and
+    writes y; the update reads and writes the state and reads x, g, eta and
+    alpha; the fused step reads and writes the state once and reads W0, both
+    tokens' x, g, eta and alpha, and writes y."""
+    e = {"bf16": 2, "f32": 4, "f64": 8}[w.dtype]
+    es = 8 if w.dtype == "f64" else 4
+    bh, dd = w.B * w.H, w.d_in * w.d_out
+    rd = bh * (dd * es + e * (w.d_in + w.d_out)) + w.H * dd * e
+    up = bh * (2 * dd * es + e * (w.d_in + w.d_out) + 2 * es)
+    st = bh * (2 * dd * es + e * (2 * w.d_in + 2 * w.d_out) + 2 * es) + w.H * dd * e
+    return rd, up, st
+
+
+def cpu_decode(w, inp, budget_s=10.0):
+    """The oracle's readout + update over every sequence-head, token after
+    token, for about budget_s seconds (one thread: the oracle is serial)."""
+    import numpy as np
+
+    import oracle
+
+    S = np.zeros((w.B, w.H, w.d_out, w.d_in))
+    n, t0 = 0, time.perf_counter()
+    while time.perf_counter() - t0 < budget_s:
+        k = n % inp["x"].shape[0]
+        oracle.decode_readout(inp["x"][k], inp["W0"], S)
+        S = oracle.decode_update(inp["x"][k], inp["g"][k], inp["eta"][k], inp["alpha"][k], S)
+        n += 1
+    dt = time.perf_counter() - t0
+    return {"value": n * w.B / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{n} decode tokens of all {w.B * w.H} sequence-heads "
+                      f"(d={w.d_in}), fp64 serial oracle, {dt:.1f} s wall"}
+
+
+def decode_main(args, w):
+    import numpy as np
+    import torch
+
+    import weight_scans_amd as ws
+    from weight_scans_amd.synth import make_inputs, round_to
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    tio = {"f64": torch.float64, "f32": torch.float32, "bf16": torch.bfloat16}[w.dtype]
+    gd = ws.gate_dtype(tio)
+    inp = make_inputs(w)
+    pre = {k: torch.from_numpy(inp[k]).to(dev, tio) for k in ("x", "g", "W0")}
+    pre.update({k: torch.from_numpy(inp[k]).to(dev, gd) for k in ("eta", "alpha")})
+    del inp
+    # the decode tokens: one per sequence and step, all resident before timing
+    K = args.warmup + args.steps + 1
+    rng = np.random.Generator(np.random.PCG64(4242))
+    dec = {
+        "x": round_to(rng.standard_normal((K, w.B, w.H, w.d_in)) / np.sqrt(w.d_in), w.dtype),
+        "g": round_to(rng.standard_normal((K, w.B, w.H, w.d_out)) / np.sqrt(w.d_out), w.dtype),
+        "eta": round_to(0.1 / (1 + np.exp(-rng.normal(-1.0, 1.0, (K, w.B, w.H)))),
+                        "f64" if w.dtype == "f64" else "f32"),
+        "alpha": round_to(1 / (1 + np.exp(-rng.normal(3.0, 1.0, (K, w.B, w.H)))),
+                          "f64" if w.dtype == "f64" else "f32"),
+    }
+    dd = {k: torch.from_numpy(dec[k]).to(dev, tio if k in ("x", "g") else gd) for k in dec}
+    L = ws.lib()
+    stream = torch.cuda.current_stream(dev)
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    P = lambda a: ctypes.c_void_p(a.data_ptr())  # noqa: E731
+    io = {"f64": 0, "f32": 1, "bf16": 2}[w.dtype]
+    state = torch.empty((w.B, w.H, w.d_out, w.d_in), dtype=gd, device=dev)
+    y = torch.empty((w.B, w.H, w.d_out), dtype=tio, device=dev)
+    pdesc = ws.make_desc(w.B, w.H, w.T, w.d_in, w.d_out, io)
+    ddesc = ws.make_desc(w.B, w.H, 1, w.d_in, w.d_out, io)
+
+    # the hand-over from the prefill
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for i in range(2):
+        e0.record(stream)
+        ws._check(L.gl_scan_final_state(ctypes.byref(pdesc), P(pre["x"]), P(pre["g"]),
+                                        P(pre["eta"]), P(pre["alpha"]), P(state), sp))
+        e1.record(stream)
+    torch.cuda.synchronize()
+    final_ms = e0.elapsed_time(e1)
+
+    hand_over = state.clone()
+
+    # every token's call arguments are marshalled before timing starts, so
+    # the timed loop is one C call per launch (Python's argument handling
+    # would otherwise take longer than a decode kernel runs)
+    dp = ctypes.byref(ddesc)
+    a_rd = [(dp, P(dd["x"][k]), P(pre["W0"]), P(state), P(y), sp) for k in range(K)]
+    a_up = [(dp, P(dd["x"][k]), P(dd["g"][k]), P(dd["eta"][k]), P(dd["alpha"][k]), P(state), sp)
+            for k in range(K)]
+    a_st = [None] + [(dp, P(dd["x"][k - 1]), P(dd["g"][k - 1]), P(dd["eta"][k - 1]),
+                      P(dd["alpha"][k - 1]), P(dd["x"][k]), P(pre["W0"]), P(state), P(y), sp)
+                     for k in range(1, K)]
+    f_rd, f_up, f_st = L.gl_decode_readout, L.gl_decode_update, L.gl_decode_step
+    bad = []
+
+    def readout(k):
+        if f_rd(*a_rd[k]):
+            bad.append("readout")
+
+    def update(k):
+        if f_up(*a_up[k]):
+            bad.append("update")
+
+    # tokens are issued back to back, as a serving loop does; one pair of
+    # events brackets the timed tokens (events between kernels would add gaps)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def timed(body):
+        for k in range(1, args.warmup + 1):
+            body(k)
+        e0.record(stream)
+        for k in range(args.warmup + 1, K):
+            body(k)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps
+
+    # the separate calls: readout then update of every token, and each alone
+    mp = timed(lambda k: (readout(k), update(k)))
+    mr = timed(readout)
+    mu = timed(update)
+
+    # the serving loop: token 0's readout, then token k-1's update fused with
+    # token k's readout
+    def fused_step(k):
+        if f_st(*a_st[k]):
+            bad.append("step")
+
+    state.copy_(hand_over)
+    readout(0)
+    ms = timed(fused_step)
+    tot_ms = ms * args.steps
+    if bad:
+        raise RuntimeError(f"decode {bad[0]} call failed: {L.gl_last_error().decode()}")
+    nbytes = decode_bytes(w)[2]
+    achieved = nbytes / 1e9 / (ms / 1e3)
+    fused = w.d_in % 4 == 0 and ((w.d_in // 4) & (w.d_in // 4 - 1)) == 0
+    rec = {
+        "metric": "decode tokens/s (readout + update, every sequence of the batch)",
+        "value": w.B * args.steps / (tot_ms / 1e3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": tot_ms / args.steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {"bf16": "bf16 io / fp32 state", "f32": "f32", "f64": "f64"}[w.dtype],
+        "data": "synthetic (seeded; distributions of the named workload)",
+        "config": {"workload": f"{w.name} decode: B={w.B} sequences, H={w.H}, "
+                               f"d={w.d_in}, state handed over after T={w.T}",
+                   "B": w.B, "H": w.H, "d_in": w.d_in, "d_out": w.d_out, "io": w.dtype,
+                   "parallelism": "single GPU"},
+        "passes_ms": {"step_mean": ms, "separate_readout_plus_update": mp,
+                      "readout_alone": mr, "update_alone": mu, "final_state_ms": final_ms},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM / 1e9,
+                     "unit": "GB/s", "frac": achieved / (PEAK_HBM / 1e9), "traffic": None,
+                     "algorithmic_bytes": nbytes,
+                     "kernel": ("decode_readout_v (fused update + readout)" if fused else
+                                "decode_update + decode_readout") +
+                               "; state cache-resident between tokens"},
+    }
+    if not args.no_cpu:
+        rec["cpu_baseline"] = cpu_decode(w, {**{k: dec[k] for k in ("x", "g", "eta", "alpha")},
+                                             "W0": np.asarray(pre["W0"].double().cpu())})
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -116,6 +295,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-flush", action="store_true", help="do not flush caches between steps")
     ap.add_argument("--generic", action="store_true", help="force the portable VALU kernels")
+    ap.add_argument("--decode", action="store_true",
+                    help="time one-token decode steps (readout + update) instead of the scan")
     ap.add_argument("--segments", type=int, default=0,
                     help="segments per sequence (0 = the library's automatic choice)")
     args = ap.parse_args()
@@ -131,6 +312,8 @@ def main():
     from weight_scans_amd.synth import CONFIGS, make_inputs
 
     w = CONFIGS[args.config]
+    if args.decode:
+        return decode_main(args, w)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     tio = {"f64": torch.float64, "f32": torch.float32, "bf16": torch.bfloat16}[w.dtype]

@@ -112,6 +112,57 @@ gl_status_t gl_scan_bwd(const gl_scan_desc_t* desc, const void* x, const void* g
                         void* deta, void* dalpha, void* dW0, void* ws,
                         size_t ws_bytes, void* stream);
 
+/* ---- Deployment: one token at a time, and the prefill -> decode handoff.
+ *
+ * Once trained, the learner runs serially: for each new token the layer reads
+ * out from its cached weight, the costate g of that token comes back, and the
+ * cache takes one exact gradient step ("Parallelize the Training, Keep the
+ * Learning Serial", cognaptus.com, section "The bottleneck appears before
+ * deployment"; ParaTTT news summary, section "Perspective").  The cache is the
+ * adaptation D = W - W0 of every sequence-head:
+ *
+ *   state                    [B][H][d_out][d_in]  state dtype (fp64 if io is
+ *                                                 F64, else fp32)
+ *
+ * These calls take the same descriptor as the scans (B, H, d_in, d_out,
+ * io_dtype; chunk, flags and segments are ignored) and follow the same rules:
+ * device pointers owned by the caller, 16-byte aligned, outputs must not alias
+ * inputs (gl_decode_update updates `state` in place), asynchronous on
+ * `stream`, every check before any launch, nothing allocated.  B*H == 0 is a
+ * no-op. */
+
+/* Readout of one token against the cache, from the pre-update weight:
+ * y = (W0 + D) x.   x [B][H][d_in] io, W0 [H][d_out][d_in] io,
+ * y [B][H][d_out] io.  desc->T is ignored. */
+gl_status_t gl_decode_readout(const gl_scan_desc_t* desc, const void* x, const void* W0,
+                              const void* state, void* y, void* stream);
+
+/* One exact gradient step of the cache: D <- alpha D - eta g x^T (the scan's
+ * recurrence for one token).  x [B][H][d_in] io, g [B][H][d_out] io,
+ * eta, alpha [B][H] gate dtype.  desc->T is ignored. */
+gl_status_t gl_decode_update(const gl_scan_desc_t* desc, const void* x, const void* g,
+                             const void* eta, const void* alpha, void* state, void* stream);
+
+/* The steady state of serving, fused: the update of the previous token (once
+ * its costate has come back), then the readout of the next one,
+ *   D <- alpha_prev D - eta_prev g_prev x_prev^T;   y = (W0 + D) x,
+ * in one pass over the state where the shape allows (d_in a multiple of 4
+ * with d_in / 4 a power of two), else as gl_decode_update followed by
+ * gl_decode_readout.  x_prev, x [B][H][d_in] io, g_prev [B][H][d_out] io,
+ * eta_prev, alpha_prev [B][H] gate dtype, W0 [H][d_out][d_in] io,
+ * y [B][H][d_out] io; `state` is updated in place.  desc->T is ignored. */
+gl_status_t gl_decode_step(const gl_scan_desc_t* desc, const void* x_prev, const void* g_prev,
+                           const void* eta_prev, const void* alpha_prev, const void* x,
+                           const void* W0, void* state, void* y, void* stream);
+
+/* Hand-over from a prefill of desc->T tokens (the inputs of gl_scan_fwd) to
+ * decoding: writes the adaptation after the last token,
+ * D_T = sum_t (prod_{s>t} alpha_s)(-eta_t) g_t x_t^T, into `state` (zero for
+ * T == 0). */
+gl_status_t gl_scan_final_state(const gl_scan_desc_t* desc, const void* x, const void* g,
+                                const void* eta, const void* alpha, void* state,
+                                void* stream);
+
 /* Static description of a status code. */
 const char* gl_status_string(gl_status_t status);
 

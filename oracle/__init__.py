@@ -11,7 +11,11 @@ the recurrence and the page passages it follows.
 Parity status of each function: ``fwd`` and ``bwd`` are pinned by the CPU tests
 in ``tests/test_oracle.py`` (closed forms, the parallel discounted-sum form,
 torch autograd, finite differences, serial-learner recovery, the causal fixed
-point and the gate-gradient identity).
+point and the gate-gradient identity).  ``final_state``, ``decode_readout`` and
+``decode_update`` (the serial recurrence of ``seq_fwd`` applied per
+sequence-head) are pinned there too: the unrolled discounted sum of the final
+adaptation, hand-computed single steps, and a decode loop that reproduces the
+whole-sequence readouts.
 """
 from __future__ import annotations
 
@@ -118,3 +122,47 @@ def seq_fwd(x, g, eta, alpha, W0, S_init=None):
     _load().oracle_seq_fwd(T, d_in, d_out, _ptr(x), _ptr(g), _ptr(eta),
                            _ptr(alpha), _ptr(W0), _ptr(Si), _ptr(y), _ptr(S))
     return y, S
+
+
+def final_state(x, g, eta, alpha):
+    """Adaptation after the last token of every sequence-head, from zero
+    ([B,H,T,d] inputs -> [B,H,d_out,d_in]); the serial recurrence with W0 = 0."""
+    x, g, eta, alpha = map(_f64, (x, g, eta, alpha))
+    B, H, T, d_in = x.shape
+    d_out = g.shape[-1]
+    out = np.empty((B, H, d_out, d_in), np.float64)
+    Wz = np.zeros((d_out, d_in), np.float64)
+    for b in range(B):
+        for h in range(H):
+            _, out[b, h] = seq_fwd(x[b, h], g[b, h], eta[b, h], alpha[b, h], Wz)
+    return out
+
+
+def decode_readout(x1, W0, S):
+    """One token against the cached adaptation S: y = (W0 + S) x
+    (x1 [B,H,d_in], W0 [H,d_out,d_in], S [B,H,d_out,d_in] -> [B,H,d_out])."""
+    x1, W0, S = map(_f64, (x1, W0, S))
+    B, H, d_in = x1.shape
+    d_out = W0.shape[1]
+    y = np.empty((B, H, d_out), np.float64)
+    for b in range(B):
+        for h in range(H):
+            yt, _ = seq_fwd(x1[b, h][None], np.zeros((1, d_out)), np.zeros(1), np.ones(1),
+                            W0[h], S_init=S[b, h])
+            y[b, h] = yt[0]
+    return y
+
+
+def decode_update(x1, g1, eta1, alpha1, S):
+    """One step of the recurrence on the cached adaptation: returns
+    alpha S - eta g x^T (x1 [B,H,d_in], g1 [B,H,d_out], eta1/alpha1 [B,H])."""
+    x1, g1, eta1, alpha1, S = map(_f64, (x1, g1, eta1, alpha1, S))
+    B, H, d_in = x1.shape
+    d_out = g1.shape[-1]
+    out = np.empty_like(S)
+    Wz = np.zeros((d_out, d_in), np.float64)
+    for b in range(B):
+        for h in range(H):
+            _, out[b, h] = seq_fwd(x1[b, h][None], g1[b, h][None], eta1[b, h][None],
+                                   alpha1[b, h][None], Wz, S_init=S[b, h])
+    return out

@@ -153,3 +153,38 @@ def test_empty_forward_is_a_noop():
         assert _fwd(desc(**kw), [None] * 7) == 0
     # an empty head count needs no dW0 either
     assert _bwd(desc(H=0), [None] * 12, None, 0) == 0
+
+
+def _dec(fn, d, ptrs):
+    P = [ctypes.c_void_p(p) if p is not None else None for p in ptrs]
+    return getattr(ws.lib(), fn)(ctypes.byref(d) if d is not None else None, *P, None)
+
+
+DEC_CALLS = (("gl_decode_readout", 4), ("gl_decode_update", 5), ("gl_decode_step", 8),
+             ("gl_scan_final_state", 5))
+
+
+@pytest.mark.parametrize("fn,nptr", DEC_CALLS)
+def test_decode_argument_errors_before_launch(fn, nptr):
+    ok = [FAKE] * nptr
+    assert _dec(fn, None, ok) == 1
+    for kw, code in ((dict(B=-1), 1), (dict(d_in=0), 1), (dict(io_dtype=5), 1),
+                     (dict(d_out=129), 2), (dict(d_in=200), 2)):
+        assert _dec(fn, desc(**kw), ok) == code, kw
+    for i in range(nptr):
+        p = list(ok)
+        p[i] = None
+        assert _dec(fn, desc(), p) == 1
+        p[i] = FAKE + 4
+        assert _dec(fn, desc(), p) == 3
+    # no sequence-heads: nothing is launched and no pointer is needed
+    assert _dec(fn, desc(B=0), [None] * nptr) == 0
+    assert _dec(fn, desc(H=0), [None] * nptr) == 0
+
+
+def test_decode_ignores_the_scan_only_fields():
+    # chunk / segments / T have no meaning for one token; only the final state
+    # checks T
+    bad_scan = desc(chunk=48, segments=7, T=-3)
+    assert _dec("gl_decode_readout", bad_scan, [None] * 4) == 1  # still needs pointers
+    assert _dec("gl_scan_final_state", bad_scan, [FAKE] * 5) == 1  # negative T

@@ -332,3 +332,53 @@ def test_control_variant_is_caught():
     page = _golden()
     # same order as the printed control discrepancies (0.3757 / 0.6261)
     assert relmax(bad[0][0, 0], tx.grad.numpy()) > 0.1 * page["control_hidden_costates"]
+
+
+# ---- deployment: the cached adaptation ("The bottleneck appears before
+# deployment"; ParaTTT news summary, section "Perspective")
+
+def test_final_state_is_the_discounted_sum():
+    # unrolled: D_T = sum_t (prod_{s>t} alpha_s)(-eta_t) g_t x_t^T
+    inp = small(B=2, H=2, T=37, d_in=5, d_out=3, seed=21, alpha="mix")
+    got = oracle.final_state(inp["x"], inp["g"], inp["eta"], inp["alpha"])
+    a = inp["alpha"]
+    suffix = np.concatenate([np.cumprod(a[..., ::-1], axis=-1)[..., ::-1][..., 1:],
+                             np.ones(a.shape[:-1] + (1,))], axis=-1)
+    w = -suffix * inp["eta"]
+    want = np.einsum("bht,bhtr,bhtc->bhrc", w, inp["g"], inp["x"])
+    assert relmax(got, want) < 1e-13
+    # T = 0: the empty sum; T = 1: one step from zero
+    assert np.all(oracle.final_state(inp["x"][:, :, :0], inp["g"][:, :, :0],
+                                     inp["eta"][:, :, :0], inp["alpha"][:, :, :0]) == 0)
+    one = oracle.final_state(inp["x"][:, :, :1], inp["g"][:, :, :1], inp["eta"][:, :, :1],
+                             inp["alpha"][:, :, :1])
+    assert np.allclose(one[0, 1], -inp["eta"][0, 1, 0] * np.outer(inp["g"][0, 1, 0],
+                                                                    inp["x"][0, 1, 0]))
+
+
+def test_decode_steps_by_hand():
+    S = np.array([[[[1.0, 2.0]]]])        # [B=1,H=1,d_out=1,d_in=2]
+    W0 = np.array([[[0.5, 0.5]]])
+    x1 = np.array([[[1.0, -1.0]]])
+    # (W0 + S) x = 1.5 - 2.5
+    assert np.array_equal(oracle.decode_readout(x1, W0, S), np.array([[[-1.0]]]))
+    # 0.5 S - 2 * 3 * x^T
+    got = oracle.decode_update(x1, np.array([[[3.0]]]), np.array([[2.0]]),
+                               np.array([[0.5]]), S)
+    assert np.array_equal(got, np.array([[[[-5.5, 7.0]]]]))
+
+
+def test_decode_loop_reproduces_the_whole_sequence():
+    # prefill T0 tokens, hand the adaptation over, decode the rest one at a
+    # time: every readout and the last adaptation agree with the whole scan
+    inp = small(B=2, H=2, T=50, d_in=6, d_out=4, seed=22)
+    T0 = 31
+    y_all = oracle.fwd(inp["x"], inp["g"], inp["eta"], inp["alpha"], inp["W0"])
+    S = oracle.final_state(*(inp[k][:, :, :T0] for k in ("x", "g", "eta", "alpha")))
+    for t in range(T0, 50):
+        y_t = oracle.decode_readout(inp["x"][:, :, t], inp["W0"], S)
+        assert relmax(y_t, y_all[:, :, t]) < 1e-13
+        S = oracle.decode_update(inp["x"][:, :, t], inp["g"][:, :, t], inp["eta"][:, :, t],
+                                 inp["alpha"][:, :, t], S)
+    want = oracle.final_state(inp["x"], inp["g"], inp["eta"], inp["alpha"])
+    assert relmax(S, want) < 1e-13

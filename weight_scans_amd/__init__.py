@@ -8,8 +8,14 @@ raises if the library is missing.
     y, saved = gl_scan_fwd(x, g, eta, alpha, W0)
     dx, dg, deta, dalpha, dW0 = gl_scan_bwd(x, g, eta, alpha, W0, dy, saved)
     y = scan(x, g, eta, alpha, W0)          # autograd-aware
+    state = gl_scan_final_state(x, g, eta, alpha)     # prefill -> decode
+    y1 = gl_decode_readout(x1, W0, state)             # one token
+    gl_decode_update(x1, g1, eta1, alpha1, state)     # in place
+    y2 = gl_decode_step(x1, g1, eta1, alpha1, x2, W0, state)  # both, fused
 
-Shapes: x [B,H,T,d_in], g [B,H,T,d_out], eta/alpha [B,H,T], W0 [H,d_out,d_in].
+Shapes: x [B,H,T,d_in], g [B,H,T,d_out], eta/alpha [B,H,T], W0 [H,d_out,d_in];
+one decode token: x1 [B,H,d_in], g1 [B,H,d_out], eta1/alpha1 [B,H];
+state [B,H,d_out,d_in] in the gate dtype.
 """
 from __future__ import annotations
 
@@ -26,6 +32,10 @@ EXPORTS = (
     "gl_status_string",
     "gl_last_error",
     "gl_scan_path_name",
+    "gl_decode_readout",
+    "gl_decode_update",
+    "gl_decode_step",
+    "gl_scan_final_state",
 )
 
 GL_FLAG_GENERIC = 1
@@ -65,7 +75,13 @@ def lib():
         L.gl_scan_workspace_size.argtypes = [pd, I, ps, ps]
         L.gl_scan_fwd.argtypes = [pd] + [P] * 7 + [P, S, P]
         L.gl_scan_bwd.argtypes = [pd] + [P] * 12 + [P, S, P]
-        for f in ("gl_scan_saved_size", "gl_scan_workspace_size", "gl_scan_fwd", "gl_scan_bwd"):
+        L.gl_decode_readout.argtypes = [pd] + [P] * 5
+        L.gl_decode_update.argtypes = [pd] + [P] * 6
+        L.gl_scan_final_state.argtypes = [pd] + [P] * 6
+        L.gl_decode_step.argtypes = [pd] + [P] * 9
+        for f in ("gl_scan_saved_size", "gl_scan_workspace_size", "gl_scan_fwd", "gl_scan_bwd",
+                  "gl_decode_readout", "gl_decode_update", "gl_decode_step",
+                  "gl_scan_final_state"):
             getattr(L, f).restype = ctypes.c_int
         L.gl_status_string.argtypes = [I]
         L.gl_status_string.restype = ctypes.c_char_p
@@ -190,6 +206,98 @@ def gl_scan_bwd(x, g, eta, alpha, W0, dy, saved=None, *, chunk=0, flags=0, segme
                              _ptr(W0), _ptr(dy), _ptr(saved), _ptr(dx), _ptr(dg), _ptr(deta),
                              _ptr(dalpha), _ptr(dW0), _ptr(ws), bws, _stream(x.device)))
     return dx, dg, deta, dalpha, dW0
+
+
+def _check_dec(tensors, gates, state, io_dtype):
+    gd = gate_dtype(io_dtype)
+    for t in tensors:
+        if t.dtype != io_dtype:
+            raise TypeError("x, g and W0 must share the io dtype")
+    for t in gates + (state,):
+        if t.dtype != gd:
+            raise TypeError(f"eta/alpha/state must be {gd}")
+    for t in tensors + gates + (state,):
+        if not t.is_cuda:
+            raise ValueError("all tensors must be on a GPU device")
+        if not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous")
+
+
+def gl_scan_final_state(x, g, eta, alpha):
+    """Adaptation after the last of T prefill tokens, [B,H,d_out,d_in]."""
+    torch = _torch()
+    if x.dim() != 4 or g.dim() != 4:
+        raise ValueError("x and g must be [B,H,T,d]")
+    B, H, T, d_in = x.shape
+    d_out = g.shape[-1]
+    if g.shape[:3] != (B, H, T) or eta.shape != (B, H, T) or alpha.shape != (B, H, T):
+        raise ValueError("shape mismatch between x, g, eta and alpha")
+    state = torch.empty((B, H, d_out, d_in), dtype=gate_dtype(x.dtype), device=x.device)
+    _check_dec((x, g), (eta, alpha), state, x.dtype)
+    desc = make_desc(B, H, T, d_in, d_out, _io_code(x.dtype))
+    _check(lib().gl_scan_final_state(ctypes.byref(desc), _ptr(x), _ptr(g), _ptr(eta),
+                                     _ptr(alpha), _ptr(state), _stream(x.device)))
+    return state
+
+
+def gl_decode_readout(x, W0, state, y=None):
+    """y = (W0 + state) x for one token; x [B,H,d_in] -> y [B,H,d_out]."""
+    torch = _torch()
+    if x.dim() != 3 or state.dim() != 4:
+        raise ValueError("x must be [B,H,d_in] and state [B,H,d_out,d_in]")
+    B, H, d_in = x.shape
+    d_out = state.shape[2]
+    if tuple(state.shape) != (B, H, d_out, d_in) or tuple(W0.shape) != (H, d_out, d_in):
+        raise ValueError("shape mismatch between x, W0 and state")
+    if y is None:
+        y = torch.empty((B, H, d_out), dtype=x.dtype, device=x.device)
+    elif tuple(y.shape) != (B, H, d_out):
+        raise ValueError("y must be [B,H,d_out]")
+    _check_dec((x, W0, y), (), state, x.dtype)
+    desc = make_desc(B, H, 1, d_in, d_out, _io_code(x.dtype))
+    _check(lib().gl_decode_readout(ctypes.byref(desc), _ptr(x), _ptr(W0), _ptr(state), _ptr(y),
+                                   _stream(x.device)))
+    return y
+
+
+def gl_decode_update(x, g, eta, alpha, state):
+    """state <- alpha state - eta g x^T in place for one token; returns state."""
+    if x.dim() != 3 or g.dim() != 3 or state.dim() != 4:
+        raise ValueError("x, g must be [B,H,d] and state [B,H,d_out,d_in]")
+    B, H, d_in = x.shape
+    d_out = g.shape[-1]
+    if (g.shape[:2] != (B, H) or tuple(state.shape) != (B, H, d_out, d_in)
+            or eta.shape != (B, H) or alpha.shape != (B, H)):
+        raise ValueError("shape mismatch between x, g, eta, alpha and state")
+    _check_dec((x, g), (eta, alpha), state, x.dtype)
+    desc = make_desc(B, H, 1, d_in, d_out, _io_code(x.dtype))
+    _check(lib().gl_decode_update(ctypes.byref(desc), _ptr(x), _ptr(g), _ptr(eta), _ptr(alpha),
+                                  _ptr(state), _stream(x.device)))
+    return state
+
+
+def gl_decode_step(x_prev, g_prev, eta_prev, alpha_prev, x, W0, state, y=None):
+    """Update of the previous token, then readout of x; state in place.
+    Returns y [B,H,d_out]."""
+    torch = _torch()
+    if x.dim() != 3 or x_prev.shape != x.shape or state.dim() != 4:
+        raise ValueError("x, x_prev must be [B,H,d_in] and state [B,H,d_out,d_in]")
+    B, H, d_in = x.shape
+    d_out = state.shape[2]
+    if (tuple(state.shape) != (B, H, d_out, d_in) or tuple(W0.shape) != (H, d_out, d_in)
+            or tuple(g_prev.shape) != (B, H, d_out) or eta_prev.shape != (B, H)
+            or alpha_prev.shape != (B, H)):
+        raise ValueError("shape mismatch between the step's tensors")
+    if y is None:
+        y = torch.empty((B, H, d_out), dtype=x.dtype, device=x.device)
+    elif tuple(y.shape) != (B, H, d_out):
+        raise ValueError("y must be [B,H,d_out]")
+    _check_dec((x_prev, g_prev, x, W0, y), (eta_prev, alpha_prev), state, x.dtype)
+    desc = make_desc(B, H, 1, d_in, d_out, _io_code(x.dtype))
+    _check(lib().gl_decode_step(ctypes.byref(desc), _ptr(x_prev), _ptr(g_prev), _ptr(eta_prev),
+                                _ptr(alpha_prev), _ptr(x), _ptr(W0), _ptr(state), _ptr(y),
+                                _stream(x.device)))
+    return y
 
 
 def _make_function():

@@ -9,6 +9,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <initializer_list>
 
 #include "internal.hpp"
 
@@ -202,6 +203,36 @@ hipError_t launch_fwd(const Plan& p, const gls::FwdArgs& a, void* seg_ws, hipStr
   return gls::launch_mfma_fwd(a3, s);
 }
 
+// Checks shared by the deployment calls (the descriptor fields they use).
+gl_status_t check_dec(const gl_scan_desc_t* d, bool need_T) {
+  if (!d) return fail(GL_ERROR_INVALID_VALUE, "desc is NULL");
+  if (d->B < 0 || d->H < 0 || (need_T && d->T < 0))
+    return fail(GL_ERROR_INVALID_VALUE, "negative B/H/T");
+  if (d->d_in < 1 || d->d_out < 1)
+    return fail(GL_ERROR_INVALID_VALUE, "d_in and d_out must be >= 1");
+  if (d->io_dtype < GL_DTYPE_F64 || d->io_dtype > GL_DTYPE_BF16)
+    return fail(GL_ERROR_INVALID_VALUE, "unknown io_dtype %d", d->io_dtype);
+  if (d->d_in > gls::kGenericMaxD || d->d_out > gls::kGenericMaxD)
+    return fail(GL_ERROR_NOT_SUPPORTED, "d_in/d_out above %d", gls::kGenericMaxD);
+  if (d->B * d->H > 0x7fffffffLL) return fail(GL_ERROR_NOT_SUPPORTED, "B*H above 2^31-1");
+  return GL_SUCCESS;
+}
+
+gl_status_t check_ptrs(std::initializer_list<const void*> ps) {
+  for (const void* q : ps) {
+    if (!q) return fail(GL_ERROR_INVALID_VALUE, "NULL input or output pointer");
+    if (misaligned(q)) return fail(GL_ERROR_MISALIGNED, "pointer %p not 16-byte aligned", q);
+  }
+  return GL_SUCCESS;
+}
+
+gls::DecArgs dec_args(const gl_scan_desc_t* d) {
+  gls::DecArgs a{};
+  a.B = d->B; a.H = d->H; a.T = d->T;
+  a.d_in = static_cast<int>(d->d_in); a.d_out = static_cast<int>(d->d_out);
+  return a;
+}
+
 }  // namespace
 
 extern "C" {
@@ -346,6 +377,57 @@ gl_status_t gl_scan_bwd(const gl_scan_desc_t* desc, const void* x, const void* g
   f.alpha_done = p.fused;
   f.eta_done = p.fused;
   return hip_status(gls::launch_finalize(p.io, f, s), "finalize launch");
+}
+
+gl_status_t gl_decode_readout(const gl_scan_desc_t* desc, const void* x, const void* W0,
+                              const void* state, void* y, void* stream) {
+  gl_status_t st = check_dec(desc, false);
+  if (st != GL_SUCCESS || desc->B * desc->H == 0) return st;
+  st = check_ptrs({x, W0, state, y});
+  if (st != GL_SUCCESS) return st;
+  gls::DecArgs a = dec_args(desc);
+  a.x = x; a.W0 = W0; a.state = const_cast<void*>(state); a.y = y;
+  return hip_status(gls::launch_decode_readout(desc->io_dtype, a, static_cast<hipStream_t>(stream)),
+                    "decode readout launch");
+}
+
+gl_status_t gl_decode_update(const gl_scan_desc_t* desc, const void* x, const void* g,
+                             const void* eta, const void* alpha, void* state, void* stream) {
+  gl_status_t st = check_dec(desc, false);
+  if (st != GL_SUCCESS || desc->B * desc->H == 0) return st;
+  st = check_ptrs({x, g, eta, alpha, state});
+  if (st != GL_SUCCESS) return st;
+  gls::DecArgs a = dec_args(desc);
+  a.x = x; a.g = g; a.eta = eta; a.alpha = alpha; a.state = state;
+  return hip_status(gls::launch_decode_update(desc->io_dtype, a, static_cast<hipStream_t>(stream)),
+                    "decode update launch");
+}
+
+gl_status_t gl_decode_step(const gl_scan_desc_t* desc, const void* x_prev, const void* g_prev,
+                           const void* eta_prev, const void* alpha_prev, const void* x,
+                           const void* W0, void* state, void* y, void* stream) {
+  gl_status_t st = check_dec(desc, false);
+  if (st != GL_SUCCESS || desc->B * desc->H == 0) return st;
+  st = check_ptrs({x_prev, g_prev, eta_prev, alpha_prev, x, W0, state, y});
+  if (st != GL_SUCCESS) return st;
+  gls::DecArgs a = dec_args(desc);
+  a.x_prev = x_prev; a.g = g_prev; a.eta = eta_prev; a.alpha = alpha_prev;
+  a.x = x; a.W0 = W0; a.state = state; a.y = y;
+  return hip_status(gls::launch_decode_step(desc->io_dtype, a, static_cast<hipStream_t>(stream)),
+                    "decode step launch");
+}
+
+gl_status_t gl_scan_final_state(const gl_scan_desc_t* desc, const void* x, const void* g,
+                                const void* eta, const void* alpha, void* state,
+                                void* stream) {
+  gl_status_t st = check_dec(desc, true);
+  if (st != GL_SUCCESS || desc->B * desc->H == 0) return st;
+  st = desc->T > 0 ? check_ptrs({x, g, eta, alpha, state}) : check_ptrs({state});
+  if (st != GL_SUCCESS) return st;
+  gls::DecArgs a = dec_args(desc);
+  a.x = x; a.g = g; a.eta = eta; a.alpha = alpha; a.state = state;
+  return hip_status(gls::launch_final_state(desc->io_dtype, a, static_cast<hipStream_t>(stream)),
+                    "final state launch");
 }
 
 const char* gl_status_string(gl_status_t status) {

@@ -75,6 +75,21 @@ struct BwdArgs {
   void* dalpha_out = nullptr;
 };
 
+// Deployment (one token at a time): the cached adaptation `state`
+// [B*H][d_out][d_in] in the compute type.
+struct DecArgs {
+  const void* x;      // readout / update: [B*H][d_in];  final state: [B*H][T][d_in]
+  const void* g;      // update: [B*H][d_out];           final state: [B*H][T][d_out]
+  const void* eta;    // update: [B*H];                  final state: [B*H][T]
+  const void* alpha;  // (as eta)
+  const void* W0;     // readout: [H][d_out][d_in]
+  void* state;
+  void* y;            // readout: [B*H][d_out]
+  const void* x_prev = nullptr;  // step: the previous token's x [B*H][d_in]
+  int64_t B, H, T;
+  int d_in, d_out;
+};
+
 struct FinArgs {
   const void* part_eta;
   const void* part_alpha;
@@ -98,6 +113,10 @@ int generic_default_chunk(int io);
 hipError_t launch_generic_fwd(int io, const FwdArgs& a, hipStream_t s);
 hipError_t launch_generic_bwd(int io, const BwdArgs& a, hipStream_t s);
 hipError_t launch_finalize(int io, const FinArgs& a, hipStream_t s);
+hipError_t launch_decode_readout(int io, const DecArgs& a, hipStream_t s);
+hipError_t launch_decode_update(int io, const DecArgs& a, hipStream_t s);
+hipError_t launch_decode_step(int io, const DecArgs& a, hipStream_t s);
+hipError_t launch_final_state(int io, const DecArgs& a, hipStream_t s);
 
 // Matrix-core kernels: bf16 io, d_in == d_out in {64, 128}, chunk 64.
 constexpr int kMfmaChunk = 64;
