@@ -50,6 +50,8 @@ def state_dtype(io):
     ("bf16", 2, 3, 300, 128, 128),
     ("bf16", 1, 2, 77, 37, 19),      # ragged sizes, a partial last chunk
     ("f32", 1, 1, 5, 1, 128),        # d_in = 1
+    ("f64", 1, 2, 70, 80, 40),       # 6 rows per thread, scalar LDS reads
+    ("f32", 2, 1, 45, 100, 24),      # 8 rows per thread, idle threads
     ("f64", 1, 2, 0, 8, 8),          # no tokens: the zero adaptation
 ])
 def test_final_state_parity(io, B, H, T, d_in, d_out):

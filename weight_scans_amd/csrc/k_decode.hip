@@ -17,8 +17,8 @@
 //
 // All three are bound by moving the d_out x d_in state (fp32, fp64 for fp64
 // io): the readout reads it once, the update reads and writes it.  The final
-// state is a hand-over utility (one work-group per sequence-head and block of
-// rows, tokens from the right in chunks staged through LDS), not tuned.
+// state is a hand-over pass (one work-group per sequence-head and block of
+// rows, tokens from the right in chunks staged through LDS).
 #include <algorithm>
 #include <cstddef>
 
@@ -186,67 +186,134 @@ __global__ __launch_bounds__(kDecThreads) void decode_update_k(DecArgs a) {
 
 // D_T of one sequence-head from zero, one work-group per block of kRT rows
 // (block x: the sequence-head, block y: the row block).  Thread t owns column
-// c = t % d_in of the rows rg, rg + RG, ... of the block (rg = t / d_in,
-// RG = 256 / d_in >= 2; threads with rg >= kRT hold nothing); tokens are taken
-// from the right in chunks of kCT staged in LDS, with the weights
-// w_t = (prod_{s>t} alpha_s)(-eta_t) formed by one thread.
+// c = t % d_in and the RPT = ceil(kRT / RG) consecutive rows from
+// rg RPT of the block (rg = t / d_in, RG = 256 / d_in >= 2; threads with
+// rg >= RG hold nothing).  Tokens are taken from the right in chunks of kCT:
+// each thread keeps its own column of x for the chunk in registers, the g
+// rows of the block, eta and alpha go through LDS, and the next chunk's loads
+// are in flight while this one is folded in.  Every thread forms the weights
+// w_t = (prod_{s>t} alpha_s)(-eta_t) itself from the chunk's gates and the
+// running product of the gates already taken; a short chunk is padded with
+// neutral gates (eta = 0, alpha = 1), so every chunk folds in kCT tokens
+// without branches.  NR accumulators per thread (NR >= RPT); with VEC
+// (RG NR == kRT) a thread's g values of a token are read from LDS as one
+// vector.
 constexpr int kMaxD = 128;
-constexpr int kRT = 16;               // rows per work-group
-constexpr int kMaxRows = kRT / 2;     // rows per thread (RG >= 2)
-constexpr int kCT = 16;               // tokens per staged chunk
+constexpr int kRT = 16;                              // rows per work-group
+constexpr int kCT = 32;                              // tokens per chunk
+constexpr int kGPer = kCT * kRT / kDecThreads;       // g values staged per thread
 
-template <typename IO, typename S>
+// NR consecutive values from 16-byte aligned LDS, 16 bytes per read
+template <int NR>
+__device__ __forceinline__ void lds_row(const float* p, float (&v)[NR]) {
+#pragma unroll
+  for (int i = 0; i < NR / 4; ++i) {
+    const float4 t = reinterpret_cast<const float4*>(p)[i];
+    v[4 * i] = t.x; v[4 * i + 1] = t.y; v[4 * i + 2] = t.z; v[4 * i + 3] = t.w;
+  }
+}
+template <int NR>
+__device__ __forceinline__ void lds_row(const double* p, double (&v)[NR]) {
+#pragma unroll
+  for (int i = 0; i < NR / 2; ++i) {
+    const double2 t = reinterpret_cast<const double2*>(p)[i];
+    v[2 * i] = t.x; v[2 * i + 1] = t.y;
+  }
+}
+
+template <typename IO, typename S, int NR, bool VEC>
 __global__ __launch_bounds__(kDecThreads) void final_state_k(DecArgs a) {
-  __shared__ S xs[kCT][kMaxD], gs[kCT][kRT], ws[kCT];
-  __shared__ S carry;  // prod of alpha over the tokens already taken
+  __shared__ S es[kCT], as[kCT];
+  __shared__ __attribute__((aligned(16))) S gs[kCT][kRT];
   const int64_t bh = blockIdx.x;
   const int r0 = blockIdx.y * kRT;
   const int rows = min(kRT, a.d_out - r0);
   const int tid = threadIdx.x;
   const int64_t T = a.T;
-  const int RG = kDecThreads / a.d_in;
-  const int c = tid % a.d_in, rg = tid / a.d_in;
-  const int nr = rg < min(RG, rows) ? (rows - rg + RG - 1) / RG : 0;  // rows of this thread
-  const IO* x = static_cast<const IO*>(a.x) + bh * T * a.d_in;
+  const int d_in = a.d_in;
+  const int RG = kDecThreads / d_in;
+  const int RPT = (kRT + RG - 1) / RG;
+  const int c = tid % d_in, rg = tid / d_in;
+  // first row of this thread (idle threads fold in row 0 and store nothing)
+  const int rbase = rg < RG ? rg * RPT : 0;
+  const int nrow = rg < RG ? max(0, min(RPT, rows - rbase)) : 0;
+  const IO* x = static_cast<const IO*>(a.x) + bh * T * d_in + c;
   const IO* g = static_cast<const IO*>(a.g) + bh * T * a.d_out + r0;
   const S* eta = static_cast<const S*>(a.eta) + bh * T;
   const S* alpha = static_cast<const S*>(a.alpha) + bh * T;
-  S acc[kMaxRows];
+
+  S xn[kCT], rgv[kGPer], re = S(0), ra = S(1);
+  const auto fetch = [&](int64_t lo, int n) {
+    // padding positions load the chunk's last token (its weight is zero)
 #pragma unroll
-  for (int k = 0; k < kMaxRows; ++k) acc[k] = S(0);
-  if (tid == 0) carry = S(1);
-  for (int64_t hi = T; hi > 0; hi -= kCT) {
-    const int64_t lo = hi - kCT > 0 ? hi - kCT : 0;
-    const int n = static_cast<int>(hi - lo);
-    __syncthreads();  // the previous chunk's reads are done
-    for (int i = tid; i < n * a.d_in; i += kDecThreads)
-      xs[i / a.d_in][i % a.d_in] = load_as<S>(x, lo * a.d_in + i);
-    for (int i = tid; i < n * kRT; i += kDecThreads) {
-      const int j = i / kRT, r = i % kRT;
-      if (r < rows) gs[j][r] = load_as<S>(g, (lo + j) * a.d_out + r);
-    }
-    if (tid == 0) {
-      S p = carry;
-      for (int j = n - 1; j >= 0; --j) {
-        ws[j] = -p * eta[lo + j];
-        p *= alpha[lo + j];
-      }
-      carry = p;
-    }
-    __syncthreads();
-    if (nr > 0) {
-      for (int j = 0; j < n; ++j) {
-        const S wx = ws[j] * xs[j][c];
+    for (int j = 0; j < kCT; ++j) xn[j] = load_as<S>(x, (lo + min(j, n - 1)) * d_in);
 #pragma unroll
-        for (int k = 0; k < kMaxRows; ++k)
-          if (k < nr) acc[k] += wx * gs[j][rg + RG * k];
-      }
+    for (int i = 0; i < kGPer; ++i) {
+      const int idx = tid + i * kDecThreads, j = idx / kRT, r = idx % kRT;
+      rgv[i] = load_as<S>(g, (lo + min(j, n - 1)) * a.d_out + min(r, rows - 1));
     }
+    if (tid < kCT) {
+      re = eta[lo + min(tid, n - 1)];
+      ra = alpha[lo + min(tid, n - 1)];
+    }
+  };
+  const auto stash = [&](int n) {
+#pragma unroll
+    for (int i = 0; i < kGPer; ++i) {
+      const int idx = tid + i * kDecThreads, j = idx / kRT, r = idx % kRT;
+      gs[j][r] = r < rows ? rgv[i] : S(0);
+    }
+    if (tid < kCT) {
+      es[tid] = tid < n ? re : S(0);
+      as[tid] = tid < n ? ra : S(1);
+    }
+  };
+
+  S acc[NR];
+  int grow[NR];  // this thread's rows within the block, clamped into it
+#pragma unroll
+  for (int k = 0; k < NR; ++k) {
+    acc[k] = S(0);
+    grow[k] = min(rbase + k, kRT - 1);
   }
-  S* d = static_cast<S*>(a.state) + (bh * a.d_out + r0) * static_cast<int64_t>(a.d_in);
+  S carry = S(1);  // prod of alpha over the tokens already taken
+  int64_t hi = T, lo = T - kCT > 0 ? T - kCT : 0;
+  if (T > 0) fetch(lo, static_cast<int>(hi - lo));
+  while (hi > 0) {
+    const int n = static_cast<int>(hi - lo);
+    __syncthreads();  // the previous chunk is folded in by every thread
+    stash(n);
+    __syncthreads();
+    S xc[kCT];
 #pragma unroll
-  for (int k = 0; k < kMaxRows; ++k)
-    if (k < nr) d[static_cast<int64_t>(rg + RG * k) * a.d_in + c] = acc[k];
+    for (int j = 0; j < kCT; ++j) xc[j] = xn[j];
+    const int64_t hi2 = lo, lo2 = lo - kCT > 0 ? lo - kCT : 0;
+    if (hi2 > 0) fetch(lo2, static_cast<int>(hi2 - lo2));
+    // every thread folds in NR rows (rows past its own read a valid entry of
+    // the block and are never stored)
+    S p = carry;
+#pragma unroll
+    for (int j = kCT - 1; j >= 0; --j) {
+      const S wx = -p * es[j] * xc[j];
+      if constexpr (VEC) {
+        S gv[NR];
+        lds_row<NR>(&gs[j][rbase], gv);
+#pragma unroll
+        for (int k = 0; k < NR; ++k) acc[k] += wx * gv[k];
+      } else {
+#pragma unroll
+        for (int k = 0; k < NR; ++k) acc[k] += wx * gs[j][grow[k]];
+      }
+      p *= as[j];
+    }
+    carry = p;
+    hi = hi2;
+    lo = lo2;
+  }
+  S* d = static_cast<S*>(a.state) + (bh * a.d_out + r0) * static_cast<int64_t>(d_in);
+#pragma unroll
+  for (int k = 0; k < NR; ++k)
+    if (k < nrow) d[static_cast<int64_t>(rbase + k) * d_in + c] = acc[k];
 }
 
 bool readout_vec(const DecArgs& a) {
@@ -301,7 +368,15 @@ hipError_t step_t(const DecArgs& a, hipStream_t s) {
 template <typename IO, typename S>
 hipError_t final_t(const DecArgs& a, hipStream_t s) {
   const dim3 grid(static_cast<unsigned>(a.B * a.H), (a.d_out + kRT - 1) / kRT);
-  hipLaunchKernelGGL((final_state_k<IO, S>), grid, dim3(kDecThreads), 0, s, a);
+  const int RG = kDecThreads / a.d_in, RPT = (kRT + RG - 1) / RG;
+  if (RG * 8 == kRT)
+    hipLaunchKernelGGL((final_state_k<IO, S, 8, true>), grid, dim3(kDecThreads), 0, s, a);
+  else if (RG * 4 == kRT)
+    hipLaunchKernelGGL((final_state_k<IO, S, 4, true>), grid, dim3(kDecThreads), 0, s, a);
+  else if (RPT > 4)
+    hipLaunchKernelGGL((final_state_k<IO, S, 8, false>), grid, dim3(kDecThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL((final_state_k<IO, S, 4, false>), grid, dim3(kDecThreads), 0, s, a);
   return hipGetLastError();
 }
 
