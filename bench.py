@@ -20,6 +20,12 @@ token's readout), starting from the hand-over state of the named workload's
 prefill (gl_scan_final_state, timed once).  The separate readout and update
 calls are timed too and reported beside it.  The cached adaptation stays on the
 GPU between tokens, as in serving, so no flush runs between decode steps.
+
+With --costate it prints the line of one Picard sweep of costate
+reconstruction under the quadratic token loss: gl_scan_fwd driven by the
+proposed costates, then gl_costate_quadratic (g~ = y - r and the per-token
+consistency residuals), on the named workload, caches flushed between sweeps
+as for the main line.
 """
 from __future__ import annotations
 
@@ -286,6 +292,131 @@ def decode_main(args, w):
     print(json.dumps(rec), flush=True)
 
 
+def costate_bytes(w):
+    """Algorithmic bytes of gl_costate_quadratic: y, r and g^ read once, g~
+    written once, two residuals per token."""
+    e = {"bf16": 2, "f32": 4, "f64": 8}[w.dtype]
+    es = 8 if w.dtype == "f64" else 4
+    n = w.B * w.H * w.T
+    return n * (4 * e * w.d_out + 2 * es)
+
+
+def cpu_costate(w, inp, R, budget_s=10.0):
+    """The oracle's sweep (its serial scan, then the reconstruction) on whole
+    sequence-heads for about budget_s seconds."""
+    import numpy as np
+
+    import oracle
+
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count() or 1
+    cores = max(1, min(cores, 16))
+    G = np.zeros((1, 1, w.T, w.d_out))
+    n, t0 = 0, time.perf_counter()
+    while time.perf_counter() - t0 < budget_s and n < w.B * w.H:
+        b, h = divmod(n, w.H)
+        y = oracle.fwd(inp["x"][b, h][None, None], G, inp["eta"][b, h][None, None],
+                       inp["alpha"][b, h][None, None], inp["W0"][h][None], nthreads=cores)
+        oracle.costate_quadratic(y, R[b, h][None, None], G)
+        n += 1
+    dt = time.perf_counter() - t0
+    return {"value": n * w.T / w.H / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{n} of {w.B * w.H} sequence-heads (T={w.T}, d={w.d_in}), one sweep "
+                      f"(fp64 scan + reconstruction), {dt:.1f} s wall; tokens counted as "
+                      f"sequence-heads*T/H"}
+
+
+def costate_main(args, w):
+    import numpy as np
+    import torch
+
+    import weight_scans_amd as ws
+    from weight_scans_amd.synth import make_inputs, round_to
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    tio = {"f64": torch.float64, "f32": torch.float32, "bf16": torch.bfloat16}[w.dtype]
+    gd = ws.gate_dtype(tio)
+    inp = make_inputs(w)
+    R = round_to(np.random.default_rng(w.seed + 7).standard_normal(inp["g"].shape), w.dtype)
+    t = {k: torch.from_numpy(inp[k]).to(dev, tio) for k in ("x", "W0")}
+    t.update({k: torch.from_numpy(inp[k]).to(dev, gd) for k in ("eta", "alpha")})
+    r = torch.from_numpy(R).to(dev, tio)
+    g = torch.zeros_like(r)
+    g_next = torch.empty_like(r)
+    y = torch.empty_like(r)
+    res_sq = torch.empty((w.B, w.H, w.T), dtype=gd, device=dev)
+    res_max = torch.empty_like(res_sq)
+    io = {"f64": 0, "f32": 1, "bf16": 2}[w.dtype]
+    desc = ws.make_desc(w.B, w.H, w.T, w.d_in, w.d_out, io)
+    fws, _ = ws.workspace_size(desc, False)
+    wsb = torch.empty(max(fws, 16), dtype=torch.uint8, device=dev)
+    flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    L = ws.lib()
+    stream = torch.cuda.current_stream(dev)
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    P = lambda a: ctypes.c_void_p(a.data_ptr())  # noqa: E731
+
+    def sweep(ev=None):
+        nonlocal g, g_next
+        if ev:
+            ev[0].record(stream)
+        ws._check(L.gl_scan_fwd(ctypes.byref(desc), P(t["x"]), P(g), P(t["eta"]), P(t["alpha"]),
+                                P(t["W0"]), P(y), None, P(wsb), fws, sp))
+        if ev:
+            ev[1].record(stream)
+        ws._check(L.gl_costate_quadratic(ctypes.byref(desc), P(y), P(r), P(g), P(g_next),
+                                         P(res_sq), P(res_max), sp))
+        if ev:
+            ev[2].record(stream)
+        g, g_next = g_next, g
+
+    for _ in range(args.warmup):
+        sweep()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        if not args.no_flush:
+            flush_sink = torch.sum(flush)  # noqa: F841
+        sweep(ev[i])
+    torch.cuda.synchronize()
+    tf = [a.elapsed_time(b) for a, b, _ in ev]
+    tc = [b.elapsed_time(c) for _, b, c in ev]
+    mf, mc = sum(tf) / len(tf), sum(tc) / len(tc)
+    tot_ms = sum(tf) + sum(tc)
+    nbytes = costate_bytes(w)
+    achieved = nbytes / 1e9 / (mc / 1e3)
+    rec = {
+        "metric": "tokens/s per Picard sweep (forward scan + costate reconstruction)",
+        "value": w.B * w.T * args.steps / (tot_ms / 1e3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": tot_ms / args.steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {"bf16": "bf16 io / fp32 state", "f32": "f32", "f64": "f64"}[w.dtype],
+        "data": "synthetic (seeded; distributions of the named workload; targets N(0,1))",
+        "config": {"workload": f"{w.name}: [B,H,T,d]=[{w.B},{w.H},{w.T},{w.d_in}] "
+                               f"{w.dtype}, quadratic token loss",
+                   "B": w.B, "H": w.H, "T": w.T, "d_in": w.d_in, "d_out": w.d_out,
+                   "io": w.dtype, "parallelism": "single GPU"},
+        "passes_ms": {"fwd_mean": mf, "costate_mean": mc},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM / 1e9,
+                     "unit": "GB/s", "frac": achieved / (PEAK_HBM / 1e9), "traffic": None,
+                     "algorithmic_bytes": nbytes,
+                     "kernel": "costate_k (the scan's own roofline is the main bench line)"},
+        "last_res_max": float(res_max.max()),
+    }
+    if not args.no_cpu:
+        rec["cpu_baseline"] = cpu_costate(w, inp, R)
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -295,6 +426,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-flush", action="store_true", help="do not flush caches between steps")
     ap.add_argument("--generic", action="store_true", help="force the portable VALU kernels")
+    ap.add_argument("--costate", action="store_true",
+                    help="time Picard sweeps (forward scan + costate reconstruction)")
     ap.add_argument("--decode", action="store_true",
                     help="time one-token decode steps (readout + update) instead of the scan")
     ap.add_argument("--segments", type=int, default=0,
@@ -314,6 +447,8 @@ def main():
     w = CONFIGS[args.config]
     if args.decode:
         return decode_main(args, w)
+    if args.costate:
+        return costate_main(args, w)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     tio = {"f64": torch.float64, "f32": torch.float32, "bf16": torch.bfloat16}[w.dtype]

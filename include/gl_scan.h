@@ -163,6 +163,27 @@ gl_status_t gl_scan_final_state(const gl_scan_desc_t* desc, const void* x, const
                                 const void* eta, const void* alpha, void* state,
                                 void* stream);
 
+/* ---- Costate reconstruction and the consistency residual.
+ *
+ * GradLev trains proposed costates g^ toward the costates the model
+ * reconstructs on the trajectory they propose ("Parallelize the Training, Keep
+ * the Learning Serial", cognaptus.com, section "The predictor is constrained by
+ * the learner it is supposed to reproduce").  For the quadratic token loss
+ * l_t = |y_t - r_t|^2 / 2 of the pages' synthetic test, with y the output of
+ * gl_scan_fwd driven by g^:
+ *
+ *   g~_t = y_t - r_t,  res_sq_t = |g^_t - g~_t|^2,  res_max_t = max |g^_t - g~_t|
+ *
+ * y, target, g_hat, g_tilde [B][H][T][d_out] io; res_sq, res_max [B][H][T]
+ * gate dtype.  The residuals are taken with g~ in the gate dtype, before it
+ * is rounded to io.  Sweeping g^ <- g~ (scan, then this call) is the Picard
+ * iteration of the causal map, whose unique fixed point is the serial
+ * learner's costate trajectory.  Same descriptor (d_in, chunk, flags and
+ * segments are not used) and rules as the scans; B*H*T == 0 is a no-op. */
+gl_status_t gl_costate_quadratic(const gl_scan_desc_t* desc, const void* y, const void* target,
+                                 const void* g_hat, void* g_tilde, void* res_sq, void* res_max,
+                                 void* stream);
+
 /* Static description of a status code. */
 const char* gl_status_string(gl_status_t status);
 

@@ -15,7 +15,11 @@ point and the gate-gradient identity).  ``final_state``, ``decode_readout`` and
 ``decode_update`` (the serial recurrence of ``seq_fwd`` applied per
 sequence-head) are pinned there too: the unrolled discounted sum of the final
 adaptation, hand-computed single steps, and a decode loop that reproduces the
-whole-sequence readouts.
+whole-sequence readouts.  ``serial_learner`` (the closed-loop learner of the
+synthetic test) is pinned by the exact-recovery test (the open-loop C scan
+driven by its costates reproduces its outputs, at the rounding scale the
+pages print) and the causal fixed-point test; ``costate_quadratic`` by
+hand-computed values and by vanishing at the serial learner's costates.
 """
 from __future__ import annotations
 
@@ -166,3 +170,32 @@ def decode_update(x1, g1, eta1, alpha1, S):
             _, out[b, h] = seq_fwd(x1[b, h][None], g1[b, h][None], eta1[b, h][None],
                                    alpha1[b, h][None], Wz, S_init=S[b, h])
     return out
+
+
+def serial_learner(X, R, eta, alpha, W0):
+    """The ordinary serial learner of one sequence-head under the quadratic
+    token loss |y_t - r_t|^2 / 2 ("Parallelize the Training, Keep the Learning
+    Serial", section "The synthetic test checks the mechanism, not model
+    quality"): each token reads out from the current weight, takes its own
+    costate g_t = y_t - r_t and updates at once.  Returns (Y [T,d_out],
+    G [T,d_out])."""
+    X, R, eta, alpha, W0 = map(_f64, (X, R, eta, alpha, W0))
+    D = np.zeros_like(W0)
+    Y = np.empty((X.shape[0], W0.shape[0]))
+    G = np.empty_like(Y)
+    for t in range(X.shape[0]):
+        Y[t] = (W0 + D) @ X[t]
+        G[t] = Y[t] - R[t]
+        D = alpha[t] * D - eta[t] * np.outer(G[t], X[t])
+    return Y, G
+
+
+def costate_quadratic(y, target, g_hat):
+    """Reconstructed costates under the quadratic token loss and the
+    consistency residual per token (section "The predictor is constrained by
+    the learner it is supposed to reproduce"): g~ = y - target,
+    res_sq = sum_r (g^ - g~)^2, res_max = max_r |g^ - g~|."""
+    y, target, g_hat = map(_f64, (y, target, g_hat))
+    g_tilde = y - target
+    e = g_hat - g_tilde
+    return g_tilde, np.sum(e * e, axis=-1), np.max(np.abs(e), axis=-1, initial=0.0)

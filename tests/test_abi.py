@@ -161,7 +161,7 @@ def _dec(fn, d, ptrs):
 
 
 DEC_CALLS = (("gl_decode_readout", 4), ("gl_decode_update", 5), ("gl_decode_step", 8),
-             ("gl_scan_final_state", 5))
+             ("gl_scan_final_state", 5), ("gl_costate_quadratic", 6))
 
 
 @pytest.mark.parametrize("fn,nptr", DEC_CALLS)

@@ -220,20 +220,6 @@ def _golden():
     return vals
 
 
-def _closed_loop_learner(X, R, eta, alpha, W0):
-    """Ordinary serial learner with token loss 0.5 |y_t - r_t|^2: it computes
-    its own costate g_t = y_t - r_t and updates immediately."""
-    D = np.zeros_like(W0)
-    Y, G = [], []
-    for t in range(X.shape[0]):
-        y = (W0 + D) @ X[t]
-        g = y - R[t]
-        D = alpha[t] * D - eta[t] * np.outer(g, X[t])
-        Y.append(y)
-        G.append(g)
-    return np.array(Y), np.array(G)
-
-
 def test_exact_recovery_of_serial_learner():
     """Supplying the serial learner's own costates G* to the open-loop scan
     reproduces its outputs, and the costates reconstructed from those outputs
@@ -242,7 +228,7 @@ def test_exact_recovery_of_serial_learner():
     inp = small(T=200, d_in=16, d_out=16, seed=61, alpha="mix")
     X, eta, alpha, W0 = inp["x"][0, 0], inp["eta"][0, 0], inp["alpha"][0, 0], inp["W0"][0]
     R = np.random.default_rng(62).standard_normal((200, 16))
-    Y_star, G_star = _closed_loop_learner(X, R, eta, alpha, W0)
+    Y_star, G_star = oracle.serial_learner(X, R, eta, alpha, W0)
     y = oracle.fwd(X[None, None], G_star[None, None], eta[None, None],
                    alpha[None, None], W0[None])[0, 0]
     g_rec = y - R
@@ -266,7 +252,7 @@ def test_causal_fixed_point_iteration():
     inp["eta"][:] = 0.5  # strong coupling so that the iterates really differ
     eta = inp["eta"][0, 0]
     R = np.random.default_rng(72).standard_normal((T, 5))
-    _, G_star = _closed_loop_learner(X, R, eta, alpha, W0)
+    _, G_star = oracle.serial_learner(X, R, eta, alpha, W0)
     G = np.zeros_like(G_star)
     for k in range(1, T + 1):
         y = oracle.fwd(X[None, None], G[None, None], eta[None, None],
@@ -382,3 +368,35 @@ def test_decode_loop_reproduces_the_whole_sequence():
                                  inp["alpha"][:, :, t], S)
     want = oracle.final_state(inp["x"], inp["g"], inp["eta"], inp["alpha"])
     assert relmax(S, want) < 1e-13
+
+
+# ---- costate reconstruction under the quadratic token loss ("The predictor
+# is constrained by the learner it is supposed to reproduce")
+
+def test_costate_quadratic_by_hand():
+    y = np.array([[[[1.0, -2.0], [0.5, 0.5]]]])       # [1,1,T=2,d=2]
+    r = np.array([[[[0.0, -1.0], [1.5, 0.5]]]])
+    gh = np.array([[[[1.0, 0.0], [0.0, 0.0]]]])
+    gt, sq, mx = oracle.costate_quadratic(y, r, gh)
+    assert np.array_equal(gt, np.array([[[[1.0, -1.0], [-1.0, 0.0]]]]))
+    # token 0: (0, 1) -> 1, 1; token 1: (1, 0) -> 1, 1
+    assert np.array_equal(sq, np.array([[[1.0, 1.0]]]))
+    assert np.array_equal(mx, np.array([[[1.0, 1.0]]]))
+
+
+def test_costate_vanishes_at_the_serial_learner():
+    # proposing the serial learner's own costates, the scan reproduces its
+    # outputs and the reconstruction returns the proposal: residual ~ 0; a
+    # perturbed proposal does not
+    inp = small(T=64, d_in=12, d_out=12, seed=91, alpha="mix")
+    X, eta, alpha, W0 = inp["x"][0, 0], inp["eta"][0, 0], inp["alpha"][0, 0], inp["W0"][0]
+    R = np.random.default_rng(92).standard_normal((64, 12))
+    _, G = oracle.serial_learner(X, R, eta, alpha, W0)
+    y = oracle.fwd(X[None, None], G[None, None], eta[None, None], alpha[None, None], W0[None])
+    gt, sq, mx = oracle.costate_quadratic(y, R[None, None], G[None, None])
+    assert np.max(mx) < 1e-12 and np.max(sq) < 1e-24
+    G2 = G.copy()
+    G2[10] += 0.1
+    y2 = oracle.fwd(X[None, None], G2[None, None], eta[None, None], alpha[None, None], W0[None])
+    _, _, mx2 = oracle.costate_quadratic(y2, R[None, None], G2[None, None])
+    assert mx2[0, 0, 10] > 0.09 and np.max(mx2[0, 0, :10]) < 1e-12  # causal: earlier tokens unmoved

@@ -12,6 +12,8 @@ raises if the library is missing.
     y1 = gl_decode_readout(x1, W0, state)             # one token
     gl_decode_update(x1, g1, eta1, alpha1, state)     # in place
     y2 = gl_decode_step(x1, g1, eta1, alpha1, x2, W0, state)  # both, fused
+    g_t, res_sq, res_max = gl_costate_quadratic(y, target, g_hat)  # quadratic loss
+    g, y, sweeps = picard(x, eta, alpha, W0, target)   # fixed point of g -> g~
 
 Shapes: x [B,H,T,d_in], g [B,H,T,d_out], eta/alpha [B,H,T], W0 [H,d_out,d_in];
 one decode token: x1 [B,H,d_in], g1 [B,H,d_out], eta1/alpha1 [B,H];
@@ -36,6 +38,7 @@ EXPORTS = (
     "gl_decode_update",
     "gl_decode_step",
     "gl_scan_final_state",
+    "gl_costate_quadratic",
 )
 
 GL_FLAG_GENERIC = 1
@@ -79,9 +82,10 @@ def lib():
         L.gl_decode_update.argtypes = [pd] + [P] * 6
         L.gl_scan_final_state.argtypes = [pd] + [P] * 6
         L.gl_decode_step.argtypes = [pd] + [P] * 9
+        L.gl_costate_quadratic.argtypes = [pd] + [P] * 7
         for f in ("gl_scan_saved_size", "gl_scan_workspace_size", "gl_scan_fwd", "gl_scan_bwd",
                   "gl_decode_readout", "gl_decode_update", "gl_decode_step",
-                  "gl_scan_final_state"):
+                  "gl_scan_final_state", "gl_costate_quadratic"):
             getattr(L, f).restype = ctypes.c_int
         L.gl_status_string.argtypes = [I]
         L.gl_status_string.restype = ctypes.c_char_p
@@ -298,6 +302,48 @@ def gl_decode_step(x_prev, g_prev, eta_prev, alpha_prev, x, W0, state, y=None):
                                 _ptr(alpha_prev), _ptr(x), _ptr(W0), _ptr(state), _ptr(y),
                                 _stream(x.device)))
     return y
+
+
+def gl_costate_quadratic(y, target, g_hat, g_tilde=None):
+    """Reconstructed costates g~ = y - target and the per-token consistency
+    residuals (|g^ - g~|^2, max |g^ - g~|) for the quadratic token loss."""
+    torch = _torch()
+    if y.dim() != 4 or target.shape != y.shape or g_hat.shape != y.shape:
+        raise ValueError("y, target and g_hat must be [B,H,T,d_out] of one shape")
+    B, H, T, d_out = y.shape
+    if g_tilde is None:
+        g_tilde = torch.empty_like(y)
+    elif g_tilde.shape != y.shape:
+        raise ValueError("g_tilde must have the shape of y")
+    gd = gate_dtype(y.dtype)
+    res_sq = torch.empty((B, H, T), dtype=gd, device=y.device)
+    res_max = torch.empty((B, H, T), dtype=gd, device=y.device)
+    _check_dec((y, target, g_hat, g_tilde), (res_sq, res_max), res_max, y.dtype)
+    desc = make_desc(B, H, T, 1, d_out, _io_code(y.dtype))
+    _check(lib().gl_costate_quadratic(ctypes.byref(desc), _ptr(y), _ptr(target), _ptr(g_hat),
+                                      _ptr(g_tilde), _ptr(res_sq), _ptr(res_max),
+                                      _stream(y.device)))
+    return g_tilde, res_sq, res_max
+
+
+def picard(x, eta, alpha, W0, target, g0=None, max_sweeps=None, tol=0.0):
+    """Picard iteration of the causal costate map for the quadratic token loss:
+    g <- y(g) - target, y(g) = gl_scan_fwd(x, g, ...), from g0 (zero by
+    default), until the largest residual is <= tol or max_sweeps (default T)
+    sweeps have run.  Returns (g, y, sweeps, res_max of the last sweep)."""
+    torch = _torch()
+    B, H, T, _ = x.shape
+    g = torch.zeros_like(target) if g0 is None else g0.clone()
+    g_next = torch.empty_like(g)
+    n = T if max_sweeps is None else max_sweeps
+    y, res_max, k = None, None, 0
+    for k in range(1, n + 1):
+        y, _ = gl_scan_fwd(x, g, eta, alpha, W0, save=False)
+        _, _, res_max = gl_costate_quadratic(y, target, g, g_tilde=g_next)
+        g, g_next = g_next, g
+        if float(res_max.max()) <= tol:
+            break
+    return g, y, k, res_max
 
 
 def _make_function():

@@ -430,6 +430,22 @@ gl_status_t gl_scan_final_state(const gl_scan_desc_t* desc, const void* x, const
                     "final state launch");
 }
 
+gl_status_t gl_costate_quadratic(const gl_scan_desc_t* desc, const void* y, const void* target,
+                                 const void* g_hat, void* g_tilde, void* res_sq, void* res_max,
+                                 void* stream) {
+  gl_status_t st = check_dec(desc, true);
+  if (st != GL_SUCCESS || desc->B * desc->H * desc->T == 0) return st;
+  st = check_ptrs({y, target, g_hat, g_tilde, res_sq, res_max});
+  if (st != GL_SUCCESS) return st;
+  gls::CostArgs a;
+  a.y = y; a.target = target; a.g_hat = g_hat; a.g_tilde = g_tilde;
+  a.res_sq = res_sq; a.res_max = res_max;
+  a.rows = desc->B * desc->H * desc->T;
+  a.d_out = static_cast<int>(desc->d_out);
+  return hip_status(gls::launch_costate(desc->io_dtype, a, static_cast<hipStream_t>(stream)),
+                    "costate launch");
+}
+
 const char* gl_status_string(gl_status_t status) {
   switch (status) {
     case GL_SUCCESS: return "success";

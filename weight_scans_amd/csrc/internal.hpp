@@ -90,6 +90,19 @@ struct DecArgs {
   int d_in, d_out;
 };
 
+// Costate reconstruction under the quadratic token loss: rows = B*H*T token
+// rows of d_out elements.
+struct CostArgs {
+  const void* y;       // [rows][d_out] io
+  const void* target;  // [rows][d_out] io
+  const void* g_hat;   // [rows][d_out] io
+  void* g_tilde;       // [rows][d_out] io
+  void* res_sq;        // [rows] compute type
+  void* res_max;       // [rows] compute type
+  int64_t rows;
+  int d_out;
+};
+
 struct FinArgs {
   const void* part_eta;
   const void* part_alpha;
@@ -117,6 +130,7 @@ hipError_t launch_decode_readout(int io, const DecArgs& a, hipStream_t s);
 hipError_t launch_decode_update(int io, const DecArgs& a, hipStream_t s);
 hipError_t launch_decode_step(int io, const DecArgs& a, hipStream_t s);
 hipError_t launch_final_state(int io, const DecArgs& a, hipStream_t s);
+hipError_t launch_costate(int io, const CostArgs& a, hipStream_t s);
 
 // Matrix-core kernels: bf16 io, d_in == d_out in {64, 128}, chunk 64.
 constexpr int kMfmaChunk = 64;
