@@ -26,6 +26,10 @@ reconstruction under the quadratic token loss: gl_scan_fwd driven by the
 proposed costates, then gl_costate_quadratic (g~ = y - r and the per-token
 consistency residuals), on the named workload, caches flushed between sweeps
 as for the main line.
+
+With --qkv it prints the line of the transpose read z_t = (W0 + D_t)^T u_t
+(gl_scan_qkv_fwd with q = u, k = g, v = x, W0 transposed) on the named
+workload, caches flushed between steps; its roofline is the vector ALU.
 """
 from __future__ import annotations
 
@@ -417,6 +421,98 @@ def costate_main(args, w):
     print(json.dumps(rec), flush=True)
 
 
+PEAK_VALU = {"bf16": 157.3e12, "f32": 157.3e12, "f64": 78.6e12}  # vector flop/s
+
+
+def qkv_main(args, w):
+    import numpy as np
+    import torch
+
+    import oracle
+    import weight_scans_amd as ws
+    from weight_scans_amd.synth import make_inputs
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    tio = {"f64": torch.float64, "f32": torch.float32, "bf16": torch.bfloat16}[w.dtype]
+    gd = ws.gate_dtype(tio)
+    inp = make_inputs(w)
+    t = {k: torch.from_numpy(inp[k]).to(dev, tio) for k in ("x", "g", "W0", "dy")}
+    t.update({k: torch.from_numpy(inp[k]).to(dev, gd) for k in ("eta", "alpha")})
+    z = torch.empty_like(t["x"])
+    io = {"f64": 0, "f32": 1, "bf16": 2}[w.dtype]
+    # transpose read: q = u (length d_out), k = g, v = x (length d_in)
+    desc = ws.make_desc(w.B, w.H, w.T, w.d_out, w.d_in, io)
+    flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    L = ws.lib()
+    stream = torch.cuda.current_stream(dev)
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    P = lambda a: ctypes.c_void_p(a.data_ptr())  # noqa: E731
+
+    def step():
+        ws._check(L.gl_scan_qkv_fwd(ctypes.byref(desc), P(t["dy"]), P(t["g"]), P(t["x"]),
+                                    P(t["eta"]), P(t["alpha"]), P(t["W0"]), 1, P(z), sp))
+
+    for _ in range(args.warmup):
+        step()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        if not args.no_flush:
+            flush_sink = torch.sum(flush)  # noqa: F841
+        ev[i][0].record(stream)
+        step()
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    ts = [a.elapsed_time(b) for a, b in ev]
+    ms = sum(ts) / len(ts)
+    # 4 d_in d_out flops per token and head: the readout's and the rank-one
+    # update's multiply-adds
+    nflops = 4 * w.B * w.H * w.T * w.d_in * w.d_out
+    achieved = nflops / 1e12 / (ms / 1e3)
+    peak = PEAK_VALU[w.dtype] / 1e12
+    rec = {
+        "metric": "tokens/s (transpose read of the adapted weight)",
+        "value": w.B * w.T / (ms / 1e3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {"bf16": "bf16 io / fp32 state", "f32": "f32", "f64": "f64"}[w.dtype],
+        "data": "synthetic (seeded; distributions of the named workload; u ~ the dy draw)",
+        "config": {"workload": f"{w.name}: [B,H,T,d]=[{w.B},{w.H},{w.T},{w.d_in}] "
+                               f"{w.dtype}, z_t = (W0 + D_t)^T u_t",
+                   "B": w.B, "H": w.H, "T": w.T, "d_in": w.d_in, "d_out": w.d_out,
+                   "io": w.dtype, "parallelism": "single GPU"},
+        "roofline": {"bound": "alu", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+                     "frac": achieved / peak, "traffic": None, "algorithmic_flops": nflops,
+                     "kernel": "qkv_fwd_k (tokens in order, rows across lanes)"},
+    }
+    if not args.no_cpu:
+        try:
+            cores = len(os.sched_getaffinity(0))
+        except AttributeError:
+            cores = os.cpu_count() or 1
+        W0T = np.ascontiguousarray(np.transpose(inp["W0"], (0, 2, 1)))
+        n, t0 = 0, time.perf_counter()
+        while time.perf_counter() - t0 < 10.0 and n < w.B * w.H:
+            b, h = divmod(n, w.H)
+            sl = lambda k: inp[k][b:b + 1, h:h + 1]  # noqa: E731
+            oracle.qkv_fwd(sl("dy"), sl("g"), sl("x"), sl("eta"), sl("alpha"), W0T[h:h + 1])
+            n += 1
+        dt = time.perf_counter() - t0
+        rec["cpu_baseline"] = {"value": n * w.T / w.H / dt, "unit": "tokens/s", "cores": 1,
+                               "kind": "oracle",
+                               "sample": f"{n} of {w.B * w.H} sequence-heads (T={w.T}), fp64 "
+                                         f"numpy loop, {dt:.1f} s wall; tokens counted as "
+                                         f"sequence-heads*T/H"}
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -426,6 +522,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-flush", action="store_true", help="do not flush caches between steps")
     ap.add_argument("--generic", action="store_true", help="force the portable VALU kernels")
+    ap.add_argument("--qkv", action="store_true",
+                    help="time the transpose read (scan with its own read vector and key)")
     ap.add_argument("--costate", action="store_true",
                     help="time Picard sweeps (forward scan + costate reconstruction)")
     ap.add_argument("--decode", action="store_true",
@@ -449,6 +547,8 @@ def main():
         return decode_main(args, w)
     if args.costate:
         return costate_main(args, w)
+    if args.qkv:
+        return qkv_main(args, w)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     tio = {"f64": torch.float64, "f32": torch.float32, "bf16": torch.bfloat16}[w.dtype]

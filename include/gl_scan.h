@@ -184,6 +184,26 @@ gl_status_t gl_costate_quadratic(const gl_scan_desc_t* desc, const void* y, cons
                                  const void* g_hat, void* g_tilde, void* res_sq, void* res_max,
                                  void* stream);
 
+/* ---- The scan with its own read vector and write key.
+ *
+ *   y_t = (W0' + D_t) q_t,   D_{t+1} = alpha_t D_t - eta_t v_t k_t^T,  D_0 = 0
+ *
+ * per sequence-head, tokens in order; gl_scan_fwd is the case q = k = x,
+ * v = g.  With q = u, k = g, v = x and W0' = W0^T it is the transpose read
+ * (W0 + D_t)^T u_t that carries a hidden costate back through an adapted
+ * layer ("Parallelize the Training, Keep the Learning Serial", cognaptus.com,
+ * section "The synthetic test checks the mechanism, not model quality"); with
+ * q = x, k = x_bar, v = g a write key of its own (section "Once the gradient
+ * signals are known, the weight trajectory becomes parallelizable").
+ * desc->d_in = dk (length of q and k), desc->d_out = dv (length of v and y);
+ * chunk, flags and segments are not used.  q, k [B][H][T][dk] io,
+ * v, y [B][H][T][dv] io, eta, alpha [B][H][T] gate dtype, W0 [H][dv][dk] io,
+ * or [H][dk][dv] when w0_transposed != 0.  Same rules as gl_scan_fwd;
+ * B*H*T == 0 is a no-op. */
+gl_status_t gl_scan_qkv_fwd(const gl_scan_desc_t* desc, const void* q, const void* k,
+                            const void* v, const void* eta, const void* alpha, const void* W0,
+                            int w0_transposed, void* y, void* stream);
+
 /* Static description of a status code. */
 const char* gl_status_string(gl_status_t status);
 

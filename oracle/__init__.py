@@ -20,6 +20,10 @@ synthetic test) is pinned by the exact-recovery test (the open-loop C scan
 driven by its costates reproduces its outputs, at the rounding scale the
 pages print) and the causal fixed-point test; ``costate_quadratic`` by
 hand-computed values and by vanishing at the serial learner's costates.
+``qkv_fwd`` (read vector q and write key k of their own) is pinned by
+reducing to ``fwd`` when q = k = x, by the transpose read against the
+adaptation states of ``seq_fwd``, and by the unrolled discounted sum for a
+separate write key.
 """
 from __future__ import annotations
 
@@ -199,3 +203,24 @@ def costate_quadratic(y, target, g_hat):
     g_tilde = y - target
     e = g_hat - g_tilde
     return g_tilde, np.sum(e * e, axis=-1), np.max(np.abs(e), axis=-1, initial=0.0)
+
+
+def qkv_fwd(q, k, v, eta, alpha, W0p):
+    """The scan with its own read vector and write key, token by token:
+    y_t = (W0' + D_t) q_t, D_{t+1} = alpha_t D_t - eta_t v_t k_t^T, D_0 = 0
+    (q, k [B,H,T,dk], v [B,H,T,dv], W0p [H,dv,dk] -> y [B,H,T,dv]).  With
+    q = k = x, v = g it is the forward scan; with q = u, k = g, v = x and
+    W0p = W0^T the transpose read (W0 + D_t)^T u_t ("Parallelize the Training,
+    Keep the Learning Serial", section "The synthetic test checks the
+    mechanism, not model quality")."""
+    q, k, v, eta, alpha, W0p = map(_f64, (q, k, v, eta, alpha, W0p))
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    y = np.empty((B, H, T, dv))
+    for b in range(B):
+        for h in range(H):
+            D = np.zeros((dv, dk))
+            for t in range(T):
+                y[b, h, t] = (W0p[h] + D) @ q[b, h, t]
+                D = alpha[b, h, t] * D - eta[b, h, t] * np.outer(v[b, h, t], k[b, h, t])
+    return y

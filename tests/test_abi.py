@@ -164,6 +164,24 @@ DEC_CALLS = (("gl_decode_readout", 4), ("gl_decode_update", 5), ("gl_decode_step
              ("gl_scan_final_state", 5), ("gl_costate_quadratic", 6))
 
 
+def test_qkv_argument_errors_before_launch():
+    L = ws.lib()
+    P = lambda p: ctypes.c_void_p(p) if p is not None else None  # noqa: E731
+    ok = [FAKE] * 6
+    call = lambda d, ptrs, yp=FAKE: L.gl_scan_qkv_fwd(  # noqa: E731
+        ctypes.byref(d), *[P(p) for p in ptrs], 0, P(yp), None)
+    for i in range(6):
+        p = list(ok)
+        p[i] = None
+        assert call(desc(), p) == 1
+        p[i] = FAKE + 8
+        assert call(desc(), p) == 3
+    assert call(desc(), ok, None) == 1
+    assert call(desc(d_in=129), ok) == 2
+    assert call(desc(T=-1), ok) == 1
+    assert call(desc(T=0), [None] * 6, None) == 0
+
+
 @pytest.mark.parametrize("fn,nptr", DEC_CALLS)
 def test_decode_argument_errors_before_launch(fn, nptr):
     ok = [FAKE] * nptr

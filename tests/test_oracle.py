@@ -400,3 +400,43 @@ def test_costate_vanishes_at_the_serial_learner():
     y2 = oracle.fwd(X[None, None], G2[None, None], eta[None, None], alpha[None, None], W0[None])
     _, _, mx2 = oracle.costate_quadratic(y2, R[None, None], G2[None, None])
     assert mx2[0, 0, 10] > 0.09 and np.max(mx2[0, 0, :10]) < 1e-12  # causal: earlier tokens unmoved
+
+
+# ---- the scan with its own read vector and write key (transpose read and
+# write-key readings; "The synthetic test checks the mechanism, not model
+# quality", "Once the gradient signals are known...")
+
+def test_qkv_reduces_to_the_forward_scan():
+    inp = small(B=2, H=2, T=40, d_in=6, d_out=5, seed=101, alpha="mix")
+    want = oracle.fwd(inp["x"], inp["g"], inp["eta"], inp["alpha"], inp["W0"])
+    got = oracle.qkv_fwd(inp["x"], inp["x"], inp["g"], inp["eta"], inp["alpha"], inp["W0"])
+    assert relmax(got, want) < 1e-13
+
+
+def test_transpose_read_against_the_adaptation_states():
+    # z_t = (W0 + D_t)^T u_t with D_t taken from the serial recurrence of the
+    # C oracle on the prefix [0, t)
+    inp = small(T=20, d_in=6, d_out=4, seed=102)
+    X, G, e, a = (inp[k][0, 0] for k in ("x", "g", "eta", "alpha"))
+    W0 = inp["W0"][0]
+    U = np.random.default_rng(103).standard_normal((20, 4))
+    z = oracle.qkv_fwd(U[None, None], G[None, None], X[None, None], e[None, None], a[None, None],
+                       W0.T[None])[0, 0]
+    for t in range(20):
+        _, D = oracle.seq_fwd(X[:t], G[:t], e[:t], a[:t], W0)
+        assert np.max(np.abs(z[t] - (W0 + D).T @ U[t])) < 1e-13
+
+
+def test_write_key_closed_form():
+    # y_t = W0 x_t + sum_{s<t} (prod_{s<u<t} alpha_u)(-eta_s) g_s (xbar_s . x_t)
+    inp = small(T=30, d_in=5, d_out=3, seed=104, alpha="mix")
+    X, G, e, a = (inp[k][0, 0] for k in ("x", "g", "eta", "alpha"))
+    W0 = inp["W0"][0]
+    Xb = X - X.mean(axis=0)  # a centered key
+    y = oracle.qkv_fwd(X[None, None], Xb[None, None], G[None, None], e[None, None],
+                       a[None, None], W0[None])[0, 0]
+    for t in range(30):
+        want = W0 @ X[t]
+        for s_ in range(t):
+            want = want + np.prod(a[s_ + 1:t]) * (-e[s_]) * G[s_] * (Xb[s_] @ X[t])
+        assert np.max(np.abs(y[t] - want)) < 1e-13

@@ -14,6 +14,8 @@ raises if the library is missing.
     y2 = gl_decode_step(x1, g1, eta1, alpha1, x2, W0, state)  # both, fused
     g_t, res_sq, res_max = gl_costate_quadratic(y, target, g_hat)  # quadratic loss
     g, y, sweeps = picard(x, eta, alpha, W0, target)   # fixed point of g -> g~
+    y = gl_scan_qkv_fwd(q, k, v, eta, alpha, W0)       # read vector != write key
+    z = transpose_read(u, g, x, eta, alpha, W0)       # (W0 + D_t)^T u_t
 
 Shapes: x [B,H,T,d_in], g [B,H,T,d_out], eta/alpha [B,H,T], W0 [H,d_out,d_in];
 one decode token: x1 [B,H,d_in], g1 [B,H,d_out], eta1/alpha1 [B,H];
@@ -39,6 +41,7 @@ EXPORTS = (
     "gl_decode_step",
     "gl_scan_final_state",
     "gl_costate_quadratic",
+    "gl_scan_qkv_fwd",
 )
 
 GL_FLAG_GENERIC = 1
@@ -83,9 +86,10 @@ def lib():
         L.gl_scan_final_state.argtypes = [pd] + [P] * 6
         L.gl_decode_step.argtypes = [pd] + [P] * 9
         L.gl_costate_quadratic.argtypes = [pd] + [P] * 7
+        L.gl_scan_qkv_fwd.argtypes = [pd] + [P] * 6 + [I] + [P] * 2
         for f in ("gl_scan_saved_size", "gl_scan_workspace_size", "gl_scan_fwd", "gl_scan_bwd",
                   "gl_decode_readout", "gl_decode_update", "gl_decode_step",
-                  "gl_scan_final_state", "gl_costate_quadratic"):
+                  "gl_scan_final_state", "gl_costate_quadratic", "gl_scan_qkv_fwd"):
             getattr(L, f).restype = ctypes.c_int
         L.gl_status_string.argtypes = [I]
         L.gl_status_string.restype = ctypes.c_char_p
@@ -344,6 +348,32 @@ def picard(x, eta, alpha, W0, target, g0=None, max_sweeps=None, tol=0.0):
         if float(res_max.max()) <= tol:
             break
     return g, y, k, res_max
+
+
+def gl_scan_qkv_fwd(q, k, v, eta, alpha, W0, w0_transposed=False):
+    """y_t = (W0' + D_t) q_t, D_{t+1} = alpha_t D_t - eta_t v_t k_t^T: q, k
+    [B,H,T,dk], v [B,H,T,dv], W0 [H,dv,dk] (or [H,dk,dv] transposed)."""
+    torch = _torch()
+    if q.dim() != 4 or k.shape != q.shape or v.dim() != 4 or v.shape[:3] != q.shape[:3]:
+        raise ValueError("q, k must be [B,H,T,dk] and v [B,H,T,dv]")
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    want = (H, dk, dv) if w0_transposed else (H, dv, dk)
+    if tuple(W0.shape) != want or eta.shape != (B, H, T) or alpha.shape != (B, H, T):
+        raise ValueError("shape mismatch between q, v, W0, eta and alpha")
+    y = torch.empty((B, H, T, dv), dtype=q.dtype, device=q.device)
+    _check_dec((q, k, v, W0, y), (eta,), alpha, q.dtype)
+    desc = make_desc(B, H, T, dk, dv, _io_code(q.dtype))
+    _check(lib().gl_scan_qkv_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(eta),
+                                 _ptr(alpha), _ptr(W0), int(bool(w0_transposed)), _ptr(y),
+                                 _stream(q.device)))
+    return y
+
+
+def transpose_read(u, g, x, eta, alpha, W0):
+    """z_t = (W0 + D_t)^T u_t along the adaptation D_t that (x, g, eta, alpha)
+    write (u [B,H,T,d_out] -> z [B,H,T,d_in])."""
+    return gl_scan_qkv_fwd(u, g, x, eta, alpha, W0, w0_transposed=True)
 
 
 def _make_function():

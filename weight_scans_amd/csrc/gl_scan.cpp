@@ -446,6 +446,22 @@ gl_status_t gl_costate_quadratic(const gl_scan_desc_t* desc, const void* y, cons
                     "costate launch");
 }
 
+gl_status_t gl_scan_qkv_fwd(const gl_scan_desc_t* desc, const void* q, const void* k,
+                            const void* v, const void* eta, const void* alpha, const void* W0,
+                            int w0_transposed, void* y, void* stream) {
+  gl_status_t st = check_dec(desc, true);
+  if (st != GL_SUCCESS || desc->B * desc->H * desc->T == 0) return st;
+  st = check_ptrs({q, k, v, eta, alpha, W0, y});
+  if (st != GL_SUCCESS) return st;
+  gls::QkvArgs a;
+  a.q = q; a.k = k; a.v = v; a.eta = eta; a.alpha = alpha; a.W0 = W0; a.y = y;
+  a.B = desc->B; a.H = desc->H; a.T = desc->T;
+  a.dk = static_cast<int>(desc->d_in); a.dv = static_cast<int>(desc->d_out);
+  a.w0_transposed = w0_transposed != 0;
+  return hip_status(gls::launch_qkv_fwd(desc->io_dtype, a, static_cast<hipStream_t>(stream)),
+                    "qkv scan launch");
+}
+
 const char* gl_status_string(gl_status_t status) {
   switch (status) {
     case GL_SUCCESS: return "success";

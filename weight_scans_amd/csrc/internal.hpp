@@ -103,6 +103,20 @@ struct CostArgs {
   int d_out;
 };
 
+// The scan with its own read vector and write key (q != k): D is dv x dk.
+struct QkvArgs {
+  const void* q;      // [B*H][T][dk] io
+  const void* k;      // [B*H][T][dk] io
+  const void* v;      // [B*H][T][dv] io
+  const void* eta;    // [B*H][T] gate type
+  const void* alpha;  // [B*H][T] gate type
+  const void* W0;     // [H][dv][dk] io, or [H][dk][dv] with w0_transposed
+  void* y;            // [B*H][T][dv] io
+  int64_t B, H, T;
+  int dk, dv;
+  bool w0_transposed;
+};
+
 struct FinArgs {
   const void* part_eta;
   const void* part_alpha;
@@ -131,6 +145,7 @@ hipError_t launch_decode_update(int io, const DecArgs& a, hipStream_t s);
 hipError_t launch_decode_step(int io, const DecArgs& a, hipStream_t s);
 hipError_t launch_final_state(int io, const DecArgs& a, hipStream_t s);
 hipError_t launch_costate(int io, const CostArgs& a, hipStream_t s);
+hipError_t launch_qkv_fwd(int io, const QkvArgs& a, hipStream_t s);
 
 // Matrix-core kernels: bf16 io, d_in == d_out in {64, 128}, chunk 64.
 constexpr int kMfmaChunk = 64;
