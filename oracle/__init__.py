@@ -20,7 +20,9 @@ synthetic test) is pinned by the exact-recovery test (the open-loop C scan
 driven by its costates reproduces its outputs, at the rounding scale the
 pages print) and the causal fixed-point test; ``costate_quadratic`` by
 hand-computed values and by vanishing at the serial learner's costates.
-``qkv_fwd`` (read vector q and write key k of their own) is pinned by
+``serial_two_layer`` (two adapted linear layers) is pinned by the open-loop
+composition of ``fwd`` and the transpose read of ``qkv_fwd`` driven by its
+costates.  ``qkv_fwd`` (read vector q and write key k of their own) is pinned by
 reducing to ``fwd`` when q = k = x, by the transpose read against the
 adaptation states of ``seq_fwd``, and by the unrolled discounted sum for a
 separate write key.
@@ -224,3 +226,28 @@ def qkv_fwd(q, k, v, eta, alpha, W0p):
                 y[b, h, t] = (W0p[h] + D) @ q[b, h, t]
                 D = alpha[b, h, t] * D - eta[b, h, t] * np.outer(v[b, h, t], k[b, h, t])
     return y
+
+
+def serial_two_layer(X, R, eta1, alpha1, W1, eta2, alpha2, W2):
+    """The serial learner of the two-layer synthetic test ("Parallelize the
+    Training, Keep the Learning Serial", section "The synthetic test checks the
+    mechanism, not model quality"), read with both layers linear and adapted:
+    h_t = W1_{t-1} x_t, y_t = W2_{t-1} h_t, g2_t = y_t - r_t, the hidden
+    costate g1_t = W2_{t-1}^T g2_t (through the weight that produced y_t), then
+    both layers take their step.  Returns (H, Y, G1, G2)."""
+    X, R, eta1, alpha1, W1, eta2, alpha2, W2 = map(
+        _f64, (X, R, eta1, alpha1, W1, eta2, alpha2, W2))
+    T = X.shape[0]
+    D1 = np.zeros_like(W1)
+    D2 = np.zeros_like(W2)
+    Hs = np.empty((T, W1.shape[0]))
+    Y = np.empty((T, W2.shape[0]))
+    G1, G2 = np.empty_like(Hs), np.empty_like(Y)
+    for t in range(T):
+        Hs[t] = (W1 + D1) @ X[t]
+        Y[t] = (W2 + D2) @ Hs[t]
+        G2[t] = Y[t] - R[t]
+        G1[t] = (W2 + D2).T @ G2[t]
+        D2 = alpha2[t] * D2 - eta2[t] * np.outer(G2[t], Hs[t])
+        D1 = alpha1[t] * D1 - eta1[t] * np.outer(G1[t], X[t])
+    return Hs, Y, G1, G2

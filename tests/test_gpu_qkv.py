@@ -91,3 +91,41 @@ def test_transpose_read_full_size_sampled():
                               inp["W0"][h:h + 1].transpose(0, 2, 1))
         err = relmax(z[b, h], want[0, 0])
         assert err <= TOL["bf16"], (b, h, err)
+
+
+@pytest.mark.parametrize("io,bound", [("f64", 1e-12), ("f32", 1e-4)])
+def test_two_layer_mechanism_and_control(io, bound):
+    # the pages' mechanism test, read with two linear adapted layers: given
+    # the serial learner's costates, the forward scans reproduce its outputs,
+    # and the transpose read through the adapted second layer reproduces its
+    # hidden costates; the control reads through W2^T (eta = 0: D stays zero)
+    # and misses them by a large margin while the outputs are unchanged
+    T, d0, d1, d2 = 300, 32, 64, 48
+    say(f"two-layer mechanism io={io} T={T} d={d0},{d1},{d2}")
+    rng = np.random.default_rng(1800)
+    X = round_to(rng.standard_normal((1, 1, T, d0)) / np.sqrt(d0), io)
+    R = round_to(rng.standard_normal((1, 1, T, d2)), io)
+    W1 = round_to(rng.standard_normal((1, d1, d0)) / np.sqrt(d0), io)
+    W2 = round_to(rng.standard_normal((1, d2, d1)) / np.sqrt(d1), io)
+    gate = "f64" if io == "f64" else "f32"
+    e1 = round_to(np.full((1, 1, T), 0.05), gate)
+    e2 = round_to(np.full((1, 1, T), 0.08), gate)
+    a1 = round_to(np.full((1, 1, T), 0.97), gate)
+    a2 = round_to(np.full((1, 1, T), 0.95), gate)
+    Hs, Y, G1, G2 = oracle.serial_two_layer(X[0, 0], R[0, 0], e1[0, 0], a1[0, 0], W1[0],
+                                            e2[0, 0], a2[0, 0], W2[0])
+    tio, tg = TORCH_IO[io], TORCH_IO[gate]
+    D = lambda A, t=tio: torch.from_numpy(np.ascontiguousarray(A)).to("cuda", t)  # noqa: E731
+    h, _ = ws.gl_scan_fwd(D(X), D(G1[None, None]), D(e1, tg), D(a1, tg), D(W1), save=False)
+    y, _ = ws.gl_scan_fwd(h, D(G2[None, None]), D(e2, tg), D(a2, tg), D(W2), save=False)
+    g2, _, _ = ws.gl_costate_quadratic(y, D(R), D(G2[None, None]))
+    g1 = ws.transpose_read(g2, D(G2[None, None]), h, D(e2, tg), D(a2, tg), D(W2))
+    g1c = ws.transpose_read(g2, D(G2[None, None]), h, D(np.zeros_like(e2), tg), D(a2, tg), D(W2))
+    torch.cuda.synchronize()
+    scale = max(float(np.max(np.abs(G1))), 1.0)
+    err_y = np.max(np.abs(host(y)[0, 0] - Y)) / max(float(np.max(np.abs(Y))), 1.0)
+    err_g1 = np.max(np.abs(host(g1)[0, 0] - G1)) / scale
+    err_ctrl = np.max(np.abs(host(g1c)[0, 0] - G1)) / scale
+    say(f"  outputs {err_y:.3g}  hidden costates {err_g1:.3g}  control {err_ctrl:.3g}")
+    assert err_y <= bound and err_g1 <= bound
+    assert err_ctrl > 1e-2

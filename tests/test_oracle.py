@@ -440,3 +440,30 @@ def test_write_key_closed_form():
         for s_ in range(t):
             want = want + np.prod(a[s_ + 1:t]) * (-e[s_]) * G[s_] * (Xb[s_] @ X[t])
         assert np.max(np.abs(y[t] - want)) < 1e-13
+
+
+def test_two_layer_mechanism_and_control():
+    # supplied with the serial learner's costates, the open-loop scans
+    # reproduce its outputs, and the transpose read through the adapted second
+    # layer reproduces its hidden costates at rounding scale; reading through
+    # W2^T (the persistent weight) instead leaves the outputs alone but not the
+    # hidden costates (the pages' control)
+    T, d0, d1, d2 = 60, 6, 8, 5
+    rng = np.random.default_rng(111)
+    X = rng.standard_normal((T, d0)) / np.sqrt(d0)
+    R = rng.standard_normal((T, d2))
+    W1 = rng.standard_normal((d1, d0)) / np.sqrt(d0)
+    W2 = rng.standard_normal((d2, d1)) / np.sqrt(d1)
+    e1, e2 = np.full(T, 0.2), np.full(T, 0.3)
+    a1, a2 = np.full(T, 0.95), np.full(T, 0.9)
+    Hs, Y, G1, G2 = oracle.serial_two_layer(X, R, e1, a1, W1, e2, a2, W2)
+    b = lambda A: A[None, None]  # noqa: E731
+    h = oracle.fwd(b(X), b(G1), b(e1), b(a1), W1[None])[0, 0]
+    y = oracle.fwd(b(h), b(G2), b(e2), b(a2), W2[None])[0, 0]
+    g2 = y - R
+    g1 = oracle.qkv_fwd(b(g2), b(G2), b(h), b(e2), b(a2), W2.T[None])[0, 0]
+    g1_ctrl = oracle.qkv_fwd(b(g2), b(G2), b(h), b(np.zeros(T)), b(a2), W2.T[None])[0, 0]
+    page = _golden()
+    bound = 100 * max(page["outputs"], page["hidden_costates"])
+    assert np.max(np.abs(y - Y)) < bound and np.max(np.abs(g1 - G1)) < bound
+    assert np.max(np.abs(g1_ctrl - G1)) > 1e-2
