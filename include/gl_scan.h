@@ -158,7 +158,10 @@ gl_status_t gl_decode_step(const gl_scan_desc_t* desc, const void* x_prev, const
 /* Hand-over from a prefill of desc->T tokens (the inputs of gl_scan_fwd) to
  * decoding: writes the adaptation after the last token,
  * D_T = sum_t (prod_{s>t} alpha_s)(-eta_t) g_t x_t^T, into `state` (zero for
- * T == 0). */
+ * T == 0).  BF16 io with d_in == d_out in {64, 128}: the forward scan's
+ * matrix-core arithmetic (bf16 operands, fp32 accumulation: the state the
+ * prefill's own readouts used); GL_FLAG_GENERIC or other shapes: fp32 (fp64)
+ * vector arithmetic. */
 gl_status_t gl_scan_final_state(const gl_scan_desc_t* desc, const void* x, const void* g,
                                 const void* eta, const void* alpha, void* state,
                                 void* stream);

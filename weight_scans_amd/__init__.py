@@ -231,8 +231,9 @@ def _check_dec(tensors, gates, state, io_dtype):
             raise ValueError("all tensors must be contiguous")
 
 
-def gl_scan_final_state(x, g, eta, alpha):
-    """Adaptation after the last of T prefill tokens, [B,H,d_out,d_in]."""
+def gl_scan_final_state(x, g, eta, alpha, flags=0):
+    """Adaptation after the last of T prefill tokens, [B,H,d_out,d_in]
+    (flags=GL_FLAG_GENERIC: fp32 vector arithmetic for the matrix-core shapes)."""
     torch = _torch()
     if x.dim() != 4 or g.dim() != 4:
         raise ValueError("x and g must be [B,H,T,d]")
@@ -242,7 +243,7 @@ def gl_scan_final_state(x, g, eta, alpha):
         raise ValueError("shape mismatch between x, g, eta and alpha")
     state = torch.empty((B, H, d_out, d_in), dtype=gate_dtype(x.dtype), device=x.device)
     _check_dec((x, g), (eta, alpha), state, x.dtype)
-    desc = make_desc(B, H, T, d_in, d_out, _io_code(x.dtype))
+    desc = make_desc(B, H, T, d_in, d_out, _io_code(x.dtype), flags=flags)
     _check(lib().gl_scan_final_state(ctypes.byref(desc), _ptr(x), _ptr(g), _ptr(eta),
                                      _ptr(alpha), _ptr(state), _stream(x.device)))
     return state

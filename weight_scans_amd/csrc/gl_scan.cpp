@@ -424,6 +424,27 @@ gl_status_t gl_scan_final_state(const gl_scan_desc_t* desc, const void* x, const
   if (st != GL_SUCCESS || desc->B * desc->H == 0) return st;
   st = desc->T > 0 ? check_ptrs({x, g, eta, alpha, state}) : check_ptrs({state});
   if (st != GL_SUCCESS) return st;
+  const bool mfma = desc->io_dtype == GL_DTYPE_BF16 && desc->d_in == desc->d_out &&
+                    (desc->d_in == 64 || desc->d_in == 128) && desc->T > 0 &&
+                    !(desc->flags & GL_FLAG_GENERIC);
+  if (mfma) {
+    // the forward kernel's state-only instance over one segment: D_T from a
+    // zero start, on the matrix cores (the scan's own arithmetic)
+    gls::FwdArgs f;
+    f.x = x; f.g = g; f.eta = eta; f.alpha = alpha;
+    f.W0 = x;  // not read by the state-only instance
+    f.y = nullptr;
+    f.states = nullptr;
+    f.B = desc->B; f.H = desc->H; f.T = desc->T;
+    f.d_in = static_cast<int>(desc->d_in); f.d_out = static_cast<int>(desc->d_out);
+    f.chunk = gls::kMfmaChunk;
+    f.n_chunks = static_cast<int>((desc->T + gls::kMfmaChunk - 1) / gls::kMfmaChunk);
+    f.ckpt_every = 1; f.n_ckpt = f.n_chunks;
+    f.seg_chunks = f.n_chunks; f.n_seg = 1;
+    f.seg_out = static_cast<float*>(state);
+    return hip_status(gls::launch_mfma_final_state(f, static_cast<hipStream_t>(stream)),
+                      "final state launch");
+  }
   gls::DecArgs a = dec_args(desc);
   a.x = x; a.g = g; a.eta = eta; a.alpha = alpha; a.state = state;
   return hip_status(gls::launch_final_state(desc->io_dtype, a, static_cast<hipStream_t>(stream)),

@@ -146,6 +146,7 @@ hipError_t launch_decode_step(int io, const DecArgs& a, hipStream_t s);
 hipError_t launch_final_state(int io, const DecArgs& a, hipStream_t s);
 hipError_t launch_costate(int io, const CostArgs& a, hipStream_t s);
 hipError_t launch_qkv_fwd(int io, const QkvArgs& a, hipStream_t s);
+hipError_t launch_mfma_final_state(const FwdArgs& a, hipStream_t s);
 
 // Matrix-core kernels: bf16 io, d_in == d_out in {64, 128}, chunk 64.
 constexpr int kMfmaChunk = 64;

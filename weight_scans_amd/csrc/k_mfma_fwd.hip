@@ -34,7 +34,8 @@
 // Segments: work-group (segment s, head, tile) scans only the chunks of s,
 // starting from the state given in seg_in (zero if absent).  The state-only
 // instance (no y, no states) instead reports the segment's final state from
-// a zero start and its summed log2 alpha; an exclusive affine scan over the
+// a zero start and its summed log2 alpha (with one segment, the hand-over
+// state D_T for decoding); an exclusive affine scan over the
 // segments (k_seg.hip) turns these into each segment's starting state.  This
 // is the associative composition of the scan across chunks
 // ("Parallelize the Training, Keep the Learning Serial", cognaptus.com,
@@ -500,16 +501,16 @@ __global__ __launch_bounds__(kNT) void fwd_mfma(FwdArgs a) {
       *reinterpret_cast<f32x4*>(so + (r0 + rbw * 16 + l16) * D + cb * 16 + 4 * g4) = sacc[s];
     }
   }
-  if (a.seg_out && role == (HAS_Y ? 1 : 0) && tile == 0 && w8 == kPrepWave && lane == 0)
+  if (a.seg_out && a.seg_lg && role == (HAS_Y ? 1 : 0) && tile == 0 && w8 == kPrepWave && lane == 0)
     a.seg_lg[bh * a.n_seg + seg] = lsum;
 }
 
 template <int D, bool HAS_Y, bool HAS_ST>
-hipError_t launch_v(const FwdArgs& a, hipStream_t s) {
+hipError_t launch_v(const FwdArgs& a, hipStream_t s, bool every_segment = false) {
   const int64_t groups = (a.B * a.H + 7) / 8;
-  // the state-only pass skips the last segment (nothing lies to its right
-  // that would use its final state)
-  const int nseg = (!HAS_Y && !HAS_ST) ? a.n_seg - 1 : a.n_seg;
+  // the state-only pass of the segmented scan skips the last segment (nothing
+  // lies to its right that would use its final state)
+  const int nseg = (!HAS_Y && !HAS_ST && !every_segment) ? a.n_seg - 1 : a.n_seg;
   if (nseg <= 0) return hipSuccess;
   const dim3 grid(static_cast<unsigned>(groups * 8 * (D / kTN) * nseg));
   hipLaunchKernelGGL((fwd_mfma<D, HAS_Y, HAS_ST>), grid, dim3(kNT), 0, s, a);
@@ -529,6 +530,13 @@ hipError_t launch_d(const FwdArgs& a, hipStream_t s) {
 
 hipError_t launch_mfma_fwd(const FwdArgs& a, hipStream_t s) {
   return a.d_in == 128 ? launch_d<128>(a, s) : launch_d<64>(a, s);
+}
+
+// The final state of every segment from a zero start (with one segment: the
+// adaptation after the last token, D_T) into a.seg_out [B*H][n_seg][D][D].
+hipError_t launch_mfma_final_state(const FwdArgs& a, hipStream_t s) {
+  return a.d_in == 128 ? launch_v<128, false, false>(a, s, true)
+                       : launch_v<64, false, false>(a, s, true);
 }
 
 }  // namespace gls
