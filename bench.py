@@ -259,6 +259,25 @@ def decode_main(args, w):
     readout(0)
     ms = timed(fused_step)
     tot_ms = ms * args.steps
+    # the same fused steps captured once in a HIP graph and replayed (a serving
+    # loop's launch path; reported beside the eager line)
+    graph_ms = None
+    try:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            cs = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)  # the capture stream
+            for k in range(args.warmup + 1, K):
+                if f_st(*(a_st[k][:-1] + (cs,))):
+                    bad.append("step (captured)")
+        graph.replay()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        graph.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        graph_ms = e0.elapsed_time(e1) / args.steps
+    except RuntimeError as exc:  # capture not available: report the eager line only
+        print(f"graph replay skipped: {exc}", file=sys.stderr)
     if bad:
         raise RuntimeError(f"decode {bad[0]} call failed: {L.gl_last_error().decode()}")
     nbytes = decode_bytes(w)[2]
@@ -281,7 +300,8 @@ def decode_main(args, w):
                                f"d={w.d_in}, state handed over after T={w.T}",
                    "B": w.B, "H": w.H, "d_in": w.d_in, "d_out": w.d_out, "io": w.dtype,
                    "parallelism": "single GPU"},
-        "passes_ms": {"step_mean": ms, "separate_readout_plus_update": mp,
+        "passes_ms": {"step_mean": ms, "step_mean_graph_replay": graph_ms,
+                      "separate_readout_plus_update": mp,
                       "readout_alone": mr, "update_alone": mu, "final_state_ms": final_ms},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM / 1e9,
                      "unit": "GB/s", "frac": achieved / (PEAK_HBM / 1e9), "traffic": None,

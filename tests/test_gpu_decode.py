@@ -199,3 +199,38 @@ def test_empty_batch_is_a_noop():
     S = torch.empty((0, 2, 4, 8), dtype=torch.float32, device="cuda")
     W0 = torch.zeros((2, 4, 8), dtype=torch.float32, device="cuda")
     assert ws.gl_decode_readout(x, W0, S).shape == (0, 2, 4)
+
+
+def test_decode_steps_replay_in_a_hip_graph():
+    # a serving loop captured once and replayed: eight fused steps on fixed
+    # buffers; every replay (with eager work in between) matches the eager
+    # run bit for bit (the decode kernels clear nothing with memset nodes)
+    io, B, H, d, K = "bf16", 2, 4, 128, 8
+    say(f"decode graph io={io} B={B} H={H} d={d} K={K}")
+    _, dev = inputs(io, B, H, K + 1, d, d, seed=1900)
+    S0 = ws.gl_scan_final_state(dev["x"], dev["g"], dev["eta"], dev["alpha"])
+    tok = lambda k, i: dev[k][:, :, i].contiguous()  # noqa: E731
+    toks = [{k: tok(k, i) for k in ("x", "g", "eta", "alpha")} for i in range(K + 1)]
+    ys_e = [torch.empty((B, H, d), dtype=TORCH_IO[io], device="cuda") for _ in range(K)]
+    S_e = S0.clone()
+    for i in range(K):
+        p, n = toks[i], toks[i + 1]
+        ws.gl_decode_step(p["x"], p["g"], p["eta"], p["alpha"], n["x"], dev["W0"], S_e, y=ys_e[i])
+    torch.cuda.synchronize()
+    ys_g = [torch.empty_like(y) for y in ys_e]
+    S_g = S0.clone()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for i in range(K):
+            p, n = toks[i], toks[i + 1]
+            ws.gl_decode_step(p["x"], p["g"], p["eta"], p["alpha"], n["x"], dev["W0"], S_g,
+                              y=ys_g[i])
+    for rep in range(3):
+        S_g.copy_(S0)
+        for y in ys_g:
+            y.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(S_g, S_e), rep
+        assert all(torch.equal(a, b) for a, b in zip(ys_g, ys_e)), rep
