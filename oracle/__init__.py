@@ -22,7 +22,11 @@ pages print) and the causal fixed-point test; ``costate_quadratic`` by
 hand-computed values and by vanishing at the serial learner's costates.
 ``serial_two_layer`` (two adapted linear layers) is pinned by the open-loop
 composition of ``fwd`` and the transpose read of ``qkv_fwd`` driven by its
-costates.  ``qkv_fwd`` (read vector q and write key k of their own) is pinned by
+costates, and its first-matrix gradient by torch autograd through a serial
+two-layer loop of the test's own.  ``qkv_bwd`` (the adjoint of ``qkv_fwd``) is
+pinned by torch autograd through a serial loop written in the test, central
+finite differences, the adjoint dot test, and by reducing to the C oracle's
+``bwd`` when q = k = x (dq + dk = dx).  ``qkv_fwd`` (read vector q and write key k of their own) is pinned by
 reducing to ``fwd`` when q = k = x, by the transpose read against the
 adaptation states of ``seq_fwd``, and by the unrolled discounted sum for a
 separate write key.
@@ -228,13 +232,67 @@ def qkv_fwd(q, k, v, eta, alpha, W0p):
     return y
 
 
+def qkv_bwd(q, k, v, eta, alpha, W0p, dy, ckpt: int = 64):
+    """The exact adjoint of qkv_fwd for L = sum_t <dy_t, y_t>, token by token
+    in reverse ("Parallelize the Training, Keep the Learning Serial", section
+    "Once the gradient signals are known, the weight trajectory becomes
+    parallelizable": the recurrence is affine in D, so its adjoint is the same
+    recurrence run backwards).  With A the adjoint of the adaptation written
+    by token t (A = 0 after the last token):
+        dq_t = (W0' + D_t)^T dy_t        dk_t = -eta_t A^T v_t
+        dv_t = -eta_t A k_t              deta_t = -v_t^T A k_t
+        dalpha_t = <A, D_t>              dW0' += dy_t q_t^T
+        A <- alpha_t A + dy_t q_t^T
+    D_t is kept every `ckpt` tokens and recomputed forward within a block.
+    Returns (dq, dk, dv, deta, dalpha, dW0p) with dW0p [H,dv,dk] summed over
+    the batch."""
+    q, k, v, eta, alpha, W0p, dy = map(_f64, (q, k, v, eta, alpha, W0p, dy))
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    dq, dkk = np.zeros_like(q), np.zeros_like(k)
+    dvv = np.zeros_like(v)
+    deta, dalpha = np.zeros_like(eta), np.zeros_like(alpha)
+    dW0p = np.zeros_like(W0p)
+    for b in range(B):
+        for h in range(H):
+            qs, ks, vs = q[b, h], k[b, h], v[b, h]
+            es, al, g = eta[b, h], alpha[b, h], dy[b, h]
+            # forward: the adaptation read by token t, kept at block starts
+            marks = {}
+            D = np.zeros((dv, dk))
+            for t in range(T):
+                if t % ckpt == 0:
+                    marks[t] = D.copy()
+                D = al[t] * D - es[t] * np.outer(vs[t], ks[t])
+            A = np.zeros((dv, dk))
+            for t0 in range(((T - 1) // ckpt) * ckpt if T else 0, -1, -ckpt):
+                t1 = min(T, t0 + ckpt)
+                Ds = [marks[t0]]
+                for t in range(t0, t1 - 1):
+                    Ds.append(al[t] * Ds[-1] - es[t] * np.outer(vs[t], ks[t]))
+                for t in range(t1 - 1, t0 - 1, -1):
+                    Dt = Ds[t - t0]
+                    dq[b, h, t] = (W0p[h] + Dt).T @ g[t]
+                    dkk[b, h, t] = -es[t] * (A.T @ vs[t])
+                    dvv[b, h, t] = -es[t] * (A @ ks[t])
+                    deta[b, h, t] = -vs[t] @ A @ ks[t]
+                    dalpha[b, h, t] = np.sum(A * Dt)
+                    dW0p[h] += np.outer(g[t], qs[t])
+                    A = al[t] * A + np.outer(g[t], qs[t])
+    return dq, dkk, dvv, deta, dalpha, dW0p
+
+
 def serial_two_layer(X, R, eta1, alpha1, W1, eta2, alpha2, W2):
     """The serial learner of the two-layer synthetic test ("Parallelize the
     Training, Keep the Learning Serial", section "The synthetic test checks the
     mechanism, not model quality"), read with both layers linear and adapted:
     h_t = W1_{t-1} x_t, y_t = W2_{t-1} h_t, g2_t = y_t - r_t, the hidden
     costate g1_t = W2_{t-1}^T g2_t (through the weight that produced y_t), then
-    both layers take their step.  Returns (H, Y, G1, G2)."""
+    both layers take their step.  Returns (H, Y, G1, G2, GW1): GW1 is the
+    first matrix's gradient, the sum over tokens of the test-time gradients
+    d l_t / d W1 = g1_t x_t^T taken at each token's weights (with the
+    costates held as data it is the gradient of sum_t l_t w.r.t. the
+    persistent W1)."""
     X, R, eta1, alpha1, W1, eta2, alpha2, W2 = map(
         _f64, (X, R, eta1, alpha1, W1, eta2, alpha2, W2))
     T = X.shape[0]
@@ -243,11 +301,13 @@ def serial_two_layer(X, R, eta1, alpha1, W1, eta2, alpha2, W2):
     Hs = np.empty((T, W1.shape[0]))
     Y = np.empty((T, W2.shape[0]))
     G1, G2 = np.empty_like(Hs), np.empty_like(Y)
+    GW1 = np.zeros_like(W1)
     for t in range(T):
         Hs[t] = (W1 + D1) @ X[t]
         Y[t] = (W2 + D2) @ Hs[t]
         G2[t] = Y[t] - R[t]
         G1[t] = (W2 + D2).T @ G2[t]
+        GW1 += np.outer(G1[t], X[t])
         D2 = alpha2[t] * D2 - eta2[t] * np.outer(G2[t], Hs[t])
         D1 = alpha1[t] * D1 - eta1[t] * np.outer(G1[t], X[t])
-    return Hs, Y, G1, G2
+    return Hs, Y, G1, G2, GW1

@@ -112,7 +112,7 @@ def test_two_layer_mechanism_and_control(io, bound):
     e2 = round_to(np.full((1, 1, T), 0.08), gate)
     a1 = round_to(np.full((1, 1, T), 0.97), gate)
     a2 = round_to(np.full((1, 1, T), 0.95), gate)
-    Hs, Y, G1, G2 = oracle.serial_two_layer(X[0, 0], R[0, 0], e1[0, 0], a1[0, 0], W1[0],
+    Hs, Y, G1, G2, GW1 = oracle.serial_two_layer(X[0, 0], R[0, 0], e1[0, 0], a1[0, 0], W1[0],
                                             e2[0, 0], a2[0, 0], W2[0])
     tio, tg = TORCH_IO[io], TORCH_IO[gate]
     D = lambda A, t=tio: torch.from_numpy(np.ascontiguousarray(A)).to("cuda", t)  # noqa: E731

@@ -456,7 +456,7 @@ def test_two_layer_mechanism_and_control():
     W2 = rng.standard_normal((d2, d1)) / np.sqrt(d1)
     e1, e2 = np.full(T, 0.2), np.full(T, 0.3)
     a1, a2 = np.full(T, 0.95), np.full(T, 0.9)
-    Hs, Y, G1, G2 = oracle.serial_two_layer(X, R, e1, a1, W1, e2, a2, W2)
+    Hs, Y, G1, G2, GW1 = oracle.serial_two_layer(X, R, e1, a1, W1, e2, a2, W2)
     b = lambda A: A[None, None]  # noqa: E731
     h = oracle.fwd(b(X), b(G1), b(e1), b(a1), W1[None])[0, 0]
     y = oracle.fwd(b(h), b(G2), b(e2), b(a2), W2[None])[0, 0]
@@ -467,3 +467,144 @@ def test_two_layer_mechanism_and_control():
     bound = 100 * max(page["outputs"], page["hidden_costates"])
     assert np.max(np.abs(y - Y)) < bound and np.max(np.abs(g1 - G1)) < bound
     assert np.max(np.abs(g1_ctrl - G1)) > 1e-2
+    # the first matrix's gradient: the reverse scan of the first layer driven
+    # by the reconstructed hidden costates (dW0 of bwd with dy = g1) against
+    # the serial learner's sum of per-token gradients; the control's hidden
+    # costates move it by O(1)
+    dW1 = oracle.bwd(b(X), b(G1), b(e1), b(a1), W1[None], b(g1))[4][0]
+    dW1_ctrl = oracle.bwd(b(X), b(G1), b(e1), b(a1), W1[None], b(g1_ctrl))[4][0]
+    scale = max(float(np.max(np.abs(GW1))), 1.0)
+    assert np.max(np.abs(dW1 - GW1)) / scale < 100 * page["first_matrix_gradients"]
+    assert np.max(np.abs(dW1_ctrl - GW1)) / scale > 1e-2
+
+
+def _torch_two_layer_first_matrix(X, R, e1, a1, W1, e2, a2, W2):
+    """Serial autograd of the two-layer learner, written here independently of
+    the oracle: at each token the loss |y_t - r_t|^2 / 2 is differentiated by
+    torch w.r.t. the first matrix at that token's weights (the adaptations are
+    data, detached), the per-token gradients summed; also returns the hidden
+    costates dl_t / dh_t."""
+    T = X.shape[0]
+    W1t, W2t = torch.tensor(W1), torch.tensor(W2)
+    D1 = torch.zeros_like(W1t)
+    D2 = torch.zeros_like(W2t)
+    acc = torch.zeros_like(W1t)
+    G1 = []
+    for t in range(T):
+        A1 = (W1t + D1).clone().requires_grad_(True)
+        x = torch.tensor(X[t])
+        h = A1 @ x
+        h.retain_grad()
+        y = (W2t + D2) @ h
+        loss = 0.5 * torch.sum((y - torch.tensor(R[t])) ** 2)
+        loss.backward()
+        acc += A1.grad
+        g1, g2 = h.grad.detach(), (y - torch.tensor(R[t])).detach()
+        G1.append(g1)
+        D2 = a2[t] * D2 - e2[t] * torch.outer(g2, h.detach())
+        D1 = a1[t] * D1 - e1[t] * torch.outer(g1, x)
+    return acc.numpy(), torch.stack(G1).numpy()
+
+
+def test_two_layer_first_matrix_gradient_by_autograd():
+    T, d0, d1, d2 = 40, 5, 7, 4
+    rng = np.random.default_rng(112)
+    X = rng.standard_normal((T, d0)) / np.sqrt(d0)
+    R = rng.standard_normal((T, d2))
+    W1 = rng.standard_normal((d1, d0)) / np.sqrt(d0)
+    W2 = rng.standard_normal((d2, d1)) / np.sqrt(d1)
+    e1, e2 = np.full(T, 0.15), np.full(T, 0.25)
+    a1, a2 = rng.uniform(0.8, 1.0, T), rng.uniform(0.8, 1.0, T)
+    _, _, G1, _, GW1 = oracle.serial_two_layer(X, R, e1, a1, W1, e2, a2, W2)
+    want, G1t = _torch_two_layer_first_matrix(X, R, e1, a1, W1, e2, a2, W2)
+    assert relmax(G1, G1t) < 1e-13
+    assert relmax(GW1, want) < 1e-13
+
+
+# ---- the adjoint of the scan with its own read vector and write key
+
+def _torch_qkv(q, k, v, eta, alpha, W0p):
+    T = q.shape[0]
+    D = torch.zeros_like(W0p)
+    ys = []
+    for t in range(T):
+        ys.append((W0p + D) @ q[t])
+        D = alpha[t] * D - eta[t] * torch.outer(v[t], k[t])
+    return torch.stack(ys)
+
+
+def _qkv_inputs(T, dk, dv, seed, alpha="mix"):
+    inp = small(T=T, d_in=dk, d_out=dv, seed=seed, alpha=alpha)
+    rng = np.random.default_rng(seed + 1)
+    q = rng.standard_normal(inp["x"].shape) / np.sqrt(dk)
+    return q, inp["x"], inp["g"], inp["eta"], inp["alpha"], inp["W0"], inp["dy"]
+
+
+def test_qkv_adjoint_by_torch_autograd():
+    q, k, v, e, a, W0, dy = _qkv_inputs(15, 5, 4, 121)
+    names = ("q", "k", "v", "eta", "alpha")
+    vals = dict(zip(names, (q, k, v, e, a)))
+    tens = {n: torch.tensor(vals[n][0, 0], requires_grad=True) for n in names}
+    W0t = torch.tensor(W0[0], requires_grad=True)
+    y = _torch_qkv(tens["q"], tens["k"], tens["v"], tens["eta"], tens["alpha"], W0t)
+    (y * torch.tensor(dy[0, 0])).sum().backward()
+    got = oracle.qkv_bwd(q, k, v, e, a, W0, dy, ckpt=4)
+    for n, gr in zip(names, got[:5]):
+        assert relmax(gr[0, 0], tens[n].grad.numpy()) < 1e-13, n
+    assert relmax(got[5][0], W0t.grad.numpy()) < 1e-13
+
+
+def test_qkv_adjoint_finite_differences():
+    q, k, v, e, a, W0, dy = _qkv_inputs(6, 3, 2, 131)
+    inp = dict(q=q, k=k, v=v, eta=e, alpha=a, W0=W0)
+    got = dict(zip(("q", "k", "v", "eta", "alpha", "W0"),
+                   oracle.qkv_bwd(q, k, v, e, a, W0, dy)))
+    h = 1e-6
+
+    def f(d):
+        y = oracle.qkv_fwd(d["q"], d["k"], d["v"], d["eta"], d["alpha"], d["W0"])
+        return float(np.sum(y * dy))
+
+    for name in inp:
+        fd = np.zeros_like(inp[name])
+        for idx in np.ndindex(inp[name].shape):
+            pp = {kk: vv.copy() for kk, vv in inp.items()}
+            mm = {kk: vv.copy() for kk, vv in inp.items()}
+            pp[name][idx] += h
+            mm[name][idx] -= h
+            fd[idx] = (f(pp) - f(mm)) / (2 * h)
+        assert np.max(np.abs(fd - got[name])) < 1e-8, name
+
+
+def test_qkv_adjoint_dot_product_and_blocks():
+    q, k, v, e, a, W0, dy = _qkv_inputs(150, 9, 7, 141)
+    g1 = oracle.qkv_bwd(q, k, v, e, a, W0, dy, ckpt=64)
+    g2 = oracle.qkv_bwd(q, k, v, e, a, W0, dy, ckpt=1)   # every state kept
+    for x1, x2 in zip(g1, g2):
+        assert np.array_equal(x1, x2)
+    names = ("q", "k", "v", "eta", "alpha", "W0")
+    base = dict(zip(names, (q, k, v, e, a, W0)))
+    rng = np.random.default_rng(1)
+    dirs = {n: rng.standard_normal(base[n].shape) for n in names}
+    eps = 1e-5
+
+    def f(sc):
+        d = {n: base[n] + sc * dirs[n] for n in names}
+        return float(np.sum(oracle.qkv_fwd(d["q"], d["k"], d["v"], d["eta"], d["alpha"],
+                                           d["W0"]) * dy))
+
+    fd = (f(eps) - f(-eps)) / (2 * eps)
+    an = sum(float(np.sum(gr * dirs[n])) for n, gr in zip(names, g1))
+    assert abs(fd - an) <= 1e-7 * max(1.0, abs(an))
+
+
+def test_qkv_adjoint_reduces_to_the_scan_adjoint():
+    # q = k = x, v = g: dq + dk is the C oracle's dx, the rest coincide
+    inp = small(B=2, H=2, T=70, d_in=6, d_out=5, seed=151, alpha="mix")
+    dx, dg, de, da, dW = oracle.bwd(inp["x"], inp["g"], inp["eta"], inp["alpha"], inp["W0"],
+                                    inp["dy"])
+    dq, dk, dv, de2, da2, dW2 = oracle.qkv_bwd(inp["x"], inp["x"], inp["g"], inp["eta"],
+                                               inp["alpha"], inp["W0"], inp["dy"])
+    assert relmax(dq + dk, dx) < 1e-12
+    assert relmax(dv, dg) < 1e-12
+    assert relmax(de2, de) < 1e-12 and relmax(da2, da) < 1e-12 and relmax(dW2, dW) < 1e-12
