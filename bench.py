@@ -38,6 +38,7 @@ import ctypes
 import json
 import math
 import os
+import statistics
 import sys
 import time
 
@@ -87,19 +88,35 @@ def pass_kernels(w, which, segmented, generic):
     return pre + ("bwd_f64" if w.d_in == 64 else "bwd_f128") + " + finalize_kernel"
 
 
+def host_cores():
+    """(threads to use, description): every CPU this process may run on
+    (sched_getaffinity), and the host's CPU model."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return max(1, n), model
+
+
 def cpu_baseline(w, budget_s=20.0):
     """Time the fp64 oracle (fwd + bwd) on whole sequence-heads of the same
-    workload, as many as fit ~budget_s of CPU work, on this host's cores."""
+    workload, as many as fit ~budget_s of CPU work, on every core of the
+    process's affinity set."""
     import numpy as np
 
     import oracle
     from weight_scans_amd.synth import make_inputs
 
-    try:
-        cores = len(os.sched_getaffinity(0))
-    except AttributeError:
-        cores = os.cpu_count() or 1
-    cores = max(1, min(cores, 16))
+    cores, model = host_cores()
     est = 9e-9 * w.T * w.d_in * w.d_out          # s of CPU per sequence-head
     nseq = int(max(1, min(w.B * w.H, math.ceil(budget_s / max(est, 1e-9)))))
     inp = make_inputs(w)
@@ -120,9 +137,10 @@ def cpu_baseline(w, budget_s=20.0):
     dt = time.perf_counter() - t0
     tokens = nseq * w.T / w.H                    # token = all H heads of one position
     return {"value": tokens / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "cpu_model": model, "affinity_cpus": cores,
             "sample": f"{nseq} of {w.B * w.H} sequence-heads (T={w.T}, d={w.d_in}), fwd+bwd, "
-                      f"fp64 serial oracle, {dt:.1f} s wall; tokens counted as "
-                      f"sequence-heads*T/H"}
+                      f"fp64 serial oracle, {dt:.1f} s wall on {cores} threads ({model}); "
+                      f"tokens counted as sequence-heads*T/H"}
 
 
 def decode_bytes(w):
@@ -332,11 +350,7 @@ def cpu_costate(w, inp, R, budget_s=10.0):
 
     import oracle
 
-    try:
-        cores = len(os.sched_getaffinity(0))
-    except AttributeError:
-        cores = os.cpu_count() or 1
-    cores = max(1, min(cores, 16))
+    cores, _ = host_cores()
     G = np.zeros((1, 1, w.T, w.d_out))
     n, t0 = 0, time.perf_counter()
     while time.perf_counter() - t0 < budget_s and n < w.B * w.H:
@@ -441,7 +455,9 @@ def costate_main(args, w):
     print(json.dumps(rec), flush=True)
 
 
-PEAK_VALU = {"bf16": 157.3e12, "f32": 157.3e12, "f64": 78.6e12}  # vector flop/s
+# vector ALU flop/s without packed-fp32 instructions (the library is built with
+# them disabled): 256 CUs x 4 SIMDs x 16 lanes x 2 (fma) x 2.4 GHz; fp64 the same
+PEAK_VALU = {"bf16": 78.6e12, "f32": 78.6e12, "f64": 78.6e12}
 
 
 def qkv_main(args, w):
@@ -644,6 +660,7 @@ def main():
 
     alg = algorithmic(w)
     mf, mb = sum(tf) / len(tf), sum(tb) / len(tb)
+    med = statistics.median
     dom, dom_ms = ("bwd", mb) if mb >= mf else ("fwd", mf)
     nbytes, nflops = alg[dom]
     bound, amount, peak, unit = binding(w, nbytes, nflops)
@@ -676,7 +693,10 @@ def main():
                                f"{w.dtype}", "B": w.B, "H": w.H, "T": w.T, "d_in": w.d_in,
                    "d_out": w.d_out, "io": w.dtype, "kernels": path,
                    "parallelism": "single GPU"},
-        "passes_ms": {"fwd_mean": mf, "bwd_mean": mb, "fwd_min": min(tf), "bwd_min": min(tb)},
+        "passes_ms": {"fwd_mean": mf, "bwd_mean": mb,
+                      "fwd_median": med(tf), "fwd_min": min(tf), "fwd_max": max(tf),
+                      "bwd_median": med(tb), "bwd_min": min(tb), "bwd_max": max(tb)},
+        "tokens_per_s_median": tokens / ((med(tf) + med(tb)) / 1e3),
         "roofline": {"bound": bound, "achieved": achieved, "peak": peak, "unit": unit,
                      "frac": achieved / peak, "traffic": traffic,
                      "algorithmic_bytes": nbytes, "algorithmic_flops": nflops,

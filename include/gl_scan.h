@@ -37,9 +37,13 @@
  * call returns a status and touches no output.  GL_ERROR_HIP reports a failed
  * launch (text via gl_last_error()).  Nothing aborts, prints or throws.
  *
- * Numerical preconditions (documented, not checked on the device): inputs
- * are finite; 0 < alpha_t (the scan works with log alpha; alpha <= 1 keeps
- * every decay factor at or below one).
+ * Numerical preconditions of every path (documented, not checked on the
+ * device): inputs are finite and 0 < alpha_t <= 1.  The scans work with
+ * log alpha, and the matrix-core kernels build their decay factors on the
+ * assumption that every product of gates is at most one (the rank-one factors
+ * of the off-diagonal score blocks are clamped at one); an alpha above one
+ * gives results that are silently wrong there.  The oracle and the serial
+ * recurrence accept any alpha.
  */
 #ifndef GL_SCAN_H
 #define GL_SCAN_H
@@ -69,13 +73,24 @@ typedef enum {
 /* Flags for gl_scan_desc_t.flags */
 #define GL_FLAG_GENERIC 1u  /* use the portable VALU kernels even where a matrix-
                                core kernel exists (cross-checking only)        */
+#define GL_FLAG_OUT_F32 2u  /* gl_scan_fwd / gl_scan_bwd: y, dx and dg are fp32
+                               (the accumulators, not rounded to the io type)
+                               although io is BF16; no effect with F32 io;
+                               F64 io: GL_ERROR_NOT_SUPPORTED.  Inputs keep
+                               the io dtype.                                   */
 
 typedef struct {
   int64_t B, H, T;      /* batch, heads, tokens; any may be 0 (no-op)          */
   int64_t d_in, d_out;  /* 1..128 each; the matrix-core kernels take
                            d_in == d_out in {64, 128} with BF16 io            */
   int32_t io_dtype;     /* gl_dtype_t                                          */
-  int32_t chunk;        /* tokens per chunk; 0 = default of the chosen kernels */
+  int32_t chunk;        /* tokens per chunk; 0 = default of the chosen kernels.
+                           The result does not depend on it (the chunked form
+                           is exact).  Taken: 8, 16, 32 by the VALU kernels
+                           (F64: 8, 16), 64 by the matrix-core kernels; any
+                           other value (128 included: its 128 x 128 score
+                           tiles do not fit LDS beside the d = 128 state) is
+                           GL_ERROR_NOT_SUPPORTED                             */
   uint32_t flags;       /* GL_FLAG_*                                           */
   uint32_t segments;    /* matrix-core kernels: 0 = automatic (long sequences
                            with few heads are cut into segments so that a pass
@@ -114,9 +129,9 @@ gl_status_t gl_scan_bwd(const gl_scan_desc_t* desc, const void* x, const void* g
 
 /* ---- Deployment: one token at a time, and the prefill -> decode handoff.
  *
- * Once trained, the learner runs serially: for each new token the layer reads
- * out from its cached weight, the costate g of that token comes back, and the
- * cache takes one exact gradient step ("Parallelize the Training, Keep the
+ * Once trained, the learner runs token by token: the layer reads out with its
+ * cached weight, the costate g of that token comes back, and the cache is
+ * advanced by the recurrence's update for that token ("Parallelize the Training, Keep the
  * Learning Serial", cognaptus.com, section "The bottleneck appears before
  * deployment"; ParaTTT news summary, section "Perspective").  The cache is the
  * adaptation D = W - W0 of every sequence-head:
@@ -206,6 +221,28 @@ gl_status_t gl_costate_quadratic(const gl_scan_desc_t* desc, const void* y, cons
 gl_status_t gl_scan_qkv_fwd(const gl_scan_desc_t* desc, const void* q, const void* k,
                             const void* v, const void* eta, const void* alpha, const void* W0,
                             int w0_transposed, void* y, void* stream);
+
+/* The reverse scan of gl_scan_qkv_fwd: for upstream dy [B][H][T][dv] io,
+ * the gradients of L = sum_t <dy_t, y_t> w.r.t. q, k, v, eta, alpha and W0',
+ *
+ *   A_T = 0,  A_{t} = alpha_t A_{t+1} + dy_t q_t^T       (A_t = dL / dD_t)
+ *   dq_t = (W0' + D_t)^T dy_t,       dk_t = -eta_t A_{t+1}^T v_t,
+ *   dv_t = -eta_t A_{t+1} k_t,       deta_t = -v_t^T A_{t+1} k_t,
+ *   dalpha_t = <A_{t+1}, D_t>,       dW0' = sum_b sum_t dy_t q_t^T
+ *
+ * (the same adjoint as gl_scan_bwd, whose dx is dq + dk when q = k = x).
+ * dq, dk [B][H][T][dk] io; dv [B][H][T][dv] io; deta, dalpha [B][H][T] gate
+ * dtype; dW0 [H][dv][dk] gate dtype, or [H][dk][dv] when w0_transposed != 0
+ * (the layout W0 is passed in).  The chunk states of the forward are
+ * recomputed inside the workspace `ws` of gl_scan_qkv_workspace_size bytes.
+ * Portable chunked VALU kernels, any 1 <= dk, dv <= 128 (chunk 32, F64: 8).
+ * Same rules as gl_scan_bwd; B*H*T == 0 writes the zero dW0 only. */
+gl_status_t gl_scan_qkv_workspace_size(const gl_scan_desc_t* desc, size_t* ws_bytes);
+gl_status_t gl_scan_qkv_bwd(const gl_scan_desc_t* desc, const void* q, const void* k,
+                            const void* v, const void* eta, const void* alpha, const void* W0,
+                            int w0_transposed, const void* dy, void* dq, void* dk, void* dv,
+                            void* deta, void* dalpha, void* dW0, void* ws, size_t ws_bytes,
+                            void* stream);
 
 /* Static description of a status code. */
 const char* gl_status_string(gl_status_t status);

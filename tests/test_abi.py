@@ -53,12 +53,28 @@ def test_status_strings():
     (dict(io_dtype=ws.GL_DTYPE_F64, chunk=32), 2),
     (dict(segments=1 << 21), 1), (dict(io_dtype=ws.GL_DTYPE_F32, segments=2), 2),
     (dict(flags=ws.GL_FLAG_GENERIC, segments=3), 2),
+    (dict(chunk=128), 2), (dict(io_dtype=ws.GL_DTYPE_F32, chunk=128), 2),
+    (dict(io_dtype=ws.GL_DTYPE_F64, chunk=128), 2), (dict(chunk=24), 2),
+    (dict(io_dtype=ws.GL_DTYPE_F64, flags=ws.GL_FLAG_OUT_F32), 2),
+    (dict(flags=4), 1),
 ])
 def test_descriptor_validation(kw, code):
     d = desc(**kw)
     n = ctypes.c_size_t()
     assert ws.lib().gl_scan_saved_size(ctypes.byref(d), ctypes.byref(n)) == code
     assert ws.path_name(d) is None
+
+
+@pytest.mark.parametrize("kw,path", [
+    (dict(), "mfma-bf16-d64"), (dict(chunk=64), "mfma-bf16-d64"),
+    (dict(chunk=16), "generic-bf16"), (dict(chunk=32), "generic-bf16"),
+    (dict(flags=ws.GL_FLAG_OUT_F32), "generic-bf16-out-f32"),
+    (dict(io_dtype=ws.GL_DTYPE_F32, flags=ws.GL_FLAG_OUT_F32), "generic-f32"),
+    (dict(io_dtype=ws.GL_DTYPE_F64, chunk=8), "generic-f64"),
+    (dict(io_dtype=ws.GL_DTYPE_F64, chunk=16), "generic-f64"),
+])
+def test_chunk_and_flag_routing(kw, path):
+    assert ws.path_name(desc(**kw)) == path
 
 
 def test_null_desc():
@@ -180,6 +196,35 @@ def test_qkv_argument_errors_before_launch():
     assert call(desc(d_in=129), ok) == 2
     assert call(desc(T=-1), ok) == 1
     assert call(desc(T=0), [None] * 6, None) == 0
+
+
+def test_qkv_bwd_argument_errors_before_launch():
+    L = ws.lib()
+    P = lambda p: ctypes.c_void_p(p) if p is not None else None  # noqa: E731
+    d = desc()
+    n = ctypes.c_size_t()
+    assert L.gl_scan_qkv_workspace_size(ctypes.byref(d), ctypes.byref(n)) == 0
+    need = n.value
+    assert need > 0
+    assert L.gl_scan_qkv_workspace_size(ctypes.byref(desc(d_in=129)), ctypes.byref(n)) == 2
+    assert L.gl_scan_qkv_workspace_size(ctypes.byref(d), None) == 1
+    ok = [FAKE] * 13   # q k v eta alpha W0 dy dq dk dv deta dalpha dW0
+
+    def call(dd, ptrs, wsp=FAKE, nb=need):
+        pre, post = ptrs[:6], ptrs[6:]
+        return L.gl_scan_qkv_bwd(ctypes.byref(dd), *[P(x) for x in pre], 0,
+                                 *[P(x) for x in post], P(wsp), nb, None)
+    for i in range(13):
+        pp = list(ok)
+        pp[i] = None
+        assert call(d, pp) == 1, i
+        pp[i] = FAKE + 8
+        assert call(d, pp) == 3, i
+    assert call(d, ok, nb=need - 1) == 4
+    assert call(d, ok, wsp=None) == 1
+    # empty: only dW0 is written (the zero sum), H == 0 needs nothing
+    assert call(desc(H=0), [None] * 13, wsp=None, nb=0) == 0
+    assert call(desc(T=0), [None] * 12 + [None], wsp=None, nb=0) == 1
 
 
 @pytest.mark.parametrize("fn,nptr", DEC_CALLS)

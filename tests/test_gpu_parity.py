@@ -190,6 +190,23 @@ def test_autograd_function_matches_bwd():
         assert relmax(host(leaves[k].grad), ref[n]) < TOL["f64"], k
 
 
+@pytest.mark.parametrize("d,T", [(64, 200), (128, 130), (40, 77)])
+def test_out_f32(d, T):
+    """GL_FLAG_OUT_F32: bf16 inputs, y / dx / dg returned in fp32 (not rounded
+    to bf16), every output within the bf16 tolerance of the oracle."""
+    w = Workload("of32", 2, 2, T, d, d, "bf16", "mix", "gauss", 2100 + d)
+    inp = make_inputs(w)
+    dev = to_device(inp, "bf16")
+    gpu = run_gpu(dev, flags=ws.GL_FLAG_OUT_F32)
+    for n in ("y", "dx", "dg"):
+        assert gpu[n].dtype == torch.float32, n
+    ref = oracle_all(inp)
+    errs, bad = compare_full(gpu, ref, TOL["bf16"])
+    say(f"  errs {errs}")
+    report(f"out_f32 d={d}", errs)
+    assert not bad, errs
+
+
 def test_empty_inputs():
     for io in ("f64", "bf16"):
         w = Workload("e", 2, 3, 0, 16, 16, io, "base", "gauss", 1)

@@ -121,11 +121,79 @@ def test_two_layer_mechanism_and_control(io, bound):
     g2, _, _ = ws.gl_costate_quadratic(y, D(R), D(G2[None, None]))
     g1 = ws.transpose_read(g2, D(G2[None, None]), h, D(e2, tg), D(a2, tg), D(W2))
     g1c = ws.transpose_read(g2, D(G2[None, None]), h, D(np.zeros_like(e2), tg), D(a2, tg), D(W2))
+    # the first matrix's gradient: the first layer's reverse scan driven by
+    # the reconstructed hidden costates (dW0 of gl_scan_bwd with dy = g1)
+    xs, g1s = D(X), D(G1[None, None])
+    dW1 = ws.gl_scan_bwd(xs, g1s, D(e1, tg), D(a1, tg), D(W1), g1, None)[4]
+    dW1c = ws.gl_scan_bwd(xs, g1s, D(e1, tg), D(a1, tg), D(W1), g1c, None)[4]
     torch.cuda.synchronize()
     scale = max(float(np.max(np.abs(G1))), 1.0)
     err_y = np.max(np.abs(host(y)[0, 0] - Y)) / max(float(np.max(np.abs(Y))), 1.0)
     err_g1 = np.max(np.abs(host(g1)[0, 0] - G1)) / scale
     err_ctrl = np.max(np.abs(host(g1c)[0, 0] - G1)) / scale
-    say(f"  outputs {err_y:.3g}  hidden costates {err_g1:.3g}  control {err_ctrl:.3g}")
-    assert err_y <= bound and err_g1 <= bound
-    assert err_ctrl > 1e-2
+    sw = max(float(np.max(np.abs(GW1))), 1.0)
+    err_w = np.max(np.abs(host(dW1)[0] - GW1)) / sw
+    err_wc = np.max(np.abs(host(dW1c)[0] - GW1)) / sw
+    say(f"  outputs {err_y:.3g}  hidden costates {err_g1:.3g}  first-matrix gradient "
+        f"{err_w:.3g}; control: hidden costates {err_ctrl:.3g}, first-matrix gradient {err_wc:.3g}")
+    assert err_y <= bound and err_g1 <= bound and err_w <= bound
+    assert err_ctrl > 1e-2 and err_wc > 1e-2
+
+
+QKV_BWD = [
+    ("f64", 2, 2, 70, 16, 16, False),
+    ("f32", 1, 2, 150, 64, 48, False),
+    ("bf16", 1, 2, 200, 128, 128, False),
+    ("f32", 1, 1, 77, 100, 37, True),      # ragged dk, dv; W0 given transposed
+    ("bf16", 1, 1, 5, 1, 3, False),
+    ("f64", 1, 2, 33, 7, 40, True),
+]
+
+
+@pytest.mark.parametrize("io,B,H,T,dk,dv,w0t", QKV_BWD)
+def test_qkv_bwd_parity(io, B, H, T, dk, dv, w0t):
+    say(f"qkv backward io={io} B={B} H={H} T={T} dk={dk} dv={dv} w0t={w0t}")
+    w = Workload("qkvb", B, H, T, dk, dv, io, "mix", "gauss", 1900 + dk + dv)
+    inp = make_inputs(w)
+    rng = np.random.default_rng(1950 + T)
+    q = round_to(rng.standard_normal(inp["x"].shape) / np.sqrt(dk), io)
+    W0p = inp["W0"]                                      # [H, dv, dk]
+    W0g = np.ascontiguousarray(W0p.transpose(0, 2, 1)) if w0t else W0p
+    dev = to_device(inp, io)
+    qd = torch.from_numpy(q).to("cuda", TORCH_IO[io])
+    W0d = torch.from_numpy(W0g).to("cuda", TORCH_IO[io])
+    got = ws.gl_scan_qkv_bwd(qd, dev["x"], dev["g"], dev["eta"], dev["alpha"], W0d, dev["dy"],
+                             w0_transposed=w0t)
+    torch.cuda.synchronize()
+    want = oracle.qkv_bwd(q, inp["x"], inp["g"], inp["eta"], inp["alpha"], W0p, inp["dy"])
+    want = list(want)
+    if w0t:
+        want[5] = want[5].transpose(0, 2, 1)
+    errs = {n: relmax(host(gv), wv) for n, gv, wv in
+            zip(("dq", "dk", "dv", "deta", "dalpha", "dW0"), got, want)}
+    say(f"  errs {errs}")
+    bad = {n: e for n, e in errs.items() if not e <= TOL[io]}
+    assert not bad, errs
+
+
+def test_qkv_bwd_transpose_read_full_size_sampled():
+    # the transpose read's reverse scan at the 340M-model shape, every head on
+    # the GPU, two heads and one head's dW0 against the oracle
+    w = CONFIGS["c3"]
+    say(f"qkv backward full size {w}")
+    inp = make_inputs(w)
+    dev = to_device(inp, w.dtype)
+    # transpose read: q = u (the dy draw), k = g, v = x, W0 given transposed
+    rng = np.random.default_rng(1990)
+    dz = round_to(rng.standard_normal(inp["x"].shape), w.dtype)
+    dzd = torch.from_numpy(dz).to("cuda", TORCH_IO[w.dtype])
+    got = ws.gl_scan_qkv_bwd(dev["dy"], dev["g"], dev["x"], dev["eta"], dev["alpha"], dev["W0"],
+                             dzd, w0_transposed=True)
+    got = [host(t) for t in got]
+    for b, h in ((0, 0), (7, 15)):
+        sl = lambda a: a[b:b + 1, h:h + 1]  # noqa: E731
+        want = oracle.qkv_bwd(sl(inp["dy"]), sl(inp["g"]), sl(inp["x"]), sl(inp["eta"]),
+                              sl(inp["alpha"]), inp["W0"][h:h + 1].transpose(0, 2, 1), sl(dz))
+        for n, gv, wv in zip(("dq", "dk", "dv", "deta", "dalpha"), got, want):
+            err = relmax(gv[b, h], wv[0, 0])
+            assert err <= TOL["bf16"], (b, h, n, err)

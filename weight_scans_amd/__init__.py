@@ -15,6 +15,7 @@ raises if the library is missing.
     g_t, res_sq, res_max = gl_costate_quadratic(y, target, g_hat)  # quadratic loss
     g, y, sweeps = picard(x, eta, alpha, W0, target)   # fixed point of g -> g~
     y = gl_scan_qkv_fwd(q, k, v, eta, alpha, W0)       # read vector != write key
+    dq, dk, dv, deta, dalpha, dW0 = gl_scan_qkv_bwd(q, k, v, eta, alpha, W0, dy)
     z = transpose_read(u, g, x, eta, alpha, W0)       # (W0 + D_t)^T u_t
 
 Shapes: x [B,H,T,d_in], g [B,H,T,d_out], eta/alpha [B,H,T], W0 [H,d_out,d_in];
@@ -42,9 +43,12 @@ EXPORTS = (
     "gl_scan_final_state",
     "gl_costate_quadratic",
     "gl_scan_qkv_fwd",
+    "gl_scan_qkv_workspace_size",
+    "gl_scan_qkv_bwd",
 )
 
 GL_FLAG_GENERIC = 1
+GL_FLAG_OUT_F32 = 2
 GL_DTYPE_F64, GL_DTYPE_F32, GL_DTYPE_BF16 = 0, 1, 2
 STATUS_NAMES = {0: "GL_SUCCESS", 1: "GL_ERROR_INVALID_VALUE", 2: "GL_ERROR_NOT_SUPPORTED",
                 3: "GL_ERROR_MISALIGNED", 4: "GL_ERROR_WORKSPACE_TOO_SMALL", 5: "GL_ERROR_HIP"}
@@ -87,9 +91,12 @@ def lib():
         L.gl_decode_step.argtypes = [pd] + [P] * 9
         L.gl_costate_quadratic.argtypes = [pd] + [P] * 7
         L.gl_scan_qkv_fwd.argtypes = [pd] + [P] * 6 + [I] + [P] * 2
+        L.gl_scan_qkv_workspace_size.argtypes = [pd, ps]
+        L.gl_scan_qkv_bwd.argtypes = [pd] + [P] * 6 + [I] + [P] * 7 + [P, S, P]
         for f in ("gl_scan_saved_size", "gl_scan_workspace_size", "gl_scan_fwd", "gl_scan_bwd",
                   "gl_decode_readout", "gl_decode_update", "gl_decode_step",
-                  "gl_scan_final_state", "gl_costate_quadratic", "gl_scan_qkv_fwd"):
+                  "gl_scan_final_state", "gl_costate_quadratic", "gl_scan_qkv_fwd",
+                  "gl_scan_qkv_workspace_size", "gl_scan_qkv_bwd"):
             getattr(L, f).restype = ctypes.c_int
         L.gl_status_string.argtypes = [I]
         L.gl_status_string.restype = ctypes.c_char_p
@@ -180,12 +187,20 @@ def _validate(x, g, eta, alpha, W0, dy=None):
     return B, H, T, d_in, d_out
 
 
+def _out_dtype(io_dtype, flags):
+    """dtype of y, dx and dg: fp32 for bf16 io under GL_FLAG_OUT_F32."""
+    torch = _torch()
+    if (flags & GL_FLAG_OUT_F32) and io_dtype == torch.bfloat16:
+        return torch.float32
+    return io_dtype
+
+
 def gl_scan_fwd(x, g, eta, alpha, W0, *, chunk=0, flags=0, save=True, segments=0):
     """Forward scan.  Returns (y, saved) where saved is None if save=False."""
     torch = _torch()
     B, H, T, d_in, d_out = _validate(x, g, eta, alpha, W0)
     desc = make_desc(B, H, T, d_in, d_out, _io_code(x.dtype), chunk, flags, segments)
-    y = torch.empty((B, H, T, d_out), dtype=x.dtype, device=x.device)
+    y = torch.empty((B, H, T, d_out), dtype=_out_dtype(x.dtype, flags), device=x.device)
     saved = None
     if save:
         saved = torch.empty(max(saved_size(desc), 16), dtype=torch.uint8, device=x.device)
@@ -203,8 +218,9 @@ def gl_scan_bwd(x, g, eta, alpha, W0, dy, saved=None, *, chunk=0, flags=0, segme
     B, H, T, d_in, d_out = _validate(x, g, eta, alpha, W0, dy)
     desc = make_desc(B, H, T, d_in, d_out, _io_code(x.dtype), chunk, flags, segments)
     gd = gate_dtype(x.dtype)
-    dx = torch.empty_like(x)
-    dg = torch.empty_like(g)
+    od = _out_dtype(x.dtype, flags)
+    dx = torch.empty(x.shape, dtype=od, device=x.device)
+    dg = torch.empty(g.shape, dtype=od, device=x.device)
     deta = torch.empty_like(eta)
     dalpha = torch.empty_like(alpha)
     dW0 = torch.empty((H, d_out, d_in), dtype=gd, device=x.device)
@@ -369,6 +385,34 @@ def gl_scan_qkv_fwd(q, k, v, eta, alpha, W0, w0_transposed=False):
                                  _ptr(alpha), _ptr(W0), int(bool(w0_transposed)), _ptr(y),
                                  _stream(q.device)))
     return y
+
+
+def gl_scan_qkv_bwd(q, k, v, eta, alpha, W0, dy, w0_transposed=False):
+    """Reverse scan of gl_scan_qkv_fwd for upstream dy [B,H,T,dv].  Returns
+    (dq, dk, dv, deta, dalpha, dW0) with dW0 in the layout W0 is given in."""
+    torch = _torch()
+    if q.dim() != 4 or k.shape != q.shape or v.dim() != 4 or v.shape[:3] != q.shape[:3]:
+        raise ValueError("q, k must be [B,H,T,dk] and v [B,H,T,dv]")
+    B, H, T, dk = q.shape
+    dvv = v.shape[-1]
+    want = (H, dk, dvv) if w0_transposed else (H, dvv, dk)
+    if (tuple(W0.shape) != want or eta.shape != (B, H, T) or alpha.shape != (B, H, T)
+            or dy.shape != v.shape):
+        raise ValueError("shape mismatch between q, v, W0, eta, alpha and dy")
+    gd = gate_dtype(q.dtype)
+    dq, dk_, dv_ = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    deta, dalpha = torch.empty_like(eta), torch.empty_like(alpha)
+    dW0 = torch.empty(want, dtype=gd, device=q.device)
+    _check_dec((q, k, v, W0, dy, dq, dk_, dv_), (eta, deta, dalpha), alpha, q.dtype)
+    desc = make_desc(B, H, T, dk, dvv, _io_code(q.dtype))
+    n = ctypes.c_size_t()
+    _check(lib().gl_scan_qkv_workspace_size(ctypes.byref(desc), ctypes.byref(n)))
+    ws = torch.empty(max(n.value, 16), dtype=torch.uint8, device=q.device)
+    _check(lib().gl_scan_qkv_bwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(eta),
+                                 _ptr(alpha), _ptr(W0), int(bool(w0_transposed)), _ptr(dy),
+                                 _ptr(dq), _ptr(dk_), _ptr(dv_), _ptr(deta), _ptr(dalpha),
+                                 _ptr(dW0), _ptr(ws), n.value, _stream(q.device)))
+    return dq, dk_, dv_, deta, dalpha, dW0
 
 
 def transpose_read(u, g, x, eta, alpha, W0):

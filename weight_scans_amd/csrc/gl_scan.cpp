@@ -49,6 +49,7 @@ constexpr int kBwdCombineAbove = 4;
 struct Plan {
   int io = 0;
   bool mfma = false;
+  bool out_f32 = false;     // y, dx, dg in fp32 (bf16 io)
   int chunk = 0, n_chunks = 0, ckpt_every = 1, n_ckpt = 0, n_tiles = 0;
   size_t comp = 8;          // bytes of the compute / gate / state type
   size_t saved_bytes = 0;   // chunk-boundary states
@@ -76,7 +77,10 @@ gl_status_t make_plan(const gl_scan_desc_t* d, Plan* p) {
     return fail(GL_ERROR_INVALID_VALUE, "d_in and d_out must be >= 1");
   if (d->io_dtype < GL_DTYPE_F64 || d->io_dtype > GL_DTYPE_BF16)
     return fail(GL_ERROR_INVALID_VALUE, "unknown io_dtype %d", d->io_dtype);
-  if ((d->flags & ~GL_FLAG_GENERIC) != 0) return fail(GL_ERROR_INVALID_VALUE, "unknown flags");
+  if ((d->flags & ~(GL_FLAG_GENERIC | GL_FLAG_OUT_F32)) != 0)
+    return fail(GL_ERROR_INVALID_VALUE, "unknown flags");
+  if ((d->flags & GL_FLAG_OUT_F32) && d->io_dtype == GL_DTYPE_F64)
+    return fail(GL_ERROR_NOT_SUPPORTED, "GL_FLAG_OUT_F32 with fp64 io");
   if (d->segments > (1u << 20)) return fail(GL_ERROR_INVALID_VALUE, "segments above 2^20");
   if (d->chunk < 0) return fail(GL_ERROR_INVALID_VALUE, "negative chunk");
   if (d->d_in > gls::kGenericMaxD || d->d_out > gls::kGenericMaxD)
@@ -86,8 +90,10 @@ gl_status_t make_plan(const gl_scan_desc_t* d, Plan* p) {
 
   p->io = d->io_dtype;
   p->comp = (p->io == GL_DTYPE_F64) ? 8 : 4;
+  p->out_f32 = (d->flags & GL_FLAG_OUT_F32) && p->io == GL_DTYPE_BF16;
   const bool mfma_shape = p->io == GL_DTYPE_BF16 && d->d_in == d->d_out &&
-                          (d->d_in == 64 || d->d_in == 128) && !(d->flags & GL_FLAG_GENERIC);
+                          (d->d_in == 64 || d->d_in == 128) && !(d->flags & GL_FLAG_GENERIC) &&
+                          !p->out_f32;
   const size_t dd = static_cast<size_t>(d->d_in) * static_cast<size_t>(d->d_out);
   const size_t BH = static_cast<size_t>(d->B) * static_cast<size_t>(d->H);
   if (mfma_shape && (d->chunk == 0 || d->chunk == gls::kMfmaChunk)) {
@@ -104,7 +110,8 @@ gl_status_t make_plan(const gl_scan_desc_t* d, Plan* p) {
     p->n_tiles = static_cast<int>((std::max(d->d_in, d->d_out) + gls::kGenericTile - 1) /
                                   gls::kGenericTile);
     p->name = (p->io == GL_DTYPE_F64) ? "generic-f64"
-              : (p->io == GL_DTYPE_F32) ? "generic-f32" : "generic-bf16";
+              : (p->io == GL_DTYPE_F32) ? "generic-f32"
+              : p->out_f32 ? "generic-bf16-out-f32" : "generic-bf16";
     p->state_elem = p->comp;
     if (d->segments > 1)
       return fail(GL_ERROR_NOT_SUPPORTED, "segments apply to the matrix-core kernels only");
@@ -178,6 +185,7 @@ gls::FwdArgs fwd_args(const gl_scan_desc_t* d, const Plan& p, const void* x, con
   a.d_in = static_cast<int>(d->d_in); a.d_out = static_cast<int>(d->d_out);
   a.chunk = p.chunk; a.n_chunks = p.n_chunks; a.ckpt_every = p.ckpt_every; a.n_ckpt = p.n_ckpt;
   a.seg_chunks = p.seg_chunks; a.n_seg = p.n_seg;
+  a.out_f32 = p.out_f32;
   return a;
 }
 
@@ -294,7 +302,7 @@ gl_status_t gl_scan_bwd(const gl_scan_desc_t* desc, const void* x, const void* g
     if (desc->H == 0) return GL_SUCCESS;
     if (!dW0) return fail(GL_ERROR_INVALID_VALUE, "dW0 is NULL");
     if (misaligned(dW0)) return fail(GL_ERROR_MISALIGNED, "dW0 not 16-byte aligned");
-    return hip_status(hipMemsetAsync(dW0, 0, desc->H * dd * p.comp, s), "dW0 clear");
+    return hip_status(gls::launch_clear(dW0, desc->H * dd * p.comp, s), "dW0 clear");
   }
   if (!x || !g || !eta || !alpha || !W0 || !dy || !dx || !dg || !deta || !dalpha || !dW0)
     return fail(GL_ERROR_INVALID_VALUE, "NULL input or output pointer");
@@ -331,6 +339,7 @@ gl_status_t gl_scan_bwd(const gl_scan_desc_t* desc, const void* x, const void* g
   b.chunk = p.chunk; b.n_chunks = p.n_chunks; b.ckpt_every = p.ckpt_every; b.n_ckpt = p.n_ckpt;
   b.n_tiles = p.n_tiles;
   b.seg_chunks = p.seg_chunks; b.n_seg = p.n_seg;
+  b.out_f32 = p.out_f32;
   if (!p.mfma) {
     st = hip_status(gls::launch_generic_bwd(p.io, b, s), "backward launch");
   } else {
@@ -481,6 +490,102 @@ gl_status_t gl_scan_qkv_fwd(const gl_scan_desc_t* desc, const void* q, const voi
   a.w0_transposed = w0_transposed != 0;
   return hip_status(gls::launch_qkv_fwd(desc->io_dtype, a, static_cast<hipStream_t>(stream)),
                     "qkv scan launch");
+}
+
+// The reverse scan with a read vector and write key of their own: the forward
+// chunk states recomputed by the generic forward (states only) into the
+// workspace, the generic reverse scan, then the fixed-order sums.  Layout of
+// the workspace: states [B*H][n_chunks][dv][dk], deta / dalpha tile partials
+// [n_tiles][B*H*T] each, dW0 partials [B*H][dv][dk] (compute type).
+namespace {
+struct QkvPlan {
+  int chunk = 0, n_chunks = 0, n_tiles = 0;
+  size_t comp = 8, states = 0, part = 0, dw = 0, total = 0;
+};
+gl_status_t qkv_plan(const gl_scan_desc_t* d, QkvPlan* p) {
+  gl_status_t st = check_dec(d, true);
+  if (st != GL_SUCCESS) return st;
+  const size_t dd = static_cast<size_t>(d->d_in) * static_cast<size_t>(d->d_out);
+  const size_t BH = static_cast<size_t>(d->B) * static_cast<size_t>(d->H);
+  p->comp = d->io_dtype == GL_DTYPE_F64 ? 8 : 4;
+  p->chunk = d->io_dtype == GL_DTYPE_F64 ? 8 : 32;  // LDS of the generic kernels with a read tile
+  p->n_chunks = static_cast<int>((d->T + p->chunk - 1) / p->chunk);
+  p->n_tiles = static_cast<int>((std::max(d->d_in, d->d_out) + gls::kGenericTile - 1) /
+                                gls::kGenericTile);
+  p->states = round_up(BH * p->n_chunks * dd * p->comp);
+  p->part = round_up(static_cast<size_t>(p->n_tiles) * BH * d->T * p->comp);
+  p->dw = round_up(BH * dd * p->comp);
+  p->total = p->states + 2 * p->part + p->dw;
+  return GL_SUCCESS;
+}
+}  // namespace
+
+gl_status_t gl_scan_qkv_workspace_size(const gl_scan_desc_t* desc, size_t* ws_bytes) {
+  QkvPlan p;
+  gl_status_t st = qkv_plan(desc, &p);
+  if (st != GL_SUCCESS) return st;
+  if (!ws_bytes) return fail(GL_ERROR_INVALID_VALUE, "ws_bytes is NULL");
+  *ws_bytes = p.total;
+  return GL_SUCCESS;
+}
+
+gl_status_t gl_scan_qkv_bwd(const gl_scan_desc_t* desc, const void* q, const void* k,
+                            const void* v, const void* eta, const void* alpha, const void* W0,
+                            int w0_transposed, const void* dy, void* dq, void* dk, void* dv,
+                            void* deta, void* dalpha, void* dW0, void* ws, size_t ws_bytes,
+                            void* stream) {
+  QkvPlan p;
+  gl_status_t st = qkv_plan(desc, &p);
+  if (st != GL_SUCCESS) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const size_t dd = static_cast<size_t>(desc->d_in) * static_cast<size_t>(desc->d_out);
+  if (desc->B * desc->H * desc->T == 0) {
+    if (desc->H == 0) return GL_SUCCESS;
+    st = check_ptrs({dW0});
+    if (st != GL_SUCCESS) return st;
+    return hip_status(gls::launch_clear(dW0, desc->H * dd * p.comp, s), "dW0 clear");
+  }
+  st = check_ptrs({q, k, v, eta, alpha, W0, dy, dq, dk, dv, deta, dalpha, dW0, ws});
+  if (st != GL_SUCCESS) return st;
+  if (ws_bytes < p.total)
+    return fail(GL_ERROR_WORKSPACE_TOO_SMALL, "workspace %zu bytes, need %zu", ws_bytes, p.total);
+  char* w = static_cast<char*>(ws);
+  void* states = w;
+  void* part_eta = w + p.states;
+  void* part_alpha = w + p.states + p.part;
+  void* part_dW0 = w + p.states + 2 * p.part;
+
+  gls::FwdArgs f;
+  f.x = k; f.q = q; f.g = v; f.eta = eta; f.alpha = alpha; f.W0 = W0;
+  f.y = nullptr; f.states = states;
+  f.B = desc->B; f.H = desc->H; f.T = desc->T;
+  f.d_in = static_cast<int>(desc->d_in); f.d_out = static_cast<int>(desc->d_out);
+  f.chunk = p.chunk; f.n_chunks = p.n_chunks; f.ckpt_every = 1; f.n_ckpt = p.n_chunks;
+  f.seg_chunks = p.n_chunks; f.n_seg = 1;
+  f.w0_t = w0_transposed != 0;
+  st = hip_status(gls::launch_generic_fwd(desc->io_dtype, f, s), "qkv state recompute");
+  if (st != GL_SUCCESS) return st;
+
+  gls::BwdArgs b;
+  b.x = k; b.q = q; b.g = v; b.eta = eta; b.alpha = alpha; b.W0 = W0; b.dy = dy;
+  b.states = states;
+  b.dx = dk; b.dq = dq; b.dg = dv;
+  b.part_eta = part_eta; b.part_alpha = part_alpha; b.part_dW0 = part_dW0;
+  b.B = desc->B; b.H = desc->H; b.T = desc->T;
+  b.d_in = f.d_in; b.d_out = f.d_out;
+  b.chunk = p.chunk; b.n_chunks = p.n_chunks; b.ckpt_every = 1; b.n_ckpt = p.n_chunks;
+  b.n_tiles = p.n_tiles;
+  b.seg_chunks = p.n_chunks; b.n_seg = 1;
+  b.w0_t = w0_transposed != 0;
+  st = hip_status(gls::launch_generic_bwd(desc->io_dtype, b, s), "qkv backward launch");
+  if (st != GL_SUCCESS) return st;
+
+  gls::FinArgs fa;
+  fa.part_eta = part_eta; fa.part_alpha = part_alpha; fa.part_dW0 = part_dW0;
+  fa.deta = deta; fa.dalpha = dalpha; fa.dW0 = dW0;
+  fa.B = desc->B; fa.H = desc->H; fa.T = desc->T;
+  fa.d_in = f.d_in; fa.d_out = f.d_out; fa.n_tiles = p.n_tiles; fa.n_seg = 1;
+  return hip_status(gls::launch_finalize(desc->io_dtype, fa, s), "qkv finalize launch");
 }
 
 const char* gl_status_string(gl_status_t status) {

@@ -36,6 +36,12 @@ struct FwdArgs {
   const float* seg_in = nullptr;
   float* seg_out = nullptr;
   float* seg_lg = nullptr;
+  // A read vector of its own (generic kernels): y_t = (W0' + D_t) q_t while the
+  // update keeps x as the write key; NULL = read with x.  w0_t: W0' is stored
+  // transposed ([H][d_in][d_out]).  out_f32: y is fp32 (bf16 io only).
+  const void* q = nullptr;
+  bool w0_t = false;
+  bool out_f32 = false;
 };
 
 // Reverse scan.  Work-group (k, b*H+h) owns column tile k of D and Lambda
@@ -73,6 +79,12 @@ struct BwdArgs {
   // Fused backward: deta and dalpha written directly ([B,H,T]).
   void* deta_out = nullptr;
   void* dalpha_out = nullptr;
+  // A read vector of its own (generic kernels; see FwdArgs): x is then the
+  // write key only, dx receives its gradient and dq that of q.
+  const void* q = nullptr;
+  void* dq = nullptr;
+  bool w0_t = false;
+  bool out_f32 = false;   // dx, dg (and dq) in fp32 (bf16 io only)
 };
 
 // Deployment (one token at a time): the cached adaptation `state`
@@ -140,6 +152,8 @@ int generic_default_chunk(int io);
 hipError_t launch_generic_fwd(int io, const FwdArgs& a, hipStream_t s);
 hipError_t launch_generic_bwd(int io, const BwdArgs& a, hipStream_t s);
 hipError_t launch_finalize(int io, const FinArgs& a, hipStream_t s);
+// Zero fill of `bytes` (a multiple of 4) at the 4-byte aligned device pointer p.
+hipError_t launch_clear(void* p, size_t bytes, hipStream_t s);
 hipError_t launch_decode_readout(int io, const DecArgs& a, hipStream_t s);
 hipError_t launch_decode_update(int io, const DecArgs& a, hipStream_t s);
 hipError_t launch_decode_step(int io, const DecArgs& a, hipStream_t s);

@@ -1,13 +1,14 @@
 // k_decode.hip -- deployment: one token at a time against the cached
 // adaptation (any io dtype, 1 <= d_in, d_out <= 128).
 //
-// Deployment runs the learner serially: for each new token the layer reads
-// out from the cached weight, the network's backward pass supplies the
-// token's costate g, and the cache takes one exact gradient step ("Parallelize
-// the Training, Keep the Learning Serial", cognaptus.com, section "The
-// bottleneck appears before deployment"; ParaTTT news summary, section
-// "Perspective": a single new token is one exact gradient step from the
-// cached weights, with no iteration).  With the cached adaptation D = W - W0:
+// At deployment the learner runs token by token: the layer reads out with
+// the cached weight, the network's backward pass returns the costate g of
+// that token, and the cache is advanced by the recurrence's update for that
+// one token ("Parallelize the Training, Keep the Learning Serial",
+// cognaptus.com, section "The bottleneck appears before deployment"; ParaTTT
+// news summary, section "Perspective": decoding needs no iteration, each
+// token costs a single update of the cache).  With the cached adaptation
+// D = W - W0:
 //   readout:  y = (W0 + D) x
 //   update:   D <- alpha D - eta g x^T
 //   step:     the update of token t, then the readout of token t + 1 (the

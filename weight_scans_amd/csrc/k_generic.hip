@@ -13,8 +13,9 @@
 // The adaptation read by token i and the adjoint after token i are
 //   D_i   = e^{l_{i-1}} D_in + sum_{j<i} Mf_ij (-eta_j) g_j x_j^T
 //   Lam_i = e^{l_{cv-1}-l_i} Lam_out + sum_{u>i} Mf_ui dy_u x_u^T
-// which is the "discounted sum of earlier rank-one gradient updates" of
-// "Parallelize the Training, Keep the Learning Serial" (cognaptus.com, section
+// i.e. the correction is a sum of the earlier rank-one updates, each damped by
+// the retention gates applied after it ("Parallelize the Training, Keep the
+// Learning Serial", cognaptus.com, section
 // "Once the gradient signals are known, the weight trajectory becomes
 // parallelizable"), composed chunk to chunk as an affine scan:
 //   D_out  = Gamma D_in  + sum_j e^{l_{cv-1}-l_j} (-eta_j) g_j x_j^T
@@ -32,13 +33,16 @@ constexpr int kThreads = 256;
 // ---------------------------------------------------------------------------
 // Forward: grid (B*H, ceil(d_out / TN)).  The row tile [r0, r0+TN) of D lives
 // in LDS across chunks; each chunk forms the causal decayed score matrix
-// A_ij = Mf_ij (x_i . x_j)(-eta_j) and emits
-//   y_i = W0 x_i + e^{l_{i-1}} D_in x_i + sum_{j<i} A_ij g_j.
+// A_ij = Mf_ij (q_i . x_j)(-eta_j) and emits
+//   y_i = W0 q_i + e^{l_{i-1}} D_in q_i + sum_{j<i} A_ij g_j,
+// with q = x (the scan) or, with QK, a read vector of its own (x is then
+// only the write key).  OT is the type y is stored in.
 // ---------------------------------------------------------------------------
-template <typename T, typename IO, int C, int TN>
+template <typename T, typename IO, typename OT, int C, int TN, bool QK>
 __global__ __launch_bounds__(kThreads) void fwd_generic(FwdArgs a) {
   constexpr int DM = kGenericMaxD, P = DM + 1;
   __shared__ T sX[C][P];
+  __shared__ T sQv[QK ? C : 1][QK ? P : 1];
   __shared__ T sG[C][TN];
   __shared__ T sA[C][C + 1];
   __shared__ T sS[TN][P];
@@ -53,16 +57,23 @@ __global__ __launch_bounds__(kThreads) void fwd_generic(FwdArgs a) {
   const int din = a.d_in, dout = a.d_out;
   const int nr = min(TN, dout - r0);
   const IO* x = static_cast<const IO*>(a.x) + bh * a.T * din;
+  const IO* q = QK ? static_cast<const IO*>(a.q) + bh * a.T * din : x;
   const IO* g = static_cast<const IO*>(a.g) + bh * a.T * dout;
   const T* eta = static_cast<const T*>(a.eta) + bh * a.T;
   const T* alpha = static_cast<const T*>(a.alpha) + bh * a.T;
   const IO* W0 = static_cast<const IO*>(a.W0) + static_cast<int64_t>(h) * dout * din;
-  IO* y = a.y ? static_cast<IO*>(a.y) + bh * a.T * dout : nullptr;
+  OT* y = a.y ? static_cast<OT*>(a.y) + bh * a.T * dout : nullptr;
+  // the read vectors: the key tile itself, or a tile of their own
+  const auto QT = [&](int i, int k) -> T {
+    if constexpr (QK) return sQv[i][k]; else return sX[i][k];
+  };
 
   for (int idx = tid; idx < TN * din; idx += kThreads) {
     const int r = idx / din, k = idx % din;
     sS[r][k] = T(0);
-    sW[r][k] = (r < nr) ? load_as<T>(W0, static_cast<int64_t>(r0 + r) * din + k) : T(0);
+    const int64_t wi = a.w0_t ? static_cast<int64_t>(k) * dout + r0 + r
+                              : static_cast<int64_t>(r0 + r) * din + k;
+    sW[r][k] = (r < nr) ? load_as<T>(W0, wi) : T(0);
   }
   __syncthreads();
 
@@ -74,8 +85,10 @@ __global__ __launch_bounds__(kThreads) void fwd_generic(FwdArgs a) {
               ((bh * a.n_ckpt + c / a.ckpt_every) * dout + r0) * static_cast<int64_t>(din);
       for (int idx = tid; idx < nr * din; idx += kThreads) st[idx] = sS[idx / din][idx % din];
     }
-    for (int idx = tid; idx < cv * din; idx += kThreads)
+    for (int idx = tid; idx < cv * din; idx += kThreads) {
       sX[idx / din][idx % din] = load_as<T>(x, (t0 + idx / din) * din + idx % din);
+      if constexpr (QK) sQv[idx / din][idx % din] = load_as<T>(q, (t0 + idx / din) * din + idx % din);
+    }
     for (int idx = tid; idx < cv * TN; idx += kThreads) {
       const int i = idx / TN, r = idx % TN;
       sG[i][r] = (r < nr) ? load_as<T>(g, (t0 + i) * dout + r0 + r) : T(0);
@@ -98,7 +111,7 @@ __global__ __launch_bounds__(kThreads) void fwd_generic(FwdArgs a) {
       T v = T(0);
       if (j < i && i < cv) {
         T dot = T(0);
-        for (int k = 0; k < din; ++k) dot += sX[i][k] * sX[j][k];
+        for (int k = 0; k < din; ++k) dot += QT(i, k) * sX[j][k];
         v = dot * exp(sL[i - 1] - sL[j]) * (-sEta[j]);
       }
       sA[i][j] = v;
@@ -111,8 +124,8 @@ __global__ __launch_bounds__(kThreads) void fwd_generic(FwdArgs a) {
         if (r >= nr) continue;
         T a0 = T(0), a1 = T(0), a2 = T(0);
         for (int k = 0; k < din; ++k) {
-          a0 += sW[r][k] * sX[i][k];
-          a1 += sS[r][k] * sX[i][k];
+          a0 += sW[r][k] * QT(i, k);
+          a1 += sS[r][k] * QT(i, k);
         }
         for (int j = 0; j < i; ++j) a2 += sA[i][j] * sG[j][r];
         store_from<T>(y, (t0 + i) * dout + r0 + r, a0 + sQ[i] * a1 + a2);
@@ -134,22 +147,26 @@ __global__ __launch_bounds__(kThreads) void fwd_generic(FwdArgs a) {
 // Backward: grid (B*H, n_tiles), reverse over chunks.  Work-group k holds
 //   columns K = [k0, k0+TK) of D_in (from the stored chunk states) and of Lam,
 //   rows    R = [k0, k0+TK) of Lam,  and the columns K of dW0.
-// Per chunk, with Be_ij = Mf_ij (dy_i . g_j)(-eta_j) and P_ij = Mf_ij (x_i.x_j)
-// for j < i (zero otherwise):
-//   dx_i[K]  = W0[:,K]^T dy_i + e^{l_{i-1}} D_in[:,K]^T dy_i
-//              + sum_j (Be_ij + Be_ji) x_j[K] - eta_i e^{l_{cv-1}-l_i} Lam_out[:,K]^T g_i
+// With q the read vector and x the write key (q = x for the scan), per chunk,
+// for j < i:  Be_ij = Mf_ij (dy_i . g_j)(-eta_j),  P_ij = Mf_ij (q_i . x_j):
+//   dq_i[K]  = W0[:,K]^T dy_i + e^{l_{i-1}} D_in[:,K]^T dy_i + sum_{j<i} Be_ij x_j[K]
+//   dx_i[K]  = -eta_i e^{l_{cv-1}-l_i} Lam_out[:,K]^T g_i + sum_{u>i} Be_ui q_u[K]
+//              (the scan returns dq + dx as dx)
 //   u_i[R]   = e^{l_{cv-1}-l_i} Lam_out[R,:] x_i + sum_{u>i} P_ui dy_u[R]
 //   dg_i[R]  = -eta_i u_i[R],  deta_i partial = -g_i[R] . u_i[R]
 //   dalpha_i = <Lam_i, D_i> = e^{l_{cv-1}-l_i+l_{i-1}} <Lam_out, D_in>
 //              + e^{l_{cv-1}-l_i} sum_{j<i} Mf_ij (-eta_j) x_j.(Lam_out^T g_j)
-//              + e^{l_{i-1}} sum_{u>i} Mf_ui x_u.(D_in^T dy_u)
-//              + (1/alpha_i) sum_{u>i, j<i} Be_uj (x_u . x_j)
-//   (the first three split over column tiles; the last is added by tile 0).
+//              + e^{l_{i-1}} sum_{u>i} Mf_ui q_u.(D_in^T dy_u)
+//              + (1/alpha_i) sum_{u>i, j<i} Be_uj (q_u . x_j)
+//   (the first three split over column tiles; the last is added by tile 0),
+//   Lam_in = Gamma Lam_out + sum_u e^{l_{u-1}} dy_u q_u^T,  dW0 += dy_u q_u^T.
+// OT is the type dx, dg and dq are stored in.
 // ---------------------------------------------------------------------------
-template <typename T, typename IO, int C, int TK>
+template <typename T, typename IO, typename OT, int C, int TK, bool QK>
 __global__ __launch_bounds__(kThreads) void bwd_generic(BwdArgs a) {
   constexpr int DM = kGenericMaxD, P = DM + 1, PK = TK + 1;
   __shared__ T sX[C][P], sG[C][P], sD[C][P];
+  __shared__ T sQv[QK ? C : 1][QK ? P : 1];
   __shared__ T sPm[C][C + 1], sBe[C][C + 1], sZ[C][C + 1];
   __shared__ T sSin[DM][PK], sLk[DM][PK], sW[DM][PK], sdW[DM][PK];
   __shared__ T sLr[TK][P];
@@ -168,21 +185,28 @@ __global__ __launch_bounds__(kThreads) void bwd_generic(BwdArgs a) {
   const int nrr = max(0, min(TK, dout - k0));  // rows of this tile
   const int64_t BHT = a.B * a.H * a.T;
   const IO* x = static_cast<const IO*>(a.x) + bh * a.T * din;
+  const IO* q = QK ? static_cast<const IO*>(a.q) + bh * a.T * din : x;
   const IO* g = static_cast<const IO*>(a.g) + bh * a.T * dout;
   const IO* dy = static_cast<const IO*>(a.dy) + bh * a.T * dout;
   const T* eta = static_cast<const T*>(a.eta) + bh * a.T;
   const T* alpha = static_cast<const T*>(a.alpha) + bh * a.T;
   const IO* W0 = static_cast<const IO*>(a.W0) + static_cast<int64_t>(h) * dout * din;
-  IO* dx = static_cast<IO*>(a.dx) + bh * a.T * din;
-  IO* dg = static_cast<IO*>(a.dg) + bh * a.T * dout;
+  OT* dx = static_cast<OT*>(a.dx) + bh * a.T * din;
+  OT* dq = QK ? static_cast<OT*>(a.dq) + bh * a.T * din : nullptr;
+  OT* dg = static_cast<OT*>(a.dg) + bh * a.T * dout;
   T* pe = static_cast<T*>(a.part_eta) + k * BHT + bh * a.T;
   T* pa = static_cast<T*>(a.part_alpha) + k * BHT + bh * a.T;
+  const auto QT = [&](int i, int kk) -> T {
+    if constexpr (QK) return sQv[i][kk]; else return sX[i][kk];
+  };
 
   for (int idx = tid; idx < dout * TK; idx += kThreads) {
     const int r = idx / TK, kk = idx % TK;
     sLk[r][kk] = T(0);
     sdW[r][kk] = T(0);
-    sW[r][kk] = (kk < nk) ? load_as<T>(W0, static_cast<int64_t>(r) * din + k0 + kk) : T(0);
+    const int64_t wi = a.w0_t ? static_cast<int64_t>(k0 + kk) * dout + r
+                              : static_cast<int64_t>(r) * din + k0 + kk;
+    sW[r][kk] = (kk < nk) ? load_as<T>(W0, wi) : T(0);
   }
   for (int idx = tid; idx < TK * din; idx += kThreads) sLr[idx / din][idx % din] = T(0);
   __syncthreads();
@@ -190,8 +214,10 @@ __global__ __launch_bounds__(kThreads) void bwd_generic(BwdArgs a) {
   for (int c = a.n_chunks - 1; c >= 0; --c) {
     const int64_t t0 = static_cast<int64_t>(c) * C;
     const int cv = static_cast<int>(min(static_cast<int64_t>(C), a.T - t0));
-    for (int idx = tid; idx < cv * din; idx += kThreads)
+    for (int idx = tid; idx < cv * din; idx += kThreads) {
       sX[idx / din][idx % din] = load_as<T>(x, (t0 + idx / din) * din + idx % din);
+      if constexpr (QK) sQv[idx / din][idx % din] = load_as<T>(q, (t0 + idx / din) * din + idx % din);
+    }
     for (int idx = tid; idx < cv * dout; idx += kThreads) {
       const int i = idx / dout, r = idx % dout;
       sG[i][r] = load_as<T>(g, (t0 + i) * dout + r);
@@ -229,8 +255,8 @@ __global__ __launch_bounds__(kThreads) void bwd_generic(BwdArgs a) {
       T p = T(0), be = T(0), z = T(0);
       if (j < i && i < cv) {
         T xx = T(0), dgd = T(0);
-        for (int q = 0; q < din; ++q) xx += sX[i][q] * sX[j][q];
-        for (int q = 0; q < dout; ++q) dgd += sD[i][q] * sG[j][q];
+        for (int qq = 0; qq < din; ++qq) xx += QT(i, qq) * sX[j][qq];
+        for (int qq = 0; qq < dout; ++qq) dgd += sD[i][qq] * sG[j][qq];
         const T mf = exp(sL[i - 1] - sL[j]);
         p = mf * xx;
         be = mf * dgd * (-sEta[j]);
@@ -250,7 +276,7 @@ __global__ __launch_bounds__(kThreads) void bwd_generic(BwdArgs a) {
         }
       }
       if (kk < nrr)
-        for (int q = 0; q < din; ++q) lx += sLr[kk][q] * sX[i][q];
+        for (int qq = 0; qq < din; ++qq) lx += sLr[kk][qq] * sX[i][qq];
       sLg[i][kk] = lg;
       sSd[i][kk] = sd;
       sLx[i][kk] = lx;
@@ -267,15 +293,15 @@ __global__ __launch_bounds__(kThreads) void bwd_generic(BwdArgs a) {
     __syncthreads();
 
     if (tid == 0) {
-      T s = T(0);
-      for (int q = 0; q < kThreads; ++q) s += sRed[q];
-      sC0 = s;
+      T sm = T(0);
+      for (int qq = 0; qq < kThreads; ++qq) sm += sRed[qq];
+      sC0 = sm;
     }
     if (tid < cv) {
       T pj = T(0), ru = T(0);
       for (int kk = 0; kk < nk; ++kk) {
         pj += sX[tid][k0 + kk] * sLg[tid][kk];
-        ru += sX[tid][k0 + kk] * sSd[tid][kk];
+        ru += QT(tid, k0 + kk) * sSd[tid][kk];
       }
       sPj[tid] = pj;
       sRu[tid] = ru;
@@ -286,12 +312,18 @@ __global__ __launch_bounds__(kThreads) void bwd_generic(BwdArgs a) {
       const int i = idx / TK, kk = idx % TK;
       if (kk >= nk) continue;
       const int col = k0 + kk;
-      T v = T(0);
-      for (int r = 0; r < dout; ++r) v += sW[r][kk] * sD[i][r];
-      v += sE1[i] * sSd[i][kk] - sEta[i] * sE2[i] * sLg[i][kk];
-      for (int j = 0; j < i; ++j) v += sBe[i][j] * sX[j][col];
-      for (int j = i + 1; j < cv; ++j) v += sBe[j][i] * sX[j][col];
-      store_from<T>(dx, (t0 + i) * din + col, v);
+      T vq = T(0);
+      for (int r = 0; r < dout; ++r) vq += sW[r][kk] * sD[i][r];
+      vq += sE1[i] * sSd[i][kk];
+      for (int j = 0; j < i; ++j) vq += sBe[i][j] * sX[j][col];
+      T vk = -sEta[i] * sE2[i] * sLg[i][kk];
+      for (int j = i + 1; j < cv; ++j) vk += sBe[j][i] * QT(j, col);
+      if constexpr (QK) {
+        store_from<T>(dq, (t0 + i) * din + col, vq);
+        store_from<T>(dx, (t0 + i) * din + col, vk);
+      } else {
+        store_from<T>(dx, (t0 + i) * din + col, vq + vk);
+      }
     }
     if (tid < cv) {
       const int i = tid;
@@ -323,19 +355,19 @@ __global__ __launch_bounds__(kThreads) void bwd_generic(BwdArgs a) {
       const int col = k0 + kk;
       T s1 = T(0), s2 = T(0);
       for (int u = 0; u < cv; ++u) {
-        const T p = sD[u][r] * sX[u][col];
-        s1 += sE1[u] * p;
-        s2 += p;
+        const T pr = sD[u][r] * QT(u, col);
+        s1 += sE1[u] * pr;
+        s2 += pr;
       }
       sLk[r][kk] = sGam * sLk[r][kk] + s1;
       sdW[r][kk] += s2;
     }
     for (int idx = tid; nrr > 0 && idx < nrr * din; idx += kThreads) {
-      const int rr = idx / din, q = idx % din;
+      const int rr = idx / din, qq = idx % din;
       const int r = k0 + rr;
       T s1 = T(0);
-      for (int u = 0; u < cv; ++u) s1 += sE1[u] * sD[u][r] * sX[u][q];
-      sLr[rr][q] = sGam * sLr[rr][q] + s1;
+      for (int u = 0; u < cv; ++u) s1 += sE1[u] * sD[u][r] * QT(u, qq);
+      sLr[rr][qq] = sGam * sLr[rr][qq] + s1;
     }
     __syncthreads();
   }
@@ -343,7 +375,9 @@ __global__ __launch_bounds__(kThreads) void bwd_generic(BwdArgs a) {
   T* pw = static_cast<T*>(a.part_dW0) + bh * static_cast<int64_t>(dout) * din;
   for (int idx = tid; nk > 0 && idx < dout * nk; idx += kThreads) {
     const int r = idx / nk, kk = idx % nk;
-    pw[static_cast<int64_t>(r) * din + k0 + kk] = sdW[r][kk];
+    const int64_t wi = a.w0_t ? static_cast<int64_t>(k0 + kk) * dout + r
+                              : static_cast<int64_t>(r) * din + k0 + kk;
+    pw[wi] = sdW[r][kk];
   }
 }
 
@@ -399,18 +433,50 @@ __global__ __launch_bounds__(kThreads) void finalize_kernel(FinArgs a) {
   }
 }
 
-template <typename T, typename IO, int C>
+// Zero fill of n 4-byte words (a kernel rather than a memset node, so that a
+// captured graph replays it like any other launch).
+__global__ __launch_bounds__(kThreads) void clear_kernel(uint32_t* p, int64_t n) {
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  for (int64_t i = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; i < n; i += stride)
+    p[i] = 0u;
+}
+
+template <typename T, typename IO, typename OT, int C, bool QK>
 hipError_t fwd_c(const FwdArgs& a, hipStream_t s) {
   dim3 grid(static_cast<unsigned>(a.B * a.H), (a.d_out + kGenericTile - 1) / kGenericTile);
-  hipLaunchKernelGGL((fwd_generic<T, IO, C, kGenericTile>), grid, dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL((fwd_generic<T, IO, OT, C, kGenericTile, QK>), grid, dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
-template <typename T, typename IO, int C>
+template <typename T, typename IO, typename OT, int C, bool QK>
 hipError_t bwd_c(const BwdArgs& a, hipStream_t s) {
   dim3 grid(static_cast<unsigned>(a.B * a.H), a.n_tiles);
-  hipLaunchKernelGGL((bwd_generic<T, IO, C, kGenericTile>), grid, dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL((bwd_generic<T, IO, OT, C, kGenericTile, QK>), grid, dim3(kThreads), 0, s, a);
   return hipGetLastError();
+}
+
+// chunk dispatch (the host has checked the chunk against generic_chunk_ok)
+template <typename T, typename IO, typename OT, bool QK>
+hipError_t fwd_q(const FwdArgs& a, hipStream_t s) {
+  if (a.chunk == 8) return fwd_c<T, IO, OT, 8, QK>(a, s);
+  if constexpr (sizeof(T) == 8) {
+    return fwd_c<T, IO, OT, 16, QK>(a, s);
+  } else {
+    if (a.chunk == 16) return fwd_c<T, IO, OT, 16, QK>(a, s);
+    return fwd_c<T, IO, OT, 32, QK>(a, s);
+  }
+}
+template <typename T, typename IO, typename OT, bool QK>
+hipError_t bwd_q(const BwdArgs& a, hipStream_t s) {
+  if (a.chunk == 8) return bwd_c<T, IO, OT, 8, QK>(a, s);
+  if constexpr (sizeof(T) == 8) {
+    // fp64 with a read vector of its own fits LDS at chunk 8 only
+    if constexpr (QK) return hipErrorInvalidValue;
+    else return bwd_c<T, IO, OT, 16, QK>(a, s);
+  } else {
+    if (a.chunk == 16) return bwd_c<T, IO, OT, 16, QK>(a, s);
+    return bwd_c<T, IO, OT, 32, QK>(a, s);
+  }
 }
 
 }  // namespace
@@ -423,33 +489,39 @@ bool generic_chunk_ok(int io, int chunk) {
 int generic_default_chunk(int io) { return io == IO_F64 ? 16 : 32; }
 
 hipError_t launch_generic_fwd(int io, const FwdArgs& a, hipStream_t s) {
+  const bool qk = a.q != nullptr;
   switch (io) {
     case IO_F64:
-      return a.chunk == 8 ? fwd_c<double, double, 8>(a, s) : fwd_c<double, double, 16>(a, s);
+      return qk ? fwd_q<double, double, double, true>(a, s) : fwd_q<double, double, double, false>(a, s);
     case IO_F32:
-      if (a.chunk == 8) return fwd_c<float, float, 8>(a, s);
-      if (a.chunk == 16) return fwd_c<float, float, 16>(a, s);
-      return fwd_c<float, float, 32>(a, s);
+      return qk ? fwd_q<float, float, float, true>(a, s) : fwd_q<float, float, float, false>(a, s);
     default:
-      if (a.chunk == 8) return fwd_c<float, bf16, 8>(a, s);
-      if (a.chunk == 16) return fwd_c<float, bf16, 16>(a, s);
-      return fwd_c<float, bf16, 32>(a, s);
+      if (a.out_f32)
+        return qk ? fwd_q<float, bf16, float, true>(a, s) : fwd_q<float, bf16, float, false>(a, s);
+      return qk ? fwd_q<float, bf16, bf16, true>(a, s) : fwd_q<float, bf16, bf16, false>(a, s);
   }
 }
 
 hipError_t launch_generic_bwd(int io, const BwdArgs& a, hipStream_t s) {
+  const bool qk = a.q != nullptr;
   switch (io) {
     case IO_F64:
-      return a.chunk == 8 ? bwd_c<double, double, 8>(a, s) : bwd_c<double, double, 16>(a, s);
+      return qk ? bwd_q<double, double, double, true>(a, s) : bwd_q<double, double, double, false>(a, s);
     case IO_F32:
-      if (a.chunk == 8) return bwd_c<float, float, 8>(a, s);
-      if (a.chunk == 16) return bwd_c<float, float, 16>(a, s);
-      return bwd_c<float, float, 32>(a, s);
+      return qk ? bwd_q<float, float, float, true>(a, s) : bwd_q<float, float, float, false>(a, s);
     default:
-      if (a.chunk == 8) return bwd_c<float, bf16, 8>(a, s);
-      if (a.chunk == 16) return bwd_c<float, bf16, 16>(a, s);
-      return bwd_c<float, bf16, 32>(a, s);
+      if (a.out_f32)
+        return qk ? bwd_q<float, bf16, float, true>(a, s) : bwd_q<float, bf16, float, false>(a, s);
+      return qk ? bwd_q<float, bf16, bf16, true>(a, s) : bwd_q<float, bf16, bf16, false>(a, s);
   }
+}
+
+hipError_t launch_clear(void* p, size_t bytes, hipStream_t s) {
+  const int64_t n = static_cast<int64_t>(bytes / 4);
+  if (n == 0) return hipSuccess;
+  const unsigned blocks = static_cast<unsigned>(std::min<int64_t>(1024, (n + kThreads - 1) / kThreads));
+  hipLaunchKernelGGL(clear_kernel, dim3(blocks), dim3(kThreads), 0, s, static_cast<uint32_t*>(p), n);
+  return hipGetLastError();
 }
 
 hipError_t launch_finalize(int io, const FinArgs& a, hipStream_t s) {

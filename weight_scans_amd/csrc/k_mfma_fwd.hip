@@ -9,10 +9,10 @@
 //   A_ij  = (x_i . x_j) e(lq_i - l_j) (-eta_j)        j < i  (else 0)
 //   y_i   = W0 x_i + e(lq_i) D_in x_i + sum_j A_ij g_j
 //   D_out = e(l_last) D_in + sum_j e(l_last - l_j)(-eta_j) g_j x_j^T
-// i.e. the discounted sum of rank-one updates of "Parallelize the Training,
-// Keep the Learning Serial" (cognaptus.com, section "Once the gradient signals
-// are known, the weight trajectory becomes parallelizable") composed as an
-// affine scan across chunks.  Every exponent is <= 0.
+// i.e. earlier rank-one updates damped by the later gates, composed as an
+// affine scan across chunks ("Parallelize the Training, Keep the Learning
+// Serial", cognaptus.com, section "Once the gradient signals are known, the
+// weight trajectory becomes parallelizable").  Every exponent is <= 0.
 //
 // Pipeline (one work-group barrier per chunk): chunk tiles are copied
 // HBM -> LDS by direct buffer loads into a ring of kRing slots; while chunk c
