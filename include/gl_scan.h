@@ -127,6 +127,23 @@ gl_status_t gl_scan_bwd(const gl_scan_desc_t* desc, const void* x, const void* g
                         void* deta, void* dalpha, void* dW0, void* ws,
                         size_t ws_bytes, void* stream);
 
+/* gl_scan_bwd for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same reverse scan, arguments and results as gl_scan_bwd, without a
+ * workspace argument.  Its scratch memory is a static device buffer of 64 MiB
+ * per GPU that the library holds until the process ends; nothing is
+ * allocated or freed by the call.  A descriptor whose backward needs more
+ * scratch than that (gl_scan_workspace_size's bwd figure; passing the
+ * forward's `saved` keeps it small) returns GL_ERROR_WORKSPACE_TOO_SMALL before
+ * anything is launched.  Every call on one GPU shares that GPU's buffer:
+ * calls that overlap in time on one GPU (two streams, two threads) race and
+ * must be serialised by the caller.  The buffer keeps the last call's
+ * contents; no kernel relies on it being zero. */
+gl_status_t gl_scan_bwd_static(const gl_scan_desc_t* desc, const void* x, const void* g,
+                               const void* eta, const void* alpha, const void* W0,
+                               const void* dy, const void* saved, void* dx, void* dg,
+                               void* deta, void* dalpha, void* dW0, void* stream);
+
 /* ---- Deployment: one token at a time, and the prefill -> decode handoff.
  *
  * Once trained, the learner runs token by token: the layer reads out with its

@@ -251,3 +251,15 @@ def test_decode_ignores_the_scan_only_fields():
     bad_scan = desc(chunk=48, segments=7, T=-3)
     assert _dec("gl_decode_readout", bad_scan, [None] * 4) == 1  # still needs pointers
     assert _dec("gl_scan_final_state", bad_scan, [FAKE] * 5) == 1  # negative T
+
+
+def test_static_backward_refuses_a_workspace_beyond_its_scratch():
+    # checked before the scratch address is taken or anything is launched
+    d = desc(B=8, H=16, T=32768, d_in=128, d_out=128)
+    _, need = ws.workspace_size(d, False)
+    assert need > 64 << 20
+    f = ctypes.c_void_p(FAKE)
+    st = ws.lib().gl_scan_bwd_static(ctypes.byref(d), *([f] * 6), None, *([f] * 5), None)
+    assert st == 4 and b"static scratch" in ws.lib().gl_last_error()
+    # argument errors come first, as in gl_scan_bwd
+    assert ws.lib().gl_scan_bwd_static(None, *([f] * 12), None) == 1

@@ -45,6 +45,7 @@ EXPORTS = (
     "gl_scan_qkv_fwd",
     "gl_scan_qkv_workspace_size",
     "gl_scan_qkv_bwd",
+    "gl_scan_bwd_static",
 )
 
 GL_FLAG_GENERIC = 1
@@ -92,11 +93,12 @@ def lib():
         L.gl_costate_quadratic.argtypes = [pd] + [P] * 7
         L.gl_scan_qkv_fwd.argtypes = [pd] + [P] * 6 + [I] + [P] * 2
         L.gl_scan_qkv_workspace_size.argtypes = [pd, ps]
+        L.gl_scan_bwd_static.argtypes = [pd] + [P] * 12 + [P]
         L.gl_scan_qkv_bwd.argtypes = [pd] + [P] * 6 + [I] + [P] * 7 + [P, S, P]
         for f in ("gl_scan_saved_size", "gl_scan_workspace_size", "gl_scan_fwd", "gl_scan_bwd",
                   "gl_decode_readout", "gl_decode_update", "gl_decode_step",
                   "gl_scan_final_state", "gl_costate_quadratic", "gl_scan_qkv_fwd",
-                  "gl_scan_qkv_workspace_size", "gl_scan_qkv_bwd"):
+                  "gl_scan_qkv_workspace_size", "gl_scan_qkv_bwd", "gl_scan_bwd_static"):
             getattr(L, f).restype = ctypes.c_int
         L.gl_status_string.argtypes = [I]
         L.gl_status_string.restype = ctypes.c_char_p
@@ -229,6 +231,29 @@ def gl_scan_bwd(x, g, eta, alpha, W0, dy, saved=None, *, chunk=0, flags=0, segme
     _check(lib().gl_scan_bwd(ctypes.byref(desc), _ptr(x), _ptr(g), _ptr(eta), _ptr(alpha),
                              _ptr(W0), _ptr(dy), _ptr(saved), _ptr(dx), _ptr(dg), _ptr(deta),
                              _ptr(dalpha), _ptr(dW0), _ptr(ws), bws, _stream(x.device)))
+    return dx, dg, deta, dalpha, dW0
+
+
+def gl_scan_bwd_static(x, g, eta, alpha, W0, dy, saved=None, *, chunk=0, flags=0, segments=0,
+                       out=None):
+    """gl_scan_bwd through the no-allocation entry point (the library's static
+    scratch, no workspace).  `out` may hold preallocated (dx, dg, deta, dalpha,
+    dW0); returns them."""
+    torch = _torch()
+    B, H, T, d_in, d_out = _validate(x, g, eta, alpha, W0, dy)
+    desc = make_desc(B, H, T, d_in, d_out, _io_code(x.dtype), chunk, flags, segments)
+    if out is None:
+        gd = gate_dtype(x.dtype)
+        od = _out_dtype(x.dtype, flags)
+        out = (torch.empty(x.shape, dtype=od, device=x.device),
+               torch.empty(g.shape, dtype=od, device=x.device),
+               torch.empty_like(eta), torch.empty_like(alpha),
+               torch.empty((H, d_out, d_in), dtype=gd, device=x.device))
+    dx, dg, deta, dalpha, dW0 = out
+    _check(lib().gl_scan_bwd_static(ctypes.byref(desc), _ptr(x), _ptr(g), _ptr(eta),
+                                    _ptr(alpha), _ptr(W0), _ptr(dy), _ptr(saved), _ptr(dx),
+                                    _ptr(dg), _ptr(deta), _ptr(dalpha), _ptr(dW0),
+                                    _stream(x.device)))
     return dx, dg, deta, dalpha, dW0
 
 

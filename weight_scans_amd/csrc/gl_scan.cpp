@@ -388,6 +388,29 @@ gl_status_t gl_scan_bwd(const gl_scan_desc_t* desc, const void* x, const void* g
   return hip_status(gls::launch_finalize(p.io, f, s), "finalize launch");
 }
 
+gl_status_t gl_scan_bwd_static(const gl_scan_desc_t* desc, const void* x, const void* g,
+                               const void* eta, const void* alpha, const void* W0,
+                               const void* dy, const void* saved, void* dx, void* dg,
+                               void* deta, void* dalpha, void* dW0, void* stream) {
+  Plan p;
+  gl_status_t st = make_plan(desc, &p);
+  if (st != GL_SUCCESS) return st;
+  if (desc->B * desc->H * desc->T == 0)  // only the zero dW0: no scratch
+    return gl_scan_bwd(desc, x, g, eta, alpha, W0, dy, saved, dx, dg, deta, dalpha, dW0,
+                       nullptr, 0, stream);
+  const size_t need = bwd_ws(p, saved != nullptr);
+  if (need > gls::kStaticScratchBytes)
+    return fail(GL_ERROR_WORKSPACE_TOO_SMALL,
+                "this backward needs %zu bytes of scratch; the static scratch holds %zu "
+                "(pass the forward's saved states, or use gl_scan_bwd with a workspace)",
+                need, gls::kStaticScratchBytes);
+  void* ws = nullptr;
+  st = hip_status(gls::static_scratch(&ws), "static scratch address");
+  if (st != GL_SUCCESS) return st;
+  return gl_scan_bwd(desc, x, g, eta, alpha, W0, dy, saved, dx, dg, deta, dalpha, dW0, ws,
+                     gls::kStaticScratchBytes, stream);
+}
+
 gl_status_t gl_decode_readout(const gl_scan_desc_t* desc, const void* x, const void* W0,
                               const void* state, void* y, void* stream) {
   gl_status_t st = check_dec(desc, false);

@@ -152,6 +152,10 @@ int generic_default_chunk(int io);
 hipError_t launch_generic_fwd(int io, const FwdArgs& a, hipStream_t s);
 hipError_t launch_generic_bwd(int io, const BwdArgs& a, hipStream_t s);
 hipError_t launch_finalize(int io, const FinArgs& a, hipStream_t s);
+// The no-allocation backward: the device address, on the current device, of
+// a static scratch buffer of kStaticScratchBytes (taken once per device).
+constexpr size_t kStaticScratchBytes = size_t(64) << 20;
+hipError_t static_scratch(void** ptr);
 // Zero fill of `bytes` (a multiple of 4) at the 4-byte aligned device pointer p.
 hipError_t launch_clear(void* p, size_t bytes, hipStream_t s);
 hipError_t launch_decode_readout(int io, const DecArgs& a, hipStream_t s);
