@@ -68,7 +68,8 @@ def test_descriptor_validation(kw, code):
 @pytest.mark.parametrize("kw,path", [
     (dict(), "mfma-bf16-d64"), (dict(chunk=64), "mfma-bf16-d64"),
     (dict(chunk=16), "generic-bf16"), (dict(chunk=32), "generic-bf16"),
-    (dict(flags=ws.GL_FLAG_OUT_F32), "generic-bf16-out-f32"),
+    (dict(flags=ws.GL_FLAG_OUT_F32), "mfma-bf16-d64"),
+    (dict(flags=ws.GL_FLAG_OUT_F32 | ws.GL_FLAG_GENERIC), "generic-bf16-out-f32"),
     (dict(io_dtype=ws.GL_DTYPE_F32, flags=ws.GL_FLAG_OUT_F32), "generic-f32"),
     (dict(io_dtype=ws.GL_DTYPE_F64, chunk=8), "generic-f64"),
     (dict(io_dtype=ws.GL_DTYPE_F64, chunk=16), "generic-f64"),

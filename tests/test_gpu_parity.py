@@ -13,8 +13,9 @@ import pytest
 import torch
 
 import weight_scans_amd as ws
-from parity_util import (NAMES, TOL, compare_full, compare_sampled, host, oracle_all,
-                         oracle_sampled, relmax, run_gpu, to_device)
+from parity_util import (NAMES, TOL, compare_full, compare_sampled, error_stats, host,
+                         oracle_all, oracle_sampled, relmax, run_gpu, stats_ok, to_device)
+import oracle
 from weight_scans_amd.synth import CONFIGS, Workload, make_inputs
 
 pytestmark = pytest.mark.gpu
@@ -82,6 +83,31 @@ def test_large_sampled(name, pairs, head):
     assert not bad, "\n".join(f"{k}: {v:.3e}" for k, v in errs.items())
     for n in NAMES:
         assert torch.isfinite(gpu[n]).all(), n
+
+
+@pytest.mark.parametrize("name", ["c3", "c4"])
+def test_whole_batch_entry_statistics(name):
+    """Batch entry 0 with all of its H heads against the oracle: the max-norm
+    gate and the RMS / bias / slope statistics of every per-token output."""
+    w = CONFIGS[name]
+    say(f"case {w} batch entry 0, all heads")
+    inp = make_inputs(w)
+    gpu = run_gpu(to_device(inp, w.dtype))
+    sl = {k: np.ascontiguousarray(inp[k][0:1]) for k in ("x", "g", "eta", "alpha", "dy")}
+    y = oracle.fwd(sl["x"], sl["g"], sl["eta"], sl["alpha"], inp["W0"], nthreads=16)
+    dx, dg, de, da, _ = oracle.bwd(sl["x"], sl["g"], sl["eta"], sl["alpha"], inp["W0"], sl["dy"],
+                                   nthreads=16)
+    ref = dict(y=y[0], dx=dx[0], dg=dg[0], deta=de[0], dalpha=da[0])
+    bad = {}
+    for n, r in ref.items():
+        got = host(gpu[n][0])
+        st = error_stats(got, r)
+        st["relmax"] = relmax(got, r)
+        say(f"  {n}: " + ", ".join(f"{k} {v:.2e}" for k, v in st.items()))
+        report(f"{name} b0 {n}", st)
+        if not (stats_ok(st) and st["relmax"] <= TOL["bf16"]):
+            bad[n] = st
+    assert not bad, bad
 
 
 EDGE = [
@@ -205,6 +231,12 @@ def test_out_f32(d, T):
     say(f"  errs {errs}")
     report(f"out_f32 d={d}", errs)
     assert not bad, errs
+    # without the final rounding to bf16 the outputs sit closer to the oracle
+    plain = run_gpu(dev)
+    for n in ("y", "dx", "dg"):
+        e32 = error_stats(host(gpu[n]), ref[n])["rel_rms"]
+        e16 = error_stats(host(plain[n]), ref[n])["rel_rms"]
+        assert e32 < e16, (n, e32, e16)
 
 
 def test_empty_inputs():

@@ -12,6 +12,7 @@
 
 #include <algorithm>
 #include <cstddef>
+#include <type_traits>
 
 #include "dev_common.hpp"
 #include "internal.hpp"
@@ -81,6 +82,26 @@ __device__ __forceinline__ bf16x8 scale8(const bf16x8& f, const f32x4& e0, const
     r[q + 4] = static_cast<__bf16>(static_cast<float>(f[q + 4]) * e1[q]);
   }
   return r;
+}
+
+// Outputs dx, dg in bf16 (four per 8-byte store) or, for fp32 outputs, as
+// the fp32 accumulators (four per 16-byte store at twice the offset).
+template <bool F32>
+using out4_t = typename std::conditional<F32, f32x4, uint2>::type;
+template <bool F32>
+__device__ __forceinline__ out4_t<F32> pack_out(const f32x4& v) {
+  if constexpr (F32) return v;
+  else return pack4f(v);
+}
+template <bool F32>
+__device__ __forceinline__ void store_out(__amdgpu_buffer_rsrc_t r, uint32_t off_bf16,
+                                          const out4_t<F32>& v) {
+  if constexpr (F32) {
+    typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), r, 2 * off_bf16, 0, 0);
+  } else {
+    store8(r, off_bf16, v);
+  }
 }
 
 // Sum over the 16 lanes of each row of 16; valid in lane 15 of the row.

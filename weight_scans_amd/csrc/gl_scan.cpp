@@ -92,8 +92,7 @@ gl_status_t make_plan(const gl_scan_desc_t* d, Plan* p) {
   p->comp = (p->io == GL_DTYPE_F64) ? 8 : 4;
   p->out_f32 = (d->flags & GL_FLAG_OUT_F32) && p->io == GL_DTYPE_BF16;
   const bool mfma_shape = p->io == GL_DTYPE_BF16 && d->d_in == d->d_out &&
-                          (d->d_in == 64 || d->d_in == 128) && !(d->flags & GL_FLAG_GENERIC) &&
-                          !p->out_f32;
+                          (d->d_in == 64 || d->d_in == 128) && !(d->flags & GL_FLAG_GENERIC);
   const size_t dd = static_cast<size_t>(d->d_in) * static_cast<size_t>(d->d_out);
   const size_t BH = static_cast<size_t>(d->B) * static_cast<size_t>(d->H);
   if (mfma_shape && (d->chunk == 0 || d->chunk == gls::kMfmaChunk)) {

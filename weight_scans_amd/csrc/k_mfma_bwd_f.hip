@@ -104,7 +104,9 @@ __device__ __forceinline__ void issue_f(SlotF& sl, const DmaOffF& od, uint32_t o
   dma4(buffer_rsrc(((ld & 1) == 0 ? eta : alpha) + tq, cq * 4), oq, sl.q[ld & 1]);
 }
 
+template <bool F32>
 __global__ __launch_bounds__(kNT) void bwd_f64(BwdArgs a) {
+  constexpr int OE = F32 ? 4 : 2;  // bytes per element of dx, dg
   __shared__ SlotF ring0, ring1, ring2;
   __shared__ __bf16 PT_s[2][kC * kC];  // P^T by chunk parity (W0 staging at the start)
   __shared__ __bf16 M_s[2][kC * kC + kMPad];  // Be + Be^T by chunk parity (+ pad)
@@ -135,8 +137,8 @@ __global__ __launch_bounds__(kNT) void bwd_f64(BwdArgs a) {
   const float* alpha = static_cast<const float*>(a.alpha) + bh * T;
   const uint16_t* W0 = static_cast<const uint16_t*>(a.W0) + static_cast<int64_t>(h) * kD * kD;
   const uint16_t* st = static_cast<const uint16_t*>(a.states) + bh * static_cast<int64_t>(n) * kD * kD;
-  uint16_t* dx = static_cast<uint16_t*>(a.dx) + bh * T * kD;
-  uint16_t* dg = static_cast<uint16_t*>(a.dg) + bh * T * kD;
+  char* dx = static_cast<char*>(a.dx) + bh * T * kD * OE;
+  char* dg = static_cast<char*>(a.dg) + bh * T * kD * OE;
   float* dal = static_cast<float*>(a.dalpha_out) + bh * T;
   float* det = static_cast<float*>(a.deta_out) + bh * T;
 
@@ -250,7 +252,7 @@ __global__ __launch_bounds__(kNT) void bwd_f64(BwdArgs a) {
     const int c = chunk_at(j);
     const int64_t t0 = c >= 0 ? static_cast<int64_t>(c) * kC : 0;
     const int cv = cv_of(c);
-    uint2 s8[2][2];
+    out4_t<F32> s8[2][2];
     float s4a = 0.f, s4b = 0.f;
     __amdgpu_buffer_rsrc_t ra = r_none, rb = r_none;
 
@@ -351,12 +353,13 @@ __global__ __launch_bounds__(kNT) void bwd_f64(BwdArgs a) {
 #pragma unroll
         for (int aa = 0; aa < 2; ++aa)
 #pragma unroll
-          for (int bb = 0; bb < 2; ++bb) s8[aa][bb] = pack4f(acc[aa][bb]);
-        const __amdgpu_buffer_rsrc_t r8 = buffer_rsrc(dx + t0 * kD, cv * kD * 2);
+          for (int bb = 0; bb < 2; ++bb) s8[aa][bb] = pack_out<F32>(acc[aa][bb]);
+        const __amdgpu_buffer_rsrc_t r8 = buffer_rsrc(dx + t0 * kD * OE, cv * kD * OE);
 #pragma unroll
         for (int aa = 0; aa < 2; ++aa)
 #pragma unroll
-          for (int bb = 0; bb < 2; ++bb) store8(r8, o8 + aa * 32 + bb * 16 * kD * 2, s8[aa][bb]);
+          for (int bb = 0; bb < 2; ++bb)
+            store_out<F32>(r8, o8 + aa * 32 + bb * 16 * kD * 2, s8[aa][bb]);
       }
       causal_next(qd);
     } else if constexpr (R == 1) {
@@ -459,7 +462,7 @@ __global__ __launch_bounds__(kNT) void bwd_f64(BwdArgs a) {
             const f32x4 gv = unpack4f(get4<kD>(cur.G, o, (2 * lq2 + bb) * 16, (2 * hq + aa) * 16));
             dp += dot4f(gv, u);
             pp += dot4f(gv, ain[aa][bb]);
-            s8[aa][bb] = pack4f(u * nbi);
+            s8[aa][bb] = pack_out<F32>(u * nbi);
           }
           dp = sum_rows(dp);
           pp = sum_rows(pp);
@@ -468,11 +471,12 @@ __global__ __launch_bounds__(kNT) void bwd_f64(BwdArgs a) {
             pw.pp[hq][i] = pp;
           }
         }
-        const __amdgpu_buffer_rsrc_t r8 = buffer_rsrc(dg + t0 * kD, cv * kD * 2);
+        const __amdgpu_buffer_rsrc_t r8 = buffer_rsrc(dg + t0 * kD * OE, cv * kD * OE);
 #pragma unroll
         for (int aa = 0; aa < 2; ++aa)
 #pragma unroll
-          for (int bb = 0; bb < 2; ++bb) store8(r8, o8 + aa * 32 + bb * 16 * kD * 2, s8[aa][bb]);
+          for (int bb = 0; bb < 2; ++bb)
+            store_out<F32>(r8, o8 + aa * 32 + bb * 16 * kD * 2, s8[aa][bb]);
       }
     } else {
       if (qd < 2) causal_next(8 + qd);
@@ -546,7 +550,10 @@ __global__ __launch_bounds__(kNT) void bwd_f64(BwdArgs a) {
 hipError_t launch_mfma_bwd_f64(const BwdArgs& a, hipStream_t s) {
   const int64_t groups = a.B * a.H * a.n_seg;
   if (groups == 0) return hipSuccess;
-  hipLaunchKernelGGL(bwd_f64, dim3(static_cast<unsigned>(groups)), dim3(kNT), 0, s, a);
+  if (a.out_f32)
+    hipLaunchKernelGGL(bwd_f64<true>, dim3(static_cast<unsigned>(groups)), dim3(kNT), 0, s, a);
+  else
+    hipLaunchKernelGGL(bwd_f64<false>, dim3(static_cast<unsigned>(groups)), dim3(kNT), 0, s, a);
   return hipGetLastError();
 }
 

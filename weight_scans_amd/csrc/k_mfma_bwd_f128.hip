@@ -70,8 +70,10 @@ __device__ __forceinline__ u32x4 load16(__amdgpu_buffer_rsrc_t r, uint32_t off) 
   return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
 }
 
+template <bool F32>
 __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(1, 2)))
 void bwd_f128(BwdArgs a) {
+  constexpr int OE = F32 ? 4 : 2;  // bytes per element of dx, dg
   __shared__ SlotH sl;
   __shared__ __bf16 L_s[kD * kD];           // Lam_out, bf16 [r][k]; W0 staging at the start
   __shared__ __bf16 PT_s[kC * kC];          // P^T
@@ -102,8 +104,8 @@ void bwd_f128(BwdArgs a) {
   const float* alpha = static_cast<const float*>(a.alpha) + bh * T;
   const uint16_t* W0 = static_cast<const uint16_t*>(a.W0) + static_cast<int64_t>(h) * kD * kD;
   const uint16_t* st = static_cast<const uint16_t*>(a.states) + bh * static_cast<int64_t>(n) * kD * kD;
-  uint16_t* dxp = static_cast<uint16_t*>(a.dx) + bh * T * kD;
-  uint16_t* dgp = static_cast<uint16_t*>(a.dg) + bh * T * kD;
+  char* dxp = static_cast<char*>(a.dx) + bh * T * kD * OE;
+  char* dgp = static_cast<char*>(a.dg) + bh * T * kD * OE;
   float* dal = static_cast<float*>(a.dalpha_out) + bh * T;
   float* det = static_cast<float*>(a.deta_out) + bh * T;
 
@@ -365,7 +367,7 @@ void bwd_f128(BwdArgs a) {
         // dx for columns 16 w .., all tokens:
         // -eta_i e(l_last - l_i) Lam_out^T g_i + W0^T dy_i + e(lq_i) D_in^T dy_i
         // + (M X)_i; rr_i = x_i . D_in^T dy_i over these 16 columns
-        const __amdgpu_buffer_rsrc_t rdx = buffer_rsrc(dxp + t0 * kD, cv * kD * 2);
+        const __amdgpu_buffer_rsrc_t rdx = buffer_rsrc(dxp + t0 * kD * OE, cv * kD * OE);
         f32x4 acc[4], t[4];
 #pragma unroll
         for (int b = 0; b < 4; ++b) t[b] = zero4();
@@ -410,13 +412,13 @@ void bwd_f128(BwdArgs a) {
         }
 #pragma unroll
         for (int b = 0; b < 4; ++b)
-          store8(rdx, static_cast<uint32_t>(((b * 16 + l16) * kD + wave * 16 + 4 * g4) * 2),
-                 pack4f(acc[b]));
+          store_out<F32>(rdx, static_cast<uint32_t>(((b * 16 + l16) * kD + wave * 16 + 4 * g4) * 2),
+                         pack_out<F32>(acc[b]));
       }
       {
         // u = e(l_last - l_i) Lam_out x_i + sum_u P_ui dy_u for rows 32 kq ..: dg,
         // and the deta, pp shares over these 32 rows
-        const __amdgpu_buffer_rsrc_t rdg = buffer_rsrc(dgp + t0 * kD, cv * kD * 2);
+        const __amdgpu_buffer_rsrc_t rdg = buffer_rsrc(dgp + t0 * kD * OE, cv * kD * OE);
         f32x4 ain[2][2], apd[2][2];
 #pragma unroll
         for (int aa = 0; aa < 2; ++aa)
@@ -461,8 +463,8 @@ void bwd_f128(BwdArgs a) {
             const f32x4 gv = unpack4f(get4<kD>(sl.G, o, (2 * th + b) * 16, (2 * kq + aa) * 16));
             dp += dot4f(gv, u);
             pp += dot4f(gv, ain[aa][b]);
-            store8(rdg, static_cast<uint32_t>((i * kD + (2 * kq + aa) * 16 + 4 * g4) * 2),
-                   pack4f(u * nbv[b]));
+            store_out<F32>(rdg, static_cast<uint32_t>((i * kD + (2 * kq + aa) * 16 + 4 * g4) * 2),
+                           pack_out<F32>(u * nbv[b]));
           }
           dp = sum_rows(dp);
           pp = sum_rows(pp);
@@ -490,7 +492,10 @@ void bwd_f128(BwdArgs a) {
 hipError_t launch_mfma_bwd_f128(const BwdArgs& a, hipStream_t s) {
   const int64_t groups = a.B * a.H * a.n_seg;
   if (groups == 0) return hipSuccess;
-  hipLaunchKernelGGL(bwd_f128, dim3(static_cast<unsigned>(groups)), dim3(kNT), 0, s, a);
+  if (a.out_f32)
+    hipLaunchKernelGGL(bwd_f128<true>, dim3(static_cast<unsigned>(groups)), dim3(kNT), 0, s, a);
+  else
+    hipLaunchKernelGGL(bwd_f128<false>, dim3(static_cast<unsigned>(groups)), dim3(kNT), 0, s, a);
   return hipGetLastError();
 }
 

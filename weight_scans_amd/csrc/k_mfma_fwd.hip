@@ -237,7 +237,7 @@ __device__ __forceinline__ void scale_g(const Slot<D>& sl, __bf16* GS, uint32_t 
   *reinterpret_cast<uint2*>(reinterpret_cast<char*>(GS) + off) = r;
 }
 
-template <int D, bool HAS_Y, bool HAS_ST>
+template <int D, bool HAS_Y, bool HAS_ST, bool F32 = false>
 __global__ __launch_bounds__(kNT) void fwd_mfma(FwdArgs a) {
   static_assert(D == 64 || D == 128, "D");
   constexpr int NTILE = D / kTN;
@@ -281,7 +281,8 @@ __global__ __launch_bounds__(kNT) void fwd_mfma(FwdArgs a) {
   const float* eta = static_cast<const float*>(a.eta) + bh * T;
   const float* alpha = static_cast<const float*>(a.alpha) + bh * T;
   const uint16_t* W0 = static_cast<const uint16_t*>(a.W0) + static_cast<int64_t>(h) * D * D;
-  uint16_t* y = HAS_Y ? static_cast<uint16_t*>(a.y) + bh * T * D : nullptr;
+  constexpr int YE = F32 ? 4 : 2;  // bytes per element of y
+  char* y = HAS_Y ? static_cast<char*>(a.y) + bh * T * D * YE : nullptr;
   uint16_t* st = HAS_ST ? static_cast<uint16_t*>(a.states) + bh * static_cast<int64_t>(n) * D * D
                         : nullptr;
 
@@ -458,11 +459,17 @@ __global__ __launch_bounds__(kNT) void fwd_mfma(FwdArgs a) {
         yb = mfma16x16x32(frag_s<D>(S_in, oX, rbw * 16, kb * 32), xf, yb);
       }
       const float eqi = cur.f.eq[tb * 16 + l16];
-      const __amdgpu_buffer_rsrc_t ry = buffer_rsrc(y + t0 * D, cv * D * 2);
-      uint2 pk;
-      pk.x = pack2(ya[0] + eqi * yb[0], ya[1] + eqi * yb[1]);
-      pk.y = pack2(ya[2] + eqi * yb[2], ya[3] + eqi * yb[3]);
-      store8(ry, oy, pk);
+      const __amdgpu_buffer_rsrc_t ry = buffer_rsrc(y + t0 * D * YE, cv * D * YE);
+      if constexpr (F32) {
+        typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+        const f32x4 yo = ya + eqi * yb;
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, yo), ry, 2 * oy, 0, 0);
+      } else {
+        uint2 pk;
+        pk.x = pack2(ya[0] + eqi * yb[0], ya[1] + eqi * yb[1]);
+        pk.y = pack2(ya[2] + eqi * yb[2], ya[3] + eqi * yb[3]);
+        store8(ry, oy, pk);
+      }
     }
   };
   using I0 = std::integral_constant<int, 0>;
@@ -505,7 +512,7 @@ __global__ __launch_bounds__(kNT) void fwd_mfma(FwdArgs a) {
     a.seg_lg[bh * a.n_seg + seg] = lsum;
 }
 
-template <int D, bool HAS_Y, bool HAS_ST>
+template <int D, bool HAS_Y, bool HAS_ST, bool F32 = false>
 hipError_t launch_v(const FwdArgs& a, hipStream_t s, bool every_segment = false) {
   const int64_t groups = (a.B * a.H + 7) / 8;
   // the state-only pass of the segmented scan skips the last segment (nothing
@@ -513,12 +520,14 @@ hipError_t launch_v(const FwdArgs& a, hipStream_t s, bool every_segment = false)
   const int nseg = (!HAS_Y && !HAS_ST && !every_segment) ? a.n_seg - 1 : a.n_seg;
   if (nseg <= 0) return hipSuccess;
   const dim3 grid(static_cast<unsigned>(groups * 8 * (D / kTN) * nseg));
-  hipLaunchKernelGGL((fwd_mfma<D, HAS_Y, HAS_ST>), grid, dim3(kNT), 0, s, a);
+  hipLaunchKernelGGL((fwd_mfma<D, HAS_Y, HAS_ST, F32>), grid, dim3(kNT), 0, s, a);
   return hipGetLastError();
 }
 
 template <int D>
 hipError_t launch_d(const FwdArgs& a, hipStream_t s) {
+  if (a.y && a.out_f32)
+    return a.states ? launch_v<D, true, true, true>(a, s) : launch_v<D, true, false, true>(a, s);
   if (a.y && a.states) return launch_v<D, true, true>(a, s);
   if (a.y) return launch_v<D, true, false>(a, s);
   if (a.states) return launch_v<D, false, true>(a, s);
