@@ -57,6 +57,9 @@ def test_status_strings():
     (dict(io_dtype=ws.GL_DTYPE_F64, chunk=128), 2), (dict(chunk=24), 2),
     (dict(io_dtype=ws.GL_DTYPE_F64, flags=ws.GL_FLAG_OUT_F32), 2),
     (dict(flags=4), 1),
+    (dict(io_dtype=ws.GL_DTYPE_F32, d_in=100, chunk=64), 2),
+    (dict(io_dtype=ws.GL_DTYPE_F64, chunk=64), 2),
+    (dict(io_dtype=ws.GL_DTYPE_F32, segments=3), 2),
 ])
 def test_descriptor_validation(kw, code):
     d = desc(**kw)
@@ -70,7 +73,14 @@ def test_descriptor_validation(kw, code):
     (dict(chunk=16), "generic-bf16"), (dict(chunk=32), "generic-bf16"),
     (dict(flags=ws.GL_FLAG_OUT_F32), "mfma-bf16-d64"),
     (dict(flags=ws.GL_FLAG_OUT_F32 | ws.GL_FLAG_GENERIC), "generic-bf16-out-f32"),
-    (dict(io_dtype=ws.GL_DTYPE_F32, flags=ws.GL_FLAG_OUT_F32), "generic-f32"),
+    (dict(io_dtype=ws.GL_DTYPE_F32, flags=ws.GL_FLAG_OUT_F32), "mfma-f32"),
+    (dict(io_dtype=ws.GL_DTYPE_F32), "mfma-f32"), (dict(io_dtype=ws.GL_DTYPE_F32, chunk=64), "mfma-f32"),
+    (dict(io_dtype=ws.GL_DTYPE_F32, chunk=32), "generic-f32"),
+    (dict(io_dtype=ws.GL_DTYPE_F32, d_in=100), "generic-f32"),
+    (dict(io_dtype=ws.GL_DTYPE_F32, flags=ws.GL_FLAG_GENERIC), "generic-f32"),
+    (dict(io_dtype=ws.GL_DTYPE_F64, d_in=32, d_out=32), "mfma-f64"),
+    (dict(io_dtype=ws.GL_DTYPE_F64, d_in=32, d_out=20, chunk=64), "mfma-f64"),
+    (dict(io_dtype=ws.GL_DTYPE_F64), "generic-f64"),
     (dict(io_dtype=ws.GL_DTYPE_F64, chunk=8), "generic-f64"),
     (dict(io_dtype=ws.GL_DTYPE_F64, chunk=16), "generic-f64"),
 ])

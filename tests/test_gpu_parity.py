@@ -61,7 +61,34 @@ def test_c1_fp64_recompute_path():
 
 
 def test_c2_fp32_full():
-    _full_case(CONFIGS["c2"].with_(chunk=0))
+    # c2 as specified: fp32 throughout, chunk 64 (the fp32 matrix-core kernels)
+    w = CONFIGS["c2"]
+    assert w.chunk == 64
+    d = ws.make_desc(w.B, w.H, w.T, w.d_in, w.d_out, ws.GL_DTYPE_F32, w.chunk)
+    assert ws.path_name(d) == "mfma-f32"
+    _full_case(w)
+
+
+def test_c1_on_the_matrix_cores():
+    w = CONFIGS["c1"]
+    d = ws.make_desc(w.B, w.H, w.T, w.d_in, w.d_out, ws.GL_DTYPE_F64, w.chunk)
+    assert ws.path_name(d) == "mfma-f64"
+
+
+@pytest.mark.parametrize("io,d_in,d_out", [("f32", 64, 64), ("f32", 20, 50), ("f64", 32, 32),
+                                           ("f64", 7, 30)])
+def test_matrix_core_and_vector_paths_agree(io, d_in, d_out):
+    """fp32 / fp64 on the matrix cores (chunk 64) and on the vector ALU
+    (GL_FLAG_GENERIC): both within tolerance of the oracle."""
+    w = Workload("mv", 2, 2, 300, d_in, d_out, io, "mix", "gauss", 2200 + d_in + d_out)
+    inp = make_inputs(w)
+    dev = to_device(inp, io)
+    ref = oracle_all(inp)
+    for flags in (0, ws.GL_FLAG_GENERIC):
+        gpu = run_gpu(dev, flags=flags)
+        errs, bad = compare_full(gpu, ref, TOL[io])
+        say(f"  flags {flags} errs {errs}")
+        assert not bad, (flags, errs)
 
 
 @pytest.mark.parametrize("name,pairs,head", [
@@ -165,7 +192,7 @@ def test_identity_gates(io):
     assert float(gpu["dg"].abs().max()) == 0.0
 
 
-@pytest.mark.parametrize("io,chunks", [("f64", (8, 16)), ("f32", (8, 16, 32)),
+@pytest.mark.parametrize("io,chunks", [("f64", (8, 16, 64)), ("f32", (8, 16, 32, 64)),
                                         ("bf16", (8, 16, 32))])
 def test_chunk_invariance(io, chunks):
     w = Workload("ch", 1, 2, 200, 32, 32, io, "mix", "gauss", 91)

@@ -48,7 +48,8 @@ constexpr int kBwdCombineAbove = 4;
 // forward and the backward agree on the layout of `saved`.
 struct Plan {
   int io = 0;
-  bool mfma = false;
+  bool mfma = false;        // bf16 matrix-core kernels
+  bool mf = false;          // fp32 / fp64 matrix-core kernels
   bool out_f32 = false;     // y, dx, dg in fp32 (bf16 io)
   int chunk = 0, n_chunks = 0, ckpt_every = 1, n_ckpt = 0, n_tiles = 0;
   size_t comp = 8;          // bytes of the compute / gate / state type
@@ -101,6 +102,16 @@ gl_status_t make_plan(const gl_scan_desc_t* d, Plan* p) {
     p->n_tiles = 1;  // the fused backward writes deta / dalpha itself (no tile partials)
     p->name = d->d_in == 64 ? "mfma-bf16-d64" : "mfma-bf16-d128";
     p->state_elem = 2;  // bf16 chunk-start states
+  } else if (p->io != GL_DTYPE_BF16 && !(d->flags & GL_FLAG_GENERIC) &&
+             (d->chunk == 0 || d->chunk == gls::kMfmaChunk) &&
+             gls::mf_shape_ok(p->io, static_cast<int>(d->d_in), static_cast<int>(d->d_out))) {
+    p->mf = true;
+    p->chunk = gls::kMfmaChunk;
+    p->n_tiles = 1;
+    p->name = p->io == GL_DTYPE_F64 ? "mfma-f64" : "mfma-f32";
+    p->state_elem = p->comp;
+    if (d->segments > 1)
+      return fail(GL_ERROR_NOT_SUPPORTED, "segments apply to the bf16 matrix-core kernels only");
   } else {
     if (d->chunk != 0 && !gls::generic_chunk_ok(p->io, d->chunk))
       return fail(GL_ERROR_NOT_SUPPORTED, "chunk %d not supported for this dtype/shape", d->chunk);
@@ -136,7 +147,7 @@ gl_status_t make_plan(const gl_scan_desc_t* d, Plan* p) {
   p->ckpt_every = 1;
   p->n_ckpt = p->n_chunks;
   p->saved_bytes = round_up(BH * p->n_ckpt * dd * p->state_elem);
-  p->part_bytes = round_up(static_cast<size_t>(p->n_tiles) * BH * d->T * p->comp);
+  p->part_bytes = p->mf ? 0 : round_up(static_cast<size_t>(p->n_tiles) * BH * d->T * p->comp);
   p->fused = p->mfma;
   if (p->fused && p->n_chunks > 0) {
     int nb = 1;
@@ -192,6 +203,7 @@ gls::FwdArgs fwd_args(const gl_scan_desc_t* d, const Plan& p, const void* x, con
 // state-only pass per segment from a zero start, the exclusive affine scan
 // over segments, then the full pass per segment from its incoming state.
 hipError_t launch_fwd(const Plan& p, const gls::FwdArgs& a, void* seg_ws, hipStream_t s) {
+  if (p.mf) return gls::launch_mf_fwd(p.io, a, s);
   if (!p.mfma) return gls::launch_generic_fwd(p.io, a, s);
   if (p.n_seg <= 1) return gls::launch_mfma_fwd(a, s);
   float* seg = static_cast<float*>(seg_ws);
@@ -339,7 +351,11 @@ gl_status_t gl_scan_bwd(const gl_scan_desc_t* desc, const void* x, const void* g
   b.n_tiles = p.n_tiles;
   b.seg_chunks = p.seg_chunks; b.n_seg = p.n_seg;
   b.out_f32 = p.out_f32;
-  if (!p.mfma) {
+  if (p.mf) {
+    b.deta_out = deta;
+    b.dalpha_out = dalpha;
+    st = hip_status(gls::launch_mf_bwd(p.io, b, s), "backward launch");
+  } else if (!p.mfma) {
     st = hip_status(gls::launch_generic_bwd(p.io, b, s), "backward launch");
   } else {
     // one work-group per (segment, sequence-head) walks its chunks from the
@@ -382,8 +398,8 @@ gl_status_t gl_scan_bwd(const gl_scan_desc_t* desc, const void* x, const void* g
   f.deta = deta; f.dalpha = dalpha; f.dW0 = dW0;
   f.B = desc->B; f.H = desc->H; f.T = desc->T;
   f.d_in = b.d_in; f.d_out = b.d_out; f.n_tiles = p.n_tiles; f.n_seg = p.dw_groups;
-  f.alpha_done = p.fused;
-  f.eta_done = p.fused;
+  f.alpha_done = p.fused || p.mf;
+  f.eta_done = p.fused || p.mf;
   return hip_status(gls::launch_finalize(p.io, f, s), "finalize launch");
 }
 

@@ -166,6 +166,13 @@ hipError_t launch_costate(int io, const CostArgs& a, hipStream_t s);
 hipError_t launch_qkv_fwd(int io, const QkvArgs& a, hipStream_t s);
 hipError_t launch_mfma_final_state(const FwdArgs& a, hipStream_t s);
 
+// Matrix-core kernels in fp32 / fp64 (io = compute type), chunk 64: any
+// d_in, d_out <= 64 (fp32) or <= 32 (fp64).  The backward writes deta, dalpha
+// directly (deta_out, dalpha_out) and one dW0 partial per sequence-head.
+bool mf_shape_ok(int io, int d_in, int d_out);
+hipError_t launch_mf_fwd(int io, const FwdArgs& a, hipStream_t s);
+hipError_t launch_mf_bwd(int io, const BwdArgs& a, hipStream_t s);
+
 // Matrix-core kernels: bf16 io, d_in == d_out in {64, 128}, chunk 64.
 constexpr int kMfmaChunk = 64;
 hipError_t launch_mfma_fwd(const FwdArgs& a, hipStream_t s);
