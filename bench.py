@@ -78,6 +78,9 @@ def pass_kernels(w, which, segmented, generic):
     """The kernels one pass launches (the event-timed region of that pass)."""
     if generic:
         return {"fwd": "fwd_generic", "bwd": "bwd_generic + finalize_kernel"}[which]
+    if w.dtype in ("f32", "f64"):  # the fp32 / fp64 matrix-core kernels, chunk-parallel
+        return {"fwd": "fwd_inc + mf_carry + fwd_chunk",
+                "bwd": "bwd_inc + mf_carry + bwd_chunk + finalize_kernel"}[which]
     if which == "fwd":
         return ("fwd_mfma (state-only) + seg_combine + fwd_mfma" if segmented else "fwd_mfma")
     # the fused backward takes its own segment count: enough (segment,
@@ -697,6 +700,9 @@ def main():
                       "fwd_median": med(tf), "fwd_min": min(tf), "fwd_max": max(tf),
                       "bwd_median": med(tb), "bwd_min": min(tb), "bwd_max": max(tb)},
         "tokens_per_s_median": tokens / ((med(tf) + med(tb)) / 1e3),
+        # one step (fwd + bwd pass) end to end: the figure for latency-bound
+        # workloads such as a single short sequence
+        "step_latency_us_median": med([a + b for a, b in zip(tf, tb)]) * 1e3,
         "roofline": {"bound": bound, "achieved": achieved, "peak": peak, "unit": unit,
                      "frac": achieved / peak, "traffic": traffic,
                      "algorithmic_bytes": nbytes, "algorithmic_flops": nflops,

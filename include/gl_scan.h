@@ -104,11 +104,13 @@ typedef struct {
  * must be used for both calls). */
 gl_status_t gl_scan_saved_size(const gl_scan_desc_t* desc, size_t* saved_bytes);
 
-/* Workspace bytes for gl_scan_fwd and gl_scan_bwd.  have_saved != 0: the bwd
- * call will receive the fwd's `saved` buffer; 0: the bwd recomputes the
- * chunk-boundary states itself inside the workspace.  The fwd needs a
- * workspace only when the sequences are cut into segments (0 bytes
- * otherwise; ws may then be NULL). */
+/* Workspace bytes for gl_scan_fwd and gl_scan_bwd.  have_saved != 0: the fwd
+ * call receives a `saved` buffer and the bwd call the same buffer; 0: neither
+ * does, and the bwd recomputes the chunk-boundary states itself inside its
+ * workspace.  The fwd needs a workspace when the sequences are cut into
+ * segments, and on the fp32 / fp64 matrix-core kernels (per-chunk decays, plus
+ * the chunk-boundary states when there is no `saved`); otherwise 0 bytes and
+ * ws may be NULL. */
 gl_status_t gl_scan_workspace_size(const gl_scan_desc_t* desc, int have_saved,
                                    size_t* fwd_ws_bytes, size_t* bwd_ws_bytes);
 

@@ -205,8 +205,9 @@ def test_chunk_invariance(io, chunks):
         assert not bad, (c, errs)
 
 
-def test_run_to_run_bitwise_determinism():
-    w = CONFIGS["c3"].with_(B=2, T=1024)
+@pytest.mark.parametrize("name", ["c3", "c2"])
+def test_run_to_run_bitwise_determinism(name):
+    w = CONFIGS[name].with_(B=2, T=1024)
     dev = to_device(make_inputs(w), w.dtype)
     a = run_gpu(dev)
     b = run_gpu(dev)

@@ -167,8 +167,24 @@ gl_status_t make_plan(const gl_scan_desc_t* d, Plan* p) {
   }
   if (p->fused) p->part_bytes = 0;
   p->dw_groups = p->fused ? p->bwd_nseg : p->n_seg;
+  if (p->mf) {
+    // per-chunk decays (fwd); adjoint leaving every chunk + decays (bwd); a
+    // dW0 share per chunk
+    if (static_cast<int64_t>(BH) * std::max(p->n_chunks, 1) > 0x7fffffffLL)
+      return fail(GL_ERROR_NOT_SUPPORTED, "B*H*chunks above 2^31-1");
+    p->seg_bytes = round_up(BH * p->n_chunks * p->comp);
+    p->bwd_seg_state_bytes = round_up(BH * p->n_chunks * dd * p->comp);
+    p->bwd_seg_bytes = p->bwd_seg_state_bytes + p->seg_bytes;
+    p->dw_groups = std::max(p->n_chunks, 1);
+  }
   p->dw_bytes = round_up(BH * dd * p->comp * p->dw_groups);
   return GL_SUCCESS;
+}
+
+// fwd workspace: segment buffers; the fp32 / fp64 matrix-core kernels also
+// keep the chunk-boundary states there when the call has no `saved` buffer
+size_t fwd_ws(const Plan& p, bool have_saved) {
+  return p.seg_bytes + (p.mf && !have_saved ? p.saved_bytes : 0);
 }
 
 // bwd workspace: deta / dalpha partials, dW0 partials, segment buffers (also
@@ -203,7 +219,11 @@ gls::FwdArgs fwd_args(const gl_scan_desc_t* d, const Plan& p, const void* x, con
 // state-only pass per segment from a zero start, the exclusive affine scan
 // over segments, then the full pass per segment from its incoming state.
 hipError_t launch_fwd(const Plan& p, const gls::FwdArgs& a, void* seg_ws, hipStream_t s) {
-  if (p.mf) return gls::launch_mf_fwd(p.io, a, s);
+  if (p.mf) {
+    gls::FwdArgs am = a;
+    am.mf_gam = seg_ws;
+    return gls::launch_mf_fwd(p.io, am, s);
+  }
   if (!p.mfma) return gls::launch_generic_fwd(p.io, a, s);
   if (p.n_seg <= 1) return gls::launch_mfma_fwd(a, s);
   float* seg = static_cast<float*>(seg_ws);
@@ -270,7 +290,7 @@ gl_status_t gl_scan_workspace_size(const gl_scan_desc_t* desc, int have_saved,
   Plan p;
   gl_status_t st = make_plan(desc, &p);
   if (st != GL_SUCCESS) return st;
-  if (fwd_ws_bytes) *fwd_ws_bytes = p.seg_bytes;
+  if (fwd_ws_bytes) *fwd_ws_bytes = fwd_ws(p, have_saved != 0);
   if (bwd_ws_bytes) *bwd_ws_bytes = bwd_ws(p, have_saved != 0);
   return GL_SUCCESS;
 }
@@ -287,15 +307,17 @@ gl_status_t gl_scan_fwd(const gl_scan_desc_t* desc, const void* x, const void* g
   for (const void* q : {x, g, eta, alpha, W0, static_cast<const void*>(y),
                         static_cast<const void*>(saved)})
     if (q && misaligned(q)) return fail(GL_ERROR_MISALIGNED, "pointer %p not 16-byte aligned", q);
-  if (p.seg_bytes > 0) {
+  const size_t need = fwd_ws(p, saved != nullptr);
+  if (need > 0) {
     if (!ws) return fail(GL_ERROR_INVALID_VALUE, "workspace is NULL");
     if (misaligned(ws)) return fail(GL_ERROR_MISALIGNED, "workspace not 16-byte aligned");
-    if (ws_bytes < p.seg_bytes)
-      return fail(GL_ERROR_WORKSPACE_TOO_SMALL, "workspace %zu bytes, need %zu", ws_bytes,
-                  p.seg_bytes);
+    if (ws_bytes < need)
+      return fail(GL_ERROR_WORKSPACE_TOO_SMALL, "workspace %zu bytes, need %zu", ws_bytes, need);
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
-  return hip_status(launch_fwd(p, fwd_args(desc, p, x, g, eta, alpha, W0, y, saved), ws, s),
+  void* states = saved;
+  if (p.mf && !saved) states = static_cast<char*>(ws) + p.seg_bytes;
+  return hip_status(launch_fwd(p, fwd_args(desc, p, x, g, eta, alpha, W0, y, states), ws, s),
                     "forward launch");
 }
 
@@ -354,6 +376,8 @@ gl_status_t gl_scan_bwd(const gl_scan_desc_t* desc, const void* x, const void* g
   if (p.mf) {
     b.deta_out = deta;
     b.dalpha_out = dalpha;
+    b.mf_lam = seg_ws;
+    b.mf_gam = seg_ws + p.bwd_seg_state_bytes;
     st = hip_status(gls::launch_mf_bwd(p.io, b, s), "backward launch");
   } else if (!p.mfma) {
     st = hip_status(gls::launch_generic_bwd(p.io, b, s), "backward launch");

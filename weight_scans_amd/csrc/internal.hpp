@@ -42,6 +42,8 @@ struct FwdArgs {
   const void* q = nullptr;
   bool w0_t = false;
   bool out_f32 = false;
+  // fp32 / fp64 matrix-core scans: [B*H][n_chunks] per-chunk decay (compute type)
+  void* mf_gam = nullptr;
 };
 
 // Reverse scan.  Work-group (k, b*H+h) owns column tile k of D and Lambda
@@ -85,6 +87,11 @@ struct BwdArgs {
   void* dq = nullptr;
   bool w0_t = false;
   bool out_f32 = false;   // dx, dg (and dq) in fp32 (bf16 io only)
+  // fp32 / fp64 matrix-core scans: the adjoint leaving every chunk
+  // [B*H][n_chunks][d_out][d_in] and the per-chunk decay [B*H][n_chunks]
+  // (compute type); part_dW0 then holds [n_chunks][B*H][d_out][d_in]
+  void* mf_lam = nullptr;
+  void* mf_gam = nullptr;
 };
 
 // Deployment (one token at a time): the cached adaptation `state`

@@ -2,6 +2,7 @@
 
     python -m weight_scans_amd.profiling stats  <kernel_stats.csv>
     python -m weight_scans_amd.profiling traffic <fetch_dir> <write_dir> <config>
+    python -m weight_scans_amd.profiling counters <pmc_dir> [<pmc_dir> ...]
 
 `stats` prints a markdown table from a rocprofv3 `--stats` kernel summary CSV
 (or a rocpd2summary kernels CSV).  `traffic` reads the counter CSVs of two
@@ -12,6 +13,18 @@ once with a known size (256 MiB read, 256 MiB written), and prints per-pass
 HBM traffic.  With --json it also writes
 the record bench.py reads back into its roofline `traffic` field, keyed by a
 hash of the kernel sources so that a changed kernel invalidates it.
+`counters` reads the counter CSVs of `--pmc` runs (SQ_* and GRBM_GUI_ACTIVE,
+several runs merged) and prints, per kernel and dispatch, how the matrix
+cores, the vector ALU and the LDS were used:
+  MFMA busy   SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 x 1024 SIMDs):
+              the share of all SIMD cycles of the dispatch with an MFMA in
+              flight (GRBM_GUI_ACTIVE sums the eight XCDs)
+  per wave    SQ_INSTS_MFMA, SQ_INSTS_VALU (MFMA included), SQ_INSTS_LDS
+              divided by SQ_WAVES
+  LDS conflict  SQ_LDS_BANK_CONFLICT / SQ_ACTIVE_INST_LDS (cycles lost to bank
+              conflicts per cycle of LDS issue)
+  wait LDS / wait any  SQ_WAIT_INST_LDS and SQ_WAIT_ANY over SQ_WAVE_CYCLES
+              (share of the waves' lifetime spent waiting)
 """
 from __future__ import annotations
 
@@ -39,7 +52,7 @@ def kernel_source_hash() -> str:
 
 
 def short_name(kernel: str) -> str:
-    if kernel.startswith("seg_combine ("):  # already a pass-labelled name
+    if kernel.startswith(("seg_combine (", "mf_carry (")):  # already a pass-labelled name
         return kernel
     k = kernel
     for pre in ("void ", "gls::(anonymous namespace)::", "at::native::"):
@@ -82,6 +95,8 @@ def _counter(dirpath: str, counter: str):
         k = name[key]
         if "seg_combine" in k:
             k = "seg_combine (bwd)" if prev is not None and "bwd_lam" in prev else "seg_combine (fwd)"
+        if "mf_carry" in k:  # the carry scan of the fp32 / fp64 kernels serves both passes
+            k = "mf_carry (bwd)" if prev is not None and "bwd_inc" in prev else "mf_carry (fwd)"
         out[k].append(per[key])
         prev = name[key]
     return dict(out)
@@ -89,6 +104,46 @@ def _counter(dirpath: str, counter: str):
 
 def _mean(v):
     return sum(v) / len(v) if v else float("nan")
+
+
+def counters(dirs):
+    """{kernel: {counter: mean per dispatch}} over every counter of the runs."""
+    names = set()
+    for d in dirs:
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            for r in csv.DictReader(open(f)):
+                names.add(r["Counter_Name"])
+    res = defaultdict(dict)
+    for c in sorted(names):
+        for d in dirs:
+            for k, v in _counter(d, c).items():
+                if v:
+                    res[short_name(k)][c] = _mean(v)
+    return res
+
+
+def counters_table(dirs) -> str:
+    res = counters(dirs)
+    out = ["| kernel | waves | MFMA busy | MFMA / wave | VALU / wave | LDS / wave | "
+           "LDS conflict | wait LDS | wait any |", "|---|---|---|---|---|---|---|---|---|"]
+
+    def ratio(a, b):
+        return a / b if b else float("nan")
+
+    for k, c in sorted(res.items()):
+        if "GRBM_GUI_ACTIVE" not in c or "SQ_WAVES" not in c:
+            continue
+        w = c["SQ_WAVES"]
+        simd = c["GRBM_GUI_ACTIVE"] / 8.0 * 1024.0
+        out.append(
+            f"| `{k}` | {w:.0f} | {ratio(c.get('SQ_VALU_MFMA_BUSY_CYCLES', 0.0), simd):.3f} | "
+            f"{ratio(c.get('SQ_INSTS_MFMA', float('nan')), w):.0f} | "
+            f"{ratio(c.get('SQ_INSTS_VALU', float('nan')), w):.0f} | "
+            f"{ratio(c.get('SQ_INSTS_LDS', float('nan')), w):.0f} | "
+            f"{ratio(c.get('SQ_LDS_BANK_CONFLICT', float('nan')), c.get('SQ_ACTIVE_INST_LDS', 0.0)):.3f} | "
+            f"{ratio(c.get('SQ_WAIT_INST_LDS', float('nan')), c.get('SQ_WAVE_CYCLES', 0.0)):.3f} | "
+            f"{ratio(c.get('SQ_WAIT_ANY', float('nan')), c.get('SQ_WAVE_CYCLES', 0.0)):.3f} |")
+    return "\n".join(out)
 
 
 def traffic(fetch_dir: str, write_dir: str):
@@ -115,6 +170,9 @@ def main(argv):
     if len(argv) >= 2 and argv[0] == "stats":
         print(stats_table(argv[1]))
         return 0
+    if len(argv) >= 2 and argv[0] == "counters":
+        print(counters_table(argv[1:]))
+        return 0
     if len(argv) >= 4 and argv[0] == "traffic":
         res = traffic(argv[1], argv[2])
         cfg = argv[3]
@@ -131,8 +189,9 @@ def main(argv):
             def moved(pred):
                 return sum(v["fetch_bytes"] + v["write_bytes"] for k, v in res["kernels"].items()
                            if pred(k))
-            fwd = moved(lambda k: k.startswith("fwd_") or k == "seg_combine (fwd)")
-            bwd = moved(lambda k: k.startswith("bwd_") or "finalize" in k or k == "seg_combine (bwd)")
+            fwd = moved(lambda k: k.startswith("fwd_") or k in ("seg_combine (fwd)", "mf_carry (fwd)"))
+            bwd = moved(lambda k: k.startswith("bwd_") or "finalize" in k or
+                        k in ("seg_combine (bwd)", "mf_carry (bwd)"))
             db[cfg] = {"kernel_hash": kernel_source_hash(), "fwd_bytes": fwd, "bwd_bytes": bwd,
                        "fetch_scale": res["fetch_scale"], "write_scale": res["write_scale"]}
             with open(path, "w") as fh:
