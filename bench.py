@@ -481,7 +481,9 @@ def qkv_main(args, w):
     z = torch.empty_like(t["x"])
     io = {"f64": 0, "f32": 1, "bf16": 2}[w.dtype]
     # transpose read: q = u (length d_out), k = g, v = x (length d_in)
-    desc = ws.make_desc(w.B, w.H, w.T, w.d_out, w.d_in, io)
+    flags = ws.GL_FLAG_GENERIC if args.generic else 0
+    desc = ws.make_desc(w.B, w.H, w.T, w.d_out, w.d_in, io, flags=flags)
+    on_mfma = w.dtype == "bf16" and w.d_in == 64 and w.d_out == 64 and not args.generic
     flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)
     L = ws.lib()
     stream = torch.cuda.current_stream(dev)
@@ -508,8 +510,24 @@ def qkv_main(args, w):
     # 4 d_in d_out flops per token and head: the readout's and the rank-one
     # update's multiply-adds
     nflops = 4 * w.B * w.H * w.T * w.d_in * w.d_out
-    achieved = nflops / 1e12 / (ms / 1e3)
-    peak = PEAK_VALU[w.dtype] / 1e12
+    if on_mfma:
+        # the chunked matrix-core kernel: bound by HBM; algorithmic bytes per
+        # token-head u, g, x read and z written once (e (2 d_out + 2 d_in)) and
+        # the two gates (fp32), plus W0 once; its flops (6 d^2 + 2 64 d per
+        # token-head) take a fifth of the HBM time at the bf16 matrix peak
+        e = 2
+        nbytes = (w.B * w.H * w.T * (e * (2 * w.d_out + 2 * w.d_in) + 8)
+                  + w.H * w.d_in * w.d_out * e)
+        roof = {"bound": "hbm", "achieved": nbytes / 1e9 / (ms / 1e3), "peak": PEAK_HBM / 1e9,
+                "unit": "GB/s", "traffic": None, "algorithmic_bytes": nbytes,
+                "kernel": "fwd_mfma<64> with a read tile of its own (chunked, matrix cores)"}
+    else:
+        achieved = nflops / 1e12 / (ms / 1e3)
+        peak = PEAK_VALU[w.dtype] / 1e12
+        roof = {"bound": "alu", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+                "traffic": None, "algorithmic_flops": nflops,
+                "kernel": "qkv_fwd_k (tokens in order, rows across lanes)"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
     rec = {
         "metric": "tokens/s (transpose read of the adapted weight)",
         "value": w.B * w.T / (ms / 1e3),
@@ -527,9 +545,8 @@ def qkv_main(args, w):
                                f"{w.dtype}, z_t = (W0 + D_t)^T u_t",
                    "B": w.B, "H": w.H, "T": w.T, "d_in": w.d_in, "d_out": w.d_out,
                    "io": w.dtype, "parallelism": "single GPU"},
-        "roofline": {"bound": "alu", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
-                     "frac": achieved / peak, "traffic": None, "algorithmic_flops": nflops,
-                     "kernel": "qkv_fwd_k (tokens in order, rows across lanes)"},
+        "roofline": roof,
+        "passes_ms": {"mean": ms, "median": statistics.median(ts), "min": min(ts), "max": max(ts)},
     }
     if not args.no_cpu:
         try:

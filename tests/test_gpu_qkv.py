@@ -76,6 +76,32 @@ def test_qkv_with_equal_keys_is_the_forward_scan():
     assert relmax(host(y1), host(y2)) <= 1e-4
 
 
+@pytest.mark.parametrize("T", [1, 63, 65, 300])
+@pytest.mark.parametrize("transposed", [True, False])
+def test_bf16_d64_on_the_matrix_cores(T, transposed):
+    # bf16 with dk = dv = 64 runs the forward matrix-core kernel with a read
+    # tile of its own; GL_FLAG_GENERIC keeps it on the token-serial kernel.
+    # Both within the scan's bf16 bounds of the oracle (max-norm and the
+    # RMS / bias / slope statistics).
+    from parity_util import error_stats, stats_ok
+    say(f"bf16 d=64 matrix cores T={T} transposed={transposed}")
+    inp, dev = case("bf16", 2, 3, T, 64, 64, seed=1900 + T + int(transposed))
+    rng = np.random.default_rng(1950 + T)
+    qn = round_to(rng.standard_normal(inp["x"].shape) / 8.0, "bf16")
+    qd = torch.from_numpy(qn).to("cuda", torch.bfloat16)
+    W0p = np.ascontiguousarray(np.transpose(inp["W0"], (0, 2, 1))) if transposed else inp["W0"]
+    want = oracle.qkv_fwd(qn, inp["g"], inp["x"], inp["eta"], inp["alpha"], W0p)
+    for flags in (0, ws.GL_FLAG_GENERIC):
+        y = ws.gl_scan_qkv_fwd(qd, dev["g"], dev["x"], dev["eta"], dev["alpha"], dev["W0"],
+                               w0_transposed=transposed, flags=flags)
+        torch.cuda.synchronize()
+        err = relmax(host(y), want)
+        st = error_stats(host(y), want)
+        say(f"  flags {flags}: relmax {err:.3g} {st}")
+        assert err <= TOL["bf16"], (flags, err)
+        assert stats_ok(st), (flags, st)
+
+
 def test_transpose_read_full_size_sampled():
     # the 340M-model shape (B=8, H=16, T=4096, d=64, bf16), every head on the
     # GPU, two heads against the oracle

@@ -392,9 +392,10 @@ def picard(x, eta, alpha, W0, target, g0=None, max_sweeps=None, tol=0.0):
     return g, y, k, res_max
 
 
-def gl_scan_qkv_fwd(q, k, v, eta, alpha, W0, w0_transposed=False):
+def gl_scan_qkv_fwd(q, k, v, eta, alpha, W0, w0_transposed=False, flags=0):
     """y_t = (W0' + D_t) q_t, D_{t+1} = alpha_t D_t - eta_t v_t k_t^T: q, k
-    [B,H,T,dk], v [B,H,T,dv], W0 [H,dv,dk] (or [H,dk,dv] transposed)."""
+    [B,H,T,dk], v [B,H,T,dv], W0 [H,dv,dk] (or [H,dk,dv] transposed).
+    flags: GL_FLAG_GENERIC keeps bf16 d = 64 off the matrix cores."""
     torch = _torch()
     if q.dim() != 4 or k.shape != q.shape or v.dim() != 4 or v.shape[:3] != q.shape[:3]:
         raise ValueError("q, k must be [B,H,T,dk] and v [B,H,T,dv]")
@@ -405,7 +406,7 @@ def gl_scan_qkv_fwd(q, k, v, eta, alpha, W0, w0_transposed=False):
         raise ValueError("shape mismatch between q, v, W0, eta and alpha")
     y = torch.empty((B, H, T, dv), dtype=q.dtype, device=q.device)
     _check_dec((q, k, v, W0, y), (eta,), alpha, q.dtype)
-    desc = make_desc(B, H, T, dk, dv, _io_code(q.dtype))
+    desc = make_desc(B, H, T, dk, dv, _io_code(q.dtype), flags=flags)
     _check(lib().gl_scan_qkv_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(eta),
                                  _ptr(alpha), _ptr(W0), int(bool(w0_transposed)), _ptr(y),
                                  _stream(q.device)))
@@ -440,10 +441,10 @@ def gl_scan_qkv_bwd(q, k, v, eta, alpha, W0, dy, w0_transposed=False):
     return dq, dk_, dv_, deta, dalpha, dW0
 
 
-def transpose_read(u, g, x, eta, alpha, W0):
+def transpose_read(u, g, x, eta, alpha, W0, flags=0):
     """z_t = (W0 + D_t)^T u_t along the adaptation D_t that (x, g, eta, alpha)
     write (u [B,H,T,d_out] -> z [B,H,T,d_in])."""
-    return gl_scan_qkv_fwd(u, g, x, eta, alpha, W0, w0_transposed=True)
+    return gl_scan_qkv_fwd(u, g, x, eta, alpha, W0, w0_transposed=True, flags=flags)
 
 
 def _make_function():

@@ -545,6 +545,25 @@ gl_status_t gl_scan_qkv_fwd(const gl_scan_desc_t* desc, const void* q, const voi
   if (st != GL_SUCCESS || desc->B * desc->H * desc->T == 0) return st;
   st = check_ptrs({q, k, v, eta, alpha, W0, y});
   if (st != GL_SUCCESS) return st;
+  if (desc->io_dtype == GL_DTYPE_BF16 && desc->d_in == 64 && desc->d_out == 64 &&
+      !(desc->flags & GL_FLAG_GENERIC)) {
+    // the forward matrix-core kernel with a read tile of its own: x is the
+    // write key, g the value (one segment; every pointer 16-byte aligned)
+    for (const void* p : {q, k, v, eta, alpha, W0, static_cast<const void*>(y)})
+      if (misaligned(p)) return fail(GL_ERROR_MISALIGNED, "pointer %p not 16-byte aligned", p);
+    gls::FwdArgs f;
+    f.x = k; f.g = v; f.q = q; f.eta = eta; f.alpha = alpha; f.W0 = W0; f.y = y;
+    f.states = nullptr;
+    f.B = desc->B; f.H = desc->H; f.T = desc->T;
+    f.d_in = 64; f.d_out = 64;
+    f.chunk = gls::kMfmaChunk;
+    f.n_chunks = static_cast<int>((desc->T + gls::kMfmaChunk - 1) / gls::kMfmaChunk);
+    f.ckpt_every = 1; f.n_ckpt = f.n_chunks;
+    f.seg_chunks = f.n_chunks; f.n_seg = 1;
+    f.w0_t = w0_transposed != 0;
+    return hip_status(gls::launch_mfma_qkv_fwd(f, static_cast<hipStream_t>(stream)),
+                      "qkv scan launch");
+  }
   gls::QkvArgs a;
   a.q = q; a.k = k; a.v = v; a.eta = eta; a.alpha = alpha; a.W0 = W0; a.y = y;
   a.B = desc->B; a.H = desc->H; a.T = desc->T;

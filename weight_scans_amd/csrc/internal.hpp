@@ -183,6 +183,7 @@ hipError_t launch_mf_bwd(int io, const BwdArgs& a, hipStream_t s);
 // Matrix-core kernels: bf16 io, d_in == d_out in {64, 128}, chunk 64.
 constexpr int kMfmaChunk = 64;
 hipError_t launch_mfma_fwd(const FwdArgs& a, hipStream_t s);
+hipError_t launch_mfma_qkv_fwd(const FwdArgs& a, hipStream_t s);  // read tile of its own, d = 64
 hipError_t launch_mfma_bwd_lam(const BwdArgs& a, hipStream_t s);  // adjoint-only segment pass
 hipError_t launch_mfma_bwd_f64(const BwdArgs& a, hipStream_t s);   // fused reverse scan, d = 64
 hipError_t launch_mfma_bwd_f128(const BwdArgs& a, hipStream_t s);  // fused reverse scan, d = 128

@@ -72,9 +72,9 @@ struct GateRows {
   float alpha[kC], C3[kC], eq[kC], pad[kC];
 };
 
-template <int D>
+template <int D, bool QK = false>
 struct alignas(16) Slot {
-  __bf16 X[kC * D];                      // x of the chunk, swizzled [token][D]
+  __bf16 X[kC * D];                      // x (the write key) of the chunk, swizzled [token][D]
   __bf16 G[kC * kTN];                    // g of the row tile, swizzled [token][kTN]
   union {
     float q[2][4 * kC];                  // loaded: eta = q[0][0..63], alpha = q[1][0..63]
@@ -82,6 +82,7 @@ struct alignas(16) Slot {
   };
   float lq[kC], li[kC], nb[kC], bk[kC];  // l_{i-1}, l_i, -eta_i, e(l_last - l_i)(-eta_i)
   float gam[4];                          // gam[0] = e(l_last)
+  __bf16 Q[QK ? kC * D : 8];             // a read vector of its own, swizzled [token][D]
 };
 
 // Per-lane byte offsets of the chunk loads (loop invariant).  Wave w loads
@@ -113,15 +114,15 @@ __device__ __forceinline__ DmaOff<D> dma_off(int wave, int lane) {
 }
 
 // Vector-memory instructions one wave issues per chunk load.
-template <int D>
-constexpr int kLoadOps = D / 64 + 1;
+template <int D, bool QK = false>
+constexpr int kLoadOps = (QK ? 2 : 1) * (D / 64) + 1;
 
 // Queue the loads of chunk k into `sl`.  Rows past the sequence end, and
 // chunks from c_end on, are zero-filled by the buffer bounds (every wave
 // always issues the same number of loads).
-template <int D>
-__device__ __forceinline__ void issue_chunk(Slot<D>& sl, const DmaOff<D>& o, const uint16_t* x,
-                                            const uint16_t* g, const float* eta,
+template <int D, bool QK>
+__device__ __forceinline__ void issue_chunk(Slot<D, QK>& sl, const DmaOff<D>& o, const uint16_t* x,
+                                            const uint16_t* q, const uint16_t* g, const float* eta,
                                             const float* alpha, int64_t T, int k, int c_end,
                                             int r0, int wave) {
   const bool in = k < c_end;
@@ -130,6 +131,11 @@ __device__ __forceinline__ void issue_chunk(Slot<D>& sl, const DmaOff<D>& o, con
   const __amdgpu_buffer_rsrc_t rx = buffer_rsrc(x + t0 * D, cv * D * 2);
 #pragma unroll
   for (int s = 0; s < D / 64; ++s) dma16(rx, o.x[s], sl.X + (wave + 8 * s) * 512);
+  if constexpr (QK) {
+    const __amdgpu_buffer_rsrc_t rq = buffer_rsrc(q + t0 * D, cv * D * 2);
+#pragma unroll
+    for (int s = 0; s < D / 64; ++s) dma16(rq, o.x[s], sl.Q + (wave + 8 * s) * 512);
+  }
   // the same instruction in every wave (no branch): scalar-selected source
   // and destination offset within the slot
   const bool gw = wave < 4;
@@ -138,6 +144,10 @@ __device__ __forceinline__ void issue_chunk(Slot<D>& sl, const DmaOff<D>& o, con
          : buffer_rsrc(((wave & 1) == 0 ? eta : alpha) + t0, cv * 4);
   const int lds_off = gw ? static_cast<int>(offsetof(Slot<D>, G)) + wave * 1024
                          : static_cast<int>(offsetof(Slot<D>, q)) + (wave & 1) * 1024;
+  using SlotQ = Slot<D, true>;
+  static_assert(offsetof(Slot<D>, G) == offsetof(SlotQ, G) &&
+                    offsetof(Slot<D>, q) == offsetof(SlotQ, q),
+                "the read tile follows the common part of a slot");
   // a gate row is 64 floats: one 4-byte load per lane
   if (gw)
     dma16(r4, o.gq, reinterpret_cast<char*>(&sl) + lds_off);
@@ -149,8 +159,8 @@ __device__ __forceinline__ void issue_chunk(Slot<D>& sl, const DmaOff<D>& o, con
 // (returns l_last), PART 1 the rank-one factors of the off-diagonal score
 // blocks, PART 2 both (one wave).  Two waves can each take one part, each
 // deriving the log2 cumsum itself.
-template <int D, int PART>
-__device__ __forceinline__ float prep_gates(Slot<D>& sl, int cv, int lane) {
+template <int D, int PART, bool QK>
+__device__ __forceinline__ float prep_gates(Slot<D, QK>& sl, int cv, int lane) {
   const ChunkGates gt = chunk_gates(lane < cv ? sl.f.alpha[lane] : 1.f, lane);
   if constexpr (PART == 2) {
     const float et = lane < cv ? sl.f.eta[lane] : 0.f;
@@ -193,16 +203,16 @@ __device__ __forceinline__ float prep_gates(Slot<D>& sl, int cv, int lane) {
 // Block b (0..9, row-major over the causal triangle of 16 x 16 blocks) of the
 // decayed scores of a chunk, written transposed: AT[j][i] = A_ij.  Blocks
 // above the diagonal are never written (they stay zero).
-template <int D>
-__device__ __forceinline__ void score_block(const Slot<D>& sl, __bf16* AT, const LaneOff<D>& oX,
+template <int D, bool QK>
+__device__ __forceinline__ void score_block(const Slot<D, QK>& sl, __bf16* AT, const LaneOff<D>& oX,
                                             const LaneOff<kC>& oA, int b, int lane) {
   const int g4 = lane >> 4, l16 = lane & 15;
   const int ib = tri_i(b), jb = tri_j(b);
   f32x4 xx = zero4();
 #pragma unroll
   for (int kb = 0; kb < D / 32; ++kb)
-    xx = mfma16x16x32(frag_s<D>(sl.X, oX, ib * 16, kb * 32), frag_s<D>(sl.X, oX, jb * 16, kb * 32),
-                      xx);
+    xx = mfma16x16x32(frag_s<D>(QK ? sl.Q : sl.X, oX, ib * 16, kb * 32),
+                      frag_s<D>(sl.X, oX, jb * 16, kb * 32), xx);
   const int j = jb * 16 + l16, i0 = ib * 16 + 4 * g4;
   f32x4 v;
   if (ib == jb) {  // diagonal block: decay per element, causal mask
@@ -227,8 +237,8 @@ __device__ __forceinline__ void score_block(const Slot<D>& sl, __bf16* AT, const
 
 // One thread's share of the decay-scaled g tile of a chunk:
 // GS[j][r] = bf16(g_j[r] e(l_last - l_j)(-eta_j)) for 4 consecutive r.
-template <int D>
-__device__ __forceinline__ void scale_g(const Slot<D>& sl, __bf16* GS, uint32_t off, int row) {
+template <int D, bool QK>
+__device__ __forceinline__ void scale_g(const Slot<D, QK>& sl, __bf16* GS, uint32_t off, int row) {
   const uint2 v = *reinterpret_cast<const uint2*>(reinterpret_cast<const char*>(sl.G) + off);
   const float s = sl.bk[row];
   uint2 r;
@@ -237,22 +247,24 @@ __device__ __forceinline__ void scale_g(const Slot<D>& sl, __bf16* GS, uint32_t 
   *reinterpret_cast<uint2*>(reinterpret_cast<char*>(GS) + off) = r;
 }
 
-template <int D, bool HAS_Y, bool HAS_ST, bool F32 = false>
+template <int D, bool HAS_Y, bool HAS_ST, bool F32 = false, bool QK = false>
 __global__ __launch_bounds__(kNT) void fwd_mfma(FwdArgs a) {
   static_assert(D == 64 || D == 128, "D");
+  static_assert(!QK || (D == 64 && HAS_Y && !HAS_ST), "a read tile of its own: d = 64, y only");
+  using SL = Slot<D, QK>;
   constexpr int NTILE = D / kTN;
   constexpr int NS = D / 64;  // 16x16 state blocks per state wave
-  constexpr int P = kLoadOps<D>;
+  constexpr int P = kLoadOps<D, QK>;
   constexpr int S = HAS_ST ? 1 : 0;  // stores per state wave per chunk
   // Each ring slot is a separate LDS object, and every reference to one is
   // static (the chunk loop is unrolled by kRing), so the compiler can tell a
   // slot being read from the slots still being filled and adds no waits.
-  __shared__ Slot<D> ring0, ring1, ring2, ring3, ring4;
+  __shared__ SL ring0, ring1, ring2, ring3, ring4;
   __shared__ __bf16 AT_s[2][kC * kC];  // AT[j][i] = A_ij, swizzled, by chunk parity
   __shared__ __bf16 S_s[2][kTN * D];   // D_in of the tile, bf16, swizzled [row][col], by parity
   __shared__ __bf16 GS_s[2][kC * kTN]; // decay-scaled g tile, swizzled, by chunk parity
   static_assert(kRing == 5, "ring objects");
-  Slot<D>* const rs[kRing] = {&ring0, &ring1, &ring2, &ring3, &ring4};
+  SL* const rs[kRing] = {&ring0, &ring1, &ring2, &ring3, &ring4};
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
@@ -277,6 +289,7 @@ __global__ __launch_bounds__(kNT) void fwd_mfma(FwdArgs a) {
   const int c_end = std::min(n, c_beg + a.seg_chunks);
   const int nloc = c_end - c_beg;
   const uint16_t* x = static_cast<const uint16_t*>(a.x) + bh * T * D;
+  const uint16_t* qv = QK ? static_cast<const uint16_t*>(a.q) + bh * T * D : nullptr;
   const uint16_t* g = static_cast<const uint16_t*>(a.g) + bh * T * D;
   const float* eta = static_cast<const float*>(a.eta) + bh * T;
   const float* alpha = static_cast<const float*>(a.alpha) + bh * T;
@@ -290,10 +303,18 @@ __global__ __launch_bounds__(kNT) void fwd_mfma(FwdArgs a) {
   // registers throughout
   bf16x8 wf[D / 32];
   if (HAS_Y && role == 0) {
+    const int wr = r0 + rbw * 16 + l16;
+    if (QK && a.w0_t) {  // W0' given transposed, [D (k)][D (r)]: gathered once
 #pragma unroll
-    for (int kb = 0; kb < D / 32; ++kb)
-      wf[kb] = *reinterpret_cast<const bf16x8*>(
-          W0 + static_cast<int64_t>(r0 + rbw * 16 + l16) * D + kb * 32 + 8 * g4);
+      for (int kb = 0; kb < D / 32; ++kb)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          wf[kb][e] = __builtin_bit_cast(__bf16, W0[static_cast<int64_t>(kb * 32 + 8 * g4 + e) * D + wr]);
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < D / 32; ++kb)
+        wf[kb] = *reinterpret_cast<const bf16x8*>(W0 + static_cast<int64_t>(wr) * D + kb * 32 + 8 * g4);
+    }
   }
   // state waves: starting state of the tile, zero or the segment's incoming
   // state (fp32 accumulators, and its bf16 copy for the first readout)
@@ -351,7 +372,7 @@ __global__ __launch_bounds__(kNT) void fwd_mfma(FwdArgs a) {
     // Then the wait at the top of every iteration is the same constant.
 #pragma unroll
     for (int k = 0; k < kRing - 1; ++k) {
-      issue_chunk<D>(*rs[k], od, x, g, eta, alpha, T, c_beg + k, c_end, r0, w8);
+      issue_chunk<D>(*rs[k], od, x, qv, g, eta, alpha, T, c_beg + k, c_end, r0, w8);
 #pragma unroll
       for (int s = 0; s < S; ++s) store8(r_none, 64 * k, make_uint2(0, 0));  // not merged
     }
@@ -383,10 +404,10 @@ __global__ __launch_bounds__(kNT) void fwd_mfma(FwdArgs a) {
   const auto step = [&](auto RC, auto KC, int c) {
     constexpr int R = decltype(RC)::value;
     constexpr int K = decltype(KC)::value;
-    Slot<D>& cur = *rs[K];
-    Slot<D>& nx1 = *rs[(K + 1) % kRing];
-    Slot<D>& nx2 = *rs[(K + 2) % kRing];
-    Slot<D>& dst = *rs[(K + kRing - 1) % kRing];
+    SL& cur = *rs[K];
+    SL& nx1 = *rs[(K + 1) % kRing];
+    SL& nx2 = *rs[(K + 2) % kRing];
+    SL& dst = *rs[(K + kRing - 1) % kRing];
     const int vl = c - c_beg;  // position in the segment: double-buffer parity
     const int64_t t0 = static_cast<int64_t>(c) * kC;
     const int cv = cv_of(c);
@@ -396,7 +417,7 @@ __global__ __launch_bounds__(kNT) void fwd_mfma(FwdArgs a) {
     if constexpr (R == 1) wait_vm<P + 2 * S>();
     lds_barrier();  // scores and gates of c + 1, D_in of c visible
     if constexpr (R == 1) {
-      issue_chunk<D>(dst, od, x, g, eta, alpha, T, c + kRing - 1, c_end, r0, w8);
+      issue_chunk<D>(dst, od, x, qv, g, eta, alpha, T, c + kRing - 1, c_end, r0, w8);
       if (HAS_ST) {
         // chunk-start state (natural layout, bf16): the copy in LDS that the
         // y waves read in this step, whole rows per store instruction
@@ -454,7 +475,7 @@ __global__ __launch_bounds__(kNT) void fwd_mfma(FwdArgs a) {
                           frag_ts<kC>(AT, oA, kb * 32, tb * 16), ya);
 #pragma unroll
       for (int kb = 0; kb < D / 32; ++kb) {
-        const bf16x8 xf = frag_s<D>(cur.X, oX, tb * 16, kb * 32);
+        const bf16x8 xf = frag_s<D>(QK ? cur.Q : cur.X, oX, tb * 16, kb * 32);
         ya = mfma16x16x32(wf[kb], xf, ya);
         yb = mfma16x16x32(frag_s<D>(S_in, oX, rbw * 16, kb * 32), xf, yb);
       }
@@ -512,7 +533,7 @@ __global__ __launch_bounds__(kNT) void fwd_mfma(FwdArgs a) {
     a.seg_lg[bh * a.n_seg + seg] = lsum;
 }
 
-template <int D, bool HAS_Y, bool HAS_ST, bool F32 = false>
+template <int D, bool HAS_Y, bool HAS_ST, bool F32 = false, bool QK = false>
 hipError_t launch_v(const FwdArgs& a, hipStream_t s, bool every_segment = false) {
   const int64_t groups = (a.B * a.H + 7) / 8;
   // the state-only pass of the segmented scan skips the last segment (nothing
@@ -520,7 +541,7 @@ hipError_t launch_v(const FwdArgs& a, hipStream_t s, bool every_segment = false)
   const int nseg = (!HAS_Y && !HAS_ST && !every_segment) ? a.n_seg - 1 : a.n_seg;
   if (nseg <= 0) return hipSuccess;
   const dim3 grid(static_cast<unsigned>(groups * 8 * (D / kTN) * nseg));
-  hipLaunchKernelGGL((fwd_mfma<D, HAS_Y, HAS_ST, F32>), grid, dim3(kNT), 0, s, a);
+  hipLaunchKernelGGL((fwd_mfma<D, HAS_Y, HAS_ST, F32, QK>), grid, dim3(kNT), 0, s, a);
   return hipGetLastError();
 }
 
@@ -539,6 +560,14 @@ hipError_t launch_d(const FwdArgs& a, hipStream_t s) {
 
 hipError_t launch_mfma_fwd(const FwdArgs& a, hipStream_t s) {
   return a.d_in == 128 ? launch_d<128>(a, s) : launch_d<64>(a, s);
+}
+
+// The scan with a read vector of its own (a.q; a.x is the write key, a.g the
+// value), d = 64, y only, one segment.
+hipError_t launch_mfma_qkv_fwd(const FwdArgs& a, hipStream_t s) {
+  if (a.d_in != 64 || a.d_out != 64 || !a.q || !a.y || a.states || a.n_seg != 1)
+    return hipErrorInvalidValue;
+  return launch_v<64, true, false, false, true>(a, s);
 }
 
 // The final state of every segment from a zero start (with one segment: the
