@@ -300,19 +300,23 @@ void bwd_f128(BwdArgs a) {
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
         __builtin_amdgcn_sched_barrier(0);
-        bf16x8 xf[2];
-#pragma unroll
-        for (int aa = 0; aa < 2; ++aa) xf[aa] = frag_ts<kD>(sl.X, o, kk * 32, (2 * kq + aa) * 16);
+        // the per-token factor e(lq_u) goes on the x fragments (two per K
+        // step) rather than on the four dy fragments: X^T (e o dy) = (e o X)^T dy
+        bf16x8 xf[2], xe[2];
         const f32x4 e0 = *reinterpret_cast<const f32x4*>(&rc.eq[kk * 32 + 8 * g4]);
         const f32x4 e1 = *reinterpret_cast<const f32x4*>(&rc.eq[kk * 32 + 8 * g4 + 4]);
 #pragma unroll
+        for (int aa = 0; aa < 2; ++aa) {
+          xf[aa] = frag_ts<kD>(sl.X, o, kk * 32, (2 * kq + aa) * 16);
+          xe[aa] = scale8(xf[aa], e0, e1);
+        }
+#pragma unroll
         for (int b = 0; b < 4; ++b) {
           const bf16x8 df = frag_ts<kD>(sl.DY, o, kk * 32, (4 * rh + b) * 16);
-          const bf16x8 de = scale8(df, e0, e1);
 #pragma unroll
           for (int aa = 0; aa < 2; ++aa) {
             dw[aa][b] = mfma16x16x32(xf[aa], df, dw[aa][b]);
-            lam[aa][b] = mfma16x16x32(xf[aa], de, lam[aa][b]);
+            lam[aa][b] = mfma16x16x32(xe[aa], df, lam[aa][b]);
           }
         }
       }
