@@ -200,19 +200,14 @@ __device__ __forceinline__ float prep_gates(Slot<D, QK>& sl, int cv, int lane) {
   }
 }
 
-// Block b (0..9, row-major over the causal triangle of 16 x 16 blocks) of the
-// decayed scores of a chunk, written transposed: AT[j][i] = A_ij.  Blocks
-// above the diagonal are never written (they stay zero).
+// Decayed score block (ib, jb), jb <= ib, of a chunk from its raw products
+// xx = (x_i . x_j) (q_i . k_j with a read tile), written transposed:
+// AT[j][i] = A_ij.  Blocks above the diagonal are never written (they stay
+// zero).
 template <int D, bool QK>
-__device__ __forceinline__ void score_block(const Slot<D, QK>& sl, __bf16* AT, const LaneOff<D>& oX,
-                                            const LaneOff<kC>& oA, int b, int lane) {
+__device__ __forceinline__ void score_out(const Slot<D, QK>& sl, __bf16* AT, const LaneOff<kC>& oA,
+                                          int ib, int jb, const f32x4& xx, int lane) {
   const int g4 = lane >> 4, l16 = lane & 15;
-  const int ib = tri_i(b), jb = tri_j(b);
-  f32x4 xx = zero4();
-#pragma unroll
-  for (int kb = 0; kb < D / 32; ++kb)
-    xx = mfma16x16x32(frag_s<D>(QK ? sl.Q : sl.X, oX, ib * 16, kb * 32),
-                      frag_s<D>(sl.X, oX, jb * 16, kb * 32), xx);
   const int j = jb * 16 + l16, i0 = ib * 16 + 4 * g4;
   f32x4 v;
   if (ib == jb) {  // diagonal block: decay per element, causal mask
@@ -233,6 +228,38 @@ __device__ __forceinline__ void score_block(const Slot<D, QK>& sl, __bf16* AT, c
   pk.x = pack2(v[0], v[1]);
   pk.y = pack2(v[2], v[3]);
   put4<kC>(AT, oA, jb * 16, ib * 16, pk);
+}
+
+// Strip s (0..3) of the causal triangle of 16 x 16 score blocks: the row
+// block's fragments are read once and serve every block of the strip.
+//   s = 0: row block 3, column blocks 0-1;  s = 1: row block 3, blocks 2-3;
+//   s = 2: row block 2, blocks 0-2;  s = 3: row block 1, blocks 0-1, and
+//   row block 0, block 0.
+template <int D, bool QK>
+__device__ __forceinline__ void score_strip(const Slot<D, QK>& sl, __bf16* AT, const LaneOff<D>& oX,
+                                            const LaneOff<kC>& oA, int s, int lane) {
+  const auto strip = [&](int ib, int jb0, int nj) {
+    bf16x8 af[D / 32];
+#pragma unroll
+    for (int kb = 0; kb < D / 32; ++kb) af[kb] = frag_s<D>(QK ? sl.Q : sl.X, oX, ib * 16, kb * 32);
+    for (int jb = jb0; jb < jb0 + nj; ++jb) {
+      __builtin_amdgcn_sched_barrier(0);  // one block's fragments live at a time
+      f32x4 xx = zero4();
+#pragma unroll
+      for (int kb = 0; kb < D / 32; ++kb) xx = mfma16x16x32(af[kb], frag_s<D>(sl.X, oX, jb * 16, kb * 32), xx);
+      score_out<D>(sl, AT, oA, ib, jb, xx, lane);
+    }
+  };
+  if (s == 0) {
+    strip(3, 0, 2);
+  } else if (s == 1) {
+    strip(3, 2, 2);
+  } else if (s == 2) {
+    strip(2, 0, 3);
+  } else {
+    strip(1, 0, 2);
+    strip(0, 0, 1);
+  }
 }
 
 // One thread's share of the decay-scaled g tile of a chunk:
@@ -345,7 +372,9 @@ __global__ __launch_bounds__(kNT) void fwd_mfma(FwdArgs a) {
   const DmaOff<D> od = dma_off<D>(w8, lane);
   // per-lane byte offsets of the stores (loop invariant; the buffer base
   // moves per chunk and its byte count drops rows past the sequence end)
-  const uint32_t oy = static_cast<uint32_t>(((tb * 16 + l16) * D + r0 + rbw * 16 + 4 * g4) * 2);
+  // (y waves 0-3: the first of their two token blocks, 2 (w8 / 2))
+  const uint32_t oy =
+      static_cast<uint32_t>(((2 * (w8 >> 1) * 16 + l16) * D + r0 + rbw * 16 + 4 * g4) * 2);
   const __amdgpu_buffer_rsrc_t r_none = buffer_rsrc(a.x, 0);
   // a state-wave thread's 4 elements of the scaled g tile: row t/8, columns 4 (t%8)..
   const int gt_id = tid & 511;
@@ -395,10 +424,7 @@ __global__ __launch_bounds__(kNT) void fwd_mfma(FwdArgs a) {
   }
   lds_barrier();
   if (role == 1) scale_g<D>(*rs[0], GS_s[0], gs_off, gs_row);
-  if (HAS_Y && role == 0) {
-    score_block<D>(*rs[0], AT_s[0], oX, oA, w8, lane);
-    if (w8 < 2) score_block<D>(*rs[0], AT_s[0], oX, oA, w8 + 8, lane);
-  }
+  if (HAS_Y && role == 0 && w8 >= 4) score_strip<D>(*rs[0], AT_s[0], oX, oA, w8 - 4, lane);
 
   // one chunk; K = (c - c_beg) % kRing is a compile-time constant
   const auto step = [&](auto RC, auto KC, int c) {
@@ -452,10 +478,7 @@ __global__ __launch_bounds__(kNT) void fwd_mfma(FwdArgs a) {
         put4<D>(S_out, oX, rbw * 16, cb * 16, pk);
       }
     } else {
-      if (HAS_Y) {
-        score_block<D>(nx1, AT_s[(vl + 1) & 1], oX, oA, w8, lane);
-        if (w8 < 2) score_block<D>(nx1, AT_s[(vl + 1) & 1], oX, oA, w8 + 8, lane);
-      }
+      if (HAS_Y && w8 >= 4) score_strip<D>(nx1, AT_s[(vl + 1) & 1], oX, oA, w8 - 4, lane);
       // gates of chunk c + 2 (loaded: the state waves waited for it before
       // the barrier), two halves on two waves
       if (!HAS_Y) {
@@ -463,33 +486,48 @@ __global__ __launch_bounds__(kNT) void fwd_mfma(FwdArgs a) {
         if (w8 == kPrepWave + 1) prep_gates<D, 1>(nx2, cv_of(c + 2), lane);
         return;
       }
-      // y^T[r][i] for this wave's block; each lane stores 4 consecutive rows
-      // of one token straight from the accumulators.  (For token blocks 0
-      // and 1 the second K block of A^T is zero.)
+      // y waves 0-3: y^T[r][i] for row block rbw and the token blocks 2 p,
+      // 2 p + 1 (p = w8 / 2), sharing the row block's fragments of G^T and
+      // D_in; each lane stores 4 consecutive rows of one token straight from
+      // the accumulators.  (For token blocks 0 and 1 the second K block of
+      // A^T is zero.)  Waves 4-7 form the scores of the next chunk.
+      if (w8 >= 4) return;
+      const int pb = 2 * (w8 >> 1);
       const __bf16* S_in = S_s[vl & 1];
       const __bf16* AT = AT_s[vl & 1];
-      f32x4 ya = zero4(), yb = zero4();
+      f32x4 ya[2] = {zero4(), zero4()}, yb[2] = {zero4(), zero4()};
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-        ya = mfma16x16x32(frag_ts<kTN>(cur.G, oG, kb * 32, rbw * 16),
-                          frag_ts<kC>(AT, oA, kb * 32, tb * 16), ya);
+      for (int kb = 0; kb < 2; ++kb) {
+        const bf16x8 gf = frag_ts<kTN>(cur.G, oG, kb * 32, rbw * 16);
+#pragma unroll
+        for (int t = 0; t < 2; ++t) ya[t] = mfma16x16x32(gf, frag_ts<kC>(AT, oA, kb * 32, (pb + t) * 16), ya[t]);
+      }
 #pragma unroll
       for (int kb = 0; kb < D / 32; ++kb) {
-        const bf16x8 xf = frag_s<D>(QK ? cur.Q : cur.X, oX, tb * 16, kb * 32);
-        ya = mfma16x16x32(wf[kb], xf, ya);
-        yb = mfma16x16x32(frag_s<D>(S_in, oX, rbw * 16, kb * 32), xf, yb);
+        __builtin_amdgcn_sched_barrier(0);  // one K step of fragments live at a time
+        const bf16x8 sf = frag_s<D>(S_in, oX, rbw * 16, kb * 32);
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const bf16x8 xf = frag_s<D>(QK ? cur.Q : cur.X, oX, (pb + t) * 16, kb * 32);
+          ya[t] = mfma16x16x32(wf[kb], xf, ya[t]);
+          yb[t] = mfma16x16x32(sf, xf, yb[t]);
+        }
       }
-      const float eqi = cur.f.eq[tb * 16 + l16];
       const __amdgpu_buffer_rsrc_t ry = buffer_rsrc(y + t0 * D * YE, cv * D * YE);
-      if constexpr (F32) {
-        typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
-        const f32x4 yo = ya + eqi * yb;
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, yo), ry, 2 * oy, 0, 0);
-      } else {
-        uint2 pk;
-        pk.x = pack2(ya[0] + eqi * yb[0], ya[1] + eqi * yb[1]);
-        pk.y = pack2(ya[2] + eqi * yb[2], ya[3] + eqi * yb[3]);
-        store8(ry, oy, pk);
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const float eqi = cur.f.eq[(pb + t) * 16 + l16];
+        const uint32_t oyt = oy + static_cast<uint32_t>(t * 16 * D * 2);
+        if constexpr (F32) {
+          typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+          const f32x4 yo = ya[t] + eqi * yb[t];
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, yo), ry, 2 * oyt, 0, 0);
+        } else {
+          uint2 pk;
+          pk.x = pack2(ya[t][0] + eqi * yb[t][0], ya[t][1] + eqi * yb[t][1]);
+          pk.y = pack2(ya[t][2] + eqi * yb[t][2], ya[t][3] + eqi * yb[t][3]);
+          store8(ry, oyt, pk);
+        }
       }
     }
   };
