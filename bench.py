@@ -485,6 +485,12 @@ def qkv_main(args, w):
     desc = ws.make_desc(w.B, w.H, w.T, w.d_out, w.d_in, io, flags=flags)
     on_mfma = w.dtype == "bf16" and w.d_in == 64 and w.d_out == 64 and not args.generic
     flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    # the plain copy of known size that calibrates FETCH_SIZE / WRITE_SIZE
+    calib_src = torch.ones(64 << 20, dtype=torch.float32, device=dev)
+    calib_dst = torch.empty_like(calib_src)
+    torch.neg(calib_src, out=calib_dst)  # 256 MiB in, 256 MiB out
+    torch.cuda.synchronize()
+    del calib_src, calib_dst
     L = ws.lib()
     stream = torch.cuda.current_stream(dev)
     sp = ctypes.c_void_p(stream.cuda_stream)
