@@ -10,8 +10,9 @@ Tolerances (relative-max error, as in parity_util):
              exact in the io dtype, so the only error is fp32 rounding of the
              accumulation; at T = 4096 tokens 1e-3 (T * 2^-24 = 2.4e-4, x4).
              The matrix-core hand-over (bf16, d_in = d_out in {64, 128}) takes
-             the forward scan's arithmetic: x and the decay-scaled g are bf16
-             MFMA operands, two roundings of 2^-9 per term: 1e-2.
+             the decay-scaled g as a pair of bf16 MFMA operands (value and
+             remainder, about 2^-17 per term) against the exact bf16 x: the
+             same bounds as the fp32 route.
 """
 import numpy as np
 import pytest
@@ -25,12 +26,12 @@ from weight_scans_amd.synth import CONFIGS, Workload, make_inputs, round_to
 pytestmark = pytest.mark.gpu
 
 STATE_TOL = {"f64": 1e-10, "f32": 1e-4, "bf16": 1e-4}
-MFMA_STATE_TOL = 1e-2
 
 
 def hand_over_tol(io, d_in, d_out, flags=0):
-    mfma = io == "bf16" and d_in == d_out and d_in in (64, 128) and not flags
-    return MFMA_STATE_TOL if mfma else STATE_TOL[io]
+    # the matrix-core route (bf16, d_in = d_out in {64, 128}) and the vector
+    # route are held to the same bound
+    return STATE_TOL[io]
 
 
 def say(msg):
@@ -191,7 +192,7 @@ def test_final_state_full_size_sampled():
         _, want = oracle.seq_fwd(inp["x"][b, h], inp["g"][b, h], inp["eta"][b, h],
                                  inp["alpha"][b, h], np.zeros((w.d_out, w.d_in)))
         err, errg = relmax(S[b, h], want), relmax(Sg[b, h], want)
-        assert err <= MFMA_STATE_TOL and errg <= 1e-3, (b, h, err, errg)
+        assert err <= 1e-3 and errg <= 1e-3, (b, h, err, errg)
 
 
 def test_empty_batch_is_a_noop():

@@ -274,7 +274,34 @@ __device__ __forceinline__ void scale_g(const Slot<D, QK>& sl, __bf16* GS, uint3
   *reinterpret_cast<uint2*>(reinterpret_cast<char*>(GS) + off) = r;
 }
 
-template <int D, bool HAS_Y, bool HAS_ST, bool F32 = false, bool QK = false>
+// The same with the remainder of each product, v - bf16(v) (exact in fp32),
+// rounded to bf16 into GL: the pair carries the product to about 2^-17.
+template <int D, bool QK>
+__device__ __forceinline__ void scale_g_split(const Slot<D, QK>& sl, __bf16* GS, __bf16* GL,
+                                              uint32_t off, int row) {
+  const uint2 v = *reinterpret_cast<const uint2*>(reinterpret_cast<const char*>(sl.G) + off);
+  const float s = sl.bk[row];
+  const float p0 = bf16_val(v.x & 0xffffu) * s, p1 = bf16_val(v.x >> 16) * s;
+  const float p2 = bf16_val(v.y & 0xffffu) * s, p3 = bf16_val(v.y >> 16) * s;
+  uint2 h, l;
+  h.x = pack2(p0, p1);
+  h.y = pack2(p2, p3);
+  l.x = pack2(p0 - bf16_val(h.x & 0xffffu), p1 - bf16_val(h.x >> 16));
+  l.y = pack2(p2 - bf16_val(h.y & 0xffffu), p3 - bf16_val(h.y >> 16));
+  *reinterpret_cast<uint2*>(reinterpret_cast<char*>(GS) + off) = h;
+  *reinterpret_cast<uint2*>(reinterpret_cast<char*>(GL) + off) = l;
+}
+
+// The remainder tiles of the split decay-scaled g, by chunk parity; empty
+// where the split is not used.
+template <bool ON>
+struct RemTiles {
+  __bf16 t[2][kC * kTN];
+};
+template <>
+struct RemTiles<false> {};
+
+template <int D, bool HAS_Y, bool HAS_ST, bool F32 = false, bool QK = false, bool SPLIT = false>
 __global__ __launch_bounds__(kNT) void fwd_mfma(FwdArgs a) {
   static_assert(D == 64 || D == 128, "D");
   static_assert(!QK || (D == 64 && HAS_Y && !HAS_ST), "a read tile of its own: d = 64, y only");
@@ -290,6 +317,12 @@ __global__ __launch_bounds__(kNT) void fwd_mfma(FwdArgs a) {
   __shared__ __bf16 AT_s[2][kC * kC];  // AT[j][i] = A_ij, swizzled, by chunk parity
   __shared__ __bf16 S_s[2][kTN * D];   // D_in of the tile, bf16, swizzled [row][col], by parity
   __shared__ __bf16 GS_s[2][kC * kTN]; // decay-scaled g tile, swizzled, by chunk parity
+  // The hand-over instance carries the decay-scaled g as a bf16 pair (value
+  // and remainder): its state is a result of its own, not only an operand of
+  // the next readout.
+  constexpr bool HILO = SPLIT;
+  static_assert(!SPLIT || (!HAS_Y && !HAS_ST), "the split is for the state-only instance");
+  __shared__ RemTiles<HILO> GL;  // (empty in the other instances)
   static_assert(kRing == 5, "ring objects");
   SL* const rs[kRing] = {&ring0, &ring1, &ring2, &ring3, &ring4};
 
@@ -423,7 +456,12 @@ __global__ __launch_bounds__(kNT) void fwd_mfma(FwdArgs a) {
     prep_gates<D, 1>(*rs[1], cv_of(c_beg + 1), lane);
   }
   lds_barrier();
-  if (role == 1) scale_g<D>(*rs[0], GS_s[0], gs_off, gs_row);
+  if (role == 1) {
+    if constexpr (HILO)
+      scale_g_split<D>(*rs[0], GS_s[0], GL.t[0], gs_off, gs_row);
+    else
+      scale_g<D>(*rs[0], GS_s[0], gs_off, gs_row);
+  }
   if (HAS_Y && role == 0 && w8 >= 4) score_strip<D>(*rs[0], AT_s[0], oX, oA, w8 - 4, lane);
 
   // one chunk; K = (c - c_beg) % kRing is a compile-time constant
@@ -456,13 +494,19 @@ __global__ __launch_bounds__(kNT) void fwd_mfma(FwdArgs a) {
           store8(r_st, st_g, *reinterpret_cast<const uint2*>(sp));
       }
       if (HAS_Y && w8 == kPrepWave) lsum += prep_gates<D, 2>(nx2, cv_of(c + 2), lane);
-      scale_g<D>(nx1, GS_s[(vl + 1) & 1], gs_off, gs_row);
+      if constexpr (HILO)
+        scale_g_split<D>(nx1, GS_s[(vl + 1) & 1], GL.t[(vl + 1) & 1], gs_off, gs_row);
+      else
+        scale_g<D>(nx1, GS_s[(vl + 1) & 1], gs_off, gs_row);
       // state update, transposed: D^T[c][r] = Gamma D^T + sum_j x_j[c] (bk_j g_j[r]),
       // into the other state buffer (the current one may still be read)
       const __bf16* GS = GS_s[vl & 1];
-      bf16x8 gs[2];
+      bf16x8 gs[2], gl[2];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) gs[kb] = frag_ts<kTN>(GS, oG, kb * 32, rbw * 16);
+      for (int kb = 0; kb < 2; ++kb) {
+        gs[kb] = frag_ts<kTN>(GS, oG, kb * 32, rbw * 16);
+        if constexpr (HILO) gl[kb] = frag_ts<kTN>(GL.t[vl & 1], oG, kb * 32, rbw * 16);
+      }
       const float gam = cur.gam[0];
       __bf16* S_out = S_s[(vl + 1) & 1];
 #pragma unroll
@@ -470,8 +514,11 @@ __global__ __launch_bounds__(kNT) void fwd_mfma(FwdArgs a) {
         const int cb = tb + 4 * s;
         sacc[s] = sacc[s] * gam;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-          sacc[s] = mfma16x16x32(frag_ts<D>(cur.X, oX, kb * 32, cb * 16), gs[kb], sacc[s]);
+        for (int kb = 0; kb < 2; ++kb) {
+          const bf16x8 xf = frag_ts<D>(cur.X, oX, kb * 32, cb * 16);
+          sacc[s] = mfma16x16x32(xf, gs[kb], sacc[s]);
+          if constexpr (HILO) sacc[s] = mfma16x16x32(xf, gl[kb], sacc[s]);
+        }
         uint2 pk;
         pk.x = pack2(sacc[s][0], sacc[s][1]);
         pk.y = pack2(sacc[s][2], sacc[s][3]);
@@ -571,7 +618,7 @@ __global__ __launch_bounds__(kNT) void fwd_mfma(FwdArgs a) {
     a.seg_lg[bh * a.n_seg + seg] = lsum;
 }
 
-template <int D, bool HAS_Y, bool HAS_ST, bool F32 = false, bool QK = false>
+template <int D, bool HAS_Y, bool HAS_ST, bool F32 = false, bool QK = false, bool SPLIT = false>
 hipError_t launch_v(const FwdArgs& a, hipStream_t s, bool every_segment = false) {
   const int64_t groups = (a.B * a.H + 7) / 8;
   // the state-only pass of the segmented scan skips the last segment (nothing
@@ -579,7 +626,7 @@ hipError_t launch_v(const FwdArgs& a, hipStream_t s, bool every_segment = false)
   const int nseg = (!HAS_Y && !HAS_ST && !every_segment) ? a.n_seg - 1 : a.n_seg;
   if (nseg <= 0) return hipSuccess;
   const dim3 grid(static_cast<unsigned>(groups * 8 * (D / kTN) * nseg));
-  hipLaunchKernelGGL((fwd_mfma<D, HAS_Y, HAS_ST, F32, QK>), grid, dim3(kNT), 0, s, a);
+  hipLaunchKernelGGL((fwd_mfma<D, HAS_Y, HAS_ST, F32, QK, SPLIT>), grid, dim3(kNT), 0, s, a);
   return hipGetLastError();
 }
 
@@ -611,8 +658,8 @@ hipError_t launch_mfma_qkv_fwd(const FwdArgs& a, hipStream_t s) {
 // The final state of every segment from a zero start (with one segment: the
 // adaptation after the last token, D_T) into a.seg_out [B*H][n_seg][D][D].
 hipError_t launch_mfma_final_state(const FwdArgs& a, hipStream_t s) {
-  return a.d_in == 128 ? launch_v<128, false, false>(a, s, true)
-                       : launch_v<64, false, false>(a, s, true);
+  return a.d_in == 128 ? launch_v<128, false, false, false, false, true>(a, s, true)
+                       : launch_v<64, false, false, false, false, true>(a, s, true);
 }
 
 }  // namespace gls
