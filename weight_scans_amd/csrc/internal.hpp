@@ -149,6 +149,7 @@ struct FinArgs {
   int n_seg = 1;             // dW0 partials per (b, h)
   bool alpha_done = false;   // dalpha already written (fused backward)
   bool eta_done = false;     // deta already written (fused backward)
+  int lanes = 1;             // lanes summing one dW0 element group (set by the launcher)
 };
 
 // Generic (VALU) kernels: any 1 <= d_in, d_out <= 128, all io types.

@@ -401,27 +401,36 @@ __global__ __launch_bounds__(kThreads) void finalize_kernel(FinArgs a) {
     if (!a.eta_done) static_cast<T*>(a.deta)[i] = se;
     if (!a.alpha_done) static_cast<T*>(a.dalpha)[i] = sa;
   }
-  const int64_t nb = a.B * a.n_seg;  // partials [n_seg][B][H][.], summed in this order
+  const int64_t nb = a.B * a.n_seg;  // partials [n_seg][B][H][.]
   if constexpr (sizeof(T) == 4) {
     if ((HD & 3) == 0) {
-      // four elements per thread, the loads of four partials in flight
+      // four elements per lane group of L = a.lanes lanes (a power of two up
+      // to 64): lane j of a group sums partials j, j + L, ... in that order,
+      // then the group folds by xor-shuffles over 1, 2, .., L / 2 -- a fixed
+      // order, so the result is the same from run to run
       typedef float f4 __attribute__((ext_vector_type(4)));
       const f4* pw4 = reinterpret_cast<const f4*>(pw);
       const int64_t HD4 = HD >> 2;
-      for (int64_t i = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; i < HD4;
-           i += stride) {
+      const int L = a.lanes, lg = __builtin_ctz(static_cast<unsigned>(L));
+      const int gpw = 64 >> lg;  // groups per wave
+      const int lane = static_cast<int>(threadIdx.x) & 63, j = lane & (L - 1);
+      const int64_t wave = (blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x) >> 6;
+      const int64_t n_waves = (static_cast<int64_t>(gridDim.x) * blockDim.x) >> 6;
+      // the loop bound is the same for every lane of a wave (the shuffles
+      // below need the whole wave)
+      for (int64_t base = wave * gpw; base < HD4; base += n_waves * gpw) {
+        const int64_t gi = base + (lane >> lg);
+        const bool on = gi < HD4;
         f4 s = {0.f, 0.f, 0.f, 0.f};
-        int64_t b = 0;
-        for (; b + 4 <= nb; b += 4) {
-          const f4 v0 = pw4[b * HD4 + i], v1 = pw4[(b + 1) * HD4 + i];
-          const f4 v2 = pw4[(b + 2) * HD4 + i], v3 = pw4[(b + 3) * HD4 + i];
-          s += v0;
-          s += v1;
-          s += v2;
-          s += v3;
+        if (on)
+          for (int64_t b = j; b < nb; b += L) s += pw4[b * HD4 + gi];
+        for (int o = 1; o < L; o <<= 1) {
+          s[0] += __shfl_xor(s[0], o, 64);
+          s[1] += __shfl_xor(s[1], o, 64);
+          s[2] += __shfl_xor(s[2], o, 64);
+          s[3] += __shfl_xor(s[3], o, 64);
         }
-        for (; b < nb; ++b) s += pw4[b * HD4 + i];
-        reinterpret_cast<f4*>(a.dW0)[i] = s;
+        if (on && j == 0) reinterpret_cast<f4*>(a.dW0)[gi] = s;
       }
       return;
     }
@@ -524,9 +533,19 @@ hipError_t launch_clear(void* p, size_t bytes, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_finalize(int io, const FinArgs& a, hipStream_t s) {
-  const int64_t n = std::max<int64_t>((a.eta_done && a.alpha_done) ? 0 : a.B * a.H * a.T,
-                                      a.H * static_cast<int64_t>(a.d_in) * a.d_out);
+hipError_t launch_finalize(int io, const FinArgs& a0, hipStream_t s) {
+  FinArgs a = a0;
+  // lanes per dW0 element group: the partial count rounded up to a power of
+  // two, at most 64
+  const int64_t nb = a.B * a.n_seg;
+  a.lanes = 1;
+  while (a.lanes < 64 && a.lanes < nb) a.lanes <<= 1;
+  // threads: the per-token sums, the lane groups of the 4-wide dW0 sums, or
+  // one per dW0 element (the element-wise path: fp64, or H d_in d_out not a
+  // multiple of 4)
+  const int64_t HD = a.H * static_cast<int64_t>(a.d_in) * a.d_out;
+  const int64_t n = std::max<int64_t>({(a.eta_done && a.alpha_done) ? 0 : a.B * a.H * a.T, HD,
+                                       (HD + 3) / 4 * a.lanes});
   const unsigned blocks = static_cast<unsigned>(std::min<int64_t>(4096, (n + kThreads - 1) / kThreads));
   if (blocks == 0) return hipSuccess;
   if (io == IO_F64)

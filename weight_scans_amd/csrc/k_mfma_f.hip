@@ -345,8 +345,8 @@ __global__ __launch_bounds__(kCarryThreads) void mf_carry(T* buf, const T* gam, 
   if (e >= dd) return;
   T* p = buf + bh * n * static_cast<int64_t>(dd) + e;
   const T* gm = gam + bh * n;
-  // chunks in groups of eight: the group's loads are issued together
-  constexpr int kG = 8;
+  // chunks in groups of sixteen: the group's loads are issued together
+  constexpr int kG = 16;
   T carry = T(0);
   for (int k0 = 0; k0 < n; k0 += kG) {
     T inc[kG], dec[kG];
