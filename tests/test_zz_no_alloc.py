@@ -39,6 +39,9 @@ def _pair(w, flags=0):
      Workload("na4", 1, 2, 700, 128, 128, "bf16", "mix", "unit", 3004)),
     (Workload("na5", 2, 3, 300, 48, 40, "f64", "mix", "gauss", 3005),
      Workload("na6", 1, 2, 70, 20, 24, "f64", "base", "gauss", 3006)),
+    # the fp32 matrix-core kernels (their adjoint and decay buffers in the scratch)
+    (Workload("na7", 4, 8, 1024, 64, 64, "f32", "base", "gauss", 3007),
+     Workload("na8", 1, 3, 130, 30, 50, "f32", "mix", "gauss", 3008)),
 ])
 def test_static_scratch_matches_workspace(first, second):
     for w in (first, second):
