@@ -142,6 +142,10 @@ EDGE = [
     ("f64", 1, 2, 33, 128, 3), ("f32", 2, 2, 63, 32, 32), ("f32", 1, 3, 64, 48, 80),
     ("f32", 1, 1, 65, 64, 64), ("f32", 1, 2, 1000, 16, 24), ("bf16", 2, 2, 65, 64, 64),
     ("bf16", 1, 2, 1000, 128, 128), ("bf16", 1, 1, 2, 128, 128), ("bf16", 3, 1, 129, 40, 72),
+    # the fp32 / fp64 matrix-core kernels with ragged widths (element-wise tile
+    # loads) and one full width against a ragged one
+    ("f32", 2, 2, 129, 64, 17), ("f32", 1, 3, 191, 33, 64), ("f64", 2, 2, 129, 32, 31),
+    ("f64", 1, 1, 64, 1, 32),
 ]
 
 
