@@ -483,7 +483,11 @@ def qkv_main(args, w):
     # transpose read: q = u (length d_out), k = g, v = x (length d_in)
     flags = ws.GL_FLAG_GENERIC if args.generic else 0
     desc = ws.make_desc(w.B, w.H, w.T, w.d_out, w.d_in, io, flags=flags)
-    on_mfma = w.dtype == "bf16" and w.d_in == 64 and w.d_out == 64 and not args.generic
+    on_mfma = (w.dtype == "bf16" and w.d_in == w.d_out and w.d_in in (64, 128)
+               and not args.generic)
+    nws = ctypes.c_size_t()
+    ws._check(ws.lib().gl_scan_qkv_fwd_workspace_size(ctypes.byref(desc), ctypes.byref(nws)))
+    qws = torch.empty(max(nws.value, 16), dtype=torch.uint8, device=dev)
     flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)
     # the plain copy of known size that calibrates FETCH_SIZE / WRITE_SIZE
     calib_src = torch.ones(64 << 20, dtype=torch.float32, device=dev)
@@ -497,8 +501,9 @@ def qkv_main(args, w):
     P = lambda a: ctypes.c_void_p(a.data_ptr())  # noqa: E731
 
     def step():
-        ws._check(L.gl_scan_qkv_fwd(ctypes.byref(desc), P(t["dy"]), P(t["g"]), P(t["x"]),
-                                    P(t["eta"]), P(t["alpha"]), P(t["W0"]), 1, P(z), sp))
+        ws._check(L.gl_scan_qkv_fwd_ws(ctypes.byref(desc), P(t["dy"]), P(t["g"]), P(t["x"]),
+                                       P(t["eta"]), P(t["alpha"]), P(t["W0"]), 1, P(z), P(qws),
+                                       nws.value, sp))
 
     for _ in range(args.warmup):
         step()
@@ -524,9 +529,10 @@ def qkv_main(args, w):
         e = 2
         nbytes = (w.B * w.H * w.T * (e * (2 * w.d_out + 2 * w.d_in) + 8)
                   + w.H * w.d_in * w.d_out * e)
+        kern = ("fwd_mfma<64> with a read tile of its own (chunked, matrix cores)" if w.d_in == 64
+                else "fwd_mfma<128> state pass + qkv_chunk (chunk-parallel outputs, matrix cores)")
         roof = {"bound": "hbm", "achieved": nbytes / 1e9 / (ms / 1e3), "peak": PEAK_HBM / 1e9,
-                "unit": "GB/s", "traffic": None, "algorithmic_bytes": nbytes,
-                "kernel": "fwd_mfma<64> with a read tile of its own (chunked, matrix cores)"}
+                "unit": "GB/s", "traffic": None, "algorithmic_bytes": nbytes, "kernel": kern}
     else:
         achieved = nflops / 1e12 / (ms / 1e3)
         peak = PEAK_VALU[w.dtype] / 1e12

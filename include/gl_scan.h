@@ -233,13 +233,34 @@ gl_status_t gl_costate_quadratic(const gl_scan_desc_t* desc, const void* y, cons
  * q = x, k = x_bar, v = g a write key of its own (section "Once the gradient
  * signals are known, the weight trajectory becomes parallelizable").
  * desc->d_in = dk (length of q and k), desc->d_out = dv (length of v and y);
- * chunk, flags and segments are not used.  q, k [B][H][T][dk] io,
- * v, y [B][H][T][dv] io, eta, alpha [B][H][T] gate dtype, W0 [H][dv][dk] io,
- * or [H][dk][dv] when w0_transposed != 0.  Same rules as gl_scan_fwd;
- * B*H*T == 0 is a no-op. */
+ * chunk and segments are not used; GL_FLAG_GENERIC keeps every shape on the
+ * token-serial vector kernel.  q, k [B][H][T][dk] io, v, y [B][H][T][dv] io,
+ * eta, alpha [B][H][T] gate dtype, W0 [H][dv][dk] io, or [H][dk][dv] when
+ * w0_transposed != 0.  Same rules as gl_scan_fwd; B*H*T == 0 is a no-op.
+ * bf16 with dk = dv = 64 runs on the matrix cores (the chunked forward with a
+ * read tile of its own); bf16 with dk = dv = 128 does so only through
+ * gl_scan_qkv_fwd_ws with a workspace (here it takes the token-serial kernel);
+ * every other case runs the token-serial kernel. */
 gl_status_t gl_scan_qkv_fwd(const gl_scan_desc_t* desc, const void* q, const void* k,
                             const void* v, const void* eta, const void* alpha, const void* W0,
                             int w0_transposed, void* y, void* stream);
+
+/* Workspace bytes gl_scan_qkv_fwd_ws uses: the chunk-start states of the
+ * write-key scan (bf16, B*H*ceil(T/64)*dv*dk elements) for bf16 with
+ * dk = dv = 128 without GL_FLAG_GENERIC; 0 otherwise. */
+gl_status_t gl_scan_qkv_fwd_workspace_size(const gl_scan_desc_t* desc, size_t* ws_bytes);
+
+/* gl_scan_qkv_fwd with a caller workspace (ws_bytes from
+ * gl_scan_qkv_fwd_workspace_size; ws may be NULL when that is 0).  For bf16
+ * with dk = dv = 128 it runs in two launches on the matrix cores: the
+ * forward scan's state-only pass writes the chunk-start states into ws, then
+ * every chunk's outputs are formed from them in parallel.  A smaller
+ * workspace returns GL_ERROR_WORKSPACE_TOO_SMALL before any launch.  Results
+ * as gl_scan_qkv_fwd. */
+gl_status_t gl_scan_qkv_fwd_ws(const gl_scan_desc_t* desc, const void* q, const void* k,
+                               const void* v, const void* eta, const void* alpha, const void* W0,
+                               int w0_transposed, void* y, void* ws, size_t ws_bytes,
+                               void* stream);
 
 /* The reverse scan of gl_scan_qkv_fwd: for upstream dy [B][H][T][dv] io,
  * the gradients of L = sum_t <dy_t, y_t> w.r.t. q, k, v, eta, alpha and W0',

@@ -274,3 +274,23 @@ def test_static_backward_refuses_a_workspace_beyond_its_scratch():
     assert st == 4 and b"static scratch" in ws.lib().gl_last_error()
     # argument errors come first, as in gl_scan_bwd
     assert ws.lib().gl_scan_bwd_static(None, *([f] * 12), None) == 1
+
+
+def test_qkv_forward_workspace():
+    # bf16 at dk = dv = 128: the chunk-start states (bf16) in the caller's
+    # workspace; GL_FLAG_GENERIC and other shapes need none; a workspace below
+    # the figure is refused before any launch (fake device pointers)
+    d = ws.make_desc(2, 3, 300, 128, 128, ws.GL_DTYPE_BF16)
+    n = ctypes.c_size_t()
+    assert ws.lib().gl_scan_qkv_fwd_workspace_size(ctypes.byref(d), ctypes.byref(n)) == 0
+    assert n.value >= 2 * 3 * 5 * 128 * 128 * 2
+    for dd in (ws.make_desc(2, 3, 300, 128, 128, ws.GL_DTYPE_BF16, flags=ws.GL_FLAG_GENERIC),
+               ws.make_desc(2, 3, 300, 64, 64, ws.GL_DTYPE_BF16),
+               ws.make_desc(2, 3, 300, 128, 128, ws.GL_DTYPE_F32)):
+        m = ctypes.c_size_t(1)
+        assert ws.lib().gl_scan_qkv_fwd_workspace_size(ctypes.byref(dd), ctypes.byref(m)) == 0
+        assert m.value == 0
+    fake = ctypes.c_void_p(0x10000)
+    st = ws.lib().gl_scan_qkv_fwd_ws(ctypes.byref(d), *([fake] * 6), 0, fake, fake, n.value - 256,
+                                    None)
+    assert st == 4

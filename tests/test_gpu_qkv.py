@@ -78,14 +78,16 @@ def test_qkv_with_equal_keys_is_the_forward_scan():
 
 @pytest.mark.parametrize("T", [1, 63, 65, 300])
 @pytest.mark.parametrize("transposed", [True, False])
-def test_bf16_d64_on_the_matrix_cores(T, transposed):
+@pytest.mark.parametrize("d", [64, 128])
+def test_bf16_on_the_matrix_cores(d, T, transposed):
     # bf16 with dk = dv = 64 runs the forward matrix-core kernel with a read
-    # tile of its own; GL_FLAG_GENERIC keeps it on the token-serial kernel.
-    # Both within the scan's bf16 bounds of the oracle (max-norm and the
-    # RMS / bias / slope statistics).
+    # tile of its own, dk = dv = 128 the state pass and the chunk-parallel
+    # outputs (with the workspace the binding passes); GL_FLAG_GENERIC keeps
+    # both on the token-serial kernel.  Every route within the scan's bf16
+    # bounds of the oracle (max-norm and the RMS / bias / slope statistics).
     from parity_util import error_stats, stats_ok
-    say(f"bf16 d=64 matrix cores T={T} transposed={transposed}")
-    inp, dev = case("bf16", 2, 3, T, 64, 64, seed=1900 + T + int(transposed))
+    say(f"bf16 d={d} matrix cores T={T} transposed={transposed}")
+    inp, dev = case("bf16", 2, 3, T, d, d, seed=1900 + T + int(transposed) + d)
     rng = np.random.default_rng(1950 + T)
     qn = round_to(rng.standard_normal(inp["x"].shape) / 8.0, "bf16")
     qd = torch.from_numpy(qn).to("cuda", torch.bfloat16)
@@ -100,6 +102,23 @@ def test_bf16_d64_on_the_matrix_cores(T, transposed):
         say(f"  flags {flags}: relmax {err:.3g} {st}")
         assert err <= TOL["bf16"], (flags, err)
         assert stats_ok(st), (flags, st)
+
+
+def test_transpose_read_full_size_sampled_d128():
+    # the 1.3B-model shape (B=4, H=16, T=4096, d=128, bf16) on the matrix
+    # cores, three heads against the oracle
+    w = CONFIGS["c4"]
+    say(f"transpose read full size {w}")
+    inp = make_inputs(w)
+    dev = to_device(inp, w.dtype)
+    z = host(ws.transpose_read(dev["dy"], dev["g"], dev["x"], dev["eta"], dev["alpha"],
+                               dev["W0"]))
+    for b, h in ((0, 0), (2, 9), (3, 15)):
+        sl = lambda k: inp[k][b:b + 1, h:h + 1]  # noqa: E731
+        want = oracle.qkv_fwd(sl("dy"), sl("g"), sl("x"), sl("eta"), sl("alpha"),
+                              inp["W0"][h:h + 1].transpose(0, 2, 1))
+        err = relmax(z[b, h], want[0, 0])
+        assert err <= TOL["bf16"], (b, h, err)
 
 
 def test_transpose_read_full_size_sampled():

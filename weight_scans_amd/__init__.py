@@ -46,6 +46,8 @@ EXPORTS = (
     "gl_scan_qkv_workspace_size",
     "gl_scan_qkv_bwd",
     "gl_scan_bwd_static",
+    "gl_scan_qkv_fwd_workspace_size",
+    "gl_scan_qkv_fwd_ws",
 )
 
 GL_FLAG_GENERIC = 1
@@ -95,10 +97,13 @@ def lib():
         L.gl_scan_qkv_workspace_size.argtypes = [pd, ps]
         L.gl_scan_bwd_static.argtypes = [pd] + [P] * 12 + [P]
         L.gl_scan_qkv_bwd.argtypes = [pd] + [P] * 6 + [I] + [P] * 7 + [P, S, P]
+        L.gl_scan_qkv_fwd_workspace_size.argtypes = [pd, ps]
+        L.gl_scan_qkv_fwd_ws.argtypes = [pd] + [P] * 6 + [I, P, P, S, P]
         for f in ("gl_scan_saved_size", "gl_scan_workspace_size", "gl_scan_fwd", "gl_scan_bwd",
                   "gl_decode_readout", "gl_decode_update", "gl_decode_step",
                   "gl_scan_final_state", "gl_costate_quadratic", "gl_scan_qkv_fwd",
-                  "gl_scan_qkv_workspace_size", "gl_scan_qkv_bwd", "gl_scan_bwd_static"):
+                  "gl_scan_qkv_workspace_size", "gl_scan_qkv_bwd", "gl_scan_bwd_static",
+                  "gl_scan_qkv_fwd_workspace_size", "gl_scan_qkv_fwd_ws"):
             getattr(L, f).restype = ctypes.c_int
         L.gl_status_string.argtypes = [I]
         L.gl_status_string.restype = ctypes.c_char_p
@@ -407,9 +412,12 @@ def gl_scan_qkv_fwd(q, k, v, eta, alpha, W0, w0_transposed=False, flags=0):
     y = torch.empty((B, H, T, dv), dtype=q.dtype, device=q.device)
     _check_dec((q, k, v, W0, y), (eta,), alpha, q.dtype)
     desc = make_desc(B, H, T, dk, dv, _io_code(q.dtype), flags=flags)
-    _check(lib().gl_scan_qkv_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(eta),
-                                 _ptr(alpha), _ptr(W0), int(bool(w0_transposed)), _ptr(y),
-                                 _stream(q.device)))
+    n = ctypes.c_size_t()
+    _check(lib().gl_scan_qkv_fwd_workspace_size(ctypes.byref(desc), ctypes.byref(n)))
+    ws = torch.empty(n.value, dtype=torch.uint8, device=q.device) if n.value else None
+    _check(lib().gl_scan_qkv_fwd_ws(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(eta),
+                                    _ptr(alpha), _ptr(W0), int(bool(w0_transposed)), _ptr(y),
+                                    _ptr(ws), n.value, _stream(q.device)))
     return y
 
 

@@ -541,10 +541,54 @@ gl_status_t gl_costate_quadratic(const gl_scan_desc_t* desc, const void* y, cons
 gl_status_t gl_scan_qkv_fwd(const gl_scan_desc_t* desc, const void* q, const void* k,
                             const void* v, const void* eta, const void* alpha, const void* W0,
                             int w0_transposed, void* y, void* stream) {
+  return gl_scan_qkv_fwd_ws(desc, q, k, v, eta, alpha, W0, w0_transposed, y, nullptr, 0, stream);
+}
+
+namespace {
+bool qkv_two_pass(const gl_scan_desc_t* d) {
+  return !(d->flags & GL_FLAG_GENERIC) &&
+         gls::mfma_qkv_two_pass(d->io_dtype, static_cast<int>(d->d_in), static_cast<int>(d->d_out));
+}
+}  // namespace
+
+gl_status_t gl_scan_qkv_fwd_workspace_size(const gl_scan_desc_t* desc, size_t* ws_bytes) {
+  gl_status_t st = check_dec(desc, true);
+  if (st != GL_SUCCESS) return st;
+  if (!ws_bytes) return fail(GL_ERROR_INVALID_VALUE, "ws_bytes is NULL");
+  *ws_bytes = qkv_two_pass(desc) ? round_up(gls::mfma_qkv_states_bytes(desc->B * desc->H, desc->T)) : 0;
+  return GL_SUCCESS;
+}
+
+gl_status_t gl_scan_qkv_fwd_ws(const gl_scan_desc_t* desc, const void* q, const void* k,
+                               const void* v, const void* eta, const void* alpha, const void* W0,
+                               int w0_transposed, void* y, void* ws, size_t ws_bytes,
+                               void* stream) {
   gl_status_t st = check_dec(desc, true);
   if (st != GL_SUCCESS || desc->B * desc->H * desc->T == 0) return st;
   st = check_ptrs({q, k, v, eta, alpha, W0, y});
   if (st != GL_SUCCESS) return st;
+  if (qkv_two_pass(desc) && ws) {
+    const size_t need = round_up(gls::mfma_qkv_states_bytes(desc->B * desc->H, desc->T));
+    if (ws_bytes < need)
+      return fail(GL_ERROR_WORKSPACE_TOO_SMALL, "workspace %zu bytes, need %zu", ws_bytes, need);
+    for (const void* p : {q, k, v, eta, alpha, W0, static_cast<const void*>(y),
+                          static_cast<const void*>(ws)})
+      if (misaligned(p)) return fail(GL_ERROR_MISALIGNED, "pointer %p not 16-byte aligned", p);
+    gls::FwdArgs f;
+    f.x = k; f.g = v; f.q = q; f.eta = eta; f.alpha = alpha; f.W0 = W0; f.y = y;
+    f.states = ws;
+    f.B = desc->B; f.H = desc->H; f.T = desc->T;
+    f.d_in = 128; f.d_out = 128;
+    f.chunk = gls::kMfmaChunk;
+    f.n_chunks = static_cast<int>((desc->T + gls::kMfmaChunk - 1) / gls::kMfmaChunk);
+    f.ckpt_every = 1; f.n_ckpt = f.n_chunks;
+    f.seg_chunks = f.n_chunks; f.n_seg = 1;
+    f.w0_t = w0_transposed != 0;
+    if (desc->B * desc->H * static_cast<int64_t>(f.n_chunks) > 0x7fffffffLL)
+      return fail(GL_ERROR_NOT_SUPPORTED, "B*H*chunks above 2^31-1");
+    return hip_status(gls::launch_mfma_qkv_two_pass(f, static_cast<hipStream_t>(stream)),
+                      "qkv scan launch");
+  }
   if (desc->io_dtype == GL_DTYPE_BF16 && desc->d_in == 64 && desc->d_out == 64 &&
       !(desc->flags & GL_FLAG_GENERIC)) {
     // the forward matrix-core kernel with a read tile of its own: x is the

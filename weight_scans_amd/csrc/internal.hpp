@@ -185,6 +185,10 @@ hipError_t launch_mf_bwd(int io, const BwdArgs& a, hipStream_t s);
 constexpr int kMfmaChunk = 64;
 hipError_t launch_mfma_fwd(const FwdArgs& a, hipStream_t s);
 hipError_t launch_mfma_qkv_fwd(const FwdArgs& a, hipStream_t s);  // read tile of its own, d = 64
+// the write-key scan at d_k = d_v = 128 (bf16): states pass, then chunk outputs
+bool mfma_qkv_two_pass(int io, int dk, int dv);
+size_t mfma_qkv_states_bytes(int64_t BH, int64_t T);
+hipError_t launch_mfma_qkv_two_pass(const FwdArgs& a, hipStream_t s);
 hipError_t launch_mfma_bwd_lam(const BwdArgs& a, hipStream_t s);  // adjoint-only segment pass
 hipError_t launch_mfma_bwd_f64(const BwdArgs& a, hipStream_t s);   // fused reverse scan, d = 64
 hipError_t launch_mfma_bwd_f128(const BwdArgs& a, hipStream_t s);  // fused reverse scan, d = 128
