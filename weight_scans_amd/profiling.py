@@ -189,7 +189,8 @@ def main(argv):
             def moved(pred):
                 return sum(v["fetch_bytes"] + v["write_bytes"] for k, v in res["kernels"].items()
                            if pred(k))
-            fwd = moved(lambda k: k.startswith("fwd_") or k in ("seg_combine (fwd)", "mf_carry (fwd)"))
+            fwd = moved(lambda k: k.startswith(("fwd_", "qkv_")) or
+                        k in ("seg_combine (fwd)", "mf_carry (fwd)"))
             bwd = moved(lambda k: k.startswith("bwd_") or "finalize" in k or
                         k in ("seg_combine (bwd)", "mf_carry (bwd)"))
             db[cfg] = {"kernel_hash": kernel_source_hash(), "fwd_bytes": fwd, "bwd_bytes": bwd,
