@@ -463,6 +463,111 @@ def costate_main(args, w):
 PEAK_VALU = {"bf16": 78.6e12, "f32": 78.6e12, "f64": 78.6e12}
 
 
+def qkv_bwd_main(args, w):
+    """The reverse scan of the transpose read: gl_scan_qkv_bwd with q = u,
+    k = g, v = x, W0 read transposed, upstream dz seeded N(0, 1)."""
+    import numpy as np
+    import torch
+
+    import oracle
+    import weight_scans_amd as ws
+    from weight_scans_amd.synth import make_inputs
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    tio = {"f64": torch.float64, "f32": torch.float32, "bf16": torch.bfloat16}[w.dtype]
+    gd = ws.gate_dtype(tio)
+    inp = make_inputs(w)
+    dz_h = np.random.default_rng(w.seed + 77).standard_normal(inp["x"].shape)
+    t = {k: torch.from_numpy(inp[k]).to(dev, tio) for k in ("x", "g", "W0", "dy")}
+    t.update({k: torch.from_numpy(inp[k]).to(dev, gd) for k in ("eta", "alpha")})
+    t["dz"] = torch.from_numpy(dz_h).to(dev, tio)
+    dq, dk, dv = torch.empty_like(t["dy"]), torch.empty_like(t["g"]), torch.empty_like(t["x"])
+    deta, dalpha = torch.empty_like(t["eta"]), torch.empty_like(t["alpha"])
+    dW0 = torch.empty((w.H, w.d_out, w.d_in), dtype=gd, device=dev)
+    io = {"f64": 0, "f32": 1, "bf16": 2}[w.dtype]
+    desc = ws.make_desc(w.B, w.H, w.T, w.d_out, w.d_in, io)
+    n = ctypes.c_size_t()
+    ws._check(ws.lib().gl_scan_qkv_workspace_size(ctypes.byref(desc), ctypes.byref(n)))
+    wsb = torch.empty(max(n.value, 16), dtype=torch.uint8, device=dev)
+    flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    L = ws.lib()
+    stream = torch.cuda.current_stream(dev)
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    P = lambda a: ctypes.c_void_p(a.data_ptr())  # noqa: E731
+
+    def step():
+        ws._check(L.gl_scan_qkv_bwd(ctypes.byref(desc), P(t["dy"]), P(t["g"]), P(t["x"]),
+                                    P(t["eta"]), P(t["alpha"]), P(t["W0"]), 1, P(t["dz"]),
+                                    P(dq), P(dk), P(dv), P(deta), P(dalpha), P(dW0), P(wsb),
+                                    n.value, sp))
+
+    for _ in range(args.warmup):
+        if not args.no_flush:
+            flush_sink = torch.sum(flush)  # noqa: F841
+        step()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        if not args.no_flush:
+            flush_sink = torch.sum(flush)  # noqa: F841
+        ev[i][0].record(stream)
+        step()
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    ts = [a.elapsed_time(b) for a, b in ev]
+    ms = sum(ts) / len(ts)
+    # the scan's reverse-pass model with dk = d_out, dv = d_in: flops of the
+    # chunked method (16 dk dv + 8 64 (dk + dv) / 2 per token-head); on the
+    # vector-ALU kernels the binding peak is the fp32 (fp64) vector rate
+    e = {"bf16": 2, "f32": 4, "f64": 8}[w.dtype]
+    eg = 8 if w.dtype == "f64" else 4
+    nt = w.B * w.H * w.T
+    nflops = nt * (16 * w.d_in * w.d_out + 8 * 64 * (w.d_in + w.d_out) // 2)
+    nbytes = nt * (e * (4 * w.d_out + 2 * w.d_in) + 4 * eg) + w.H * w.d_in * w.d_out * (e + eg)
+    peak = PEAK_VALU[w.dtype] / 1e12
+    achieved = nflops / 1e12 / (ms / 1e3)
+    rec = {
+        "metric": "tokens/s (reverse scan of the transpose read)",
+        "value": w.B * w.T / (ms / 1e3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {"bf16": "bf16 io / fp32 state", "f32": "f32", "f64": "f64"}[w.dtype],
+        "data": "synthetic (seeded; distributions of the named workload; u ~ the dy draw)",
+        "config": {"workload": f"{w.name}: [B,H,T,d]=[{w.B},{w.H},{w.T},{w.d_in}] "
+                               f"{w.dtype}, gradients of z_t = (W0 + D_t)^T u_t",
+                   "B": w.B, "H": w.H, "T": w.T, "d_in": w.d_in, "d_out": w.d_out,
+                   "io": w.dtype, "parallelism": "single GPU"},
+        "roofline": {"bound": "alu", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+                     "frac": achieved / peak, "traffic": None, "algorithmic_flops": nflops,
+                     "algorithmic_bytes": nbytes,
+                     "kernel": "fwd_generic (states) + bwd_generic + finalize_kernel (vector ALU)"},
+        "passes_ms": {"mean": ms, "median": statistics.median(ts), "min": min(ts), "max": max(ts)},
+    }
+    if not args.no_cpu:
+        W0T = np.ascontiguousarray(np.transpose(inp["W0"], (0, 2, 1)))
+        k_, t0 = 0, time.perf_counter()
+        while time.perf_counter() - t0 < 10.0 and k_ < w.B * w.H:
+            b, h = divmod(k_, w.H)
+            sl = lambda a: a[b:b + 1, h:h + 1]  # noqa: E731
+            oracle.qkv_bwd(sl(inp["dy"]), sl(inp["g"]), sl(inp["x"]), sl(inp["eta"]),
+                           sl(inp["alpha"]), W0T[h:h + 1], sl(dz_h))
+            k_ += 1
+        wall = time.perf_counter() - t0
+        rec["cpu_baseline"] = {"value": k_ * w.T / w.H / wall, "unit": "tokens/s", "cores": 1,
+                               "kind": "oracle",
+                               "sample": f"{k_} of {w.B * w.H} sequence-heads (T={w.T}), "
+                                         f"fp64 numpy token loop, {wall:.1f} s wall; "
+                                         f"tokens counted as sequence-heads*T/H"}
+    print(json.dumps(rec), flush=True)
+
+
 def qkv_main(args, w):
     import numpy as np
     import torch
@@ -595,6 +700,8 @@ def main():
     ap.add_argument("--generic", action="store_true", help="force the portable VALU kernels")
     ap.add_argument("--qkv", action="store_true",
                     help="time the transpose read (scan with its own read vector and key)")
+    ap.add_argument("--qkv-bwd", action="store_true",
+                    help="time the reverse scan of the transpose read (gl_scan_qkv_bwd)")
     ap.add_argument("--costate", action="store_true",
                     help="time Picard sweeps (forward scan + costate reconstruction)")
     ap.add_argument("--decode", action="store_true",
@@ -620,6 +727,8 @@ def main():
         return costate_main(args, w)
     if args.qkv:
         return qkv_main(args, w)
+    if args.qkv_bwd:
+        return qkv_bwd_main(args, w)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     tio = {"f64": torch.float64, "f32": torch.float32, "bf16": torch.bfloat16}[w.dtype]
