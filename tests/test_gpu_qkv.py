@@ -221,6 +221,41 @@ def test_qkv_bwd_parity(io, B, H, T, dk, dv, w0t):
     assert not bad, errs
 
 
+@pytest.mark.parametrize("B,H,T,w0t", [
+    (1, 2, 200, False),      # three full chunks and a ragged one
+    (2, 1, 129, True),       # one token past two chunks; W0 given transposed
+    (1, 1, 64, False),       # exactly one chunk
+    (1, 3, 1, True),
+    (3, 2, 320, True),       # five full chunks
+])
+def test_qkv_bwd_bf16_on_the_matrix_cores(B, H, T, w0t):
+    # bf16 with dk = dv = 64 takes the chunk-parallel matrix-core reverse scan;
+    # against the oracle, and against the vector kernels (GL_FLAG_GENERIC)
+    say(f"qkv backward matrix cores B={B} H={H} T={T} w0t={w0t}")
+    w = Workload("qkvb", B, H, T, 64, 64, "bf16", "mix", "gauss", 2100 + T)
+    inp = make_inputs(w)
+    rng = np.random.default_rng(2150 + T)
+    q = round_to(rng.standard_normal(inp["x"].shape) / 8.0, "bf16")
+    W0p = inp["W0"]
+    W0g = np.ascontiguousarray(W0p.transpose(0, 2, 1)) if w0t else W0p
+    dev = to_device(inp, "bf16")
+    qd = torch.from_numpy(q).to("cuda", torch.bfloat16)
+    W0d = torch.from_numpy(W0g).to("cuda", torch.bfloat16)
+    args = (qd, dev["x"], dev["g"], dev["eta"], dev["alpha"], W0d, dev["dy"])
+    got = ws.gl_scan_qkv_bwd(*args, w0_transposed=w0t)
+    gen = ws.gl_scan_qkv_bwd(*args, w0_transposed=w0t, flags=ws.GL_FLAG_GENERIC)
+    torch.cuda.synchronize()
+    want = list(oracle.qkv_bwd(q, inp["x"], inp["g"], inp["eta"], inp["alpha"], W0p, inp["dy"]))
+    if w0t:
+        want[5] = want[5].transpose(0, 2, 1)
+    names = ("dq", "dk", "dv", "deta", "dalpha", "dW0")
+    errs = {n: relmax(host(gv), wv) for n, gv, wv in zip(names, got, want)}
+    errg = {n: relmax(host(gv), host(hv)) for n, gv, hv in zip(names, got, gen)}
+    say(f"  vs oracle {errs}\n  vs vector kernels {errg}")
+    assert all(e <= TOL["bf16"] for e in errs.values()), errs
+    assert all(e <= TOL["bf16"] for e in errg.values()), errg
+
+
 def test_qkv_bwd_transpose_read_full_size_sampled():
     # the transpose read's reverse scan at the 340M-model shape, every head on
     # the GPU, two heads and one head's dW0 against the oracle

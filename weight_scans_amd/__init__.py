@@ -421,9 +421,10 @@ def gl_scan_qkv_fwd(q, k, v, eta, alpha, W0, w0_transposed=False, flags=0):
     return y
 
 
-def gl_scan_qkv_bwd(q, k, v, eta, alpha, W0, dy, w0_transposed=False):
+def gl_scan_qkv_bwd(q, k, v, eta, alpha, W0, dy, w0_transposed=False, flags=0):
     """Reverse scan of gl_scan_qkv_fwd for upstream dy [B,H,T,dv].  Returns
-    (dq, dk, dv, deta, dalpha, dW0) with dW0 in the layout W0 is given in."""
+    (dq, dk, dv, deta, dalpha, dW0) with dW0 in the layout W0 is given in.
+    flags: GL_FLAG_GENERIC keeps bf16 d = 64 off the matrix cores."""
     torch = _torch()
     if q.dim() != 4 or k.shape != q.shape or v.dim() != 4 or v.shape[:3] != q.shape[:3]:
         raise ValueError("q, k must be [B,H,T,dk] and v [B,H,T,dv]")
@@ -438,7 +439,7 @@ def gl_scan_qkv_bwd(q, k, v, eta, alpha, W0, dy, w0_transposed=False):
     deta, dalpha = torch.empty_like(eta), torch.empty_like(alpha)
     dW0 = torch.empty(want, dtype=gd, device=q.device)
     _check_dec((q, k, v, W0, dy, dq, dk_, dv_), (eta, deta, dalpha), alpha, q.dtype)
-    desc = make_desc(B, H, T, dk, dvv, _io_code(q.dtype))
+    desc = make_desc(B, H, T, dk, dvv, _io_code(q.dtype), flags=flags)
     n = ctypes.c_size_t()
     _check(lib().gl_scan_qkv_workspace_size(ctypes.byref(desc), ctypes.byref(n)))
     ws = torch.empty(max(n.value, 16), dtype=torch.uint8, device=q.device)

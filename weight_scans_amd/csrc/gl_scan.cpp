@@ -626,6 +626,11 @@ namespace {
 struct QkvPlan {
   int chunk = 0, n_chunks = 0, n_tiles = 0;
   size_t comp = 8, states = 0, part = 0, dw = 0, total = 0;
+  // bf16, dk = dv = 64 on the matrix cores: bf16 chunk-start states, the fp32
+  // adjoint leaving every chunk (lam), per-chunk decays (gam) and a dW0'
+  // share per chunk (dw); part is unused
+  bool mfma = false;
+  size_t lam = 0, gam = 0;
 };
 gl_status_t qkv_plan(const gl_scan_desc_t* d, QkvPlan* p) {
   gl_status_t st = check_dec(d, true);
@@ -633,6 +638,21 @@ gl_status_t qkv_plan(const gl_scan_desc_t* d, QkvPlan* p) {
   const size_t dd = static_cast<size_t>(d->d_in) * static_cast<size_t>(d->d_out);
   const size_t BH = static_cast<size_t>(d->B) * static_cast<size_t>(d->H);
   p->comp = d->io_dtype == GL_DTYPE_F64 ? 8 : 4;
+  if (!(d->flags & GL_FLAG_GENERIC) &&
+      gls::mfma_qkv_bwd_ok(d->io_dtype, static_cast<int>(d->d_in), static_cast<int>(d->d_out))) {
+    p->mfma = true;
+    p->chunk = gls::kMfmaChunk;
+    p->n_chunks = static_cast<int>((d->T + p->chunk - 1) / p->chunk);
+    if (static_cast<int64_t>(BH) * p->n_chunks > 0x7fffffffLL)
+      return fail(GL_ERROR_NOT_SUPPORTED, "B*H*chunks above 2^31-1");
+    const size_t cells = BH * static_cast<size_t>(p->n_chunks);
+    p->states = round_up(cells * dd * 2);
+    p->lam = round_up(cells * dd * sizeof(float));
+    p->gam = round_up(cells * sizeof(float));
+    p->dw = round_up(cells * dd * sizeof(float));
+    p->total = p->states + p->lam + p->gam + p->dw;
+    return GL_SUCCESS;
+  }
   p->chunk = d->io_dtype == GL_DTYPE_F64 ? 8 : 32;  // LDS of the generic kernels with a read tile
   p->n_chunks = static_cast<int>((d->T + p->chunk - 1) / p->chunk);
   p->n_tiles = static_cast<int>((std::max(d->d_in, d->d_out) + gls::kGenericTile - 1) /
@@ -676,6 +696,32 @@ gl_status_t gl_scan_qkv_bwd(const gl_scan_desc_t* desc, const void* q, const voi
     return fail(GL_ERROR_WORKSPACE_TOO_SMALL, "workspace %zu bytes, need %zu", ws_bytes, p.total);
   char* w = static_cast<char*>(ws);
   void* states = w;
+  if (p.mfma) {
+    gls::BwdArgs b;
+    b.x = k; b.q = q; b.g = v; b.eta = eta; b.alpha = alpha; b.W0 = W0; b.dy = dy;
+    b.states = states;
+    b.dx = dk; b.dq = dq; b.dg = dv;
+    b.mf_lam = w + p.states;
+    b.mf_gam = w + p.states + p.lam;
+    b.part_dW0 = w + p.states + p.lam + p.gam;
+    b.deta_out = deta; b.dalpha_out = dalpha;
+    b.B = desc->B; b.H = desc->H; b.T = desc->T;
+    b.d_in = 64; b.d_out = 64;
+    b.chunk = p.chunk; b.n_chunks = p.n_chunks; b.ckpt_every = 1; b.n_ckpt = p.n_chunks;
+    b.n_tiles = 1;
+    b.seg_chunks = p.n_chunks; b.n_seg = 1;
+    b.w0_t = w0_transposed != 0;
+    st = hip_status(gls::launch_mfma_qkv_bwd(b, s), "qkv backward launch");
+    if (st != GL_SUCCESS) return st;
+    gls::FinArgs fa;
+    fa.part_eta = nullptr; fa.part_alpha = nullptr; fa.part_dW0 = b.part_dW0;
+    fa.deta = deta; fa.dalpha = dalpha; fa.dW0 = dW0;
+    fa.B = desc->B; fa.H = desc->H; fa.T = desc->T;
+    fa.d_in = 64; fa.d_out = 64; fa.n_tiles = 1; fa.n_seg = p.n_chunks;
+    fa.alpha_done = true;
+    fa.eta_done = true;
+    return hip_status(gls::launch_finalize(desc->io_dtype, fa, s), "qkv finalize launch");
+  }
   void* part_eta = w + p.states;
   void* part_alpha = w + p.states + p.part;
   void* part_dW0 = w + p.states + 2 * p.part;

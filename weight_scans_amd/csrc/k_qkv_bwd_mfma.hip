@@ -1,0 +1,343 @@
+// k_qkv_bwd_mfma.hip -- the reverse scan of the scan with a read vector and a
+// write key of their own on the matrix cores, bf16 io, d_k = d_v = 64
+// (gfx950, v_mfma_f32_16x16x32_bf16).
+//
+//   y_t = (W0' + D_t) q_t,   D_{t+1} = alpha_t D_t - eta_t v_t k_t^T
+// and its exact adjoint for L = sum_t <dy_t, y_t> (the recurrence is affine
+// in D, so its adjoint is the same recurrence run backwards: "Parallelize
+// the Training, Keep the Learning Serial", cognaptus.com, section "Once the
+// gradient signals are known, the weight trajectory becomes
+// parallelizable"), with A_{t+1} = dL/dD_{t+1}:
+//   dq_t = (W0' + D_t)^T dy_t,  dk_t = -eta_t A_{t+1}^T v_t,  dv_t = -eta_t A_{t+1} k_t,
+//   deta_t = -v_t^T A_{t+1} k_t,  dalpha_t = <A_{t+1}, D_t>,  dW0' = sum dy_t q_t^T.
+// Per chunk of 64 tokens (l = chunk-local inclusive cumsum of log2 alpha,
+// lq_t = l_{t-1}, e(.) = 2^(.), D_in / A_out the carries at the chunk's ends):
+//   D_t     = e(lq_t) D_in + sum_{j<t} e(lq_t - l_j)(-eta_j) v_j k_j^T
+//   A_{t+1} = e(l_last - l_t) A_out + sum_{u>t} e(lq_u - l_t) dy_u q_u^T
+// so that, with P_ut = e(lq_u - l_t)(q_u . k_t) and
+// Be_tj = e(lq_t - l_j)(-eta_j)(dy_t . v_j) (zero unless the first index is the later token):
+//   dq = W0'^T dy + e(lq) D_in^T dy + Be K
+//   u  = e(l_last - l) A_out k + P^T dy,   dv = -eta u,   deta = -v . u
+//   dk = Be^T Q - eta e(l_last - l) A_out^T v
+// and dalpha from <A_out, D_in>, pp_j = v_j . (A_out k_j), rr_u = q_u . (D_in^T dy_u)
+// and the row / column sums of Be o (Q K^T) (the same identity as the scan's).
+//
+// Five launches: the forward kernel's state-only instance (x = k, g = v)
+// writes D_in of every chunk (bf16); qkv_bwd_inc forms every chunk's adjoint
+// increment V = sum_u e(lq_u) dy_u q_u^T and its dW0' share; the carry scan
+// over chunks turns the increments into A_out of every chunk; qkv_bwd_chunk
+// forms every chunk's gradients from its tiles and the two carries; the
+// finalize kernel sums the dW0' shares in a fixed order.
+#include <algorithm>
+#include <cstdint>
+
+#include "bwd_fused.hpp"
+
+namespace gls {
+namespace {
+
+constexpr int kD = 64;    // d_k = d_v
+constexpr int kCk = 64;   // tokens per chunk
+constexpr int kNI = 256;  // threads of the increment kernel (four waves)
+constexpr int kNG = 512;  // threads of the gradient kernel (eight waves)
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// 16-byte unit u (8 per row) of a [rows][64] bf16 tile: its swizzled LDS offset in bytes.
+__device__ __forceinline__ uint32_t unit64(int u) {
+  return static_cast<uint32_t>(sidx<kD>(u >> 3, 8 * (u & 7)) * 2);
+}
+
+// ---- adjoint increments and dW0' shares of every chunk ----
+struct alignas(16) IncLds {
+  __bf16 Q[kCk * kD], DY[kCk * kD];  // swizzled [token][64]
+  float eq[kCk];
+  float gam;
+};
+
+__global__ __launch_bounds__(kNI) void qkv_bwd_inc(BwdArgs a) {
+  __shared__ IncLds L;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g4 = lane >> 4, l16 = lane & 15;
+  const int n = a.n_chunks;
+  const int64_t bh = blockIdx.x / n, BH = a.B * a.H;
+  const int c = static_cast<int>(blockIdx.x % n);
+  const int64_t T = a.T, t0 = static_cast<int64_t>(c) * kCk;
+  const int cv = static_cast<int>(std::min<int64_t>(kCk, T - t0));
+  const __amdgpu_buffer_rsrc_t rq =
+      buffer_rsrc(static_cast<const uint16_t*>(a.q) + (bh * T + t0) * kD, cv * kD * 2);
+  const __amdgpu_buffer_rsrc_t rd =
+      buffer_rsrc(static_cast<const uint16_t*>(a.dy) + (bh * T + t0) * kD, cv * kD * 2);
+  u32x4 uq[2], ud[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const uint32_t off = static_cast<uint32_t>((tid + kNI * j) * 16);
+    uq[j] = __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0);
+    ud[j] = __builtin_amdgcn_raw_buffer_load_b128(rd, off, 0, 0);
+  }
+  float al = 1.f;
+  if (wave == 0 && lane < cv) al = static_cast<const float*>(a.alpha)[bh * T + t0 + lane];
+  if (wave == 0) {
+    const ChunkGates gt = chunk_gates(al, lane);
+    L.eq[lane] = fexp2(gt.lq);
+    if (lane == 0) L.gam = fexp2(gt.llast);
+  }
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const uint32_t lo = unit64(tid + kNI * j);
+    *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(L.Q) + lo) = uq[j];
+    *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(L.DY) + lo) = ud[j];
+  }
+  __syncthreads();
+
+  // V^T-free form: block (r block w, k block cb) of dy^T q over the chunk's
+  // tokens, with and without the factor e(lq_u) (on the q fragments)
+  const LaneOff<kD> o = lane_off<kD>(lane);
+  const int rb = wave;
+  f32x4 v[4], w[4];
+#pragma unroll
+  for (int cb = 0; cb < 4; ++cb) v[cb] = w[cb] = zero4();
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    const bf16x8 df = frag_ts<kD>(L.DY, o, kb * 32, rb * 16);
+    const f32x4 e0 = *reinterpret_cast<const f32x4*>(&L.eq[kb * 32 + 8 * g4]);
+    const f32x4 e1 = *reinterpret_cast<const f32x4*>(&L.eq[kb * 32 + 8 * g4 + 4]);
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) {
+      const bf16x8 qf = frag_ts<kD>(L.Q, o, kb * 32, cb * 16);
+      w[cb] = mfma16x16x32(df, qf, w[cb]);
+      v[cb] = mfma16x16x32(df, scale8(qf, e0, e1), v[cb]);
+    }
+  }
+  const int64_t dd = static_cast<int64_t>(kD) * kD;
+  float* pw = static_cast<float*>(a.part_dW0) + (static_cast<int64_t>(c) * BH + bh) * dd;
+  float* pv = c > 0 ? static_cast<float*>(a.mf_lam) + (bh * n + c - 1) * dd : nullptr;
+#pragma unroll
+  for (int cb = 0; cb < 4; ++cb) {
+    const int k = cb * 16 + l16;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int r = rb * 16 + 4 * g4 + q;
+      pw[a.w0_t ? k * kD + r : r * kD + k] = w[cb][q];
+      if (pv) pv[r * kD + k] = v[cb][q];
+    }
+  }
+  if (tid == 0) static_cast<float*>(a.mf_gam)[bh * n + c] = L.gam;
+}
+
+// ---- the gradients of every chunk ----
+struct alignas(16) GradLds {
+  __bf16 Q[kCk * kD], K[kCk * kD], V[kCk * kD], DY[kCk * kD];  // swizzled [token][64]
+  __bf16 S[kD * kD], A[kD * kD], W[kD * kD];  // D_in [r][k], A_out [r][k], W0' as stored
+  __bf16 PT[kCk * kCk], BT[kCk * kCk];        // PT[t][u] = P_ut, BT[j][t] = Be_tj
+  RecF rc;
+  QkF qk;
+  float pp[2][kCk], rr[2][kCk], de[2][kCk];   // shares over two column halves
+  float c0[8];
+};
+
+__global__ __launch_bounds__(kNG) void qkv_bwd_chunk(BwdArgs a) {
+  __shared__ GradLds L;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g4 = lane >> 4, l16 = lane & 15;
+  const int n = a.n_chunks;
+  const int64_t bh = blockIdx.x / n;
+  const int c = static_cast<int>(blockIdx.x % n);
+  const int h = static_cast<int>(bh % a.H);
+  const int64_t T = a.T, t0 = static_cast<int64_t>(c) * kCk;
+  const int cv = static_cast<int>(std::min<int64_t>(kCk, T - t0));
+  const int64_t dd = static_cast<int64_t>(kD) * kD;
+  const int64_t tok = (bh * T + t0) * kD;
+
+  // ---- loads: one 16-byte unit per thread of q, k, v, dy, D_in and W0',
+  // and the matching 8 floats of A_out
+  const auto tile_rsrc = [&](const void* base) {
+    return buffer_rsrc(static_cast<const uint16_t*>(base) + tok, cv * kD * 2);
+  };
+  const uint32_t off = static_cast<uint32_t>(tid * 16);
+  const u32x4 uq = __builtin_amdgcn_raw_buffer_load_b128(tile_rsrc(a.q), off, 0, 0);
+  const u32x4 uk = __builtin_amdgcn_raw_buffer_load_b128(tile_rsrc(a.x), off, 0, 0);
+  const u32x4 uv = __builtin_amdgcn_raw_buffer_load_b128(tile_rsrc(a.g), off, 0, 0);
+  const u32x4 ud = __builtin_amdgcn_raw_buffer_load_b128(tile_rsrc(a.dy), off, 0, 0);
+  const u32x4 us = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.states) +
+                                                   (bh * n + c) * dd + 8 * tid);
+  const u32x4 uw = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.W0) + h * dd +
+                                                   8 * tid);
+  const float* ap = static_cast<const float*>(a.mf_lam) + (bh * n + c) * dd + 8 * tid;
+  const f32x4 a0 = *reinterpret_cast<const f32x4*>(ap);
+  const f32x4 a1 = *reinterpret_cast<const f32x4*>(ap + 4);
+  if (wave == 0) {
+    const float* et = static_cast<const float*>(a.eta) + bh * T + t0;
+    const float* al = static_cast<const float*>(a.alpha) + bh * T + t0;
+    gates_f(et, al, L.rc, cv, lane);
+  }
+  // P^T and Be^T start at zero (only the causal parts are written)
+  reinterpret_cast<u32x4*>(L.PT)[tid] = u32x4{0u, 0u, 0u, 0u};
+  reinterpret_cast<u32x4*>(L.BT)[tid] = u32x4{0u, 0u, 0u, 0u};
+  {
+    const uint32_t lo = unit64(tid);
+    *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(L.Q) + lo) = uq;
+    *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(L.K) + lo) = uk;
+    *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(L.V) + lo) = uv;
+    *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(L.DY) + lo) = ud;
+    *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(L.S) + lo) = us;
+    *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(L.W) + lo) = uw;
+    uint2 p0 = pack4f(a0), p1 = pack4f(a1);
+    *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(L.A) + lo) = u32x4{p0.x, p0.y, p1.x, p1.y};
+    // <A_out, D_in> over this thread's 8 elements (A_out in fp32)
+    const f32x4 s0 = unpack4f(uint2{us[0], us[1]}), s1 = unpack4f(uint2{us[2], us[3]});
+    const float cp = wave_sum(dot4f(a0, s0) + dot4f(a1, s1));
+    if (lane == 0) L.c0[wave] = cp;
+  }
+  __syncthreads();
+
+  const LaneOff<kD> o = lane_off<kD>(lane);
+  const LaneOff<kCk> o64 = lane_off<kCk>(lane);
+  // ---- causal blocks w and w + 8 of the ten: Q K^T and DY V^T, decayed;
+  // P and Be written transposed, the row / column sums of Be o (Q K^T)
+  for (int b = wave; b < 10; b += 8) {
+    const int ib = tri_i(b), jb = tri_j(b);
+    f32x4 qk = zero4(), dv = zero4();
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      qk = mfma16x16x32(frag_s<kD>(L.Q, o, ib * 16, kb * 32), frag_s<kD>(L.K, o, jb * 16, kb * 32), qk);
+      dv = mfma16x16x32(frag_s<kD>(L.DY, o, ib * 16, kb * 32), frag_s<kD>(L.V, o, jb * 16, kb * 32),
+                        dv);
+    }
+    const int col = jb * 16 + l16, r0 = ib * 16 + 4 * g4;
+    const float lc = L.rc.li[col], nbc = L.rc.nb[col];
+    f32x4 p, be, z;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const bool on = col < r0 + q;
+      const float e = on ? fexp2(L.rc.lq[r0 + q] - lc) : 0.f;
+      p[q] = qk[q] * e;
+      be[q] = dv[q] * (e * nbc);
+      z[q] = be[q] * qk[q];
+    }
+    put4<kCk>(L.PT, o64, jb * 16, ib * 16, pack4f(p));
+    put4<kCk>(L.BT, o64, jb * 16, ib * 16, pack4f(be));
+    f32x4 zr;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) zr[q] = row16_sum(z[q]);
+    if (l16 == 15) *reinterpret_cast<f32x4*>(&L.qk.qq[b][4 * g4]) = zr;
+    const float t = sum_rows(z[0] + z[1] + z[2] + z[3]);
+    if (g4 == 0) L.qk.kk[b][l16] = t;
+  }
+  __syncthreads();
+
+  // ---- outputs, transposed (rows = columns of dq, dk, dv; columns =
+  // tokens): token block tb = w % 4, column blocks cb = 2 (w / 4) + {0, 1}
+  const int tb = wave & 3, hf = wave >> 2;
+  const int ti = tb * 16 + l16;  // this lane's token
+  const float eqi = L.rc.eq[ti], e2i = L.rc.e2[ti], nbi = L.rc.nb[ti];
+  const __amdgpu_buffer_rsrc_t rdq = buffer_rsrc(static_cast<uint16_t*>(a.dq) + tok, cv * kD * 2);
+  const __amdgpu_buffer_rsrc_t rdk = buffer_rsrc(static_cast<uint16_t*>(a.dx) + tok, cv * kD * 2);
+  const __amdgpu_buffer_rsrc_t rdv = buffer_rsrc(static_cast<uint16_t*>(a.dg) + tok, cv * kD * 2);
+  float rr = 0.f, pp = 0.f, de = 0.f;
+#pragma unroll
+  for (int h2 = 0; h2 < 2; ++h2) {
+    const int cb = 2 * hf + h2;
+    const uint32_t so = static_cast<uint32_t>((ti * kD + cb * 16 + 4 * g4) * 2);
+    // dq^T: W0'^T dy + e(lq) D_in^T dy + (Be K)^T
+    f32x4 aq = zero4(), sq = zero4();
+#pragma unroll
+    for (int kr = 0; kr < 2; ++kr) {
+      const bf16x8 dyf = frag_s<kD>(L.DY, o, tb * 16, kr * 32);
+      const bf16x8 wf = a.w0_t ? frag_s<kD>(L.W, o, cb * 16, kr * 32)
+                               : frag_ts<kD>(L.W, o, kr * 32, cb * 16);
+      aq = mfma16x16x32(wf, dyf, aq);
+      sq = mfma16x16x32(frag_ts<kD>(L.S, o, kr * 32, cb * 16), dyf, sq);
+    }
+#pragma unroll
+    for (int kj = 0; kj < 2; ++kj)
+      aq = mfma16x16x32(frag_ts<kD>(L.K, o, kj * 32, cb * 16), frag_ts<kCk>(L.BT, o64, kj * 32, tb * 16),
+                        aq);
+    const f32x4 qv = unpack4f(get4<kD>(L.Q, o, tb * 16, cb * 16));  // q_t[k], k = cb 16 + 4 g4 ..
+    rr += dot4f(qv, sq);
+    store8(rdq, so, pack4f(aq + eqi * sq));
+    // dk^T: (Be^T Q)^T - eta e(l_last - l) (A_out^T v)^T
+    f32x4 ak = zero4(), sk = zero4();
+#pragma unroll
+    for (int ku = 0; ku < 2; ++ku)
+      ak = mfma16x16x32(frag_ts<kD>(L.Q, o, ku * 32, cb * 16), frag_s<kCk>(L.BT, o64, tb * 16, ku * 32),
+                        ak);
+#pragma unroll
+    for (int kr = 0; kr < 2; ++kr)
+      sk = mfma16x16x32(frag_ts<kD>(L.A, o, kr * 32, cb * 16), frag_s<kD>(L.V, o, tb * 16, kr * 32), sk);
+    store8(rdk, so, pack4f(ak + (nbi * e2i) * sk));
+    // u^T: e(l_last - l) (A_out k)^T + (P^T dy)^T;  dv = -eta u
+    f32x4 au = zero4(), su = zero4();
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+      su = mfma16x16x32(frag_s<kD>(L.A, o, cb * 16, kk * 32), frag_s<kD>(L.K, o, tb * 16, kk * 32), su);
+#pragma unroll
+    for (int ku = 0; ku < 2; ++ku)
+      au = mfma16x16x32(frag_ts<kD>(L.DY, o, ku * 32, cb * 16), frag_s<kCk>(L.PT, o64, tb * 16, ku * 32),
+                        au);
+    const f32x4 u = au + e2i * su;
+    const f32x4 vv = unpack4f(get4<kD>(L.V, o, tb * 16, cb * 16));  // v_t[r], r = cb 16 + 4 g4 ..
+    de -= dot4f(vv, u);
+    pp += dot4f(vv, su);
+    store8(rdv, so, pack4f(nbi * u));
+  }
+  // shares over this wave's 32 columns: sum over the four lane groups
+  rr = sum_rows(rr);
+  pp = sum_rows(pp);
+  de = sum_rows(de);
+  if (g4 == 0) {
+    L.rr[hf][ti] = rr;
+    L.pp[hf][ti] = pp;
+    L.de[hf][ti] = de;
+  }
+  __syncthreads();
+
+  // ---- dalpha and deta of the chunk (wave 0, lane = token)
+  if (wave == 0) {
+    const int ir = kCk - 1 - lane;
+    float c0 = 0.f;
+#pragma unroll
+    for (int w = 0; w < 8; ++w) c0 += L.c0[w];
+    const float ppl = L.pp[0][lane] + L.pp[1][lane];
+    const float rr_r = L.rr[0][ir] + L.rr[1][ir];
+    const float del = L.de[0][lane] + L.de[1][lane];
+    const float da = dalpha_f(L.rc, L.qk, ppl, rr_r, c0, lane);
+    store4(buffer_rsrc(static_cast<float*>(a.dalpha_out) + bh * T + t0, cv * 4),
+           static_cast<uint32_t>(lane * 4), da);
+    store4(buffer_rsrc(static_cast<float*>(a.deta_out) + bh * T + t0, cv * 4),
+           static_cast<uint32_t>(lane * 4), del);
+  }
+}
+
+}  // namespace
+
+bool mfma_qkv_bwd_ok(int io, int dk, int dv) { return io == IO_BF16 && dk == kD && dv == kD; }
+
+// a: x = k (write key), g = v, q the read vector; dx <- dk, dg <- dv, dq;
+// states, mf_lam, mf_gam, part_dW0 in the workspace; deta_out / dalpha_out.
+hipError_t launch_mfma_qkv_bwd(const BwdArgs& a, hipStream_t s) {
+  const int64_t BH = a.B * a.H;
+  const int n = a.n_chunks;
+  if (BH * n == 0) return hipSuccess;
+  FwdArgs f;  // chunk-start states of the write-key scan (x = k, g = v)
+  f.x = a.x; f.g = a.g; f.eta = a.eta; f.alpha = a.alpha; f.W0 = a.W0;
+  f.y = nullptr; f.states = const_cast<void*>(a.states);
+  f.B = a.B; f.H = a.H; f.T = a.T;
+  f.d_in = kD; f.d_out = kD;
+  f.chunk = kCk; f.n_chunks = n; f.ckpt_every = 1; f.n_ckpt = n;
+  f.seg_chunks = n; f.n_seg = 1;
+  hipError_t e = launch_mfma_fwd(f, s);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(qkv_bwd_inc, dim3(static_cast<unsigned>(BH * n)), dim3(kNI), 0, s, a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  e = launch_mf_carry_f32(static_cast<float*>(a.mf_lam), static_cast<const float*>(a.mf_gam), BH, n,
+                          kD * kD, true, s);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(qkv_bwd_chunk, dim3(static_cast<unsigned>(BH * n)), dim3(kNG), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace gls
