@@ -486,11 +486,19 @@ def qkv_bwd_main(args, w):
     deta, dalpha = torch.empty_like(t["eta"]), torch.empty_like(t["alpha"])
     dW0 = torch.empty((w.H, w.d_out, w.d_in), dtype=gd, device=dev)
     io = {"f64": 0, "f32": 1, "bf16": 2}[w.dtype]
-    desc = ws.make_desc(w.B, w.H, w.T, w.d_out, w.d_in, io)
+    flags = ws.GL_FLAG_GENERIC if args.generic else 0
+    desc = ws.make_desc(w.B, w.H, w.T, w.d_out, w.d_in, io, flags=flags)
+    on_mfma = w.dtype == "bf16" and w.d_in == w.d_out == 64 and not args.generic
     n = ctypes.c_size_t()
     ws._check(ws.lib().gl_scan_qkv_workspace_size(ctypes.byref(desc), ctypes.byref(n)))
     wsb = torch.empty(max(n.value, 16), dtype=torch.uint8, device=dev)
     flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    # the plain copy of known size that calibrates FETCH_SIZE / WRITE_SIZE
+    calib_src = torch.ones(64 << 20, dtype=torch.float32, device=dev)
+    calib_dst = torch.empty_like(calib_src)
+    torch.neg(calib_src, out=calib_dst)  # 256 MiB in, 256 MiB out
+    torch.cuda.synchronize()
+    del calib_src, calib_dst
     L = ws.lib()
     stream = torch.cuda.current_stream(dev)
     sp = ctypes.c_void_p(stream.cuda_stream)
@@ -517,16 +525,31 @@ def qkv_bwd_main(args, w):
     torch.cuda.synchronize()
     ts = [a.elapsed_time(b) for a, b in ev]
     ms = sum(ts) / len(ts)
-    # the scan's reverse-pass model with dk = d_out, dv = d_in: flops of the
-    # chunked method (16 dk dv + 8 64 (dk + dv) / 2 per token-head); on the
-    # vector-ALU kernels the binding peak is the fp32 (fp64) vector rate
+    # dk = d_out (q = u, k = g), dv = d_in (v = x, upstream dz).  Algorithmic
+    # bytes per token-head: q, k, v, dz read and dq, dk, dv written once
+    # (e (4 dk + 3 dv)), eta, alpha read and deta, dalpha written (4 eg);
+    # W0 read and dW0 written once per head.  Flops of the chunked method:
+    # 16 dk dv + 8 64 (dk + dv) / 2 per token-head.
     e = {"bf16": 2, "f32": 4, "f64": 8}[w.dtype]
     eg = 8 if w.dtype == "f64" else 4
     nt = w.B * w.H * w.T
     nflops = nt * (16 * w.d_in * w.d_out + 8 * 64 * (w.d_in + w.d_out) // 2)
-    nbytes = nt * (e * (4 * w.d_out + 2 * w.d_in) + 4 * eg) + w.H * w.d_in * w.d_out * (e + eg)
-    peak = PEAK_VALU[w.dtype] / 1e12
-    achieved = nflops / 1e12 / (ms / 1e3)
+    nbytes = nt * (e * (4 * w.d_out + 3 * w.d_in) + 4 * eg) + w.H * w.d_in * w.d_out * (e + eg)
+    if on_mfma:
+        # chunk-parallel on the matrix cores: bound by HBM (its flops take
+        # about a tenth of the HBM time at the bf16 matrix peak)
+        roof = {"bound": "hbm", "achieved": nbytes / 1e9 / (ms / 1e3), "peak": PEAK_HBM / 1e9,
+                "unit": "GB/s", "traffic": None, "algorithmic_bytes": nbytes,
+                "algorithmic_flops": nflops,
+                "kernel": "fwd_mfma<64> state pass + qkv_bwd_inc + mf_carry + qkv_bwd_chunk + "
+                          "finalize_kernel (whole reverse pass)"}
+    else:
+        # the vector-ALU kernels: the binding peak is the fp32 (fp64) vector rate
+        roof = {"bound": "alu", "achieved": nflops / 1e12 / (ms / 1e3),
+                "peak": PEAK_VALU[w.dtype] / 1e12, "unit": "TFLOP/s", "traffic": None,
+                "algorithmic_flops": nflops, "algorithmic_bytes": nbytes,
+                "kernel": "fwd_generic (states) + bwd_generic + finalize_kernel (vector ALU)"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
     rec = {
         "metric": "tokens/s (reverse scan of the transpose read)",
         "value": w.B * w.T / (ms / 1e3),
@@ -544,11 +567,9 @@ def qkv_bwd_main(args, w):
                                f"{w.dtype}, gradients of z_t = (W0 + D_t)^T u_t",
                    "B": w.B, "H": w.H, "T": w.T, "d_in": w.d_in, "d_out": w.d_out,
                    "io": w.dtype, "parallelism": "single GPU"},
-        "roofline": {"bound": "alu", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
-                     "frac": achieved / peak, "traffic": None, "algorithmic_flops": nflops,
-                     "algorithmic_bytes": nbytes,
-                     "kernel": "fwd_generic (states) + bwd_generic + finalize_kernel (vector ALU)"},
-        "passes_ms": {"mean": ms, "median": statistics.median(ts), "min": min(ts), "max": max(ts)},
+        "roofline": roof,
+        "passes_ms": {"mean": ms, "median": statistics.median(ts), "min": min(ts), "max": max(ts),
+                      "each": [round(x, 5) for x in ts]},
     }
     if not args.no_cpu:
         W0T = np.ascontiguousarray(np.transpose(inp["W0"], (0, 2, 1)))

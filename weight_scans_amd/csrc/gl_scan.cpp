@@ -626,10 +626,11 @@ namespace {
 struct QkvPlan {
   int chunk = 0, n_chunks = 0, n_tiles = 0;
   size_t comp = 8, states = 0, part = 0, dw = 0, total = 0;
-  // bf16, dk = dv = 64 on the matrix cores: bf16 chunk-start states, the fp32
+  // bf16, dk = dv = 64 on the matrix cores: bf16 chunk-start states, the bf16
   // adjoint leaving every chunk (lam), per-chunk decays (gam) and a dW0'
-  // share per chunk (dw); part is unused
+  // share per group of chunks (dw); part is unused
   bool mfma = false;
+  int n_grp = 0;
   size_t lam = 0, gam = 0;
 };
 gl_status_t qkv_plan(const gl_scan_desc_t* d, QkvPlan* p) {
@@ -646,10 +647,11 @@ gl_status_t qkv_plan(const gl_scan_desc_t* d, QkvPlan* p) {
     if (static_cast<int64_t>(BH) * p->n_chunks > 0x7fffffffLL)
       return fail(GL_ERROR_NOT_SUPPORTED, "B*H*chunks above 2^31-1");
     const size_t cells = BH * static_cast<size_t>(p->n_chunks);
+    p->n_grp = gls::mfma_qkv_bwd_groups(p->n_chunks);
     p->states = round_up(cells * dd * 2);
-    p->lam = round_up(cells * dd * sizeof(float));
+    p->lam = round_up(cells * dd * 2);
     p->gam = round_up(cells * sizeof(float));
-    p->dw = round_up(cells * dd * sizeof(float));
+    p->dw = round_up(BH * static_cast<size_t>(p->n_grp) * dd * sizeof(float));
     p->total = p->states + p->lam + p->gam + p->dw;
     return GL_SUCCESS;
   }
@@ -717,7 +719,7 @@ gl_status_t gl_scan_qkv_bwd(const gl_scan_desc_t* desc, const void* q, const voi
     fa.part_eta = nullptr; fa.part_alpha = nullptr; fa.part_dW0 = b.part_dW0;
     fa.deta = deta; fa.dalpha = dalpha; fa.dW0 = dW0;
     fa.B = desc->B; fa.H = desc->H; fa.T = desc->T;
-    fa.d_in = 64; fa.d_out = 64; fa.n_tiles = 1; fa.n_seg = p.n_chunks;
+    fa.d_in = 64; fa.d_out = 64; fa.n_tiles = 1; fa.n_seg = p.n_grp;
     fa.alpha_done = true;
     fa.eta_done = true;
     return hip_status(gls::launch_finalize(desc->io_dtype, fa, s), "qkv finalize launch");

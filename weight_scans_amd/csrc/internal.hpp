@@ -180,11 +180,6 @@ hipError_t launch_mfma_final_state(const FwdArgs& a, hipStream_t s);
 bool mf_shape_ok(int io, int d_in, int d_out);
 hipError_t launch_mf_fwd(int io, const FwdArgs& a, hipStream_t s);
 hipError_t launch_mf_bwd(int io, const BwdArgs& a, hipStream_t s);
-// The carry scan over chunks of those kernels (fp32): buf [BH][n][dd], slot c
-// holding the increment arriving at chunk c from the chunk visited before it
-// (forward: c - 1, reverse: c + 1), becomes the carry at every chunk.
-hipError_t launch_mf_carry_f32(float* buf, const float* gam, int64_t BH, int n, int dd,
-                               bool reverse, hipStream_t s);
 
 // Matrix-core kernels: bf16 io, d_in == d_out in {64, 128}, chunk 64.
 constexpr int kMfmaChunk = 64;
@@ -198,6 +193,7 @@ hipError_t launch_mfma_qkv_two_pass(const FwdArgs& a, hipStream_t s);
 // adjoint increments, carry scan, chunk gradients (x = k, g = v; dx <- dk,
 // dg <- dv; states / mf_lam / mf_gam / part_dW0 in the workspace)
 bool mfma_qkv_bwd_ok(int io, int dk, int dv);
+int mfma_qkv_bwd_groups(int n_chunks);  // dW0' shares per sequence-head
 hipError_t launch_mfma_qkv_bwd(const BwdArgs& a, hipStream_t s);
 hipError_t launch_mfma_bwd_lam(const BwdArgs& a, hipStream_t s);  // adjoint-only segment pass
 hipError_t launch_mfma_bwd_f64(const BwdArgs& a, hipStream_t s);   // fused reverse scan, d = 64

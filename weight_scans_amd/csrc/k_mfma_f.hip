@@ -704,12 +704,6 @@ hipError_t bwd_passes(const BwdArgs& a, hipStream_t s) {
 
 }  // namespace
 
-hipError_t launch_mf_carry_f32(float* buf, const float* gam, int64_t BH, int n, int dd,
-                               bool reverse, hipStream_t s) {
-  if (BH * n == 0) return hipSuccess;
-  return carry<float>(buf, gam, BH, n, dd, reverse, s);
-}
-
 bool mf_shape_ok(int io, int d_in, int d_out) {
   const int dm = io == IO_F64 ? 32 : io == IO_F32 ? 64 : 0;
   return d_in <= dm && d_out <= dm;

@@ -48,82 +48,139 @@ __device__ __forceinline__ uint32_t unit64(int u) {
   return static_cast<uint32_t>(sidx<kD>(u >> 3, 8 * (u & 7)) * 2);
 }
 
-// ---- adjoint increments and dW0' shares of every chunk ----
+// ---- adjoint increments of every chunk, dW0' shares of every group ----
+// Work-group (bh, group) walks the kInc chunks of its group in order; the
+// loads of the next chunk are in flight while the current one is multiplied.
+constexpr int kInc = 8;  // chunks per work-group (one dW0' share each)
+
 struct alignas(16) IncLds {
   __bf16 Q[kCk * kD], DY[kCk * kD];  // swizzled [token][64]
   float eq[kCk];
   float gam;
 };
 
-__global__ __launch_bounds__(kNI) void qkv_bwd_inc(BwdArgs a) {
+__global__ __launch_bounds__(kNI) void qkv_bwd_inc(BwdArgs a, int n_grp) {
   __shared__ IncLds L;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g4 = lane >> 4, l16 = lane & 15;
   const int n = a.n_chunks;
-  const int64_t bh = blockIdx.x / n, BH = a.B * a.H;
-  const int c = static_cast<int>(blockIdx.x % n);
-  const int64_t T = a.T, t0 = static_cast<int64_t>(c) * kCk;
-  const int cv = static_cast<int>(std::min<int64_t>(kCk, T - t0));
-  const __amdgpu_buffer_rsrc_t rq =
-      buffer_rsrc(static_cast<const uint16_t*>(a.q) + (bh * T + t0) * kD, cv * kD * 2);
-  const __amdgpu_buffer_rsrc_t rd =
-      buffer_rsrc(static_cast<const uint16_t*>(a.dy) + (bh * T + t0) * kD, cv * kD * 2);
+  const int64_t bh = blockIdx.x / n_grp, BH = a.B * a.H;
+  const int grp = static_cast<int>(blockIdx.x % n_grp);
+  const int c_beg = grp * kInc, c_end = std::min(n, c_beg + kInc);
+  const int64_t T = a.T, dd = static_cast<int64_t>(kD) * kD;
+  const uint16_t* qb = static_cast<const uint16_t*>(a.q) + bh * T * kD;
+  const uint16_t* db = static_cast<const uint16_t*>(a.dy) + bh * T * kD;
+  const float* ab = static_cast<const float*>(a.alpha) + bh * T;
   u32x4 uq[2], ud[2];
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const uint32_t off = static_cast<uint32_t>((tid + kNI * j) * 16);
-    uq[j] = __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0);
-    ud[j] = __builtin_amdgcn_raw_buffer_load_b128(rd, off, 0, 0);
-  }
   float al = 1.f;
-  if (wave == 0 && lane < cv) al = static_cast<const float*>(a.alpha)[bh * T + t0 + lane];
-  if (wave == 0) {
-    const ChunkGates gt = chunk_gates(al, lane);
-    L.eq[lane] = fexp2(gt.lq);
-    if (lane == 0) L.gam = fexp2(gt.llast);
-  }
+  const auto fetch = [&](int c) {
+    const int64_t t0 = static_cast<int64_t>(c) * kCk;
+    const int cv = static_cast<int>(std::min<int64_t>(kCk, T - t0));
+    const __amdgpu_buffer_rsrc_t rq = buffer_rsrc(qb + t0 * kD, cv * kD * 2);
+    const __amdgpu_buffer_rsrc_t rd = buffer_rsrc(db + t0 * kD, cv * kD * 2);
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const uint32_t lo = unit64(tid + kNI * j);
-    *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(L.Q) + lo) = uq[j];
-    *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(L.DY) + lo) = ud[j];
-  }
-  __syncthreads();
-
-  // V^T-free form: block (r block w, k block cb) of dy^T q over the chunk's
-  // tokens, with and without the factor e(lq_u) (on the q fragments)
+    for (int j = 0; j < 2; ++j) {
+      const uint32_t off = static_cast<uint32_t>((tid + kNI * j) * 16);
+      uq[j] = __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0);
+      ud[j] = __builtin_amdgcn_raw_buffer_load_b128(rd, off, 0, 0);
+    }
+    al = (wave == 0 && lane < cv) ? ab[t0 + lane] : 1.f;
+  };
+  fetch(c_beg);
   const LaneOff<kD> o = lane_off<kD>(lane);
   const int rb = wave;
-  f32x4 v[4], w[4];
+  // W^T-layout accumulators: lane holds rows r = rb 16 + l16, columns
+  // k = cb 16 + 4 g4 .. + 3 of sum dy q^T (operands swapped: the product
+  // comes out transposed, four consecutive columns per lane)
+  f32x4 w[4];
 #pragma unroll
-  for (int cb = 0; cb < 4; ++cb) v[cb] = w[cb] = zero4();
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
-    const bf16x8 df = frag_ts<kD>(L.DY, o, kb * 32, rb * 16);
-    const f32x4 e0 = *reinterpret_cast<const f32x4*>(&L.eq[kb * 32 + 8 * g4]);
-    const f32x4 e1 = *reinterpret_cast<const f32x4*>(&L.eq[kb * 32 + 8 * g4 + 4]);
-#pragma unroll
-    for (int cb = 0; cb < 4; ++cb) {
-      const bf16x8 qf = frag_ts<kD>(L.Q, o, kb * 32, cb * 16);
-      w[cb] = mfma16x16x32(df, qf, w[cb]);
-      v[cb] = mfma16x16x32(df, scale8(qf, e0, e1), v[cb]);
+  for (int cb = 0; cb < 4; ++cb) w[cb] = zero4();
+  for (int c = c_beg; c < c_end; ++c) {
+    __syncthreads();  // the previous chunk's fragment reads are done
+    if (wave == 0) {
+      const ChunkGates gt = chunk_gates(al, lane);
+      L.eq[lane] = fexp2(gt.lq);
+      if (lane == 0) L.gam = fexp2(gt.llast);
     }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const uint32_t lo = unit64(tid + kNI * j);
+      *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(L.Q) + lo) = uq[j];
+      *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(L.DY) + lo) = ud[j];
+    }
+    if (c + 1 < c_end) fetch(c + 1);
+    __syncthreads();
+    f32x4 v[4];
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) v[cb] = zero4();
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const bf16x8 df = frag_ts<kD>(L.DY, o, kb * 32, rb * 16);
+      const f32x4 e0 = *reinterpret_cast<const f32x4*>(&L.eq[kb * 32 + 8 * g4]);
+      const f32x4 e1 = *reinterpret_cast<const f32x4*>(&L.eq[kb * 32 + 8 * g4 + 4]);
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb) {
+        const bf16x8 qf = frag_ts<kD>(L.Q, o, kb * 32, cb * 16);
+        w[cb] = mfma16x16x32(qf, df, w[cb]);
+        v[cb] = mfma16x16x32(scale8(qf, e0, e1), df, v[cb]);
+      }
+    }
+    // V of chunk c is the increment arriving at chunk c - 1 (bf16)
+    if (c > 0) {
+      uint16_t* pv = static_cast<uint16_t*>(a.mf_lam) + (bh * n + c - 1) * dd;
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb)
+        *reinterpret_cast<uint2*>(pv + (rb * 16 + l16) * kD + cb * 16 + 4 * g4) = pack4f(v[cb]);
+    }
+    if (tid == 0) static_cast<float*>(a.mf_gam)[bh * n + c] = L.gam;
   }
-  const int64_t dd = static_cast<int64_t>(kD) * kD;
-  float* pw = static_cast<float*>(a.part_dW0) + (static_cast<int64_t>(c) * BH + bh) * dd;
-  float* pv = c > 0 ? static_cast<float*>(a.mf_lam) + (bh * n + c - 1) * dd : nullptr;
+  float* pw = static_cast<float*>(a.part_dW0) + (static_cast<int64_t>(grp) * BH + bh) * dd;
+  const int r = rb * 16 + l16;
 #pragma unroll
   for (int cb = 0; cb < 4; ++cb) {
-    const int k = cb * 16 + l16;
+    const int k = cb * 16 + 4 * g4;
+    if (a.w0_t) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int r = rb * 16 + 4 * g4 + q;
-      pw[a.w0_t ? k * kD + r : r * kD + k] = w[cb][q];
-      if (pv) pv[r * kD + k] = v[cb][q];
+      for (int q = 0; q < 4; ++q) pw[(k + q) * kD + r] = w[cb][q];
+    } else {
+      *reinterpret_cast<f32x4*>(pw + r * kD + k) = w[cb];
     }
   }
-  if (tid == 0) static_cast<float*>(a.mf_gam)[bh * n + c] = L.gam;
+}
+
+// ---- the adjoint leaving every chunk, from the increments (bf16 in and
+// out, fp32 sums): slot c holds V of chunk c + 1 on entry and A_out of chunk
+// c on exit; A_out of the last chunk is zero, A_out(c) = gam(c + 1) A_out(c + 1) + V(c + 1).
+constexpr int kCarryT = 256;  // threads per work-group; four elements per thread
+constexpr int kCarryG = 16;   // chunks whose loads are issued together
+
+__global__ __launch_bounds__(kCarryT) void qkv_lam_carry(uint16_t* buf, const float* gam, int n,
+                                                          int n_eb) {
+  const int64_t bh = blockIdx.x / n_eb;
+  const int e4 = static_cast<int>(blockIdx.x % n_eb) * kCarryT + threadIdx.x;  // < kD kD / 4
+  constexpr int64_t dd = static_cast<int64_t>(kD) * kD;
+  uint16_t* p = buf + bh * n * dd + 4 * e4;
+  const float* gm = gam + bh * n;
+  f32x4 carry = zero4();
+  for (int k0 = 0; k0 < n; k0 += kCarryG) {
+    uint2 inc[kCarryG];
+    float dec[kCarryG];
+#pragma unroll
+    for (int j = 0; j < kCarryG; ++j) {
+      const int k = k0 + j, c = n - 1 - k;
+      const bool use = k >= 1 && k < n;
+      inc[j] = use ? *reinterpret_cast<const uint2*>(p + c * dd) : uint2{0u, 0u};
+      dec[j] = use ? gm[c + 1] : 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < kCarryG; ++j) {
+      const int k = k0 + j;
+      if (k >= n) break;
+      carry = dec[j] * carry + unpack4f(inc[j]);
+      *reinterpret_cast<uint2*>(p + (n - 1 - k) * dd) = pack4f(carry);
+    }
+  }
 }
 
 // ---- the gradients of every chunk ----
@@ -165,9 +222,8 @@ __global__ __launch_bounds__(kNG) void qkv_bwd_chunk(BwdArgs a) {
                                                    (bh * n + c) * dd + 8 * tid);
   const u32x4 uw = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.W0) + h * dd +
                                                    8 * tid);
-  const float* ap = static_cast<const float*>(a.mf_lam) + (bh * n + c) * dd + 8 * tid;
-  const f32x4 a0 = *reinterpret_cast<const f32x4*>(ap);
-  const f32x4 a1 = *reinterpret_cast<const f32x4*>(ap + 4);
+  const u32x4 ua = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.mf_lam) +
+                                                   (bh * n + c) * dd + 8 * tid);
   if (wave == 0) {
     const float* et = static_cast<const float*>(a.eta) + bh * T + t0;
     const float* al = static_cast<const float*>(a.alpha) + bh * T + t0;
@@ -184,11 +240,10 @@ __global__ __launch_bounds__(kNG) void qkv_bwd_chunk(BwdArgs a) {
     *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(L.DY) + lo) = ud;
     *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(L.S) + lo) = us;
     *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(L.W) + lo) = uw;
-    uint2 p0 = pack4f(a0), p1 = pack4f(a1);
-    *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(L.A) + lo) = u32x4{p0.x, p0.y, p1.x, p1.y};
-    // <A_out, D_in> over this thread's 8 elements (A_out in fp32)
-    const f32x4 s0 = unpack4f(uint2{us[0], us[1]}), s1 = unpack4f(uint2{us[2], us[3]});
-    const float cp = wave_sum(dot4f(a0, s0) + dot4f(a1, s1));
+    *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(L.A) + lo) = ua;
+    // <A_out, D_in> over this thread's 8 elements
+    const float cp = wave_sum(dot4f(unpack4f(uint2{ua[0], ua[1]}), unpack4f(uint2{us[0], us[1]})) +
+                              dot4f(unpack4f(uint2{ua[2], ua[3]}), unpack4f(uint2{us[2], us[3]})));
     if (lane == 0) L.c0[wave] = cp;
   }
   __syncthreads();
@@ -315,8 +370,12 @@ __global__ __launch_bounds__(kNG) void qkv_bwd_chunk(BwdArgs a) {
 
 bool mfma_qkv_bwd_ok(int io, int dk, int dv) { return io == IO_BF16 && dk == kD && dv == kD; }
 
+int mfma_qkv_bwd_groups(int n_chunks) { return (n_chunks + kInc - 1) / kInc; }
+
 // a: x = k (write key), g = v, q the read vector; dx <- dk, dg <- dv, dq;
-// states, mf_lam, mf_gam, part_dW0 in the workspace; deta_out / dalpha_out.
+// states (bf16 [BH][n][64][64]), mf_lam (bf16 [BH][n][64][64]), mf_gam
+// (fp32 [BH][n]), part_dW0 (fp32 [groups][BH][64][64]) in the workspace;
+// deta_out / dalpha_out.
 hipError_t launch_mfma_qkv_bwd(const BwdArgs& a, hipStream_t s) {
   const int64_t BH = a.B * a.H;
   const int n = a.n_chunks;
@@ -330,11 +389,15 @@ hipError_t launch_mfma_qkv_bwd(const BwdArgs& a, hipStream_t s) {
   f.seg_chunks = n; f.n_seg = 1;
   hipError_t e = launch_mfma_fwd(f, s);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(qkv_bwd_inc, dim3(static_cast<unsigned>(BH * n)), dim3(kNI), 0, s, a);
+  const int n_grp = mfma_qkv_bwd_groups(n);
+  hipLaunchKernelGGL(qkv_bwd_inc, dim3(static_cast<unsigned>(BH * n_grp)), dim3(kNI), 0, s, a,
+                     n_grp);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  e = launch_mf_carry_f32(static_cast<float*>(a.mf_lam), static_cast<const float*>(a.mf_gam), BH, n,
-                          kD * kD, true, s);
+  constexpr int n_eb = kD * kD / 4 / kCarryT;
+  hipLaunchKernelGGL(qkv_lam_carry, dim3(static_cast<unsigned>(BH * n_eb)), dim3(kCarryT), 0, s,
+                     static_cast<uint16_t*>(a.mf_lam), static_cast<const float*>(a.mf_gam), n, n_eb);
+  e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(qkv_bwd_chunk, dim3(static_cast<unsigned>(BH * n)), dim3(kNG), 0, s, a);
   return hipGetLastError();
