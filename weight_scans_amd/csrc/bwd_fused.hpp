@@ -33,12 +33,9 @@ struct alignas(16) QkF {  // per causal block: row sums (qq) and column sums (kk
   float qq[10][16], kk[10][16];
 };
 
-// Gates of a chunk from its eta / alpha rows (one wave, lane = token).
-// Padding tokens carry alpha = 1, eta = 0.
-__device__ __forceinline__ void gates_f(const float* eta_row, const float* alpha_row, RecF& r,
-                                        int cv, int lane) {
-  const float et = lane < cv ? eta_row[lane] : 0.f;
-  const float al = lane < cv ? alpha_row[lane] : 1.f;
+// Gates of a chunk from this lane's token's eta and alpha (one wave, lane =
+// token).  Padding tokens carry alpha = 1, eta = 0.
+__device__ __forceinline__ void gates_v(float et, float al, RecF& r, int lane) {
   const ChunkGates gt = chunk_gates(al, lane);
   r.lq[lane] = gt.lq;
   r.li[lane] = gt.l;
@@ -50,6 +47,11 @@ __device__ __forceinline__ void gates_f(const float* eta_row, const float* alpha
     r.gam = fexp2(gt.llast);
     r.llast = gt.llast;
   }
+}
+// The same from the chunk's eta / alpha rows (cv valid tokens).
+__device__ __forceinline__ void gates_f(const float* eta_row, const float* alpha_row, RecF& r,
+                                        int cv, int lane) {
+  gates_v(lane < cv ? eta_row[lane] : 0.f, lane < cv ? alpha_row[lane] : 1.f, r, lane);
 }
 
 __device__ __forceinline__ f32x4 unpack4f(const uint2& p) {

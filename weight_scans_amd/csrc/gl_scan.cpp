@@ -626,9 +626,9 @@ namespace {
 struct QkvPlan {
   int chunk = 0, n_chunks = 0, n_tiles = 0;
   size_t comp = 8, states = 0, part = 0, dw = 0, total = 0;
-  // bf16, dk = dv = 64 on the matrix cores: bf16 chunk-start states, the bf16
-  // adjoint leaving every chunk (lam), per-chunk decays (gam) and a dW0'
-  // share per group of chunks (dw); part is unused
+  // bf16, dk = dv = 64 on the matrix cores: bf16 chunk-start states; per
+  // group of chunks the fp32 adjoint leaving it (lam), its decay (gam) and
+  // a dW0' share (dw); part is unused
   bool mfma = false;
   int n_grp = 0;
   size_t lam = 0, gam = 0;
@@ -649,8 +649,9 @@ gl_status_t qkv_plan(const gl_scan_desc_t* d, QkvPlan* p) {
     const size_t cells = BH * static_cast<size_t>(p->n_chunks);
     p->n_grp = gls::mfma_qkv_bwd_groups(p->n_chunks);
     p->states = round_up(cells * dd * 2);
-    p->lam = round_up(cells * dd * 2);
-    p->gam = round_up(cells * sizeof(float));
+    const size_t groups = BH * static_cast<size_t>(p->n_grp);
+    p->lam = round_up(groups * dd * sizeof(float));
+    p->gam = round_up(groups * sizeof(float));
     p->dw = round_up(BH * static_cast<size_t>(p->n_grp) * dd * sizeof(float));
     p->total = p->states + p->lam + p->gam + p->dw;
     return GL_SUCCESS;

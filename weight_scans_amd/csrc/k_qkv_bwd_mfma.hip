@@ -22,12 +22,16 @@
 // and dalpha from <A_out, D_in>, pp_j = v_j . (A_out k_j), rr_u = q_u . (D_in^T dy_u)
 // and the row / column sums of Be o (Q K^T) (the same identity as the scan's).
 //
-// Five launches: the forward kernel's state-only instance (x = k, g = v)
-// writes D_in of every chunk (bf16); qkv_bwd_inc forms every chunk's adjoint
-// increment V = sum_u e(lq_u) dy_u q_u^T and its dW0' share; the carry scan
-// over chunks turns the increments into A_out of every chunk; qkv_bwd_chunk
-// forms every chunk's gradients from its tiles and the two carries; the
-// finalize kernel sums the dW0' shares in a fixed order.
+// Chunks are taken in groups of kGrp (eight).  Five launches: the forward
+// kernel's state-only instance (x = k, g = v) writes D_in of every chunk
+// (bf16); qkv_bwd_inc forms every group's adjoint increment (the chunk
+// formula over the group's tokens: sum_u e(L_{u-1}) dy_u q_u^T with L the
+// group-local cumsum of log2 alpha), its decay and its dW0' share;
+// qkv_grp_carry turns the increments into the adjoint leaving every group;
+// qkv_bwd_chunk walks the chunks of its group from right to left carrying
+// the adjoint in fp32 registers (A_in = e(l_last) A_out + sum_u e(lq_u)
+// dy_u q_u^T) and forms every chunk's gradients from its tiles and the two
+// carries; the finalize kernel sums the dW0' shares in a fixed order.
 #include <algorithm>
 #include <cstdint>
 
@@ -48,15 +52,14 @@ __device__ __forceinline__ uint32_t unit64(int u) {
   return static_cast<uint32_t>(sidx<kD>(u >> 3, 8 * (u & 7)) * 2);
 }
 
-// ---- adjoint increments of every chunk, dW0' shares of every group ----
-// Work-group (bh, group) walks the kInc chunks of its group in order; the
-// loads of the next chunk are in flight while the current one is multiplied.
-constexpr int kInc = 8;  // chunks per work-group (one dW0' share each)
+constexpr int kGrp = 8;  // chunks per group (one work-group of each kind)
 
+// ---- adjoint increment, decay and dW0' share of every group ----
+// Work-group (bh, group) walks the chunks of its group in order; the loads
+// of the next chunk are in flight while the current one is multiplied.
 struct alignas(16) IncLds {
   __bf16 Q[kCk * kD], DY[kCk * kD];  // swizzled [token][64]
-  float eq[kCk];
-  float gam;
+  float eq[kCk];                     // e(L_{u-1}) from the group's start
 };
 
 __global__ __launch_bounds__(kNI) void qkv_bwd_inc(BwdArgs a, int n_grp) {
@@ -67,11 +70,10 @@ __global__ __launch_bounds__(kNI) void qkv_bwd_inc(BwdArgs a, int n_grp) {
   const int n = a.n_chunks;
   const int64_t bh = blockIdx.x / n_grp, BH = a.B * a.H;
   const int grp = static_cast<int>(blockIdx.x % n_grp);
-  const int c_beg = grp * kInc, c_end = std::min(n, c_beg + kInc);
+  const int c_beg = grp * kGrp, c_end = std::min(n, c_beg + kGrp);
   const int64_t T = a.T, dd = static_cast<int64_t>(kD) * kD;
   const uint16_t* qb = static_cast<const uint16_t*>(a.q) + bh * T * kD;
   const uint16_t* db = static_cast<const uint16_t*>(a.dy) + bh * T * kD;
-  const float* ab = static_cast<const float*>(a.alpha) + bh * T;
   u32x4 uq[2], ud[2];
   float al = 1.f;
   const auto fetch = [&](int c) {
@@ -85,23 +87,27 @@ __global__ __launch_bounds__(kNI) void qkv_bwd_inc(BwdArgs a, int n_grp) {
       uq[j] = __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0);
       ud[j] = __builtin_amdgcn_raw_buffer_load_b128(rd, off, 0, 0);
     }
-    al = (wave == 0 && lane < cv) ? ab[t0 + lane] : 1.f;
+    const __amdgpu_buffer_rsrc_t ra =
+        buffer_rsrc(static_cast<const float*>(a.alpha) + bh * T + t0, cv * 4);
+    const float x = __builtin_bit_cast(
+        float, __builtin_amdgcn_raw_buffer_load_b32(ra, static_cast<uint32_t>(lane * 4), 0, 0));
+    al = lane < cv ? x : 1.f;
   };
   fetch(c_beg);
   const LaneOff<kD> o = lane_off<kD>(lane);
   const int rb = wave;
-  // W^T-layout accumulators: lane holds rows r = rb 16 + l16, columns
-  // k = cb 16 + 4 g4 .. + 3 of sum dy q^T (operands swapped: the product
-  // comes out transposed, four consecutive columns per lane)
-  f32x4 w[4];
+  // accumulators in the transposed MFMA layout (operands swapped): lane
+  // holds row r = rb 16 + l16, columns k = cb 16 + 4 g4 .. + 3
+  f32x4 w[4], v[4];
 #pragma unroll
-  for (int cb = 0; cb < 4; ++cb) w[cb] = zero4();
+  for (int cb = 0; cb < 4; ++cb) w[cb] = v[cb] = zero4();
+  float lg = 0.f;  // log2 of the decay from the group's start to chunk c (wave 0)
   for (int c = c_beg; c < c_end; ++c) {
     __syncthreads();  // the previous chunk's fragment reads are done
     if (wave == 0) {
       const ChunkGates gt = chunk_gates(al, lane);
-      L.eq[lane] = fexp2(gt.lq);
-      if (lane == 0) L.gam = fexp2(gt.llast);
+      L.eq[lane] = fexp2(lg + gt.lq);
+      lg += gt.llast;
     }
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
@@ -111,9 +117,6 @@ __global__ __launch_bounds__(kNI) void qkv_bwd_inc(BwdArgs a, int n_grp) {
     }
     if (c + 1 < c_end) fetch(c + 1);
     __syncthreads();
-    f32x4 v[4];
-#pragma unroll
-    for (int cb = 0; cb < 4; ++cb) v[cb] = zero4();
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       const bf16x8 df = frag_ts<kD>(L.DY, o, kb * 32, rb * 16);
@@ -126,17 +129,17 @@ __global__ __launch_bounds__(kNI) void qkv_bwd_inc(BwdArgs a, int n_grp) {
         v[cb] = mfma16x16x32(scale8(qf, e0, e1), df, v[cb]);
       }
     }
-    // V of chunk c is the increment arriving at chunk c - 1 (bf16)
-    if (c > 0) {
-      uint16_t* pv = static_cast<uint16_t*>(a.mf_lam) + (bh * n + c - 1) * dd;
-#pragma unroll
-      for (int cb = 0; cb < 4; ++cb)
-        *reinterpret_cast<uint2*>(pv + (rb * 16 + l16) * kD + cb * 16 + 4 * g4) = pack4f(v[cb]);
-    }
-    if (tid == 0) static_cast<float*>(a.mf_gam)[bh * n + c] = L.gam;
   }
-  float* pw = static_cast<float*>(a.part_dW0) + (static_cast<int64_t>(grp) * BH + bh) * dd;
+  // the group's increment arrives at the group before it (fp32); its decay
   const int r = rb * 16 + l16;
+  if (grp > 0) {
+    float* pv = static_cast<float*>(a.mf_lam) + (bh * n_grp + grp - 1) * dd;
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb)
+      *reinterpret_cast<f32x4*>(pv + r * kD + cb * 16 + 4 * g4) = v[cb];
+  }
+  if (tid == 0) static_cast<float*>(a.mf_gam)[bh * n_grp + grp] = fexp2(lg);
+  float* pw = static_cast<float*>(a.part_dW0) + (static_cast<int64_t>(grp) * BH + bh) * dd;
 #pragma unroll
   for (int cb = 0; cb < 4; ++cb) {
     const int k = cb * 16 + 4 * g4;
@@ -149,41 +152,50 @@ __global__ __launch_bounds__(kNI) void qkv_bwd_inc(BwdArgs a, int n_grp) {
   }
 }
 
-// ---- the adjoint leaving every chunk, from the increments (bf16 in and
-// out, fp32 sums): slot c holds V of chunk c + 1 on entry and A_out of chunk
-// c on exit; A_out of the last chunk is zero, A_out(c) = gam(c + 1) A_out(c + 1) + V(c + 1).
+// ---- the adjoint leaving every group, from the group increments (fp32):
+// slot g holds the increment of group g + 1 on entry and the adjoint
+// leaving group g on exit; zero for the last group, then
+// A_out(g) = gam(g + 1) A_out(g + 1) + V(g + 1).
 constexpr int kCarryT = 256;  // threads per work-group; four elements per thread
-constexpr int kCarryG = 16;   // chunks whose loads are issued together
+constexpr int kCarryG = 16;   // groups whose loads are issued together
 
-__global__ __launch_bounds__(kCarryT) void qkv_lam_carry(uint16_t* buf, const float* gam, int n,
+__global__ __launch_bounds__(kCarryT) void qkv_grp_carry(float* buf, const float* gam, int ng,
                                                           int n_eb) {
   const int64_t bh = blockIdx.x / n_eb;
   const int e4 = static_cast<int>(blockIdx.x % n_eb) * kCarryT + threadIdx.x;  // < kD kD / 4
   constexpr int64_t dd = static_cast<int64_t>(kD) * kD;
-  uint16_t* p = buf + bh * n * dd + 4 * e4;
-  const float* gm = gam + bh * n;
+  float* p = buf + bh * ng * dd + 4 * e4;
+  const float* gm = gam + bh * ng;
   f32x4 carry = zero4();
-  for (int k0 = 0; k0 < n; k0 += kCarryG) {
-    uint2 inc[kCarryG];
+  for (int k0 = 0; k0 < ng; k0 += kCarryG) {
+    f32x4 inc[kCarryG];
     float dec[kCarryG];
 #pragma unroll
     for (int j = 0; j < kCarryG; ++j) {
-      const int k = k0 + j, c = n - 1 - k;
-      const bool use = k >= 1 && k < n;
-      inc[j] = use ? *reinterpret_cast<const uint2*>(p + c * dd) : uint2{0u, 0u};
-      dec[j] = use ? gm[c + 1] : 0.f;
+      const int k = k0 + j, g = ng - 1 - k;
+      const bool use = k >= 1 && k < ng;
+      inc[j] = use ? *reinterpret_cast<const f32x4*>(p + g * dd) : zero4();
+      dec[j] = use ? gm[g + 1] : 0.f;
     }
 #pragma unroll
     for (int j = 0; j < kCarryG; ++j) {
       const int k = k0 + j;
-      if (k >= n) break;
-      carry = dec[j] * carry + unpack4f(inc[j]);
-      *reinterpret_cast<uint2*>(p + (n - 1 - k) * dd) = pack4f(carry);
+      if (k < ng) {
+        carry = dec[j] * carry + inc[j];
+        *reinterpret_cast<f32x4*>(p + (ng - 1 - k) * dd) = carry;
+      }
     }
   }
 }
 
 // ---- the gradients of every chunk ----
+// Work-group (bh, group) walks the chunks of its group from right to left.
+// The adjoint A_out of the chunk at hand is kept in fp32 registers (wave w:
+// blocks 2w, 2w + 1 of the 16 x 16 blocks of A, rows r = 16 (b / 4) + l16,
+// columns 16 (b % 4) + 4 g4 .. + 3) and copied to LDS in bf16 for the
+// products; W0' is staged once; the tiles of the next chunk (q, k, v, dy,
+// D_in and the gate rows) are loaded into registers while the current one
+// is worked on.
 struct alignas(16) GradLds {
   __bf16 Q[kCk * kD], K[kCk * kD], V[kCk * kD], DY[kCk * kD];  // swizzled [token][64]
   __bf16 S[kD * kD], A[kD * kD], W[kD * kD];  // D_in [r][k], A_out [r][k], W0' as stored
@@ -194,175 +206,244 @@ struct alignas(16) GradLds {
   float c0[8];
 };
 
-__global__ __launch_bounds__(kNG) void qkv_bwd_chunk(BwdArgs a) {
+// One chunk's global inputs as this thread holds them: 16 bytes of each
+// [64][64] bf16 tile (unit tid) and its lane's token's gates.
+struct GradIn {
+  u32x4 q, k, v, dy, s;
+  float eta, alpha;
+};
+
+__global__ __launch_bounds__(kNG) __attribute__((amdgpu_waves_per_eu(4, 4))) void qkv_bwd_chunk(
+    BwdArgs a, int n_grp) {
   __shared__ GradLds L;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g4 = lane >> 4, l16 = lane & 15;
   const int n = a.n_chunks;
-  const int64_t bh = blockIdx.x / n;
-  const int c = static_cast<int>(blockIdx.x % n);
+  const int64_t bh = blockIdx.x / n_grp;
+  const int grp = static_cast<int>(blockIdx.x % n_grp);
+  const int c_beg = grp * kGrp, c_end = std::min(n, c_beg + kGrp);
   const int h = static_cast<int>(bh % a.H);
-  const int64_t T = a.T, t0 = static_cast<int64_t>(c) * kCk;
-  const int cv = static_cast<int>(std::min<int64_t>(kCk, T - t0));
+  const int64_t T = a.T;
   const int64_t dd = static_cast<int64_t>(kD) * kD;
-  const int64_t tok = (bh * T + t0) * kD;
-
-  // ---- loads: one 16-byte unit per thread of q, k, v, dy, D_in and W0',
-  // and the matching 8 floats of A_out
-  const auto tile_rsrc = [&](const void* base) {
-    return buffer_rsrc(static_cast<const uint16_t*>(base) + tok, cv * kD * 2);
-  };
   const uint32_t off = static_cast<uint32_t>(tid * 16);
-  const u32x4 uq = __builtin_amdgcn_raw_buffer_load_b128(tile_rsrc(a.q), off, 0, 0);
-  const u32x4 uk = __builtin_amdgcn_raw_buffer_load_b128(tile_rsrc(a.x), off, 0, 0);
-  const u32x4 uv = __builtin_amdgcn_raw_buffer_load_b128(tile_rsrc(a.g), off, 0, 0);
-  const u32x4 ud = __builtin_amdgcn_raw_buffer_load_b128(tile_rsrc(a.dy), off, 0, 0);
-  const u32x4 us = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.states) +
-                                                   (bh * n + c) * dd + 8 * tid);
-  const u32x4 uw = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.W0) + h * dd +
-                                                   8 * tid);
-  const u32x4 ua = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.mf_lam) +
-                                                   (bh * n + c) * dd + 8 * tid);
-  if (wave == 0) {
-    const float* et = static_cast<const float*>(a.eta) + bh * T + t0;
-    const float* al = static_cast<const float*>(a.alpha) + bh * T + t0;
-    gates_f(et, al, L.rc, cv, lane);
-  }
-  // P^T and Be^T start at zero (only the causal parts are written)
-  reinterpret_cast<u32x4*>(L.PT)[tid] = u32x4{0u, 0u, 0u, 0u};
-  reinterpret_cast<u32x4*>(L.BT)[tid] = u32x4{0u, 0u, 0u, 0u};
+  const uint32_t lo = unit64(tid);
+
+  const auto fetch = [&](int c, GradIn& in) {
+    const int64_t t0 = static_cast<int64_t>(c) * kCk;
+    const int cv = static_cast<int>(std::min<int64_t>(kCk, T - t0));
+    const int64_t tok = (bh * T + t0) * kD;
+    const auto rs = [&](const void* base) {
+      return buffer_rsrc(static_cast<const uint16_t*>(base) + tok, cv * kD * 2);
+    };
+    in.q = __builtin_amdgcn_raw_buffer_load_b128(rs(a.q), off, 0, 0);
+    in.k = __builtin_amdgcn_raw_buffer_load_b128(rs(a.x), off, 0, 0);
+    in.v = __builtin_amdgcn_raw_buffer_load_b128(rs(a.g), off, 0, 0);
+    in.dy = __builtin_amdgcn_raw_buffer_load_b128(rs(a.dy), off, 0, 0);
+    in.s = __builtin_amdgcn_raw_buffer_load_b128(
+        buffer_rsrc(static_cast<const uint16_t*>(a.states) + (bh * n + c) * dd, kD * kD * 2), off,
+        0, 0);
+    // gates (every wave loads them; wave 0 uses them): zero past the end
+    const auto rg = [&](const void* base) {
+      return buffer_rsrc(static_cast<const float*>(base) + bh * T + t0, cv * 4);
+    };
+    const uint32_t go = static_cast<uint32_t>(lane * 4);
+    in.eta = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rg(a.eta), go, 0, 0));
+    const float al =
+        __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rg(a.alpha), go, 0, 0));
+    in.alpha = lane < cv ? al : 1.f;
+  };
+  GradIn in;
+  *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(L.W) + lo) =
+      *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.W0) + h * dd + 8 * tid);
+  // the adjoint leaving the group (zero for the last one)
+  f32x4 A[2];
   {
-    const uint32_t lo = unit64(tid);
-    *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(L.Q) + lo) = uq;
-    *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(L.K) + lo) = uk;
-    *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(L.V) + lo) = uv;
-    *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(L.DY) + lo) = ud;
-    *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(L.S) + lo) = us;
-    *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(L.W) + lo) = uw;
-    *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(L.A) + lo) = ua;
-    // <A_out, D_in> over this thread's 8 elements
-    const float cp = wave_sum(dot4f(unpack4f(uint2{ua[0], ua[1]}), unpack4f(uint2{us[0], us[1]})) +
-                              dot4f(unpack4f(uint2{ua[2], ua[3]}), unpack4f(uint2{us[2], us[3]})));
-    if (lane == 0) L.c0[wave] = cp;
+    const float* pa = static_cast<const float*>(a.mf_lam) + (bh * n_grp + grp) * dd;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int b = 2 * wave + i;
+      A[i] = *reinterpret_cast<const f32x4*>(pa + ((b >> 2) * 16 + l16) * kD + (b & 3) * 16 +
+                                             4 * g4);
+    }
   }
-  __syncthreads();
 
   const LaneOff<kD> o = lane_off<kD>(lane);
   const LaneOff<kCk> o64 = lane_off<kCk>(lane);
-  // ---- causal blocks w and w + 8 of the ten: Q K^T and DY V^T, decayed;
-  // P and Be written transposed, the row / column sums of Be o (Q K^T)
-  for (int b = wave; b < 10; b += 8) {
-    const int ib = tri_i(b), jb = tri_j(b);
-    f32x4 qk = zero4(), dv = zero4();
+  for (int c = c_end - 1; c >= c_beg; --c) {
+    const int64_t t0 = static_cast<int64_t>(c) * kCk;
+    const int cv = static_cast<int>(std::min<int64_t>(kCk, T - t0));
+    const int64_t tok = (bh * T + t0) * kD;
+    fetch(c, in);
+    __syncthreads();  // the previous chunk is done with every LDS array
+    if (wave == 0) gates_v(in.eta, in.alpha, L.rc, lane);
+    // P^T and Be^T start at zero (only the causal parts are written)
+    reinterpret_cast<u32x4*>(L.PT)[tid] = u32x4{0u, 0u, 0u, 0u};
+    reinterpret_cast<u32x4*>(L.BT)[tid] = u32x4{0u, 0u, 0u, 0u};
+    *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(L.Q) + lo) = in.q;
+    *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(L.K) + lo) = in.k;
+    *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(L.V) + lo) = in.v;
+    *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(L.DY) + lo) = in.dy;
+    *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(L.S) + lo) = in.s;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      qk = mfma16x16x32(frag_s<kD>(L.Q, o, ib * 16, kb * 32), frag_s<kD>(L.K, o, jb * 16, kb * 32), qk);
-      dv = mfma16x16x32(frag_s<kD>(L.DY, o, ib * 16, kb * 32), frag_s<kD>(L.V, o, jb * 16, kb * 32),
-                        dv);
+    for (int i = 0; i < 2; ++i) {
+      const int b = 2 * wave + i;
+      put4<kD>(L.A, o, (b >> 2) * 16, (b & 3) * 16, pack4f(A[i]));
     }
-    const int col = jb * 16 + l16, r0 = ib * 16 + 4 * g4;
-    const float lc = L.rc.li[col], nbc = L.rc.nb[col];
-    f32x4 p, be, z;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const bool on = col < r0 + q;
-      const float e = on ? fexp2(L.rc.lq[r0 + q] - lc) : 0.f;
-      p[q] = qk[q] * e;
-      be[q] = dv[q] * (e * nbc);
-      z[q] = be[q] * qk[q];
-    }
-    put4<kCk>(L.PT, o64, jb * 16, ib * 16, pack4f(p));
-    put4<kCk>(L.BT, o64, jb * 16, ib * 16, pack4f(be));
-    f32x4 zr;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) zr[q] = row16_sum(z[q]);
-    if (l16 == 15) *reinterpret_cast<f32x4*>(&L.qk.qq[b][4 * g4]) = zr;
-    const float t = sum_rows(z[0] + z[1] + z[2] + z[3]);
-    if (g4 == 0) L.qk.kk[b][l16] = t;
-  }
-  __syncthreads();
+    __syncthreads();
 
-  // ---- outputs, transposed (rows = columns of dq, dk, dv; columns =
-  // tokens): token block tb = w % 4, column blocks cb = 2 (w / 4) + {0, 1}
-  const int tb = wave & 3, hf = wave >> 2;
-  const int ti = tb * 16 + l16;  // this lane's token
-  const float eqi = L.rc.eq[ti], e2i = L.rc.e2[ti], nbi = L.rc.nb[ti];
-  const __amdgpu_buffer_rsrc_t rdq = buffer_rsrc(static_cast<uint16_t*>(a.dq) + tok, cv * kD * 2);
-  const __amdgpu_buffer_rsrc_t rdk = buffer_rsrc(static_cast<uint16_t*>(a.dx) + tok, cv * kD * 2);
-  const __amdgpu_buffer_rsrc_t rdv = buffer_rsrc(static_cast<uint16_t*>(a.dg) + tok, cv * kD * 2);
-  float rr = 0.f, pp = 0.f, de = 0.f;
+    // <A_out, D_in> over this wave's two blocks (A_out in fp32)
+    {
+      float cp = 0.f;
 #pragma unroll
-  for (int h2 = 0; h2 < 2; ++h2) {
-    const int cb = 2 * hf + h2;
-    const uint32_t so = static_cast<uint32_t>((ti * kD + cb * 16 + 4 * g4) * 2);
-    // dq^T: W0'^T dy + e(lq) D_in^T dy + (Be K)^T
-    f32x4 aq = zero4(), sq = zero4();
-#pragma unroll
-    for (int kr = 0; kr < 2; ++kr) {
-      const bf16x8 dyf = frag_s<kD>(L.DY, o, tb * 16, kr * 32);
-      const bf16x8 wf = a.w0_t ? frag_s<kD>(L.W, o, cb * 16, kr * 32)
-                               : frag_ts<kD>(L.W, o, kr * 32, cb * 16);
-      aq = mfma16x16x32(wf, dyf, aq);
-      sq = mfma16x16x32(frag_ts<kD>(L.S, o, kr * 32, cb * 16), dyf, sq);
+      for (int i = 0; i < 2; ++i) {
+        const int b = 2 * wave + i;
+        cp += dot4f(A[i], unpack4f(get4<kD>(L.S, o, (b >> 2) * 16, (b & 3) * 16)));
+      }
+      cp = wave_sum(cp);
+      if (lane == 0) L.c0[wave] = cp;
     }
+    // ---- causal blocks w and w + 8 of the ten: Q K^T and DY V^T, decayed;
+    // P and Be written transposed, the row / column sums of Be o (Q K^T)
+    for (int b = wave; b < 10; b += 8) {
+      __builtin_amdgcn_sched_barrier(0);
+      const int ib = tri_i(b), jb = tri_j(b);
+      f32x4 qk = zero4(), dv = zero4();
 #pragma unroll
-    for (int kj = 0; kj < 2; ++kj)
-      aq = mfma16x16x32(frag_ts<kD>(L.K, o, kj * 32, cb * 16), frag_ts<kCk>(L.BT, o64, kj * 32, tb * 16),
-                        aq);
-    const f32x4 qv = unpack4f(get4<kD>(L.Q, o, tb * 16, cb * 16));  // q_t[k], k = cb 16 + 4 g4 ..
-    rr += dot4f(qv, sq);
-    store8(rdq, so, pack4f(aq + eqi * sq));
-    // dk^T: (Be^T Q)^T - eta e(l_last - l) (A_out^T v)^T
-    f32x4 ak = zero4(), sk = zero4();
+      for (int kb = 0; kb < 2; ++kb) {
+        qk = mfma16x16x32(frag_s<kD>(L.Q, o, ib * 16, kb * 32), frag_s<kD>(L.K, o, jb * 16, kb * 32),
+                          qk);
+        dv = mfma16x16x32(frag_s<kD>(L.DY, o, ib * 16, kb * 32),
+                          frag_s<kD>(L.V, o, jb * 16, kb * 32), dv);
+      }
+      const int col = jb * 16 + l16, r0 = ib * 16 + 4 * g4;
+      const float lc = L.rc.li[col], nbc = L.rc.nb[col];
+      f32x4 p, be, z;
 #pragma unroll
-    for (int ku = 0; ku < 2; ++ku)
-      ak = mfma16x16x32(frag_ts<kD>(L.Q, o, ku * 32, cb * 16), frag_s<kCk>(L.BT, o64, tb * 16, ku * 32),
-                        ak);
+      for (int q = 0; q < 4; ++q) {
+        const bool on = col < r0 + q;
+        const float e = on ? fexp2(L.rc.lq[r0 + q] - lc) : 0.f;
+        p[q] = qk[q] * e;
+        be[q] = dv[q] * (e * nbc);
+        z[q] = be[q] * qk[q];
+      }
+      put4<kCk>(L.PT, o64, jb * 16, ib * 16, pack4f(p));
+      put4<kCk>(L.BT, o64, jb * 16, ib * 16, pack4f(be));
+      f32x4 zr;
 #pragma unroll
-    for (int kr = 0; kr < 2; ++kr)
-      sk = mfma16x16x32(frag_ts<kD>(L.A, o, kr * 32, cb * 16), frag_s<kD>(L.V, o, tb * 16, kr * 32), sk);
-    store8(rdk, so, pack4f(ak + (nbi * e2i) * sk));
-    // u^T: e(l_last - l) (A_out k)^T + (P^T dy)^T;  dv = -eta u
-    f32x4 au = zero4(), su = zero4();
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk)
-      su = mfma16x16x32(frag_s<kD>(L.A, o, cb * 16, kk * 32), frag_s<kD>(L.K, o, tb * 16, kk * 32), su);
-#pragma unroll
-    for (int ku = 0; ku < 2; ++ku)
-      au = mfma16x16x32(frag_ts<kD>(L.DY, o, ku * 32, cb * 16), frag_s<kCk>(L.PT, o64, tb * 16, ku * 32),
-                        au);
-    const f32x4 u = au + e2i * su;
-    const f32x4 vv = unpack4f(get4<kD>(L.V, o, tb * 16, cb * 16));  // v_t[r], r = cb 16 + 4 g4 ..
-    de -= dot4f(vv, u);
-    pp += dot4f(vv, su);
-    store8(rdv, so, pack4f(nbi * u));
-  }
-  // shares over this wave's 32 columns: sum over the four lane groups
-  rr = sum_rows(rr);
-  pp = sum_rows(pp);
-  de = sum_rows(de);
-  if (g4 == 0) {
-    L.rr[hf][ti] = rr;
-    L.pp[hf][ti] = pp;
-    L.de[hf][ti] = de;
-  }
-  __syncthreads();
+      for (int q = 0; q < 4; ++q) zr[q] = row16_sum(z[q]);
+      if (l16 == 15) *reinterpret_cast<f32x4*>(&L.qk.qq[b][4 * g4]) = zr;
+      const float t = sum_rows(z[0] + z[1] + z[2] + z[3]);
+      if (g4 == 0) L.qk.kk[b][l16] = t;
+    }
+    __syncthreads();
 
-  // ---- dalpha and deta of the chunk (wave 0, lane = token)
-  if (wave == 0) {
-    const int ir = kCk - 1 - lane;
-    float c0 = 0.f;
+    // ---- outputs, transposed (rows = columns of dq, dk, dv; columns =
+    // tokens): token block tb = w % 4, column blocks cb = 2 (w / 4) + {0, 1}
+    const int tb = wave & 3, hf = wave >> 2;
+    const int ti = tb * 16 + l16;  // this lane's token
+    const float eqi = L.rc.eq[ti], e2i = L.rc.e2[ti], nbi = L.rc.nb[ti];
+    const __amdgpu_buffer_rsrc_t rdq = buffer_rsrc(static_cast<uint16_t*>(a.dq) + tok, cv * kD * 2);
+    const __amdgpu_buffer_rsrc_t rdk = buffer_rsrc(static_cast<uint16_t*>(a.dx) + tok, cv * kD * 2);
+    const __amdgpu_buffer_rsrc_t rdv = buffer_rsrc(static_cast<uint16_t*>(a.dg) + tok, cv * kD * 2);
+    float rr = 0.f, pp = 0.f, de = 0.f;
 #pragma unroll
-    for (int w = 0; w < 8; ++w) c0 += L.c0[w];
-    const float ppl = L.pp[0][lane] + L.pp[1][lane];
-    const float rr_r = L.rr[0][ir] + L.rr[1][ir];
-    const float del = L.de[0][lane] + L.de[1][lane];
-    const float da = dalpha_f(L.rc, L.qk, ppl, rr_r, c0, lane);
-    store4(buffer_rsrc(static_cast<float*>(a.dalpha_out) + bh * T + t0, cv * 4),
-           static_cast<uint32_t>(lane * 4), da);
-    store4(buffer_rsrc(static_cast<float*>(a.deta_out) + bh * T + t0, cv * 4),
-           static_cast<uint32_t>(lane * 4), del);
+    for (int h2 = 0; h2 < 2; ++h2) {
+      __builtin_amdgcn_sched_barrier(0);  // one column block's fragments live at a time
+      const int cb = 2 * hf + h2;
+      const uint32_t so = static_cast<uint32_t>((ti * kD + cb * 16 + 4 * g4) * 2);
+      // dq^T: W0'^T dy + e(lq) D_in^T dy + (Be K)^T
+      f32x4 aq = zero4(), sq = zero4();
+#pragma unroll
+      for (int kr = 0; kr < 2; ++kr) {
+        const bf16x8 dyf = frag_s<kD>(L.DY, o, tb * 16, kr * 32);
+        const bf16x8 wf = a.w0_t ? frag_s<kD>(L.W, o, cb * 16, kr * 32)
+                                 : frag_ts<kD>(L.W, o, kr * 32, cb * 16);
+        aq = mfma16x16x32(wf, dyf, aq);
+        sq = mfma16x16x32(frag_ts<kD>(L.S, o, kr * 32, cb * 16), dyf, sq);
+      }
+#pragma unroll
+      for (int kj = 0; kj < 2; ++kj)
+        aq = mfma16x16x32(frag_ts<kD>(L.K, o, kj * 32, cb * 16),
+                          frag_ts<kCk>(L.BT, o64, kj * 32, tb * 16), aq);
+      const f32x4 qv = unpack4f(get4<kD>(L.Q, o, tb * 16, cb * 16));  // q_t[k], k = cb 16 + 4 g4 ..
+      rr += dot4f(qv, sq);
+      store8(rdq, so, pack4f(aq + eqi * sq));
+      __builtin_amdgcn_sched_barrier(0);
+      // dk^T: (Be^T Q)^T - eta e(l_last - l) (A_out^T v)^T
+      f32x4 ak = zero4(), sk = zero4();
+#pragma unroll
+      for (int ku = 0; ku < 2; ++ku)
+        ak = mfma16x16x32(frag_ts<kD>(L.Q, o, ku * 32, cb * 16),
+                          frag_s<kCk>(L.BT, o64, tb * 16, ku * 32), ak);
+#pragma unroll
+      for (int kr = 0; kr < 2; ++kr)
+        sk = mfma16x16x32(frag_ts<kD>(L.A, o, kr * 32, cb * 16), frag_s<kD>(L.V, o, tb * 16, kr * 32),
+                          sk);
+      store8(rdk, so, pack4f(ak + (nbi * e2i) * sk));
+      __builtin_amdgcn_sched_barrier(0);
+      // u^T: e(l_last - l) (A_out k)^T + (P^T dy)^T;  dv = -eta u
+      f32x4 au = zero4(), su = zero4();
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+        su = mfma16x16x32(frag_s<kD>(L.A, o, cb * 16, kk * 32), frag_s<kD>(L.K, o, tb * 16, kk * 32),
+                          su);
+#pragma unroll
+      for (int ku = 0; ku < 2; ++ku)
+        au = mfma16x16x32(frag_ts<kD>(L.DY, o, ku * 32, cb * 16),
+                          frag_s<kCk>(L.PT, o64, tb * 16, ku * 32), au);
+      const f32x4 u = au + e2i * su;
+      const f32x4 vv = unpack4f(get4<kD>(L.V, o, tb * 16, cb * 16));  // v_t[r], r = cb 16 + 4 g4 ..
+      de -= dot4f(vv, u);
+      pp += dot4f(vv, su);
+      store8(rdv, so, pack4f(nbi * u));
+    }
+    // shares over this wave's 32 columns: sum over the four lane groups
+    rr = sum_rows(rr);
+    pp = sum_rows(pp);
+    de = sum_rows(de);
+    if (g4 == 0) {
+      L.rr[hf][ti] = rr;
+      L.pp[hf][ti] = pp;
+      L.de[hf][ti] = de;
+    }
+    // ---- the adjoint entering this chunk, which leaves the one before it:
+    // A <- e(l_last) A + sum_u e(lq_u) dy_u q_u^T (this wave's two blocks;
+    // operands swapped, so the product comes out in A's register layout)
+    __builtin_amdgcn_sched_barrier(0);
+    {
+      const float gam = L.rc.gam;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int b = 2 * wave + i, rb = b >> 2, cb = b & 3;
+        f32x4 vi = zero4();
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const f32x4 e0 = *reinterpret_cast<const f32x4*>(&L.rc.eq[kb * 32 + 8 * g4]);
+          const f32x4 e1 = *reinterpret_cast<const f32x4*>(&L.rc.eq[kb * 32 + 8 * g4 + 4]);
+          vi = mfma16x16x32(scale8(frag_ts<kD>(L.Q, o, kb * 32, cb * 16), e0, e1),
+                            frag_ts<kD>(L.DY, o, kb * 32, rb * 16), vi);
+        }
+        A[i] = gam * A[i] + vi;
+      }
+    }
+    __syncthreads();
+
+    // ---- dalpha and deta of the chunk (wave 0, lane = token)
+    if (wave == 0) {
+      const int ir = kCk - 1 - lane;
+      float c0 = 0.f;
+#pragma unroll
+      for (int w = 0; w < 8; ++w) c0 += L.c0[w];
+      const float ppl = L.pp[0][lane] + L.pp[1][lane];
+      const float rr_r = L.rr[0][ir] + L.rr[1][ir];
+      const float del = L.de[0][lane] + L.de[1][lane];
+      const float da = dalpha_f(L.rc, L.qk, ppl, rr_r, c0, lane);
+      store4(buffer_rsrc(static_cast<float*>(a.dalpha_out) + bh * T + t0, cv * 4),
+             static_cast<uint32_t>(lane * 4), da);
+      store4(buffer_rsrc(static_cast<float*>(a.deta_out) + bh * T + t0, cv * 4),
+             static_cast<uint32_t>(lane * 4), del);
+    }
   }
 }
 
@@ -370,12 +451,12 @@ __global__ __launch_bounds__(kNG) void qkv_bwd_chunk(BwdArgs a) {
 
 bool mfma_qkv_bwd_ok(int io, int dk, int dv) { return io == IO_BF16 && dk == kD && dv == kD; }
 
-int mfma_qkv_bwd_groups(int n_chunks) { return (n_chunks + kInc - 1) / kInc; }
+int mfma_qkv_bwd_groups(int n_chunks) { return (n_chunks + kGrp - 1) / kGrp; }
 
 // a: x = k (write key), g = v, q the read vector; dx <- dk, dg <- dv, dq;
-// states (bf16 [BH][n][64][64]), mf_lam (bf16 [BH][n][64][64]), mf_gam
-// (fp32 [BH][n]), part_dW0 (fp32 [groups][BH][64][64]) in the workspace;
-// deta_out / dalpha_out.
+// in the workspace: states (bf16 [BH][n][64][64]), mf_lam (fp32
+// [BH][groups][64][64]), mf_gam (fp32 [BH][groups]), part_dW0 (fp32
+// [groups][BH][64][64]); deta_out / dalpha_out.
 hipError_t launch_mfma_qkv_bwd(const BwdArgs& a, hipStream_t s) {
   const int64_t BH = a.B * a.H;
   const int n = a.n_chunks;
@@ -390,16 +471,17 @@ hipError_t launch_mfma_qkv_bwd(const BwdArgs& a, hipStream_t s) {
   hipError_t e = launch_mfma_fwd(f, s);
   if (e != hipSuccess) return e;
   const int n_grp = mfma_qkv_bwd_groups(n);
-  hipLaunchKernelGGL(qkv_bwd_inc, dim3(static_cast<unsigned>(BH * n_grp)), dim3(kNI), 0, s, a,
-                     n_grp);
+  const dim3 grid(static_cast<unsigned>(BH * n_grp));
+  hipLaunchKernelGGL(qkv_bwd_inc, grid, dim3(kNI), 0, s, a, n_grp);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   constexpr int n_eb = kD * kD / 4 / kCarryT;
-  hipLaunchKernelGGL(qkv_lam_carry, dim3(static_cast<unsigned>(BH * n_eb)), dim3(kCarryT), 0, s,
-                     static_cast<uint16_t*>(a.mf_lam), static_cast<const float*>(a.mf_gam), n, n_eb);
+  hipLaunchKernelGGL(qkv_grp_carry, dim3(static_cast<unsigned>(BH * n_eb)), dim3(kCarryT), 0, s,
+                     static_cast<float*>(a.mf_lam), static_cast<const float*>(a.mf_gam), n_grp,
+                     n_eb);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(qkv_bwd_chunk, dim3(static_cast<unsigned>(BH * n)), dim3(kNG), 0, s, a);
+  hipLaunchKernelGGL(qkv_bwd_chunk, grid, dim3(kNG), 0, s, a, n_grp);
   return hipGetLastError();
 }
 
