@@ -488,7 +488,7 @@ def qkv_bwd_main(args, w):
     io = {"f64": 0, "f32": 1, "bf16": 2}[w.dtype]
     flags = ws.GL_FLAG_GENERIC if args.generic else 0
     desc = ws.make_desc(w.B, w.H, w.T, w.d_out, w.d_in, io, flags=flags)
-    on_mfma = w.dtype == "bf16" and w.d_in == w.d_out == 64 and not args.generic
+    on_mfma = w.dtype == "bf16" and w.d_in == w.d_out and w.d_in in (64, 128) and not args.generic
     n = ctypes.c_size_t()
     ws._check(ws.lib().gl_scan_qkv_workspace_size(ctypes.byref(desc), ctypes.byref(n)))
     wsb = torch.empty(max(n.value, 16), dtype=torch.uint8, device=dev)
@@ -541,8 +541,9 @@ def qkv_bwd_main(args, w):
         roof = {"bound": "hbm", "achieved": nbytes / 1e9 / (ms / 1e3), "peak": PEAK_HBM / 1e9,
                 "unit": "GB/s", "traffic": None, "algorithmic_bytes": nbytes,
                 "algorithmic_flops": nflops,
-                "kernel": "fwd_mfma<64> state pass + qkv_bwd_inc + mf_carry + qkv_bwd_chunk + "
-                          "finalize_kernel (whole reverse pass)"}
+                "kernel": f"fwd_mfma<{w.d_in}> state pass + qkv_bwd_inc<{w.d_in}> + "
+                          f"qkv_grp_carry + qkv_bwd_chunk<{w.d_in}> + finalize_kernel "
+                          "(whole reverse pass)"}
     else:
         # the vector-ALU kernels: the binding peak is the fp32 (fp64) vector rate
         roof = {"bound": "alu", "achieved": nflops / 1e12 / (ms / 1e3),

@@ -221,21 +221,28 @@ def test_qkv_bwd_parity(io, B, H, T, dk, dv, w0t):
     assert not bad, errs
 
 
-@pytest.mark.parametrize("B,H,T,w0t", [
-    (1, 2, 200, False),      # three full chunks and a ragged one
-    (2, 1, 129, True),       # one token past two chunks; W0 given transposed
-    (1, 1, 64, False),       # exactly one chunk
-    (1, 3, 1, True),
-    (3, 2, 320, True),       # five full chunks
+@pytest.mark.parametrize("d,B,H,T,w0t", [
+    (64, 1, 2, 200, False),       # three full chunks and a ragged one
+    (64, 2, 1, 129, True),        # one token past two chunks; W0 given transposed
+    (64, 1, 1, 64, False),        # exactly one chunk
+    (64, 1, 3, 1, True),
+    (64, 3, 2, 320, True),        # five full chunks
+    (64, 1, 1, 1100, False),      # 18 chunks: three groups of eight, the last ragged
+    (128, 1, 2, 200, False),      # W0 transposed by the library
+    (128, 2, 1, 129, True),
+    (128, 1, 1, 64, True),
+    (128, 1, 2, 1, False),
+    (128, 1, 1, 1100, True),
 ])
-def test_qkv_bwd_bf16_on_the_matrix_cores(B, H, T, w0t):
-    # bf16 with dk = dv = 64 takes the chunk-parallel matrix-core reverse scan;
-    # against the oracle, and against the vector kernels (GL_FLAG_GENERIC)
-    say(f"qkv backward matrix cores B={B} H={H} T={T} w0t={w0t}")
-    w = Workload("qkvb", B, H, T, 64, 64, "bf16", "mix", "gauss", 2100 + T)
+def test_qkv_bwd_bf16_on_the_matrix_cores(d, B, H, T, w0t):
+    # bf16 with dk = dv in {64, 128} takes the chunk-parallel matrix-core
+    # reverse scan; against the oracle, and against the vector kernels
+    # (GL_FLAG_GENERIC)
+    say(f"qkv backward matrix cores d={d} B={B} H={H} T={T} w0t={w0t}")
+    w = Workload("qkvb", B, H, T, d, d, "bf16", "mix", "gauss", 2100 + T + d)
     inp = make_inputs(w)
     rng = np.random.default_rng(2150 + T)
-    q = round_to(rng.standard_normal(inp["x"].shape) / 8.0, "bf16")
+    q = round_to(rng.standard_normal(inp["x"].shape) / np.sqrt(d), "bf16")
     W0p = inp["W0"]
     W0g = np.ascontiguousarray(W0p.transpose(0, 2, 1)) if w0t else W0p
     dev = to_device(inp, "bf16")
@@ -256,10 +263,11 @@ def test_qkv_bwd_bf16_on_the_matrix_cores(B, H, T, w0t):
     assert all(e <= TOL["bf16"] for e in errg.values()), errg
 
 
-def test_qkv_bwd_transpose_read_full_size_sampled():
-    # the transpose read's reverse scan at the 340M-model shape, every head on
-    # the GPU, two heads and one head's dW0 against the oracle
-    w = CONFIGS["c3"]
+@pytest.mark.parametrize("cfg", ["c3", "c4"])
+def test_qkv_bwd_transpose_read_full_size_sampled(cfg):
+    # the transpose read's reverse scan at the 340M- and 1.3B-model shapes,
+    # every head on the GPU, two heads against the oracle
+    w = CONFIGS[cfg]
     say(f"qkv backward full size {w}")
     inp = make_inputs(w)
     dev = to_device(inp, w.dtype)
@@ -270,7 +278,7 @@ def test_qkv_bwd_transpose_read_full_size_sampled():
     got = ws.gl_scan_qkv_bwd(dev["dy"], dev["g"], dev["x"], dev["eta"], dev["alpha"], dev["W0"],
                              dzd, w0_transposed=True)
     got = [host(t) for t in got]
-    for b, h in ((0, 0), (7, 15)):
+    for b, h in ((0, 0), (w.B - 1, w.H - 1)):
         sl = lambda a: a[b:b + 1, h:h + 1]  # noqa: E731
         want = oracle.qkv_bwd(sl(inp["dy"]), sl(inp["g"]), sl(inp["x"]), sl(inp["eta"]),
                               sl(inp["alpha"]), inp["W0"][h:h + 1].transpose(0, 2, 1), sl(dz))

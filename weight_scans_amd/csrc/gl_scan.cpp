@@ -631,7 +631,7 @@ struct QkvPlan {
   // a dW0' share (dw); part is unused
   bool mfma = false;
   int n_grp = 0;
-  size_t lam = 0, gam = 0;
+  size_t lam = 0, gam = 0, w0t = 0;  // w0t: W0' transposed (d = 128, bf16)
 };
 gl_status_t qkv_plan(const gl_scan_desc_t* d, QkvPlan* p) {
   gl_status_t st = check_dec(d, true);
@@ -653,7 +653,8 @@ gl_status_t qkv_plan(const gl_scan_desc_t* d, QkvPlan* p) {
     p->lam = round_up(groups * dd * sizeof(float));
     p->gam = round_up(groups * sizeof(float));
     p->dw = round_up(BH * static_cast<size_t>(p->n_grp) * dd * sizeof(float));
-    p->total = p->states + p->lam + p->gam + p->dw;
+    p->w0t = d->d_in == 128 ? round_up(static_cast<size_t>(d->H) * dd * 2) : 0;
+    p->total = p->states + p->lam + p->gam + p->dw + p->w0t;
     return GL_SUCCESS;
   }
   p->chunk = d->io_dtype == GL_DTYPE_F64 ? 8 : 32;  // LDS of the generic kernels with a read tile
@@ -707,9 +708,10 @@ gl_status_t gl_scan_qkv_bwd(const gl_scan_desc_t* desc, const void* q, const voi
     b.mf_lam = w + p.states;
     b.mf_gam = w + p.states + p.lam;
     b.part_dW0 = w + p.states + p.lam + p.gam;
+    b.W0t = p.w0t ? w + p.states + p.lam + p.gam + p.dw : nullptr;
     b.deta_out = deta; b.dalpha_out = dalpha;
     b.B = desc->B; b.H = desc->H; b.T = desc->T;
-    b.d_in = 64; b.d_out = 64;
+    b.d_in = static_cast<int>(desc->d_in); b.d_out = b.d_in;
     b.chunk = p.chunk; b.n_chunks = p.n_chunks; b.ckpt_every = 1; b.n_ckpt = p.n_chunks;
     b.n_tiles = 1;
     b.seg_chunks = p.n_chunks; b.n_seg = 1;
@@ -720,7 +722,7 @@ gl_status_t gl_scan_qkv_bwd(const gl_scan_desc_t* desc, const void* q, const voi
     fa.part_eta = nullptr; fa.part_alpha = nullptr; fa.part_dW0 = b.part_dW0;
     fa.deta = deta; fa.dalpha = dalpha; fa.dW0 = dW0;
     fa.B = desc->B; fa.H = desc->H; fa.T = desc->T;
-    fa.d_in = 64; fa.d_out = 64; fa.n_tiles = 1; fa.n_seg = p.n_grp;
+    fa.d_in = b.d_in; fa.d_out = b.d_in; fa.n_tiles = 1; fa.n_seg = p.n_grp;
     fa.alpha_done = true;
     fa.eta_done = true;
     return hip_status(gls::launch_finalize(desc->io_dtype, fa, s), "qkv finalize launch");

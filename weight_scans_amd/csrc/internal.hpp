@@ -87,6 +87,9 @@ struct BwdArgs {
   void* dq = nullptr;
   bool w0_t = false;
   bool out_f32 = false;   // dx, dg (and dq) in fp32 (bf16 io only)
+  // The write-key reverse scan on the matrix cores at d = 128: room for W0'
+  // transposed ([H][dk][dv] bf16) when it is not given so
+  const void* W0t = nullptr;
   // fp32 / fp64 matrix-core scans: the adjoint leaving every chunk
   // [B*H][n_chunks][d_out][d_in] and the per-chunk decay [B*H][n_chunks]
   // (compute type); part_dW0 then holds [n_chunks][B*H][d_out][d_in]
@@ -189,9 +192,10 @@ hipError_t launch_mfma_qkv_fwd(const FwdArgs& a, hipStream_t s);  // read tile o
 bool mfma_qkv_two_pass(int io, int dk, int dv);
 size_t mfma_qkv_states_bytes(int64_t BH, int64_t T);
 hipError_t launch_mfma_qkv_two_pass(const FwdArgs& a, hipStream_t s);
-// the reverse scan of the write-key scan at d_k = d_v = 64 (bf16): states,
-// adjoint increments, carry scan, chunk gradients (x = k, g = v; dx <- dk,
-// dg <- dv; states / mf_lam / mf_gam / part_dW0 in the workspace)
+// the reverse scan of the write-key scan at d_k = d_v in {64, 128} (bf16):
+// states, group increments, carry over groups, chunk gradients (x = k,
+// g = v; dx <- dk, dg <- dv; states / mf_lam / mf_gam / part_dW0 / W0t in
+// the workspace)
 bool mfma_qkv_bwd_ok(int io, int dk, int dv);
 int mfma_qkv_bwd_groups(int n_chunks);  // dW0' shares per sequence-head
 hipError_t launch_mfma_qkv_bwd(const BwdArgs& a, hipStream_t s);

@@ -1,6 +1,6 @@
 // k_qkv_bwd_mfma.hip -- the reverse scan of the scan with a read vector and a
-// write key of their own on the matrix cores, bf16 io, d_k = d_v = 64
-// (gfx950, v_mfma_f32_16x16x32_bf16).
+// write key of their own on the matrix cores, bf16 io, d_k = d_v = D in
+// {64, 128} (gfx950, v_mfma_f32_16x16x32_bf16).
 //
 //   y_t = (W0' + D_t) q_t,   D_{t+1} = alpha_t D_t - eta_t v_t k_t^T
 // and its exact adjoint for L = sum_t <dy_t, y_t> (the recurrence is affine
@@ -31,7 +31,10 @@
 // qkv_bwd_chunk walks the chunks of its group from right to left carrying
 // the adjoint in fp32 registers (A_in = e(l_last) A_out + sum_u e(lq_u)
 // dy_u q_u^T) and forms every chunk's gradients from its tiles and the two
-// carries; the finalize kernel sums the dW0' shares in a fixed order.
+// carries; the finalize kernel sums the dW0' shares in a fixed order.  At
+// D = 128 with W0' not given transposed, a small kernel first writes W0'
+// transposed into the workspace (the gradient kernel reads its fragments
+// from there).
 #include <algorithm>
 #include <cstdint>
 
@@ -40,30 +43,37 @@
 namespace gls {
 namespace {
 
-constexpr int kD = 64;    // d_k = d_v
 constexpr int kCk = 64;   // tokens per chunk
-constexpr int kNI = 256;  // threads of the increment kernel (four waves)
-constexpr int kNG = 512;  // threads of the gradient kernel (eight waves)
+constexpr int kGrp = 8;   // chunks per group (one work-group of each kind)
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-// 16-byte unit u (8 per row) of a [rows][64] bf16 tile: its swizzled LDS offset in bytes.
-__device__ __forceinline__ uint32_t unit64(int u) {
-  return static_cast<uint32_t>(sidx<kD>(u >> 3, 8 * (u & 7)) * 2);
+// 16-byte unit u (D / 8 per row) of a [rows][D] bf16 tile: its swizzled LDS
+// offset in bytes.
+template <int D>
+__device__ __forceinline__ uint32_t unit_off(int u) {
+  return static_cast<uint32_t>(sidx<D>(u / (D / 8), 8 * (u % (D / 8))) * 2);
+}
+template <int D>
+__device__ __forceinline__ void put_unit(__bf16* tile, int u, const u32x4& v) {
+  *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(tile) + unit_off<D>(u)) = v;
 }
 
-constexpr int kGrp = 8;  // chunks per group (one work-group of each kind)
-
 // ---- adjoint increment, decay and dW0' share of every group ----
-// Work-group (bh, group) walks the chunks of its group in order; the loads
-// of the next chunk are in flight while the current one is multiplied.
+// Work-group (bh, group), D / 16 waves (wave w: rows 16 w .. of the
+// increment and of the dW0' share), walks the chunks of its group in order;
+// the loads of the next chunk are in flight while the current one is
+// multiplied.
+template <int D>
 struct alignas(16) IncLds {
-  __bf16 Q[kCk * kD], DY[kCk * kD];  // swizzled [token][64]
-  float eq[kCk];                     // e(L_{u-1}) from the group's start
+  __bf16 Q[kCk * D], DY[kCk * D];  // swizzled [token][D]
+  float eq[kCk];                   // e(L_{u-1}) from the group's start
 };
 
-__global__ __launch_bounds__(kNI) void qkv_bwd_inc(BwdArgs a, int n_grp) {
-  __shared__ IncLds L;
+template <int D>
+__global__ __launch_bounds__(4 * D) void qkv_bwd_inc(BwdArgs a, int n_grp) {
+  constexpr int NT = 4 * D, NB = D / 16;
+  __shared__ IncLds<D> L;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g4 = lane >> 4, l16 = lane & 15;
@@ -71,19 +81,19 @@ __global__ __launch_bounds__(kNI) void qkv_bwd_inc(BwdArgs a, int n_grp) {
   const int64_t bh = blockIdx.x / n_grp, BH = a.B * a.H;
   const int grp = static_cast<int>(blockIdx.x % n_grp);
   const int c_beg = grp * kGrp, c_end = std::min(n, c_beg + kGrp);
-  const int64_t T = a.T, dd = static_cast<int64_t>(kD) * kD;
-  const uint16_t* qb = static_cast<const uint16_t*>(a.q) + bh * T * kD;
-  const uint16_t* db = static_cast<const uint16_t*>(a.dy) + bh * T * kD;
-  u32x4 uq[2], ud[2];
+  const int64_t T = a.T, dd = static_cast<int64_t>(D) * D;
+  const uint16_t* qb = static_cast<const uint16_t*>(a.q) + bh * T * D;
+  const uint16_t* db = static_cast<const uint16_t*>(a.dy) + bh * T * D;
+  u32x4 uq[2], ud[2];  // 8 D units per tile, two per thread
   float al = 1.f;
   const auto fetch = [&](int c) {
     const int64_t t0 = static_cast<int64_t>(c) * kCk;
     const int cv = static_cast<int>(std::min<int64_t>(kCk, T - t0));
-    const __amdgpu_buffer_rsrc_t rq = buffer_rsrc(qb + t0 * kD, cv * kD * 2);
-    const __amdgpu_buffer_rsrc_t rd = buffer_rsrc(db + t0 * kD, cv * kD * 2);
+    const __amdgpu_buffer_rsrc_t rq = buffer_rsrc(qb + t0 * D, cv * D * 2);
+    const __amdgpu_buffer_rsrc_t rd = buffer_rsrc(db + t0 * D, cv * D * 2);
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      const uint32_t off = static_cast<uint32_t>((tid + kNI * j) * 16);
+      const uint32_t off = static_cast<uint32_t>((tid + NT * j) * 16);
       uq[j] = __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0);
       ud[j] = __builtin_amdgcn_raw_buffer_load_b128(rd, off, 0, 0);
     }
@@ -94,13 +104,13 @@ __global__ __launch_bounds__(kNI) void qkv_bwd_inc(BwdArgs a, int n_grp) {
     al = lane < cv ? x : 1.f;
   };
   fetch(c_beg);
-  const LaneOff<kD> o = lane_off<kD>(lane);
+  const LaneOff<D> o = lane_off<D>(lane);
   const int rb = wave;
   // accumulators in the transposed MFMA layout (operands swapped): lane
   // holds row r = rb 16 + l16, columns k = cb 16 + 4 g4 .. + 3
-  f32x4 w[4], v[4];
+  f32x4 w[NB], v[NB];
 #pragma unroll
-  for (int cb = 0; cb < 4; ++cb) w[cb] = v[cb] = zero4();
+  for (int cb = 0; cb < NB; ++cb) w[cb] = v[cb] = zero4();
   float lg = 0.f;  // log2 of the decay from the group's start to chunk c (wave 0)
   for (int c = c_beg; c < c_end; ++c) {
     __syncthreads();  // the previous chunk's fragment reads are done
@@ -111,20 +121,19 @@ __global__ __launch_bounds__(kNI) void qkv_bwd_inc(BwdArgs a, int n_grp) {
     }
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      const uint32_t lo = unit64(tid + kNI * j);
-      *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(L.Q) + lo) = uq[j];
-      *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(L.DY) + lo) = ud[j];
+      put_unit<D>(L.Q, tid + NT * j, uq[j]);
+      put_unit<D>(L.DY, tid + NT * j, ud[j]);
     }
     if (c + 1 < c_end) fetch(c + 1);
     __syncthreads();
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      const bf16x8 df = frag_ts<kD>(L.DY, o, kb * 32, rb * 16);
+      const bf16x8 df = frag_ts<D>(L.DY, o, kb * 32, rb * 16);
       const f32x4 e0 = *reinterpret_cast<const f32x4*>(&L.eq[kb * 32 + 8 * g4]);
       const f32x4 e1 = *reinterpret_cast<const f32x4*>(&L.eq[kb * 32 + 8 * g4 + 4]);
 #pragma unroll
-      for (int cb = 0; cb < 4; ++cb) {
-        const bf16x8 qf = frag_ts<kD>(L.Q, o, kb * 32, cb * 16);
+      for (int cb = 0; cb < NB; ++cb) {
+        const bf16x8 qf = frag_ts<D>(L.Q, o, kb * 32, cb * 16);
         w[cb] = mfma16x16x32(qf, df, w[cb]);
         v[cb] = mfma16x16x32(scale8(qf, e0, e1), df, v[cb]);
       }
@@ -135,19 +144,19 @@ __global__ __launch_bounds__(kNI) void qkv_bwd_inc(BwdArgs a, int n_grp) {
   if (grp > 0) {
     float* pv = static_cast<float*>(a.mf_lam) + (bh * n_grp + grp - 1) * dd;
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb)
-      *reinterpret_cast<f32x4*>(pv + r * kD + cb * 16 + 4 * g4) = v[cb];
+    for (int cb = 0; cb < NB; ++cb)
+      *reinterpret_cast<f32x4*>(pv + r * D + cb * 16 + 4 * g4) = v[cb];
   }
   if (tid == 0) static_cast<float*>(a.mf_gam)[bh * n_grp + grp] = fexp2(lg);
   float* pw = static_cast<float*>(a.part_dW0) + (static_cast<int64_t>(grp) * BH + bh) * dd;
 #pragma unroll
-  for (int cb = 0; cb < 4; ++cb) {
+  for (int cb = 0; cb < NB; ++cb) {
     const int k = cb * 16 + 4 * g4;
     if (a.w0_t) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) pw[(k + q) * kD + r] = w[cb][q];
+      for (int q = 0; q < 4; ++q) pw[(k + q) * D + r] = w[cb][q];
     } else {
-      *reinterpret_cast<f32x4*>(pw + r * kD + k) = w[cb];
+      *reinterpret_cast<f32x4*>(pw + r * D + k) = w[cb];
     }
   }
 }
@@ -160,11 +169,10 @@ constexpr int kCarryT = 256;  // threads per work-group; four elements per threa
 constexpr int kCarryG = 16;   // groups whose loads are issued together
 
 __global__ __launch_bounds__(kCarryT) void qkv_grp_carry(float* buf, const float* gam, int ng,
-                                                          int n_eb) {
+                                                          int dd, int n_eb) {
   const int64_t bh = blockIdx.x / n_eb;
-  const int e4 = static_cast<int>(blockIdx.x % n_eb) * kCarryT + threadIdx.x;  // < kD kD / 4
-  constexpr int64_t dd = static_cast<int64_t>(kD) * kD;
-  float* p = buf + bh * ng * dd + 4 * e4;
+  const int e4 = static_cast<int>(blockIdx.x % n_eb) * kCarryT + threadIdx.x;  // < dd / 4
+  float* p = buf + bh * ng * static_cast<int64_t>(dd) + 4 * e4;
   const float* gm = gam + bh * ng;
   f32x4 carry = zero4();
   for (int k0 = 0; k0 < ng; k0 += kCarryG) {
@@ -174,7 +182,7 @@ __global__ __launch_bounds__(kCarryT) void qkv_grp_carry(float* buf, const float
     for (int j = 0; j < kCarryG; ++j) {
       const int k = k0 + j, g = ng - 1 - k;
       const bool use = k >= 1 && k < ng;
-      inc[j] = use ? *reinterpret_cast<const f32x4*>(p + g * dd) : zero4();
+      inc[j] = use ? *reinterpret_cast<const f32x4*>(p + static_cast<int64_t>(g) * dd) : zero4();
       dec[j] = use ? gm[g + 1] : 0.f;
     }
 #pragma unroll
@@ -182,40 +190,49 @@ __global__ __launch_bounds__(kCarryT) void qkv_grp_carry(float* buf, const float
       const int k = k0 + j;
       if (k < ng) {
         carry = dec[j] * carry + inc[j];
-        *reinterpret_cast<f32x4*>(p + (ng - 1 - k) * dd) = carry;
+        *reinterpret_cast<f32x4*>(p + static_cast<int64_t>(ng - 1 - k) * dd) = carry;
       }
     }
   }
 }
 
+// ---- W0' transposed ([H][D][D], [r][k] -> [k][r]) for the d = 128
+// gradient kernel, which reads W0' fragments from global memory
+__global__ __launch_bounds__(256) void qkv_w0_transpose(const uint16_t* w, uint16_t* wt, int D,
+                                                         int64_t total) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= total) return;
+  const int64_t dd = static_cast<int64_t>(D) * D;
+  const int64_t h = i / dd, e = i % dd;
+  const int64_t k = e / D, r = e % D;  // output element [h][k][r]
+  wt[i] = w[h * dd + r * D + k];
+}
+
 // ---- the gradients of every chunk ----
-// Work-group (bh, group) walks the chunks of its group from right to left.
-// The adjoint A_out of the chunk at hand is kept in fp32 registers (wave w:
-// blocks 2w, 2w + 1 of the 16 x 16 blocks of A, rows r = 16 (b / 4) + l16,
-// columns 16 (b % 4) + 4 g4 .. + 3) and copied to LDS in bf16 for the
-// products; W0' is staged once; the tiles of the next chunk (q, k, v, dy,
-// D_in and the gate rows) are loaded into registers while the current one
-// is worked on.
+// Work-group (bh, group), D / 8 waves, walks the chunks of its group from
+// right to left.  The adjoint A_out of the chunk at hand is kept in fp32
+// registers (wave w: D / 32 of the 16 x 16 blocks of A, block b holding rows
+// r = 16 (b / (D / 16)) + l16, columns 16 (b % (D / 16)) + 4 g4 .. + 3) and
+// copied to LDS in bf16 for the products.  At D = 64 W0' is staged in LDS
+// once; at D = 128 (no LDS room left) its fragments are read from global
+// memory, from W0' stored [k][r].
+template <int D>
 struct alignas(16) GradLds {
-  __bf16 Q[kCk * kD], K[kCk * kD], V[kCk * kD], DY[kCk * kD];  // swizzled [token][64]
-  __bf16 S[kD * kD], A[kD * kD], W[kD * kD];  // D_in [r][k], A_out [r][k], W0' as stored
-  __bf16 PT[kCk * kCk], BT[kCk * kCk];        // PT[t][u] = P_ut, BT[j][t] = Be_tj
+  __bf16 Q[kCk * D], K[kCk * D], V[kCk * D], DY[kCk * D];  // swizzled [token][D]
+  __bf16 S[D * D], A[D * D];                 // D_in [r][k], A_out [r][k]
+  __bf16 W[D == 64 ? D * D : 8];             // W0' as stored (D = 64)
+  __bf16 PT[kCk * kCk], BT[kCk * kCk];       // PT[t][u] = P_ut, BT[j][t] = Be_tj
   RecF rc;
   QkF qk;
-  float pp[2][kCk], rr[2][kCk], de[2][kCk];   // shares over two column halves
-  float c0[8];
+  float pp[D / 32][kCk], rr[D / 32][kCk], de[D / 32][kCk];  // shares over column groups
+  float c0[D / 8];
 };
 
-// One chunk's global inputs as this thread holds them: 16 bytes of each
-// [64][64] bf16 tile (unit tid) and its lane's token's gates.
-struct GradIn {
-  u32x4 q, k, v, dy, s;
-  float eta, alpha;
-};
-
-__global__ __launch_bounds__(kNG) __attribute__((amdgpu_waves_per_eu(4, 4))) void qkv_bwd_chunk(
+template <int D>
+__global__ __launch_bounds__(8 * D) __attribute__((amdgpu_waves_per_eu(4, 4))) void qkv_bwd_chunk(
     BwdArgs a, int n_grp) {
-  __shared__ GradLds L;
+  constexpr int NT = 8 * D, NW = D / 8, NB = D / 16, NA = D / 32, KS = D / 32;
+  __shared__ GradLds<D> L;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g4 = lane >> 4, l16 = lane & 15;
@@ -225,96 +242,95 @@ __global__ __launch_bounds__(kNG) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
   const int c_beg = grp * kGrp, c_end = std::min(n, c_beg + kGrp);
   const int h = static_cast<int>(bh % a.H);
   const int64_t T = a.T;
-  const int64_t dd = static_cast<int64_t>(kD) * kD;
+  const int64_t dd = static_cast<int64_t>(D) * D;
   const uint32_t off = static_cast<uint32_t>(tid * 16);
-  const uint32_t lo = unit64(tid);
 
-  const auto fetch = [&](int c, GradIn& in) {
-    const int64_t t0 = static_cast<int64_t>(c) * kCk;
-    const int cv = static_cast<int>(std::min<int64_t>(kCk, T - t0));
-    const int64_t tok = (bh * T + t0) * kD;
-    const auto rs = [&](const void* base) {
-      return buffer_rsrc(static_cast<const uint16_t*>(base) + tok, cv * kD * 2);
-    };
-    in.q = __builtin_amdgcn_raw_buffer_load_b128(rs(a.q), off, 0, 0);
-    in.k = __builtin_amdgcn_raw_buffer_load_b128(rs(a.x), off, 0, 0);
-    in.v = __builtin_amdgcn_raw_buffer_load_b128(rs(a.g), off, 0, 0);
-    in.dy = __builtin_amdgcn_raw_buffer_load_b128(rs(a.dy), off, 0, 0);
-    in.s = __builtin_amdgcn_raw_buffer_load_b128(
-        buffer_rsrc(static_cast<const uint16_t*>(a.states) + (bh * n + c) * dd, kD * kD * 2), off,
-        0, 0);
-    // gates (every wave loads them; wave 0 uses them): zero past the end
-    const auto rg = [&](const void* base) {
-      return buffer_rsrc(static_cast<const float*>(base) + bh * T + t0, cv * 4);
-    };
-    const uint32_t go = static_cast<uint32_t>(lane * 4);
-    in.eta = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rg(a.eta), go, 0, 0));
-    const float al =
-        __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rg(a.alpha), go, 0, 0));
-    in.alpha = lane < cv ? al : 1.f;
-  };
-  GradIn in;
-  *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(L.W) + lo) =
-      *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.W0) + h * dd + 8 * tid);
+  if constexpr (D == 64)
+    put_unit<D>(L.W, tid,
+                *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.W0) + h * dd + 8 * tid));
+  // W0' stored [k][r] (D = 128): the given one if transposed, else the copy
+  const uint16_t* wt = static_cast<const uint16_t*>(a.w0_t ? a.W0 : a.W0t) + h * dd;
   // the adjoint leaving the group (zero for the last one)
-  f32x4 A[2];
+  f32x4 A[NA];
   {
     const float* pa = static_cast<const float*>(a.mf_lam) + (bh * n_grp + grp) * dd;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int b = 2 * wave + i;
-      A[i] = *reinterpret_cast<const f32x4*>(pa + ((b >> 2) * 16 + l16) * kD + (b & 3) * 16 +
+    for (int i = 0; i < NA; ++i) {
+      const int b = NA * wave + i;
+      A[i] = *reinterpret_cast<const f32x4*>(pa + ((b / NB) * 16 + l16) * D + (b % NB) * 16 +
                                              4 * g4);
     }
   }
 
-  const LaneOff<kD> o = lane_off<kD>(lane);
+  const LaneOff<D> o = lane_off<D>(lane);
   const LaneOff<kCk> o64 = lane_off<kCk>(lane);
   for (int c = c_end - 1; c >= c_beg; --c) {
     const int64_t t0 = static_cast<int64_t>(c) * kCk;
     const int cv = static_cast<int>(std::min<int64_t>(kCk, T - t0));
-    const int64_t tok = (bh * T + t0) * kD;
-    fetch(c, in);
-    __syncthreads();  // the previous chunk is done with every LDS array
-    if (wave == 0) gates_v(in.eta, in.alpha, L.rc, lane);
-    // P^T and Be^T start at zero (only the causal parts are written)
-    reinterpret_cast<u32x4*>(L.PT)[tid] = u32x4{0u, 0u, 0u, 0u};
-    reinterpret_cast<u32x4*>(L.BT)[tid] = u32x4{0u, 0u, 0u, 0u};
-    *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(L.Q) + lo) = in.q;
-    *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(L.K) + lo) = in.k;
-    *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(L.V) + lo) = in.v;
-    *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(L.DY) + lo) = in.dy;
-    *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(L.S) + lo) = in.s;
+    const int64_t tok = (bh * T + t0) * D;
+    // this chunk's tiles: one 16-byte unit per thread of q, k, v, dy
+    // (8 D units each) and D / 64 of D_in; its lane's gates
+    const auto rs = [&](const void* base) {
+      return buffer_rsrc(static_cast<const uint16_t*>(base) + tok, cv * D * 2);
+    };
+    const u32x4 uq = __builtin_amdgcn_raw_buffer_load_b128(rs(a.q), off, 0, 0);
+    const u32x4 uk = __builtin_amdgcn_raw_buffer_load_b128(rs(a.x), off, 0, 0);
+    const u32x4 uv = __builtin_amdgcn_raw_buffer_load_b128(rs(a.g), off, 0, 0);
+    const u32x4 ud = __builtin_amdgcn_raw_buffer_load_b128(rs(a.dy), off, 0, 0);
+    const __amdgpu_buffer_rsrc_t rst =
+        buffer_rsrc(static_cast<const uint16_t*>(a.states) + (bh * n + c) * dd, D * D * 2);
+    u32x4 us[D / 64];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int b = 2 * wave + i;
-      put4<kD>(L.A, o, (b >> 2) * 16, (b & 3) * 16, pack4f(A[i]));
+    for (int j = 0; j < D / 64; ++j)
+      us[j] = __builtin_amdgcn_raw_buffer_load_b128(rst, off + NT * 16 * j, 0, 0);
+    const uint32_t go = static_cast<uint32_t>(lane * 4);
+    const float eta_l = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+        buffer_rsrc(static_cast<const float*>(a.eta) + bh * T + t0, cv * 4), go, 0, 0));
+    const float al_l = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+        buffer_rsrc(static_cast<const float*>(a.alpha) + bh * T + t0, cv * 4), go, 0, 0));
+    __syncthreads();  // the previous chunk is done with every LDS array
+    if (wave == 0) gates_v(eta_l, lane < cv ? al_l : 1.f, L.rc, lane);
+    // P^T and Be^T start at zero (only the causal parts are written)
+    if (tid < kCk * kCk / 8) {
+      reinterpret_cast<u32x4*>(L.PT)[tid] = u32x4{0u, 0u, 0u, 0u};
+      reinterpret_cast<u32x4*>(L.BT)[tid] = u32x4{0u, 0u, 0u, 0u};
+    }
+    put_unit<D>(L.Q, tid, uq);
+    put_unit<D>(L.K, tid, uk);
+    put_unit<D>(L.V, tid, uv);
+    put_unit<D>(L.DY, tid, ud);
+#pragma unroll
+    for (int j = 0; j < D / 64; ++j) put_unit<D>(L.S, tid + NT * j, us[j]);
+#pragma unroll
+    for (int i = 0; i < NA; ++i) {
+      const int b = NA * wave + i;
+      put4<D>(L.A, o, (b / NB) * 16, (b % NB) * 16, pack4f(A[i]));
     }
     __syncthreads();
 
-    // <A_out, D_in> over this wave's two blocks (A_out in fp32)
+    // <A_out, D_in> over this wave's blocks (A_out in fp32)
     {
       float cp = 0.f;
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int b = 2 * wave + i;
-        cp += dot4f(A[i], unpack4f(get4<kD>(L.S, o, (b >> 2) * 16, (b & 3) * 16)));
+      for (int i = 0; i < NA; ++i) {
+        const int b = NA * wave + i;
+        cp += dot4f(A[i], unpack4f(get4<D>(L.S, o, (b / NB) * 16, (b % NB) * 16)));
       }
       cp = wave_sum(cp);
       if (lane == 0) L.c0[wave] = cp;
     }
-    // ---- causal blocks w and w + 8 of the ten: Q K^T and DY V^T, decayed;
-    // P and Be written transposed, the row / column sums of Be o (Q K^T)
-    for (int b = wave; b < 10; b += 8) {
+    // ---- causal blocks (ten): Q K^T and DY V^T, decayed; P and Be
+    // written transposed, the row / column sums of Be o (Q K^T)
+    for (int b = wave; b < 10; b += NW) {
       __builtin_amdgcn_sched_barrier(0);
       const int ib = tri_i(b), jb = tri_j(b);
       f32x4 qk = zero4(), dv = zero4();
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        qk = mfma16x16x32(frag_s<kD>(L.Q, o, ib * 16, kb * 32), frag_s<kD>(L.K, o, jb * 16, kb * 32),
+      for (int kb = 0; kb < KS; ++kb) {
+        qk = mfma16x16x32(frag_s<D>(L.Q, o, ib * 16, kb * 32), frag_s<D>(L.K, o, jb * 16, kb * 32),
                           qk);
-        dv = mfma16x16x32(frag_s<kD>(L.DY, o, ib * 16, kb * 32),
-                          frag_s<kD>(L.V, o, jb * 16, kb * 32), dv);
+        dv = mfma16x16x32(frag_s<D>(L.DY, o, ib * 16, kb * 32), frag_s<D>(L.V, o, jb * 16, kb * 32),
+                          dv);
       }
       const int col = jb * 16 + l16, r0 = ib * 16 + 4 * g4;
       const float lc = L.rc.li[col], nbc = L.rc.nb[col];
@@ -340,33 +356,41 @@ __global__ __launch_bounds__(kNG) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
 
     // ---- outputs, transposed (rows = columns of dq, dk, dv; columns =
     // tokens): token block tb = w % 4, column blocks cb = 2 (w / 4) + {0, 1}
-    const int tb = wave & 3, hf = wave >> 2;
+    const int tb = wave & 3, cg = wave >> 2;
     const int ti = tb * 16 + l16;  // this lane's token
     const float eqi = L.rc.eq[ti], e2i = L.rc.e2[ti], nbi = L.rc.nb[ti];
-    const __amdgpu_buffer_rsrc_t rdq = buffer_rsrc(static_cast<uint16_t*>(a.dq) + tok, cv * kD * 2);
-    const __amdgpu_buffer_rsrc_t rdk = buffer_rsrc(static_cast<uint16_t*>(a.dx) + tok, cv * kD * 2);
-    const __amdgpu_buffer_rsrc_t rdv = buffer_rsrc(static_cast<uint16_t*>(a.dg) + tok, cv * kD * 2);
+    const __amdgpu_buffer_rsrc_t rdq = buffer_rsrc(static_cast<uint16_t*>(a.dq) + tok, cv * D * 2);
+    const __amdgpu_buffer_rsrc_t rdk = buffer_rsrc(static_cast<uint16_t*>(a.dx) + tok, cv * D * 2);
+    const __amdgpu_buffer_rsrc_t rdv = buffer_rsrc(static_cast<uint16_t*>(a.dg) + tok, cv * D * 2);
     float rr = 0.f, pp = 0.f, de = 0.f;
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2) {
       __builtin_amdgcn_sched_barrier(0);  // one column block's fragments live at a time
-      const int cb = 2 * hf + h2;
-      const uint32_t so = static_cast<uint32_t>((ti * kD + cb * 16 + 4 * g4) * 2);
-      // dq^T: W0'^T dy + e(lq) D_in^T dy + (Be K)^T
+      const int cb = 2 * cg + h2;
+      const uint32_t so = static_cast<uint32_t>((ti * D + cb * 16 + 4 * g4) * 2);
+      // dq^T: (Be K)^T + W0'^T dy + e(lq) D_in^T dy (at D = 128 the W0'
+      // fragments come from global memory: issued first, used last)
+      bf16x8 wf[KS];
+#pragma unroll
+      for (int kr = 0; kr < KS; ++kr) {
+        if constexpr (D == 64)
+          wf[kr] = a.w0_t ? frag_s<D>(L.W, o, cb * 16, kr * 32) : frag_ts<D>(L.W, o, kr * 32, cb * 16);
+        else
+          wf[kr] = *reinterpret_cast<const bf16x8*>(wt + (cb * 16 + l16) * D + kr * 32 + 8 * g4);
+      }
       f32x4 aq = zero4(), sq = zero4();
 #pragma unroll
-      for (int kr = 0; kr < 2; ++kr) {
-        const bf16x8 dyf = frag_s<kD>(L.DY, o, tb * 16, kr * 32);
-        const bf16x8 wf = a.w0_t ? frag_s<kD>(L.W, o, cb * 16, kr * 32)
-                                 : frag_ts<kD>(L.W, o, kr * 32, cb * 16);
-        aq = mfma16x16x32(wf, dyf, aq);
-        sq = mfma16x16x32(frag_ts<kD>(L.S, o, kr * 32, cb * 16), dyf, sq);
-      }
+      for (int kr = 0; kr < KS; ++kr)
+        sq = mfma16x16x32(frag_ts<D>(L.S, o, kr * 32, cb * 16), frag_s<D>(L.DY, o, tb * 16, kr * 32),
+                          sq);
 #pragma unroll
       for (int kj = 0; kj < 2; ++kj)
-        aq = mfma16x16x32(frag_ts<kD>(L.K, o, kj * 32, cb * 16),
+        aq = mfma16x16x32(frag_ts<D>(L.K, o, kj * 32, cb * 16),
                           frag_ts<kCk>(L.BT, o64, kj * 32, tb * 16), aq);
-      const f32x4 qv = unpack4f(get4<kD>(L.Q, o, tb * 16, cb * 16));  // q_t[k], k = cb 16 + 4 g4 ..
+#pragma unroll
+      for (int kr = 0; kr < KS; ++kr)
+        aq = mfma16x16x32(wf[kr], frag_s<D>(L.DY, o, tb * 16, kr * 32), aq);
+      const f32x4 qv = unpack4f(get4<D>(L.Q, o, tb * 16, cb * 16));  // q_t[k], k = cb 16 + 4 g4 ..
       rr += dot4f(qv, sq);
       store8(rdq, so, pack4f(aq + eqi * sq));
       __builtin_amdgcn_sched_barrier(0);
@@ -374,26 +398,26 @@ __global__ __launch_bounds__(kNG) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
       f32x4 ak = zero4(), sk = zero4();
 #pragma unroll
       for (int ku = 0; ku < 2; ++ku)
-        ak = mfma16x16x32(frag_ts<kD>(L.Q, o, ku * 32, cb * 16),
+        ak = mfma16x16x32(frag_ts<D>(L.Q, o, ku * 32, cb * 16),
                           frag_s<kCk>(L.BT, o64, tb * 16, ku * 32), ak);
 #pragma unroll
-      for (int kr = 0; kr < 2; ++kr)
-        sk = mfma16x16x32(frag_ts<kD>(L.A, o, kr * 32, cb * 16), frag_s<kD>(L.V, o, tb * 16, kr * 32),
+      for (int kr = 0; kr < KS; ++kr)
+        sk = mfma16x16x32(frag_ts<D>(L.A, o, kr * 32, cb * 16), frag_s<D>(L.V, o, tb * 16, kr * 32),
                           sk);
       store8(rdk, so, pack4f(ak + (nbi * e2i) * sk));
       __builtin_amdgcn_sched_barrier(0);
       // u^T: e(l_last - l) (A_out k)^T + (P^T dy)^T;  dv = -eta u
       f32x4 au = zero4(), su = zero4();
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk)
-        su = mfma16x16x32(frag_s<kD>(L.A, o, cb * 16, kk * 32), frag_s<kD>(L.K, o, tb * 16, kk * 32),
+      for (int kk = 0; kk < KS; ++kk)
+        su = mfma16x16x32(frag_s<D>(L.A, o, cb * 16, kk * 32), frag_s<D>(L.K, o, tb * 16, kk * 32),
                           su);
 #pragma unroll
       for (int ku = 0; ku < 2; ++ku)
-        au = mfma16x16x32(frag_ts<kD>(L.DY, o, ku * 32, cb * 16),
+        au = mfma16x16x32(frag_ts<D>(L.DY, o, ku * 32, cb * 16),
                           frag_s<kCk>(L.PT, o64, tb * 16, ku * 32), au);
       const f32x4 u = au + e2i * su;
-      const f32x4 vv = unpack4f(get4<kD>(L.V, o, tb * 16, cb * 16));  // v_t[r], r = cb 16 + 4 g4 ..
+      const f32x4 vv = unpack4f(get4<D>(L.V, o, tb * 16, cb * 16));  // v_t[r], r = cb 16 + 4 g4 ..
       de -= dot4f(vv, u);
       pp += dot4f(vv, su);
       store8(rdv, so, pack4f(nbi * u));
@@ -403,26 +427,26 @@ __global__ __launch_bounds__(kNG) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
     pp = sum_rows(pp);
     de = sum_rows(de);
     if (g4 == 0) {
-      L.rr[hf][ti] = rr;
-      L.pp[hf][ti] = pp;
-      L.de[hf][ti] = de;
+      L.rr[cg][ti] = rr;
+      L.pp[cg][ti] = pp;
+      L.de[cg][ti] = de;
     }
     // ---- the adjoint entering this chunk, which leaves the one before it:
-    // A <- e(l_last) A + sum_u e(lq_u) dy_u q_u^T (this wave's two blocks;
+    // A <- e(l_last) A + sum_u e(lq_u) dy_u q_u^T (this wave's blocks;
     // operands swapped, so the product comes out in A's register layout)
     __builtin_amdgcn_sched_barrier(0);
     {
       const float gam = L.rc.gam;
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int b = 2 * wave + i, rb = b >> 2, cb = b & 3;
+      for (int i = 0; i < NA; ++i) {
+        const int b = NA * wave + i, rb = b / NB, cb = b % NB;
         f32x4 vi = zero4();
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
           const f32x4 e0 = *reinterpret_cast<const f32x4*>(&L.rc.eq[kb * 32 + 8 * g4]);
           const f32x4 e1 = *reinterpret_cast<const f32x4*>(&L.rc.eq[kb * 32 + 8 * g4 + 4]);
-          vi = mfma16x16x32(scale8(frag_ts<kD>(L.Q, o, kb * 32, cb * 16), e0, e1),
-                            frag_ts<kD>(L.DY, o, kb * 32, rb * 16), vi);
+          vi = mfma16x16x32(scale8(frag_ts<D>(L.Q, o, kb * 32, cb * 16), e0, e1),
+                            frag_ts<D>(L.DY, o, kb * 32, rb * 16), vi);
         }
         A[i] = gam * A[i] + vi;
       }
@@ -434,10 +458,14 @@ __global__ __launch_bounds__(kNG) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
       const int ir = kCk - 1 - lane;
       float c0 = 0.f;
 #pragma unroll
-      for (int w = 0; w < 8; ++w) c0 += L.c0[w];
-      const float ppl = L.pp[0][lane] + L.pp[1][lane];
-      const float rr_r = L.rr[0][ir] + L.rr[1][ir];
-      const float del = L.de[0][lane] + L.de[1][lane];
+      for (int w = 0; w < NW; ++w) c0 += L.c0[w];
+      float ppl = 0.f, rr_r = 0.f, del = 0.f;
+#pragma unroll
+      for (int j = 0; j < D / 32; ++j) {
+        ppl += L.pp[j][lane];
+        rr_r += L.rr[j][ir];
+        del += L.de[j][lane];
+      }
       const float da = dalpha_f(L.rc, L.qk, ppl, rr_r, c0, lane);
       store4(buffer_rsrc(static_cast<float*>(a.dalpha_out) + bh * T + t0, cv * 4),
              static_cast<uint32_t>(lane * 4), da);
@@ -447,42 +475,60 @@ __global__ __launch_bounds__(kNG) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
   }
 }
 
-}  // namespace
-
-bool mfma_qkv_bwd_ok(int io, int dk, int dv) { return io == IO_BF16 && dk == kD && dv == kD; }
-
-int mfma_qkv_bwd_groups(int n_chunks) { return (n_chunks + kGrp - 1) / kGrp; }
-
-// a: x = k (write key), g = v, q the read vector; dx <- dk, dg <- dv, dq;
-// in the workspace: states (bf16 [BH][n][64][64]), mf_lam (fp32
-// [BH][groups][64][64]), mf_gam (fp32 [BH][groups]), part_dW0 (fp32
-// [groups][BH][64][64]); deta_out / dalpha_out.
-hipError_t launch_mfma_qkv_bwd(const BwdArgs& a, hipStream_t s) {
+template <int D>
+hipError_t launch_d(const BwdArgs& a, hipStream_t s) {
   const int64_t BH = a.B * a.H;
   const int n = a.n_chunks;
-  if (BH * n == 0) return hipSuccess;
   FwdArgs f;  // chunk-start states of the write-key scan (x = k, g = v)
   f.x = a.x; f.g = a.g; f.eta = a.eta; f.alpha = a.alpha; f.W0 = a.W0;
   f.y = nullptr; f.states = const_cast<void*>(a.states);
   f.B = a.B; f.H = a.H; f.T = a.T;
-  f.d_in = kD; f.d_out = kD;
+  f.d_in = D; f.d_out = D;
   f.chunk = kCk; f.n_chunks = n; f.ckpt_every = 1; f.n_ckpt = n;
   f.seg_chunks = n; f.n_seg = 1;
   hipError_t e = launch_mfma_fwd(f, s);
   if (e != hipSuccess) return e;
+  if (D == 128 && !a.w0_t) {
+    const int64_t total = a.H * static_cast<int64_t>(D) * D;
+    hipLaunchKernelGGL(qkv_w0_transpose, dim3(static_cast<unsigned>((total + 255) / 256)),
+                       dim3(256), 0, s, static_cast<const uint16_t*>(a.W0),
+                       static_cast<uint16_t*>(const_cast<void*>(a.W0t)), D, total);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   const int n_grp = mfma_qkv_bwd_groups(n);
   const dim3 grid(static_cast<unsigned>(BH * n_grp));
-  hipLaunchKernelGGL(qkv_bwd_inc, grid, dim3(kNI), 0, s, a, n_grp);
+  hipLaunchKernelGGL(qkv_bwd_inc<D>, grid, dim3(4 * D), 0, s, a, n_grp);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  constexpr int n_eb = kD * kD / 4 / kCarryT;
+  const int n_eb = D * D / 4 / kCarryT;
   hipLaunchKernelGGL(qkv_grp_carry, dim3(static_cast<unsigned>(BH * n_eb)), dim3(kCarryT), 0, s,
                      static_cast<float*>(a.mf_lam), static_cast<const float*>(a.mf_gam), n_grp,
-                     n_eb);
+                     D * D, n_eb);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(qkv_bwd_chunk, grid, dim3(kNG), 0, s, a, n_grp);
+  hipLaunchKernelGGL(qkv_bwd_chunk<D>, grid, dim3(8 * D), 0, s, a, n_grp);
   return hipGetLastError();
+}
+
+}  // namespace
+
+bool mfma_qkv_bwd_ok(int io, int dk, int dv) {
+  return io == IO_BF16 && dk == dv && (dk == 64 || dk == 128);
+}
+
+int mfma_qkv_bwd_groups(int n_chunks) { return (n_chunks + kGrp - 1) / kGrp; }
+
+// a: x = k (write key), g = v, q the read vector; dx <- dk, dg <- dv, dq;
+// in the workspace: states (bf16 [BH][n][D][D]), mf_lam (fp32
+// [BH][groups][D][D]), mf_gam (fp32 [BH][groups]), part_dW0 (fp32
+// [groups][BH][D][D]) and, at D = 128 with W0' not given transposed, W0t
+// (bf16 [H][D][D]); deta_out / dalpha_out.
+hipError_t launch_mfma_qkv_bwd(const BwdArgs& a, hipStream_t s) {
+  if (a.d_in != a.d_out || (a.d_in != 64 && a.d_in != 128)) return hipErrorInvalidValue;
+  if (a.d_in == 128 && !a.w0_t && !a.W0t) return hipErrorInvalidValue;
+  if (a.B * a.H * a.n_chunks == 0) return hipSuccess;
+  return a.d_in == 64 ? launch_d<64>(a, s) : launch_d<128>(a, s);
 }
 
 }  // namespace gls
