@@ -255,12 +255,16 @@ def test_qkv_bwd_bf16_on_the_matrix_cores(d, B, H, T, w0t):
     want = list(oracle.qkv_bwd(q, inp["x"], inp["g"], inp["eta"], inp["alpha"], W0p, inp["dy"]))
     if w0t:
         want[5] = want[5].transpose(0, 2, 1)
+    from parity_util import error_stats, stats_ok
     names = ("dq", "dk", "dv", "deta", "dalpha", "dW0")
     errs = {n: relmax(host(gv), wv) for n, gv, wv in zip(names, got, want)}
     errg = {n: relmax(host(gv), host(hv)) for n, gv, hv in zip(names, got, gen)}
-    say(f"  vs oracle {errs}\n  vs vector kernels {errg}")
+    stats = {n: error_stats(host(gv), wv) for n, gv, wv in zip(names, got, want)}
+    say(f"  vs oracle {errs}\n  vs vector kernels {errg}\n  statistics {stats}")
     assert all(e <= TOL["bf16"] for e in errs.values()), errs
     assert all(e <= TOL["bf16"] for e in errg.values()), errg
+    # the scan's bf16 RMS / bias / slope bounds for every gradient
+    assert all(stats_ok(st) for st in stats.values()), stats
 
 
 @pytest.mark.parametrize("cfg", ["c3", "c4"])

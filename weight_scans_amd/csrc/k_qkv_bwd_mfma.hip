@@ -228,6 +228,29 @@ struct alignas(16) GradLds {
   float c0[D / 8];
 };
 
+// dalpha and deta of the chunk whose gates, sums and shares sit in L (wave
+// 0, lane = token): t0 its first token, cv its valid tokens.
+template <int D>
+__device__ __forceinline__ void chunk_gate_grads(const GradLds<D>& L, const BwdArgs& a, int64_t bh,
+                                                 int64_t t0, int cv, int lane) {
+  const int ir = kCk - 1 - lane;
+  float c0 = 0.f;
+#pragma unroll
+  for (int w = 0; w < D / 8; ++w) c0 += L.c0[w];
+  float ppl = 0.f, rr_r = 0.f, del = 0.f;
+#pragma unroll
+  for (int j = 0; j < D / 32; ++j) {
+    ppl += L.pp[j][lane];
+    rr_r += L.rr[j][ir];
+    del += L.de[j][lane];
+  }
+  const float da = dalpha_f(L.rc, L.qk, ppl, rr_r, c0, lane);
+  store4(buffer_rsrc(static_cast<float*>(a.dalpha_out) + bh * a.T + t0, cv * 4),
+         static_cast<uint32_t>(lane * 4), da);
+  store4(buffer_rsrc(static_cast<float*>(a.deta_out) + bh * a.T + t0, cv * 4),
+         static_cast<uint32_t>(lane * 4), del);
+}
+
 template <int D>
 __global__ __launch_bounds__(8 * D) __attribute__((amdgpu_waves_per_eu(4, 4))) void qkv_bwd_chunk(
     BwdArgs a, int n_grp) {
@@ -288,8 +311,17 @@ __global__ __launch_bounds__(8 * D) __attribute__((amdgpu_waves_per_eu(4, 4))) v
         buffer_rsrc(static_cast<const float*>(a.eta) + bh * T + t0, cv * 4), go, 0, 0));
     const float al_l = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
         buffer_rsrc(static_cast<const float*>(a.alpha) + bh * T + t0, cv * 4), go, 0, 0));
-    __syncthreads();  // the previous chunk is done with every LDS array
-    if (wave == 0) gates_v(eta_l, lane < cv ? al_l : 1.f, L.rc, lane);
+    __syncthreads();  // the previous chunk is done with every tile and share
+    if (wave == 0) {
+      // dalpha and deta of the previous chunk in walk order (the one to the
+      // right) from its gates, sums and shares, then this chunk's gates in
+      // their place (the other arrays are rewritten only after the next barrier)
+      if (c + 1 < c_end) {
+        const int64_t tp = t0 + kCk;
+        chunk_gate_grads<D>(L, a, bh, tp, static_cast<int>(std::min<int64_t>(kCk, T - tp)), lane);
+      }
+      gates_v(eta_l, lane < cv ? al_l : 1.f, L.rc, lane);
+    }
     // P^T and Be^T start at zero (only the causal parts are written)
     if (tid < kCk * kCk / 8) {
       reinterpret_cast<u32x4*>(L.PT)[tid] = u32x4{0u, 0u, 0u, 0u};
@@ -451,27 +483,12 @@ __global__ __launch_bounds__(8 * D) __attribute__((amdgpu_waves_per_eu(4, 4))) v
         A[i] = gam * A[i] + vi;
       }
     }
-    __syncthreads();
-
-    // ---- dalpha and deta of the chunk (wave 0, lane = token)
-    if (wave == 0) {
-      const int ir = kCk - 1 - lane;
-      float c0 = 0.f;
-#pragma unroll
-      for (int w = 0; w < NW; ++w) c0 += L.c0[w];
-      float ppl = 0.f, rr_r = 0.f, del = 0.f;
-#pragma unroll
-      for (int j = 0; j < D / 32; ++j) {
-        ppl += L.pp[j][lane];
-        rr_r += L.rr[j][ir];
-        del += L.de[j][lane];
-      }
-      const float da = dalpha_f(L.rc, L.qk, ppl, rr_r, c0, lane);
-      store4(buffer_rsrc(static_cast<float*>(a.dalpha_out) + bh * T + t0, cv * 4),
-             static_cast<uint32_t>(lane * 4), da);
-      store4(buffer_rsrc(static_cast<float*>(a.deta_out) + bh * T + t0, cv * 4),
-             static_cast<uint32_t>(lane * 4), del);
-    }
+  }
+  // dalpha and deta of the last chunk walked (the group's first)
+  __syncthreads();
+  if (wave == 0) {
+    const int64_t t0 = static_cast<int64_t>(c_beg) * kCk;
+    chunk_gate_grads<D>(L, a, bh, t0, static_cast<int>(std::min<int64_t>(kCk, T - t0)), lane);
   }
 }
 
