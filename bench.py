@@ -50,6 +50,20 @@ PEAK_MATRIX = {"bf16": 2.5e15, "f32": 157.3e12, "f64": 78.6e12}  # dense flop/s
 C0 = 64                                 # chunk length used to count flops
 
 
+
+def timing_events(steps, per_step, stream):
+    """HIP events for a timed loop, created before it: torch creates an
+    event's HIP handle on its first record(), and a creation that stalls the
+    host between two records (the runtime growing its event pool) would be
+    timed as GPU work.  Recording each once here forces the creation."""
+    import torch
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(per_step)] for _ in range(steps)]
+    for row in ev:
+        for e in row:
+            e.record(stream)
+    torch.cuda.synchronize()
+    return ev
+
 def algorithmic(w):
     """Bytes and flops per pass: every input read once, every output written
     once; flops of the chunked method at chunk C0."""
@@ -253,7 +267,7 @@ def decode_main(args, w):
 
     # tokens are issued back to back, as a serving loop does; one pair of
     # events brackets the timed tokens (events between kernels would add gaps)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0, e1 = timing_events(1, 2, stream)[0]
 
     def timed(body):
         for k in range(1, args.warmup + 1):
@@ -416,7 +430,7 @@ def costate_main(args, w):
 
     for _ in range(args.warmup):
         sweep()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    ev = timing_events(args.steps, 3, stream)
     torch.cuda.synchronize()
     for i in range(args.steps):
         if not args.no_flush:
@@ -514,8 +528,7 @@ def qkv_bwd_main(args, w):
         if not args.no_flush:
             flush_sink = torch.sum(flush)  # noqa: F841
         step()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
+    ev = timing_events(args.steps, 2, stream)
     for i in range(args.steps):
         if not args.no_flush:
             flush_sink = torch.sum(flush)  # noqa: F841
@@ -636,8 +649,7 @@ def qkv_main(args, w):
         if not args.no_flush:
             flush_sink = torch.sum(flush)  # noqa: F841
         step()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
+    ev = timing_events(args.steps, 2, stream)
     for i in range(args.steps):
         if not args.no_flush:
             flush_sink = torch.sum(flush)  # noqa: F841
@@ -805,8 +817,7 @@ def main():
         bwd()
     torch.cuda.synchronize()
 
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
-           torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    ev = timing_events(args.steps, 3, stream)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     for i in range(args.steps):
@@ -863,7 +874,8 @@ def main():
                    "parallelism": "single GPU"},
         "passes_ms": {"fwd_mean": mf, "bwd_mean": mb,
                       "fwd_median": med(tf), "fwd_min": min(tf), "fwd_max": max(tf),
-                      "bwd_median": med(tb), "bwd_min": min(tb), "bwd_max": max(tb)},
+                      "bwd_median": med(tb), "bwd_min": min(tb), "bwd_max": max(tb),
+                      "fwd_each": [round(x, 5) for x in tf], "bwd_each": [round(x, 5) for x in tb]},
         "tokens_per_s_median": tokens / ((med(tf) + med(tb)) / 1e3),
         # one step (fwd + bwd pass) end to end: the figure for latency-bound
         # workloads such as a single short sequence
