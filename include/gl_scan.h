@@ -275,12 +275,13 @@ gl_status_t gl_scan_qkv_fwd_ws(const gl_scan_desc_t* desc, const void* q, const 
  * dtype; dW0 [H][dv][dk] gate dtype, or [H][dk][dv] when w0_transposed != 0
  * (the layout W0 is passed in).  The chunk states of the forward are
  * recomputed inside the workspace `ws` of gl_scan_qkv_workspace_size bytes.
- * bf16 with dk = dv = 64 (without GL_FLAG_GENERIC) runs chunk-parallel on the
- * matrix cores: the forward's chunk-start states (bf16), then per group of
- * eight 64-token chunks the adjoint increment, decay and dW0 share, the
- * adjoint carry over groups (fp32), and the gradients of every chunk with
- * the adjoint walked right to left through its group; every pointer must
- * then be 16-byte aligned.  Every other case (and GL_FLAG_GENERIC) runs
+ * bf16 with dk = dv in {64, 128} (without GL_FLAG_GENERIC) runs
+ * chunk-parallel on the matrix cores: the forward's chunk-start states
+ * (bf16), then per group of eight 64-token chunks the adjoint increment,
+ * decay and dW0 share, the adjoint carry over groups (fp32), and the
+ * gradients of every chunk with the adjoint walked right to left through
+ * its group (at 128, with W0' not given transposed, a transposed copy of it
+ * in the workspace first); every pointer must then be 16-byte aligned.  Every other case (and GL_FLAG_GENERIC) runs
  * portable chunked VALU kernels, any 1 <= dk, dv <= 128 (chunk 32, F64: 8).
  * Same rules as gl_scan_bwd; B*H*T == 0 writes the zero dW0 only. */
 gl_status_t gl_scan_qkv_workspace_size(const gl_scan_desc_t* desc, size_t* ws_bytes);

@@ -289,3 +289,21 @@ def test_qkv_bwd_transpose_read_full_size_sampled(cfg):
         for n, gv, wv in zip(("dq", "dk", "dv", "deta", "dalpha"), got, want):
             err = relmax(gv[b, h], wv[0, 0])
             assert err <= TOL["bf16"], (b, h, n, err)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_qkv_bwd_matrix_cores_bitwise_repeatable(d):
+    # the chunk-parallel reverse scan sums in a fixed order (no atomics): two
+    # calls on the same inputs agree bit for bit, W0' plain and transposed
+    say(f"qkv backward determinism d={d}")
+    w = Workload("qkvd", 2, 2, 700, d, d, "bf16", "mix", "gauss", 2300 + d)
+    inp = make_inputs(w)
+    dev = to_device(inp, "bf16")
+    for w0t in (False, True):
+        W0 = dev["W0"].transpose(1, 2).contiguous() if w0t else dev["W0"]
+        args = (dev["dy"], dev["g"], dev["x"], dev["eta"], dev["alpha"], W0, dev["dy"])
+        first = ws.gl_scan_qkv_bwd(*args, w0_transposed=w0t)
+        second = ws.gl_scan_qkv_bwd(*args, w0_transposed=w0t)
+        torch.cuda.synchronize()
+        for n, a, b in zip(("dq", "dk", "dv", "deta", "dalpha", "dW0"), first, second):
+            assert torch.equal(a, b), (w0t, n)
