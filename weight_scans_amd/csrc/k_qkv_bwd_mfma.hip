@@ -218,14 +218,16 @@ __global__ __launch_bounds__(256) void qkv_w0_transpose(const uint16_t* w, uint1
 // memory, from W0' stored [k][r].
 template <int D>
 struct alignas(16) GradLds {
-  __bf16 Q[kCk * D], K[kCk * D], V[kCk * D], DY[kCk * D];  // swizzled [token][D]
-  __bf16 S[D * D], A[D * D];                 // D_in [r][k], A_out [r][k]
-  __bf16 W[D == 64 ? D * D : 8];             // W0' as stored (D = 64)
-  __bf16 PT[kCk * kCk], BT[kCk * kCk];       // PT[t][u] = P_ut, BT[j][t] = Be_tj
+  // the small per-chunk arrays first: their addresses stay within the 64 KB
+  // reach of the LDS instructions' offset field
   RecF rc;
   QkF qk;
   float pp[D / 32][kCk], rr[D / 32][kCk], de[D / 32][kCk];  // shares over column groups
   float c0[D / 8];
+  __bf16 PT[kCk * kCk], BT[kCk * kCk];       // PT[t][u] = P_ut, BT[j][t] = Be_tj
+  __bf16 Q[kCk * D], K[kCk * D], V[kCk * D], DY[kCk * D];  // swizzled [token][D]
+  __bf16 S[D * D], A[D * D];                 // D_in [r][k], A_out [r][k]
+  __bf16 W[D == 64 ? D * D : 8];             // W0' as stored (D = 64)
 };
 
 // dalpha and deta of the chunk whose gates, sums and shares sit in L (wave
@@ -285,9 +287,19 @@ __global__ __launch_bounds__(8 * D) __attribute__((amdgpu_waves_per_eu(4, 4))) v
     }
   }
 
-  const LaneOff<D> o = lane_off<D>(lane);
-  const LaneOff<kCk> o64 = lane_off<kCk>(lane);
+  LaneOff<D> o = lane_off<D>(lane);
+  LaneOff<kCk> o64 = lane_off<kCk>(lane);
   for (int c = c_end - 1; c >= c_beg; --c) {
+    if constexpr (D == 128) {
+      // Most of this kernel's LDS lies beyond the 64 KB reach of the LDS
+      // instructions' offset field, so each (array, column block) address
+      // needs a register of its own; hoisted out of the chunk loop they
+      // overflow the 128 registers of sixteen waves.  An empty asm on the
+      // lane offsets makes them new values every chunk: the addresses are
+      // formed where they are used instead.
+      asm volatile("" : "+v"(o.b), "+v"(o.t0), "+v"(o.t1), "+v"(o.w));
+      asm volatile("" : "+v"(o64.b), "+v"(o64.t0), "+v"(o64.t1), "+v"(o64.w));
+    }
     const int64_t t0 = static_cast<int64_t>(c) * kCk;
     const int cv = static_cast<int>(std::min<int64_t>(kCk, T - t0));
     const int64_t tok = (bh * T + t0) * D;
