@@ -671,7 +671,8 @@ def qkv_main(args, w):
         nbytes = (w.B * w.H * w.T * (e * (2 * w.d_out + 2 * w.d_in) + 8)
                   + w.H * w.d_in * w.d_out * e)
         kern = ("fwd_mfma<64> with a read tile of its own (chunked, matrix cores)" if w.d_in == 64
-                else "fwd_mfma<128> state pass + qkv_chunk (chunk-parallel outputs, matrix cores)")
+                else "fwd_mfma<128> state pass (a state per group of eight chunks) + qkv_group "
+                "(groups in parallel, each walked in order; matrix cores)")
         roof = {"bound": "hbm", "achieved": nbytes / 1e9 / (ms / 1e3), "peak": PEAK_HBM / 1e9,
                 "unit": "GB/s", "traffic": None, "algorithmic_bytes": nbytes, "kernel": kern}
     else:

@@ -245,16 +245,18 @@ gl_status_t gl_scan_qkv_fwd(const gl_scan_desc_t* desc, const void* q, const voi
                             const void* v, const void* eta, const void* alpha, const void* W0,
                             int w0_transposed, void* y, void* stream);
 
-/* Workspace bytes gl_scan_qkv_fwd_ws uses: the chunk-start states of the
- * write-key scan (bf16, B*H*ceil(T/64)*dv*dk elements) for bf16 with
- * dk = dv = 128 without GL_FLAG_GENERIC; 0 otherwise. */
+/* Workspace bytes gl_scan_qkv_fwd_ws uses: the state of the write-key scan
+ * entering every group of eight 64-token chunks (bf16,
+ * B*H*ceil(T/512)*dv*dk elements) for bf16 with dk = dv = 128 without
+ * GL_FLAG_GENERIC; 0 otherwise. */
 gl_status_t gl_scan_qkv_fwd_workspace_size(const gl_scan_desc_t* desc, size_t* ws_bytes);
 
 /* gl_scan_qkv_fwd with a caller workspace (ws_bytes from
  * gl_scan_qkv_fwd_workspace_size; ws may be NULL when that is 0).  For bf16
  * with dk = dv = 128 it runs in two launches on the matrix cores: the
- * forward scan's state-only pass writes the chunk-start states into ws, then
- * every chunk's outputs are formed from them in parallel.  A smaller
+ * forward scan's state-only pass writes the state entering every group of
+ * eight chunks into ws, then the groups' outputs are formed in parallel, each
+ * group walking its chunks in order with the state in registers.  A smaller
  * workspace returns GL_ERROR_WORKSPACE_TOO_SMALL before any launch.  Results
  * as gl_scan_qkv_fwd. */
 gl_status_t gl_scan_qkv_fwd_ws(const gl_scan_desc_t* desc, const void* q, const void* k,

@@ -277,13 +277,18 @@ def test_static_backward_refuses_a_workspace_beyond_its_scratch():
 
 
 def test_qkv_forward_workspace():
-    # bf16 at dk = dv = 128: the chunk-start states (bf16) in the caller's
-    # workspace; GL_FLAG_GENERIC and other shapes need none; a workspace below
-    # the figure is refused before any launch (fake device pointers)
+    # bf16 at dk = dv = 128: the state entering every group of eight 64-token
+    # chunks (bf16) in the caller's workspace; GL_FLAG_GENERIC and other
+    # shapes need none; a workspace below the figure is refused before any
+    # launch (fake device pointers)
     d = ws.make_desc(2, 3, 300, 128, 128, ws.GL_DTYPE_BF16)
     n = ctypes.c_size_t()
     assert ws.lib().gl_scan_qkv_fwd_workspace_size(ctypes.byref(d), ctypes.byref(n)) == 0
-    assert n.value >= 2 * 3 * 5 * 128 * 128 * 2
+    assert n.value >= 2 * 3 * 1 * 128 * 128 * 2
+    dl = ws.make_desc(2, 3, 4096, 128, 128, ws.GL_DTYPE_BF16)
+    nl = ctypes.c_size_t()
+    assert ws.lib().gl_scan_qkv_fwd_workspace_size(ctypes.byref(dl), ctypes.byref(nl)) == 0
+    assert nl.value >= 2 * 3 * 8 * 128 * 128 * 2
     for dd in (ws.make_desc(2, 3, 300, 128, 128, ws.GL_DTYPE_BF16, flags=ws.GL_FLAG_GENERIC),
                ws.make_desc(2, 3, 300, 64, 64, ws.GL_DTYPE_BF16),
                ws.make_desc(2, 3, 300, 128, 128, ws.GL_DTYPE_F32)):

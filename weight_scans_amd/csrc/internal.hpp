@@ -44,6 +44,9 @@ struct FwdArgs {
   bool out_f32 = false;
   // fp32 / fp64 matrix-core scans: [B*H][n_chunks] per-chunk decay (compute type)
   void* mf_gam = nullptr;
+  // bf16 matrix-core kernels: `states` keeps the chunk-start state of every
+  // st_every-th chunk only ([B*H][ceil(n_chunks / st_every)][d_out][d_in])
+  int st_every = 1;
 };
 
 // Reverse scan.  Work-group (k, b*H+h) owns column tile k of D and Lambda

@@ -356,7 +356,11 @@ __global__ __launch_bounds__(kNT) void fwd_mfma(FwdArgs a) {
   const uint16_t* W0 = static_cast<const uint16_t*>(a.W0) + static_cast<int64_t>(h) * D * D;
   constexpr int YE = F32 ? 4 : 2;  // bytes per element of y
   char* y = HAS_Y ? static_cast<char*>(a.y) + bh * T * D * YE : nullptr;
-  uint16_t* st = HAS_ST ? static_cast<uint16_t*>(a.states) + bh * static_cast<int64_t>(n) * D * D
+  // states: one per a.st_every chunks (the chunk-start state of chunks c with
+  // c % st_every == 0), ceil(n / st_every) per sequence-head
+  const int st_every = a.st_every;
+  const int n_st = (n + st_every - 1) / st_every;
+  uint16_t* st = HAS_ST ? static_cast<uint16_t*>(a.states) + bh * static_cast<int64_t>(n_st) * D * D
                         : nullptr;
 
   // y waves: W0 rows of this wave's row block as MFMA A fragments, in
@@ -485,8 +489,13 @@ __global__ __launch_bounds__(kNT) void fwd_mfma(FwdArgs a) {
       if (HAS_ST) {
         // chunk-start state (natural layout, bf16): the copy in LDS that the
         // y waves read in this step, whole rows per store instruction
+        // every chunk issues its store (the waits count a fixed number of
+        // memory operations per step); a chunk whose state is not kept
+        // stores into an empty buffer, which drops it
+        const bool keep = c % st_every == 0;
         const __amdgpu_buffer_rsrc_t r_st =
-            buffer_rsrc(st + static_cast<int64_t>(c) * D * D, D * D * 2);
+            buffer_rsrc(st + static_cast<int64_t>(keep ? c / st_every : 0) * D * D,
+                        keep ? D * D * 2 : 0);
         const char* sp = reinterpret_cast<const char*>(S_s[vl & 1]) + st_l;
         if constexpr (D == 128)
           store16(r_st, st_g, *reinterpret_cast<const uint4*>(sp));
