@@ -76,7 +76,7 @@ def test_qkv_with_equal_keys_is_the_forward_scan():
     assert relmax(host(y1), host(y2)) <= 1e-4
 
 
-@pytest.mark.parametrize("T", [1, 63, 65, 300])
+@pytest.mark.parametrize("T", [1, 63, 65, 300, 1100])  # 1100: groups of 8, 8 and 2 chunks
 @pytest.mark.parametrize("transposed", [True, False])
 @pytest.mark.parametrize("d", [64, 128])
 def test_bf16_on_the_matrix_cores(d, T, transposed):
