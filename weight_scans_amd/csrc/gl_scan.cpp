@@ -43,6 +43,8 @@ constexpr int kMinSegChunks = 16;
 // Above this many backward segments the entering adjoints are composed by one
 // combine launch rather than in every fused work-group's set-up.
 constexpr int kBwdCombineAbove = 4;
+// Chunks per segment of the adjoint-only pass, at least.
+constexpr int kLamMinChunks = 8;
 
 // Everything the launches need, derived from the descriptor alone so that the
 // forward and the backward agree on the layout of `saved`.
@@ -65,6 +67,8 @@ struct Plan {
   // work-group per segment and sequence-head), deta / dalpha written directly
   bool fused = false;
   int bwd_nseg = 1, bwd_seg_chunks = 0;
+  // the adjoint-only pass: lam_r of its segments per fused segment
+  int lam_r = 1, lam_n = 1, lam_seg_chunks = 0;
   size_t bwd_seg_bytes = 0, bwd_seg_state_bytes = 0;
   const char* name = "";
 };
@@ -160,9 +164,21 @@ gl_status_t make_plan(const gl_scan_desc_t* d, Plan* p) {
     nb = std::max(1, std::min(nb, p->n_chunks));
     p->bwd_seg_chunks = (p->n_chunks + nb - 1) / nb;
     p->bwd_nseg = (p->n_chunks + p->bwd_seg_chunks - 1) / p->bwd_seg_chunks;
+    // With few fused segments the adjoint-only pass (one work-group per
+    // segment and row tile, walking its chunks in order) would leave CUs
+    // idle; it runs on segments lam_r times finer instead, as long as every
+    // fused work-group still composes at most kBwdCombineAbove of them.
+    p->lam_r = 1;
+    if (p->bwd_nseg > 1 && p->bwd_nseg <= kBwdCombineAbove) {
+      int r = std::min(kBwdCombineAbove / (p->bwd_nseg - 1), p->bwd_seg_chunks / kLamMinChunks);
+      while (r > 1 && p->bwd_seg_chunks % r) --r;
+      p->lam_r = std::max(1, r);
+    }
+    p->lam_seg_chunks = p->bwd_seg_chunks / p->lam_r;
+    p->lam_n = (p->n_chunks + p->lam_seg_chunks - 1) / p->lam_seg_chunks;
     if (p->bwd_nseg > 1) {
-      p->bwd_seg_state_bytes = round_up(BH * p->bwd_nseg * dd * sizeof(float));
-      p->bwd_seg_bytes = p->bwd_seg_state_bytes + round_up(BH * p->bwd_nseg * sizeof(float));
+      p->bwd_seg_state_bytes = round_up(BH * p->lam_n * dd * sizeof(float));
+      p->bwd_seg_bytes = p->bwd_seg_state_bytes + round_up(BH * p->lam_n * sizeof(float));
     }
   }
   if (p->fused) p->part_bytes = 0;
@@ -396,8 +412,13 @@ gl_status_t gl_scan_bwd(const gl_scan_desc_t* desc, const void* x, const void* g
       gls::BwdArgs bs = bf;
       bs.seg_out = seg;
       bs.seg_lg = lg;
+      bs.seg_chunks = p.lam_seg_chunks;
+      bs.n_seg = p.lam_n;
+      bs.seg_first = p.lam_r;  // the segments inside fused segment 0 are never needed
       st = hip_status(gls::launch_mfma_bwd_lam(bs, s), "backward segment pass");
       bf.seg_lam = seg;
+      bf.lam_r = p.lam_r;
+      bf.lam_n = p.lam_n;
       if (p.bwd_nseg > kBwdCombineAbove) {
         // the adjoint entering every segment, composed from the right in one
         // launch (in its set-up a work-group would wait for one load per

@@ -81,6 +81,13 @@ struct BwdArgs {
   const float* seg_lg_in = nullptr;
   float* seg_out = nullptr;
   float* seg_lg = nullptr;
+  // The adjoint-only pass may cut the sequence finer than the fused pass:
+  // lam_r of its segments (lam_seg_chunks chunks each) per fused segment,
+  // lam_n of them in all; seg_lam / seg_lg_in / seg_out / seg_lg are then
+  // indexed by those segments ([B*H][lam_n]).  seg_first: the first segment
+  // the adjoint-only pass computes (the ones to its left are never needed).
+  int lam_r = 1, lam_n = 0;
+  int seg_first = 1;
   // Fused backward: deta and dalpha written directly ([B,H,T]).
   void* deta_out = nullptr;
   void* dalpha_out = nullptr;

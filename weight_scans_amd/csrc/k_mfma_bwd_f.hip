@@ -178,20 +178,37 @@ __global__ __launch_bounds__(kNT) void bwd_f64(BwdArgs a) {
 #pragma unroll
   for (int e = 0; e < 8; ++e) pr[e] = zero4();
   if (role == 1 && a.seg_lam) {
-    // adjoint entering from the right: given, or composed here from the
-    // segments to the right, nearest last: Lam <- 2^(lg_s) Lam + L_s
-    const int s_lo = a.seg_lg_in ? seg + 1 : seg;
-    const int s_hi = a.seg_lg_in ? a.n_seg - 1 : seg;
-    for (int s2 = s_hi; s2 >= s_lo; --s2) {
-      const float* sl = a.seg_lam + (bh * a.n_seg + s2) * kD * kD;
-      const float gs = a.seg_lg_in ? fexp2(a.seg_lg_in[bh * a.n_seg + s2]) : 0.f;
+    // adjoint entering from the right: given (the adjoint-only pass's
+    // segment ending where this one ends), or composed here from the
+    // adjoint-only pass's segments to the right, nearest last:
+    // Lam <- 2^(lg_s) Lam + L_s
+    const int ln = a.lam_n ? a.lam_n : a.n_seg, end = (seg + 1) * a.lam_r;
+    const int s_lo = a.seg_lg_in ? end : end - 1;
+    const int s_hi = a.seg_lg_in ? ln - 1 : end - 1;
+    // four segments at a time: their loads (from clamped, valid addresses)
+    // are all issued before the first is folded in
+    for (int s0 = s_hi; s0 >= s_lo; s0 -= 4) {
+      f32x4 t[4][4];
+      float gsv[4];
 #pragma unroll
-      for (int aa = 0; aa < 2; ++aa)
+      for (int j = 0; j < 4; ++j) {
+        const int s2 = s0 - j >= s_lo ? s0 - j : s_lo;
+        const float* sl = a.seg_lam + (bh * ln + s2) * kD * kD;
+        gsv[j] = a.seg_lg_in ? a.seg_lg_in[bh * ln + s2] : 0.f;
 #pragma unroll
-        for (int bb = 0; bb < 2; ++bb)
-          pr[2 * aa + bb] = pr[2 * aa + bb] * gs +
-                            *reinterpret_cast<const f32x4*>(
-                                sl + ((2 * lq2 + bb) * 16 + l16) * kD + (2 * hq + aa) * 16 + 4 * g4);
+        for (int aa = 0; aa < 2; ++aa)
+#pragma unroll
+          for (int bb = 0; bb < 2; ++bb)
+            t[j][2 * aa + bb] = *reinterpret_cast<const f32x4*>(
+                sl + ((2 * lq2 + bb) * 16 + l16) * kD + (2 * hq + aa) * 16 + 4 * g4);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const bool use = s0 - j >= s_lo;
+        const float gs = a.seg_lg_in ? fexp2(gsv[j]) : 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) pr[e] = use ? pr[e] * gs + t[j][e] : pr[e];
+      }
     }
   }
   wait_vm<0>();

@@ -212,12 +212,14 @@ void bwd_f128(BwdArgs a) {
       dw[aa][b] = zero4();
     }
   if (a.seg_lam) {
-    const int s_lo = a.seg_lg_in ? seg + 1 : seg;
-    const int s_hi = a.seg_lg_in ? a.n_seg - 1 : seg;
+    // (the adjoint-only pass's segments: lam_r per fused segment, lam_n in all)
+    const int ln = a.lam_n ? a.lam_n : a.n_seg, end = (seg + 1) * a.lam_r;
+    const int s_lo = a.seg_lg_in ? end : end - 1;
+    const int s_hi = a.seg_lg_in ? ln - 1 : end - 1;
     // this thread's elements of segment s2's tile; the next tile's loads are
     // issued before the current one is folded in
     const auto tile = [&](int s2, f32x4 (&t)[2][4]) {
-      const float* sp = a.seg_lam + (bh * a.n_seg + s2) * kD * kD;
+      const float* sp = a.seg_lam + (bh * ln + s2) * kD * kD;
 #pragma unroll
       for (int aa = 0; aa < 2; ++aa)
 #pragma unroll
@@ -234,7 +236,7 @@ void bwd_f128(BwdArgs a) {
     stage_w0();  // (its loads overlap those of the first tile)
     for (int s2 = s_hi; s2 >= s_lo; --s2) {
       if (s2 - 1 >= s_lo) tile(s2 - 1, nxt);
-      const float gs = a.seg_lg_in ? fexp2(a.seg_lg_in[bh * a.n_seg + s2]) : 0.f;
+      const float gs = a.seg_lg_in ? fexp2(a.seg_lg_in[bh * ln + s2]) : 0.f;
 #pragma unroll
       for (int aa = 0; aa < 2; ++aa)
 #pragma unroll

@@ -116,8 +116,8 @@ __global__ __launch_bounds__(kNT) void bwd_lam(BwdArgs a) {
   SlotL<D>* const rs[2] = {&ring0, &ring1};
 
   const int per_seg = static_cast<int>((a.B * a.H + 7) / 8) * 8 * NTILE;
-  // segments 1 .. n_seg - 1 (8 consecutive heads and their tiles share an XCD)
-  const int seg = 1 + static_cast<int>(blockIdx.x / per_seg), bid = blockIdx.x % per_seg;
+  // segments seg_first .. n_seg - 1 (8 consecutive heads and their tiles share an XCD)
+  const int seg = a.seg_first + static_cast<int>(blockIdx.x / per_seg), bid = blockIdx.x % per_seg;
   const int grp = bid / (8 * NTILE), within = bid % (8 * NTILE);
   const int64_t bh = static_cast<int64_t>(grp) * 8 + (within & 7);
   if (bh >= a.B * a.H) return;
@@ -219,9 +219,9 @@ __global__ __launch_bounds__(kNT) void bwd_lam(BwdArgs a) {
 
 template <int D>
 hipError_t launch_lam(const BwdArgs& a, hipStream_t s) {
-  if (a.n_seg <= 1) return hipSuccess;
+  if (a.n_seg - a.seg_first <= 0) return hipSuccess;
   const int64_t groups = (a.B * a.H + 7) / 8;
-  const dim3 grid(static_cast<unsigned>(groups * 8 * (D / kTile<D>) * (a.n_seg - 1)));
+  const dim3 grid(static_cast<unsigned>(groups * 8 * (D / kTile<D>) * (a.n_seg - a.seg_first)));
   hipLaunchKernelGGL(bwd_lam<D>, grid, dim3(kNT), 0, s, a);
   return hipGetLastError();
 }
