@@ -279,7 +279,8 @@ gl_status_t gl_scan_qkv_fwd_ws(const gl_scan_desc_t* desc, const void* q, const 
  * recomputed inside the workspace `ws` of gl_scan_qkv_workspace_size bytes.
  * bf16 with dk = dv in {64, 128} (without GL_FLAG_GENERIC) runs
  * chunk-parallel on the matrix cores: the forward's chunk-start states
- * (bf16), then per group of eight 64-token chunks the adjoint increment,
+ * (bf16), then per group of 64-token chunks (sixteen; down to four when
+ * the problem is small) the adjoint increment,
  * decay and dW0 share, the adjoint carry over groups (fp32), and the
  * gradients of every chunk with the adjoint walked right to left through
  * its group (at 128, with W0' not given transposed, a transposed copy of it

@@ -651,7 +651,7 @@ struct QkvPlan {
   // group of chunks the fp32 adjoint leaving it (lam), its decay (gam) and
   // a dW0' share (dw); part is unused
   bool mfma = false;
-  int n_grp = 0;
+  int n_grp = 0, grp_chunks = 0;
   size_t lam = 0, gam = 0, w0t = 0;  // w0t: W0' transposed (d = 128, bf16)
 };
 gl_status_t qkv_plan(const gl_scan_desc_t* d, QkvPlan* p) {
@@ -668,7 +668,9 @@ gl_status_t qkv_plan(const gl_scan_desc_t* d, QkvPlan* p) {
     if (static_cast<int64_t>(BH) * p->n_chunks > 0x7fffffffLL)
       return fail(GL_ERROR_NOT_SUPPORTED, "B*H*chunks above 2^31-1");
     const size_t cells = BH * static_cast<size_t>(p->n_chunks);
-    p->n_grp = gls::mfma_qkv_bwd_groups(p->n_chunks);
+    p->grp_chunks = gls::mfma_qkv_bwd_group_chunks(static_cast<int64_t>(BH), p->n_chunks,
+                                                   static_cast<int>(d->d_in));
+    p->n_grp = gls::mfma_qkv_bwd_groups(p->n_chunks, p->grp_chunks);
     p->states = round_up(cells * dd * 2);
     const size_t groups = BH * static_cast<size_t>(p->n_grp);
     p->lam = round_up(groups * dd * sizeof(float));
@@ -730,6 +732,7 @@ gl_status_t gl_scan_qkv_bwd(const gl_scan_desc_t* desc, const void* q, const voi
     b.mf_gam = w + p.states + p.lam;
     b.part_dW0 = w + p.states + p.lam + p.gam;
     b.W0t = p.w0t ? w + p.states + p.lam + p.gam + p.dw : nullptr;
+    b.grp_chunks = p.grp_chunks;
     b.deta_out = deta; b.dalpha_out = dalpha;
     b.B = desc->B; b.H = desc->H; b.T = desc->T;
     b.d_in = static_cast<int>(desc->d_in); b.d_out = b.d_in;

@@ -100,6 +100,7 @@ struct BwdArgs {
   // The write-key reverse scan on the matrix cores at d = 128: room for W0'
   // transposed ([H][dk][dv] bf16) when it is not given so
   const void* W0t = nullptr;
+  int grp_chunks = 8;  // chunks per group of that scan's reverse pass
   // fp32 / fp64 matrix-core scans: the adjoint leaving every chunk
   // [B*H][n_chunks][d_out][d_in] and the per-chunk decay [B*H][n_chunks]
   // (compute type); part_dW0 then holds [n_chunks][B*H][d_out][d_in]
@@ -207,7 +208,8 @@ hipError_t launch_mfma_qkv_two_pass(const FwdArgs& a, hipStream_t s);
 // g = v; dx <- dk, dg <- dv; states / mf_lam / mf_gam / part_dW0 / W0t in
 // the workspace)
 bool mfma_qkv_bwd_ok(int io, int dk, int dv);
-int mfma_qkv_bwd_groups(int n_chunks);  // dW0' shares per sequence-head
+int mfma_qkv_bwd_groups(int n_chunks, int grp_chunks);  // groups (dW0' shares) per sequence-head
+int mfma_qkv_bwd_group_chunks(int64_t BH, int n_chunks, int d);  // chunks per group
 hipError_t launch_mfma_qkv_bwd(const BwdArgs& a, hipStream_t s);
 hipError_t launch_mfma_bwd_lam(const BwdArgs& a, hipStream_t s);  // adjoint-only segment pass
 hipError_t launch_mfma_bwd_f64(const BwdArgs& a, hipStream_t s);   // fused reverse scan, d = 64

@@ -22,7 +22,9 @@
 // and dalpha from <A_out, D_in>, pp_j = v_j . (A_out k_j), rr_u = q_u . (D_in^T dy_u)
 // and the row / column sums of Be o (Q K^T) (the same identity as the scan's).
 //
-// Chunks are taken in groups of kGrp (eight).  Five launches: the forward
+// Chunks are taken in groups (a.grp_chunks of them, chosen by the host:
+// sixteen, fewer when that would leave the GPU short of work-groups).  Five
+// launches: the forward
 // kernel's state-only instance (x = k, g = v) writes D_in of every chunk
 // (bf16); qkv_bwd_inc forms every group's adjoint increment (the chunk
 // formula over the group's tokens: sum_u e(L_{u-1}) dy_u q_u^T with L the
@@ -44,7 +46,6 @@ namespace gls {
 namespace {
 
 constexpr int kCk = 64;   // tokens per chunk
-constexpr int kGrp = 8;   // chunks per group (one work-group of each kind)
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
@@ -80,7 +81,7 @@ __global__ __launch_bounds__(4 * D) void qkv_bwd_inc(BwdArgs a, int n_grp) {
   const int n = a.n_chunks;
   const int64_t bh = blockIdx.x / n_grp, BH = a.B * a.H;
   const int grp = static_cast<int>(blockIdx.x % n_grp);
-  const int c_beg = grp * kGrp, c_end = std::min(n, c_beg + kGrp);
+  const int c_beg = grp * a.grp_chunks, c_end = std::min(n, c_beg + a.grp_chunks);
   const int64_t T = a.T, dd = static_cast<int64_t>(D) * D;
   const uint16_t* qb = static_cast<const uint16_t*>(a.q) + bh * T * D;
   const uint16_t* db = static_cast<const uint16_t*>(a.dy) + bh * T * D;
@@ -264,7 +265,7 @@ __global__ __launch_bounds__(8 * D) __attribute__((amdgpu_waves_per_eu(4, 4))) v
   const int n = a.n_chunks;
   const int64_t bh = blockIdx.x / n_grp;
   const int grp = static_cast<int>(blockIdx.x % n_grp);
-  const int c_beg = grp * kGrp, c_end = std::min(n, c_beg + kGrp);
+  const int c_beg = grp * a.grp_chunks, c_end = std::min(n, c_beg + a.grp_chunks);
   const int h = static_cast<int>(bh % a.H);
   const int64_t T = a.T;
   const int64_t dd = static_cast<int64_t>(D) * D;
@@ -525,7 +526,7 @@ hipError_t launch_d(const BwdArgs& a, hipStream_t s) {
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  const int n_grp = mfma_qkv_bwd_groups(n);
+  const int n_grp = mfma_qkv_bwd_groups(n, a.grp_chunks);
   const dim3 grid(static_cast<unsigned>(BH * n_grp));
   hipLaunchKernelGGL(qkv_bwd_inc<D>, grid, dim3(4 * D), 0, s, a, n_grp);
   e = hipGetLastError();
@@ -546,7 +547,20 @@ bool mfma_qkv_bwd_ok(int io, int dk, int dv) {
   return io == IO_BF16 && dk == dv && (dk == 64 || dk == 128);
 }
 
-int mfma_qkv_bwd_groups(int n_chunks) { return (n_chunks + kGrp - 1) / kGrp; }
+int mfma_qkv_bwd_groups(int n_chunks, int grp_chunks) {
+  return (n_chunks + grp_chunks - 1) / grp_chunks;
+}
+
+// Sixteen chunks per group, halved (down to four) while the gradient kernel
+// would have fewer work-groups than the GPU runs at once (two per CU at
+// d = 64, one at d = 128, 256 CUs).  Longer groups write fewer dW0' shares
+// and carries and walk more chunks per work-group.
+int mfma_qkv_bwd_group_chunks(int64_t BH, int n_chunks, int d) {
+  const int64_t want = d == 64 ? 512 : 256;
+  int g = 16;
+  while (g > 4 && BH * mfma_qkv_bwd_groups(n_chunks, g) < want) g /= 2;
+  return g;
+}
 
 // a: x = k (write key), g = v, q the read vector; dx <- dk, dg <- dv, dq;
 // in the workspace: states (bf16 [BH][n][D][D]), mf_lam (fp32
