@@ -232,14 +232,15 @@ struct alignas(16) GradLds {
 };
 
 // dalpha and deta of the chunk whose gates, sums and shares sit in L (wave
-// 0, lane = token): t0 its first token, cv its valid tokens.
-template <int D>
+// 0, lane = token): t0 its first token, cv its valid tokens; NC shares of
+// <A_out, D_in> (one per wave).
+template <int D, int NC = D / 8>
 __device__ __forceinline__ void chunk_gate_grads(const GradLds<D>& L, const BwdArgs& a, int64_t bh,
                                                  int64_t t0, int cv, int lane) {
   const int ir = kCk - 1 - lane;
   float c0 = 0.f;
 #pragma unroll
-  for (int w = 0; w < D / 8; ++w) c0 += L.c0[w];
+  for (int w = 0; w < NC; ++w) c0 += L.c0[w];
   float ppl = 0.f, rr_r = 0.f, del = 0.f;
 #pragma unroll
   for (int j = 0; j < D / 32; ++j) {
@@ -505,6 +506,366 @@ __global__ __launch_bounds__(8 * D) __attribute__((amdgpu_waves_per_eu(4, 4))) v
   }
 }
 
+// ---- the gradients of every chunk at D = 128, eight waves ----
+// The same walk and products as qkv_bwd_chunk, laid out for fewer LDS
+// fragment reads: wave w forms the 32 x 32 block (columns 32 (w / 2) ..,
+// tokens 32 (w % 2) ..) of every output, so each fragment it reads feeds two
+// MFMAs, and keeps eight 16 x 16 blocks of the fp32 adjoint (row blocks
+// 2 (w % 4) + {0, 1}, column blocks 4 (w / 4) + {0, .., 3}).  Two waves per
+// SIMD with 256 registers each hold the next chunk's tiles (twelve 16-byte
+// units per thread) while the current one is multiplied.
+constexpr int kW8T = 512;  // threads
+
+__global__ __launch_bounds__(kW8T) __attribute__((amdgpu_waves_per_eu(2, 2))) void qkv_bwd_chunk128(
+    BwdArgs a, int n_grp) {
+  constexpr int D = 128, NT = kW8T, NW = NT / 64, KS = D / 32;
+  constexpr int NU = kCk * D / 8 / NT;  // 16-byte units of a token tile per thread (2)
+  constexpr int NS = D * D / 8 / NT;    // of D_in (4)
+  __shared__ GradLds<D> L;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g4 = lane >> 4, l16 = lane & 15;
+  const int n = a.n_chunks;
+  const int64_t bh = blockIdx.x / n_grp;
+  const int grp = static_cast<int>(blockIdx.x % n_grp);
+  const int c_beg = grp * a.grp_chunks, c_end = std::min(n, c_beg + a.grp_chunks);
+  const int h = static_cast<int>(bh % a.H);
+  const int64_t T = a.T;
+  const int64_t dd = static_cast<int64_t>(D) * D;
+  // W0' stored [k][r]: the given one if transposed, else the copy
+  const uint16_t* wt = static_cast<const uint16_t*>(a.w0_t ? a.W0 : a.W0t) + h * dd;
+  // adjoint blocks of this wave: i -> row block 2 (w % 4) + i / 4, column block 4 (w / 4) + i % 4
+  const int arb = 2 * (wave & 3), acb = 4 * (wave >> 2);
+  // output blocks of this wave: column blocks 2 cg + {0, 1}, token blocks 2 tp + {0, 1}
+  const int cg = wave >> 1, tp = wave & 1;
+  // W0'^T fragments of this wave's two column blocks (the same for every chunk)
+  bf16x8 wf[2][KS];
+#pragma unroll
+  for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+    for (int kr = 0; kr < KS; ++kr)
+      wf[h2][kr] = *reinterpret_cast<const bf16x8*>(wt + ((2 * cg + h2) * 16 + l16) * D + kr * 32 +
+                                                    8 * g4);
+  f32x4 A[8];
+  {
+    const float* pa = static_cast<const float*>(a.mf_lam) + (bh * n_grp + grp) * dd;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      A[i] = *reinterpret_cast<const f32x4*>(pa + ((arb + i / 4) * 16 + l16) * D +
+                                             (acb + i % 4) * 16 + 4 * g4);
+  }
+  // the next chunk's tiles and gates, in registers
+  u32x4 uq[NU], uk[NU], uv[NU], ud[NU], us[NS];
+  float eta_l = 0.f, al_l = 1.f;
+  const auto fetch = [&](int c) {
+    const int64_t t0 = static_cast<int64_t>(c) * kCk;
+    const int cv = static_cast<int>(std::min<int64_t>(kCk, T - t0));
+    const int64_t tok = (bh * T + t0) * D;
+    const auto rs = [&](const void* base) {
+      return buffer_rsrc(static_cast<const uint16_t*>(base) + tok, cv * D * 2);
+    };
+#pragma unroll
+    for (int j = 0; j < NU; ++j) {
+      const uint32_t off = static_cast<uint32_t>((tid + NT * j) * 16);
+      uq[j] = __builtin_amdgcn_raw_buffer_load_b128(rs(a.q), off, 0, 0);
+      uk[j] = __builtin_amdgcn_raw_buffer_load_b128(rs(a.x), off, 0, 0);
+      uv[j] = __builtin_amdgcn_raw_buffer_load_b128(rs(a.g), off, 0, 0);
+      ud[j] = __builtin_amdgcn_raw_buffer_load_b128(rs(a.dy), off, 0, 0);
+    }
+    const __amdgpu_buffer_rsrc_t rst =
+        buffer_rsrc(static_cast<const uint16_t*>(a.states) + (bh * n + c) * dd, D * D * 2);
+#pragma unroll
+    for (int j = 0; j < NS; ++j)
+      us[j] = __builtin_amdgcn_raw_buffer_load_b128(rst, static_cast<uint32_t>((tid + NT * j) * 16),
+                                                    0, 0);
+    const uint32_t go = static_cast<uint32_t>(lane * 4);
+    eta_l = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+        buffer_rsrc(static_cast<const float*>(a.eta) + bh * T + t0, cv * 4), go, 0, 0));
+    al_l = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+        buffer_rsrc(static_cast<const float*>(a.alpha) + bh * T + t0, cv * 4), go, 0, 0));
+  };
+  if (c_end > c_beg) fetch(c_end - 1);
+  // the set-up loads done: the waits the compiler places inside the walk
+  // then count only the walk's own loads and stores
+  wait_vm<0>();
+
+  LaneOff<D> o = lane_off<D>(lane);
+  LaneOff<kCk> o64 = lane_off<kCk>(lane);
+  for (int c = c_end - 1; c >= c_beg; --c) {
+    // Most of the LDS lies beyond the 64 KB reach of the LDS instructions'
+    // offset field; an empty asm on the lane offsets keeps the addresses
+    // derived from them from being hoisted out of the loop.
+    asm volatile("" : "+v"(o.b), "+v"(o.t0), "+v"(o.t1), "+v"(o.w));
+    asm volatile("" : "+v"(o64.b), "+v"(o64.t0), "+v"(o64.t1), "+v"(o64.w));
+    const int64_t t0 = static_cast<int64_t>(c) * kCk;
+    const int cv = static_cast<int>(std::min<int64_t>(kCk, T - t0));
+    const int64_t tok = (bh * T + t0) * D;
+    __syncthreads();  // the previous chunk is done with every tile and share
+    if (wave == 0) {
+      // dalpha and deta of the previous chunk in walk order, then this
+      // chunk's gates in their place
+      // (also in the first step, with no valid tokens: the stores are then
+      // dropped, and every step issues the same number of them)
+      const int64_t tq = t0 + kCk;
+      chunk_gate_grads<D, NW>(L, a, bh, tq,
+                              c + 1 < c_end ? static_cast<int>(std::min<int64_t>(kCk, T - tq)) : 0,
+                              lane);
+      gates_v(eta_l, lane < cv ? al_l : 1.f, L.rc, lane);
+    }
+    // P^T and Be^T start at zero (only the causal parts are written)
+    reinterpret_cast<u32x4*>(L.PT)[tid] = u32x4{0u, 0u, 0u, 0u};
+    reinterpret_cast<u32x4*>(L.BT)[tid] = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int j = 0; j < NU; ++j) {
+      put_unit<D>(L.Q, tid + NT * j, uq[j]);
+      put_unit<D>(L.K, tid + NT * j, uk[j]);
+      put_unit<D>(L.V, tid + NT * j, uv[j]);
+      put_unit<D>(L.DY, tid + NT * j, ud[j]);
+    }
+#pragma unroll
+    for (int j = 0; j < NS; ++j) put_unit<D>(L.S, tid + NT * j, us[j]);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) put4<D>(L.A, o, (arb + i / 4) * 16, (acb + i % 4) * 16, pack4f(A[i]));
+    if (c > c_beg) fetch(c - 1);
+    __syncthreads();
+
+    // <A_out, D_in> over this wave's blocks (A_out in fp32)
+    {
+      float cp = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        cp += dot4f(A[i], unpack4f(get4<D>(L.S, o, (arb + i / 4) * 16, (acb + i % 4) * 16)));
+      cp = wave_sum(cp);
+      if (lane == 0) L.c0[wave] = cp;
+    }
+    // ---- causal blocks (ten): Q K^T and DY V^T, decayed; P and Be
+    // written transposed, the row / column sums of Be o (Q K^T)
+    for (int b = wave; b < 10; b += NW) {
+      __builtin_amdgcn_sched_barrier(0);
+      const int ib = tri_i(b), jb = tri_j(b);
+      f32x4 qk = zero4(), dv = zero4();
+#pragma unroll
+      for (int kb = 0; kb < KS; ++kb) {
+        qk = mfma16x16x32(frag_s<D>(L.Q, o, ib * 16, kb * 32), frag_s<D>(L.K, o, jb * 16, kb * 32),
+                          qk);
+        dv = mfma16x16x32(frag_s<D>(L.DY, o, ib * 16, kb * 32), frag_s<D>(L.V, o, jb * 16, kb * 32),
+                          dv);
+      }
+      const int col = jb * 16 + l16, r0 = ib * 16 + 4 * g4;
+      const float lc = L.rc.li[col], nbc = L.rc.nb[col];
+      f32x4 p, be, z;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const bool on = col < r0 + q;
+        const float e = on ? fexp2(L.rc.lq[r0 + q] - lc) : 0.f;
+        p[q] = qk[q] * e;
+        be[q] = dv[q] * (e * nbc);
+        z[q] = be[q] * qk[q];
+      }
+      put4<kCk>(L.PT, o64, jb * 16, ib * 16, pack4f(p));
+      put4<kCk>(L.BT, o64, jb * 16, ib * 16, pack4f(be));
+      f32x4 zr;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) zr[q] = row16_sum(z[q]);
+      if (l16 == 15) *reinterpret_cast<f32x4*>(&L.qk.qq[b][4 * g4]) = zr;
+      const float t = sum_rows(z[0] + z[1] + z[2] + z[3]);
+      if (g4 == 0) L.qk.kk[b][l16] = t;
+    }
+    __syncthreads();
+
+    // ---- outputs, transposed (rows = columns of dq, dk, dv; columns =
+    // tokens); tile [h2][hb]: column block 2 cg + h2, token block 2 tp + hb
+    float eqi[2], sci[2], nbi[2], e2i[2];
+    uint32_t so[2][2];
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
+      const int ti = (2 * tp + hb) * 16 + l16;  // this lane's token
+      eqi[hb] = L.rc.eq[ti];
+      e2i[hb] = L.rc.e2[ti];
+      nbi[hb] = L.rc.nb[ti];
+      sci[hb] = nbi[hb] * e2i[hb];
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2)
+        so[h2][hb] = static_cast<uint32_t>((ti * D + (2 * cg + h2) * 16 + 4 * g4) * 2);
+    }
+    const __amdgpu_buffer_rsrc_t rdq = buffer_rsrc(static_cast<uint16_t*>(a.dq) + tok, cv * D * 2);
+    const __amdgpu_buffer_rsrc_t rdk = buffer_rsrc(static_cast<uint16_t*>(a.dx) + tok, cv * D * 2);
+    const __amdgpu_buffer_rsrc_t rdv = buffer_rsrc(static_cast<uint16_t*>(a.dg) + tok, cv * D * 2);
+    float rr[2] = {0.f, 0.f}, pp[2] = {0.f, 0.f}, de[2] = {0.f, 0.f};
+    {
+      // dq^T: (Be K)^T + W0'^T dy + e(lq) D_in^T dy
+      f32x4 aq[2][2], sq[2][2];
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb) aq[h2][hb] = sq[h2][hb] = zero4();
+#pragma unroll
+      for (int kj = 0; kj < 2; ++kj) {
+        __builtin_amdgcn_sched_barrier(0);  // one K step of fragments live at a time
+        bf16x8 kf[2], bf[2];
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) kf[h2] = frag_ts<D>(L.K, o, kj * 32, (2 * cg + h2) * 16);
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb) bf[hb] = frag_ts<kCk>(L.BT, o64, kj * 32, (2 * tp + hb) * 16);
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+          for (int hb = 0; hb < 2; ++hb) aq[h2][hb] = mfma16x16x32(kf[h2], bf[hb], aq[h2][hb]);
+      }
+#pragma unroll
+      for (int kr = 0; kr < KS; ++kr) {
+        __builtin_amdgcn_sched_barrier(0);
+        bf16x8 sf[2], df[2];
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) sf[h2] = frag_ts<D>(L.S, o, kr * 32, (2 * cg + h2) * 16);
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb) df[hb] = frag_s<D>(L.DY, o, (2 * tp + hb) * 16, kr * 32);
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+          for (int hb = 0; hb < 2; ++hb) {
+            sq[h2][hb] = mfma16x16x32(sf[h2], df[hb], sq[h2][hb]);
+            aq[h2][hb] = mfma16x16x32(wf[h2][kr], df[hb], aq[h2][hb]);
+          }
+      }
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb) {
+          // q_t[k], k = (2 cg + h2) 16 + 4 g4 ..
+          const f32x4 qv = unpack4f(get4<D>(L.Q, o, (2 * tp + hb) * 16, (2 * cg + h2) * 16));
+          rr[hb] += dot4f(qv, sq[h2][hb]);
+          store8(rdq, so[h2][hb], pack4f(aq[h2][hb] + eqi[hb] * sq[h2][hb]));
+        }
+    }
+    {
+      // dk^T: (Be^T Q)^T - eta e(l_last - l) (A_out^T v)^T
+      f32x4 ak[2][2], sk[2][2];
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb) ak[h2][hb] = sk[h2][hb] = zero4();
+#pragma unroll
+      for (int ku = 0; ku < 2; ++ku) {
+        __builtin_amdgcn_sched_barrier(0);
+        bf16x8 qf[2], bf[2];
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) qf[h2] = frag_ts<D>(L.Q, o, ku * 32, (2 * cg + h2) * 16);
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb) bf[hb] = frag_s<kCk>(L.BT, o64, (2 * tp + hb) * 16, ku * 32);
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+          for (int hb = 0; hb < 2; ++hb) ak[h2][hb] = mfma16x16x32(qf[h2], bf[hb], ak[h2][hb]);
+      }
+#pragma unroll
+      for (int kr = 0; kr < KS; ++kr) {
+        __builtin_amdgcn_sched_barrier(0);
+        bf16x8 af[2], vf[2];
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) af[h2] = frag_ts<D>(L.A, o, kr * 32, (2 * cg + h2) * 16);
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb) vf[hb] = frag_s<D>(L.V, o, (2 * tp + hb) * 16, kr * 32);
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+          for (int hb = 0; hb < 2; ++hb) sk[h2][hb] = mfma16x16x32(af[h2], vf[hb], sk[h2][hb]);
+      }
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb)
+          store8(rdk, so[h2][hb], pack4f(ak[h2][hb] + sci[hb] * sk[h2][hb]));
+    }
+    {
+      // u^T: e(l_last - l) (A_out k)^T + (P^T dy)^T;  dv = -eta u
+      f32x4 au[2][2], su[2][2];
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb) au[h2][hb] = su[h2][hb] = zero4();
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk) {
+        __builtin_amdgcn_sched_barrier(0);
+        bf16x8 af[2], kf[2];
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) af[h2] = frag_s<D>(L.A, o, (2 * cg + h2) * 16, kk * 32);
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb) kf[hb] = frag_s<D>(L.K, o, (2 * tp + hb) * 16, kk * 32);
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+          for (int hb = 0; hb < 2; ++hb) su[h2][hb] = mfma16x16x32(af[h2], kf[hb], su[h2][hb]);
+      }
+#pragma unroll
+      for (int ku = 0; ku < 2; ++ku) {
+        __builtin_amdgcn_sched_barrier(0);
+        bf16x8 df[2], pf[2];
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) df[h2] = frag_ts<D>(L.DY, o, ku * 32, (2 * cg + h2) * 16);
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb) pf[hb] = frag_s<kCk>(L.PT, o64, (2 * tp + hb) * 16, ku * 32);
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+          for (int hb = 0; hb < 2; ++hb) au[h2][hb] = mfma16x16x32(df[h2], pf[hb], au[h2][hb]);
+      }
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb) {
+          const f32x4 u = au[h2][hb] + e2i[hb] * su[h2][hb];
+          // v_t[r], r = (2 cg + h2) 16 + 4 g4 ..
+          const f32x4 vv = unpack4f(get4<D>(L.V, o, (2 * tp + hb) * 16, (2 * cg + h2) * 16));
+          de[hb] -= dot4f(vv, u);
+          pp[hb] += dot4f(vv, su[h2][hb]);
+          store8(rdv, so[h2][hb], pack4f(nbi[hb] * u));
+        }
+    }
+    // shares over this wave's 32 columns: sum over the four lane groups
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
+      const float r1 = sum_rows(rr[hb]), p1 = sum_rows(pp[hb]), d1 = sum_rows(de[hb]);
+      if (g4 == 0) {
+        const int ti = (2 * tp + hb) * 16 + l16;
+        L.rr[cg][ti] = r1;
+        L.pp[cg][ti] = p1;
+        L.de[cg][ti] = d1;
+      }
+    }
+    // ---- the adjoint entering this chunk, which leaves the one before it:
+    // A <- e(l_last) A + sum_u e(lq_u) dy_u q_u^T (operands swapped, so the
+    // product comes out in A's register layout)
+    __builtin_amdgcn_sched_barrier(0);
+    {
+      const float gam = L.rc.gam;
+      f32x4 vi[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) vi[i] = zero4();
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const f32x4 e0 = *reinterpret_cast<const f32x4*>(&L.rc.eq[kb * 32 + 8 * g4]);
+        const f32x4 e1 = *reinterpret_cast<const f32x4*>(&L.rc.eq[kb * 32 + 8 * g4 + 4]);
+        bf16x8 qf[4], df[2];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) qf[j] = scale8(frag_ts<D>(L.Q, o, kb * 32, (acb + j) * 16), e0, e1);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) df[j] = frag_ts<D>(L.DY, o, kb * 32, (arb + j) * 16);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) vi[i] = mfma16x16x32(qf[i % 4], df[i / 4], vi[i]);
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) A[i] = gam * A[i] + vi[i];
+    }
+  }
+  // dalpha and deta of the last chunk walked (the group's first)
+  __syncthreads();
+  if (wave == 0 && c_end > c_beg) {
+    const int64_t t0 = static_cast<int64_t>(c_beg) * kCk;
+    chunk_gate_grads<D, NW>(L, a, bh, t0, static_cast<int>(std::min<int64_t>(kCk, T - t0)), lane);
+  }
+}
+
 template <int D>
 hipError_t launch_d(const BwdArgs& a, hipStream_t s) {
   const int64_t BH = a.B * a.H;
@@ -537,7 +898,10 @@ hipError_t launch_d(const BwdArgs& a, hipStream_t s) {
                      D * D, n_eb);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(qkv_bwd_chunk<D>, grid, dim3(8 * D), 0, s, a, n_grp);
+  if constexpr (D == 128)
+    hipLaunchKernelGGL(qkv_bwd_chunk128, grid, dim3(kW8T), 0, s, a, n_grp);
+  else
+    hipLaunchKernelGGL(qkv_bwd_chunk<D>, grid, dim3(8 * D), 0, s, a, n_grp);
   return hipGetLastError();
 }
 
