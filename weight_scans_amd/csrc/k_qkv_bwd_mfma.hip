@@ -626,7 +626,6 @@ __global__ __launch_bounds__(kW8T) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
     for (int j = 0; j < NS; ++j) put_unit<D>(L.S, tid + NT * j, us[j]);
 #pragma unroll
     for (int i = 0; i < 8; ++i) put4<D>(L.A, o, (arb + i / 4) * 16, (acb + i % 4) * 16, pack4f(A[i]));
-    if (c > c_beg) fetch(c - 1);
     __syncthreads();
 
     // <A_out, D_in> over this wave's blocks (A_out in fp32)
@@ -638,6 +637,11 @@ __global__ __launch_bounds__(kW8T) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
       cp = wave_sum(cp);
       if (lane == 0) L.c0[wave] = cp;
     }
+    // The next chunk's loads: issued here by the waves with one causal
+    // block, after their second block by waves 0 and 1, so that they do not
+    // hold up the tile writes above or the waves with the most work (the
+    // loads have the rest of the step to arrive).
+    if (wave >= 10 - NW && c > c_beg) fetch(c - 1);
     // ---- causal blocks (ten): Q K^T and DY V^T, decayed; P and Be
     // written transposed, the row / column sums of Be o (Q K^T)
     for (int b = wave; b < 10; b += NW) {
@@ -671,6 +675,7 @@ __global__ __launch_bounds__(kW8T) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
       const float t = sum_rows(z[0] + z[1] + z[2] + z[3]);
       if (g4 == 0) L.qk.kk[b][l16] = t;
     }
+    if (wave < 10 - NW && c > c_beg) fetch(c - 1);
     __syncthreads();
 
     // ---- outputs, transposed (rows = columns of dq, dk, dv; columns =
