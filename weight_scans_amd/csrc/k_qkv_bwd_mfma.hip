@@ -63,7 +63,7 @@ __device__ __forceinline__ void put_unit(__bf16* tile, int u, const u32x4& v) {
 // ---- adjoint increment, decay and dW0' share of every group ----
 // Work-group (bh, group), D / 16 waves (wave w: rows 16 w .. of the
 // increment and of the dW0' share), walks the chunks of its group in order;
-// the loads of the next chunk are in flight while the current one is
+// the loads of the next two chunks are in flight while the current one is
 // multiplied.
 template <int D>
 struct alignas(16) IncLds {
@@ -85,26 +85,38 @@ __global__ __launch_bounds__(4 * D) void qkv_bwd_inc(BwdArgs a, int n_grp) {
   const int64_t T = a.T, dd = static_cast<int64_t>(D) * D;
   const uint16_t* qb = static_cast<const uint16_t*>(a.q) + bh * T * D;
   const uint16_t* db = static_cast<const uint16_t*>(a.dy) + bh * T * D;
-  u32x4 uq[2], ud[2];  // 8 D units per tile, two per thread
-  float al = 1.f;
-  const auto fetch = [&](int c) {
-    const int64_t t0 = static_cast<int64_t>(c) * kCk;
-    const int cv = static_cast<int>(std::min<int64_t>(kCk, T - t0));
+  // two chunks in flight: 8 D units per tile, two per thread, and the
+  // lane's alpha (raw: the padding select is made where it is used, so that
+  // no wait follows the loads)
+  u32x4 uq[2][2], ud[2][2];
+  float alr[2];
+  // every step issues the same loads (past the group's end into empty
+  // buffers), so the waits the compiler places are the same in every step
+  const auto valid = [&](int c) {
+    return c < c_end ? static_cast<int>(std::min<int64_t>(kCk, T - static_cast<int64_t>(c) * kCk))
+                     : 0;
+  };
+  const auto fetch = [&](auto PC, int c) {
+    constexpr int P = decltype(PC)::value;
+    const int cv = valid(c);
+    const int64_t t0 = cv > 0 ? static_cast<int64_t>(c) * kCk : 0;
     const __amdgpu_buffer_rsrc_t rq = buffer_rsrc(qb + t0 * D, cv * D * 2);
     const __amdgpu_buffer_rsrc_t rd = buffer_rsrc(db + t0 * D, cv * D * 2);
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const uint32_t off = static_cast<uint32_t>((tid + NT * j) * 16);
-      uq[j] = __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0);
-      ud[j] = __builtin_amdgcn_raw_buffer_load_b128(rd, off, 0, 0);
+      uq[P][j] = __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0);
+      ud[P][j] = __builtin_amdgcn_raw_buffer_load_b128(rd, off, 0, 0);
     }
     const __amdgpu_buffer_rsrc_t ra =
         buffer_rsrc(static_cast<const float*>(a.alpha) + bh * T + t0, cv * 4);
-    const float x = __builtin_bit_cast(
+    alr[P] = __builtin_bit_cast(
         float, __builtin_amdgcn_raw_buffer_load_b32(ra, static_cast<uint32_t>(lane * 4), 0, 0));
-    al = lane < cv ? x : 1.f;
   };
-  fetch(c_beg);
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  fetch(I0{}, c_beg);
+  fetch(I1{}, c_beg + 1);
   const LaneOff<D> o = lane_off<D>(lane);
   const int rb = wave;
   // accumulators in the transposed MFMA layout (operands swapped): lane
@@ -113,19 +125,20 @@ __global__ __launch_bounds__(4 * D) void qkv_bwd_inc(BwdArgs a, int n_grp) {
 #pragma unroll
   for (int cb = 0; cb < NB; ++cb) w[cb] = v[cb] = zero4();
   float lg = 0.f;  // log2 of the decay from the group's start to chunk c (wave 0)
-  for (int c = c_beg; c < c_end; ++c) {
+  const auto step = [&](auto PC, int c) {
+    constexpr int P = decltype(PC)::value;
     __syncthreads();  // the previous chunk's fragment reads are done
     if (wave == 0) {
-      const ChunkGates gt = chunk_gates(al, lane);
+      const ChunkGates gt = chunk_gates(lane < valid(c) ? alr[P] : 1.f, lane);
       L.eq[lane] = fexp2(lg + gt.lq);
       lg += gt.llast;
     }
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      put_unit<D>(L.Q, tid + NT * j, uq[j]);
-      put_unit<D>(L.DY, tid + NT * j, ud[j]);
+      put_unit<D>(L.Q, tid + NT * j, uq[P][j]);
+      put_unit<D>(L.DY, tid + NT * j, ud[P][j]);
     }
-    if (c + 1 < c_end) fetch(c + 1);
+    fetch(PC, c + 2);
     __syncthreads();
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -139,7 +152,15 @@ __global__ __launch_bounds__(4 * D) void qkv_bwd_inc(BwdArgs a, int n_grp) {
         v[cb] = mfma16x16x32(scale8(qf, e0, e1), df, v[cb]);
       }
     }
+  };
+  // (the loop's back edge always follows both steps, so the waits in it see
+  // one pattern of loads)
+  int c = c_beg;
+  for (; c + 1 < c_end; c += 2) {
+    step(I0{}, c);
+    step(I1{}, c + 1);
   }
+  if (c < c_end) step(I0{}, c);
   // the group's increment arrives at the group before it (fp32); its decay
   const int r = rb * 16 + l16;
   if (grp > 0) {
