@@ -19,12 +19,15 @@
 // is finished (y and the state update), the scores of chunk c + 1 are formed
 // and the gates of chunk c + 2 derived, and the loads of chunks
 // c + 3 and c + 4 are in flight.  Sixteen waves (four per SIMD) in two roles:
-// y waves 0-7 own the 16 x 16 output block (token block w/2, row block w%2)
-// of y and the score blocks (w, and 8 + w for w < 2); state waves 8-15 own
-// D/64 16 x 16 blocks of the fp32 state, issue every load (and wait for
-// them), store the chunk-start states, scale the g tile and (one of them)
-// derive the gates.  In the state-only instance the idle y waves 2 and 3
-// derive the gates instead, one half each.  Each role runs its own copy
+// y waves 0-3 own two 16 x 16 blocks of y (token blocks 2 (w/2) and
+// 2 (w/2) + 1, row block w%2), y waves 4-7 one strip each of the next
+// chunk's score blocks, and y wave 4 also derives the gates; state waves
+// 8-15 own D/64 16 x 16 blocks of the fp32 state, issue every load (and wait
+// for them), store the chunk-start states and scale the g tile.  (The state
+// waves' step is the longest: the gates moved off them shortened it a
+// little, the g scaling or score blocks moved onto them lengthened it.)  In
+// the state-only instance the idle y waves 2 and 3 derive the gates, one
+// half each.  Each role runs its own copy
 // of the chunk loop, so registers are allocated per role.  All LDS tiles are
 // XOR-swizzled (mfma.hpp) so that fragment reads are free of bank conflicts.
 //
@@ -57,10 +60,13 @@ constexpr int kTN = 32;        // rows of the adaptation per work-group
 constexpr int kNW = 16;        // waves per work-group: 8 y waves, 8 state (loader) waves
 constexpr int kNT = 64 * kNW;  // threads
 constexpr int kRing = 5;       // chunk slots: 3 in use, 2 in flight
-// the gates: with y, state wave kPrepWave alone; without y (the state-only
-// instance, where the y waves are otherwise idle), y waves kPrepWave and
-// kPrepWave + 1, one half each
+// the gates: with y, y wave kPrepWaveY alone (the one with the lightest
+// score strip: the state waves carry the loads and the state update, the
+// longest chain of a step); without y (the state-only instance, where the y
+// waves are otherwise idle), y waves kPrepWave and kPrepWave + 1, one half
+// each
 constexpr int kPrepWave = 2;
+constexpr int kPrepWaveY = 4;
 
 // Per-token factors of a chunk derived from the gates (i = token, b = 16-token
 // block of i, m_b = l_{16 b - 1} with m_0 = 0):
@@ -447,7 +453,7 @@ __global__ __launch_bounds__(kNT) void fwd_mfma(FwdArgs a) {
   }
   lds_barrier();
   float lsum = 0.f;  // sum of l_last over the segment's chunks (prep wave)
-  if (HAS_Y && role == 1 && w8 == kPrepWave) {
+  if (HAS_Y && role == 0 && w8 == kPrepWaveY) {
     lsum += prep_gates<D, 2>(*rs[0], cv_of(c_beg), lane);
     lsum += prep_gates<D, 2>(*rs[1], cv_of(c_beg + 1), lane);
   }
@@ -502,7 +508,6 @@ __global__ __launch_bounds__(kNT) void fwd_mfma(FwdArgs a) {
         else
           store8(r_st, st_g, *reinterpret_cast<const uint2*>(sp));
       }
-      if (HAS_Y && w8 == kPrepWave) lsum += prep_gates<D, 2>(nx2, cv_of(c + 2), lane);
       if constexpr (HILO)
         scale_g_split<D>(nx1, GS_s[(vl + 1) & 1], GL.t[(vl + 1) & 1], gs_off, gs_row);
       else
@@ -535,6 +540,9 @@ __global__ __launch_bounds__(kNT) void fwd_mfma(FwdArgs a) {
       }
     } else {
       if (HAS_Y && w8 >= 4) score_strip<D>(nx1, AT_s[(vl + 1) & 1], oX, oA, w8 - 4, lane);
+      // gates of chunk c + 2 (loaded: the state waves waited for it before
+      // the barrier)
+      if (HAS_Y && w8 == kPrepWaveY) lsum += prep_gates<D, 2>(nx2, cv_of(c + 2), lane);
       // gates of chunk c + 2 (loaded: the state waves waited for it before
       // the barrier), two halves on two waves
       if (!HAS_Y) {
@@ -623,7 +631,8 @@ __global__ __launch_bounds__(kNT) void fwd_mfma(FwdArgs a) {
       *reinterpret_cast<f32x4*>(so + (r0 + rbw * 16 + l16) * D + cb * 16 + 4 * g4) = sacc[s];
     }
   }
-  if (a.seg_out && a.seg_lg && role == (HAS_Y ? 1 : 0) && tile == 0 && w8 == kPrepWave && lane == 0)
+  if (a.seg_out && a.seg_lg && role == 0 && tile == 0 && w8 == (HAS_Y ? kPrepWaveY : kPrepWave) &&
+      lane == 0)
     a.seg_lg[bh * a.n_seg + seg] = lsum;
 }
 
